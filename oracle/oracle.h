@@ -1,0 +1,113 @@
+/*
+ * CPU oracle for the verification step of tree speculative decoding.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is the plain, slow, scalar fp64 statement of
+ * what the verification step computes.  It is used by the test-suite, by the
+ * smoke check and by the benchmark's CPU-baseline leg; nothing on the product
+ * path links or calls it.  It shares no source with the GPU library.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [EP]  "EAGLE-Pangu: Accelerator-Safe Tree Speculative Decoding on Ascend
+ *        NPUs" (gist.science summary), technical summary section 2
+ *        (Metodologia): branchable KV cache with length / path-index commit;
+ *        shifted indexing with a dummy row 0 for the root instead of -1;
+ *        ancestor index tables; range, acyclicity and depth checks; the tree
+ *        attention mask that lets a token see only itself and its ancestors.
+ *  [PX]  "Accelerating Sonar Through Speculation" (Perplexity), sections
+ *        "Decodificacion Especulativa", "Objetivo-Borrador" and "EAGLE":
+ *        n drafted tokens give up to n+1 emitted tokens; the longest
+ *        acceptable sequence is kept; acceptance compares the full draft and
+ *        target distributions; the target logits after the accepted sequence
+ *        give one extra (bonus) token.
+ *  [SSD] "Speculative Speculative Decoding" (gist.science summary), sections 3B
+ *        and 5: residual probability mass, exactness of the output distribution.
+ *
+ * Index conventions: node i in [0,N) owns row r = i+1; row 0 is the root
+ * (the dummy row of [EP] sec. 2).  parents[i] = -1 means "child of the root".
+ *
+ * Per-sequence status codes (shared meaning with the GPU library, not code):
+ *  0 ok, 1 parent out of range, 2 cycle, 3 depth > max_depth,
+ *  4 token id outside [0,V), 5 needed block-table entry is the ghost block 0
+ *  or outside the pool, 6 capacity exceeded.
+ */
+#ifndef SV_ORACLE_H
+#define SV_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Tree tensorisation ([EP] sec. 2, "Semantica de Tensores de Arbol Segura").
+ * parents [B,N]; outputs anc_bits [B,N,W] (W = ceil(N/64)), depth [B,N],
+ * path_rows [B,N+1,max_depth] (nullable), status [B].  Returns 0, or -1 on bad
+ * sizes. */
+int orc_build_tree_mask(const int32_t* parents, int32_t B, int32_t N, int32_t max_depth,
+                        uint64_t* anc_bits, int32_t* depth, int32_t* path_rows, int32_t* status);
+
+/* Ancestor-masked GQA tree attention ([EP] sec. 2, "Ejecucion del Maestro con
+ * Mascara de Arbol Fusionada"), fp64 throughout.
+ * dtype 0 = fp32, 1 = bf16 (uint16 bit patterns) for q / caches / tree KV.
+ * Output is fp64: out[n_sel][D] for the selected (b, node, q-head) triples, or
+ * out[B][N][Hq][D] when sel == NULL. */
+typedef struct {
+  int32_t B, N, Hq, Hkv, D, dtype;
+  double scale;
+  int32_t paged, Lcap, block_size, max_blocks, num_blocks;
+  const void* q;          /* [B,N,Hq,D] */
+  const void* k_cache;    /* contiguous [B,Hkv,Lcap,D] | paged [num_blocks,Hkv,bs,D] */
+  const void* v_cache;
+  const void* k_tree;     /* [B,Hkv,N+1,D], row 0 is the ghost row */
+  const void* v_tree;
+  const int32_t* block_table; /* [B,max_blocks] */
+  const int32_t* prefix_len;  /* [B] */
+  const int32_t* parents;     /* [B,N] */
+  int32_t max_depth;
+  const int64_t* sel;         /* flat (b*N + i)*Hq + h, or NULL for all */
+  int64_t n_sel;
+  double* out;
+} orc_attn_args;
+int orc_tree_attention(const orc_attn_args* a);
+
+/* Speculative acceptance ([PX], [SSD]); mode 0 greedy, 1 stochastic.
+ * logits dtype 0 = fp32, 1 = bf16.  target/draft logits [B,N+1,V];
+ * u_accept, u_sample [B,N+1] (stochastic only).
+ * Outputs: accept_len [B], accept_rows [B,max_depth], out_tokens [B,max_depth+1],
+ * num_out [B], stop_row [B], status [B], flagged [B] (stochastic: a draw was
+ * within 1e-6 of its threshold). */
+typedef struct {
+  int32_t B, N, V, max_depth, logits_dtype, mode;
+  double temperature;
+  const int32_t* parents;
+  const int32_t* tokens;
+  const void* target_logits;
+  const void* draft_logits;
+  const float* u_accept;
+  const float* u_sample;
+  int32_t *accept_len, *accept_rows, *out_tokens, *num_out, *stop_row, *status, *flagged;
+} orc_accept_args;
+int orc_accept(const orc_accept_args* a);
+
+/* Commit of the accepted branch's KV ([EP] sec. 2, "Gestion de Cache KV
+ * Ramificada").  commit_mode 0 = path-index (rows accept_rows[b][k]),
+ * 1 = length (rows 1..A, chains only).  elem_bytes 2 or 4.  The caches are
+ * updated in place; new_len [B], committed_slots [B,max_depth], status [B]. */
+typedef struct {
+  int32_t B, N, Hkv, D, elem_bytes, max_depth, commit_mode;
+  int32_t paged, Lcap, block_size, max_blocks, num_blocks;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* block_table;
+  const void* k_tree;
+  const void* v_tree;
+  const int32_t* prefix_len;
+  const int32_t* accept_len;
+  const int32_t* accept_rows;
+  int32_t *new_len, *committed_slots, *status;
+} orc_commit_args;
+int orc_kv_commit(const orc_commit_args* a);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
