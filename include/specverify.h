@@ -1,0 +1,254 @@
+/*
+ * libspecverify -- the verification step of tree speculative decoding on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One verify step is four calls, issued in this order on one HIP stream:
+ *
+ *   sv_build_tree_mask  parent array -> ancestor bitsets, depths, path rows
+ *   sv_tree_attention   ancestor-masked GQA attention of the draft-tree query
+ *                       tokens over a contiguous or paged KV prefix
+ *   sv_accept           greedy argmax matching, or full-distribution rejection
+ *                       sampling with the residual normalize(max(0, p - q)),
+ *                       plus the bonus token
+ *   sv_kv_commit        copy the accepted branch's KV rows into the cache
+ *
+ * Sources (web pages, cited by title and section):
+ *  [EP]  "EAGLE-Pangu: Accelerator-Safe Tree Speculative Decoding on Ascend
+ *        NPUs" (gist.science summary), technical summary sec. 2 Metodologia:
+ *        branchable KV cache, commit by length or by path indices; shifted
+ *        indexing with a dummy root row 0 in place of the -1 sentinel;
+ *        ancestor index tables; range, acyclicity and depth checks before the
+ *        fused kernels; tree attention mask (a token sees itself and its
+ *        ancestors only).
+ *  [PX]  "Accelerating Sonar Through Speculation" (Perplexity), sections
+ *        "Decodificacion Especulativa", "Objetivo-Borrador", "EAGLE",
+ *        "Inferencia con Decodificacion Especulativa": n drafted tokens give
+ *        up to n+1 emitted tokens; the longest acceptable sequence is kept;
+ *        acceptance compares full draft and target distributions; the target
+ *        logits after the accepted sequence give a bonus token; the accepted
+ *        count forces a GPU->CPU sync unless device work consumes it.
+ *  [SSD] "Speculative Speculative Decoding" (gist.science summary), sec. 3B
+ *        (residual probability mass), sec. 5 (exact output distribution).
+ *
+ * Conventions shared by every call
+ *  - Tree node i in [0, N) owns row r = i + 1.  Row 0 is the root: the last
+ *    committed token, whose KV is already in the prefix and whose target and
+ *    draft logits are row 0 of the logits tensors ([EP] sec. 2 dummy row).
+ *    parents[i] = -1 means "child of the root"; no call ever forms a negative
+ *    index from it.
+ *  - All pointers are device pointers unless stated; the caller owns every
+ *    buffer.  The library allocates nothing, never synchronises the stream
+ *    and never copies to the host: calls only enqueue kernels on `stream`
+ *    (a hipStream_t, or NULL for the null stream).  It is stateless and
+ *    reentrant.
+ *  - Argument and shape problems are returned synchronously as a non-zero
+ *    sv_status and nothing is enqueued.  Data-dependent problems (a malformed
+ *    tree, a token id out of range, a ghost block table entry, capacity) are
+ *    written as per-sequence codes into a caller-provided device `status`
+ *    array; kernels then clamp the offending index to the ghost row / slot 0
+ *    and never dereference a negative or out-of-range index.
+ *  - Limits: 1 <= N <= 256, 1 <= max_depth <= 16, head_dim in {64, 128},
+ *    Hq % Hkv == 0 with Hq/Hkv <= 16, block_size 16, V >= 1.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t sv_status;
+#define SV_OK 0
+#define SV_ERR_INVALID_ARGUMENT 1
+#define SV_ERR_UNSUPPORTED 2
+#define SV_ERR_HIP 4
+
+/* element types */
+#define SV_F32 0
+#define SV_BF16 1
+
+/* acceptance modes */
+#define SV_GREEDY 0
+#define SV_STOCHASTIC 1
+
+/* commit modes ([EP] sec. 2: length-based or path-index-based commit) */
+#define SV_COMMIT_PATH 0
+#define SV_COMMIT_LENGTH 1
+
+/* per-sequence device status codes */
+#define SV_SEQ_OK 0
+#define SV_SEQ_PARENT_RANGE 1   /* a parent index outside [-1, N), or accept data out of range */
+#define SV_SEQ_CYCLE 2          /* a node reaches itself by following parents */
+#define SV_SEQ_DEPTH 3          /* a root path longer than max_depth */
+#define SV_SEQ_TOKEN 4          /* a draft token id outside [0, V) */
+#define SV_SEQ_BLOCK 5          /* a needed block-table entry is 0 (ghost) or outside the pool */
+#define SV_SEQ_CAPACITY 6       /* prefix_len (+ accepted rows) exceeds the cache capacity */
+
+/*
+ * sv_build_tree_mask -- tree tensorisation ([EP] sec. 2, "Semantica de
+ * Tensores de Arbol Segura").
+ *   parents   [B, N] int32, values in {-1} U [0, N); any order (need not be
+ *             topologically sorted).
+ *   anc_bits  [B, N, W] uint64, W = ceil(N/64): bit j of node i is set iff j
+ *             lies on the root path of i (i itself included) -- the tree
+ *             attention mask of [EP] sec. 2.
+ *   depth     [B, N] int32: number of nodes on the root path of i (1 for a
+ *             child of the root); 0 marks an invalid node.
+ *   path_rows [B, N+1, max_depth] int32 or NULL: row r = i+1 lists the rows of
+ *             the root path of node i, root-most first, padded with the ghost
+ *             row 0; row 0 is all 0 (ancestor index tables, [EP] sec. 2).
+ *   status    [B] int32: 0, or the smallest code among the sequence's nodes.
+ * Checks per node while walking up (in this order): parent in [-1, N) (code
+ * 1), parent not already on the walk (code 2), path length <= max_depth
+ * (code 3).  An invalid node gets anc_bits = {i}, depth 0 and an all-ghost
+ * path row; valid nodes are unaffected by invalid ones.
+ */
+sv_status sv_build_tree_mask(const int32_t* parents, int32_t B, int32_t N, int32_t max_depth,
+                             uint64_t* anc_bits, int32_t* depth, int32_t* path_rows, int32_t* status,
+                             void* stream);
+
+/*
+ * sv_tree_attention -- ancestor-masked GQA attention of the tree's query
+ * tokens ([EP] sec. 2, "Ejecucion del Maestro con Mascara de Arbol
+ * Fusionada").  For batch b, query head h, KV head g = h / (Hq/Hkv), node i:
+ *     keys   = prefix positions j in [0, prefix_len[b])  (cache)
+ *              then tree nodes t with bit t of anc_bits[b,i] (k_tree row t+1)
+ *     out[b,i,h,:] = sum_j softmax_j(scale * q.k_j) v_j
+ * Layouts (element type `dtype` for q, caches, tree KV and out):
+ *     q        [B, N, Hq, D]
+ *     k_cache, v_cache: contiguous [B, Hkv, Lcap, D], or paged
+ *              [num_blocks, Hkv, block_size, D] with block_table [B, max_blocks]
+ *              (block 0 is the ghost block and is never a valid entry)
+ *     k_tree, v_tree [B, Hkv, N+1, D]: the tree tokens' K/V, row 0 = ghost
+ *              (never read as a key)
+ *     anc_bits [B, N, ceil(N/64)] from sv_build_tree_mask
+ *     prefix_len [B] int32 (device)
+ *     out      [B, N, Hq, D]
+ * Scale: the caller passes it (1/sqrt(D) for standard attention); no rotary
+ * embedding, soft-capping or bias is applied inside.
+ * workspace: device scratch of at least sv_tree_attention_workspace(args)
+ * bytes (may be 0), 256-byte aligned.
+ * status (nullable) [B]: 5 if a needed block-table entry is 0 or >=
+ * num_blocks (read as the ghost block), 6 if prefix_len is outside
+ * [0, capacity] (clamped).
+ */
+typedef struct sv_attn_args {
+  int32_t B, N, Hq, Hkv, D, dtype;
+  float scale;
+  int32_t paged;                  /* 0 contiguous, 1 paged */
+  int32_t Lcap;                   /* contiguous capacity per sequence */
+  int32_t block_size, max_blocks, num_blocks;  /* paged geometry */
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const void* k_tree;
+  const void* v_tree;
+  const int32_t* block_table;
+  const int32_t* prefix_len;
+  const uint64_t* anc_bits;
+  void* out;
+  void* workspace;
+  size_t workspace_bytes;
+  int32_t* status;
+} sv_attn_args;
+size_t sv_tree_attention_workspace(const sv_attn_args* args);
+sv_status sv_tree_attention(const sv_attn_args* args, void* stream);
+
+/*
+ * sv_accept -- speculative acceptance and the bonus token ([PX], [SSD]).
+ * Inputs:
+ *   parents [B,N], tokens [B,N] int32 (draft token of node i), anc_bits and
+ *   depth from sv_build_tree_mask; target_logits [B, N+1, V] (row r = the
+ *   target's next-token logits after row r's token, row 0 = the root);
+ *   draft_logits [B, N+1, V] (stochastic only; row r = the drafter's logits
+ *   its children were drawn from); u_accept, u_sample [B, N+1] float
+ *   uniforms in [0,1) (stochastic only).
+ * A node is usable when its depth is > 0 and its token lies in [0, V).
+ * Greedy (mode 0): a_r = argmax of target row r over the stored values, the
+ *   lowest id on ties.  Node i matches when tokens[i] == a_{parents[i]+1};
+ *   it is accepted when every node of its root path is usable and matches.
+ *   The stop node is the deepest accepted node (lowest index on ties), or
+ *   the root when none; A = its depth; bonus = a_{stop row}.
+ * Stochastic (mode 1), p_r = softmax(target row r / T), q_r = softmax(draft
+ *   row r / T), exponentials in fp32 and sums over V in fp64:
+ *   start at row 0 with p_cur = p_0; test the usable children c of the
+ *   current row in ascending index, with x = tokens[c]: accept iff
+ *   u_accept[c+1] < p_cur(x)/q_r(x) (q_r(x) = 0 accepts); on accept move to
+ *   row c+1 with p_cur = p_{c+1}; on reject replace p_cur by
+ *   normalize(max(0, p_cur - q_r)).  When no child is accepted the walk stops
+ *   at the current row and the bonus is the smallest v whose ascending-id
+ *   cumulative mass of p_cur exceeds u_sample[stop row] times its total.
+ * Outputs (device, int32): accept_len [B] (A), accept_rows [B, max_depth]
+ *   (rows of the accepted path, root-most first, ghost-0 padded), out_tokens
+ *   [B, max_depth+1] (accepted tokens then the bonus, 0 padded), num_out [B]
+ *   (A+1), stop_row [B], status [B] (4 if some token id is out of range).
+ * workspace: at least sv_accept_workspace(args) bytes, 256-byte aligned.
+ */
+typedef struct sv_accept_args {
+  int32_t B, N, V, max_depth, logits_dtype, mode;
+  float temperature;
+  const int32_t* parents;
+  const int32_t* tokens;
+  const uint64_t* anc_bits;
+  const int32_t* depth;
+  const void* target_logits;
+  const void* draft_logits;
+  const float* u_accept;
+  const float* u_sample;
+  int32_t* accept_len;
+  int32_t* accept_rows;
+  int32_t* out_tokens;
+  int32_t* num_out;
+  int32_t* stop_row;
+  int32_t* status;
+  void* workspace;
+  size_t workspace_bytes;
+} sv_accept_args;
+size_t sv_accept_workspace(const sv_accept_args* args);
+sv_status sv_accept(const sv_accept_args* args, void* stream);
+
+/*
+ * sv_kv_commit -- append the accepted branch's KV to the cache ([EP] sec. 2,
+ * "Gestion de Cache KV Ramificada").  For sequence b with L = prefix_len[b]
+ * and A = accept_len[b], for k < A the tree row src_k (accept_rows[b,k] in
+ * path mode, k+1 in length mode) of k_tree / v_tree is copied, for every KV
+ * head, to position L + k: contiguous slot L + k of [B, Hkv, Lcap, D], or
+ * paged slot block_table[b][(L+k)/bs]*bs + (L+k)%bs of [num_blocks, Hkv, bs,
+ * D].  committed_slots [B, max_depth] receives the slots (0 for k >= A) and
+ * new_len [B] = L + A (new_len may alias prefix_len).
+ * Before any write, every k < A is checked in order; the first failure sets
+ * status[b] (1: A outside [0, max_depth] or a source row outside [1, N];
+ * 5: ghost or out-of-pool block; 6: beyond capacity) and then nothing of that
+ * sequence is written: new_len = L, committed_slots all 0.
+ * Element size follows dtype (SV_F32 4 bytes, SV_BF16 2 bytes).
+ */
+typedef struct sv_commit_args {
+  int32_t B, N, Hkv, D, dtype, max_depth, commit_mode;
+  int32_t paged, Lcap, block_size, max_blocks, num_blocks;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* block_table;
+  const void* k_tree;
+  const void* v_tree;
+  const int32_t* prefix_len;
+  const int32_t* accept_len;
+  const int32_t* accept_rows;
+  int32_t* new_len;
+  int32_t* committed_slots;
+  int32_t* status;
+} sv_commit_args;
+sv_status sv_kv_commit(const sv_commit_args* args, void* stream);
+
+/* Human-readable name of an sv_status (static string). */
+const char* sv_status_string(sv_status s);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t sv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

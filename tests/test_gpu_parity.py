@@ -1,0 +1,235 @@
+"""GPU (HIP path through the C ABI) vs CPU oracle parity, stage by stage and end to end.
+
+Bar: bit-exact for masks, depths, path rows, statuses, accepted lengths, rows,
+tokens, stop rows, committed slots, new lengths and committed cache bytes;
+attention within max-abs 1e-4 (fp32) or 2e-2 (bf16) plus relative-L2 <= 1e-2
+for bf16; stochastic draws the oracle flags (within 1e-6 of a threshold) are
+excluded from the exact comparison and counted.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import (attention_check_rejects_zero, check_attention, compare_accept, require_gpu, run_step,
+                      sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+# shrunk variants the oracle finishes in seconds; ragged prefix lengths and tails on purpose
+SMALL = {
+    1: dict(),
+    2: dict(L=333, V=3001),
+    3: dict(B=5, L=(40, 400), V=2500, N=32),
+    4: dict(B=6, L=161, V=2999),
+    5: dict(B=2, L=290, V=1500),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _mask_ok(w, r):
+    anc, depth, prow, st = oracle.build_tree_mask(w.parents, w.max_depth)
+    assert np.array_equal(r["anc"], anc)
+    assert np.array_equal(r["depth"], depth)
+    assert np.array_equal(r["path_rows"], prow)
+    assert np.array_equal(r["mstatus"], st)
+
+
+def _commit_ok(w, r):
+    kc, vc = w.k_cache.copy(), w.v_cache.copy()
+    ref = oracle.kv_commit(w, r["acc"]["accept_len"], r["acc"]["accept_rows"], kc, vc)
+    for k in ("new_len", "committed_slots", "status"):
+        assert np.array_equal(r["commit"][k], ref[k]), k
+    assert np.array_equal(r["k_cache"], kc)
+    assert np.array_equal(r["v_cache"], vc)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_full_step_small(cfg):
+    """All four stages on shrunk workloads, every output compared."""
+    w = W.config(cfg, **SMALL[cfg])
+    r = run_step(w)
+    _mask_ok(w, r)
+    ref = oracle.tree_attention(w)
+    err, rel = check_attention(r["out"], ref, w.dtype, f"config {cfg}")
+    print(f"  attention max-abs {err:.2e} rel-L2 {rel:.2e}")
+    acc = oracle.accept(w)
+    nflag = compare_accept(r["acc"], acc)
+    print(f"  accept_len {r['acc']['accept_len'].tolist()} flagged {nflag}")
+    _commit_ok(w, r)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_full_step_full_size(cfg):
+    """All four stages at the full workload sizes; attention on a seeded sample of rows."""
+    w = W.config(cfg)
+    r = run_step(w)
+    _mask_ok(w, r)
+    n = {1: 10**9, 2: 10**9, 3: 160, 4: 300, 5: 96}[cfg]
+    if n >= w.B * w.N * w.Hq:
+        ref = oracle.tree_attention(w)
+        got = r["out"]
+    else:
+        sel = sample_rows(w, n, seed=cfg)
+        ref = oracle.tree_attention(w, sel=sel)
+        got = r["out"].reshape(-1, w.D)[sel]
+    err, rel = check_attention(got, ref, w.dtype, f"config {cfg} full")
+    assert attention_check_rejects_zero(ref) or w.dtype == "f32"
+    print(f"  attention max-abs {err:.2e} rel-L2 {rel:.2e} on {got.shape[0]} rows")
+    acc = oracle.accept(w)
+    nflag = compare_accept(r["acc"], acc)
+    print(f"  mean accept_len {r['acc']['accept_len'].mean():.3f} flagged {nflag}/{w.B}")
+    assert nflag <= max(1, w.B // 10)
+    _commit_ok(w, r)
+
+
+@pytest.mark.parametrize("k", range(5))
+def test_greedy_planted_chain(k):
+    w = W.config(1, plant=k)
+    r = run_step(w, ("mask", "accept"))
+    acc = oracle.accept(w)
+    compare_accept(r["acc"], acc, allow_flagged=False)
+    assert r["acc"]["accept_len"][0] == k
+
+
+def test_mask_fuzz_and_shapes():
+    """Random, deep, wide and malformed parent arrays: bit-exact tensorisation and status."""
+    cases = [
+        W.randint(5, 1, 64 * 40, -3, 42).astype(np.int32).reshape(64, 40),
+        np.stack([W.tree_random_recursive(s, 256, 16) for s in range(8)]),
+        np.stack([W.tree_chain(16)] * 3),
+        np.stack([W.tree_star(256)] * 2),
+        np.stack([W.tree_outcome(s) for s in range(4)]),
+    ]
+    for par in cases:
+        B, N = par.shape
+        for maxd in (1, 6, 16):
+            w = W.Workload(name="mask", B=B, N=N, Hq=1, Hkv=1, D=64, V=1, dtype="f32", mode="greedy",
+                           temperature=1.0, max_depth=maxd, paged=False, Lcap=0, block_size=16, max_blocks=0,
+                           num_blocks=0, parents=par, tokens=np.zeros_like(par), prefix_len=np.zeros(B, np.int32),
+                           q=np.zeros((1,), np.float32), k_cache=np.zeros((1,), np.float32),
+                           v_cache=np.zeros((1,), np.float32), k_tree=np.zeros((1,), np.float32),
+                           v_tree=np.zeros((1,), np.float32), block_table=None, target_logits=np.zeros((1,), np.float32),
+                           draft_logits=None, u_accept=None, u_sample=None)
+            import torch
+            import tree_verification_sv_amd as sv
+            print(f"[gpu] mask fuzz B={B} N={N} max_depth={maxd}", flush=True)
+            out = sv.sv_build_tree_mask(torch.from_numpy(np.ascontiguousarray(par)).cuda(), maxd)
+            torch.cuda.synchronize()
+            anc, depth, prow, st = oracle.build_tree_mask(par, maxd)
+            assert np.array_equal(out["anc_bits"].cpu().numpy().view(np.uint64), anc)
+            assert np.array_equal(out["depth"].cpu().numpy(), depth)
+            assert np.array_equal(out["path_rows"].cpu().numpy(), prow)
+            assert np.array_equal(out["status"].cpu().numpy(), st)
+
+
+def test_leak_free_on_gpu():
+    """Perturbing K/V of non-ancestor tree rows by +-1e3 leaves every output bit unchanged."""
+    from _util import root_paths
+    w = W.config(2, L=40, V=64)
+    r0 = run_step(w, ("mask", "attention"))
+    paths = root_paths(w.parents[0])
+    node = max(paths, key=lambda n: len(paths[n]))
+    anc = set(paths[node])
+    for t in range(w.N):
+        if t not in anc:
+            w.k_tree[0, :, t + 1] = W.f32_to_bf16(W.bf16_to_f32(w.k_tree[0, :, t + 1]) + 1e3)
+            w.v_tree[0, :, t + 1] = W.f32_to_bf16(W.bf16_to_f32(w.v_tree[0, :, t + 1]) - 1e3)
+    r1 = run_step(w, ("mask", "attention"))
+    assert np.array_equal(r0["out"][0, node], r1["out"][0, node])
+
+
+@pytest.mark.parametrize("variant", ["peaky", "short_prefix", "empty_prefix", "d64", "gqa1", "n256"])
+def test_attention_variants(variant):
+    """Non-vacuity and edge shapes: sharp softmax, tree-dominated keys, L = 0, D = 64, G = 1, N = 256."""
+    if variant == "peaky":
+        w = W.config(2, L=700, V=64)
+        w.q = W.f32_to_bf16(W.bf16_to_f32(w.q) * 8.0)
+    elif variant == "short_prefix":
+        w = W.config(2, L=37, V=64)
+    elif variant == "empty_prefix":
+        w = W.config(4, B=3, L=0, V=64)
+    elif variant == "d64":
+        par = np.stack([W.tree_eagle_static(3, n_nodes=20)] * 2)
+        w = W.build_workload("d64", 2, 20, 8, 2, 64, 50, "bf16", "greedy", par, np.array([100, 257]), 6, seed=3,
+                             token_rule="uniform", need_draft=False)
+    elif variant == "gqa1":
+        par = np.stack([W.tree_random_recursive(4, 24, 6)] * 3)
+        w = W.build_workload("gqa1", 3, 24, 4, 4, 128, 50, "bf16", "greedy", par, np.array([65, 1, 300]), 6,
+                             seed=4, token_rule="uniform", need_draft=False)
+    else:
+        par = np.stack([W.tree_random_recursive(7, 256, 16)])
+        w = W.build_workload("n256", 1, 256, 32, 8, 128, 50, "bf16", "greedy", par, np.array([200]), 16, seed=7,
+                             token_rule="uniform", need_draft=False)
+    r = run_step(w, ("mask", "attention"))
+    ref = oracle.tree_attention(w)
+    err, rel = check_attention(r["out"], ref, w.dtype, variant)
+    assert attention_check_rejects_zero(ref)
+    print(f"  {variant}: max-abs {err:.2e} rel-L2 {rel:.2e} |ref|max {np.abs(ref).max():.3f}")
+
+
+def test_attention_fp32_paths():
+    """fp32 inputs (generic kernel) on a ragged tree with a paged cache."""
+    w = W.config(3, B=3, L=(10, 100), V=64, N=12)
+    for name in ("q", "k_cache", "v_cache", "k_tree", "v_tree"):
+        setattr(w, name, np.ascontiguousarray(W.bf16_to_f32(getattr(w, name))))
+    w.dtype = "f32"
+    r = run_step(w, ("mask", "attention"))
+    check_attention(r["out"], oracle.tree_attention(w), "f32", "fp32 paged")
+
+
+def test_invalid_inputs_report_status():
+    """Malformed trees, out-of-range tokens, ghost blocks and overlong prefixes: codes, no fault."""
+    w = W.config(3, B=4, L=(30, 90), V=300, N=16)
+    w.parents[0, 5] = 99            # parent out of range
+    w.parents[1, 3] = 3             # self-parent cycle
+    w.tokens[2, 0] = 300            # token id == V
+    w.block_table[3, 0] = 0         # ghost block in a needed position
+    r = run_step(w)
+    _mask_ok(w, r)
+    assert r["mstatus"][0] == 1 and r["mstatus"][1] == 2
+    assert r["acc"]["status"][2] == 4
+    assert r["astatus"][3] == 5
+    acc = oracle.accept(w)
+    compare_accept(r["acc"], acc, allow_flagged=False)
+    _commit_ok(w, r)
+    assert np.isfinite(r["out"]).all()
+
+
+@pytest.mark.parametrize("shape", ["chain1", "chain3", "siblings3"])
+def test_chi_square_gpu(shape):
+    """Vocab 16, 10^6 trials on the GPU: the first emitted token follows p_root."""
+    from scipy import stats
+    import torch
+    from tree_verification_sv_amd.step import StepInputs, VerifyStep
+    V = 16
+    parents = {"chain1": [-1], "chain3": [-1, 0, 1], "siblings3": [-1, -1, -1]}[shape]
+    N = len(parents)
+    p_rows = W.normal(31, 1, (N + 1, V), "f32", 1.5)
+    q_rows = W.normal(31, 2, (N + 1, V), "f32", 1.5)
+    n = 250_000
+    counts = np.zeros(V, np.int64)
+    for s in range(4):
+        par = np.tile(np.asarray(parents, np.int32), (n, 1))
+        prow = (np.arange(n)[:, None] * (N + 1) + par + 1).reshape(-1)
+        drf = np.ascontiguousarray(np.broadcast_to(q_rows, (n, N + 1, V)))
+        tgt = np.ascontiguousarray(np.broadcast_to(p_rows, (n, N + 1, V)))
+        toks = W.draft_tokens(700 + s, 2, drf.reshape(-1, V), prow, 1.0).reshape(n, N)
+        ua = W.uniform24(700 + s, 11, (n, N + 1))
+        us = W.uniform24(700 + s, 12, (n, N + 1))
+        import tree_verification_sv_amd as sv
+        d = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+        print(f"[gpu] chi-square {shape} batch {s}", flush=True)
+        m = sv.sv_build_tree_mask(d(par), N)
+        acc = sv.sv_accept(d(par), d(toks), m["anc_bits"], m["depth"], d(tgt), N, mode="stochastic",
+                           draft_logits=d(drf), u_accept=d(ua), u_sample=d(us), temperature=1.0)
+        torch.cuda.synchronize()
+        counts += np.bincount(acc["out_tokens"][:, 0].cpu().numpy(), minlength=V)
+    p0 = np.exp(p_rows[0].astype(np.float64) - p_rows[0].max())
+    p0 /= p0.sum()
+    chi = stats.chisquare(counts, p0 * counts.sum())
+    assert chi.pvalue > 0.01, chi

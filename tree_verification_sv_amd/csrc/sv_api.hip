@@ -1,0 +1,14 @@
+// Small host-side helpers of the C ABI.
+#include "sv_common.h"
+
+extern "C" const char* sv_status_string(sv_status s) {
+  switch (s) {
+    case SV_OK: return "ok";
+    case SV_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case SV_ERR_UNSUPPORTED: return "unsupported shape or type";
+    case SV_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int32_t sv_version(void) { return 100; }

@@ -1,0 +1,100 @@
+"""One verification step: the four library calls in dependency order on one stream.
+
+``VerifyStep`` owns the output and workspace buffers (allocated once through
+torch), so repeated ``run()`` calls allocate nothing and issue exactly four
+C-ABI calls: sv_build_tree_mask -> sv_tree_attention -> sv_accept ->
+sv_kv_commit.  Nothing here computes; it marshals arguments.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+from . import (SV_COMMIT_PATH, SV_STOCHASTIC, _check, _stream, accept_args, accept_outputs, attn_args, commit_args,
+               lib, sv_accept_workspace, sv_tree_attention_workspace)
+
+
+@dataclass
+class StepInputs:
+    """Device tensors of one verification batch (see include/specverify.h for layouts)."""
+    parents: object
+    tokens: object
+    q: object
+    k_cache: object
+    v_cache: object
+    k_tree: object
+    v_tree: object
+    prefix_len: object
+    target_logits: object
+    max_depth: int
+    mode: str = "greedy"
+    temperature: float = 1.0
+    draft_logits: Optional[object] = None
+    u_accept: Optional[object] = None
+    u_sample: Optional[object] = None
+    block_table: Optional[object] = None
+    paged: bool = False
+    num_blocks: int = 0
+    scale: Optional[float] = None
+    commit_mode: int = SV_COMMIT_PATH
+
+
+class VerifyStep:
+    def __init__(self, x: StepInputs):
+        import torch
+        self.x = x
+        B, N = x.parents.shape
+        dev = x.parents.device
+        W = (N + 63) // 64
+        Dm = x.max_depth
+        self.B, self.N = B, N
+        self.mask = dict(anc_bits=torch.empty((B, N, W), dtype=torch.int64, device=dev),
+                         depth=torch.empty((B, N), dtype=torch.int32, device=dev),
+                         path_rows=torch.empty((B, N + 1, Dm), dtype=torch.int32, device=dev),
+                         status=torch.empty((B,), dtype=torch.int32, device=dev))
+        self.out = torch.empty_like(x.q)
+        self.attn_status = torch.empty((B,), dtype=torch.int32, device=dev)
+        self.acc = accept_outputs(B, Dm, dev)
+        self.commit = dict(new_len=torch.empty(B, dtype=torch.int32, device=dev),
+                           committed_slots=torch.empty((B, Dm), dtype=torch.int32, device=dev),
+                           status=torch.empty(B, dtype=torch.int32, device=dev))
+        # argument blocks are built once; pointers stay valid for the tensors' lifetime
+        self._attn = attn_args(x.q, x.k_cache, x.v_cache, x.k_tree, x.v_tree, self.mask["anc_bits"], x.prefix_len,
+                               self.out, x.block_table, x.scale, x.paged, x.num_blocks, self.attn_status)
+        need = sv_tree_attention_workspace(self._attn)
+        self.attn_ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        self._attn.workspace = self.attn_ws.data_ptr() if need else None
+        self._attn.workspace_bytes = need
+        self._acc = accept_args(x.parents, x.tokens, self.mask["anc_bits"], self.mask["depth"], x.target_logits, Dm,
+                                x.mode, x.draft_logits, x.u_accept, x.u_sample, x.temperature, self.acc)
+        need = sv_accept_workspace(self._acc)
+        self.acc_ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        self._acc.workspace = self.acc_ws.data_ptr()
+        self._acc.workspace_bytes = need
+        self._com = commit_args(x.k_cache, x.v_cache, x.k_tree, x.v_tree, x.prefix_len, self.acc["accept_len"],
+                                self.acc["accept_rows"], Dm, self.commit["new_len"], self.commit["committed_slots"],
+                                self.commit["status"], x.block_table, x.paged, x.num_blocks, x.commit_mode)
+        self._L = lib()
+
+    # individual stages (same stream)
+    def build_mask(self, stream=None):
+        m = self.mask
+        _check(self._L.sv_build_tree_mask(self.x.parents.data_ptr(), self.B, self.N, self.x.max_depth,
+                                          m["anc_bits"].data_ptr(), m["depth"].data_ptr(), m["path_rows"].data_ptr(),
+                                          m["status"].data_ptr(), _stream(stream)), "sv_build_tree_mask")
+
+    def attention(self, stream=None):
+        _check(self._L.sv_tree_attention(ctypes.byref(self._attn), _stream(stream)), "sv_tree_attention")
+
+    def accept(self, stream=None):
+        _check(self._L.sv_accept(ctypes.byref(self._acc), _stream(stream)), "sv_accept")
+
+    def kv_commit(self, stream=None):
+        _check(self._L.sv_kv_commit(ctypes.byref(self._com), _stream(stream)), "sv_kv_commit")
+
+    def run(self, stream=None):
+        self.build_mask(stream)
+        self.attention(stream)
+        self.accept(stream)
+        self.kv_commit(stream)

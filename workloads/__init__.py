@@ -496,3 +496,35 @@ def config(cfg: int, seed: Optional[int] = None, **ov) -> Workload:
                               np.full(B, L), max_depth=10, seed=seed, logit_sigma=3.0,
                               target_from_draft_sigma=1.0, token_rule="sample")
     raise ValueError(cfg)
+
+
+# ------------------------------------------------- host -> device transfer
+def to_device(w: Workload, device="cuda:0"):
+    """Copy a workload's arrays to device tensors (bf16 bit patterns become torch.bfloat16)."""
+    import torch
+
+    def t(x, dt=None):
+        if x is None:
+            return None
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).to(device).view(torch.bfloat16)
+        if x.dtype == np.uint64:
+            return torch.from_numpy(x.view(np.int64)).to(device)
+        return torch.from_numpy(x).to(device)
+
+    return dict(parents=t(w.parents), tokens=t(w.tokens), q=t(w.q), k_cache=t(w.k_cache), v_cache=t(w.v_cache),
+                k_tree=t(w.k_tree), v_tree=t(w.v_tree), prefix_len=t(w.prefix_len.astype(np.int32)),
+                target_logits=t(w.target_logits), draft_logits=t(w.draft_logits), u_accept=t(w.u_accept),
+                u_sample=t(w.u_sample), block_table=t(w.block_table))
+
+
+def step_inputs(w: Workload, dev: dict):
+    """StepInputs for the library's VerifyStep from a workload and its device copy."""
+    from tree_verification_sv_amd.step import StepInputs
+    return StepInputs(parents=dev["parents"], tokens=dev["tokens"], q=dev["q"], k_cache=dev["k_cache"],
+                      v_cache=dev["v_cache"], k_tree=dev["k_tree"], v_tree=dev["v_tree"],
+                      prefix_len=dev["prefix_len"], target_logits=dev["target_logits"], max_depth=w.max_depth,
+                      mode=w.mode, temperature=w.temperature, draft_logits=dev["draft_logits"],
+                      u_accept=dev["u_accept"], u_sample=dev["u_sample"], block_table=dev["block_table"],
+                      paged=w.paged, num_blocks=w.num_blocks, scale=w.scale)
