@@ -1,0 +1,243 @@
+"""Benchmark of one tree-verification step on one MI355X.
+
+A step is the whole hot path on one batch: sv_build_tree_mask ->
+sv_tree_attention -> sv_accept -> sv_kv_commit, issued on one stream.  The
+default workload is the EAGLE-style static tree at the Llama-3-8B attention
+shape (batch 1, 32 query / 8 KV heads, head_dim 128, 4096-token bf16 prefix,
+60-node tree of depth 6, vocab 128256, stochastic acceptance at T = 1).
+
+Inputs are resident in HBM before timing starts.  R independent input
+instances are cycled so that the working set (R x step bytes) exceeds twice
+the 256 MB Infinity Cache and every step reads HBM, not a warm cache.
+
+Prints one JSON line: value = verified tree tokens/s (B*N / step time), with
+the roofline of the dominant kernel measured live with HIP events on the
+launch stream, and the CPU oracle timed on a bounded sample on the host.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 * 2**20
+
+
+def algorithmic_bytes(w, acc):
+    """Bytes each stage must move at minimum (per step), from the workload and its accept results."""
+    e = 2 if w.dtype == "bf16" else 4
+    el = 2 if w.target_logits.dtype == np.uint16 else 4
+    B, N, Hq, Hkv, D, V = w.B, w.N, w.Hq, w.Hkv, w.D, w.V
+    W = (N + 63) // 64
+    L = w.prefix_len.astype(np.int64)
+    attn = int(L.sum()) * Hkv * D * 2 * e + B * N * Hkv * D * 2 * e + 2 * B * N * Hq * D * e + B * N * W * 8
+    if w.paged:
+        attn += int(((L + w.block_size - 1) // w.block_size).sum()) * 4
+    n_t = 2 if w.mode == "stochastic" else 1
+    rows = 0
+    for b in range(B):
+        par = w.parents[b]
+        needed = {0} | set((par[par >= 0] + 1).tolist())
+        stop = int(acc["stop_row"][b])
+        rows += len(needed) * n_t + (0 if stop in needed else 1)
+    accept = rows * V * el
+    commit = int(acc["accept_len"].sum()) * Hkv * D * 2 * e * 2
+    mask = 4 * B * N + B * N * (8 * W + 4 + 4 * w.max_depth)
+    return dict(mask=mask, attention=attn, accept=accept, commit=commit,
+                total=mask + attn + accept + commit)
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_src_hash):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it still matches the source."""
+    path = os.path.join(ROOT, "profiles", "attention_pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != kernel_src_hash:
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, budget_s=10.0, max_steps=8):
+    """The CPU oracle as it stands, one host thread, on whole steps of the same workload.
+
+    Steps on independently seeded instances run until about ``budget_s`` seconds
+    of oracle work (at most ``max_steps``); input generation is not timed.
+    """
+    import oracle
+    import workloads as W
+    dt, steps, tokens = 0.0, 0, 0
+    while steps < max_steps and (dt < budget_s or steps == 0):
+        w = W.config(cfg, seed=cfg * 1000 + steps)
+        t0 = time.perf_counter()
+        oracle.build_tree_mask(w.parents, w.max_depth)
+        oracle.tree_attention(w)
+        acc = oracle.accept(w)
+        kc, vc = w.k_cache.copy(), w.v_cache.copy()
+        oracle.kv_commit(w, acc["accept_len"], acc["accept_rows"], kc, vc)
+        dt += time.perf_counter() - t0
+        steps += 1
+        tokens += w.B * w.N
+    return dict(value=round(tokens / dt, 3), unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{steps} full verification steps of the {w.name} workload (B={w.B}, N={w.N}, "
+                       f"L={int(w.prefix_len[0])}, V={w.V}): mask, fp64 attention of every query row, "
+                       f"{w.mode} acceptance, commit; {dt:.1f} s on one host thread")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--instances", type=int, default=0, help="input instances cycled (0: enough to defeat the MALL)")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU: --gpus {args.gpus} is not supported "
+              f"(sequences and KV heads shard with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    from tree_verification_sv_amd.step import VerifyStep
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    w0 = W.config(args.config)
+    # bytes one instance touches: the prefix K/V it reads plus its logits rows
+    step_bytes_est = w0.target_logits.nbytes * 2 + int(w0.prefix_len.sum()) * w0.Hkv * w0.D * 2 * (2 if w0.dtype == "bf16" else 4)
+    R = args.instances or max(1, min(32, int(np.ceil(2 * MALL_BYTES / max(step_bytes_est, 1)))))
+    print(f"[bench] workload {w0.name} B={w0.B} N={w0.N} L={int(w0.prefix_len.max())} V={w0.V} "
+          f"instances={R} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
+    ws = [w0] + [W.config(args.config, seed=args.config * 1000 + r) for r in range(1, R)]
+    devs = [W.to_device(w, dev) for w in ws]
+    steps = [VerifyStep(W.step_inputs(w, d)) for w, d in zip(ws, devs)]
+    stream = torch.cuda.current_stream()
+
+    for i in range(args.warmup):
+        steps[i % R].run()
+    torch.cuda.synchronize()
+    accs = [{k: v.cpu().numpy() for k, v in s.acc.items()} for s in steps]
+    byts = [algorithmic_bytes(w, a) for w, a in zip(ws, accs)]
+
+    use_graph = not args.no_graph
+    graph = None
+    if use_graph:
+        try:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for s in steps:
+                    s.run()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for s in steps:
+                    s.run()
+            torch.cuda.synchronize()
+            for _ in range(2):
+                graph.replay()
+            torch.cuda.synchronize()
+        except Exception as ex:  # capture not available: fall back to eager launches
+            print(f"[bench] graph capture failed ({ex}); timing eager launches", file=sys.stderr)
+            graph = None
+            use_graph = False
+
+    # ---- timed region: exactly K steps
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    if graph is not None:
+        reps = K // R
+        for _ in range(reps):
+            graph.replay()
+        for i in range(K - reps * R):
+            steps[i].run()
+    else:
+        for i in range(K):
+            steps[i % R].run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / K
+
+    # ---- per-stage durations, each stage launched alone K times on the same stream
+    stage_ms = {}
+    for name in ("build_mask", "attention", "accept", "kv_commit"):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(K):
+            getattr(steps[i % R], name)()
+        b.record(stream)
+        torch.cuda.synchronize()
+        stage_ms[name] = a.elapsed_time(b) / K
+
+    mean_bytes = {k: float(np.mean([bb[k] for bb in byts])) for k in byts[0]}
+    B, N = w0.B, w0.N
+    value = B * N / (ms_step * 1e-3)
+    hbm_gbs = mean_bytes["total"] / (ms_step * 1e-3) / 1e9
+    # dominant stage by measured time; the attention stage for this workload
+    dom = max(("attention", "accept"), key=lambda k: stage_ms[k])
+    dom_key = {"attention": "attention", "accept": "accept"}[dom]
+    achieved = mean_bytes[dom_key] / (stage_ms[dom] * 1e-3) / 1e9
+    src = {"attention": ["tree_verification_sv_amd/csrc/sv_attention.hip"],
+           "accept": ["tree_verification_sv_amd/csrc/sv_accept.hip"]}[dom]
+    traffic = load_traffic(source_hash(src)) if dom == "attention" else None
+    result = {
+        "metric": "verified tree tokens/sec + HBM GB/s (% peak), 8B-shape tree verify, 1 MI355X",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w0.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w0.name, "batch": B, "tree_nodes": N, "prefix_len": int(w0.prefix_len.max()),
+                   "q_heads": w0.Hq, "kv_heads": w0.Hkv, "head_dim": w0.D, "vocab": w0.V, "max_depth": w0.max_depth,
+                   "acceptance": w0.mode, "temperature": w0.temperature, "instances_cycled": R,
+                   "launch": "hip_graph" if use_graph else "eager"},
+        "accept_steps_per_s": round(B / (ms_step * 1e-3), 1),
+        "hbm_gbs": round(hbm_gbs, 1),
+        "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
+        "bytes_per_step": {k: int(v) for k, v in mean_bytes.items()},
+        "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "mean_accept_len": float(np.mean([a["accept_len"].mean() for a in accs])),
+        "emitted_tokens_per_s": round(float(np.mean([a["num_out"].sum() for a in accs])) / (ms_step * 1e-3), 1),
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on one step", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(args.config)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -159,7 +159,7 @@ def _alloc_workspace(nbytes, device):
     if nbytes == 0:
         return None
     # torch's caching allocator returns blocks aligned to at least 512 bytes
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
 # ------------------------------------------------------------ entry points

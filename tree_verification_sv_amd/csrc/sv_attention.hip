@@ -37,6 +37,7 @@ constexpr int TARGET_WG = 256;
 struct AttnPlan {
   int32_t G, M, QB, QT, qtiles, nsplit, chunk, ntt, W, cap;
   float cscale;  // scale * log2(e)
+  uint32_t pool_bytes;  // paged: bytes of one K (or V) pool, < 4 GiB
   float* opart;  // [units][nsplit][QT][D]
   float* mlpart; // [units][nsplit][QT][2]
 };
@@ -80,7 +81,8 @@ __global__ void __launch_bounds__(AT_THREADS, 1) k_attn_mfma(sv_attn_args a, Att
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM_BYTES];
 
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  // the wave index is uniform across the wave: keep tile bookkeeping in scalar registers
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lq = lane & 31;  // query column / row index inside a 32-block
   const int hf = lane >> 5;  // which half of the k dimension this lane feeds
 
@@ -150,75 +152,90 @@ __global__ void __launch_bounds__(AT_THREADS, 1) k_attn_mfma(sv_attn_args a, Att
   uint16_t* Ks = (uint16_t*)smem + w * LD::WAVE_ELEMS;
   uint16_t* VTs = Ks + LD::K_ELEMS;
 
-  // global -> register staging of one tile
+  // ---- global -> register staging of one 32-key tile through buffer loads.
+  // One buffer resource per source keeps the tile base in scalar registers;
+  // lanes only add precomputed 32-bit offsets.  Keys past the valid range are
+  // clamped onto the last valid key of the tile (finite data, masked out of
+  // the softmax), so no load ever leaves the tensor.
+  constexpr int CPR = D / 8;            // 16-byte chunks per row
+  constexpr int QPI = 64 / CPR;         // V key-quads covered by one load instruction
+  constexpr uint32_t ROWB = D * 2;      // bytes per K/V row
+  const int64_t plane = (int64_t)b * a.Hkv + g;
+  __amdgpu_buffer_rsrc_t rk, rv;
+  const __amdgpu_buffer_rsrc_t rkt = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(kt + (plane * (N + 1) + 1) * D), 0, (int)(N * ROWB), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rvt = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(vt + (plane * (N + 1) + 1) * D), 0, (int)(N * ROWB), 0x00020000);
+  if (a.paged) {
+    rk = __builtin_amdgcn_make_buffer_rsrc((void*)kc, 0, (int)p.pool_bytes, 0x00020000);
+    rv = __builtin_amdgcn_make_buffer_rsrc((void*)vc, 0, (int)p.pool_bytes, 0x00020000);
+  } else {
+    rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + plane * a.Lcap * D), 0, (int)(a.Lcap * ROWB), 0x00020000);
+    rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + plane * a.Lcap * D), 0, (int)(a.Lcap * ROWB), 0x00020000);
+  }
+  // lane-constant key index and chunk of every load
+  int kkey[KPIECES], kch[KPIECES];
+#pragma unroll
+  for (int it = 0; it < KPIECES; ++it) {
+    kkey[it] = (lane + 64 * it) / CPR;
+    kch[it] = (lane + 64 * it) % CPR;
+  }
+  const int vquad0 = lane % QPI, vch = lane / QPI;
+
   uint4 kreg[KPIECES];
   uint4 vreg[VITEMS][4];
   auto load_tile = [&](int tile) {
     const bool tree = tile >= ntp;
-    int64_t base_row_k[2];  // for prefix tiles in paged mode: the two 16-token blocks of the tile
-    const int j0 = tree ? 0 : k0 + tile * KT;
-    const int t0 = tree ? (tile - ntp) * KT : 0;
-    if (!tree && a.paged) {
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const int jb = j0 + hb * 16;
-        int id = 0;
-        if (jb < k1) {
-          id = a.block_table[(int64_t)b * a.max_blocks + jb / 16];
-          if (id < 0 || id >= a.num_blocks) id = 0;
-        }
-        base_row_k[hb] = ((int64_t)id * a.Hkv + g) * 16;
-      }
+    // last valid key index inside this tile (wave-uniform)
+    int klast;
+    uint32_t offA = 0, offB = 0, soff = 0;
+    if (tree) {
+      const int t0 = (tile - ntp) * KT;
+      klast = min(KT, N - t0) - 1;
+      soff = (uint32_t)t0 * ROWB;
     } else {
-      base_row_k[0] = base_row_k[1] = 0;
-    }
-    auto row_of = [&](int kk, bool& ok) -> int64_t {
-      if (tree) {
-        const int t = t0 + kk;
-        ok = t < N;
-        return ((int64_t)b * a.Hkv + g) * (N + 1) + t + 1;
+      const int j0 = k0 + tile * KT;
+      klast = min(KT, k1 - j0) - 1;
+      if (a.paged) {
+        // the tile spans two 16-token blocks; a block wholly past the end reuses the first
+        int idA = a.block_table[(int64_t)b * a.max_blocks + j0 / 16];
+        int idB = klast >= 16 ? a.block_table[(int64_t)b * a.max_blocks + j0 / 16 + 1] : idA;
+        idA = (idA < 0 || idA >= a.num_blocks) ? 0 : idA;
+        idB = (idB < 0 || idB >= a.num_blocks) ? 0 : idB;
+        offA = (uint32_t)(((int64_t)idA * a.Hkv + g) * 16) * ROWB;
+        offB = (uint32_t)(((int64_t)idB * a.Hkv + g) * 16) * ROWB;
+      } else {
+        soff = (uint32_t)j0 * ROWB;
       }
-      const int j = j0 + kk;
-      ok = j < k1;
-      if (a.paged) return base_row_k[kk >> 4] + (kk & 15);
-      return ((int64_t)b * a.Hkv + g) * a.Lcap + j;
-    };
-    const uint16_t* ksrc = tree ? kt : kc;
-    const uint16_t* vsrc = tree ? vt : vc;
-#pragma unroll
-    for (int it = 0; it < KPIECES; ++it) {
-      const int piece = lane + 64 * it;
-      const int key = piece / (D / 8), ch = piece % (D / 8);
-      bool ok;
-      const int64_t row = row_of(key, ok);
-      kreg[it] = ok ? *(const uint4*)(ksrc + row * D + ch * 8) : make_uint4(0, 0, 0, 0);
     }
+    const bool paged_tile = !tree && a.paged;
+    auto voffset = [&](int key, int ch) -> uint32_t {
+      const int k = min(key, klast);
+      if (paged_tile) return (k >= 16 ? offB : offA) + (uint32_t)(k & 15) * ROWB + ch * 16;
+      return (uint32_t)k * ROWB + ch * 16;
+    };
+    const __amdgpu_buffer_rsrc_t rK = tree ? rkt : rk;
+    const __amdgpu_buffer_rsrc_t rV = tree ? rvt : rv;
+#pragma unroll
+    for (int it = 0; it < KPIECES; ++it)
+      kreg[it] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rK, voffset(kkey[it], kch[it]), soff, 0));
 #pragma unroll
     for (int it = 0; it < VITEMS; ++it) {
-      const int item = lane + 64 * it;
-      const int quad = item % (KT / 4), ch = item / (KT / 4);
+      const int quad = vquad0 + QPI * it;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        bool ok;
-        const int64_t row = row_of(quad * 4 + kk, ok);
-        vreg[it][kk] = ok ? *(const uint4*)(vsrc + row * D + ch * 8) : make_uint4(0, 0, 0, 0);
-      }
+      for (int kk = 0; kk < 4; ++kk)
+        vreg[it][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rV, voffset(quad * 4 + kk, vch), soff, 0));
     }
   };
   auto store_tile = [&]() {
 #pragma unroll
-    for (int it = 0; it < KPIECES; ++it) {
-      const int piece = lane + 64 * it;
-      const int key = piece / (D / 8), ch = piece % (D / 8);
-      *(uint4*)(Ks + key * LD::KSTR + ch * 8) = kreg[it];
-    }
+    for (int it = 0; it < KPIECES; ++it) *(uint4*)(Ks + kkey[it] * LD::KSTR + kch[it] * 8) = kreg[it];
 #pragma unroll
     for (int it = 0; it < VITEMS; ++it) {
-      const int item = lane + 64 * it;
-      const int quad = item % (KT / 4), ch = item / (KT / 4);
+      const int quad = vquad0 + QPI * it;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        *(uint2*)(VTs + (ch * 8 + e) * LD::VSTR + quad * 4) =
+        *(uint2*)(VTs + (vch * 8 + e) * LD::VSTR + quad * 4) =
             pack_col(vreg[it][0], vreg[it][1], vreg[it][2], vreg[it][3], e);
     }
   };
@@ -248,55 +265,64 @@ __global__ void __launch_bounds__(AT_THREADS, 1) k_attn_mfma(sv_attn_args a, Att
     }
 
     // ---- masks + online softmax (lane owns query column lq; keys 8*(r/4) + 4*hf + r%4)
+    // Masks are needed only on the partial last prefix tile and on tree tiles;
+    // both conditions are wave-uniform.
+    const bool full = !tree && (j0 + KT <= k1);
     sv_bf16x8 pf[QB][2];
+    bool moved = false;
+    float alpha[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      uint64_t aw = 0;
-      if (tree) {
-        const int wi = t0 >> 6;
-        aw = wi == 0 ? anc[qb][0] : wi == 1 ? anc[qb][1] : wi == 2 ? anc[qb][2] : anc[qb][3];
-      }
       float s[16];
-      float mt = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = 8 * (r >> 2) + 4 * hf + (r & 3);
-        bool ok;
-        if (tree) {
-          const int t = t0 + kk;
-          ok = t < N && ((aw >> (t & 63)) & 1ull);
-        } else {
-          ok = j0 + kk < k1;
-        }
-        s[r] = ok ? sacc[qb][r] * p.cscale : -INFINITY;
-        mt = fmaxf(mt, s[r]);
-      }
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mnew = fmaxf(mrun[qb], mt);
-      float alpha, psum = 0.f;
-      if (mnew == -INFINITY) {
-        alpha = 1.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = 0.f;
-      } else {
-        alpha = exp2f(mrun[qb] - mnew);
+        for (int r = 0; r < 16; ++r) s[r] = sacc[qb][r] * p.cscale;
+      } else if (!tree) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          s[r] = exp2f(s[r] - mnew);
-          psum += s[r];
+          const int kk = 8 * (r >> 2) + 4 * hf + (r & 3);
+          s[r] = (j0 + kk < k1) ? sacc[qb][r] * p.cscale : -INFINITY;
+        }
+      } else {
+        const int wi = t0 >> 6;  // uniform: one 64-bit mask word covers the tile
+        const uint64_t aw = wi == 0 ? anc[qb][0] : wi == 1 ? anc[qb][1] : wi == 2 ? anc[qb][2] : anc[qb][3];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = t0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          const bool keep = (t < N) & (((aw >> (t & 63)) & 1ull) != 0);
+          s[r] = keep ? sacc[qb][r] * p.cscale : -INFINITY;
         }
       }
+      float mt = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float mnew = fmaxf(mrun[qb], mt);
+      const float msafe = mnew == -INFINITY ? 0.f : mnew;  // nothing visible yet: all weights stay 0
+      alpha[qb] = __builtin_amdgcn_exp2f(mrun[qb] - msafe);
+      moved |= mnew != mrun[qb];
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = __builtin_amdgcn_exp2f(s[r] - msafe);
+        psum += s[r];
+      }
       psum += __shfl_xor(psum, 32);
-      lrun[qb] = lrun[qb] * alpha + psum;
+      lrun[qb] = lrun[qb] * alpha[qb] + psum;
       mrun[qb] = mnew;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
         for (int e = 0; e < 8; ++e) pf[qb][t2][e] = (__bf16)s[8 * t2 + e];
+    }
+    // rescale the accumulators only when some lane's running maximum moved
+    if (__ballot(moved)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha[qb];
     }
 
     // ---- O^T += V^T P^T
@@ -339,7 +365,7 @@ __global__ void __launch_bounds__(AT_THREADS, 1) k_attn_mfma(sv_attn_args a, Att
       const float lb = mml[((slot * QB + qb) * 2 + 1) * 64 + lane];
       const float m = fmaxf(mrun[qb], mb);
       if (m == -INFINITY) continue;
-      const float fa = exp2f(mrun[qb] - m), fb = exp2f(mb - m);
+      const float fa = __builtin_amdgcn_exp2f(mrun[qb] - m), fb = __builtin_amdgcn_exp2f(mb - m);
       lrun[qb] = fa * lrun[qb] + fb * lb;
       mrun[qb] = m;
 #pragma unroll
@@ -567,7 +593,14 @@ __global__ void k_attn_check(sv_attn_args a, int32_t cap) {
   a.status[b] = code;
 }
 
-bool use_mfma(const sv_attn_args& a) { return a.dtype == SV_BF16 && (a.D == 64 || a.D == 128); }
+// bf16 with D in {64, 128} runs on MFMA; a paged pool must fit 32-bit buffer offsets
+bool use_mfma(const sv_attn_args& a) {
+  if (a.dtype != SV_BF16 || (a.D != 64 && a.D != 128)) return false;
+  if (a.paged && (uint64_t)a.num_blocks * a.Hkv * a.block_size * a.D * 2 >= (1ull << 31)) return false;
+  if (!a.paged && (uint64_t)a.Lcap * a.D * 2 >= (1ull << 31)) return false;
+  if ((uint64_t)(a.N + 1) * a.D * 2 >= (1ull << 31)) return false;
+  return true;
+}
 
 AttnPlan make_plan(const sv_attn_args& a) {
   AttnPlan p{};
@@ -576,6 +609,7 @@ AttnPlan make_plan(const sv_attn_args& a) {
   p.W = (a.N + 63) / 64;
   p.cap = a.paged ? a.max_blocks * a.block_size : a.Lcap;
   p.cscale = a.scale * LOG2E;
+  p.pool_bytes = a.paged ? (uint32_t)((uint64_t)a.num_blocks * a.Hkv * a.block_size * a.D * 2) : 0u;
   if (!use_mfma(a)) {
     p.nsplit = 1;
     return p;

@@ -69,7 +69,7 @@ class VerifyStep:
         self._acc = accept_args(x.parents, x.tokens, self.mask["anc_bits"], self.mask["depth"], x.target_logits, Dm,
                                 x.mode, x.draft_logits, x.u_accept, x.u_sample, x.temperature, self.acc)
         need = sv_accept_workspace(self._acc)
-        self.acc_ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        self.acc_ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)  # counters start at zero
         self._acc.workspace = self.acc_ws.data_ptr()
         self._acc.workspace_bytes = need
         self._com = commit_args(x.k_cache, x.v_cache, x.k_tree, x.v_tree, x.prefix_len, self.acc["accept_len"],
