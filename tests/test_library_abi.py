@@ -70,7 +70,7 @@ def test_workspace_queries():
     acc.B = 64
     big = sv.sv_accept_workspace(acc)
     assert small % 256 == 0 and big > small  # per-row results and per-sequence counters grow with B
-    assert big - small >= 62 * 61 * 8
+    assert big - small >= 62 * 61 * 8 - 512  # up to 256-byte alignment of each region
 
 
 def test_no_product_module_imports_the_oracle():
