@@ -62,9 +62,11 @@ def source_hash(files):
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_src_hash):
-    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it still matches the source."""
-    path = os.path.join(ROOT, "profiles", "attention_pmc_traffic.json")
+def load_traffic(kernel, kernel_src_hash, workload):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 PMC summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size), or None when
+    the summary is missing or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -109,6 +111,8 @@ def main():
     ap.add_argument("--instances", type=int, default=0, help="input instances cycled (0: enough to defeat the MALL)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (reference kernel for PMC byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU: --gpus {args.gpus} is not supported "
@@ -135,6 +139,12 @@ def main():
     for i in range(args.warmup):
         steps[i % R].run()
     torch.cuda.synchronize()
+    if args.copy_mib:  # untimed reference copy: its FETCH/WRITE counters calibrate the byte counts
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     accs = [{k: v.cpu().numpy() for k, v in s.acc.items()} for s in steps]
     byts = [algorithmic_bytes(w, a) for w, a in zip(ws, accs)]
 
@@ -204,7 +214,7 @@ def main():
     achieved = mean_bytes[dom_key] / (stage_ms[dom] * 1e-3) / 1e9
     src = {"attention": ["tree_verification_sv_amd/csrc/sv_attention.hip"],
            "accept": ["tree_verification_sv_amd/csrc/sv_accept.hip"]}[dom]
-    traffic = load_traffic(source_hash(src)) if dom == "attention" else None
+    traffic = load_traffic(dom, source_hash(src), w0.name)
     result = {
         "metric": "verified tree tokens/sec + HBM GB/s (% peak), 8B-shape tree verify, 1 MI355X",
         "value": round(value, 1),

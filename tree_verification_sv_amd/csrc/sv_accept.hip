@@ -181,43 +181,52 @@ struct SeqInfo {    // per-sequence facts every work-group derives the same way
   int32_t flag;
 };
 
-// usable nodes, child counts per row, live-row count, children of row r (one node per thread)
-__device__ void seq_info(const sv_accept_args& a, int b, int r, SeqInfo& si) {
+// per-sequence facts: usable nodes, child counts per row, live-row count (one node per thread)
+__device__ void seq_load(const sv_accept_args& a, int b, SeqInfo& si) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int N = a.N;
   for (int x = t; x <= N; x += AC_THREADS) si.nkids[x] = 0;
   if (t == 0) si.bad_token = 0;
   __syncthreads();
   bool u = false;
-  int pr = -1;
   if (t < N) {
     const int32_t tok = a.tokens[(int64_t)b * N + t];
     const bool ok = tok >= 0 && tok < a.V;
     if (!ok) atomicOr(&si.bad_token, 1);
-    pr = a.parents[(int64_t)b * N + t];
+    const int pr = a.parents[(int64_t)b * N + t];
     u = ok && a.depth[(int64_t)b * N + t] > 0 && pr >= -1 && pr < N;
     si.par[t] = pr;
-    si.usable[t] = u;
     if (u) atomicAdd(&si.nkids[pr + 1], 1);
   }
+  if (t < SV_MAX_N) si.usable[t] = u;
   __syncthreads();
-  // ascending compaction of the usable children of row r
-  const bool kid = u && pr + 1 == r;
-  const uint64_t m = __ballot(kid);
-  const int before_in_wave = __popcll(m & ((1ull << lane) - 1ull));
   // live rows: greedy -- rows with a usable child; stochastic -- rows of usable nodes
-  bool live = a.mode == SV_GREEDY ? (t >= 1 && t <= N && si.nkids[t] > 0) : u;
+  const bool live = a.mode == SV_GREEDY ? (t >= 1 && t <= N && si.nkids[t] > 0) : u;
   const uint64_t lm = __ballot(live);
-  if (lane == 0) { si.wcount[wv] = __popcll(m); si.wlive[wv] = __popcll(lm); }
+  if (lane == 0) si.wlive[wv] = __popcll(lm);
   __syncthreads();
-  int off = 0, K = 0, nl = 0;
+  if (t == 0) {
+    int nl = 0;
+    for (int k = 0; k < AC_THREADS / 64; ++k) nl += si.wlive[k];
+    si.nlive = nl + 1;  // + the root row
+  }
+  __syncthreads();
+}
+
+// usable children of row r in ascending index, from the cached sequence facts
+__device__ void row_kids(int N, int r, SeqInfo& si) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const bool kid = t < N && si.usable[t] && si.par[t] + 1 == r;
+  const uint64_t m = __ballot(kid);
+  if (lane == 0) si.wcount[wv] = __popcll(m);
+  __syncthreads();
+  int off = 0, K = 0;
   for (int k = 0; k < AC_THREADS / 64; ++k) {
     if (k < wv) off += si.wcount[k];
     K += si.wcount[k];
-    nl += si.wlive[k];
   }
-  if (kid) si.kids[off + before_in_wave] = t;
-  if (t == 0) { si.K = K; si.nlive = nl + 1; }  // + the root row
+  if (kid) si.kids[off + __popcll(m & ((1ull << lane) - 1ull))] = t;
+  if (t == 0) si.K = K;
   __syncthreads();
 }
 
@@ -322,8 +331,8 @@ __device__ __forceinline__ void load8(const T* row, int v, int V, float (&x)[8])
   }
 }
 
-template <typename T>
-__global__ void __launch_bounds__(AC_THREADS) k_accept(sv_accept_args a, int32_t G, AccWs ws) {
+template <typename T, int MODE>
+__global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int32_t G, AccWs ws) {
   __shared__ Red red;
   __shared__ SeqInfo si;
   __shared__ int32_t s_last, s_hit;
@@ -341,7 +350,7 @@ __global__ void __launch_bounds__(AC_THREADS) k_accept(sv_accept_args a, int32_t
   const int grp = (idx / G) * 8 + xcd;
   const int rank = idx % G;
   const int N = a.N, V = a.V;
-  const float invT = a.mode == SV_STOCHASTIC ? 1.0f / a.temperature : 1.0f;
+  const float invT = MODE == SV_STOCHASTIC ? 1.0f / a.temperature : 1.0f;
   const float l2T = invT * 1.4426950408889634f;  // bulk exponentials as exp2((x - m) * log2(e) / T)
   uint32_t* bar = ws.bar + grp;
   uint32_t nbar = 0;
@@ -350,22 +359,31 @@ __global__ void __launch_bounds__(AC_THREADS) k_accept(sv_accept_args a, int32_t
   // a work-group can run at most one row ahead of the slowest member of its group
   auto slot = [&](int k, int par) -> Xchg* { return ws.xg + ((int64_t)grp * G + k) * 2 + par; };
 
-  // this work-group's slice of the vocabulary; thread t owns AC_CT contiguous entries
-  const int v0 = rank * AC_SLICE + t * AC_CT;
   const int64_t items = (int64_t)a.B * (N + 1);
   int nrows = 0;
+  int cached_b = -1;
 
   for (int64_t item = grp; item < items; item += NG) {
+    // per-lane offsets are recomputed each row from an opaque lane index instead of
+    // being hoisted out of the loop (hoisted, they exceed the register budget and spill)
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    // this work-group's slice of the vocabulary; thread t owns AC_CT contiguous entries
+    const int v0 = rank * AC_SLICE + t * AC_CT;
     const int b = (int)(item / (N + 1));
     const int r = (int)(item % (N + 1));
-    seq_info(a, b, r, si);
+    if (b != cached_b) {  // rows of one sequence reuse its facts
+      seq_load(a, b, si);
+      cached_b = b;
+    }
     if (!row_live(a, si, r)) continue;  // uniform across the group
+    row_kids(N, r, si);
     const int par = nrows++ & 1;
     const T* prow = (const T*)a.target_logits + ((int64_t)b * (N + 1) + r) * V;
-    const T* qrow = a.mode == SV_STOCHASTIC ? (const T*)a.draft_logits + ((int64_t)b * (N + 1) + r) * V : nullptr;
+    const T* qrow = MODE == SV_STOCHASTIC ? (const T*)a.draft_logits + ((int64_t)b * (N + 1) + r) * V : nullptr;
     int done_by_me = 0;  // this work-group wrote the row result
 
-    if (a.mode == SV_GREEDY) {
+    if constexpr (MODE == SV_GREEDY) {
       float best = -FLT_MAX;
       int arg = 0x7fffffff;
       {
@@ -422,45 +440,53 @@ __global__ void __launch_bounds__(AC_THREADS) k_accept(sv_accept_args a, int32_t
       T* sq = (T*)lds_q + t * AC_PAD;
       float mp = -FLT_MAX, mq = -FLT_MAX;
       {
+        // coalesced global -> LDS copy: piece q = k * AC_THREADS + t covers entries
+        // [q * PER16, (q + 1) * PER16) of the slice, owned by thread (q * PER16) / AC_CT
         constexpr int PER16 = 16 / sizeof(T);
         constexpr int NLD = AC_CT / PER16;
-        const bool fast = v0 + AC_CT <= V && ((uintptr_t)(prow + v0) % 16) == 0;
-        // global -> LDS copies; global loads and LDS stores never alias, so the compiler issues
-        // the loads ahead of the stores
-        if (fast) {
+        const int s0 = rank * AC_SLICE;
+        const bool rowal = ((uintptr_t)prow % 16) == 0 && ((uintptr_t)qrow % 16) == 0;
+        // one tensor at a time keeps at most NLD 16-byte loads in flight per thread
+        auto copy = [&](const T* src, T* lds, float& m) {
 #pragma unroll
-          for (int k = 0; k < NLD; ++k) *(uint4*)(sp + k * PER16) = *(const uint4*)(prow + v0 + k * PER16);
-          if (need_q) {
+          for (int k = 0; k < NLD; ++k) {
+            const int q = k * AC_THREADS + t;
+            const int e0 = q * PER16;  // entry inside the slice
+            T* d = lds + (e0 / AC_CT) * AC_PAD + (e0 % AC_CT);
+            const int v = s0 + e0;
+            if (rowal && v + PER16 <= V) {
+              const uint4 w = *(const uint4*)(src + v);
+              float x[PER16];
+              unpack16<T>(w, x);
 #pragma unroll
-            for (int k = 0; k < NLD; ++k) *(uint4*)(sq + k * PER16) = *(const uint4*)(qrow + v0 + k * PER16);
+              for (int e = 0; e < PER16; ++e) m = fmaxf(m, x[e]);
+              *(uint4*)d = w;
+            } else {
+              for (int e = 0; e < PER16; ++e) {  // ragged tail: entries past V hold the lowest value
+                const T xv = v + e < V ? src[v + e] : lowest_of<T>();
+                m = fmaxf(m, to_f32(xv));
+                d[e] = xv;
+              }
+            }
           }
-        } else {
-          for (int e = 0; e < AC_CT; ++e) {  // ragged tail: entries past V hold the lowest value
-            sp[e] = v0 + e < V ? prow[v0 + e] : lowest_of<T>();
-            if (need_q) sq[e] = v0 + e < V ? qrow[v0 + e] : lowest_of<T>();
-          }
-        }
+        };
+        copy(prow, (T*)lds_p, mp);
+        if (need_q) copy(qrow, (T*)lds_q, mq);
       }
-      for (int k = 0; k < AC_CT; k += 8) {
-        float x[8];
-        lds8(sp + k, x);
-        for (int e = 0; e < 8; ++e) mp = fmaxf(mp, x[e]);
-        if (need_q) {
-          lds8(sq + k, x);
-          for (int e = 0; e < 8; ++e) mq = fmaxf(mq, x[e]);
-        }
-      }
-      mp = block_max(mp, red);
+      mp = block_max(mp, red);  // also orders the LDS copies before the passes below
       mq = block_max(mq, red);
       const float op = mp * l2T, oq = mq * l2T;  // exp2(x * l2T - o): one FMA per entry
       double zp = 0.0, zq = 0.0;
       for (int k = 0; k < AC_CT; k += 8) {
-        float x[8];
+        float x[8], g = 0.f;  // fp32 partial of 8 entries, fp64 across partials
         lds8(sp + k, x);
-        for (int e = 0; e < 8; ++e) zp += (double)__builtin_amdgcn_exp2f(fmaf(x[e], l2T, -op));
+        for (int e = 0; e < 8; ++e) g += __builtin_amdgcn_exp2f(fmaf(x[e], l2T, -op));
+        zp += (double)g;
         if (need_q) {
           lds8(sq + k, x);
-          for (int e = 0; e < 8; ++e) zq += (double)__builtin_amdgcn_exp2f(fmaf(x[e], l2T, -oq));
+          g = 0.f;
+          for (int e = 0; e < 8; ++e) g += __builtin_amdgcn_exp2f(fmaf(x[e], l2T, -oq));
+          zq += (double)g;
         }
       }
       zp = block_sum(zp, red);
@@ -490,16 +516,17 @@ __global__ void __launch_bounds__(AC_THREADS) k_accept(sv_accept_args a, int32_t
       auto slice_sum = [&](float kappa) -> double {
         double acc = 0.0;
         for (int k = 0; k < AC_CT; k += 8) {
-          float x[8], y[8];
+          float x[8], y[8], g = 0.f;  // fp32 partial of 8 entries, fp64 across partials
           lds8(sp + k, x);
           if (kappa == 0.f) {
-            for (int e = 0; e < 8; ++e) acc += (double)__builtin_amdgcn_exp2f(fmaf(x[e], l2T, -op));
+            for (int e = 0; e < 8; ++e) g += __builtin_amdgcn_exp2f(fmaf(x[e], l2T, -op));
           } else {
             lds8(sq + k, y);
             for (int e = 0; e < 8; ++e)
-              acc += (double)fmaxf(fmaf(-kappa, __builtin_amdgcn_exp2f(fmaf(y[e], l2T, -oq)),
-                                        __builtin_amdgcn_exp2f(fmaf(x[e], l2T, -op))), 0.f);
+              g += fmaxf(fmaf(-kappa, __builtin_amdgcn_exp2f(fmaf(y[e], l2T, -oq)),
+                              __builtin_amdgcn_exp2f(fmaf(x[e], l2T, -op))), 0.f);
           }
+          acc += (double)g;
         }
         return acc;
       };
@@ -618,7 +645,7 @@ __global__ void __launch_bounds__(AC_THREADS) k_accept(sv_accept_args a, int32_t
         // ----------------------------------------------------- walk of sequence b
         int A = 0, stop_row = 0, bonus = 0;
         RowRes* rr = ws.res + (int64_t)b * (N + 1);
-        if (a.mode == SV_GREEDY) {
+        if constexpr (MODE == SV_GREEDY) {
           // match[i]: token equals its parent row's argmax; accepted: the whole root path matches
           if (t < SV_MAX_W) s_match[t] = 0;
           __syncthreads();
@@ -716,17 +743,23 @@ __global__ void __launch_bounds__(AC_THREADS) k_accept(sv_accept_args a, int32_t
 }
 
 // occupancy-based size of the persistent grid (per device, cached)
-int resident_groups(int G, int dtype_bf16) {
-  static int cached[64][2] = {};
+template <typename T, int MODE>
+int occupancy_of() {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_accept<T, MODE>, AC_THREADS, 0) != hipSuccess) per_cu = 1;
+  return per_cu;
+}
+
+int resident_groups(int G, int dtype_bf16, int mode) {
+  static int cached[64][2][2] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  int& c = cached[dev][dtype_bf16];
+  int& c = cached[dev][dtype_bf16][mode];
   if (c == 0) {
-    int cus = 0, per_cu = 0;
+    int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 1;
-    hipError_t e = dtype_bf16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_accept<uint16_t>, AC_THREADS, 0)
-                              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_accept<float>, AC_THREADS, 0);
-    if (e != hipSuccess) per_cu = 1;
+    const int per_cu = dtype_bf16 ? (mode ? occupancy_of<uint16_t, SV_STOCHASTIC>() : occupancy_of<uint16_t, SV_GREEDY>())
+                                  : (mode ? occupancy_of<float, SV_STOCHASTIC>() : occupancy_of<float, SV_GREEDY>());
     c = cus * (per_cu > 0 ? per_cu : 1);
     if (c < 1) c = 1;
     if (c > AC_MAX_RESIDENT) c = AC_MAX_RESIDENT;
@@ -781,7 +814,7 @@ extern "C" sv_status sv_accept(const sv_accept_args* args, void* stream) {
   const int G = groups_G(a);
   if (G > AC_MAXG) return SV_ERR_UNSUPPORTED;
   const int bf = a.logits_dtype == SV_BF16;
-  int NG = resident_groups(G, bf);
+  int NG = resident_groups(G, bf, a.mode == SV_STOCHASTIC);
   const int64_t items = (int64_t)a.B * (a.N + 1);
   if (NG > items) NG = (int)((items + 7) / 8 * 8);
   NG = NG / 8 * 8;  // groups are placed per XCD
@@ -796,7 +829,12 @@ extern "C" sv_status sv_accept(const sv_accept_args* args, void* stream) {
   ws.xg = (Xchg*)(base + l.xg);
   hipStream_t st = (hipStream_t)stream;
   const dim3 grid((unsigned)(NG * G));
-  if (bf) hipLaunchKernelGGL(k_accept<uint16_t>, grid, dim3(AC_THREADS), 0, st, a, G, ws);
-  else hipLaunchKernelGGL(k_accept<float>, grid, dim3(AC_THREADS), 0, st, a, G, ws);
+  if (bf) {
+    if (a.mode == SV_STOCHASTIC) hipLaunchKernelGGL((k_accept<uint16_t, SV_STOCHASTIC>), grid, dim3(AC_THREADS), 0, st, a, G, ws);
+    else hipLaunchKernelGGL((k_accept<uint16_t, SV_GREEDY>), grid, dim3(AC_THREADS), 0, st, a, G, ws);
+  } else {
+    if (a.mode == SV_STOCHASTIC) hipLaunchKernelGGL((k_accept<float, SV_STOCHASTIC>), grid, dim3(AC_THREADS), 0, st, a, G, ws);
+    else hipLaunchKernelGGL((k_accept<float, SV_GREEDY>), grid, dim3(AC_THREADS), 0, st, a, G, ws);
+  }
   return sv_launch_status();
 }

@@ -44,6 +44,28 @@ struct AttnPlan {
 
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
 
+// Data checks behind the optional status array, run by one work-group per
+// sequence: 6 when prefix_len lies outside [0, capacity] (it is clamped), 5 when
+// a needed block-table entry is the ghost block 0 or outside the pool (read as
+// the ghost block).
+__device__ void write_seq_status(const sv_attn_args& a, int b, int cap) {
+  __shared__ int s_code;
+  if (threadIdx.x == 0) s_code = 0;
+  __syncthreads();
+  const int L0 = a.prefix_len[b];
+  if (L0 < 0 || L0 > cap) {
+    if (threadIdx.x == 0) s_code = SV_SEQ_CAPACITY;
+  } else if (a.paged) {
+    const int nblk = (L0 + a.block_size - 1) / a.block_size;
+    for (int k = threadIdx.x; k < nblk; k += blockDim.x) {
+      const int id = a.block_table[(int64_t)b * a.max_blocks + k];
+      if (id < 1 || id >= a.num_blocks) atomicOr(&s_code, SV_SEQ_BLOCK);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) a.status[b] = s_code;
+}
+
 // ------------------------------------------------------------------ MFMA path
 template <int D>
 struct Lds {
@@ -97,6 +119,7 @@ __global__ void __launch_bounds__(AT_THREADS, 1) k_attn_mfma(sv_attn_args a, Att
   const int g = pair % a.Hkv;
   const int N = a.N, Hq = a.Hq, G = p.G;
 
+  if (a.status && g == 0 && qtile == 0 && split == 0) write_seq_status(a, b, p.cap);
   const int L = clamp_len(a.prefix_len[b], p.cap);
   const int k0 = split * p.chunk;
   const int k1 = min(k0 + p.chunk, L);
@@ -482,6 +505,7 @@ __global__ void __launch_bounds__(256) k_attn_valu(sv_attn_args a, AttnPlan p) {
   const int i = (id / a.Hkv) % a.N;
   const int b = id / (a.Hkv * a.N);
   const int G = p.G, D = a.D, N = a.N;
+  if (a.status && i == 0 && g == 0) write_seq_status(a, b, p.cap);
   const T* qg = (const T*)a.q;
   const T* kc = (const T*)a.k_cache;
   const T* vc = (const T*)a.v_cache;
@@ -576,24 +600,6 @@ __global__ void __launch_bounds__(256) k_attn_valu(sv_attn_args a, AttnPlan p) {
   }
 }
 
-// data checks for the status array: prefix length range and block-table entries
-__global__ void k_attn_check(sv_attn_args a, int32_t cap) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= a.B) return;
-  const int32_t L0 = a.prefix_len[b];
-  int code = (L0 < 0 || L0 > cap) ? SV_SEQ_CAPACITY : 0;
-  const int L = clamp_len(L0, cap);
-  if (a.paged && code == 0) {
-    const int nblk = (L + a.block_size - 1) / a.block_size;
-    for (int k = 0; k < nblk; ++k) {
-      const int id = a.block_table[(int64_t)b * a.max_blocks + k];
-      if (id < 1 || id >= a.num_blocks) { code = SV_SEQ_BLOCK; break; }
-    }
-  }
-  a.status[b] = code;
-}
-
-// bf16 with D in {64, 128} runs on MFMA; a paged pool must fit 32-bit buffer offsets
 bool use_mfma(const sv_attn_args& a) {
   if (a.dtype != SV_BF16 || (a.D != 64 && a.D != 128)) return false;
   if (a.paged && (uint64_t)a.num_blocks * a.Hkv * a.block_size * a.D * 2 >= (1ull << 31)) return false;
@@ -679,7 +685,6 @@ extern "C" sv_status sv_tree_attention(const sv_attn_args* args, void* stream) {
     p.mlpart = (float*)((char*)a.workspace + (parts * a.D * sizeof(float) + 255) / 256 * 256);
   }
   hipStream_t s = (hipStream_t)stream;
-  if (a.status) hipLaunchKernelGGL(k_attn_check, dim3((a.B + 255) / 256), dim3(256), 0, s, a, p.cap);
   if (use_mfma(a)) {
     const int64_t grid = (int64_t)a.B * a.Hkv * p.qtiles * p.nsplit;
     if (grid > 0x7fffffff) return SV_ERR_UNSUPPORTED;
