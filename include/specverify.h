@@ -86,6 +86,7 @@ typedef int32_t sv_status;
 #define SV_SEQ_TOKEN 4          /* a draft token id outside [0, V) */
 #define SV_SEQ_BLOCK 5          /* a needed block-table entry is 0 (ghost) or outside the pool */
 #define SV_SEQ_CAPACITY 6       /* prefix_len (+ accepted rows) exceeds the cache capacity */
+#define SV_SEQ_TIMEOUT 7        /* sv_accept: a bounded wait between cooperating work-groups expired */
 
 /*
  * sv_build_tree_mask -- tree tensorisation ([EP] sec. 2, "Semantica de
@@ -185,7 +186,13 @@ sv_status sv_tree_attention(const sv_attn_args* args, void* stream);
  *   (rows of the accepted path, root-most first, ghost-0 padded), out_tokens
  *   [B, max_depth+1] (accepted tokens then the bonus, 0 padded), num_out [B]
  *   (A+1), stop_row [B], status [B] (4 if some token id is out of range).
- * workspace: at least sv_accept_workspace(args) bytes, 256-byte aligned.
+ * workspace: at least sv_accept_workspace(args) bytes, 256-byte aligned,
+ *   zero-filled by the caller before its first use; every call leaves it
+ *   zeroed again.  Calls that overlap in time must not share a workspace.
+ *   The work-groups that share one logits row wait for each other with a
+ *   bounded spin; if one never arrives (the device could not hold the whole
+ *   persistent grid at once) the wait expires and every sequence of the call
+ *   reports status 7 instead of hanging.
  */
 typedef struct sv_accept_args {
   int32_t B, N, V, max_depth, logits_dtype, mode;

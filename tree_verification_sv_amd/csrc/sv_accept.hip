@@ -19,14 +19,28 @@
 // that row alone.  Every row is therefore resolved independently and in
 // parallel, and the walk is a pointer chase over the per-row results.
 //
-// One persistent kernel.  Groups of G work-groups share one row; each keeps a
-// 16384-entry vocabulary slice in registers (exponentials computed once) and
-// the group exchanges per-slice partials through device-scope barriers.
-// Greedy rows need one pass (slice max / argmax, lowest id on ties).  The
-// group that completes the last row of a sequence performs its walk.  Rows
-// resolved: greedy -- the root row and rows with a usable child (a leaf stop
-// row's argmax is taken by the walker); stochastic -- the root row and the
-// rows of all usable nodes (leaf rows only read the target logits).
+// Work decomposition.  A group of G work-groups resolves one row; each owns a
+// 16384-entry slice of the vocabulary.  Thread t owns the 16-byte pieces
+// k * 256 + t (k = 0 .. 64 / (16 / sizeof(T)) - 1) of its slice, so every load
+// instruction of a wave reads 1 KB of consecutive logits.  The exponentials
+// are computed once into registers; each later pass over the row (a
+// rejection's residual sum, the bonus scan) is a few register operations per
+// entry.  Members of a group trade per-slice partials through tagged 64-bit
+// words (tag and payload in one atomic word, so a reader that sees the tag
+// also sees the value).  Greedy rows need one pass (slice max / argmax, lowest
+// id on ties).  The group that completes the last row of a sequence performs
+// its walk.  Rows resolved: greedy -- the root row and rows with a usable
+// child (a leaf stop row's argmax is taken by the walker); stochastic -- the
+// root row and the rows of all usable nodes (leaf rows only read the target
+// logits); the work-groups of other rows exit at once.
+//
+// Forward progress.  Work-groups are dispatched in index order, round-robin
+// over the 8 XCDs; the members of a group are consecutive in their XCD's
+// dispatch order (block indices x, x + 8, ..., x + 8 (G - 1)), and a member
+// only ever waits for members of its own group.  Every group ahead of the
+// oldest unfinished one has finished, so that group is resident or next in
+// line: no group waits for a work-group that cannot start.  The waits are
+// bounded all the same (status SV_SEQ_TIMEOUT).
 #include <float.h>
 #include <math.h>
 
@@ -35,21 +49,16 @@
 namespace {
 
 constexpr int AC_THREADS = 256;
+constexpr int AC_NW = AC_THREADS / 64;         // waves per work-group
 constexpr int AC_CT = 64;                      // vocabulary entries per thread
 constexpr int AC_SLICE = AC_THREADS * AC_CT;   // 16384 entries per work-group
-constexpr int AC_MAX_RESIDENT = 4096;          // cap on persistent work-groups
-constexpr uint32_t AC_SPIN_LIMIT = 1u << 20;   // bounded wait at a group barrier (polls)
-constexpr int SEQ_COOP_TIMEOUT = 7;            // status: a group barrier timed out
+constexpr int AC_MAXG = 64;                    // work-groups per row group (vocabulary up to 1M entries)
+constexpr int AC_XW = 8;                       // tagged words per exchange slot
+constexpr uint32_t AC_SPIN_LIMIT = 1u << 20;   // bounded wait for a group partner (polls)
 
-struct Xchg {       // one work-group's partial for the current row
-  float pm, qm;     // slice maxima
-  double pz, qz;    // slice sums of exp((l - m)/T)
-  double s[2];      // slice residual sums, alternating between rejection steps
-  double cdf;       // slice total of the final residual
-  float av;         // greedy slice maximum
-  int32_t ai;       // greedy slice argmax
+struct XSlot {      // one work-group's partials for one exchange: (tag << 32) | payload
+  uint64_t w[AC_XW];
 };
-static_assert(sizeof(Xchg) == 56, "Xchg layout");
 
 struct RowRes {     // resolved row
   int32_t child;    // first accepted child node, -1 when all rejected (stochastic)
@@ -57,12 +66,11 @@ struct RowRes {     // resolved row
 };
 
 struct AccWs {      // workspace views
-  uint32_t* bar;    // [AC_MAX_RESIDENT] group barrier counters
-  uint32_t* gexit;  // [AC_MAX_RESIDENT] group exit counters
+  uint32_t* gexit;  // [groups] group exit counters
   uint32_t* seqdone;// [B] rows resolved per sequence
-  uint32_t* err;    // [0] barrier timeout flag, [1] work-groups exited
+  uint32_t* err;    // [0] wait-timeout flag, [1] work-groups exited
   RowRes* res;      // [B, N+1]
-  Xchg* xg;         // [AC_MAX_RESIDENT][2]: (group * G + rank) * 2 + row parity
+  XSlot* xs;        // [groups * G * 2]: (group * G + rank) * 2 + exchange parity
 };
 
 template <typename T>
@@ -84,59 +92,68 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
     if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
   }
 }
+// inclusive prefix sum over the 64 lanes of a wave, ascending lane order
+__device__ __forceinline__ double wave_scand(double x, int lane) {
+  for (int o = 1; o < 64; o <<= 1) {
+    const double y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
 
 struct Red {
-  float f[AC_THREADS / 64];
-  double d[AC_THREADS / 64];
-  int i[AC_THREADS / 64];
-  double scan[AC_THREADS];
+  float f[AC_NW];
+  double d[AC_NW];
+  int i[AC_NW];
+  double scan1[AC_THREADS];  // exclusive prefixes of the bonus scan, one per thread
 };
+// LDS index of slice-local entry i in the bonus staging buffer: a stride of 68
+// floats per 64 entries keeps the 16-byte reads of consecutive threads on
+// distinct banks
+__host__ __device__ constexpr int wpad(int i) { return i + (i / AC_CT) * 4; }
 
-__device__ float block_max(float x, Red& r) {
+__device__ __forceinline__ float block_max(float x, Red& r) {
   x = wave_maxf(x);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) r.f[threadIdx.x >> 6] = x;
   __syncthreads();
   float m = r.f[0];
-  for (int k = 1; k < AC_THREADS / 64; ++k) m = fmaxf(m, r.f[k]);
+  for (int k = 1; k < AC_NW; ++k) m = fmaxf(m, r.f[k]);
   return m;
 }
-__device__ double block_sum(double x, Red& r) {
+__device__ __forceinline__ double block_sum(double x, Red& r) {
   x = wave_sumd(x);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) r.d[threadIdx.x >> 6] = x;
   __syncthreads();
   double s = 0.0;
-  for (int k = 0; k < AC_THREADS / 64; ++k) s += r.d[k];
+  for (int k = 0; k < AC_NW; ++k) s += r.d[k];
   return s;
 }
-__device__ void block_argmax(float& v, int& i, Red& r) {
+__device__ __forceinline__ void block_argmax(float& v, int& i, Red& r) {
   wave_argmax(v, i);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) { r.f[threadIdx.x >> 6] = v; r.i[threadIdx.x >> 6] = i; }
   __syncthreads();
   v = r.f[0];
   i = r.i[0];
-  for (int k = 1; k < AC_THREADS / 64; ++k)
+  for (int k = 1; k < AC_NW; ++k)
     if (r.f[k] > v || (r.f[k] == v && r.i[k] < i)) { v = r.f[k]; i = r.i[k]; }
 }
 
 // ---------------------------------------------------------------- cross-work-group messages
 // Values crossing work-groups are written with relaxed device-scope atomic
 // stores and read with relaxed device-scope atomic loads (both coherent at
-// device scope); a writer waits for its stores to complete (s_waitcnt) before
-// it bumps the counter a reader polls.  This message-passing order needs no
-// cache write-back or invalidation.
+// device scope).  Exchange words carry their tag in the same 64-bit word as
+// the payload.  Row results are published before the per-sequence counter:
+// the writer waits for its stores to complete (s_waitcnt) and then bumps the
+// counter.  Neither order needs a cache write-back or invalidation.
 #define AGENT __HIP_MEMORY_SCOPE_AGENT
 __device__ __forceinline__ void st_u32(uint32_t* p, uint32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, AGENT); }
 __device__ __forceinline__ void st_u64(uint64_t* p, uint64_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, AGENT); }
 __device__ __forceinline__ uint32_t ld_u32(uint32_t* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, AGENT); }
 __device__ __forceinline__ uint64_t ld_u64(uint64_t* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, AGENT); }
 __device__ __forceinline__ uint32_t add_u32(uint32_t* p, uint32_t v) { return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, AGENT); }
-__device__ __forceinline__ void st_f(float* p, float v) { st_u32((uint32_t*)p, __float_as_uint(v)); }
-__device__ __forceinline__ float ld_f(float* p) { return __uint_as_float(ld_u32((uint32_t*)p)); }
-__device__ __forceinline__ void st_d(double* p, double v) { st_u64((uint64_t*)p, __double_as_longlong(v)); }
-__device__ __forceinline__ double ld_d(double* p) { return __longlong_as_double(ld_u64((uint64_t*)p)); }
 __device__ __forceinline__ void st_i(int32_t* p, int32_t v) { st_u32((uint32_t*)p, (uint32_t)v); }
 __device__ __forceinline__ int32_t ld_i(int32_t* p) { return (int32_t)ld_u32((uint32_t*)p); }
 // wait until this thread's memory operations have completed
@@ -144,25 +161,42 @@ __device__ __forceinline__ void mem_complete() {
   __builtin_amdgcn_s_waitcnt(0);
   asm volatile("" ::: "memory");
 }
+__device__ __forceinline__ uint32_t dlo(double x) { return (uint32_t)__double_as_longlong(x); }
+__device__ __forceinline__ uint32_t dhi(double x) { return (uint32_t)((uint64_t)__double_as_longlong(x) >> 32); }
+__device__ __forceinline__ double dof(uint32_t lo, uint32_t hi) {
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
 
-// Arrive-and-wait among the G work-groups of a group; `target` = (barrier
-// sequence number) * G, identical across the group.  Thread 0 of each
-// work-group wrote this step's exchange values.  The wait is bounded: on
-// timeout the error flag is raised, and once it is raised no work-group waits
-// any more, so every wave exits promptly (results then carry status 7).
-__device__ void group_barrier(uint32_t* bar, uint32_t target, uint32_t* err, int G) {
-  __syncthreads();
-  if (G > 1 && threadIdx.x == 0) {
-    mem_complete();
-    add_u32(bar, 1u);
+// Exchange number `tag` (>= 1, the same on every member) of a group: this
+// work-group publishes the nw words w0..w5 (identical in all its threads) and
+// collects every member's words into xv[rank][word].  Slots alternate by tag
+// parity: a member can only reach exchange tag+2 after every member has
+// published tag+1, that is after every member has collected exchange tag.
+// The wait is bounded: on timeout the error flag is raised, and once it is
+// raised no thread waits any more, so every wave exits (results then carry
+// status SV_SEQ_TIMEOUT).
+__device__ __forceinline__ void exchange(XSlot* gs, int G, int rank, uint32_t tag, int nw, uint32_t (*xv)[AC_XW],
+                                         uint32_t* err, uint32_t w0, uint32_t w1, uint32_t w2 = 0, uint32_t w3 = 0,
+                                         uint32_t w4 = 0, uint32_t w5 = 0) {
+  const int t = threadIdx.x;
+  const int par = tag & 1;
+  if (t < nw) {
+    const uint32_t w = t == 0 ? w0 : t == 1 ? w1 : t == 2 ? w2 : t == 3 ? w3 : t == 4 ? w4 : w5;
+    st_u64(&gs[rank * 2 + par].w[t], ((uint64_t)tag << 32) | w);
+  }
+  for (int q = t; q < G * nw; q += AC_THREADS) {
+    const int k = q / nw, i = q - k * nw;
+    uint64_t* p = &gs[k * 2 + par].w[i];
+    uint64_t v = ld_u64(p);
     uint32_t spins = 0;
-    while (ld_u32(bar) < target) {
+    while ((uint32_t)(v >> 32) != tag) {
       if ((++spins & 63) == 0 && (spins > AC_SPIN_LIMIT || ld_u32(err) != 0)) {
         st_u32(err, 1u);
         break;
       }
+      v = ld_u64(p);
     }
-    asm volatile("" ::: "memory");
+    xv[k][i] = (uint32_t)v;
   }
   __syncthreads();
 }
@@ -172,8 +206,8 @@ struct SeqInfo {    // per-sequence facts every work-group derives the same way
   int32_t usable[SV_MAX_N];
   int32_t nkids[SV_MAX_N + 1];
   int32_t kids[SV_MAX_N];     // usable children of the current row, ascending
-  int32_t wcount[AC_THREADS / 64];
-  int32_t wlive[AC_THREADS / 64];
+  int32_t wcount[AC_NW];
+  int32_t wlive[AC_NW];
   int32_t K;                  // number of usable children of the current row
   int32_t nlive;              // rows this sequence resolves
   int32_t bad_token;
@@ -182,7 +216,7 @@ struct SeqInfo {    // per-sequence facts every work-group derives the same way
 };
 
 // per-sequence facts: usable nodes, child counts per row, live-row count (one node per thread)
-__device__ void seq_load(const sv_accept_args& a, int b, SeqInfo& si) {
+__device__ __forceinline__ void seq_load(const sv_accept_args& a, int b, SeqInfo& si) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int N = a.N;
   for (int x = t; x <= N; x += AC_THREADS) si.nkids[x] = 0;
@@ -207,21 +241,21 @@ __device__ void seq_load(const sv_accept_args& a, int b, SeqInfo& si) {
   __syncthreads();
   if (t == 0) {
     int nl = 0;
-    for (int k = 0; k < AC_THREADS / 64; ++k) nl += si.wlive[k];
+    for (int k = 0; k < AC_NW; ++k) nl += si.wlive[k];
     si.nlive = nl + 1;  // + the root row
   }
   __syncthreads();
 }
 
-// usable children of row r in ascending index, from the cached sequence facts
-__device__ void row_kids(int N, int r, SeqInfo& si) {
+// usable children of row r in ascending index, from the sequence facts
+__device__ __forceinline__ void row_kids(int N, int r, SeqInfo& si) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const bool kid = t < N && si.usable[t] && si.par[t] + 1 == r;
   const uint64_t m = __ballot(kid);
   if (lane == 0) si.wcount[wv] = __popcll(m);
   __syncthreads();
   int off = 0, K = 0;
-  for (int k = 0; k < AC_THREADS / 64; ++k) {
+  for (int k = 0; k < AC_NW; ++k) {
     if (k < wv) off += si.wcount[k];
     K += si.wcount[k];
   }
@@ -235,50 +269,17 @@ __device__ __forceinline__ bool row_live(const sv_accept_args& a, const SeqInfo&
   return a.mode == SV_GREEDY ? si.nkids[r] > 0 : si.usable[r - 1] != 0;
 }
 
-// AC_CT contiguous logits starting at v (entries >= V read as -FLT_MAX)
-template <typename T>
-__device__ __forceinline__ void load_chunk(const T* row, int v, int V, float (&x)[AC_CT]) {
-  constexpr int PER16 = 16 / sizeof(T);
-  if (v + AC_CT <= V && ((uintptr_t)(row + v) % 16) == 0) {
-#pragma unroll
-    for (int k = 0; k < AC_CT / PER16; ++k) {
-      const uint4 w = *(const uint4*)(row + v + k * PER16);
-      if (sizeof(T) == 2) {
-        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          x[k * 8 + 2 * h] = __uint_as_float(ww[h] << 16);
-          x[k * 8 + 2 * h + 1] = __uint_as_float(ww[h] & 0xffff0000u);
-        }
-      } else {
-        x[k * 4 + 0] = __uint_as_float(w.x);
-        x[k * 4 + 1] = __uint_as_float(w.y);
-        x[k * 4 + 2] = __uint_as_float(w.z);
-        x[k * 4 + 3] = __uint_as_float(w.w);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < AC_CT; ++e) x[e] = v + e < V ? ldf(row, v + e) : -FLT_MAX;
-  }
-}
-
-// p(x) of one entry against the row's global max / normaliser
-template <typename T>
-__device__ __forceinline__ double prob_at(const T* row, int x, float m, double z, float invT) {
-  return (double)expf((ldf(row, x) - m) * invT) / z;
-}
-
-// ---------------------------------------------------------------- the kernel
-constexpr int AC_MAXG = 64;  // work-groups per row group (vocabulary up to 1M entries)
-constexpr int AC_PAD = AC_CT + 8;  // LDS entries per thread: the padding keeps 16-byte reads conflict-free
-
+// ---------------------------------------------------------------- slice loads
+template <typename T> struct Piece {
+  static constexpr int E = 16 / sizeof(T);  // entries per 16-byte piece
+  static constexpr int NK = AC_CT / E;      // pieces per thread
+};
 template <typename T> __device__ __forceinline__ T lowest_of();
 template <> __device__ __forceinline__ float lowest_of<float>() { return -FLT_MAX; }
 template <> __device__ __forceinline__ uint16_t lowest_of<uint16_t>() { return 0xff7f; }  // bf16 -3.39e38
-__device__ __forceinline__ float to_f32(float x) { return x; }
-__device__ __forceinline__ float to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
-// the 16 bytes of w as PER16 = 16/sizeof(T) floats
+__device__ __forceinline__ uint32_t bits_of(float x) { return __float_as_uint(x); }
+__device__ __forceinline__ uint32_t bits_of(uint16_t x) { return (uint32_t)x; }
+// the 16 bytes of w as E = 16/sizeof(T) floats
 template <typename T> __device__ __forceinline__ void unpack16(const uint4& w, float (&x)[16 / sizeof(T)]);
 template <> __device__ __forceinline__ void unpack16<uint16_t>(const uint4& w, float (&x)[8]) {
   const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
@@ -291,449 +292,458 @@ template <> __device__ __forceinline__ void unpack16<uint16_t>(const uint4& w, f
 template <> __device__ __forceinline__ void unpack16<float>(const uint4& w, float (&x)[4]) {
   x[0] = __uint_as_float(w.x); x[1] = __uint_as_float(w.y); x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
 }
-// 8 consecutive LDS entries as floats
-__device__ __forceinline__ void lds8(const uint16_t* p, float (&x)[8]) {
-  const uint4 w = *(const uint4*)p;
-  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+// hide the register values from the optimiser, so that values derived from
+// them are recomputed where they are used rather than kept alive in between
+template <int NK>
+__device__ __forceinline__ void opaque(uint4 (&raw)[NK]) {
 #pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    x[2 * h] = __uint_as_float(ww[h] << 16);
-    x[2 * h + 1] = __uint_as_float(ww[h] & 0xffff0000u);
-  }
+  for (int k = 0; k < NK; ++k) asm volatile("" : "+v"(raw[k].x), "+v"(raw[k].y), "+v"(raw[k].z), "+v"(raw[k].w));
 }
-__device__ __forceinline__ void lds8(const float* p, float (&x)[8]) {
-  const float4 a0 = *(const float4*)p, a1 = *(const float4*)(p + 4);
-  x[0] = a0.x; x[1] = a0.y; x[2] = a0.z; x[3] = a0.w;
-  x[4] = a1.x; x[5] = a1.y; x[6] = a1.z; x[7] = a1.w;
-}
-
-// 8 contiguous logits starting at v (entries >= V read as -FLT_MAX)
+// first entry of piece k of thread t in a slice starting at s0
 template <typename T>
-__device__ __forceinline__ void load8(const T* row, int v, int V, float (&x)[8]) {
-  if (v + 8 <= V && ((uintptr_t)(row + v) % 16) == 0) {
-    if (sizeof(T) == 2) {
-      const uint4 w = *(const uint4*)(row + v);
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+__device__ __forceinline__ int piece_v(int s0, int k, int t) { return s0 + (k * AC_THREADS + t) * Piece<T>::E; }
+
+// Thread t's pieces of one logits row.  `aligned`: the row starts on 16 bytes
+// and V * sizeof(T) is a multiple of 16, so each piece lies wholly inside or
+// wholly past the row; the loads then go through a buffer resource sized to
+// the row, which returns zeros for pieces past V.  Otherwise entries are
+// loaded one by one and entries past V read as the lowest value.  Callers
+// treat pieces starting at or past V as absent.
+template <typename T>
+__device__ __forceinline__ void load_pieces(const T* row, int s0, int V, bool aligned, int t,
+                                            uint4 (&raw)[Piece<T>::NK]) {
+  constexpr int E = Piece<T>::E;
+  if (aligned) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)row, 0, V * (int)sizeof(T), 0x00020000);
+    const int vo = (s0 + t * E) * (int)sizeof(T);
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        x[2 * h] = __uint_as_float(ww[h] << 16);
-        x[2 * h + 1] = __uint_as_float(ww[h] & 0xffff0000u);
-      }
-    } else {
-      const float4 a0 = *(const float4*)(row + v);
-      const float4 a1 = *(const float4*)(row + v + 4);
-      x[0] = a0.x; x[1] = a0.y; x[2] = a0.z; x[3] = a0.w;
-      x[4] = a1.x; x[5] = a1.y; x[6] = a1.z; x[7] = a1.w;
-    }
+    for (int k = 0; k < Piece<T>::NK; ++k)
+      raw[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, k * AC_THREADS * 16, 0));
   } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = v + e < V ? ldf(row, v + e) : -FLT_MAX;
+    for (int k = 0; k < Piece<T>::NK; ++k) {
+      const int v = piece_v<T>(s0, k, t);
+      uint32_t wd[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const T x = v + e < V ? row[v + e] : lowest_of<T>();
+        wd[e * sizeof(T) / 4] |= bits_of(x) << (8 * ((e * sizeof(T)) % 4));
+      }
+      raw[k] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    }
   }
 }
 
+// ---------------------------------------------------------------- the kernel
 template <typename T, int MODE>
 __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int32_t G, AccWs ws) {
+  constexpr int E = Piece<T>::E, NK = Piece<T>::NK;
   __shared__ Red red;
   __shared__ SeqInfo si;
-  __shared__ int32_t s_last, s_hit;
+  __shared__ int32_t s_last, s_hit, s_first, s_lpos;
   __shared__ uint64_t s_match[SV_MAX_W];
-  __shared__ float xs_f0[AC_MAXG], xs_f1[AC_MAXG];   // group partials copied in by thread 0
-  __shared__ double xs_d0[AC_MAXG], xs_d1[AC_MAXG];
-  __shared__ int32_t xs_i[AC_MAXG];
-  __shared__ __attribute__((aligned(16))) T lds_p[AC_THREADS * AC_PAD];
-  __shared__ __attribute__((aligned(16))) T lds_q[AC_THREADS * AC_PAD];
-  const int t = threadIdx.x;
+  __shared__ uint32_t xv[AC_MAXG][AC_XW];                          // collected group partials
+  __shared__ float s_lp[SV_MAX_N], s_lq[SV_MAX_N], s_u[SV_MAX_N];  // per child: logits at its token, u_accept
+  __shared__ float s_us;                                            // u_sample of the row
+  // bonus weights of the slice in id order, 4 floats of padding after every 64 entries
+  __shared__ __attribute__((aligned(16))) float s_w[MODE == SV_STOCHASTIC ? wpad(AC_SLICE) : 4];
   // work-groups are dispatched round-robin over the 8 XCDs; the members of a
   // group share an XCD (the grid size is a multiple of 8 * G)
-  const int NG = gridDim.x / G;
+  const int t = threadIdx.x, lane = t & 63;
   const int xcd = blockIdx.x % 8, idx = blockIdx.x / 8;
   const int grp = (idx / G) * 8 + xcd;
   const int rank = idx % G;
   const int N = a.N, V = a.V;
   const float invT = MODE == SV_STOCHASTIC ? 1.0f / a.temperature : 1.0f;
   const float l2T = invT * 1.4426950408889634f;  // bulk exponentials as exp2((x - m) * log2(e) / T)
-  uint32_t* bar = ws.bar + grp;
-  uint32_t nbar = 0;
-  auto gsync = [&]() { ++nbar; group_barrier(bar, nbar * (uint32_t)G, ws.err, G); };
-  // exchange slots of this group, double-buffered by the parity of the row count:
-  // a work-group can run at most one row ahead of the slowest member of its group
-  auto slot = [&](int k, int par) -> Xchg* { return ws.xg + ((int64_t)grp * G + k) * 2 + par; };
+  XSlot* gslots = ws.xs + (int64_t)grp * G * 2;
+  uint32_t xtag = 0;  // exchanges of this group so far (identical on every member)
+  const int64_t item = grp;
+  const int s0 = rank * AC_SLICE;  // this work-group's slice of the vocabulary
 
-  const int64_t items = (int64_t)a.B * (N + 1);
-  int nrows = 0;
-  int cached_b = -1;
-
-  for (int64_t item = grp; item < items; item += NG) {
-    // per-lane offsets are recomputed each row from an opaque lane index instead of
-    // being hoisted out of the loop (hoisted, they exceed the register budget and spill)
-    int t = threadIdx.x;
-    asm volatile("" : "+v"(t));
-    // this work-group's slice of the vocabulary; thread t owns AC_CT contiguous entries
-    const int v0 = rank * AC_SLICE + t * AC_CT;
+  if (item < (int64_t)a.B * (N + 1)) {
     const int b = (int)(item / (N + 1));
     const int r = (int)(item % (N + 1));
-    if (b != cached_b) {  // rows of one sequence reuse its facts
-      seq_load(a, b, si);
-      cached_b = b;
-    }
-    if (!row_live(a, si, r)) continue;  // uniform across the group
-    row_kids(N, r, si);
-    const int par = nrows++ & 1;
-    const T* prow = (const T*)a.target_logits + ((int64_t)b * (N + 1) + r) * V;
-    const T* qrow = MODE == SV_STOCHASTIC ? (const T*)a.draft_logits + ((int64_t)b * (N + 1) + r) * V : nullptr;
-    int done_by_me = 0;  // this work-group wrote the row result
+    seq_load(a, b, si);
+    if (row_live(a, si, r)) {  // uniform across the group
+      row_kids(N, r, si);
+      const T* prow = (const T*)a.target_logits + ((int64_t)b * (N + 1) + r) * V;
+      const T* qrow = MODE == SV_STOCHASTIC ? (const T*)a.draft_logits + ((int64_t)b * (N + 1) + r) * V : nullptr;
+      const bool aligned = ((size_t)V * sizeof(T)) % 16 == 0 && ((uintptr_t)prow % 16) == 0 &&
+                           (MODE == SV_GREEDY || ((uintptr_t)qrow % 16) == 0);
+      int done_by_me = 0;  // this work-group wrote the row result
 
-    if constexpr (MODE == SV_GREEDY) {
-      float best = -FLT_MAX;
-      int arg = 0x7fffffff;
-      {
-        constexpr int PER16 = 16 / sizeof(T);
-        constexpr int NLD = AC_CT / PER16;
-        const bool fast = v0 + AC_CT <= V && ((uintptr_t)(prow + v0) % 16) == 0;
-        if (fast) {
-          uint4 rp[NLD];
+      if constexpr (MODE == SV_GREEDY) {
+        float best = -FLT_MAX;
+        int arg = 0x7fffffff;
+        {
+          uint4 raw[NK];
+          load_pieces<T>(prow, s0, V, aligned, t, raw);
 #pragma unroll
-          for (int k = 0; k < NLD; ++k) rp[k] = *(const uint4*)(prow + v0 + k * PER16);  // all loads first
+          for (int k = 0; k < NK; ++k) {
+            float x[E];
+            unpack16<T>(raw[k], x);
+            const int v = piece_v<T>(s0, k, t);
 #pragma unroll
-          for (int k = 0; k < NLD; ++k) {
-            float x[PER16];
-            unpack16<T>(rp[k], x);
-#pragma unroll
-            for (int e = 0; e < PER16; ++e)  // ascending ids: the first maximum is kept
-              if (x[e] > best) { best = x[e]; arg = v0 + k * PER16 + e; }
-          }
-        } else {
-          for (int e = 0; e < AC_CT; ++e) {
-            const int v = v0 + e;
-            if (v < V) {
-              const float x = ldf(prow, v);
-              if (x > best) { best = x; arg = v; }
-            }
+            for (int e = 0; e < E; ++e)  // a thread visits its entries in ascending id
+              if (v + e < V && x[e] > best) { best = x[e]; arg = v + e; }
           }
         }
-      }
-      block_argmax(best, arg, red);
-      if (t == 0) { st_f(&slot(rank, par)->av, best); st_i(&slot(rank, par)->ai, arg); }
-      gsync();
-      if (rank == 0) {
-        if (t == 0) {
-          float bv = ld_f(&slot(0, par)->av);
-          int bi = ld_i(&slot(0, par)->ai);
-          for (int k = 1; k < G; ++k) {
-            const float kv = ld_f(&slot(k, par)->av);
-            const int ki = ld_i(&slot(k, par)->ai);
-            if (kv > bv || (kv == bv && ki < bi)) { bv = kv; bi = ki; }
-          }
-          st_i(&ws.res[item].child, -1);
-          st_i(&ws.res[item].token, bi);
-        }
-        done_by_me = 1;
-      }
-    } else {
-      // ---- stochastic: the slice's raw logits stay in LDS (thread t's AC_CT entries at
-      // sp[t * AC_PAD ...], padded for conflict-free 16-byte reads); every pass recomputes
-      // the exponentials exp2((x - m) * log2(e) / T) from them, which keeps LDS small
-      // enough for two work-groups per CU
-      const int K = __builtin_amdgcn_readfirstlane(si.K);
-      const bool need_q = K > 0;
-      T* sp = (T*)lds_p + t * AC_PAD;
-      T* sq = (T*)lds_q + t * AC_PAD;
-      float mp = -FLT_MAX, mq = -FLT_MAX;
-      {
-        // coalesced global -> LDS copy: piece q = k * AC_THREADS + t covers entries
-        // [q * PER16, (q + 1) * PER16) of the slice, owned by thread (q * PER16) / AC_CT
-        constexpr int PER16 = 16 / sizeof(T);
-        constexpr int NLD = AC_CT / PER16;
-        const int s0 = rank * AC_SLICE;
-        const bool rowal = ((uintptr_t)prow % 16) == 0 && ((uintptr_t)qrow % 16) == 0;
-        // one tensor at a time keeps at most NLD 16-byte loads in flight per thread
-        auto copy = [&](const T* src, T* lds, float& m) {
-#pragma unroll
-          for (int k = 0; k < NLD; ++k) {
-            const int q = k * AC_THREADS + t;
-            const int e0 = q * PER16;  // entry inside the slice
-            T* d = lds + (e0 / AC_CT) * AC_PAD + (e0 % AC_CT);
-            const int v = s0 + e0;
-            if (rowal && v + PER16 <= V) {
-              const uint4 w = *(const uint4*)(src + v);
-              float x[PER16];
-              unpack16<T>(w, x);
-#pragma unroll
-              for (int e = 0; e < PER16; ++e) m = fmaxf(m, x[e]);
-              *(uint4*)d = w;
-            } else {
-              for (int e = 0; e < PER16; ++e) {  // ragged tail: entries past V hold the lowest value
-                const T xv = v + e < V ? src[v + e] : lowest_of<T>();
-                m = fmaxf(m, to_f32(xv));
-                d[e] = xv;
-              }
-            }
-          }
-        };
-        copy(prow, (T*)lds_p, mp);
-        if (need_q) copy(qrow, (T*)lds_q, mq);
-      }
-      mp = block_max(mp, red);  // also orders the LDS copies before the passes below
-      mq = block_max(mq, red);
-      const float op = mp * l2T, oq = mq * l2T;  // exp2(x * l2T - o): one FMA per entry
-      double zp = 0.0, zq = 0.0;
-      for (int k = 0; k < AC_CT; k += 8) {
-        float x[8], g = 0.f;  // fp32 partial of 8 entries, fp64 across partials
-        lds8(sp + k, x);
-        for (int e = 0; e < 8; ++e) g += __builtin_amdgcn_exp2f(fmaf(x[e], l2T, -op));
-        zp += (double)g;
-        if (need_q) {
-          lds8(sq + k, x);
-          g = 0.f;
-          for (int e = 0; e < 8; ++e) g += __builtin_amdgcn_exp2f(fmaf(x[e], l2T, -oq));
-          zq += (double)g;
-        }
-      }
-      zp = block_sum(zp, red);
-      zq = block_sum(zq, red);
-      if (t == 0) {
-        Xchg* x = slot(rank, par);
-        st_f(&x->pm, mp); st_d(&x->pz, zp); st_f(&x->qm, mq); st_d(&x->qz, zq);
-      }
-      gsync();
-      if (t < G) {
-        Xchg* x = slot(t, par);
-        xs_f0[t] = ld_f(&x->pm); xs_d0[t] = ld_d(&x->pz); xs_f1[t] = ld_f(&x->qm); xs_d1[t] = ld_d(&x->qz);
-      }
-      __syncthreads();
-      // global statistics, merged in rank order by every work-group alike
-      float Mp = xs_f0[0], Mq = xs_f1[0];
-      for (int k = 1; k < G; ++k) { Mp = fmaxf(Mp, xs_f0[k]); Mq = fmaxf(Mq, xs_f1[k]); }
-      double Zp = 0.0, Zq = 0.0;
-      for (int k = 0; k < G; ++k) {
-        Zp += xs_d0[k] * exp2((double)(xs_f0[k] - Mp) * (double)l2T);
-        if (need_q) Zq += xs_d1[k] * exp2((double)(xs_f1[k] - Mq) * (double)l2T);
-      }
-      const double fp = exp2((double)(mp - Mp) * (double)l2T) / Zp;  // p(v) = ep(v) * fp on this slice
-      const double fq = need_q ? exp2((double)(mq - Mq) * (double)l2T) / Zq : 0.0;
-      // residual weights on this slice in units of fp: max(0, ep - kappa eq), with
-      // ep = exp2(x_p * l2T - op), eq = exp2(x_q * l2T - oq)
-      auto slice_sum = [&](float kappa) -> double {
-        double acc = 0.0;
-        for (int k = 0; k < AC_CT; k += 8) {
-          float x[8], y[8], g = 0.f;  // fp32 partial of 8 entries, fp64 across partials
-          lds8(sp + k, x);
-          if (kappa == 0.f) {
-            for (int e = 0; e < 8; ++e) g += __builtin_amdgcn_exp2f(fmaf(x[e], l2T, -op));
-          } else {
-            lds8(sq + k, y);
-            for (int e = 0; e < 8; ++e)
-              g += fmaxf(fmaf(-kappa, __builtin_amdgcn_exp2f(fmaf(y[e], l2T, -oq)),
-                              __builtin_amdgcn_exp2f(fmaf(x[e], l2T, -op))), 0.f);
-          }
-          acc += (double)g;
-        }
-        return acc;
-      };
-      // ---- accept tests along the residual chain
-      double c = 0.0, Dn = 1.0, c_prev = 0.0;
-      int accepted = -1;
-      for (int j = 0; j < K; ++j) {
-        const int kid = si.kids[j];
-        const int x = a.tokens[(int64_t)b * N + kid];
-        const double px = prob_at(prow, x, Mp, Zp, invT);
-        const double qx = prob_at(qrow, x, Mq, Zq, invT);
-        const double cur = fmax(0.0, px - c * qx) / Dn;
-        const double u = (double)a.u_accept[(int64_t)b * (N + 1) + kid + 1];
-        if (qx > 0.0 ? (u < cur / qx) : true) { accepted = kid; break; }
-        // rejection: next residual coefficient; its normaliser is needed only for a later test,
-        // after the last child the bonus scan below computes it as its total
-        const double cn = c + Dn;
-        if (j == K - 1) { c_prev = c; c = cn; break; }
-        // max(0, p - cn q) = fp * max(0, ep - kappa eq) on this slice, kappa = cn fq / fp
-        const float kappa = (float)(cn * fq / fp);
-        double sl = block_sum(slice_sum(kappa), red) * fp;
-        if (t == 0) st_d(&slot(rank, par)->s[j & 1], sl);
-        gsync();
-        if (t < G) xs_d0[t] = ld_d(&slot(t, par)->s[j & 1]);
-        __syncthreads();
-        double S = 0.0;
-        for (int k = 0; k < G; ++k) S += xs_d0[k];
-        __syncthreads();
-        if (S > 0.0) { c = cn; Dn = S; }  // S == 0 only through rounding: keep the residual
-      }
-      if (accepted >= 0) {
+        block_argmax(best, arg, red);
+        exchange(gslots, G, rank, ++xtag, 2, xv, ws.err, __float_as_uint(best), (uint32_t)arg);
         if (rank == 0) {
-          if (t == 0) { st_i(&ws.res[item].child, accepted); st_i(&ws.res[item].token, -1); }
+          if (t == 0) {
+            float bv = __uint_as_float(xv[0][0]);
+            int bi = (int)xv[0][1];
+            for (int k = 1; k < G; ++k) {
+              const float kv = __uint_as_float(xv[k][0]);
+              const int ki = (int)xv[k][1];
+              if (kv > bv || (kv == bv && ki < bi)) { bv = kv; bi = ki; }
+            }
+            st_i(&ws.res[item].child, -1);
+            st_i(&ws.res[item].token, bi);
+          }
           done_by_me = 1;
         }
       } else {
-        // ---- bonus: smallest v whose ascending cumulative residual exceeds u * total.
-        // A residual of total 0 (reachable only through rounding) falls back to the previous one.
-        const double us = (double)a.u_sample[(int64_t)b * (N + 1) + r];
-        for (int attempt = 0; attempt < 2; ++attempt) {
-          // residual weights on this slice in units of fp: max(0, ep - kappa eq), kappa = c fq / fp
-          const float kappa = c == 0.0 ? 0.f : (float)(c * fq / fp);
-          red.scan[t] = slice_sum(kappa);
-          __syncthreads();
-          for (int off = 1; off < AC_THREADS; off <<= 1) {  // inclusive scan, fixed order
-            const double add = t >= off ? red.scan[t - off] : 0.0;
-            __syncthreads();
-            red.scan[t] += add;
-            __syncthreads();
+        const int K = __builtin_amdgcn_readfirstlane(si.K);
+        const bool need_q = K > 0;
+        // ---- children's logits at their tokens and their uniforms, fetched alongside the slice
+        if (t < K) {
+          const int kid = si.kids[t];
+          const int x = a.tokens[(int64_t)b * N + kid];  // usable: x in [0, V)
+          s_lp[t] = ldf(prow, x);
+          s_lq[t] = ldf(qrow, x);
+          s_u[t] = a.u_accept[(int64_t)b * (N + 1) + kid + 1];
+        }
+        if (t == AC_THREADS - 1) s_us = a.u_sample[(int64_t)b * (N + 1) + r];
+        // ---- the slice: raw logits -> slice maxima -> exponentials kept in registers
+        float ep[AC_CT], eq[AC_CT];
+        float mp = -FLT_MAX, mq = -FLT_MAX;
+        double zp = 0.0, zq = 0.0;
+        {
+          uint4 rp[NK], rq[NK];
+          load_pieces<T>(prow, s0, V, aligned, t, rp);
+          if (need_q) load_pieces<T>(qrow, s0, V, aligned, t, rq);
+#pragma unroll
+          for (int k = 0; k < NK; ++k) {
+            float x[E];
+            unpack16<T>(rp[k], x);
+#pragma unroll
+            for (int e = 0; e < E; ++e) mp = piece_v<T>(s0, k, t) < V ? fmaxf(mp, x[e]) : mp;
           }
-          if (t == 0) st_d(&slot(rank, par)->s[attempt], red.scan[AC_THREADS - 1] * fp);
-          gsync();
-          if (t < G) xs_d1[t] = ld_d(&slot(t, par)->s[attempt]);
-          __syncthreads();
-          double before = 0.0, total = 0.0;
-          for (int k = 0; k < G; ++k) {
-            if (k < rank) before += xs_d1[k];
-            total += xs_d1[k];
-          }
-          if (!(total > 0.0) && attempt == 0 && c != 0.0) {  // uniform: retry with the previous residual
-            c = c_prev;
-            __syncthreads();
-            continue;
-          }
-          // the slice whose inclusive prefix first exceeds the threshold draws the token
-          const double thr = us * total;
-          int owner = G - 1;
-          {
-            double pre = 0.0;
-            for (int k = 0; k < G; ++k) {
-              pre += xs_d1[k];
-              if (pre > thr) { owner = k; break; }
+          mp = block_max(mp, red);
+          opaque(rp);  // unpack again below instead of keeping the unpacked floats alive
+          const float op = mp * l2T;  // exp2(x * l2T - op): one FMA per entry
+#pragma unroll
+          for (int k = 0; k < NK; ++k) {
+            float x[E], g = 0.f;  // fp32 partial of one piece, fp64 across pieces
+            unpack16<T>(rp[k], x);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              ep[k * E + e] = piece_v<T>(s0, k, t) < V ? __builtin_amdgcn_exp2f(fmaf(x[e], l2T, -op)) : 0.f;
+              g += ep[k * E + e];
             }
+            zp += (double)g;
           }
-          if (rank == owner) {
-            if (t == 0) s_hit = 0x7fffffff;
-            __syncthreads();
-            const double lthr = (thr - before) / fp;  // threshold in this slice's units
-            if (red.scan[t] > lthr) atomicMin(&s_hit, t);
-            __syncthreads();
-            const int hit = s_hit == 0x7fffffff ? AC_THREADS - 1 : s_hit;
-            if (t == hit) {
-              double run = t > 0 ? red.scan[t - 1] : 0.0;
-              int pick = -1, last_pos = -1;
-              for (int e = 0; e < AC_CT; ++e) {
-                const int v = v0 + e;
-                const float ep1 = __builtin_amdgcn_exp2f(fmaf(to_f32(sp[e]), l2T, -op));
-                const float w = kappa == 0.f ? ep1
-                                             : fmaxf(fmaf(-kappa, __builtin_amdgcn_exp2f(fmaf(to_f32(sq[e]), l2T, -oq)), ep1), 0.f);
-                if (v < V && w > 0.f) last_pos = v;
-                run += (double)w;
-                if (pick < 0 && v < V && run > lthr) pick = v;
+          if (need_q) {
+#pragma unroll
+            for (int k = 0; k < NK; ++k) {
+              float x[E];
+              unpack16<T>(rq[k], x);
+#pragma unroll
+              for (int e = 0; e < E; ++e) mq = piece_v<T>(s0, k, t) < V ? fmaxf(mq, x[e]) : mq;
+            }
+            mq = block_max(mq, red);
+            opaque(rq);
+            const float oq = mq * l2T;
+#pragma unroll
+            for (int k = 0; k < NK; ++k) {
+              float x[E], g = 0.f;
+              unpack16<T>(rq[k], x);
+#pragma unroll
+              for (int e = 0; e < E; ++e) {
+                eq[k * E + e] = piece_v<T>(s0, k, t) < V ? __builtin_amdgcn_exp2f(fmaf(x[e], l2T, -oq)) : 0.f;
+                g += eq[k * E + e];
               }
-              if (pick < 0) pick = last_pos >= 0 ? last_pos : min(v0 + AC_CT, V) - 1;
-              st_i(&ws.res[item].child, -1);
-              st_i(&ws.res[item].token, pick);
-              mem_complete();
+              zq += (double)g;
             }
+          } else {
+#pragma unroll
+            for (int i = 0; i < AC_CT; ++i) eq[i] = 0.f;
+          }
+        }
+        zp = block_sum(zp, red);
+        zq = block_sum(zq, red);
+        exchange(gslots, G, rank, ++xtag, 6, xv, ws.err, __float_as_uint(mp), __float_as_uint(mq), dlo(zp), dhi(zp),
+                 dlo(zq), dhi(zq));
+        // global statistics, merged in rank order by every work-group alike
+        float Mp = __uint_as_float(xv[0][0]), Mq = __uint_as_float(xv[0][1]);
+        for (int k = 1; k < G; ++k) {
+          Mp = fmaxf(Mp, __uint_as_float(xv[k][0]));
+          Mq = fmaxf(Mq, __uint_as_float(xv[k][1]));
+        }
+        double Zp = 0.0, Zq = 0.0;
+        for (int k = 0; k < G; ++k) {
+          Zp += dof(xv[k][2], xv[k][3]) * exp2((double)(__uint_as_float(xv[k][0]) - Mp) * (double)l2T);
+          if (need_q) Zq += dof(xv[k][4], xv[k][5]) * exp2((double)(__uint_as_float(xv[k][1]) - Mq) * (double)l2T);
+        }
+        const double fp = exp2((double)(mp - Mp) * (double)l2T) / Zp;  // p(v) = ep(v) * fp on this slice
+        const double fq = need_q ? exp2((double)(mq - Mq) * (double)l2T) / Zq : 0.0;
+        // residual weight of one entry in units of fp: max(0, ep - kappa eq); kappa = 0 is p itself
+        auto wgt = [&](int i, float kappa) -> float {
+          return kappa == 0.f ? ep[i] : fmaxf(fmaf(-kappa, eq[i], ep[i]), 0.f);
+        };
+        auto slice_sum = [&](float kappa) -> double {
+          double acc = 0.0;
+#pragma unroll
+          for (int k = 0; k < NK; ++k) {
+            float g = 0.f;  // fp32 partial of one piece, fp64 across pieces
+#pragma unroll
+            for (int e = 0; e < E; ++e) g += wgt(k * E + e, kappa);
+            acc += (double)g;
+          }
+          return acc;
+        };
+        // ---- accept tests along the residual chain
+        double c = 0.0, Dn = 1.0, c_prev = 0.0;
+        int accepted = -1;
+        for (int j = 0; j < K; ++j) {
+          const double px = (double)expf((s_lp[j] - Mp) * invT) / Zp;
+          const double qx = (double)expf((s_lq[j] - Mq) * invT) / Zq;
+          const double cur = fmax(0.0, px - c * qx) / Dn;
+          const double u = (double)s_u[j];
+          if (qx > 0.0 ? (u < cur / qx) : true) { accepted = si.kids[j]; break; }
+          // rejection: next residual coefficient; its normaliser is needed only for a later test,
+          // after the last child the bonus scan below computes it as its total
+          const double cn = c + Dn;
+          if (j == K - 1) { c_prev = c; c = cn; break; }
+          // max(0, p - cn q) = fp * max(0, ep - kappa eq) on this slice, kappa = cn fq / fp
+          const float kappa = (float)(cn * fq / fp);
+          const double sl = block_sum(slice_sum(kappa), red) * fp;
+          exchange(gslots, G, rank, ++xtag, 2, xv, ws.err, dlo(sl), dhi(sl));
+          double S = 0.0;
+          for (int k = 0; k < G; ++k) S += dof(xv[k][0], xv[k][1]);
+          __syncthreads();
+          if (S > 0.0) { c = cn; Dn = S; }  // S == 0 only through rounding: keep the residual
+        }
+        if (accepted >= 0) {
+          if (rank == 0) {
+            if (t == 0) { st_i(&ws.res[item].child, accepted); st_i(&ws.res[item].token, -1); }
             done_by_me = 1;
           }
-          break;
+        } else {
+          // ---- bonus: smallest v whose ascending cumulative residual exceeds u * total.
+          // A residual of total 0 (reachable only through rounding) falls back to the previous one.
+          // The slice's weights are staged in LDS in id order; thread t then scans the 64
+          // consecutive entries [64 t, 64 t + 64) (fp32 partials of 8 entries, fp64 above).
+          const int wv = t >> 6;
+          const double us = (double)s_us;
+          for (int attempt = 0; attempt < 2; ++attempt) {
+            const float kappa = c == 0.0 ? 0.f : (float)(c * fq / fp);
+#pragma unroll
+            for (int k = 0; k < NK; ++k) {
+              const int i0 = (k * AC_THREADS + t) * E;  // slice-local id of the piece
+              float* dst = s_w + wpad(i0);
+#pragma unroll
+              for (int e = 0; e < E; e += 4)
+                *(float4*)(dst + e) = make_float4(wgt(k * E + e, kappa), wgt(k * E + e + 1, kappa),
+                                                  wgt(k * E + e + 2, kappa), wgt(k * E + e + 3, kappa));
+            }
+            __syncthreads();
+            const float* mine = s_w + wpad(t * AC_CT);
+            double tsum = 0.0;
+            int lastpos = -1;  // highest id of this thread with a positive weight (ids >= V weigh 0)
+#pragma unroll
+            for (int j = 0; j < AC_CT; j += 8) {
+              const float4 x0 = *(const float4*)(mine + j), x1 = *(const float4*)(mine + j + 4);
+              const float w8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+              float g = 0.f;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                g += w8[e];
+                lastpos = w8[e] > 0.f ? s0 + t * AC_CT + j + e : lastpos;
+              }
+              tsum += (double)g;
+            }
+            double incl = wave_scand(tsum, lane);
+            if (lane == 63) red.d[wv] = incl;
+            __syncthreads();
+            double col = 0.0;
+            for (int w2 = 0; w2 < AC_NW; ++w2) {
+              if (w2 < wv) incl += red.d[w2];
+              col += red.d[w2];
+            }
+            const double sl = col * fp;
+            exchange(gslots, G, rank, ++xtag, 2, xv, ws.err, dlo(sl), dhi(sl));
+            double before = 0.0, total = 0.0;
+            for (int k = 0; k < G; ++k) {
+              const double s = dof(xv[k][0], xv[k][1]);
+              if (k < rank) before += s;
+              total += s;
+            }
+            if (!(total > 0.0) && attempt == 0 && c != 0.0) {  // uniform: retry with the previous residual
+              c = c_prev;
+              __syncthreads();
+              continue;
+            }
+            // the slice whose inclusive prefix first exceeds the threshold draws the token
+            const double thr = us * total;
+            int owner = G - 1;
+            {
+              double pre = 0.0;
+              for (int k = 0; k < G; ++k) {
+                pre += dof(xv[k][0], xv[k][1]);
+                if (pre > thr) { owner = k; break; }
+              }
+            }
+            if (rank == owner) {
+              const double lthr = (thr - before) / fp;  // threshold in this slice's units
+              if (t == 0) { s_first = 0x7fffffff; s_lpos = -1; }
+              __syncthreads();
+              if (lastpos >= 0) atomicMax(&s_lpos, lastpos);
+              if (incl > lthr) atomicMin(&s_first, t);  // the first thread whose prefix exceeds it
+              red.scan1[t] = incl - tsum;                // exclusive prefix of each thread
+              __syncthreads();
+              const int h = s_first;
+              if (h != 0x7fffffff) {
+                if (wv == 0) {  // one wave searches thread h's 64 entries, lane e = entry e
+                  const float w = s_w[wpad(h * AC_CT) + lane];
+                  const double run = red.scan1[h] + wave_scand((double)w, lane);
+                  const uint64_t hit = __ballot(w > 0.f && run > lthr);
+                  const uint64_t pos = __ballot(w > 0.f);
+                  int pick;
+                  if (hit) pick = s0 + h * AC_CT + __ffsll((long long)hit) - 1;
+                  else if (pos) pick = s0 + h * AC_CT + 63 - __clzll((long long)pos);
+                  else pick = min(s0 + h * AC_CT + AC_CT, V) - 1;
+                  if (lane == 0) {
+                    st_i(&ws.res[item].child, -1);
+                    st_i(&ws.res[item].token, pick);
+                  }
+                }
+              } else if (t == 0) {  // rounding left the threshold unreached
+                const int pick = s_lpos >= 0 ? s_lpos : min(s0 + AC_SLICE, V) - 1;
+                st_i(&ws.res[item].child, -1);
+                st_i(&ws.res[item].token, pick);
+              }
+              done_by_me = 1;
+            }
+            break;
+          }
         }
       }
-    }
 
-    // ---- the work-group that wrote the row result counts it; the last row of a sequence walks
-    if (done_by_me) {
-      __syncthreads();
-      if (t == 0) {
-        mem_complete();
-        const uint32_t old = add_u32(&ws.seqdone[b], 1u);
-        s_last = old + 1 == (uint32_t)si.nlive;
-      }
-      __syncthreads();
-      if (s_last) {
-        // ----------------------------------------------------- walk of sequence b
-        int A = 0, stop_row = 0, bonus = 0;
-        RowRes* rr = ws.res + (int64_t)b * (N + 1);
-        if constexpr (MODE == SV_GREEDY) {
-          // match[i]: token equals its parent row's argmax; accepted: the whole root path matches
-          if (t < SV_MAX_W) s_match[t] = 0;
-          __syncthreads();
-          if (t < N && si.usable[t] && a.tokens[(int64_t)b * N + t] == ld_i(&rr[si.par[t] + 1].token))
-            atomicOr((unsigned long long*)&s_match[t >> 6], 1ull << (t & 63));
-          __syncthreads();
-          const int W = (N + 63) / 64;
-          int key = -1;
-          if (t < N && si.usable[t]) {
-            const uint64_t* arow = a.anc_bits + ((int64_t)b * N + t) * W;
-            bool ok = true;
-            for (int w = 0; w < W; ++w) ok &= (arow[w] & ~s_match[w]) == 0;
-            if (ok) key = (a.depth[(int64_t)b * N + t] << 9) | (511 - t);  // deepest, then lowest index
-          }
-          {
-            float kv = (float)key;
-            int ki = key;
-            block_argmax(kv, ki, red);
-            key = (int)kv;
-          }
-          if (key >= 0) {
-            A = key >> 9;
-            const int stop = 511 - (key & 511);
-            stop_row = stop + 1;
-            if (t == 0) {
-              int node = stop;
-              for (int k = A - 1; k >= 0; --k) { si.path[k] = node; node = si.par[node]; }
-            }
-          }
-          if (row_live(a, si, stop_row)) {
-            if (t == 0) s_hit = ld_i(&rr[stop_row].token);
-            __syncthreads();
-            bonus = s_hit;
-          } else {
-            // leaf stop row: argmax by this work-group
-            const T* srow = (const T*)a.target_logits + ((int64_t)b * (N + 1) + stop_row) * V;
-            float best = -FLT_MAX;
-            int arg = 0x7fffffff;
-            for (int v = t; v < V; v += AC_THREADS) {
-              const float x = ldf(srow, v);
-              if (x > best) { best = x; arg = v; }
-            }
-            block_argmax(best, arg, red);
-            bonus = arg;
-          }
-        } else {
-          if (t == 0) {
-            int row = 0, n = 0;
-            for (;;) {
-              const int ch = ld_i(&rr[row].child);
-              if (ch < 0 || n >= SV_MAX_DEPTH) break;
-              si.path[n++] = ch;
-              row = ch + 1;
-            }
-            si.flag = (n << 16) | row;  // A and the stop row
-            s_hit = ld_i(&rr[row].token);
-          }
-          __syncthreads();
-          A = si.flag >> 16;
-          stop_row = si.flag & 0xffff;
-          bonus = s_hit;
+      // ---- the work-group that wrote the row result counts it; the last row of a sequence walks
+      if (done_by_me) {
+        mem_complete();  // this thread's row-result stores (if any) have completed
+        __syncthreads();
+        if (t == 0) {
+          const uint32_t old = add_u32(&ws.seqdone[b], 1u);
+          s_last = old + 1 == (uint32_t)si.nlive;
         }
         __syncthreads();
-        const int Dm = a.max_depth;
-        if (t == 0) {
-          a.accept_len[b] = A;
-          a.num_out[b] = A + 1;
-          a.stop_row[b] = stop_row;
-          a.status[b] = ld_u32(ws.err) ? SEQ_COOP_TIMEOUT : (si.bad_token ? SV_SEQ_TOKEN : 0);
-          st_u32(&ws.seqdone[b], 0u);  // every row of b has been counted: ready for the next call
+        if (s_last) {
+          // ----------------------------------------------------- walk of sequence b
+          int A = 0, stop_row = 0, bonus = 0;
+          RowRes* rr = ws.res + (int64_t)b * (N + 1);
+          if constexpr (MODE == SV_GREEDY) {
+            // match[i]: token equals its parent row's argmax; accepted: the whole root path matches
+            if (t < SV_MAX_W) s_match[t] = 0;
+            __syncthreads();
+            if (t < N && si.usable[t] && a.tokens[(int64_t)b * N + t] == ld_i(&rr[si.par[t] + 1].token))
+              atomicOr((unsigned long long*)&s_match[t >> 6], 1ull << (t & 63));
+            __syncthreads();
+            const int W = (N + 63) / 64;
+            int key = -1;
+            if (t < N && si.usable[t]) {
+              const uint64_t* arow = a.anc_bits + ((int64_t)b * N + t) * W;
+              bool ok = true;
+              for (int w = 0; w < W; ++w) ok &= (arow[w] & ~s_match[w]) == 0;
+              if (ok) key = (a.depth[(int64_t)b * N + t] << 9) | (511 - t);  // deepest, then lowest index
+            }
+            {
+              float kv = (float)key;
+              int ki = key;
+              block_argmax(kv, ki, red);
+              key = (int)kv;
+            }
+            if (key >= 0) {
+              A = key >> 9;
+              const int stop = 511 - (key & 511);
+              stop_row = stop + 1;
+              if (t == 0) {
+                int node = stop;
+                for (int k = A - 1; k >= 0; --k) { si.path[k] = node; node = si.par[node]; }
+              }
+            }
+            if (row_live(a, si, stop_row)) {
+              if (t == 0) s_hit = ld_i(&rr[stop_row].token);
+              __syncthreads();
+              bonus = s_hit;
+            } else {
+              // leaf stop row: argmax by this work-group
+              const T* srow = (const T*)a.target_logits + ((int64_t)b * (N + 1) + stop_row) * V;
+              float best = -FLT_MAX;
+              int arg = 0x7fffffff;
+              for (int v = t; v < V; v += AC_THREADS) {
+                const float x = ldf(srow, v);
+                if (x > best) { best = x; arg = v; }
+              }
+              block_argmax(best, arg, red);
+              bonus = arg;
+            }
+          } else {
+            if (t == 0) {
+              int row = 0, n = 0;
+              for (;;) {
+                const int ch = ld_i(&rr[row].child);
+                if (ch < 0 || n >= SV_MAX_DEPTH) break;
+                si.path[n++] = ch;
+                row = ch + 1;
+              }
+              si.flag = (n << 16) | row;  // A and the stop row
+              s_hit = ld_i(&rr[row].token);
+            }
+            __syncthreads();
+            A = si.flag >> 16;
+            stop_row = si.flag & 0xffff;
+            bonus = s_hit;
+          }
+          __syncthreads();
+          const int Dm = a.max_depth;
+          if (t == 0) {
+            a.accept_len[b] = A;
+            a.num_out[b] = A + 1;
+            a.stop_row[b] = stop_row;
+            a.status[b] = ld_u32(ws.err) ? SV_SEQ_TIMEOUT : (si.bad_token ? SV_SEQ_TOKEN : 0);
+            st_u32(&ws.seqdone[b], 0u);  // every row of b has been counted: ready for the next call
+          }
+          if (t < Dm) a.accept_rows[(int64_t)b * Dm + t] = t < A ? si.path[t] + 1 : 0;
+          if (t <= Dm)
+            a.out_tokens[(int64_t)b * (Dm + 1) + t] = t < A ? a.tokens[(int64_t)b * N + si.path[t]] : (t == A ? bonus : 0);
         }
-        if (t < Dm) a.accept_rows[(int64_t)b * Dm + t] = t < A ? si.path[t] + 1 : 0;
-        if (t <= Dm) a.out_tokens[(int64_t)b * (Dm + 1) + t] = t < A ? a.tokens[(int64_t)b * N + si.path[t]] : (t == A ? bonus : 0);
       }
     }
-    __syncthreads();
   }
 
-  // ---- leave every counter zeroed for the next call
+  // ---- leave every counter and exchange slot zeroed for the next call
+  __syncthreads();
   if (t == 0) {
     mem_complete();
+    int last = 1;
     if (G > 1) {
       const uint32_t old = add_u32(ws.gexit + grp, 1u);
-      if (old + 1 == (uint32_t)G) {  // every member of the group passed its last barrier
-        st_u32(bar, 0u);
-        st_u32(ws.gexit + grp, 0u);
-      }
+      last = old + 1 == (uint32_t)G;  // every member of the group passed its last exchange
+      if (last) st_u32(ws.gexit + grp, 0u);
     }
+    s_last = last;
+  }
+  __syncthreads();
+  if (s_last && xtag > 0)
+    for (int i = t; i < G * 2 * AC_XW; i += AC_THREADS) st_u64(&gslots[i / AC_XW].w[i % AC_XW], 0ull);
+  mem_complete();
+  __syncthreads();
+  if (t == 0) {
     const uint32_t done = add_u32(ws.err + 1, 1u);
     if (done + 1 == gridDim.x) {  // the whole grid has finished: clear the timeout flag
       st_u32(ws.err, 0u);
@@ -742,51 +752,28 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
   }
 }
 
-// occupancy-based size of the persistent grid (per device, cached)
-template <typename T, int MODE>
-int occupancy_of() {
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_accept<T, MODE>, AC_THREADS, 0) != hipSuccess) per_cu = 1;
-  return per_cu;
-}
-
-int resident_groups(int G, int dtype_bf16, int mode) {
-  static int cached[64][2][2] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  int& c = cached[dev][dtype_bf16][mode];
-  if (c == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 1;
-    const int per_cu = dtype_bf16 ? (mode ? occupancy_of<uint16_t, SV_STOCHASTIC>() : occupancy_of<uint16_t, SV_GREEDY>())
-                                  : (mode ? occupancy_of<float, SV_STOCHASTIC>() : occupancy_of<float, SV_GREEDY>());
-    c = cus * (per_cu > 0 ? per_cu : 1);
-    if (c < 1) c = 1;
-    if (c > AC_MAX_RESIDENT) c = AC_MAX_RESIDENT;
-  }
-  return c / G;
-}
-
-struct WsLayout {
-  size_t bar, gexit, seqdone, err, res, xg, total;
-};
-WsLayout ws_layout(const sv_accept_args& a) {
-  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  WsLayout l{};
-  size_t o = 0;
-  l.bar = o; o = up(o + AC_MAX_RESIDENT * 4);
-  l.gexit = o; o = up(o + AC_MAX_RESIDENT * 4);
-  l.seqdone = o; o = up(o + (size_t)a.B * 4);
-  l.err = o; o = up(o + 8);
-  l.res = o; o = up(o + (size_t)a.B * (a.N + 1) * sizeof(RowRes));
-  l.xg = o; o = up(o + (size_t)AC_MAX_RESIDENT * 2 * sizeof(Xchg));
-  l.total = o;
-  return l;
-}
-
 int groups_G(const sv_accept_args& a) {
   const int G = (a.V + AC_SLICE - 1) / AC_SLICE;
   return G < 1 ? 1 : G;
+}
+// one group per row, rounded up to a whole number of groups per XCD
+int64_t num_groups(const sv_accept_args& a) { return ((int64_t)a.B * (a.N + 1) + 7) / 8 * 8; }
+
+struct WsLayout {
+  size_t gexit, seqdone, err, res, xs, total;
+};
+WsLayout ws_layout(const sv_accept_args& a) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t NG = (size_t)num_groups(a), G = (size_t)groups_G(a);
+  WsLayout l{};
+  size_t o = 0;
+  l.gexit = o; o = up(o + NG * 4);
+  l.seqdone = o; o = up(o + (size_t)a.B * 4);
+  l.err = o; o = up(o + 8);
+  l.res = o; o = up(o + (size_t)a.B * (a.N + 1) * sizeof(RowRes));
+  l.xs = o; o = up(o + NG * G * 2 * sizeof(XSlot));
+  l.total = o;
+  return l;
 }
 
 }  // namespace
@@ -813,23 +800,18 @@ extern "C" sv_status sv_accept(const sv_accept_args* args, void* stream) {
   if (a.workspace_bytes < l.total || ((uintptr_t)a.workspace % 256)) return SV_ERR_INVALID_ARGUMENT;
   const int G = groups_G(a);
   if (G > AC_MAXG) return SV_ERR_UNSUPPORTED;
-  const int bf = a.logits_dtype == SV_BF16;
-  int NG = resident_groups(G, bf, a.mode == SV_STOCHASTIC);
-  const int64_t items = (int64_t)a.B * (a.N + 1);
-  if (NG > items) NG = (int)((items + 7) / 8 * 8);
-  NG = NG / 8 * 8;  // groups are placed per XCD
-  if (NG < 8) return SV_ERR_UNSUPPORTED;  // the groups do not fit on the device at once
+  const int64_t blocks = num_groups(a) * G;
+  if (blocks > 0x7fffffff) return SV_ERR_UNSUPPORTED;
   char* base = (char*)a.workspace;
   AccWs ws;
-  ws.bar = (uint32_t*)(base + l.bar);
   ws.gexit = (uint32_t*)(base + l.gexit);
   ws.seqdone = (uint32_t*)(base + l.seqdone);
   ws.err = (uint32_t*)(base + l.err);
   ws.res = (RowRes*)(base + l.res);
-  ws.xg = (Xchg*)(base + l.xg);
+  ws.xs = (XSlot*)(base + l.xs);
   hipStream_t st = (hipStream_t)stream;
-  const dim3 grid((unsigned)(NG * G));
-  if (bf) {
+  const dim3 grid((unsigned)blocks);
+  if (a.logits_dtype == SV_BF16) {
     if (a.mode == SV_STOCHASTIC) hipLaunchKernelGGL((k_accept<uint16_t, SV_STOCHASTIC>), grid, dim3(AC_THREADS), 0, st, a, G, ws);
     else hipLaunchKernelGGL((k_accept<uint16_t, SV_GREEDY>), grid, dim3(AC_THREADS), 0, st, a, G, ws);
   } else {
