@@ -477,19 +477,24 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
         zq = block_sum(zq, red);
         exchange(gslots, G, rank, ++xtag, 6, xv, ws.err, __float_as_uint(mp), __float_as_uint(mq), dlo(zp), dhi(zp),
                  dlo(zq), dhi(zq));
-        // global statistics, merged in rank order by every work-group alike
-        float Mp = __uint_as_float(xv[0][0]), Mq = __uint_as_float(xv[0][1]);
-        for (int k = 1; k < G; ++k) {
-          Mp = fmaxf(Mp, __uint_as_float(xv[k][0]));
-          Mq = fmaxf(Mq, __uint_as_float(xv[k][1]));
+        // global statistics: lane k of every wave takes member k's partials (G <= 64); the
+        // butterfly reductions give every lane, wave and member the same values
+        double Zp, Zq, fp, fq;
+        float Mp, Mq;
+        {
+          const bool on = lane < G;
+          const int k = on ? lane : 0;
+          const float mpk = on ? __uint_as_float(xv[k][0]) : -FLT_MAX;
+          const float mqk = on ? __uint_as_float(xv[k][1]) : -FLT_MAX;
+          Mp = wave_maxf(mpk);
+          Mq = wave_maxf(mqk);
+          const double sp = on ? exp2((double)(mpk - Mp) * (double)l2T) : 0.0;  // member k's scale
+          const double sq = on && need_q ? exp2((double)(mqk - Mq) * (double)l2T) : 0.0;
+          Zp = wave_sumd(on ? dof(xv[k][2], xv[k][3]) * sp : 0.0);
+          Zq = wave_sumd(on && need_q ? dof(xv[k][4], xv[k][5]) * sq : 0.0);
+          fp = __shfl(sp, rank) / Zp;                   // p(v) = ep(v) * fp on this slice
+          fq = need_q ? __shfl(sq, rank) / Zq : 0.0;
         }
-        double Zp = 0.0, Zq = 0.0;
-        for (int k = 0; k < G; ++k) {
-          Zp += dof(xv[k][2], xv[k][3]) * exp2((double)(__uint_as_float(xv[k][0]) - Mp) * (double)l2T);
-          if (need_q) Zq += dof(xv[k][4], xv[k][5]) * exp2((double)(__uint_as_float(xv[k][1]) - Mq) * (double)l2T);
-        }
-        const double fp = exp2((double)(mp - Mp) * (double)l2T) / Zp;  // p(v) = ep(v) * fp on this slice
-        const double fq = need_q ? exp2((double)(mq - Mq) * (double)l2T) / Zq : 0.0;
         // residual weight of one entry in units of fp: max(0, ep - kappa eq); kappa = 0 is p itself
         auto wgt = [&](int i, float kappa) -> float {
           return kappa == 0.f ? ep[i] : fmaxf(fmaf(-kappa, eq[i], ep[i]), 0.f);
@@ -553,18 +558,10 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
             __syncthreads();
             const float* mine = s_w + wpad(t * AC_CT);
             double tsum = 0.0;
-            int lastpos = -1;  // highest id of this thread with a positive weight (ids >= V weigh 0)
 #pragma unroll
             for (int j = 0; j < AC_CT; j += 8) {
               const float4 x0 = *(const float4*)(mine + j), x1 = *(const float4*)(mine + j + 4);
-              const float w8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-              float g = 0.f;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                g += w8[e];
-                lastpos = w8[e] > 0.f ? s0 + t * AC_CT + j + e : lastpos;
-              }
-              tsum += (double)g;
+              tsum += (double)(((((((x0.x + x0.y) + x0.z) + x0.w) + x1.x) + x1.y) + x1.z) + x1.w);
             }
             double incl = wave_scand(tsum, lane);
             if (lane == 63) red.d[wv] = incl;
@@ -601,9 +598,11 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
               const double lthr = (thr - before) / fp;  // threshold in this slice's units
               if (t == 0) { s_first = 0x7fffffff; s_lpos = -1; }
               __syncthreads();
-              if (lastpos >= 0) atomicMax(&s_lpos, lastpos);
-              if (incl > lthr) atomicMin(&s_first, t);  // the first thread whose prefix exceeds it
-              red.scan1[t] = incl - tsum;                // exclusive prefix of each thread
+              {  // the first thread whose inclusive prefix exceeds the threshold: one atomic per wave
+                const uint64_t over = __ballot(incl > lthr);
+                if (over && lane == 0) atomicMin(&s_first, wv * 64 + __ffsll((long long)over) - 1);
+              }
+              red.scan1[t] = incl - tsum;  // exclusive prefix of each thread
               __syncthreads();
               const int h = s_first;
               if (h != 0x7fffffff) {
@@ -621,10 +620,17 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
                     st_i(&ws.res[item].token, pick);
                   }
                 }
-              } else if (t == 0) {  // rounding left the threshold unreached
-                const int pick = s_lpos >= 0 ? s_lpos : min(s0 + AC_SLICE, V) - 1;
-                st_i(&ws.res[item].child, -1);
-                st_i(&ws.res[item].token, pick);
+              } else {  // rounding left the threshold unreached: the highest id with a positive weight
+                int lp = -1;
+                for (int j = 0; j < AC_CT; ++j) lp = mine[j] > 0.f ? s0 + t * AC_CT + j : lp;
+                for (int o = 32; o > 0; o >>= 1) lp = max(lp, __shfl_xor(lp, o));
+                if (lane == 0) atomicMax(&s_lpos, lp);
+                __syncthreads();
+                if (t == 0) {
+                  const int pick = s_lpos >= 0 ? s_lpos : min(s0 + AC_SLICE, V) - 1;
+                  st_i(&ws.res[item].child, -1);
+                  st_i(&ws.res[item].token, pick);
+                }
               }
               done_by_me = 1;
             }
@@ -648,10 +654,11 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
           RowRes* rr = ws.res + (int64_t)b * (N + 1);
           if constexpr (MODE == SV_GREEDY) {
             // match[i]: token equals its parent row's argmax; accepted: the whole root path matches
-            if (t < SV_MAX_W) s_match[t] = 0;
-            __syncthreads();
-            if (t < N && si.usable[t] && a.tokens[(int64_t)b * N + t] == ld_i(&rr[si.par[t] + 1].token))
-              atomicOr((unsigned long long*)&s_match[t >> 6], 1ull << (t & 63));
+            {  // wave w holds nodes 64 w .. 64 w + 63: its ballot is bitset word w
+              const uint64_t mb =
+                  __ballot(t < N && si.usable[t] && a.tokens[(int64_t)b * N + t] == ld_i(&rr[si.par[t] + 1].token));
+              if (lane == 0 && (t >> 6) < SV_MAX_W) s_match[t >> 6] = mb;
+            }
             __syncthreads();
             const int W = (N + 63) / 64;
             int key = -1;
