@@ -449,7 +449,10 @@ __global__ void __launch_bounds__(AT_THREADS, 1) k_attn_mfma(sv_attn_args a, Att
   }
 }
 
-// merge split partials: one wave per output row (b, node, head)
+// merge split partials: one wave per output row (b, node, head).  Every load
+// of a row is issued before any is used (no data-dependent branch between
+// them), so the merge costs one memory round trip, not one per split.
+constexpr int AT_MAX_SPLIT_REG = 16;  // splits merged from registers; more are streamed
 template <int D>
 __global__ void __launch_bounds__(256) k_attn_combine(sv_attn_args a, AttnPlan p) {
   const int lane = threadIdx.x & 63;
@@ -463,29 +466,47 @@ __global__ void __launch_bounds__(256) k_attn_combine(sv_attn_args a, AttnPlan p
   const int m = node * p.G + (h % p.G);
   const int qtile = m / p.QT, ql = m % p.QT;
   const int64_t unit = ((int64_t)b * a.Hkv + g) * p.qtiles + qtile;
-  float mx = -INFINITY;
-  for (int s = 0; s < p.nsplit; ++s) mx = fmaxf(mx, p.mlpart[((unit * p.nsplit + s) * p.QT + ql) * 2]);
   constexpr int EPL = D / 64;
+  // lane s < nsplit holds split s's (m, l)
+  const int ns = p.nsplit;
+  float ms = -INFINITY, ls = 0.f;
+  if (lane < ns) {
+    const float2 ml = *(const float2*)(p.mlpart + ((unit * ns + lane) * p.QT + ql) * 2);
+    ms = ml.x;
+    ls = ml.y;
+  }
+  float mx = ms;
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - mx);  // weight of split `lane`
+  float l = f * ls;
+  for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  float l = 0.f;
-  if (mx != -INFINITY) {
-    for (int s = 0; s < p.nsplit; ++s) {
-      const int64_t pidx = (unit * p.nsplit + s) * p.QT + ql;
-      const float ms = p.mlpart[pidx * 2 + 0];
-      if (ms == -INFINITY) continue;
-      const float f = exp2f(ms - mx);
-      l += f * p.mlpart[pidx * 2 + 1];
-      const float* orow = p.opart + pidx * D;
+  for (int s0 = 0; s0 < ns; s0 += AT_MAX_SPLIT_REG) {
+    float part[AT_MAX_SPLIT_REG][EPL];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] += f * orow[lane * EPL + e];
+    for (int k = 0; k < AT_MAX_SPLIT_REG; ++k) {
+      const int s = s0 + k;
+      const float* orow = p.opart + ((unit * ns + (s < ns ? s : 0)) * p.QT + ql) * D + lane * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) part[k][e] = s < ns ? orow[e] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < AT_MAX_SPLIT_REG; ++k) {
+      const float fk = __shfl(f, (s0 + k) & 63);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] += fk * part[k][e];
     }
   }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float inv = (mx != -INFINITY && l > 0.f) ? 1.f / l : 0.f;
   uint16_t* orow = (uint16_t*)a.out + rowid * D;
+  if (EPL == 2) {
+    *(uint32_t*)(orow + lane * 2) = f32_to_bf16_bits(acc[0] * inv) | ((uint32_t)f32_to_bf16_bits(acc[EPL - 1] * inv) << 16);
+  } else {
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) orow[lane * EPL + e] = f32_to_bf16_bits(acc[e] * inv);
+    for (int e = 0; e < EPL; ++e) orow[lane * EPL + e] = f32_to_bf16_bits(acc[e] * inv);
+  }
 }
 
 // ------------------------------------------------------------------ VALU path
@@ -629,6 +650,7 @@ AttnPlan make_plan(const sv_attn_args& a) {
   int nsplit = (int)((TARGET_WG + units - 1) / units);
   const int max_split = tiles_cap / AT_WAVES > 1 ? tiles_cap / AT_WAVES : 1;
   if (nsplit > max_split) nsplit = max_split;
+  if (nsplit > 64) nsplit = 64;  // the combine keeps one split per lane
   if (nsplit < 1) nsplit = 1;
   const int tiles_per = (tiles_cap + nsplit - 1) / nsplit;
   p.chunk = (tiles_per > 0 ? tiles_per : 1) * KT;
