@@ -9,18 +9,20 @@
 // mask-free and only the N x N tree block reads the per-node ancestor bitsets.
 //
 // Kernels
-//  k_attn_mfma<D, QB>  bf16, the hot path.  A work-group owns one KV head g of
-//     one sequence, a tile of QT = 32*QB query rows (row m = node*G + head in
-//     group, so the G query heads that share a KV head form one dense
-//     contraction of M = N*G rows), and a contiguous key range (a split of the
-//     prefix; the last split also takes the tree block).  Its 4 waves take
-//     32-key tiles round-robin; each wave stages its tile through its own LDS
-//     slice (K row-major, V transposed), computes S^T = K Q^T and O^T += V^T P^T
-//     with v_mfma_f32_32x32x16_bf16, and keeps the online-softmax state per
-//     lane (each lane owns one query column).  The 4 waves merge in LDS; a
-//     single split writes bf16 output directly, several splits write fp32
-//     partials (m, l, O) merged by k_attn_combine.
-//  k_attn_valu<T>  generic fp32 / bf16 path (any D <= 128), scalar FMA.
+//  k_attn_mfma<D>  bf16, the hot path.  A work-group owns one KV head g of one
+//     sequence, a tile of up to 256 query rows (row m = node*G + head in group,
+//     so the G query heads that share a KV head form one dense contraction of
+//     M = N*G rows) and a contiguous key range (a split of the prefix; the last
+//     split also takes the tree block).  Each of its 4 waves owns 64 query rows
+//     for the whole key range, so no merge between waves is needed.  64-key
+//     K/V tiles are loaded once per work-group (two tiles in flight in
+//     registers, two LDS buffers), S^T = K Q^T and O^T += V^T P^T run on
+//     v_mfma_f32_32x32x16_bf16, V^T fragments come straight from row-major V
+//     through transposing LDS reads, and the online-softmax state is per lane
+//     (each lane owns one query column).  A single split writes bf16 output
+//     directly; several splits write fp32 partials (m, l, O) merged by
+//     k_attn_combine.
+//  k_attn_valu<T>  generic fp32 / bf16 path, scalar FMA.
 #include <float.h>
 #include <math.h>
 
@@ -30,7 +32,13 @@ namespace {
 
 constexpr int AT_WAVES = 4;
 constexpr int AT_THREADS = 64 * AT_WAVES;
-constexpr int KT = 32;  // keys per tile
+constexpr int MF_WAVES = 8;                // waves of the MFMA kernel (two per SIMD)
+constexpr int MF_THREADS = 64 * MF_WAVES;
+constexpr int MF_QB = 1;                   // 32-row query blocks per wave
+constexpr int KT = 64;  // keys per tile
+#ifndef SV_ATTN_MIN_SPLIT_TILES
+#define SV_ATTN_MIN_SPLIT_TILES 4  // a prefix split covers at least this many tiles
+#endif
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int TARGET_WG = 256;
 
@@ -67,46 +75,91 @@ __device__ void write_seq_status(const sv_attn_args& a, int b, int cap) {
 }
 
 // ------------------------------------------------------------------ MFMA path
+// One 64-key tile in LDS: K rows then V rows, row-major without padding.  The
+// 16-byte chunks of row r are stored XOR-swizzled (global chunk c sits in slot
+// c ^ swz(r)), which keeps both the 16-byte K fragment reads and the 8-byte
+// transposing V reads free of bank conflicts.  Tiles are written by direct
+// global -> LDS loads (each load instruction of a wave fills 1 KB: lane l's 16
+// bytes land at byte 16 l), so staging a tile costs no registers.
 template <int D>
-struct Lds {
-  static constexpr int KSTR = D + 8;   // K row stride (bf16 elements), 16-byte padding
-  static constexpr int VSTR = KT + 4;  // V^T row stride (bf16 elements), 8-byte padding
-  static constexpr int K_ELEMS = KT * KSTR;
-  static constexpr int V_ELEMS = D * VSTR;
-  static constexpr int WAVE_ELEMS = K_ELEMS + V_ELEMS;
-  static constexpr int STAGE_BYTES = AT_WAVES * WAVE_ELEMS * 2;
+struct Tile {
+  static constexpr int KT = 64;
+  static constexpr int CPR = D / 8;                   // 16-byte chunks per row
+  static constexpr int ROWB = D * 2;                  // bytes per row
+  static constexpr int RPI = 64 / CPR;                // rows filled by one load instruction
+  static constexpr int IPW = KT / RPI / MF_WAVES;     // load instructions per wave per tensor
+  static constexpr int RPW = RPI * IPW;               // rows filled by one wave
+  static constexpr int TBYTES = KT * ROWB;            // one tensor of the tile
+  static constexpr int BUF = 2 * TBYTES;              // K and V
+  static constexpr int QSTR = D + 8;                  // Q row stride in LDS (16-byte pad)
+  static constexpr int QROWS = 32 * MF_QB * MF_WAVES;  // query rows per work-group
+  __device__ static __forceinline__ int swz(int r) {
+    return CPR == 16 ? (((r << 1) & 14) | ((r >> 3) & 1)) : ((r & 6) | ((r >> 3) & 1));
+  }
 };
 
-__device__ __forceinline__ uint32_t lo16(uint32_t x) { return x & 0xffffu; }
-__device__ __forceinline__ uint32_t hi16(uint32_t x) { return x >> 16; }
+typedef __attribute__((address_space(3))) void lds_void;
 
-// pack element e (0..7) of four 8-element bf16 vectors into 4 consecutive bf16
-__device__ __forceinline__ uint2 pack_col(const uint4& a, const uint4& b, const uint4& c, const uint4& d, int e) {
-  const int comp = e >> 1;
-  const uint32_t xa = comp == 0 ? a.x : comp == 1 ? a.y : comp == 2 ? a.z : a.w;
-  const uint32_t xb = comp == 0 ? b.x : comp == 1 ? b.y : comp == 2 ? b.z : b.w;
-  const uint32_t xc = comp == 0 ? c.x : comp == 1 ? c.y : comp == 2 ? c.z : c.w;
-  const uint32_t xd = comp == 0 ? d.x : comp == 1 ? d.y : comp == 2 ? d.z : d.w;
-  if (e & 1) return make_uint2(hi16(xa) | (xb & 0xffff0000u), hi16(xc) | (xd & 0xffff0000u));
-  return make_uint2(lo16(xa) | (xb << 16), lo16(xc) | (xd << 16));
+// 32-bit LDS address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// Transposing 8-byte LDS reads (ds_read_b64_tr_b16) for one 16-key step: in
+// every 16-lane group, lane 4q+e receives element e of the 8-byte pieces
+// addressed by lanes q, 4+q, 8+q and 12+q.  Written as inline assembly with an
+// explicit LDS wait: through the builtin, the compiler cannot tell these reads
+// from the tile buffer that is still being filled by direct global->LDS loads
+// and would wait for those loads as well.
+template <int NB>
+__device__ __forceinline__ void read_tr(uint2 (&lo)[NB], uint2 (&hi)[NB], const uint32_t (&alo)[NB],
+                                        const uint32_t (&ahi)[NB]);
+template <>
+__device__ __forceinline__ void read_tr<4>(uint2 (&lo)[4], uint2 (&hi)[4], const uint32_t (&alo)[4],
+                                           const uint32_t (&ahi)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\tds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\tds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\tds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]), "=&v"(lo[3]), "=&v"(hi[3])
+      : "v"(alo[0]), "v"(ahi[0]), "v"(alo[1]), "v"(ahi[1]), "v"(alo[2]), "v"(ahi[2]), "v"(alo[3]), "v"(ahi[3])
+      : "memory");
+}
+template <>
+__device__ __forceinline__ void read_tr<2>(uint2 (&lo)[2], uint2 (&hi)[2], const uint32_t (&alo)[2],
+                                           const uint32_t (&ahi)[2]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\tds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\tds_read_b64_tr_b16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1])
+      : "v"(alo[0]), "v"(ahi[0]), "v"(alo[1]), "v"(ahi[1])
+      : "memory");
 }
 
-template <int D, int QB>
-__global__ void __launch_bounds__(AT_THREADS, 1) k_attn_mfma(sv_attn_args a, AttnPlan p) {
-  using LD = Lds<D>;
-  constexpr int DS = D / 16;                   // 16-wide k-steps of S = K Q^T
-  constexpr int DB = D / 32;                   // 32-wide d-blocks of O^T
-  constexpr int KPIECES = KT * (D / 8) / 64;   // 16-byte K pieces per lane per tile
-  constexpr int VITEMS = (KT / 4) * (D / 8) / 64;  // (key quad, 8-d chunk) items per lane per tile
-  constexpr int MERGE_BYTES = (2 * QB * DB * 16 * 64 + 2 * QB * 2 * 64) * 4;
-  constexpr int SMEM_BYTES = LD::STAGE_BYTES > MERGE_BYTES ? LD::STAGE_BYTES : MERGE_BYTES;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM_BYTES];
+template <int D>
+__global__ void __launch_bounds__(MF_THREADS, 2) k_attn_mfma(sv_attn_args a, AttnPlan p) {
+  using TL = Tile<D>;
+  constexpr int QB = MF_QB;             // 32-row query blocks per wave
+  constexpr int KT64 = TL::KT;
+  constexpr int DS = D / 16;            // 16-wide k-steps of S = K Q^T
+  constexpr int DB = D / 32;            // 32-wide d-blocks of O^T
+  constexpr uint32_t ROWB = TL::ROWB;
+  // two tile buffers as separate arrays: the compiler can then tell that the loads
+  // streaming into one never alias the reads of the other, and does not wait on them
+  __shared__ __attribute__((aligned(1024))) unsigned char kvA[TL::BUF];
+  __shared__ __attribute__((aligned(1024))) unsigned char kvB[TL::BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t qs[TL::QROWS * TL::QSTR];  // the work-group's query rows
 
-  const int lane = threadIdx.x & 63;
-  // the wave index is uniform across the wave: keep tile bookkeeping in scalar registers
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lq = lane & 31;  // query column / row index inside a 32-block
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform wave index
+  const int lq = lane & 31;  // query column / key row inside a 32-block
   const int hf = lane >> 5;  // which half of the k dimension this lane feeds
+  // the two waves sharing a SIMD get different issue priorities, so that one runs ahead
+  // of the other inside each tile and its softmax overlaps the other's MFMAs
+  if (w < MF_WAVES / 2) __builtin_amdgcn_s_setprio(1);
 
   // XCD-aware block order: consecutive logical ids land on the same XCD
   const int nb = gridDim.x;
@@ -123,10 +176,14 @@ __global__ void __launch_bounds__(AT_THREADS, 1) k_attn_mfma(sv_attn_args a, Att
   const int L = clamp_len(a.prefix_len[b], p.cap);
   const int k0 = split * p.chunk;
   const int k1 = min(k0 + p.chunk, L);
-  const int ntp = k1 > k0 ? (k1 - k0 + KT - 1) / KT : 0;
+  const int ntp = k1 > k0 ? (k1 - k0 + KT64 - 1) / KT64 : 0;
   const bool last = split == p.nsplit - 1;
   const int ntt = last ? p.ntt : 0;
   const int ntiles = ntp + ntt;
+
+  // rows of this wave: m = qtile * QT + w * 32 QB + qb * 32 + lq
+  const int mw = qtile * p.QT + w * 32 * QB;
+  const bool active = mw < p.M;  // uniform: the wave has at least one valid query row
 
   const __bf16* qg = (const __bf16*)a.q;
   const uint16_t* kc = (const uint16_t*)a.k_cache;
@@ -134,55 +191,9 @@ __global__ void __launch_bounds__(AT_THREADS, 1) k_attn_mfma(sv_attn_args a, Att
   const uint16_t* kt = (const uint16_t*)a.k_tree;
   const uint16_t* vt = (const uint16_t*)a.v_tree;
 
-  // ---- Q fragments (B operand of S^T = K Q^T): lane holds query column lq, d = 16*ds + 8*hf .. +7
-  sv_bf16x8 qf[QB][DS];
-  uint64_t anc[QB][SV_MAX_W];
-  int qnode[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int m = qtile * p.QT + qb * 32 + lq;
-    const bool valid = m < p.M;
-    const int node = valid ? m / G : 0;
-    const int h = g * G + (valid ? m % G : 0);
-    qnode[qb] = node;
-    const __bf16* qrow = qg + (((int64_t)b * N + node) * Hq + h) * D;
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      if (valid) {
-        qf[qb][ds] = *(const sv_bf16x8*)(qrow + ds * 16 + 8 * hf);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[qb][ds][e] = (__bf16)0.0f;
-      }
-    }
-#pragma unroll
-    for (int ww = 0; ww < SV_MAX_W; ++ww)
-      anc[qb][ww] = (ntt > 0 && valid && ww < p.W) ? a.anc_bits[((int64_t)b * N + node) * p.W + ww] : 0ull;
-  }
-
-  sv_f32x16 oacc[QB][DB];
-  float mrun[QB], lrun[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    mrun[qb] = -INFINITY;
-    lrun[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.f;
-  }
-
-  uint16_t* Ks = (uint16_t*)smem + w * LD::WAVE_ELEMS;
-  uint16_t* VTs = Ks + LD::K_ELEMS;
-
-  // ---- global -> register staging of one 32-key tile through buffer loads.
-  // One buffer resource per source keeps the tile base in scalar registers;
-  // lanes only add precomputed 32-bit offsets.  Keys past the valid range are
-  // clamped onto the last valid key of the tile (finite data, masked out of
-  // the softmax), so no load ever leaves the tensor.
-  constexpr int CPR = D / 8;            // 16-byte chunks per row
-  constexpr int QPI = 64 / CPR;         // V key-quads covered by one load instruction
-  constexpr uint32_t ROWB = D * 2;      // bytes per K/V row
+  // ---- tile loads: wave w fills rows RPW w .. RPW w + RPW - 1 of K and of V.  Keys past
+  // the valid range are clamped onto the last valid key of the tile (finite data,
+  // masked out of the softmax), so no load ever leaves the tensor.
   const int64_t plane = (int64_t)b * a.Hkv + g;
   __amdgpu_buffer_rsrc_t rk, rv;
   const __amdgpu_buffer_rsrc_t rkt = __builtin_amdgcn_make_buffer_rsrc(
@@ -196,147 +207,171 @@ __global__ void __launch_bounds__(AT_THREADS, 1) k_attn_mfma(sv_attn_args a, Att
     rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + plane * a.Lcap * D), 0, (int)(a.Lcap * ROWB), 0x00020000);
     rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + plane * a.Lcap * D), 0, (int)(a.Lcap * ROWB), 0x00020000);
   }
-  // lane-constant key index and chunk of every load
-  int kkey[KPIECES], kch[KPIECES];
-#pragma unroll
-  for (int it = 0; it < KPIECES; ++it) {
-    kkey[it] = (lane + 64 * it) / CPR;
-    kch[it] = (lane + 64 * it) % CPR;
-  }
-  const int vquad0 = lane % QPI, vch = lane / QPI;
-
-  uint4 kreg[KPIECES];
-  uint4 vreg[VITEMS][4];
-  auto load_tile = [&](int tile) {
+  auto load_tile = [&](int tile, unsigned char* kb) {
     const bool tree = tile >= ntp;
-    // last valid key index inside this tile (wave-uniform)
     int klast;
-    uint32_t offA = 0, offB = 0, soff = 0;
+    uint32_t soff = 0;
     if (tree) {
-      const int t0 = (tile - ntp) * KT;
-      klast = min(KT, N - t0) - 1;
+      const int t0 = (tile - ntp) * KT64;
+      klast = min(KT64, N - t0) - 1;
       soff = (uint32_t)t0 * ROWB;
     } else {
-      const int j0 = k0 + tile * KT;
-      klast = min(KT, k1 - j0) - 1;
+      const int j0 = k0 + tile * KT64;
+      klast = min(KT64, k1 - j0) - 1;
       if (a.paged) {
-        // the tile spans two 16-token blocks; a block wholly past the end reuses the first
-        int idA = a.block_table[(int64_t)b * a.max_blocks + j0 / 16];
-        int idB = klast >= 16 ? a.block_table[(int64_t)b * a.max_blocks + j0 / 16 + 1] : idA;
-        idA = (idA < 0 || idA >= a.num_blocks) ? 0 : idA;
-        idB = (idB < 0 || idB >= a.num_blocks) ? 0 : idB;
-        offA = (uint32_t)(((int64_t)idA * a.Hkv + g) * 16) * ROWB;
-        offB = (uint32_t)(((int64_t)idB * a.Hkv + g) * 16) * ROWB;
+        // the wave's rows lie in one 16-token block (RPW divides 16); past the end the
+        // clamped key min(r, klast) = klast, so its block is the one used
+        const int blk = (j0 + min(TL::RPW * w, klast)) / 16;
+        int id = __builtin_amdgcn_readfirstlane(a.block_table[(int64_t)b * a.max_blocks + blk]);
+        id = (id < 0 || id >= a.num_blocks) ? 0 : id;
+        soff = (uint32_t)(((int64_t)id * a.Hkv + g) * 16) * ROWB;
       } else {
         soff = (uint32_t)j0 * ROWB;
       }
     }
     const bool paged_tile = !tree && a.paged;
-    auto voffset = [&](int key, int ch) -> uint32_t {
-      const int k = min(key, klast);
-      if (paged_tile) return (k >= 16 ? offB : offA) + (uint32_t)(k & 15) * ROWB + ch * 16;
-      return (uint32_t)k * ROWB + ch * 16;
-    };
     const __amdgpu_buffer_rsrc_t rK = tree ? rkt : rk;
     const __amdgpu_buffer_rsrc_t rV = tree ? rvt : rv;
 #pragma unroll
-    for (int it = 0; it < KPIECES; ++it)
-      kreg[it] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rK, voffset(kkey[it], kch[it]), soff, 0));
-#pragma unroll
-    for (int it = 0; it < VITEMS; ++it) {
-      const int quad = vquad0 + QPI * it;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        vreg[it][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rV, voffset(quad * 4 + kk, vch), soff, 0));
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int it = 0; it < KPIECES; ++it) *(uint4*)(Ks + kkey[it] * LD::KSTR + kch[it] * 8) = kreg[it];
-#pragma unroll
-    for (int it = 0; it < VITEMS; ++it) {
-      const int quad = vquad0 + QPI * it;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *(uint2*)(VTs + (vch * 8 + e) * LD::VSTR + quad * 4) =
-            pack_col(vreg[it][0], vreg[it][1], vreg[it][2], vreg[it][3], e);
+    for (int it = 0; it < TL::IPW; ++it) {
+      const int n = w * TL::IPW + it;                    // 1-KB piece of the tile (uniform)
+      const int r = n * TL::RPI + lane / TL::CPR;        // row this lane fills
+      const int c = (lane % TL::CPR) ^ TL::swz(r);       // global chunk stored in its slot
+      const int key = min(r, klast);
+      const uint32_t off = (uint32_t)((paged_tile ? (key & 15) : key) * ROWB + c * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_void*)(kb + n * 1024), 16, off, soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_void*)(kb + TL::TBYTES + n * 1024), 16, off, soff, 0, 0);
     }
   };
 
-  int tile = w;
-  if (tile < ntiles) load_tile(tile);
-  for (; tile < ntiles; tile += AT_WAVES) {
-    store_tile();
+  if (0 < ntiles) load_tile(0, kvA);
+
+  // ---- the work-group's query rows into LDS (rows past M are zero); the B operand
+  // of S^T = K Q^T for lane (lq, hf) and k-step ds is Q row lq, d = 16*ds + 8*hf .. +7
+  for (int c = t; c < TL::QROWS * TL::CPR; c += MF_THREADS) {
+    const int row = c / TL::CPR, cc = c % TL::CPR;
+    const int m = qtile * p.QT + row;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (m < p.M) {
+      const int node = m / G, h = g * G + m % G;
+      v = *(const uint4*)(qg + (((int64_t)b * N + node) * Hq + h) * D + cc * 8);
+    }
+    *(uint4*)(qs + row * TL::QSTR + cc * 8) = v;
+  }
+  int qnode[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int m = mw + qb * 32 + lq;
+    qnode[qb] = m < p.M ? m / G : -1;
+  }
+  const uint16_t* qw = qs + (w * 32 * QB + lq) * TL::QSTR + 8 * hf;  // this lane's Q row in LDS
+
+  sv_f32x16 oacc[QB][DB];
+  float mrun[QB], lrun[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    mrun[qb] = -INFINITY;
+    lrun[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.f;
+  }
+
+  // lane-constant parts of the LDS fragment reads
+  const int k_off = lq * ROWB;                       // K row lq of a 32-key block (+ 32 kb rows)
+  const int k_swz = TL::swz(lq);
+  // transposing V reads: source lane (16 u + 4 j + q) addresses row 4 (u / 2) + j (+ 8 for
+  // the upper half) at element column 16 (u % 2) + 4 q, i.e. chunk 2 (u % 2) + q / 2, half q % 2
+  const int tr_row = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tr_half = (lane & 1) * 8;
+  const int tr_swz_lo = TL::swz(tr_row), tr_swz_hi = TL::swz(tr_row + 8);
+
+  auto compute = [&](int tile, const unsigned char* Kb) {
+    const unsigned char* Vb = Kb + TL::TBYTES;
     const bool tree = tile >= ntp;
-    const int j0 = k0 + tile * KT;
-    const int t0 = (tile - ntp) * KT;
-    const int nxt = tile + AT_WAVES;
-    if (nxt < ntiles) load_tile(nxt);
-    wave_lds_sync();
+    const int j0 = k0 + tile * KT64;
+    const int t0 = (tile - ntp) * KT64;
 
-    // ---- S^T = K Q^T
-    sv_f32x16 sacc[QB];
+    // ---- S^T = K Q^T for two 32-key blocks
+    sv_f32x16 sacc[QB][2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[qb][r] = 0.f;
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[qb][kb][r] = 0.f;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
-      const sv_bf16x8 kf = *(const sv_bf16x8*)(Ks + lq * LD::KSTR + ds * 16 + 8 * hf);
+      sv_bf16x8 qf[QB];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ds], sacc[qb], 0, 0, 0);
+      for (int qb = 0; qb < QB; ++qb) qf[qb] = *(const sv_bf16x8*)(qw + qb * 32 * TL::QSTR + ds * 16);
+      const int kslot = ((2 * ds + hf) ^ k_swz) * 16;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const sv_bf16x8 kf = *(const sv_bf16x8*)(Kb + kb * 32 * ROWB + k_off + kslot);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb], sacc[qb][kb], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // fragment reads stay next to their MFMAs (register pressure)
     }
 
-    // ---- masks + online softmax (lane owns query column lq; keys 8*(r/4) + 4*hf + r%4)
-    // Masks are needed only on the partial last prefix tile and on tree tiles;
-    // both conditions are wave-uniform.
-    const bool full = !tree && (j0 + KT <= k1);
-    sv_bf16x8 pf[QB][2];
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- masks + online softmax (lane owns query column lq; keys 32 kb + 8 (r/4) + 4 hf + r%4)
+    const bool full = !tree && (j0 + KT64 <= k1);
+    sv_bf16x8 pf[QB][2][2];
     bool moved = false;
     float alpha[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float s[16];
-      if (full) {
+      // scores stay unscaled here; the scale (times log2 e) is folded into the exponent
+      if (!full && !tree) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = sacc[qb][r] * p.cscale;
-      } else if (!tree) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = 8 * (r >> 2) + 4 * hf + (r & 3);
-          s[r] = (j0 + kk < k1) ? sacc[qb][r] * p.cscale : -INFINITY;
-        }
-      } else {
-        const int wi = t0 >> 6;  // uniform: one 64-bit mask word covers the tile
-        const uint64_t aw = wi == 0 ? anc[qb][0] : wi == 1 ? anc[qb][1] : wi == 2 ? anc[qb][2] : anc[qb][3];
+          for (int r = 0; r < 16; ++r) {
+            const int kk = 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (j0 + kk >= k1) sacc[qb][kb][r] = -INFINITY;
+          }
+      } else if (tree) {
+        const int wi = t0 >> 6;  // uniform: the tile is one 64-bit mask word of the query node's bitset
+        const uint64_t aw = qnode[qb] >= 0 ? a.anc_bits[((int64_t)b * N + qnode[qb]) * p.W + wi] : 0ull;
+        const uint32_t a_lo = (uint32_t)aw, a_hi = (uint32_t)(aw >> 32);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = t0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const bool keep = (t < N) & (((aw >> (t & 63)) & 1ull) != 0);
-          s[r] = keep ? sacc[qb][r] * p.cscale : -INFINITY;
-        }
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kk = 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+            const uint32_t word = kb == 0 ? a_lo : a_hi;
+            const bool keep = (t0 + kk < N) & (((word >> (kk & 31)) & 1u) != 0);
+            if (!keep) sacc[qb][kb][r] = -INFINITY;
+          }
       }
-      float mt = s[0];
+      float mt = sacc[qb][0][0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[qb][kb][r]);
       mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mnew = fmaxf(mrun[qb], mt);
-      const float msafe = mnew == -INFINITY ? 0.f : mnew;  // nothing visible yet: all weights stay 0
-      alpha[qb] = __builtin_amdgcn_exp2f(mrun[qb] - msafe);
+      const float mnew = fmaxf(mrun[qb], mt);  // running maximum of the unscaled scores
+      const float ms = mnew == -INFINITY ? 0.f : mnew * p.cscale;  // nothing visible yet: weights stay 0
+      alpha[qb] = __builtin_amdgcn_exp2f(mrun[qb] * p.cscale - ms);
       moved |= mnew != mrun[qb];
       float psum = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = __builtin_amdgcn_exp2f(s[r] - msafe);
-        psum += s[r];
-      }
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][r], p.cscale, -ms));
+          psum += e;
+          pf[qb][kb][r >> 3][r & 7] = (__bf16)e;
+        }
       psum += __shfl_xor(psum, 32);
       lrun[qb] = lrun[qb] * alpha[qb] + psum;
       mrun[qb] = mnew;
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[qb][t2][e] = (__bf16)s[8 * t2 + e];
+      __builtin_amdgcn_sched_barrier(0);  // one query block at a time (register pressure)
     }
     // rescale the accumulators only when some lane's running maximum moved
     if (__ballot(moved)) {
@@ -348,75 +383,59 @@ __global__ void __launch_bounds__(AT_THREADS, 1) k_attn_mfma(sv_attn_args a, Att
           for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha[qb];
     }
 
-    // ---- O^T += V^T P^T
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- O^T += V^T P^T; the 16-key step (kb, t2) holds keys 32 kb + 16 t2 + 4 hf + {0..3, 8..11}
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const uint16_t* vrow = VTs + (db * 32 + lq) * LD::VSTR + 16 * t2 + 4 * hf;
-        const uint2 lo = *(const uint2*)(vrow);
-        const uint2 hi = *(const uint2*)(vrow + 8);
-        uint4 raw = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        const sv_bf16x8 vf = *(const sv_bf16x8*)&raw;
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const uint32_t rlo = lds_addr(Vb) + (32 * kb + 16 * t2 + tr_row) * ROWB + tr_half;
+        const uint32_t rhi = rlo + 8 * ROWB;
+        uint32_t alo[DB], ahi[DB];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][t2], oacc[qb][db], 0, 0, 0);
+        for (int db = 0; db < DB; ++db) {
+          const int c = 4 * db + tr_chunk;
+          alo[db] = rlo + ((c ^ tr_swz_lo) << 4);
+          ahi[db] = rhi + ((c ^ tr_swz_hi) << 4);
+        }
+        uint2 vlo[DB], vhi[DB];
+        read_tr<DB>(vlo, vhi, alo, ahi);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const sv_bf16x8 vf = __builtin_bit_cast(sv_bf16x8, make_uint4(vlo[db].x, vlo[db].y, vhi[db].x, vhi[db].y));
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][kb][t2], oacc[qb][db], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    wave_lds_sync();
-  }
+  };
 
-  // ---- merge the 4 waves: 2 -> 0, 3 -> 1, then 1 -> 0
-  __syncthreads();
-  float* mo = (float*)smem;                      // [2][QB][DB][16][64]
-  float* mml = mo + 2 * QB * DB * 16 * 64;       // [2][QB][2][64]
-  auto put = [&](int slot) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mo[(((slot * QB + qb) * DB + db) * 16 + r) * 64 + lane] = oacc[qb][db][r];
-      mml[((slot * QB + qb) * 2 + 0) * 64 + lane] = mrun[qb];
-      mml[((slot * QB + qb) * 2 + 1) * 64 + lane] = lrun[qb];
-    }
-  };
-  auto take = [&](int slot) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float mb = mml[((slot * QB + qb) * 2 + 0) * 64 + lane];
-      const float lb = mml[((slot * QB + qb) * 2 + 1) * 64 + lane];
-      const float m = fmaxf(mrun[qb], mb);
-      if (m == -INFINITY) continue;
-      const float fa = __builtin_amdgcn_exp2f(mrun[qb] - m), fb = __builtin_amdgcn_exp2f(mb - m);
-      lrun[qb] = fa * lrun[qb] + fb * lb;
-      mrun[qb] = m;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          oacc[qb][db][r] = fa * oacc[qb][db][r] + fb * mo[(((slot * QB + qb) * DB + db) * 16 + r) * 64 + lane];
-    }
-  };
-  if (w >= 2) put(w - 2);
-  __syncthreads();
-  if (w < 2) take(w);
-  __syncthreads();
-  if (w == 1) put(0);
-  __syncthreads();
-  if (w != 0) return;
-  take(0);
+  // ---- main loop: even tiles compute from kvA while the next tile streams into kvB, and back
+  for (int tile = 0; tile < ntiles; tile += 2) {
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of `tile` (and the Q rows) have landed
+    __syncthreads();                // ... and everyone's; every wave is done with tile - 1
+    if (tile + 1 < ntiles) load_tile(tile + 1, kvB);
+    if (active) compute(tile, kvA);
+    if (tile + 1 >= ntiles) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tile + 2 < ntiles) load_tile(tile + 2, kvA);
+    if (active) compute(tile + 1, kvB);
+  }
+  if (!active) return;
 
   // ---- write: bf16 output (single split) or fp32 partials
   const int unit = pair * p.qtiles + qtile;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int ql = qb * 32 + lq;
+    const int ql = w * 32 * QB + qb * 32 + lq;
     const int m = qtile * p.QT + ql;
     if (m >= p.M) continue;
     if (p.nsplit == 1) {
       const float inv = lrun[qb] > 0.f ? 1.f / lrun[qb] : 0.f;
-      const int node = qnode[qb];
+      const int node = qnode[qb];  // valid: m < M
       const int h = g * G + m % G;
       uint16_t* orow = (uint16_t*)a.out + (((int64_t)b * N + node) * Hq + h) * D;
 #pragma unroll
@@ -441,10 +460,7 @@ __global__ void __launch_bounds__(AT_THREADS, 1) k_attn_mfma(sv_attn_args a, Att
           *(float4*)(orow + d) = make_float4(oacc[qb][db][4 * rq + 0], oacc[qb][db][4 * rq + 1],
                                              oacc[qb][db][4 * rq + 2], oacc[qb][db][4 * rq + 3]);
         }
-      if (hf == 0) {
-        p.mlpart[(pidx * p.QT + ql) * 2 + 0] = mrun[qb];
-        p.mlpart[(pidx * p.QT + ql) * 2 + 1] = lrun[qb];
-      }
+      if (hf == 0) *(float2*)(p.mlpart + (pidx * p.QT + ql) * 2) = make_float2(mrun[qb] * p.cscale, lrun[qb]);
     }
   }
 }
@@ -641,14 +657,14 @@ AttnPlan make_plan(const sv_attn_args& a) {
     p.nsplit = 1;
     return p;
   }
-  p.QB = p.M <= 32 ? 1 : 2;
-  p.QT = 32 * p.QB;
+  p.QB = MF_QB;
+  p.QT = 32 * MF_QB * MF_WAVES;  // each wave owns 32 MF_QB query rows
   p.qtiles = (p.M + p.QT - 1) / p.QT;
   p.ntt = (a.N + KT - 1) / KT;
   const int64_t units = (int64_t)a.B * a.Hkv * p.qtiles;
   const int tiles_cap = (p.cap + KT - 1) / KT;
   int nsplit = (int)((TARGET_WG + units - 1) / units);
-  const int max_split = tiles_cap / AT_WAVES > 1 ? tiles_cap / AT_WAVES : 1;
+  const int max_split = tiles_cap / SV_ATTN_MIN_SPLIT_TILES > 1 ? tiles_cap / SV_ATTN_MIN_SPLIT_TILES : 1;
   if (nsplit > max_split) nsplit = max_split;
   if (nsplit > 64) nsplit = 64;  // the combine keeps one split per lane
   if (nsplit < 1) nsplit = 1;
@@ -710,13 +726,8 @@ extern "C" sv_status sv_tree_attention(const sv_attn_args* args, void* stream) {
   if (use_mfma(a)) {
     const int64_t grid = (int64_t)a.B * a.Hkv * p.qtiles * p.nsplit;
     if (grid > 0x7fffffff) return SV_ERR_UNSUPPORTED;
-    if (a.D == 128) {
-      if (p.QB == 1) hipLaunchKernelGGL((k_attn_mfma<128, 1>), dim3(grid), dim3(AT_THREADS), 0, s, a, p);
-      else hipLaunchKernelGGL((k_attn_mfma<128, 2>), dim3(grid), dim3(AT_THREADS), 0, s, a, p);
-    } else {
-      if (p.QB == 1) hipLaunchKernelGGL((k_attn_mfma<64, 1>), dim3(grid), dim3(AT_THREADS), 0, s, a, p);
-      else hipLaunchKernelGGL((k_attn_mfma<64, 2>), dim3(grid), dim3(AT_THREADS), 0, s, a, p);
-    }
+    if (a.D == 128) hipLaunchKernelGGL(k_attn_mfma<128>, dim3(grid), dim3(MF_THREADS), 0, s, a, p);
+    else hipLaunchKernelGGL(k_attn_mfma<64>, dim3(grid), dim3(MF_THREADS), 0, s, a, p);
     if (p.nsplit > 1) {
       const int64_t rows = (int64_t)a.B * a.N * a.Hq;
       const dim3 cg((unsigned)((rows + 3) / 4));
