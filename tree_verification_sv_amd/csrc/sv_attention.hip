@@ -91,7 +91,6 @@ struct Tile {
   static constexpr int RPW = RPI * IPW;               // rows filled by one wave
   static constexpr int TBYTES = KT * ROWB;            // one tensor of the tile
   static constexpr int BUF = 2 * TBYTES;              // K and V
-  static constexpr int QSTR = D + 8;                  // Q row stride in LDS (16-byte pad)
   static constexpr int QROWS = 32 * MF_QB * MF_WAVES;  // query rows per work-group
   __device__ static __forceinline__ int swz(int r) {
     return CPR == 16 ? (((r << 1) & 14) | ((r >> 3) & 1)) : ((r & 6) | ((r >> 3) & 1));
@@ -150,7 +149,7 @@ __global__ void __launch_bounds__(MF_THREADS, 2) k_attn_mfma(sv_attn_args a, Att
   // streaming into one never alias the reads of the other, and does not wait on them
   __shared__ __attribute__((aligned(1024))) unsigned char kvA[TL::BUF];
   __shared__ __attribute__((aligned(1024))) unsigned char kvB[TL::BUF];
-  __shared__ __attribute__((aligned(16))) uint16_t qs[TL::QROWS * TL::QSTR];  // the work-group's query rows
+  __shared__ __attribute__((aligned(1024))) unsigned char qsb[TL::QROWS * TL::ROWB];  // the work-group's query rows
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -246,17 +245,21 @@ __global__ void __launch_bounds__(MF_THREADS, 2) k_attn_mfma(sv_attn_args a, Att
 
   if (0 < ntiles) load_tile(0, kvA);
 
-  // ---- the work-group's query rows into LDS (rows past M are zero); the B operand
-  // of S^T = K Q^T for lane (lq, hf) and k-step ds is Q row lq, d = 16*ds + 8*hf .. +7
-  for (int c = t; c < TL::QROWS * TL::CPR; c += MF_THREADS) {
-    const int row = c / TL::CPR, cc = c % TL::CPR;
-    const int m = qtile * p.QT + row;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (m < p.M) {
+  // ---- the work-group's query rows into LDS, swizzled like K (rows past M repeat row
+  // M - 1; their outputs are never written).  The B operand of S^T = K Q^T for lane
+  // (lq, hf) and k-step ds is Q row lq, d = 16*ds + 8*hf .. +7.
+  {
+    constexpr int NQ = TL::QROWS * TL::CPR / 64 / MF_WAVES;  // 1-KB pieces per wave
+#pragma unroll
+    for (int it = 0; it < NQ; ++it) {
+      const int n = w * NQ + it;
+      const int r = n * TL::RPI + lane / TL::CPR;
+      const int c = (lane % TL::CPR) ^ TL::swz(r);
+      const int m = min(qtile * p.QT + r, p.M - 1);
       const int node = m / G, h = g * G + m % G;
-      v = *(const uint4*)(qg + (((int64_t)b * N + node) * Hq + h) * D + cc * 8);
+      __builtin_amdgcn_global_load_lds((const void*)(qg + (((int64_t)b * N + node) * Hq + h) * D + c * 8),
+                                       (lds_void*)(qsb + n * 1024), 16, 0, 0);
     }
-    *(uint4*)(qs + row * TL::QSTR + cc * 8) = v;
   }
   int qnode[QB];
 #pragma unroll
@@ -264,7 +267,6 @@ __global__ void __launch_bounds__(MF_THREADS, 2) k_attn_mfma(sv_attn_args a, Att
     const int m = mw + qb * 32 + lq;
     qnode[qb] = m < p.M ? m / G : -1;
   }
-  const uint16_t* qw = qs + (w * 32 * QB + lq) * TL::QSTR + 8 * hf;  // this lane's Q row in LDS
 
   sv_f32x16 oacc[QB][DB];
   float mrun[QB], lrun[QB];
@@ -305,9 +307,10 @@ __global__ void __launch_bounds__(MF_THREADS, 2) k_attn_mfma(sv_attn_args a, Att
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
       sv_bf16x8 qf[QB];
+      const int kslot = ((2 * ds + hf) ^ k_swz) * 16;  // Q and K rows share the swizzle of row lq
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) qf[qb] = *(const sv_bf16x8*)(qw + qb * 32 * TL::QSTR + ds * 16);
-      const int kslot = ((2 * ds + hf) ^ k_swz) * 16;
+      for (int qb = 0; qb < QB; ++qb)
+        qf[qb] = *(const sv_bf16x8*)(qsb + (w * 32 * QB + qb * 32) * ROWB + k_off + kslot);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const sv_bf16x8 kf = *(const sv_bf16x8*)(Kb + kb * 32 * ROWB + k_off + kslot);
