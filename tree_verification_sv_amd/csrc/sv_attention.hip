@@ -13,10 +13,11 @@
 //     sequence, a tile of up to 256 query rows (row m = node*G + head in group,
 //     so the G query heads that share a KV head form one dense contraction of
 //     M = N*G rows) and a contiguous key range (a split of the prefix; the last
-//     split also takes the tree block).  Each of its 4 waves owns 64 query rows
-//     for the whole key range, so no merge between waves is needed.  64-key
-//     K/V tiles are loaded once per work-group (two tiles in flight in
-//     registers, two LDS buffers), S^T = K Q^T and O^T += V^T P^T run on
+//     split also takes the tree block).  Each of its 8 waves (two per SIMD)
+//     owns 32 query rows for the whole key range, so no merge between waves is
+//     needed.  The query tile and 64-key K/V tiles are written into LDS by
+//     direct global->LDS loads (XOR-swizzled rows; one K/V tile streams in
+//     while the other is consumed); S^T = K Q^T and O^T += V^T P^T run on
 //     v_mfma_f32_32x32x16_bf16, V^T fragments come straight from row-major V
 //     through transposing LDS reads, and the online-softmax state is per lane
 //     (each lane owns one query column).  A single split writes bf16 output
@@ -37,7 +38,7 @@ constexpr int MF_THREADS = 64 * MF_WAVES;
 constexpr int MF_QB = 1;                   // 32-row query blocks per wave
 constexpr int KT = 64;  // keys per tile
 #ifndef SV_ATTN_MIN_SPLIT_TILES
-#define SV_ATTN_MIN_SPLIT_TILES 4  // a prefix split covers at least this many tiles
+#define SV_ATTN_MIN_SPLIT_TILES 2  // a prefix split covers at least this many tiles
 #endif
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int TARGET_WG = 256;
