@@ -21,8 +21,8 @@
 //     v_mfma_f32_32x32x16_bf16, V^T fragments come straight from row-major V
 //     through transposing LDS reads, and the online-softmax state is per lane
 //     (each lane owns one query column).  A single split writes bf16 output
-//     directly; several splits write fp32 partials (m, l, O) merged by
-//     k_attn_combine.
+//     directly; several splits write partials (the normalised row O / l in
+//     bf16, m and l in fp32) merged by k_attn_combine.
 //  k_attn_valu<T>  generic fp32 / bf16 path, scalar FMA.
 #include <float.h>
 #include <math.h>
@@ -47,8 +47,8 @@ struct AttnPlan {
   int32_t G, M, QB, QT, qtiles, nsplit, chunk, ntt, W, cap;
   float cscale;  // scale * log2(e)
   uint32_t pool_bytes;  // paged: bytes of one K (or V) pool, < 4 GiB
-  float* opart;  // [units][nsplit][QT][D]
-  float* mlpart; // [units][nsplit][QT][2]
+  uint16_t* opart;  // [units][nsplit][QT][D] bf16: the split's output row O / l
+  float* mlpart;    // [units][nsplit][QT][2]: running max (scaled by log2 e) and l
 };
 
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
@@ -430,18 +430,26 @@ __global__ void __launch_bounds__(MF_THREADS, 2) k_attn_mfma(sv_attn_args a, Att
   }
   if (!active) return;
 
-  // ---- write: bf16 output (single split) or fp32 partials
+  // ---- write: bf16 output (single split) or per-split partials: the normalised row
+  // O / l in bf16 and (m, l) in fp32
   const int unit = pair * p.qtiles + qtile;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int ql = w * 32 * QB + qb * 32 + lq;
     const int m = qtile * p.QT + ql;
     if (m >= p.M) continue;
-    if (p.nsplit == 1) {
-      const float inv = lrun[qb] > 0.f ? 1.f / lrun[qb] : 0.f;
-      const int node = qnode[qb];  // valid: m < M
-      const int h = g * G + m % G;
-      uint16_t* orow = (uint16_t*)a.out + (((int64_t)b * N + node) * Hq + h) * D;
+    const float inv = lrun[qb] > 0.f ? 1.f / lrun[qb] : 0.f;
+    {
+      uint16_t* orow;
+      if (p.nsplit == 1) {
+        const int node = qnode[qb];  // valid: m < M
+        const int h = g * G + m % G;
+        orow = (uint16_t*)a.out + (((int64_t)b * N + node) * Hq + h) * D;
+      } else {
+        const int64_t pidx = (int64_t)unit * p.nsplit + split;
+        orow = p.opart + (pidx * p.QT + ql) * D;
+        if (hf == 0) *(float2*)(p.mlpart + (pidx * p.QT + ql) * 2) = make_float2(mrun[qb] * p.cscale, lrun[qb]);
+      }
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -453,18 +461,6 @@ __global__ void __launch_bounds__(MF_THREADS, 2) k_attn_mfma(sv_attn_args a, Att
                               ((uint32_t)f32_to_bf16_bits(oacc[qb][db][4 * rq + 3] * inv) << 16);
           *(uint2*)(orow + d) = make_uint2(w0, w1);
         }
-    } else {
-      const int64_t pidx = (int64_t)unit * p.nsplit + split;
-      float* orow = p.opart + (pidx * p.QT + ql) * D;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int d = db * 32 + 8 * rq + 4 * hf;
-          *(float4*)(orow + d) = make_float4(oacc[qb][db][4 * rq + 0], oacc[qb][db][4 * rq + 1],
-                                             oacc[qb][db][4 * rq + 2], oacc[qb][db][4 * rq + 3]);
-        }
-      if (hf == 0) *(float2*)(p.mlpart + (pidx * p.QT + ql) * 2) = make_float2(mrun[qb] * p.cscale, lrun[qb]);
     }
   }
 }
@@ -497,8 +493,8 @@ __global__ void __launch_bounds__(256) k_attn_combine(sv_attn_args a, AttnPlan p
   }
   float mx = ms;
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-  const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - mx);  // weight of split `lane`
-  float l = f * ls;
+  const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - mx) * ls;  // weight of split `lane`'s normalised row
+  float l = f;
   for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
   float acc[EPL];
 #pragma unroll
@@ -508,9 +504,15 @@ __global__ void __launch_bounds__(256) k_attn_combine(sv_attn_args a, AttnPlan p
 #pragma unroll
     for (int k = 0; k < AT_MAX_SPLIT_REG; ++k) {
       const int s = s0 + k;
-      const float* orow = p.opart + ((unit * ns + (s < ns ? s : 0)) * p.QT + ql) * D + lane * EPL;
+      const uint16_t* orow = p.opart + ((unit * ns + (s < ns ? s : 0)) * p.QT + ql) * D + lane * EPL;
+      if (EPL == 2) {
+        const uint32_t two = *(const uint32_t*)orow;
+        part[k][0] = s < ns ? __uint_as_float(two << 16) : 0.f;
+        part[k][EPL - 1] = s < ns ? __uint_as_float(two & 0xffff0000u) : 0.f;
+      } else {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) part[k][e] = s < ns ? orow[e] : 0.f;
+        for (int e = 0; e < EPL; ++e) part[k][e] = s < ns ? bf16_bits_to_f32(orow[e]) : 0.f;
+      }
     }
 #pragma unroll
     for (int k = 0; k < AT_MAX_SPLIT_REG; ++k) {
@@ -683,7 +685,7 @@ size_t workspace_bytes(const sv_attn_args& a, const AttnPlan& p) {
   if (!use_mfma(a) || p.nsplit == 1) return 0;
   const size_t units = (size_t)a.B * a.Hkv * p.qtiles;
   const size_t parts = units * p.nsplit * p.QT;
-  const size_t obytes = (parts * a.D * sizeof(float) + 255) / 256 * 256;
+  const size_t obytes = (parts * a.D * sizeof(uint16_t) + 255) / 256 * 256;
   return obytes + parts * 2 * sizeof(float);
 }
 
@@ -723,8 +725,8 @@ extern "C" sv_status sv_tree_attention(const sv_attn_args* args, void* stream) {
     if (!a.workspace || a.workspace_bytes < need || ((uintptr_t)a.workspace % 256)) return SV_ERR_INVALID_ARGUMENT;
     const size_t units = (size_t)a.B * a.Hkv * p.qtiles;
     const size_t parts = units * p.nsplit * p.QT;
-    p.opart = (float*)a.workspace;
-    p.mlpart = (float*)((char*)a.workspace + (parts * a.D * sizeof(float) + 255) / 256 * 256);
+    p.opart = (uint16_t*)a.workspace;
+    p.mlpart = (float*)((char*)a.workspace + (parts * a.D * sizeof(uint16_t) + 255) / 256 * 256);
   }
   hipStream_t s = (hipStream_t)stream;
   if (use_mfma(a)) {
