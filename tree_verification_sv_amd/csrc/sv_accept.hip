@@ -364,25 +364,28 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
   if (item < (int64_t)a.B * (N + 1)) {
     const int b = (int)(item / (N + 1));
     const int r = (int)(item % (N + 1));
+    const T* prow = (const T*)a.target_logits + ((int64_t)b * (N + 1) + r) * V;
+    const T* qrow = MODE == SV_STOCHASTIC ? (const T*)a.draft_logits + ((int64_t)b * (N + 1) + r) * V : nullptr;
+    const bool aligned = ((size_t)V * sizeof(T)) % 16 == 0 && ((uintptr_t)prow % 16) == 0 &&
+                         (MODE == SV_GREEDY || ((uintptr_t)qrow % 16) == 0);
+    // stochastic: nearly every row is resolved, so the target slice is fetched before the
+    // sequence facts that confirm it is needed (its latency overlaps them)
+    uint4 rp[NK];
+    if constexpr (MODE == SV_STOCHASTIC) load_pieces<T>(prow, s0, V, aligned, t, rp);
     seq_load(a, b, si);
     if (row_live(a, si, r)) {  // uniform across the group
       row_kids(N, r, si);
-      const T* prow = (const T*)a.target_logits + ((int64_t)b * (N + 1) + r) * V;
-      const T* qrow = MODE == SV_STOCHASTIC ? (const T*)a.draft_logits + ((int64_t)b * (N + 1) + r) * V : nullptr;
-      const bool aligned = ((size_t)V * sizeof(T)) % 16 == 0 && ((uintptr_t)prow % 16) == 0 &&
-                           (MODE == SV_GREEDY || ((uintptr_t)qrow % 16) == 0);
       int done_by_me = 0;  // this work-group wrote the row result
 
       if constexpr (MODE == SV_GREEDY) {
         float best = -FLT_MAX;
         int arg = 0x7fffffff;
         {
-          uint4 raw[NK];
-          load_pieces<T>(prow, s0, V, aligned, t, raw);
+          load_pieces<T>(prow, s0, V, aligned, t, rp);
 #pragma unroll
           for (int k = 0; k < NK; ++k) {
             float x[E];
-            unpack16<T>(raw[k], x);
+            unpack16<T>(rp[k], x);
             const int v = piece_v<T>(s0, k, t);
 #pragma unroll
             for (int e = 0; e < E; ++e)  // a thread visits its entries in ascending id
@@ -422,8 +425,7 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
         float mp = -FLT_MAX, mq = -FLT_MAX;
         double zp = 0.0, zq = 0.0;
         {
-          uint4 rp[NK], rq[NK];
-          load_pieces<T>(prow, s0, V, aligned, t, rp);
+          uint4 rq[NK];
           if (need_q) load_pieces<T>(qrow, s0, V, aligned, t, rq);
 #pragma unroll
           for (int k = 0; k < NK; ++k) {
@@ -435,17 +437,35 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
           mp = block_max(mp, red);
           opaque(rp);  // unpack again below instead of keeping the unpacked floats alive
           const float op = mp * l2T;  // exp2(x * l2T - op): one FMA per entry
+          const bool whole = s0 + AC_SLICE <= V;  // uniform: no entry of the slice lies past V
+          auto expo = [&](const uint4 (&raw)[NK], float o, float (&ex)[AC_CT], double& z) {
+            if (whole) {
 #pragma unroll
-          for (int k = 0; k < NK; ++k) {
-            float x[E], g = 0.f;  // fp32 partial of one piece, fp64 across pieces
-            unpack16<T>(rp[k], x);
+              for (int k = 0; k < NK; ++k) {
+                float x[E], g = 0.f;  // fp32 partial of one piece, fp64 across pieces
+                unpack16<T>(raw[k], x);
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-              ep[k * E + e] = piece_v<T>(s0, k, t) < V ? __builtin_amdgcn_exp2f(fmaf(x[e], l2T, -op)) : 0.f;
-              g += ep[k * E + e];
+                for (int e = 0; e < E; ++e) {
+                  ex[k * E + e] = __builtin_amdgcn_exp2f(fmaf(x[e], l2T, -o));
+                  g += ex[k * E + e];
+                }
+                z += (double)g;
+              }
+            } else {
+#pragma unroll
+              for (int k = 0; k < NK; ++k) {
+                float x[E], g = 0.f;
+                unpack16<T>(raw[k], x);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                  ex[k * E + e] = piece_v<T>(s0, k, t) < V ? __builtin_amdgcn_exp2f(fmaf(x[e], l2T, -o)) : 0.f;
+                  g += ex[k * E + e];
+                }
+                z += (double)g;
+              }
             }
-            zp += (double)g;
-          }
+          };
+          expo(rp, op, ep, zp);
           if (need_q) {
 #pragma unroll
             for (int k = 0; k < NK; ++k) {
@@ -456,18 +476,7 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
             }
             mq = block_max(mq, red);
             opaque(rq);
-            const float oq = mq * l2T;
-#pragma unroll
-            for (int k = 0; k < NK; ++k) {
-              float x[E], g = 0.f;
-              unpack16<T>(rq[k], x);
-#pragma unroll
-              for (int e = 0; e < E; ++e) {
-                eq[k * E + e] = piece_v<T>(s0, k, t) < V ? __builtin_amdgcn_exp2f(fmaf(x[e], l2T, -oq)) : 0.f;
-                g += eq[k * E + e];
-              }
-              zq += (double)g;
-            }
+            expo(rq, mq * l2T, eq, zq);
           } else {
 #pragma unroll
             for (int i = 0; i < AC_CT; ++i) eq[i] = 0.f;
