@@ -44,6 +44,8 @@
 #include <float.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "sv_common.h"
 
 namespace {
@@ -54,6 +56,7 @@ constexpr int AC_CT = 64;                      // vocabulary entries per thread
 constexpr int AC_SLICE = AC_THREADS * AC_CT;   // 16384 entries per work-group
 constexpr int AC_MAXG = 64;                    // work-groups per row group (vocabulary up to 1M entries)
 constexpr int AC_XW = 8;                       // tagged words per exchange slot
+constexpr int AC_XV = 6;                       // words an exchange carries at most
 constexpr uint32_t AC_SPIN_LIMIT = 1u << 20;   // bounded wait for a group partner (polls)
 
 struct XSlot {      // one work-group's partials for one exchange: (tag << 32) | payload
@@ -75,15 +78,62 @@ struct AccWs {      // workspace views
 
 template <typename T>
 __device__ __forceinline__ float ldf(const T* p, int64_t i) { return load_as_f32<T>(p, i); }
+// raw bits of one logit, and their value (split so that the conversion can be placed late)
+template <typename T> __device__ __forceinline__ uint32_t ldraw(const T* p, int64_t i);
+template <> __device__ __forceinline__ uint32_t ldraw<float>(const float* p, int64_t i) { return __float_as_uint(p[i]); }
+template <> __device__ __forceinline__ uint32_t ldraw<uint16_t>(const uint16_t* p, int64_t i) { return p[i]; }
+template <typename T> __device__ __forceinline__ float rawf(uint32_t b) {
+  return sizeof(T) == 2 ? __uint_as_float(b << 16) : __uint_as_float(b);
+}
 
 // ---------------------------------------------------------------- reductions
+// Cross-lane steps use DPP moves (a few cycles each) instead of LDS permutes.
+// Within a 16-lane row: quad permutations and the row mirrors for butterflies,
+// row shifts for the scan; across rows: lane reads for reductions and the row
+// broadcasts of lanes 15 and 31 for the scan.  Results are identical in every
+// lane, and the order of operations is fixed, so every work-group that reduces
+// the same values gets the same bits.
+enum : int {
+  DPP_XOR1 = 0xB1,         // quad_perm [1, 0, 3, 2]
+  DPP_XOR2 = 0x4E,         // quad_perm [2, 3, 0, 1]
+  DPP_ROW_SHR1 = 0x111,    // row_shr:n = 0x110 + n
+  DPP_ROW_MIRROR = 0x140,
+  DPP_ROW_HALF_MIRROR = 0x141,
+  DPP_ROW_BCAST15 = 0x142,
+  DPP_ROW_BCAST31 = 0x143,
+};
+template <int CTRL, int ROWS = 0xf, bool BC = true>
+__device__ __forceinline__ uint32_t dpp32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWS, 0xf, BC);
+}
+template <int CTRL, int ROWS = 0xf, bool BC = true>
+__device__ __forceinline__ float dppf(float x) { return __uint_as_float(dpp32<CTRL, ROWS, BC>(__float_as_uint(x))); }
+template <int CTRL, int ROWS = 0xf, bool BC = true>
+__device__ __forceinline__ double dppd(double x) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint64_t lo = dpp32<CTRL, ROWS, BC>((uint32_t)b), hi = dpp32<CTRL, ROWS, BC>((uint32_t)(b >> 32));
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
+__device__ __forceinline__ float lanef(float x, int l) { return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x), l)); }
+__device__ __forceinline__ double laned(double x, int l) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((uint32_t)b, l);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((uint32_t)(b >> 32), l);
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
 __device__ __forceinline__ float wave_maxf(float x) {
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+  x = fmaxf(x, dppf<DPP_XOR1>(x));
+  x = fmaxf(x, dppf<DPP_XOR2>(x));
+  x = fmaxf(x, dppf<DPP_ROW_HALF_MIRROR>(x));
+  x = fmaxf(x, dppf<DPP_ROW_MIRROR>(x));  // every lane of a row holds the row's maximum
+  return fmaxf(fmaxf(lanef(x, 0), lanef(x, 16)), fmaxf(lanef(x, 32), lanef(x, 48)));
 }
 __device__ __forceinline__ double wave_sumd(double x) {
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  x += dppd<DPP_XOR1>(x);
+  x += dppd<DPP_XOR2>(x);
+  x += dppd<DPP_ROW_HALF_MIRROR>(x);
+  x += dppd<DPP_ROW_MIRROR>(x);  // every lane of a row holds the row's sum
+  return (laned(x, 0) + laned(x, 16)) + (laned(x, 32) + laned(x, 48));
 }
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   for (int o = 32; o > 0; o >>= 1) {
@@ -94,10 +144,13 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
 }
 // inclusive prefix sum over the 64 lanes of a wave, ascending lane order
 __device__ __forceinline__ double wave_scand(double x, int lane) {
-  for (int o = 1; o < 64; o <<= 1) {
-    const double y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  (void)lane;
+  x += dppd<DPP_ROW_SHR1 + 0>(x);  // shifted-in lanes read 0
+  x += dppd<DPP_ROW_SHR1 + 1>(x);
+  x += dppd<DPP_ROW_SHR1 + 3>(x);
+  x += dppd<DPP_ROW_SHR1 + 7>(x);  // inclusive scan within each row of 16
+  x += dppd<DPP_ROW_BCAST15, 0xa, false>(x);  // rows 1, 3 add lane 15 of the row before
+  x += dppd<DPP_ROW_BCAST31, 0xc, false>(x);  // rows 2, 3 add lane 31
   return x;
 }
 
@@ -105,12 +158,7 @@ struct Red {
   float f[AC_NW];
   double d[AC_NW];
   int i[AC_NW];
-  double scan1[AC_THREADS];  // exclusive prefixes of the bonus scan, one per thread
 };
-// LDS index of slice-local entry i in the bonus staging buffer: a stride of 68
-// floats per 64 entries keeps the 16-byte reads of consecutive threads on
-// distinct banks
-__host__ __device__ constexpr int wpad(int i) { return i + (i / AC_CT) * 4; }
 
 __device__ __forceinline__ float block_max(float x, Red& r) {
   x = wave_maxf(x);
@@ -175,7 +223,7 @@ __device__ __forceinline__ double dof(uint32_t lo, uint32_t hi) {
 // The wait is bounded: on timeout the error flag is raised, and once it is
 // raised no thread waits any more, so every wave exits (results then carry
 // status SV_SEQ_TIMEOUT).
-__device__ __forceinline__ void exchange(XSlot* gs, int G, int rank, uint32_t tag, int nw, uint32_t (*xv)[AC_XW],
+__device__ __forceinline__ void exchange(XSlot* gs, int G, int rank, uint32_t tag, int nw, uint32_t (*xv)[AC_XV],
                                          uint32_t* err, uint32_t w0, uint32_t w1, uint32_t w2 = 0, uint32_t w3 = 0,
                                          uint32_t w4 = 0, uint32_t w5 = 0) {
   const int t = threadIdx.x;
@@ -202,10 +250,11 @@ __device__ __forceinline__ void exchange(XSlot* gs, int G, int rank, uint32_t ta
 }
 
 struct SeqInfo {    // per-sequence facts every work-group derives the same way
-  int32_t par[SV_MAX_N];
-  int32_t usable[SV_MAX_N];
-  int32_t nkids[SV_MAX_N + 1];
-  int32_t kids[SV_MAX_N];     // usable children of the current row, ascending
+  int32_t tok[SV_MAX_N];
+  int16_t par[SV_MAX_N];
+  uint8_t usable[SV_MAX_N];
+  uint8_t haskid[SV_MAX_N + 1];  // row has a usable child
+  int16_t kids[SV_MAX_N];     // usable children of the current row, ascending
   int32_t wcount[AC_NW];
   int32_t wlive[AC_NW];
   int32_t K;                  // number of usable children of the current row
@@ -215,27 +264,43 @@ struct SeqInfo {    // per-sequence facts every work-group derives the same way
   int32_t flag;
 };
 
-// per-sequence facts: usable nodes, child counts per row, live-row count (one node per thread)
-__device__ __forceinline__ void seq_load(const sv_accept_args& a, int b, SeqInfo& si) {
+// per-sequence facts: usable nodes, rows with children, live-row count (one node per thread).
+// The loads are issued by seq_fetch ahead of the slice loads, so that waiting for them does
+// not wait for the slice.
+struct SeqRaw {
+  int32_t tok, par, dep;
+};
+__device__ __forceinline__ SeqRaw seq_fetch(const sv_accept_args& a, int b) {
+  SeqRaw r{0, -2, 0};
+  const int t = threadIdx.x;
+  if (t < a.N) {
+    const int64_t i = (int64_t)b * a.N + t;
+    r.tok = a.tokens[i];
+    r.par = a.parents[i];
+    r.dep = a.depth[i];
+  }
+  return r;
+}
+__device__ __forceinline__ void seq_facts(const sv_accept_args& a, const SeqRaw& sr, SeqInfo& si) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int N = a.N;
-  for (int x = t; x <= N; x += AC_THREADS) si.nkids[x] = 0;
+  for (int x = t; x <= N; x += AC_THREADS) si.haskid[x] = 0;
   if (t == 0) si.bad_token = 0;
   __syncthreads();
   bool u = false;
   if (t < N) {
-    const int32_t tok = a.tokens[(int64_t)b * N + t];
-    const bool ok = tok >= 0 && tok < a.V;
-    if (!ok) atomicOr(&si.bad_token, 1);
-    const int pr = a.parents[(int64_t)b * N + t];
-    u = ok && a.depth[(int64_t)b * N + t] > 0 && pr >= -1 && pr < N;
-    si.par[t] = pr;
-    if (u) atomicAdd(&si.nkids[pr + 1], 1);
+    const bool ok = sr.tok >= 0 && sr.tok < a.V;
+    if (!ok) si.bad_token = 1;  // every writer stores the same value
+    const int pr = sr.par;
+    u = ok && sr.dep > 0 && pr >= -1 && pr < N;
+    si.par[t] = (int16_t)pr;
+    si.tok[t] = sr.tok;
+    if (u) si.haskid[pr + 1] = 1;
   }
   if (t < SV_MAX_N) si.usable[t] = u;
   __syncthreads();
   // live rows: greedy -- rows with a usable child; stochastic -- rows of usable nodes
-  const bool live = a.mode == SV_GREEDY ? (t >= 1 && t <= N && si.nkids[t] > 0) : u;
+  const bool live = a.mode == SV_GREEDY ? (t >= 1 && t <= N && si.haskid[t]) : u;
   const uint64_t lm = __ballot(live);
   if (lane == 0) si.wlive[wv] = __popcll(lm);
   __syncthreads();
@@ -266,7 +331,7 @@ __device__ __forceinline__ void row_kids(int N, int r, SeqInfo& si) {
 
 __device__ __forceinline__ bool row_live(const sv_accept_args& a, const SeqInfo& si, int r) {
   if (r == 0) return true;
-  return a.mode == SV_GREEDY ? si.nkids[r] > 0 : si.usable[r - 1] != 0;
+  return a.mode == SV_GREEDY ? si.haskid[r] != 0 : si.usable[r - 1] != 0;
 }
 
 // ---------------------------------------------------------------- slice loads
@@ -308,17 +373,24 @@ __device__ __forceinline__ int piece_v(int s0, int k, int t) { return s0 + (k * 
 // wholly past the row; the loads then go through a buffer resource sized to
 // the row, which returns zeros for pieces past V.  Otherwise entries are
 // loaded one by one and entries past V read as the lowest value.  Callers
-// treat pieces starting at or past V as absent.
+// treat pieces starting at or past V as absent.  `present` false (uniform):
+// the row is not needed; aligned loads are still issued, against an empty
+// range, so they return zeros without touching memory and the register
+// assignment does not depend on the branch.
 template <typename T>
 __device__ __forceinline__ void load_pieces(const T* row, int s0, int V, bool aligned, int t,
-                                            uint4 (&raw)[Piece<T>::NK]) {
+                                            uint4 (&raw)[Piece<T>::NK], bool present = true) {
   constexpr int E = Piece<T>::E;
   if (aligned) {
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)row, 0, V * (int)sizeof(T), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)row, 0, present ? V * (int)sizeof(T) : 0, 0x00020000);
     const int vo = (s0 + t * E) * (int)sizeof(T);
 #pragma unroll
     for (int k = 0; k < Piece<T>::NK; ++k)
       raw[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, k * AC_THREADS * 16, 0));
+  } else if (!present) {
+#pragma unroll
+    for (int k = 0; k < Piece<T>::NK; ++k) raw[k] = make_uint4(0u, 0u, 0u, 0u);
   } else {
 #pragma unroll
     for (int k = 0; k < Piece<T>::NK; ++k) {
@@ -335,18 +407,22 @@ __device__ __forceinline__ void load_pieces(const T* row, int s0, int V, bool al
 }
 
 // ---------------------------------------------------------------- the kernel
-template <typename T, int MODE>
+// ALIGNED: every logits row starts on 16 bytes (decided on the host; a compile-time choice
+// keeps the two load paths from meeting in one register assignment)
+template <typename T, int MODE, bool ALIGNED>
 __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int32_t G, AccWs ws) {
   constexpr int E = Piece<T>::E, NK = Piece<T>::NK;
   __shared__ Red red;
   __shared__ SeqInfo si;
   __shared__ int32_t s_last, s_hit, s_first, s_lpos;
   __shared__ uint64_t s_match[SV_MAX_W];
-  __shared__ uint32_t xv[AC_MAXG][AC_XW];                          // collected group partials
+  __shared__ uint32_t xv[AC_MAXG][AC_XV];                          // collected group partials
   __shared__ float s_lp[SV_MAX_N], s_lq[SV_MAX_N], s_u[SV_MAX_N];  // per child: logits at its token, u_accept
   __shared__ float s_us;                                            // u_sample of the row
-  // bonus weights of the slice in id order, 4 floats of padding after every 64 entries
-  __shared__ __attribute__((aligned(16))) float s_w[MODE == SV_STOCHASTIC ? wpad(AC_SLICE) : 4];
+  // bonus: the slice's residual weights in id order, per-piece sums [k][t] and their row totals
+  __shared__ __attribute__((aligned(16))) float s_w[MODE == SV_STOCHASTIC ? AC_SLICE : 4];
+  __shared__ float s_g[MODE == SV_STOCHASTIC ? Piece<T>::NK * AC_THREADS : 4];
+  __shared__ double s_col[Piece<T>::NK];
   // work-groups are dispatched round-robin over the 8 XCDs; the members of a
   // group share an XCD (the grid size is a multiple of 8 * G)
   const int t = threadIdx.x, lane = t & 63;
@@ -362,17 +438,20 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
   const int s0 = rank * AC_SLICE;  // this work-group's slice of the vocabulary
 
   if (item < (int64_t)a.B * (N + 1)) {
-    const int b = (int)(item / (N + 1));
-    const int r = (int)(item % (N + 1));
+    // uniform, and kept in scalar registers so that the slice loads take a scalar resource
+    const int b = __builtin_amdgcn_readfirstlane((int)(item / (N + 1)));
+    const int r = __builtin_amdgcn_readfirstlane((int)(item % (N + 1)));
     const T* prow = (const T*)a.target_logits + ((int64_t)b * (N + 1) + r) * V;
     const T* qrow = MODE == SV_STOCHASTIC ? (const T*)a.draft_logits + ((int64_t)b * (N + 1) + r) * V : nullptr;
-    const bool aligned = ((size_t)V * sizeof(T)) % 16 == 0 && ((uintptr_t)prow % 16) == 0 &&
-                         (MODE == SV_GREEDY || ((uintptr_t)qrow % 16) == 0);
+    constexpr bool aligned = ALIGNED;
     // stochastic: nearly every row is resolved, so the target slice is fetched before the
-    // sequence facts that confirm it is needed (its latency overlaps them)
+    // sequence facts that confirm it is needed (its latency overlaps them); the facts'
+    // own loads go first
+    SeqRaw sr = seq_fetch(a, b);
     uint4 rp[NK];
     if constexpr (MODE == SV_STOCHASTIC) load_pieces<T>(prow, s0, V, aligned, t, rp);
-    seq_load(a, b, si);
+    asm volatile("" : "+v"(sr.tok), "+v"(sr.par), "+v"(sr.dep));  // nothing uses them before this point
+    seq_facts(a, sr, si);
     if (row_live(a, si, r)) {  // uniform across the group
       row_kids(N, r, si);
       int done_by_me = 0;  // this work-group wrote the row result
@@ -411,22 +490,25 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
       } else {
         const int K = __builtin_amdgcn_readfirstlane(si.K);
         const bool need_q = K > 0;
-        // ---- children's logits at their tokens and their uniforms, fetched alongside the slice
-        if (t < K) {
-          const int kid = si.kids[t];
-          const int x = a.tokens[(int64_t)b * N + kid];  // usable: x in [0, V)
-          s_lp[t] = ldf(prow, x);
-          s_lq[t] = ldf(qrow, x);
-          s_u[t] = a.u_accept[(int64_t)b * (N + 1) + kid + 1];
-        }
-        if (t == AC_THREADS - 1) s_us = a.u_sample[(int64_t)b * (N + 1) + r];
         // ---- the slice: raw logits -> slice maxima -> exponentials kept in registers
         float ep[AC_CT], eq[AC_CT];
         float mp = -FLT_MAX, mq = -FLT_MAX;
         double zp = 0.0, zq = 0.0;
         {
           uint4 rq[NK];
-          if (need_q) load_pieces<T>(qrow, s0, V, aligned, t, rq);
+          load_pieces<T>(qrow, s0, V, aligned, t, rq, need_q);
+          // children's logits at their tokens and their uniforms: issued after the draft
+          // slice (so that nothing waits for them before it is issued), stored to LDS once
+          // both slices are in
+          uint32_t c_lp = 0u, c_lq = 0u, c_u = 0u, c_us = 0u;
+          if (t < K) {
+            const int kid = si.kids[t];
+            const int x = si.tok[kid];  // usable: x in [0, V)
+            c_lp = ldraw(prow, x);
+            c_lq = ldraw(qrow, x);
+            c_u = __float_as_uint(a.u_accept[(int64_t)b * (N + 1) + kid + 1]);
+          }
+          if (t == AC_THREADS - 1) c_us = __float_as_uint(a.u_sample[(int64_t)b * (N + 1) + r]);
 #pragma unroll
           for (int k = 0; k < NK; ++k) {
             float x[E];
@@ -481,8 +563,15 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
 #pragma unroll
             for (int i = 0; i < AC_CT; ++i) eq[i] = 0.f;
           }
+          asm volatile("" : "+v"(c_lp), "+v"(c_lq), "+v"(c_u), "+v"(c_us));  // first use: here
+          if (t < K) {
+            s_lp[t] = rawf<T>(c_lp);
+            s_lq[t] = rawf<T>(c_lq);
+            s_u[t] = __uint_as_float(c_u);
+          }
+          if (t == AC_THREADS - 1) s_us = __uint_as_float(c_us);
         }
-        zp = block_sum(zp, red);
+        zp = block_sum(zp, red);  // its barriers also publish the children's values
         zq = block_sum(zq, red);
         exchange(gslots, G, rank, ++xtag, 6, xv, ws.err, __float_as_uint(mp), __float_as_uint(mq), dlo(zp), dhi(zp),
                  dlo(zq), dhi(zq));
@@ -504,11 +593,9 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
           fp = __shfl(sp, rank) / Zp;                   // p(v) = ep(v) * fp on this slice
           fq = need_q ? __shfl(sq, rank) / Zq : 0.0;
         }
-        // residual weight of one entry in units of fp: max(0, ep - kappa eq); kappa = 0 is p itself
-        auto wgt = [&](int i, float kappa) -> float {
-          return kappa == 0.f ? ep[i] : fmaxf(fmaf(-kappa, eq[i], ep[i]), 0.f);
-        };
-        auto slice_sum = [&](float kappa) -> double {
+        // residual weight of one entry in units of fp: max(0, ep - kappa eq) for kappa > 0
+        auto wgt = [&](int i, float kappa) -> float { return fmaxf(fmaf(-kappa, eq[i], ep[i]), 0.f); };
+        auto slice_sum = [&](float kappa) -> double {  // kappa > 0
           double acc = 0.0;
 #pragma unroll
           for (int k = 0; k < NK; ++k) {
@@ -549,37 +636,45 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
         } else {
           // ---- bonus: smallest v whose ascending cumulative residual exceeds u * total.
           // A residual of total 0 (reachable only through rounding) falls back to the previous one.
-          // The slice's weights are staged in LDS in id order; thread t then scans the 64
-          // consecutive entries [64 t, 64 t + 64) (fp32 partials of 8 entries, fp64 above).
+          // Ids ascend piece by piece: piece (k, t) holds the slice-local ids (k * 256 + t) * E ..
+          // + E - 1.  The weights are staged in LDS in id order (after which the exponentials in
+          // registers are dead) with their piece sums; row totals over t give the coarse
+          // cumulative sum, one work-group scan over the pieces of the row that crosses the
+          // threshold finds the piece, and one thread walks its E entries.  Piece sums are fp32
+          // over E entries; every sum above that is fp64.
           const int wv = t >> 6;
           const double us = (double)s_us;
           for (int attempt = 0; attempt < 2; ++attempt) {
+            // c == 0 (no rejection at this row): the weights are p itself
             const float kappa = c == 0.0 ? 0.f : (float)(c * fq / fp);
+            auto stage = [&](auto residual) {
 #pragma unroll
-            for (int k = 0; k < NK; ++k) {
-              const int i0 = (k * AC_THREADS + t) * E;  // slice-local id of the piece
-              float* dst = s_w + wpad(i0);
+              for (int k = 0; k < NK; ++k) {
+                float w[E], x = 0.f;
 #pragma unroll
-              for (int e = 0; e < E; e += 4)
-                *(float4*)(dst + e) = make_float4(wgt(k * E + e, kappa), wgt(k * E + e + 1, kappa),
-                                                  wgt(k * E + e + 2, kappa), wgt(k * E + e + 3, kappa));
-            }
+                for (int e = 0; e < E; ++e) {
+                  if constexpr (decltype(residual)::value) w[e] = wgt(k * E + e, kappa);
+                  else w[e] = ep[k * E + e];
+                  x += w[e];
+                }
+                float* dst = s_w + (k * AC_THREADS + t) * E;
+#pragma unroll
+                for (int e = 0; e < E; e += 4) *(float4*)(dst + e) = make_float4(w[e], w[e + 1], w[e + 2], w[e + 3]);
+                s_g[k * AC_THREADS + t] = x;
+              }
+            };
+            if (kappa == 0.f) stage(std::false_type{});  // uniform branch
+            else stage(std::true_type{});
             __syncthreads();
-            const float* mine = s_w + wpad(t * AC_CT);
-            double tsum = 0.0;
-#pragma unroll
-            for (int j = 0; j < AC_CT; j += 8) {
-              const float4 x0 = *(const float4*)(mine + j), x1 = *(const float4*)(mine + j + 4);
-              tsum += (double)(((((((x0.x + x0.y) + x0.z) + x0.w) + x1.x) + x1.y) + x1.z) + x1.w);
+            for (int k = wv; k < NK; k += AC_NW) {  // wave wv totals rows wv, wv + 4, ...
+              double x = 0.0;
+              for (int i = lane; i < AC_THREADS; i += 64) x += (double)s_g[k * AC_THREADS + i];
+              x = wave_sumd(x);
+              if (lane == 0) s_col[k] = x;
             }
-            double incl = wave_scand(tsum, lane);
-            if (lane == 63) red.d[wv] = incl;
             __syncthreads();
             double col = 0.0;
-            for (int w2 = 0; w2 < AC_NW; ++w2) {
-              if (w2 < wv) incl += red.d[w2];
-              col += red.d[w2];
-            }
+            for (int k = 0; k < NK; ++k) col += s_col[k];
             const double sl = col * fp;
             exchange(gslots, G, rank, ++xtag, 2, xv, ws.err, dlo(sl), dhi(sl));
             double before = 0.0, total = 0.0;
@@ -605,34 +700,58 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
             }
             if (rank == owner) {
               const double lthr = (thr - before) / fp;  // threshold in this slice's units
-              if (t == 0) { s_first = 0x7fffffff; s_lpos = -1; }
-              __syncthreads();
-              {  // the first thread whose inclusive prefix exceeds the threshold: one atomic per wave
-                const uint64_t over = __ballot(incl > lthr);
-                if (over && lane == 0) atomicMin(&s_first, wv * 64 + __ffsll((long long)over) - 1);
+              // the piece row whose cumulative total first exceeds it (uniform)
+              int ks = -1;
+              double below = 0.0;
+              for (int k = 0; k < NK; ++k) {
+                if (below + s_col[k] > lthr) { ks = k; break; }
+                below += s_col[k];
               }
-              red.scan1[t] = incl - tsum;  // exclusive prefix of each thread
-              __syncthreads();
-              const int h = s_first;
+              int h = 0x7fffffff;
+              double excl = 0.0;
+              if (ks >= 0) {  // inclusive scan of row ks over the threads, in id order
+                const float gk = s_g[ks * AC_THREADS + t];
+                double incl = wave_scand((double)gk, lane);
+                if (lane == 63) red.d[wv] = incl;
+                if (t == 0) s_first = 0x7fffffff;
+                __syncthreads();
+                for (int w2 = 0; w2 < wv; ++w2) incl += red.d[w2];
+                incl += below;
+                excl = incl - (double)gk;
+                const uint64_t over = __ballot(incl > lthr);  // one atomic per wave
+                if (over && lane == 0) atomicMin(&s_first, wv * 64 + __ffsll((long long)over) - 1);
+                __syncthreads();
+                h = s_first;
+              }
               if (h != 0x7fffffff) {
-                if (wv == 0) {  // one wave searches thread h's 64 entries, lane e = entry e
-                  const float w = s_w[wpad(h * AC_CT) + lane];
-                  const double run = red.scan1[h] + wave_scand((double)w, lane);
-                  const uint64_t hit = __ballot(w > 0.f && run > lthr);
-                  const uint64_t pos = __ballot(w > 0.f);
-                  int pick;
-                  if (hit) pick = s0 + h * AC_CT + __ffsll((long long)hit) - 1;
-                  else if (pos) pick = s0 + h * AC_CT + 63 - __clzll((long long)pos);
-                  else pick = min(s0 + h * AC_CT + AC_CT, V) - 1;
-                  if (lane == 0) {
-                    st_i(&ws.res[item].child, -1);
-                    st_i(&ws.res[item].token, pick);
+                if (t == h) {  // walk the E entries of piece (ks, h)
+                  const int p0 = (ks * AC_THREADS + t) * E;  // slice-local id of its first entry
+                  double run = excl;
+                  int pick = -1, lastpos = -1;
+                  for (int e = 0; e < E; ++e) {
+                    const float w = s_w[p0 + e];
+                    if (w > 0.f) {
+                      lastpos = s0 + p0 + e;
+                      run += (double)w;
+                      if (pick < 0 && run > lthr) pick = s0 + p0 + e;
+                    }
                   }
+                  if (pick < 0) pick = lastpos >= 0 ? lastpos : min(s0 + p0 + E, V) - 1;
+                  st_i(&ws.res[item].child, -1);
+                  st_i(&ws.res[item].token, pick);
                 }
-              } else {  // rounding left the threshold unreached: the highest id with a positive weight
+              } else {
+                // rounding left the threshold unreached: the highest id with a positive weight
+                // (in rows up to ks when a row was found, else in the whole slice)
+                const int klim = ks >= 0 ? ks : NK - 1;
                 int lp = -1;
-                for (int j = 0; j < AC_CT; ++j) lp = mine[j] > 0.f ? s0 + t * AC_CT + j : lp;
+                for (int k = 0; k <= klim; ++k) {
+                  const int p0 = (k * AC_THREADS + t) * E;
+                  for (int e = 0; e < E; ++e) lp = s_w[p0 + e] > 0.f ? s0 + p0 + e : lp;
+                }
                 for (int o = 32; o > 0; o >>= 1) lp = max(lp, __shfl_xor(lp, o));
+                if (t == 0) s_lpos = -1;
+                __syncthreads();
                 if (lane == 0) atomicMax(&s_lpos, lp);
                 __syncthreads();
                 if (t == 0) {
@@ -709,16 +828,21 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
               bonus = arg;
             }
           } else {
+            // the sequence's row results, fetched in one parallel pass, then chased in LDS
+            // (the bonus staging buffer is no longer needed)
+            int32_t* s_rr = (int32_t*)s_w;
+            for (int q = t; q < 2 * (N + 1); q += AC_THREADS) s_rr[q] = ld_i((q & 1) ? &rr[q >> 1].token : &rr[q >> 1].child);
+            __syncthreads();
             if (t == 0) {
               int row = 0, n = 0;
               for (;;) {
-                const int ch = ld_i(&rr[row].child);
+                const int ch = s_rr[2 * row];
                 if (ch < 0 || n >= SV_MAX_DEPTH) break;
                 si.path[n++] = ch;
                 row = ch + 1;
               }
               si.flag = (n << 16) | row;  // A and the stop row
-              s_hit = ld_i(&rr[row].token);
+              s_hit = s_rr[2 * row + 1];
             }
             __syncthreads();
             A = si.flag >> 16;
@@ -827,12 +951,18 @@ extern "C" sv_status sv_accept(const sv_accept_args* args, void* stream) {
   ws.xs = (XSlot*)(base + l.xs);
   hipStream_t st = (hipStream_t)stream;
   const dim3 grid((unsigned)blocks);
+  // rows start on 16 bytes when the row pitch and the base pointers are multiples of 16
+  const size_t esz = a.logits_dtype == SV_BF16 ? 2 : 4;
+  const bool aligned = ((size_t)a.V * esz) % 16 == 0 && ((uintptr_t)a.target_logits % 16) == 0 &&
+                       (a.mode == SV_GREEDY || ((uintptr_t)a.draft_logits % 16) == 0);
+#define SV_ACC_LAUNCH(T, M, AL) hipLaunchKernelGGL((k_accept<T, M, AL>), grid, dim3(AC_THREADS), 0, st, a, G, ws)
   if (a.logits_dtype == SV_BF16) {
-    if (a.mode == SV_STOCHASTIC) hipLaunchKernelGGL((k_accept<uint16_t, SV_STOCHASTIC>), grid, dim3(AC_THREADS), 0, st, a, G, ws);
-    else hipLaunchKernelGGL((k_accept<uint16_t, SV_GREEDY>), grid, dim3(AC_THREADS), 0, st, a, G, ws);
+    if (a.mode == SV_STOCHASTIC) { if (aligned) SV_ACC_LAUNCH(uint16_t, SV_STOCHASTIC, true); else SV_ACC_LAUNCH(uint16_t, SV_STOCHASTIC, false); }
+    else { if (aligned) SV_ACC_LAUNCH(uint16_t, SV_GREEDY, true); else SV_ACC_LAUNCH(uint16_t, SV_GREEDY, false); }
   } else {
-    if (a.mode == SV_STOCHASTIC) hipLaunchKernelGGL((k_accept<float, SV_STOCHASTIC>), grid, dim3(AC_THREADS), 0, st, a, G, ws);
-    else hipLaunchKernelGGL((k_accept<float, SV_GREEDY>), grid, dim3(AC_THREADS), 0, st, a, G, ws);
+    if (a.mode == SV_STOCHASTIC) { if (aligned) SV_ACC_LAUNCH(float, SV_STOCHASTIC, true); else SV_ACC_LAUNCH(float, SV_STOCHASTIC, false); }
+    else { if (aligned) SV_ACC_LAUNCH(float, SV_GREEDY, true); else SV_ACC_LAUNCH(float, SV_GREEDY, false); }
   }
+#undef SV_ACC_LAUNCH
   return sv_launch_status();
 }

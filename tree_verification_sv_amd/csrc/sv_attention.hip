@@ -341,16 +341,18 @@ __global__ void __launch_bounds__(MF_THREADS, 2) k_attn_mfma(sv_attn_args a, Att
           }
       } else if (tree) {
         const int wi = t0 >> 6;  // uniform: the tile is one 64-bit mask word of the query node's bitset
-        const uint64_t aw = qnode[qb] >= 0 ? a.anc_bits[((int64_t)b * N + qnode[qb]) * p.W + wi] : 0ull;
-        const uint32_t a_lo = (uint32_t)aw, a_hi = (uint32_t)(aw >> 32);
+        uint64_t aw = qnode[qb] >= 0 ? a.anc_bits[((int64_t)b * N + qnode[qb]) * p.W + wi] : 0ull;
+        const int lim = N - t0;  // keys of the tile that are tree nodes
+        if (lim < 64) aw &= (1ull << lim) - 1ull;
+        // shift this lane's key half to bit 0, so every register tests a constant bit
+        const uint64_t sh = aw >> (4 * hf);
+        const uint32_t a_lo = (uint32_t)sh, a_hi = (uint32_t)(sh >> 32);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int kk = 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
             const uint32_t word = kb == 0 ? a_lo : a_hi;
-            const bool keep = (t0 + kk < N) & (((word >> (kk & 31)) & 1u) != 0);
-            if (!keep) sacc[qb][kb][r] = -INFINITY;
+            if (((word >> (8 * (r >> 2) + (r & 3))) & 1u) == 0) sacc[qb][kb][r] = -INFINITY;
           }
       }
       float mt = sacc[qb][0][0];
