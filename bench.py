@@ -1,7 +1,10 @@
 """Benchmark of one tree-verification step on one MI355X.
 
-A step is the whole hot path on one batch: sv_build_tree_mask ->
-sv_tree_attention -> sv_accept -> sv_kv_commit, issued on one stream.  The
+A step is the whole hot path on one batch: sv_build_tree_mask, then
+sv_tree_attention on the launch stream beside sv_accept -> sv_kv_commit on a
+side stream (both read only the mask outputs and the inputs; the commit writes
+cache slots the attention does not read), joined at the end of the step
+(--no-overlap: all four back to back on one stream).  The
 default workload is the EAGLE-style static tree at the Llama-3-8B attention
 shape (batch 1, 32 query / 8 KV heads, head_dim 128, 4096-token bf16 prefix,
 60-node tree of depth 6, vocab 128256, stochastic acceptance at T = 1).
@@ -110,6 +113,9 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--instances", type=int, default=0, help="input instances cycled (0: enough to defeat the MALL)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="run the four stages back to back on one stream (default: acceptance and commit on a "
+                         "side stream beside the attention, forked after the mask)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (reference kernel for PMC byte counters)")
@@ -136,8 +142,9 @@ def main():
     steps = [VerifyStep(W.step_inputs(w, d)) for w, d in zip(ws, devs)]
     stream = torch.cuda.current_stream()
 
+    ov = not args.no_overlap
     for i in range(args.warmup):
-        steps[i % R].run()
+        steps[i % R].run(overlap=ov)
     torch.cuda.synchronize()
     if args.copy_mib:  # untimed reference copy: its FETCH/WRITE counters calibrate the byte counts
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
@@ -156,13 +163,13 @@ def main():
             side.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(side):
                 for s in steps:
-                    s.run()
+                    s.run(overlap=ov)
             torch.cuda.current_stream().wait_stream(side)
             torch.cuda.synchronize()
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph):
                 for s in steps:
-                    s.run()
+                    s.run(overlap=ov)
             torch.cuda.synchronize()
             for _ in range(2):
                 graph.replay()
@@ -183,10 +190,10 @@ def main():
         for _ in range(reps):
             graph.replay()
         for i in range(K - reps * R):
-            steps[i].run()
+            steps[i].run(overlap=ov)
     else:
         for i in range(K):
-            steps[i % R].run()
+            steps[i % R].run(overlap=ov)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -231,7 +238,8 @@ def main():
         "config": {"workload": w0.name, "batch": B, "tree_nodes": N, "prefix_len": int(w0.prefix_len.max()),
                    "q_heads": w0.Hq, "kv_heads": w0.Hkv, "head_dim": w0.D, "vocab": w0.V, "max_depth": w0.max_depth,
                    "acceptance": w0.mode, "temperature": w0.temperature, "instances_cycled": R,
-                   "launch": "hip_graph" if use_graph else "eager"},
+                   "launch": "hip_graph" if use_graph else "eager",
+                   "streams": "attention | accept+commit after mask" if ov else "one"},
         "accept_steps_per_s": round(B / (ms_step * 1e-3), 1),
         "hbm_gbs": round(hbm_gbs, 1),
         "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),

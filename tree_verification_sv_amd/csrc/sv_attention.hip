@@ -433,36 +433,44 @@ __global__ void __launch_bounds__(MF_THREADS, 2) k_attn_mfma(sv_attn_args a, Att
   if (!active) return;
 
   // ---- write: bf16 output (single split) or per-split partials: the normalised row
-  // O / l in bf16 and (m, l) in fp32
+  // O / l in bf16 and (m, l) in fp32.  The wave stages its rows in its own query rows of
+  // LDS (no other wave reads them, and its own reads of them are done), swizzled like the
+  // query layout, then stores whole rows with 16 consecutive bytes per lane.
   const int unit = pair * p.qtiles + qtile;
+  const int64_t pidx = (int64_t)unit * p.nsplit + split;
+  unsigned char* ob = qsb + (w * 32 * QB) * ROWB;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int ql = w * 32 * QB + qb * 32 + lq;
     const int m = qtile * p.QT + ql;
-    if (m >= p.M) continue;
     const float inv = lrun[qb] > 0.f ? 1.f / lrun[qb] : 0.f;
-    {
-      uint16_t* orow;
-      if (p.nsplit == 1) {
-        const int node = qnode[qb];  // valid: m < M
-        const int h = g * G + m % G;
-        orow = (uint16_t*)a.out + (((int64_t)b * N + node) * Hq + h) * D;
-      } else {
-        const int64_t pidx = (int64_t)unit * p.nsplit + split;
-        orow = p.opart + (pidx * p.QT + ql) * D;
-        if (hf == 0) *(float2*)(p.mlpart + (pidx * p.QT + ql) * 2) = make_float2(mrun[qb] * p.cscale, lrun[qb]);
+    if (p.nsplit > 1 && hf == 0 && m < p.M)
+      *(float2*)(p.mlpart + (pidx * p.QT + ql) * 2) = make_float2(mrun[qb] * p.cscale, lrun[qb]);
+    const int sw = TL::swz(lq);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int c = 4 * db + rq;  // 16-byte chunk of elements db*32 + 8 rq .. + 7; this lane holds half hf
+        const uint32_t w0 = f32_to_bf16_bits(oacc[qb][db][4 * rq + 0] * inv) |
+                            ((uint32_t)f32_to_bf16_bits(oacc[qb][db][4 * rq + 1] * inv) << 16);
+        const uint32_t w1 = f32_to_bf16_bits(oacc[qb][db][4 * rq + 2] * inv) |
+                            ((uint32_t)f32_to_bf16_bits(oacc[qb][db][4 * rq + 3] * inv) << 16);
+        *(uint2*)(ob + (qb * 32 + lq) * ROWB + ((c ^ sw) << 4) + 8 * hf) = make_uint2(w0, w1);
       }
+  }
+  constexpr int CPR = TL::CPR, RPO = 64 / CPR;  // 16-byte chunks per row, rows per store
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int d = db * 32 + 8 * rq + 4 * hf;
-          const uint32_t w0 = f32_to_bf16_bits(oacc[qb][db][4 * rq + 0] * inv) |
-                              ((uint32_t)f32_to_bf16_bits(oacc[qb][db][4 * rq + 1] * inv) << 16);
-          const uint32_t w1 = f32_to_bf16_bits(oacc[qb][db][4 * rq + 2] * inv) |
-                              ((uint32_t)f32_to_bf16_bits(oacc[qb][db][4 * rq + 3] * inv) << 16);
-          *(uint2*)(orow + d) = make_uint2(w0, w1);
-        }
+  for (int i = 0; i < 32 * QB / RPO; ++i) {
+    const int r = i * RPO + lane / CPR;  // row of the wave's block
+    const int ch = lane % CPR;
+    const uint4 v = *(const uint4*)(ob + r * ROWB + ((ch ^ TL::swz(r)) << 4));
+    const int ql = w * 32 * QB + r;
+    const int m = qtile * p.QT + ql;
+    if (m < p.M) {
+      uint16_t* orow = p.nsplit == 1 ? (uint16_t*)a.out + (((int64_t)b * N + m / G) * Hq + g * G + m % G) * D
+                                     : p.opart + (pidx * p.QT + ql) * D;
+      *(uint4*)(orow + ch * 8) = v;
     }
   }
 }

@@ -1,9 +1,17 @@
-"""One verification step: the four library calls in dependency order on one stream.
+"""One verification step: the four library calls in dependency order.
 
 ``VerifyStep`` owns the output and workspace buffers (allocated once through
 torch), so repeated ``run()`` calls allocate nothing and issue exactly four
 C-ABI calls: sv_build_tree_mask -> sv_tree_attention -> sv_accept ->
-sv_kv_commit.  Nothing here computes; it marshals arguments.
+sv_kv_commit.  Nothing here computes; it marshals arguments and orders
+streams.
+
+Attention and acceptance both read only the mask outputs and the step's
+inputs, and the commit writes cache slots at positions >= prefix_len, which
+the attention never reads.  ``run(overlap=True)`` therefore forks after the
+mask: acceptance and commit go to a side stream while the attention runs on
+the caller's stream, and the caller's stream waits for the side stream at the
+end (a fork/join that HIP graph capture records as a DAG).
 """
 from __future__ import annotations
 
@@ -76,6 +84,16 @@ class VerifyStep:
                                 self.acc["accept_rows"], Dm, self.commit["new_len"], self.commit["committed_slots"],
                                 self.commit["status"], x.block_table, x.paged, x.num_blocks, x.commit_mode)
         self._L = lib()
+        self._side = None
+        self._ev_fork = self._ev_join = None
+
+    def _side_stream(self):
+        import torch
+        if self._side is None:
+            self._side = torch.cuda.Stream(device=self.x.parents.device)  # default priority
+            self._ev_fork = torch.cuda.Event()
+            self._ev_join = torch.cuda.Event()
+        return self._side
 
     # individual stages (same stream)
     def build_mask(self, stream=None):
@@ -93,8 +111,26 @@ class VerifyStep:
     def kv_commit(self, stream=None):
         _check(self._L.sv_kv_commit(ctypes.byref(self._com), _stream(stream)), "sv_kv_commit")
 
-    def run(self, stream=None):
-        self.build_mask(stream)
-        self.attention(stream)
-        self.accept(stream)
-        self.kv_commit(stream)
+    def run(self, stream=None, overlap=False, accept_first=True):
+        if not overlap:
+            self.build_mask(stream)
+            self.attention(stream)
+            self.accept(stream)
+            self.kv_commit(stream)
+            return
+        import torch
+        main = stream if stream is not None else torch.cuda.current_stream()
+        side = self._side_stream()
+        self.build_mask(main)
+        self._ev_fork.record(main)
+        side.wait_event(self._ev_fork)
+        if accept_first:
+            self.accept(side)
+            self.kv_commit(side)
+            self.attention(main)
+        else:
+            self.attention(main)
+            self.accept(side)
+            self.kv_commit(side)
+        self._ev_join.record(side)
+        main.wait_event(self._ev_join)
