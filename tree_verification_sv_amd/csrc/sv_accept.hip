@@ -474,16 +474,14 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
         block_argmax(best, arg, red);
         exchange(gslots, G, rank, ++xtag, 2, xv, ws.err, __float_as_uint(best), (uint32_t)arg);
         if (rank == 0) {
-          if (t == 0) {
-            float bv = __uint_as_float(xv[0][0]);
-            int bi = (int)xv[0][1];
-            for (int k = 1; k < G; ++k) {
-              const float kv = __uint_as_float(xv[k][0]);
-              const int ki = (int)xv[k][1];
-              if (kv > bv || (kv == bv && ki < bi)) { bv = kv; bi = ki; }
+          if (t < 64) {  // wave 0: lane k takes member k's best; the butterfly keeps the lowest id on ties
+            float bv = lane < G ? __uint_as_float(xv[lane][0]) : -FLT_MAX;
+            int bi = lane < G ? (int)xv[lane][1] : 0x7fffffff;
+            wave_argmax(bv, bi);
+            if (t == 0) {
+              st_i(&ws.res[item].child, -1);
+              st_i(&ws.res[item].token, bi);
             }
-            st_i(&ws.res[item].child, -1);
-            st_i(&ws.res[item].token, bi);
           }
           done_by_me = 1;
         }
@@ -623,8 +621,8 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
           const float kappa = (float)(cn * fq / fp);
           const double sl = block_sum(slice_sum(kappa), red) * fp;
           exchange(gslots, G, rank, ++xtag, 2, xv, ws.err, dlo(sl), dhi(sl));
-          double S = 0.0;
-          for (int k = 0; k < G; ++k) S += dof(xv[k][0], xv[k][1]);
+          // lane k of every wave takes member k's sum (G <= 64): one LDS read and a DPP reduction
+          const double S = wave_sumd(lane < G ? dof(xv[lane][0], xv[lane][1]) : 0.0);
           __syncthreads();
           if (S > 0.0) { c = cn; Dn = S; }  // S == 0 only through rounding: keep the residual
         }
@@ -677,12 +675,12 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
             for (int k = 0; k < NK; ++k) col += s_col[k];
             const double sl = col * fp;
             exchange(gslots, G, rank, ++xtag, 2, xv, ws.err, dlo(sl), dhi(sl));
-            double before = 0.0, total = 0.0;
-            for (int k = 0; k < G; ++k) {
-              const double s = dof(xv[k][0], xv[k][1]);
-              if (k < rank) before += s;
-              total += s;
-            }
+            // lane k holds member k's slice total; one inclusive scan gives every member the
+            // same prefixes, total and owner
+            const double sk = lane < G ? dof(xv[lane][0], xv[lane][1]) : 0.0;
+            const double incl_k = wave_scand(sk, lane);
+            const double total = laned(incl_k, G - 1);
+            const double before = laned(incl_k - sk, rank);
             if (!(total > 0.0) && attempt == 0 && c != 0.0) {  // uniform: retry with the previous residual
               c = c_prev;
               __syncthreads();
@@ -692,11 +690,8 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
             const double thr = us * total;
             int owner = G - 1;
             {
-              double pre = 0.0;
-              for (int k = 0; k < G; ++k) {
-                pre += dof(xv[k][0], xv[k][1]);
-                if (pre > thr) { owner = k; break; }
-              }
+              const uint64_t over = __ballot(lane < G && incl_k > thr);
+              if (over) owner = __ffsll((long long)over) - 1;
             }
             if (rank == owner) {
               const double lthr = (thr - before) / fp;  // threshold in this slice's units
