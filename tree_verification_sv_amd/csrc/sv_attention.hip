@@ -478,7 +478,7 @@ __global__ void __launch_bounds__(MF_THREADS, 2) k_attn_mfma(sv_attn_args a, Att
 // merge split partials: one wave per output row (b, node, head).  Every load
 // of a row is issued before any is used (no data-dependent branch between
 // them), so the merge costs one memory round trip, not one per split.
-constexpr int AT_MAX_SPLIT_REG = 16;  // splits merged from registers; more are streamed
+constexpr int AT_MAX_SPLIT_REG = 32;  // splits merged from registers (one round trip up to 32); more are streamed
 template <int D>
 __global__ void __launch_bounds__(256) k_attn_combine(sv_attn_args a, AttnPlan p) {
   const int lane = threadIdx.x & 63;

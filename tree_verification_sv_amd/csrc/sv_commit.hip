@@ -17,30 +17,43 @@ __global__ void __launch_bounds__(256) k_kv_commit(sv_commit_args a, int32_t es)
   const int b = blockIdx.x;
   const int t = threadIdx.x;
   const int Dm = a.max_depth;
+  // validation, one thread per accepted position: every load is issued at once (the
+  // block-table entry is the only one that depends on another load)
+  if (t == 0) s_code = 0x7fffffff;
+  __syncthreads();
+  const int32_t L0 = a.prefix_len[b];
+  const int32_t A0 = a.accept_len[b];
   if (t == 0) {
-    const int32_t L = a.prefix_len[b];
-    const int32_t A = a.accept_len[b];
-    int32_t code = (L < 0 || A < 0 || A > Dm) ? SV_SEQ_PARENT_RANGE : 0;
-    for (int k = 0; code == 0 && k < A; ++k) {
-      const int32_t src = a.commit_mode == SV_COMMIT_PATH ? a.accept_rows[(int64_t)b * Dm + k] : k + 1;
-      if (src < 1 || src > a.N) { code = SV_SEQ_PARENT_RANGE; break; }
-      const int64_t pos = (int64_t)L + k;
-      if (a.paged) {
-        const int64_t blk = pos / a.block_size;
-        if (blk >= a.max_blocks) { code = SV_SEQ_CAPACITY; break; }
-        const int32_t id = a.block_table[(int64_t)b * a.max_blocks + blk];
-        if (id < 1 || id >= a.num_blocks) { code = SV_SEQ_BLOCK; break; }
-        s_slot[k] = (int64_t)id * a.block_size + pos % a.block_size;
-      } else {
-        if (pos >= a.Lcap) { code = SV_SEQ_CAPACITY; break; }
-        s_slot[k] = pos;
-      }
-      s_src[k] = src;
-    }
-    s_code = code;
-    s_L = L;
-    s_A = A;
+    s_L = L0;
+    s_A = A0;
+    if (L0 < 0 || A0 < 0 || A0 > Dm) atomicMin(&s_code, SV_SEQ_PARENT_RANGE);
   }
+  if (t < Dm && L0 >= 0 && A0 >= 0 && A0 <= Dm && t < A0) {
+    const int k = t;
+    int32_t code = 0;
+    const int32_t src = a.commit_mode == SV_COMMIT_PATH ? a.accept_rows[(int64_t)b * Dm + k] : k + 1;
+    const int64_t pos = (int64_t)L0 + k;
+    if (src < 1 || src > a.N) {
+      code = SV_SEQ_PARENT_RANGE;
+    } else if (a.paged) {
+      const int64_t blk = pos / a.block_size;
+      if (blk >= a.max_blocks) {
+        code = SV_SEQ_CAPACITY;
+      } else {
+        const int32_t id = a.block_table[(int64_t)b * a.max_blocks + blk];
+        if (id < 1 || id >= a.num_blocks) code = SV_SEQ_BLOCK;
+        else s_slot[k] = (int64_t)id * a.block_size + pos % a.block_size;
+      }
+    } else {
+      if (pos >= a.Lcap) code = SV_SEQ_CAPACITY;
+      else s_slot[k] = pos;
+    }
+    s_src[k] = src;
+    // the first failing position decides the code, as a walk in position order would
+    if (code != 0) atomicMin(&s_code, (k << 4) | code);
+  }
+  __syncthreads();
+  if (t == 0) s_code = s_code == 0x7fffffff ? 0 : (s_code & 15);
   __syncthreads();
   const int32_t code = s_code, L = s_L, A = s_A;
   if (t < Dm) a.committed_slots[(int64_t)b * Dm + t] = (code == 0 && t < A) ? (int32_t)s_slot[t] : 0;
