@@ -28,11 +28,20 @@
 // entry.  Members of a group trade per-slice partials through tagged 64-bit
 // words (tag and payload in one atomic word, so a reader that sees the tag
 // also sees the value).  Greedy rows need one pass (slice max / argmax, lowest
-// id on ties).  The group that completes the last row of a sequence performs
-// its walk.  Rows resolved: greedy -- the root row and rows with a usable
+// id on ties).  Rows resolved: greedy -- the root row and rows with a usable
 // child (a leaf stop row's argmax is taken by the walker); stochastic -- the
 // root row and the rows of all usable nodes (leaf rows only read the target
 // logits); the work-groups of other rows exit at once.
+//
+// The walk.  Greedy, and stochastic chains or narrow trees (N <= 2 max_depth,
+// where nearly every row is on the path): the group that completes the last
+// row of a sequence walks.  Stochastic wide trees: the walk advances as rows
+// resolve -- a per-sequence frontier names the first row of the accepted path
+// not resolved yet; the work-group that publishes that row takes the frontier
+// over and follows the path through the rows already resolved, until it either
+// reaches the stop row (it writes the outputs and raises the sequence's cancel
+// flag, so its other rows stop at their next exchange) or hands the frontier
+// to the next unresolved row.  Off-path rows then cost nothing after the walk.
 //
 // Forward progress.  Work-groups are dispatched in index order, round-robin
 // over the 8 XCDs; the members of a group are consecutive in their XCD's
@@ -63,17 +72,26 @@ struct XSlot {      // one work-group's partials for one exchange: (tag << 32) |
   uint64_t w[AC_XW];
 };
 
-struct RowRes {     // resolved row
-  int32_t child;    // first accepted child node, -1 when all rejected (stochastic)
-  int32_t token;    // bonus token if the walk stops here (stochastic) / argmax (greedy)
-};
+// A resolved row, one 64-bit word (0 = not resolved in this call): bit 63 set, bits
+// 32..62 the first accepted child node + 1 (0 when all children were rejected), bits
+// 0..31 the bonus token if the walk stops here (stochastic) / the argmax (greedy).
+__device__ __forceinline__ uint64_t res_word(int child, int token) {
+  return (1ull << 63) | ((uint64_t)(uint32_t)(child + 1) << 32) | (uint32_t)token;
+}
+__device__ __forceinline__ bool res_ready(uint64_t v) { return (v >> 63) != 0; }
+__device__ __forceinline__ int res_child(uint64_t v) { return (int)((v >> 32) & 0x7fffffffu) - 1; }
+__device__ __forceinline__ int res_token(uint64_t v) { return (int)(uint32_t)v; }
+constexpr uint32_t AC_FRONT_BUSY = 0xffffffffu;  // the walk's frontier is claimed by a work-group
 
-struct AccWs {      // workspace views
-  uint32_t* gexit;  // [groups] group exit counters
-  uint32_t* seqdone;// [B] rows resolved per sequence
-  uint32_t* err;    // [0] wait-timeout flag, [1] work-groups exited
-  RowRes* res;      // [B, N+1]
-  XSlot* xs;        // [groups * G * 2]: (group * G + rank) * 2 + exchange parity
+struct AccWs {        // workspace views
+  uint32_t* gexit;    // [groups] group exit counters
+  uint32_t* seqdone;  // [B] rows resolved per sequence (greedy)
+  uint32_t* err;      // [0] wait-timeout flag, [1] work-groups exited
+  uint64_t* res;      // [B, N+1] resolved rows
+  uint32_t* frontier; // [B] stochastic walk: the first row of the path not yet resolved
+  uint32_t* cancel;   // [B] stochastic walk finished: remaining rows are not needed
+  uint32_t* seqexit;  // [B] stochastic: work-groups of the sequence that have exited
+  XSlot* xs;          // [groups * G * 2]: (group * G + rank) * 2 + exchange parity
 };
 
 template <typename T>
@@ -202,6 +220,9 @@ __device__ __forceinline__ void st_u64(uint64_t* p, uint64_t v) { __hip_atomic_s
 __device__ __forceinline__ uint32_t ld_u32(uint32_t* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, AGENT); }
 __device__ __forceinline__ uint64_t ld_u64(uint64_t* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, AGENT); }
 __device__ __forceinline__ uint32_t add_u32(uint32_t* p, uint32_t v) { return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, AGENT); }
+__device__ __forceinline__ bool cas_u32(uint32_t* p, uint32_t expect, uint32_t v) {
+  return __hip_atomic_compare_exchange_strong(p, &expect, v, __ATOMIC_RELAXED, __ATOMIC_RELAXED, AGENT);
+}
 __device__ __forceinline__ void st_i(int32_t* p, int32_t v) { st_u32((uint32_t*)p, (uint32_t)v); }
 __device__ __forceinline__ int32_t ld_i(int32_t* p) { return (int32_t)ld_u32((uint32_t*)p); }
 // wait until this thread's memory operations have completed
@@ -223,30 +244,46 @@ __device__ __forceinline__ double dof(uint32_t lo, uint32_t hi) {
 // The wait is bounded: on timeout the error flag is raised, and once it is
 // raised no thread waits any more, so every wave exits (results then carry
 // status SV_SEQ_TIMEOUT).
-__device__ __forceinline__ void exchange(XSlot* gs, int G, int rank, uint32_t tag, int nw, uint32_t (*xv)[AC_XV],
-                                         uint32_t* err, uint32_t w0, uint32_t w1, uint32_t w2 = 0, uint32_t w3 = 0,
-                                         uint32_t w4 = 0, uint32_t w5 = 0) {
+// cancel (nullable): the sequence's walk-finished flag.  It is read once per
+// exchange (alongside the polls) and while waiting; once it is seen set, the
+// work-group's sticky flag *xc is set and the exchange returns true (the row's
+// result is no longer needed; a member that waits for a member that has left
+// sees the flag too).
+__device__ __forceinline__ bool exchange(XSlot* gs, int G, int rank, uint32_t tag, int nw, uint32_t (*xv)[AC_XV],
+                                         uint32_t* err, uint32_t* cancel, int* xc, uint32_t w0, uint32_t w1,
+                                         uint32_t w2 = 0, uint32_t w3 = 0, uint32_t w4 = 0, uint32_t w5 = 0) {
   const int t = threadIdx.x;
   const int par = tag & 1;
   if (t < nw) {
     const uint32_t w = t == 0 ? w0 : t == 1 ? w1 : t == 2 ? w2 : t == 3 ? w3 : t == 4 ? w4 : w5;
     st_u64(&gs[rank * 2 + par].w[t], ((uint64_t)tag << 32) | w);
   }
+  const uint32_t c0 = (cancel && t == 0) ? ld_u32(cancel) : 0u;  // overlaps the polls below
   for (int q = t; q < G * nw; q += AC_THREADS) {
     const int k = q / nw, i = q - k * nw;
     uint64_t* p = &gs[k * 2 + par].w[i];
     uint64_t v = ld_u64(p);
     uint32_t spins = 0;
     while ((uint32_t)(v >> 32) != tag) {
-      if ((++spins & 63) == 0 && (spins > AC_SPIN_LIMIT || ld_u32(err) != 0)) {
+      ++spins;
+      if ((spins & 63) == 0 && (spins > AC_SPIN_LIMIT || ld_u32(err) != 0)) {
         st_u32(err, 1u);
         break;
       }
+      // every fourth poll also reads the cancel flag; both loads are in flight together
+      const bool chk = cancel != nullptr && (spins & 3) == 0;
       v = ld_u64(p);
+      const uint32_t cv = chk ? ld_u32(cancel) : 0u;
+      if (cv != 0u) {
+        *xc = 1;
+        break;
+      }
     }
     xv[k][i] = (uint32_t)v;
   }
+  if (c0) *xc = 1;
   __syncthreads();
+  return *xc != 0;
 }
 
 struct SeqInfo {    // per-sequence facts every work-group derives the same way
@@ -423,6 +460,7 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
   __shared__ __attribute__((aligned(16))) float s_w[MODE == SV_STOCHASTIC ? AC_SLICE : 4];
   __shared__ float s_g[MODE == SV_STOCHASTIC ? Piece<T>::NK * AC_THREADS : 4];
   __shared__ double s_col[Piece<T>::NK];
+  __shared__ int s_xc, s_claim, s_fin;  // walk finished (sticky); stochastic walk: claimed row, finisher
   // work-groups are dispatched round-robin over the 8 XCDs; the members of a
   // group share an XCD (the grid size is a multiple of 8 * G)
   const int t = threadIdx.x, lane = t & 63;
@@ -436,6 +474,8 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
   uint32_t xtag = 0;  // exchanges of this group so far (identical on every member)
   const int64_t item = grp;
   const int s0 = rank * AC_SLICE;  // this work-group's slice of the vocabulary
+  if (t == 0) s_xc = 0;
+  bool live_row = false;
 
   if (item < (int64_t)a.B * (N + 1)) {
     // uniform, and kept in scalar registers so that the slice loads take a scalar resource
@@ -448,11 +488,20 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
     // sequence facts that confirm it is needed (its latency overlaps them); the facts'
     // own loads go first
     SeqRaw sr = seq_fetch(a, b);
+    // stochastic, wide trees: the walk advances as rows resolve and ends the sequence's
+    // remaining rows (below); chains and narrow trees, where nearly every row is on the
+    // path, walk once after the last row
+    const bool incr = MODE == SV_STOCHASTIC && N > 2 * a.max_depth;
+    uint32_t* cancel = incr ? &ws.cancel[b] : nullptr;
+    uint32_t cx0 = 0u;  // the sequence's walk already finished (a late work-group)
+    if (incr && t == 0) cx0 = ld_u32(cancel);
     uint4 rp[NK];
     if constexpr (MODE == SV_STOCHASTIC) load_pieces<T>(prow, s0, V, aligned, t, rp);
-    asm volatile("" : "+v"(sr.tok), "+v"(sr.par), "+v"(sr.dep));  // nothing uses them before this point
+    asm volatile("" : "+v"(sr.tok), "+v"(sr.par), "+v"(sr.dep), "+v"(cx0));  // nothing uses them before this point
+    if (cx0) s_xc = 1;
     seq_facts(a, sr, si);
-    if (row_live(a, si, r)) {  // uniform across the group
+    live_row = row_live(a, si, r);  // the same on every member of the group
+    if (live_row && !s_xc) {
       row_kids(N, r, si);
       int done_by_me = 0;  // this work-group wrote the row result
 
@@ -472,20 +521,19 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
           }
         }
         block_argmax(best, arg, red);
-        exchange(gslots, G, rank, ++xtag, 2, xv, ws.err, __float_as_uint(best), (uint32_t)arg);
+        exchange(gslots, G, rank, ++xtag, 2, xv, ws.err, nullptr, &s_xc, __float_as_uint(best), (uint32_t)arg);
         if (rank == 0) {
           if (t < 64) {  // wave 0: lane k takes member k's best; the butterfly keeps the lowest id on ties
             float bv = lane < G ? __uint_as_float(xv[lane][0]) : -FLT_MAX;
             int bi = lane < G ? (int)xv[lane][1] : 0x7fffffff;
             wave_argmax(bv, bi);
-            if (t == 0) {
-              st_i(&ws.res[item].child, -1);
-              st_i(&ws.res[item].token, bi);
-            }
+            if (t == 0) st_u64(&ws.res[item], res_word(-1, bi));
           }
           done_by_me = 1;
         }
       } else {
+        // the row's resolution; returns early once the sequence's walk has finished
+        [&]() {
         const int K = __builtin_amdgcn_readfirstlane(si.K);
         const bool need_q = K > 0;
         // ---- the slice: raw logits -> slice maxima -> exponentials kept in registers
@@ -571,8 +619,9 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
         }
         zp = block_sum(zp, red);  // its barriers also publish the children's values
         zq = block_sum(zq, red);
-        exchange(gslots, G, rank, ++xtag, 6, xv, ws.err, __float_as_uint(mp), __float_as_uint(mq), dlo(zp), dhi(zp),
-                 dlo(zq), dhi(zq));
+        if (exchange(gslots, G, rank, ++xtag, 6, xv, ws.err, cancel, &s_xc, __float_as_uint(mp),
+                     __float_as_uint(mq), dlo(zp), dhi(zp), dlo(zq), dhi(zq)))
+          return;
         // global statistics: lane k of every wave takes member k's partials (G <= 64); the
         // butterfly reductions give every lane, wave and member the same values
         double Zp, Zq, fp, fq;
@@ -620,7 +669,7 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
           // max(0, p - cn q) = fp * max(0, ep - kappa eq) on this slice, kappa = cn fq / fp
           const float kappa = (float)(cn * fq / fp);
           const double sl = block_sum(slice_sum(kappa), red) * fp;
-          exchange(gslots, G, rank, ++xtag, 2, xv, ws.err, dlo(sl), dhi(sl));
+          if (exchange(gslots, G, rank, ++xtag, 2, xv, ws.err, cancel, &s_xc, dlo(sl), dhi(sl))) return;
           // lane k of every wave takes member k's sum (G <= 64): one LDS read and a DPP reduction
           const double S = wave_sumd(lane < G ? dof(xv[lane][0], xv[lane][1]) : 0.0);
           __syncthreads();
@@ -628,7 +677,7 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
         }
         if (accepted >= 0) {
           if (rank == 0) {
-            if (t == 0) { st_i(&ws.res[item].child, accepted); st_i(&ws.res[item].token, -1); }
+            if (t == 0) st_u64(&ws.res[item], res_word(accepted, -1));
             done_by_me = 1;
           }
         } else {
@@ -674,7 +723,7 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
             double col = 0.0;
             for (int k = 0; k < NK; ++k) col += s_col[k];
             const double sl = col * fp;
-            exchange(gslots, G, rank, ++xtag, 2, xv, ws.err, dlo(sl), dhi(sl));
+            if (exchange(gslots, G, rank, ++xtag, 2, xv, ws.err, cancel, &s_xc, dlo(sl), dhi(sl))) return;
             // lane k holds member k's slice total; one inclusive scan gives every member the
             // same prefixes, total and owner
             const double sk = lane < G ? dof(xv[lane][0], xv[lane][1]) : 0.0;
@@ -732,8 +781,7 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
                     }
                   }
                   if (pick < 0) pick = lastpos >= 0 ? lastpos : min(s0 + p0 + E, V) - 1;
-                  st_i(&ws.res[item].child, -1);
-                  st_i(&ws.res[item].token, pick);
+                  st_u64(&ws.res[item], res_word(-1, pick));
                 }
               } else {
                 // rounding left the threshold unreached: the highest id with a positive weight
@@ -751,8 +799,7 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
                 __syncthreads();
                 if (t == 0) {
                   const int pick = s_lpos >= 0 ? s_lpos : min(s0 + AC_SLICE, V) - 1;
-                  st_i(&ws.res[item].child, -1);
-                  st_i(&ws.res[item].token, pick);
+                  st_u64(&ws.res[item], res_word(-1, pick));
                 }
               }
               done_by_me = 1;
@@ -760,10 +807,97 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
             break;
           }
         }
+        }();
       }
 
-      // ---- the work-group that wrote the row result counts it; the last row of a sequence walks
-      if (done_by_me) {
+      // ---- stochastic: the walk advances as rows resolve.  frontier[b] is the first row of
+      // the accepted path not yet resolved.  The work-group that publishes that row claims
+      // the frontier (compare-and-swap to BUSY) and follows the path through the rows that
+      // are already resolved; it either reaches the stop row (it then writes the outputs
+      // and raises cancel[b], so the sequence's other rows stop) or moves the frontier to
+      // the next unresolved row and checks that row once more, since its publisher may have
+      // looked at the frontier before the move (each side completes its store before its
+      // load, so at least one of them sees the other's).
+      if (MODE == SV_STOCHASTIC && done_by_me) {
+        mem_complete();  // this thread's row-result store (if any) has completed
+        __syncthreads();
+        uint32_t* front = &ws.frontier[b];
+        uint64_t* rr = ws.res + (int64_t)b * (N + 1);
+        uint64_t* s_rr = (uint64_t*)s_w;  // the sequence's row results (the bonus staging buffer is free)
+        if (t == 0) {
+          s_fin = 0;
+          if (incr) {
+            s_claim = cas_u32(front, (uint32_t)r, AC_FRONT_BUSY) ? r : -1;
+          } else {  // the last row of the sequence to resolve walks
+            s_claim = -1;
+            s_fin = add_u32(&ws.seqdone[b], 1u) + 1 == (uint32_t)si.nlive;
+            if (s_fin) st_u32(&ws.seqdone[b], 0u);  // every row of b has been counted
+          }
+        }
+        __syncthreads();
+        if (s_fin) {
+          for (int x = t; x <= N; x += AC_THREADS) s_rr[x] = ld_u64(&rr[x]);
+          __syncthreads();
+        }
+        for (int guard = 0; s_claim >= 0 && guard <= N + 1; ++guard) {  // uniform
+          for (int x = t; x <= N; x += AC_THREADS) s_rr[x] = ld_u64(&rr[x]);
+          __syncthreads();
+          if (t == 0) {
+            int row = s_claim, claim = -1;
+            bool stop = false;
+            for (int n = 0; n <= N + 1; ++n) {
+              const uint64_t v = s_rr[row];
+              if (!res_ready(v)) break;
+              const int ch = res_child(v);
+              if (ch < 0 || ch >= N) { stop = true; break; }
+              row = ch + 1;
+            }
+            if (stop) {
+              s_fin = 1;
+            } else {
+              st_u32(front, (uint32_t)row);
+              mem_complete();
+              if (res_ready(ld_u64(&rr[row])) && cas_u32(front, (uint32_t)row, AC_FRONT_BUSY)) claim = row;
+            }
+            s_claim = claim;
+          }
+          __syncthreads();
+        }
+        if (s_fin) {
+          // the path from the root in the LDS copy: every row on it was resolved before the
+          // frontier passed it
+          if (t == 0) {
+            int row = 0, n = 0;
+            for (;;) {
+              const int ch = res_child(s_rr[row]);
+              if (ch < 0 || ch >= N || n >= SV_MAX_DEPTH) break;
+              si.path[n++] = ch;
+              row = ch + 1;
+            }
+            si.flag = (n << 16) | row;  // A and the stop row
+            s_hit = res_token(s_rr[row]);
+          }
+          __syncthreads();
+          const int A = si.flag >> 16, stop_row = si.flag & 0xffff, bonus = s_hit;
+          const int Dm = a.max_depth;
+          if (t == 0) {
+            a.accept_len[b] = A;
+            a.num_out[b] = A + 1;
+            a.stop_row[b] = stop_row;
+            a.status[b] = ld_u32(ws.err) ? SV_SEQ_TIMEOUT : (si.bad_token ? SV_SEQ_TOKEN : 0);
+          }
+          if (t < Dm) a.accept_rows[(int64_t)b * Dm + t] = t < A ? si.path[t] + 1 : 0;
+          if (t <= Dm)
+            a.out_tokens[(int64_t)b * (Dm + 1) + t] = t < A ? si.tok[si.path[t]] : (t == A ? bonus : 0);
+          if (incr && t == 0) st_u32(cancel, 1u);  // the sequence's remaining rows are not needed
+          if (!incr)  // every row result of b has been read: leave them cleared for the next call
+            for (int x = t; x <= N; x += AC_THREADS) st_u64(&rr[x], 0ull);
+        }
+      }
+
+      // ---- greedy: the work-group that wrote the row result counts it; the last row of a
+      // sequence walks
+      if (MODE == SV_GREEDY && done_by_me) {
         mem_complete();  // this thread's row-result stores (if any) have completed
         __syncthreads();
         if (t == 0) {
@@ -774,12 +908,12 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
         if (s_last) {
           // ----------------------------------------------------- walk of sequence b
           int A = 0, stop_row = 0, bonus = 0;
-          RowRes* rr = ws.res + (int64_t)b * (N + 1);
-          if constexpr (MODE == SV_GREEDY) {
+          uint64_t* rr = ws.res + (int64_t)b * (N + 1);
+          {
             // match[i]: token equals its parent row's argmax; accepted: the whole root path matches
             {  // wave w holds nodes 64 w .. 64 w + 63: its ballot is bitset word w
               const uint64_t mb =
-                  __ballot(t < N && si.usable[t] && a.tokens[(int64_t)b * N + t] == ld_i(&rr[si.par[t] + 1].token));
+                  __ballot(t < N && si.usable[t] && a.tokens[(int64_t)b * N + t] == res_token(ld_u64(&rr[si.par[t] + 1])));
               if (lane == 0 && (t >> 6) < SV_MAX_W) s_match[t >> 6] = mb;
             }
             __syncthreads();
@@ -807,7 +941,7 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
               }
             }
             if (row_live(a, si, stop_row)) {
-              if (t == 0) s_hit = ld_i(&rr[stop_row].token);
+              if (t == 0) s_hit = res_token(ld_u64(&rr[stop_row]));
               __syncthreads();
               bonus = s_hit;
             } else {
@@ -822,27 +956,6 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
               block_argmax(best, arg, red);
               bonus = arg;
             }
-          } else {
-            // the sequence's row results, fetched in one parallel pass, then chased in LDS
-            // (the bonus staging buffer is no longer needed)
-            int32_t* s_rr = (int32_t*)s_w;
-            for (int q = t; q < 2 * (N + 1); q += AC_THREADS) s_rr[q] = ld_i((q & 1) ? &rr[q >> 1].token : &rr[q >> 1].child);
-            __syncthreads();
-            if (t == 0) {
-              int row = 0, n = 0;
-              for (;;) {
-                const int ch = s_rr[2 * row];
-                if (ch < 0 || n >= SV_MAX_DEPTH) break;
-                si.path[n++] = ch;
-                row = ch + 1;
-              }
-              si.flag = (n << 16) | row;  // A and the stop row
-              s_hit = s_rr[2 * row + 1];
-            }
-            __syncthreads();
-            A = si.flag >> 16;
-            stop_row = si.flag & 0xffff;
-            bonus = s_hit;
           }
           __syncthreads();
           const int Dm = a.max_depth;
@@ -853,6 +966,8 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
             a.status[b] = ld_u32(ws.err) ? SV_SEQ_TIMEOUT : (si.bad_token ? SV_SEQ_TOKEN : 0);
             st_u32(&ws.seqdone[b], 0u);  // every row of b has been counted: ready for the next call
           }
+          // every row result of b has been read: leave them cleared for the next call
+          for (int x = t; x <= N; x += AC_THREADS) st_u64(&rr[x], 0ull);
           if (t < Dm) a.accept_rows[(int64_t)b * Dm + t] = t < A ? si.path[t] + 1 : 0;
           if (t <= Dm)
             a.out_tokens[(int64_t)b * (Dm + 1) + t] = t < A ? a.tokens[(int64_t)b * N + si.path[t]] : (t == A ? bonus : 0);
@@ -861,26 +976,39 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
     }
   }
 
-  // ---- leave every counter and exchange slot zeroed for the next call
+  // ---- leave every counter and exchange slot zeroed for the next call.  The three exit
+  // counts (group, sequence, grid) are independent and go out together; the last arrival
+  // at each clears what it guards.
+  mem_complete();  // this work-group's stores (results, outputs) have completed
   __syncthreads();
+  // (stochastic wide trees only: elsewhere the walker is the sequence's last reader of its
+  // row results and clears them itself)
+  const bool seq_item = MODE == SV_STOCHASTIC && N > 2 * a.max_depth && item < (int64_t)a.B * (N + 1);
+  const int bq = seq_item ? (int)(item / (N + 1)) : 0;
   if (t == 0) {
-    mem_complete();
-    int last = 1;
-    if (G > 1) {
-      const uint32_t old = add_u32(ws.gexit + grp, 1u);
-      last = old + 1 == (uint32_t)G;  // every member of the group passed its last exchange
-      if (last) st_u32(ws.gexit + grp, 0u);
-    }
-    s_last = last;
+    const uint32_t og = G > 1 ? add_u32(ws.gexit + grp, 1u) : 0u;
+    const uint32_t os = seq_item ? add_u32(&ws.seqexit[bq], 1u) : 0u;
+    const uint32_t oe = add_u32(ws.err + 1, 1u);
+    s_last = G == 1 || og + 1 == (uint32_t)G;  // every member of the group passed its last exchange
+    s_claim = seq_item && os + 1 == (uint32_t)((N + 1) * G);  // every work-group of the sequence left
+    s_fin = oe + 1 == gridDim.x;                              // the whole grid has finished
   }
   __syncthreads();
-  if (s_last && xtag > 0)
+  // (a member that left early on a finished walk may have exchanged less than the others,
+  // so the slots of every live row are cleared)
+  if (s_last && (xtag > 0 || live_row))
     for (int i = t; i < G * 2 * AC_XW; i += AC_THREADS) st_u64(&gslots[i / AC_XW].w[i % AC_XW], 0ull);
-  mem_complete();
-  __syncthreads();
+  if (s_claim) {  // stochastic: the sequence's row results, frontier, cancel flag and exit count
+    for (int x = t; x <= N; x += AC_THREADS) st_u64(&ws.res[(int64_t)bq * (N + 1) + x], 0ull);
+    if (t == 0) {
+      st_u32(&ws.frontier[bq], 0u);
+      st_u32(&ws.cancel[bq], 0u);
+      st_u32(&ws.seqexit[bq], 0u);
+    }
+  }
   if (t == 0) {
-    const uint32_t done = add_u32(ws.err + 1, 1u);
-    if (done + 1 == gridDim.x) {  // the whole grid has finished: clear the timeout flag
+    if (G > 1 && s_last) st_u32(ws.gexit + grp, 0u);
+    if (s_fin) {  // clear the timeout flag
       st_u32(ws.err, 0u);
       st_u32(ws.err + 1, 0u);
     }
@@ -895,7 +1023,7 @@ int groups_G(const sv_accept_args& a) {
 int64_t num_groups(const sv_accept_args& a) { return ((int64_t)a.B * (a.N + 1) + 7) / 8 * 8; }
 
 struct WsLayout {
-  size_t gexit, seqdone, err, res, xs, total;
+  size_t gexit, seqdone, err, res, frontier, cancel, seqexit, xs, total;
 };
 WsLayout ws_layout(const sv_accept_args& a) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -905,7 +1033,10 @@ WsLayout ws_layout(const sv_accept_args& a) {
   l.gexit = o; o = up(o + NG * 4);
   l.seqdone = o; o = up(o + (size_t)a.B * 4);
   l.err = o; o = up(o + 8);
-  l.res = o; o = up(o + (size_t)a.B * (a.N + 1) * sizeof(RowRes));
+  l.res = o; o = up(o + (size_t)a.B * (a.N + 1) * sizeof(uint64_t));
+  l.frontier = o; o = up(o + (size_t)a.B * 4);
+  l.cancel = o; o = up(o + (size_t)a.B * 4);
+  l.seqexit = o; o = up(o + (size_t)a.B * 4);
   l.xs = o; o = up(o + NG * G * 2 * sizeof(XSlot));
   l.total = o;
   return l;
@@ -942,7 +1073,10 @@ extern "C" sv_status sv_accept(const sv_accept_args* args, void* stream) {
   ws.gexit = (uint32_t*)(base + l.gexit);
   ws.seqdone = (uint32_t*)(base + l.seqdone);
   ws.err = (uint32_t*)(base + l.err);
-  ws.res = (RowRes*)(base + l.res);
+  ws.res = (uint64_t*)(base + l.res);
+  ws.frontier = (uint32_t*)(base + l.frontier);
+  ws.cancel = (uint32_t*)(base + l.cancel);
+  ws.seqexit = (uint32_t*)(base + l.seqexit);
   ws.xs = (XSlot*)(base + l.xs);
   hipStream_t st = (hipStream_t)stream;
   const dim3 grid((unsigned)blocks);
