@@ -305,21 +305,27 @@ __global__ void __launch_bounds__(MF_THREADS, 2) k_attn_mfma(sv_attn_args a, Att
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[qb][kb][r] = 0.f;
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      sv_bf16x8 qf[QB];
+    // the fragments of k-step ds + 1 are read while the MFMAs of step ds run, so the LDS
+    // latency is hidden behind them
+    sv_bf16x8 qf[2][QB], kf[2][2];
+    auto frag = [&](int ds, int buf) {
       const int kslot = ((2 * ds + hf) ^ k_swz) * 16;  // Q and K rows share the swizzle of row lq
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
-        qf[qb] = *(const sv_bf16x8*)(qsb + (w * 32 * QB + qb * 32) * ROWB + k_off + kslot);
+        qf[buf][qb] = *(const sv_bf16x8*)(qsb + (w * 32 * QB + qb * 32) * ROWB + k_off + kslot);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const sv_bf16x8 kf = *(const sv_bf16x8*)(Kb + kb * 32 * ROWB + k_off + kslot);
+      for (int kb = 0; kb < 2; ++kb) kf[buf][kb] = *(const sv_bf16x8*)(Kb + kb * 32 * ROWB + k_off + kslot);
+    };
+    frag(0, 0);
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      if (ds + 1 < DS) frag(ds + 1, (ds + 1) & 1);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb], sacc[qb][kb], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // fragment reads stay next to their MFMAs (register pressure)
+          sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds & 1][kb], qf[ds & 1][qb], sacc[qb][kb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);  // one step in flight at a time (register pressure)
     }
 
     __builtin_amdgcn_sched_barrier(0);
@@ -365,15 +371,25 @@ __global__ void __launch_bounds__(MF_THREADS, 2) k_attn_mfma(sv_attn_args a, Att
       const float ms = mnew == -INFINITY ? 0.f : mnew * p.cscale;  // nothing visible yet: weights stay 0
       alpha[qb] = __builtin_amdgcn_exp2f(mrun[qb] * p.cscale - ms);
       moved |= mnew != mrun[qb];
-      float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][r], p.cscale, -ms));
-          psum += e;
-          pf[qb][kb][r >> 3][r & 7] = (__bf16)e;
+        for (int r = 0; r < 16; ++r)
+          pf[qb][kb][r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][r], p.cscale, -ms));
+      // the row sum of the bf16 weights the P V product uses: two per dot instruction
+      float psum0 = 0.f, psum1 = 0.f;
+      const sv_bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const sv_bf16x8 v = pf[qb][kb][t2];
+          psum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one2, psum0, false);
+          psum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one2, psum1, false);
+          psum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one2, psum0, false);
+          psum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one2, psum1, false);
         }
+      float psum = psum0 + psum1;
       psum += __shfl_xor(psum, 32);
       lrun[qb] = lrun[qb] * alpha[qb] + psum;
       mrun[qb] = mnew;

@@ -10,6 +10,7 @@
 #define SV_MAX_W 4  // ceil(SV_MAX_N / 64)
 
 typedef __bf16 sv_bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 sv_bf16x2 __attribute__((ext_vector_type(2)));
 typedef float sv_f32x16 __attribute__((ext_vector_type(16)));
 typedef float sv_f32x4 __attribute__((ext_vector_type(4)));
 
