@@ -104,38 +104,27 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
-// Transposing 8-byte LDS reads (ds_read_b64_tr_b16) for one 16-key step: in
-// every 16-lane group, lane 4q+e receives element e of the 8-byte pieces
-// addressed by lanes q, 4+q, 8+q and 12+q.  Written as inline assembly with an
-// explicit LDS wait: through the builtin, the compiler cannot tell these reads
-// from the tile buffer that is still being filled by direct global->LDS loads
-// and would wait for those loads as well.
-template <int NB>
-__device__ __forceinline__ void read_tr(uint2 (&lo)[NB], uint2 (&hi)[NB], const uint32_t (&alo)[NB],
-                                        const uint32_t (&ahi)[NB]);
-template <>
-__device__ __forceinline__ void read_tr<4>(uint2 (&lo)[4], uint2 (&hi)[4], const uint32_t (&alo)[4],
-                                           const uint32_t (&ahi)[4]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %9\n\t"
-      "ds_read_b64_tr_b16 %2, %10\n\tds_read_b64_tr_b16 %3, %11\n\t"
-      "ds_read_b64_tr_b16 %4, %12\n\tds_read_b64_tr_b16 %5, %13\n\t"
-      "ds_read_b64_tr_b16 %6, %14\n\tds_read_b64_tr_b16 %7, %15\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]), "=&v"(lo[3]), "=&v"(hi[3])
-      : "v"(alo[0]), "v"(ahi[0]), "v"(alo[1]), "v"(ahi[1]), "v"(alo[2]), "v"(ahi[2]), "v"(alo[3]), "v"(ahi[3])
-      : "memory");
-}
-template <>
-__device__ __forceinline__ void read_tr<2>(uint2 (&lo)[2], uint2 (&hi)[2], const uint32_t (&alo)[2],
-                                           const uint32_t (&ahi)[2]) {
+// Transposing 8-byte LDS reads (ds_read_b64_tr_b16): in every 16-lane group,
+// lane 4q+e receives element e of the 8-byte pieces addressed by lanes q, 4+q,
+// 8+q and 12+q.  Written as inline assembly: through the builtin, the compiler
+// cannot tell these reads from the tile buffer that is still being filled by
+// direct global->LDS loads and would wait for those loads as well.
+// Four transposing reads (two d-blocks, low and high 8 keys) issued without waiting;
+// tr_wait<N> must run before the values are used: it waits until at most N LDS
+// operations are outstanding, and ties the registers to that point so that the
+// compiler neither reads nor moves them earlier.
+__device__ __forceinline__ void tr_read_issue(uint2 (&lo)[2], uint2 (&hi)[2], const uint32_t (&alo)[2],
+                                              const uint32_t (&ahi)[2]) {
   asm volatile(
       "ds_read_b64_tr_b16 %0, %4\n\tds_read_b64_tr_b16 %1, %5\n\t"
-      "ds_read_b64_tr_b16 %2, %6\n\tds_read_b64_tr_b16 %3, %7\n\t"
-      "s_waitcnt lgkmcnt(0)"
+      "ds_read_b64_tr_b16 %2, %6\n\tds_read_b64_tr_b16 %3, %7"
       : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1])
       : "v"(alo[0]), "v"(ahi[0]), "v"(alo[1]), "v"(ahi[1])
       : "memory");
+}
+template <int N>
+__device__ __forceinline__ void tr_wait(uint2 (&lo)[2], uint2 (&hi)[2]) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(lo[0]), "+v"(hi[0]), "+v"(lo[1]), "+v"(hi[1]) : "n"(N) : "memory");
 }
 
 template <int D>
@@ -406,31 +395,46 @@ __global__ void __launch_bounds__(MF_THREADS, 2) k_attn_mfma(sv_attn_args a, Att
     }
 
     __builtin_amdgcn_sched_barrier(0);
-    // ---- O^T += V^T P^T; the 16-key step (kb, t2) holds keys 32 kb + 16 t2 + 4 hf + {0..3, 8..11}
+    // ---- O^T += V^T P^T; the 16-key step (kb, t2) holds keys 32 kb + 16 t2 + 4 hf + {0..3, 8..11}.
+    // Half-steps of two d-blocks: the transposing reads of half-step h + 1 are issued before
+    // the MFMAs of half-step h, which wait only for their own reads (LDS reads complete in
+    // order, so at most the 4 newer reads may still be outstanding).
+    constexpr int NH = 2 * DB;  // 4 steps (kb, t2) x DB / 2 halves
+    uint2 vlo[2][2], vhi[2][2];
+    auto tr_issue = [&](int h, int buf) {
+      const int st = h / (DB / 2), d0 = (h % (DB / 2)) * 2;  // step kb * 2 + t2, first d-block
+      const int kb = st >> 1, t2 = st & 1;
+      const uint32_t rlo = lds_addr(Vb) + (32 * kb + 16 * t2 + tr_row) * ROWB + tr_half;
+      const uint32_t rhi = rlo + 8 * ROWB;
+      uint32_t alo[2], ahi[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const uint32_t rlo = lds_addr(Vb) + (32 * kb + 16 * t2 + tr_row) * ROWB + tr_half;
-        const uint32_t rhi = rlo + 8 * ROWB;
-        uint32_t alo[DB], ahi[DB];
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int c = 4 * db + tr_chunk;
-          alo[db] = rlo + ((c ^ tr_swz_lo) << 4);
-          ahi[db] = rhi + ((c ^ tr_swz_hi) << 4);
-        }
-        uint2 vlo[DB], vhi[DB];
-        read_tr<DB>(vlo, vhi, alo, ahi);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const sv_bf16x8 vf = __builtin_bit_cast(sv_bf16x8, make_uint4(vlo[db].x, vlo[db].y, vhi[db].x, vhi[db].y));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][kb][t2], oacc[qb][db], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < 2; ++j) {
+        const int c = 4 * (d0 + j) + tr_chunk;
+        alo[j] = rlo + ((c ^ tr_swz_lo) << 4);
+        ahi[j] = rhi + ((c ^ tr_swz_hi) << 4);
       }
+      tr_read_issue(vlo[buf], vhi[buf], alo, ahi);
+    };
+    tr_issue(0, 0);
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const int buf = h & 1;
+      if (h + 1 < NH) {
+        tr_issue(h + 1, buf ^ 1);
+        tr_wait<4>(vlo[buf], vhi[buf]);
+      } else {
+        tr_wait<0>(vlo[buf], vhi[buf]);
+      }
+      const int st = h / (DB / 2), d0 = (h % (DB / 2)) * 2;
+      const int kb = st >> 1, t2 = st & 1;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const sv_bf16x8 vf = __builtin_bit_cast(sv_bf16x8, make_uint4(vlo[buf][j].x, vlo[buf][j].y, vhi[buf][j].x, vhi[buf][j].y));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          oacc[qb][d0 + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][kb][t2], oacc[qb][d0 + j], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
