@@ -945,13 +945,30 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
               __syncthreads();
               bonus = s_hit;
             } else {
-              // leaf stop row: argmax by this work-group
+              // leaf stop row: argmax by this work-group, one slice at a time with the next
+              // slice's loads in flight (a thread visits its entries in ascending id)
               const T* srow = (const T*)a.target_logits + ((int64_t)b * (N + 1) + stop_row) * V;
               float best = -FLT_MAX;
               int arg = 0x7fffffff;
-              for (int v = t; v < V; v += AC_THREADS) {
-                const float x = ldf(srow, v);
-                if (x > best) { best = x; arg = v; }
+              uint4 r0[NK], r1[NK];
+              auto consume = [&](const uint4 (&raw)[NK], int gs) {
+#pragma unroll
+                for (int k = 0; k < NK; ++k) {
+                  float x[E];
+                  unpack16<T>(raw[k], x);
+                  const int v = piece_v<T>(gs * AC_SLICE, k, t);
+#pragma unroll
+                  for (int e = 0; e < E; ++e)
+                    if (v + e < V && x[e] > best) { best = x[e]; arg = v + e; }
+                }
+              };
+              load_pieces<T>(srow, 0, V, aligned, t, r0);
+              for (int gs = 0; gs < G; gs += 2) {
+                if (gs + 1 < G) load_pieces<T>(srow, (gs + 1) * AC_SLICE, V, aligned, t, r1);
+                consume(r0, gs);
+                if (gs + 1 >= G) break;
+                if (gs + 2 < G) load_pieces<T>(srow, (gs + 2) * AC_SLICE, V, aligned, t, r0);
+                consume(r1, gs + 1);
               }
               block_argmax(best, arg, red);
               bonus = arg;
