@@ -1,8 +1,8 @@
 """Benchmark of one tree-verification step on one MI355X.
 
 A step is the whole hot path on one batch: sv_build_tree_mask, then
-sv_tree_attention on the launch stream beside sv_accept -> sv_kv_commit on a
-side stream (both read only the mask outputs and the inputs; the commit writes
+sv_tree_attention on the launch stream (issued first) beside sv_accept ->
+sv_kv_commit on a side stream (both read only the mask outputs and the inputs; the commit writes
 cache slots the attention does not read), joined at the end of the step
 (--no-overlap: all four back to back on one stream).  The
 default workload is the EAGLE-style static tree at the Llama-3-8B attention

@@ -11,7 +11,10 @@ inputs, and the commit writes cache slots at positions >= prefix_len, which
 the attention never reads.  ``run(overlap=True)`` therefore forks after the
 mask: acceptance and commit go to a side stream while the attention runs on
 the caller's stream, and the caller's stream waits for the side stream at the
-end (a fork/join that HIP graph capture records as a DAG).
+end (a fork/join that HIP graph capture records as a DAG).  The attention is
+issued first by default (``accept_first=False``): measured on MI355X, the step
+is shorter when the attention's work-groups take the compute units first and
+the acceptance fills them as they free up.
 """
 from __future__ import annotations
 
@@ -111,7 +114,7 @@ class VerifyStep:
     def kv_commit(self, stream=None):
         _check(self._L.sv_kv_commit(ctypes.byref(self._com), _stream(stream)), "sv_kv_commit")
 
-    def run(self, stream=None, overlap=False, accept_first=True):
+    def run(self, stream=None, overlap=False, accept_first=False):
         if not overlap:
             self.build_mask(stream)
             self.attention(stream)
