@@ -19,11 +19,11 @@
 // that row alone.  Every row is therefore resolved independently and in
 // parallel, and the walk is a pointer chase over the per-row results.
 //
-// Work decomposition.  A group of G work-groups resolves one row; each owns a
-// 16384-entry slice of the vocabulary.  Thread t owns the 16-byte pieces
-// k * 256 + t (k = 0 .. 64 / (16 / sizeof(T)) - 1) of its slice, so every load
-// instruction of a wave reads 1 KB of consecutive logits.  The exponentials
-// are computed once into registers; each later pass over the row (a
+// Work decomposition.  A group of G work-groups resolves one row; each of TH
+// threads (512 greedy, 256 stochastic) owns a slice of TH * 128 bytes of the
+// vocabulary.  Thread t owns the 16-byte pieces k * TH + t (k = 0 .. 7) of its
+// slice, so every load instruction of a wave reads 1 KB of consecutive logits.
+// The exponentials are computed once into registers; each later pass over the row (a
 // rejection's residual sum, the bonus scan) is a few register operations per
 // entry.  Members of a group trade per-slice partials through tagged 64-bit
 // words (tag and payload in one atomic word, so a reader that sees the tag
@@ -59,10 +59,15 @@
 
 namespace {
 
-constexpr int AC_THREADS = 256;
-constexpr int AC_NW = AC_THREADS / 64;         // waves per work-group
-constexpr int AC_CT = 64;                      // vocabulary entries per thread
-constexpr int AC_SLICE = AC_THREADS * AC_CT;   // 16384 entries per work-group
+// threads per work-group: 512 for greedy rows (half the work-groups of 256-thread ones,
+// fewer to dispatch), 256 for stochastic rows (smaller barriers and bonus scans, and the
+// residual staging fits two work-groups per compute unit)
+template <int MODE> constexpr int ac_threads() { return MODE == SV_STOCHASTIC ? 256 : 512; }
+constexpr int AC_NWMAX = 8;                    // waves per work-group at most
+// vocabulary entries per thread: 8 pieces of 16 bytes (64 bf16 / 32 fp32 logits), so a
+// work-group's slice is 8 * 16 bytes per thread
+template <typename T> constexpr int ac_ct() { return 8 * (16 / (int)sizeof(T)); }
+template <typename T, int TH> constexpr int ac_slice() { return TH * ac_ct<T>(); }
 constexpr int AC_MAXG = 64;                    // work-groups per row group (vocabulary up to 1M entries)
 constexpr int AC_XW = 8;                       // tagged words per exchange slot
 constexpr int AC_XV = 6;                       // words an exchange carries at most
@@ -173,29 +178,32 @@ __device__ __forceinline__ double wave_scand(double x, int lane) {
 }
 
 struct Red {
-  float f[AC_NW];
-  double d[AC_NW];
-  int i[AC_NW];
+  float f[AC_NWMAX];
+  double d[AC_NWMAX];
+  int i[AC_NWMAX];
 };
 
+template <int TH>
 __device__ __forceinline__ float block_max(float x, Red& r) {
   x = wave_maxf(x);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) r.f[threadIdx.x >> 6] = x;
   __syncthreads();
   float m = r.f[0];
-  for (int k = 1; k < AC_NW; ++k) m = fmaxf(m, r.f[k]);
+  for (int k = 1; k < TH / 64; ++k) m = fmaxf(m, r.f[k]);
   return m;
 }
+template <int TH>
 __device__ __forceinline__ double block_sum(double x, Red& r) {
   x = wave_sumd(x);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) r.d[threadIdx.x >> 6] = x;
   __syncthreads();
   double s = 0.0;
-  for (int k = 0; k < AC_NW; ++k) s += r.d[k];
+  for (int k = 0; k < TH / 64; ++k) s += r.d[k];
   return s;
 }
+template <int TH>
 __device__ __forceinline__ void block_argmax(float& v, int& i, Red& r) {
   wave_argmax(v, i);
   __syncthreads();
@@ -203,7 +211,7 @@ __device__ __forceinline__ void block_argmax(float& v, int& i, Red& r) {
   __syncthreads();
   v = r.f[0];
   i = r.i[0];
-  for (int k = 1; k < AC_NW; ++k)
+  for (int k = 1; k < TH / 64; ++k)
     if (r.f[k] > v || (r.f[k] == v && r.i[k] < i)) { v = r.f[k]; i = r.i[k]; }
 }
 
@@ -249,6 +257,7 @@ __device__ __forceinline__ double dof(uint32_t lo, uint32_t hi) {
 // work-group's sticky flag *xc is set and the exchange returns true (the row's
 // result is no longer needed; a member that waits for a member that has left
 // sees the flag too).
+template <int TH>
 __device__ __forceinline__ bool exchange(XSlot* gs, int G, int rank, uint32_t tag, int nw, uint32_t (*xv)[AC_XV],
                                          uint32_t* err, uint32_t* cancel, int* xc, uint32_t w0, uint32_t w1,
                                          uint32_t w2 = 0, uint32_t w3 = 0, uint32_t w4 = 0, uint32_t w5 = 0) {
@@ -259,7 +268,7 @@ __device__ __forceinline__ bool exchange(XSlot* gs, int G, int rank, uint32_t ta
     st_u64(&gs[rank * 2 + par].w[t], ((uint64_t)tag << 32) | w);
   }
   const uint32_t c0 = (cancel && t == 0) ? ld_u32(cancel) : 0u;  // overlaps the polls below
-  for (int q = t; q < G * nw; q += AC_THREADS) {
+  for (int q = t; q < G * nw; q += TH) {
     const int k = q / nw, i = q - k * nw;
     uint64_t* p = &gs[k * 2 + par].w[i];
     uint64_t v = ld_u64(p);
@@ -292,8 +301,8 @@ struct SeqInfo {    // per-sequence facts every work-group derives the same way
   uint8_t usable[SV_MAX_N];
   uint8_t haskid[SV_MAX_N + 1];  // row has a usable child
   int16_t kids[SV_MAX_N];     // usable children of the current row, ascending
-  int32_t wcount[AC_NW];
-  int32_t wlive[AC_NW];
+  int32_t wcount[AC_NWMAX];
+  int32_t wlive[AC_NWMAX];
   int32_t K;                  // number of usable children of the current row
   int32_t nlive;              // rows this sequence resolves
   int32_t bad_token;
@@ -318,10 +327,11 @@ __device__ __forceinline__ SeqRaw seq_fetch(const sv_accept_args& a, int b) {
   }
   return r;
 }
+template <int TH>
 __device__ __forceinline__ void seq_facts(const sv_accept_args& a, const SeqRaw& sr, SeqInfo& si) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int N = a.N;
-  for (int x = t; x <= N; x += AC_THREADS) si.haskid[x] = 0;
+  for (int x = t; x <= N; x += TH) si.haskid[x] = 0;
   if (t == 0) si.bad_token = 0;
   __syncthreads();
   bool u = false;
@@ -343,13 +353,14 @@ __device__ __forceinline__ void seq_facts(const sv_accept_args& a, const SeqRaw&
   __syncthreads();
   if (t == 0) {
     int nl = 0;
-    for (int k = 0; k < AC_NW; ++k) nl += si.wlive[k];
+    for (int k = 0; k < TH / 64; ++k) nl += si.wlive[k];
     si.nlive = nl + 1;  // + the root row
   }
   __syncthreads();
 }
 
 // usable children of row r in ascending index, from the sequence facts
+template <int TH>
 __device__ __forceinline__ void row_kids(int N, int r, SeqInfo& si) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const bool kid = t < N && si.usable[t] && si.par[t] + 1 == r;
@@ -357,7 +368,7 @@ __device__ __forceinline__ void row_kids(int N, int r, SeqInfo& si) {
   if (lane == 0) si.wcount[wv] = __popcll(m);
   __syncthreads();
   int off = 0, K = 0;
-  for (int k = 0; k < AC_NW; ++k) {
+  for (int k = 0; k < TH / 64; ++k) {
     if (k < wv) off += si.wcount[k];
     K += si.wcount[k];
   }
@@ -374,7 +385,7 @@ __device__ __forceinline__ bool row_live(const sv_accept_args& a, const SeqInfo&
 // ---------------------------------------------------------------- slice loads
 template <typename T> struct Piece {
   static constexpr int E = 16 / sizeof(T);  // entries per 16-byte piece
-  static constexpr int NK = AC_CT / E;      // pieces per thread
+  static constexpr int NK = ac_ct<T>() / E;  // pieces per thread
 };
 template <typename T> __device__ __forceinline__ T lowest_of();
 template <> __device__ __forceinline__ float lowest_of<float>() { return -FLT_MAX; }
@@ -402,8 +413,8 @@ __device__ __forceinline__ void opaque(uint4 (&raw)[NK]) {
   for (int k = 0; k < NK; ++k) asm volatile("" : "+v"(raw[k].x), "+v"(raw[k].y), "+v"(raw[k].z), "+v"(raw[k].w));
 }
 // first entry of piece k of thread t in a slice starting at s0
-template <typename T>
-__device__ __forceinline__ int piece_v(int s0, int k, int t) { return s0 + (k * AC_THREADS + t) * Piece<T>::E; }
+template <typename T, int TH>
+__device__ __forceinline__ int piece_v(int s0, int k, int t) { return s0 + (k * TH + t) * Piece<T>::E; }
 
 // Thread t's pieces of one logits row.  `aligned`: the row starts on 16 bytes
 // and V * sizeof(T) is a multiple of 16, so each piece lies wholly inside or
@@ -414,7 +425,7 @@ __device__ __forceinline__ int piece_v(int s0, int k, int t) { return s0 + (k * 
 // the row is not needed; aligned loads are still issued, against an empty
 // range, so they return zeros without touching memory and the register
 // assignment does not depend on the branch.
-template <typename T>
+template <typename T, int TH>
 __device__ __forceinline__ void load_pieces(const T* row, int s0, int V, bool aligned, int t,
                                             uint4 (&raw)[Piece<T>::NK], bool present = true) {
   constexpr int E = Piece<T>::E;
@@ -424,14 +435,14 @@ __device__ __forceinline__ void load_pieces(const T* row, int s0, int V, bool al
     const int vo = (s0 + t * E) * (int)sizeof(T);
 #pragma unroll
     for (int k = 0; k < Piece<T>::NK; ++k)
-      raw[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, k * AC_THREADS * 16, 0));
+      raw[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, k * TH * 16, 0));
   } else if (!present) {
 #pragma unroll
     for (int k = 0; k < Piece<T>::NK; ++k) raw[k] = make_uint4(0u, 0u, 0u, 0u);
   } else {
 #pragma unroll
     for (int k = 0; k < Piece<T>::NK; ++k) {
-      const int v = piece_v<T>(s0, k, t);
+      const int v = piece_v<T, TH>(s0, k, t);
       uint32_t wd[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int e = 0; e < E; ++e) {
@@ -447,7 +458,8 @@ __device__ __forceinline__ void load_pieces(const T* row, int s0, int V, bool al
 // ALIGNED: every logits row starts on 16 bytes (decided on the host; a compile-time choice
 // keeps the two load paths from meeting in one register assignment)
 template <typename T, int MODE, bool ALIGNED>
-__global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int32_t G, AccWs ws) {
+__global__ void __launch_bounds__(ac_threads<MODE>(), 2) k_accept(sv_accept_args a, int32_t G, AccWs ws) {
+  constexpr int TH = ac_threads<MODE>(), NW = TH / 64;
   constexpr int E = Piece<T>::E, NK = Piece<T>::NK;
   __shared__ Red red;
   __shared__ SeqInfo si;
@@ -457,8 +469,8 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
   __shared__ float s_lp[SV_MAX_N], s_lq[SV_MAX_N], s_u[SV_MAX_N];  // per child: logits at its token, u_accept
   __shared__ float s_us;                                            // u_sample of the row
   // bonus: the slice's residual weights in id order, per-piece sums [k][t] and their row totals
-  __shared__ __attribute__((aligned(16))) float s_w[MODE == SV_STOCHASTIC ? AC_SLICE : 4];
-  __shared__ float s_g[MODE == SV_STOCHASTIC ? Piece<T>::NK * AC_THREADS : 4];
+  __shared__ __attribute__((aligned(16))) float s_w[MODE == SV_STOCHASTIC ? ac_slice<T, TH>() : 4];
+  __shared__ float s_g[MODE == SV_STOCHASTIC ? Piece<T>::NK * TH : 4];
   __shared__ double s_col[Piece<T>::NK];
   __shared__ int s_xc, s_claim, s_fin;  // walk finished (sticky); stochastic walk: claimed row, finisher
   // work-groups are dispatched round-robin over the 8 XCDs; the members of a
@@ -473,7 +485,7 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
   XSlot* gslots = ws.xs + (int64_t)grp * G * 2;
   uint32_t xtag = 0;  // exchanges of this group so far (identical on every member)
   const int64_t item = grp;
-  const int s0 = rank * AC_SLICE;  // this work-group's slice of the vocabulary
+  const int s0 = rank * ac_slice<T, TH>();  // this work-group's slice of the vocabulary
   if (t == 0) s_xc = 0;
   bool live_row = false;
 
@@ -496,32 +508,32 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
     uint32_t cx0 = 0u;  // the sequence's walk already finished (a late work-group)
     if (incr && t == 0) cx0 = ld_u32(cancel);
     uint4 rp[NK];
-    if constexpr (MODE == SV_STOCHASTIC) load_pieces<T>(prow, s0, V, aligned, t, rp);
+    if constexpr (MODE == SV_STOCHASTIC) load_pieces<T, TH>(prow, s0, V, aligned, t, rp);
     asm volatile("" : "+v"(sr.tok), "+v"(sr.par), "+v"(sr.dep), "+v"(cx0));  // nothing uses them before this point
     if (cx0) s_xc = 1;
-    seq_facts(a, sr, si);
+    seq_facts<TH>(a, sr, si);
     live_row = row_live(a, si, r);  // the same on every member of the group
     if (live_row && !s_xc) {
-      row_kids(N, r, si);
+      row_kids<TH>(N, r, si);
       int done_by_me = 0;  // this work-group wrote the row result
 
       if constexpr (MODE == SV_GREEDY) {
         float best = -FLT_MAX;
         int arg = 0x7fffffff;
         {
-          load_pieces<T>(prow, s0, V, aligned, t, rp);
+          load_pieces<T, TH>(prow, s0, V, aligned, t, rp);
 #pragma unroll
           for (int k = 0; k < NK; ++k) {
             float x[E];
             unpack16<T>(rp[k], x);
-            const int v = piece_v<T>(s0, k, t);
+            const int v = piece_v<T, TH>(s0, k, t);
 #pragma unroll
             for (int e = 0; e < E; ++e)  // a thread visits its entries in ascending id
               if (v + e < V && x[e] > best) { best = x[e]; arg = v + e; }
           }
         }
-        block_argmax(best, arg, red);
-        exchange(gslots, G, rank, ++xtag, 2, xv, ws.err, nullptr, &s_xc, __float_as_uint(best), (uint32_t)arg);
+        block_argmax<TH>(best, arg, red);
+        exchange<TH>(gslots, G, rank, ++xtag, 2, xv, ws.err, nullptr, &s_xc, __float_as_uint(best), (uint32_t)arg);
         if (rank == 0) {
           if (t < 64) {  // wave 0: lane k takes member k's best; the butterfly keeps the lowest id on ties
             float bv = lane < G ? __uint_as_float(xv[lane][0]) : -FLT_MAX;
@@ -537,12 +549,12 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
         const int K = __builtin_amdgcn_readfirstlane(si.K);
         const bool need_q = K > 0;
         // ---- the slice: raw logits -> slice maxima -> exponentials kept in registers
-        float ep[AC_CT], eq[AC_CT];
+        float ep[ac_ct<T>()], eq[ac_ct<T>()];
         float mp = -FLT_MAX, mq = -FLT_MAX;
         double zp = 0.0, zq = 0.0;
         {
           uint4 rq[NK];
-          load_pieces<T>(qrow, s0, V, aligned, t, rq, need_q);
+          load_pieces<T, TH>(qrow, s0, V, aligned, t, rq, need_q);
           // children's logits at their tokens and their uniforms: issued after the draft
           // slice (so that nothing waits for them before it is issued), stored to LDS once
           // both slices are in
@@ -554,19 +566,19 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
             c_lq = ldraw(qrow, x);
             c_u = __float_as_uint(a.u_accept[(int64_t)b * (N + 1) + kid + 1]);
           }
-          if (t == AC_THREADS - 1) c_us = __float_as_uint(a.u_sample[(int64_t)b * (N + 1) + r]);
+          if (t == TH - 1) c_us = __float_as_uint(a.u_sample[(int64_t)b * (N + 1) + r]);
 #pragma unroll
           for (int k = 0; k < NK; ++k) {
             float x[E];
             unpack16<T>(rp[k], x);
 #pragma unroll
-            for (int e = 0; e < E; ++e) mp = piece_v<T>(s0, k, t) < V ? fmaxf(mp, x[e]) : mp;
+            for (int e = 0; e < E; ++e) mp = piece_v<T, TH>(s0, k, t) < V ? fmaxf(mp, x[e]) : mp;
           }
-          mp = block_max(mp, red);
+          mp = block_max<TH>(mp, red);
           opaque(rp);  // unpack again below instead of keeping the unpacked floats alive
           const float op = mp * l2T;  // exp2(x * l2T - op): one FMA per entry
-          const bool whole = s0 + AC_SLICE <= V;  // uniform: no entry of the slice lies past V
-          auto expo = [&](const uint4 (&raw)[NK], float o, float (&ex)[AC_CT], double& z) {
+          const bool whole = s0 + ac_slice<T, TH>() <= V;  // uniform: no entry of the slice lies past V
+          auto expo = [&](const uint4 (&raw)[NK], float o, float (&ex)[ac_ct<T>()], double& z) {
             if (whole) {
 #pragma unroll
               for (int k = 0; k < NK; ++k) {
@@ -586,7 +598,7 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
                 unpack16<T>(raw[k], x);
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                  ex[k * E + e] = piece_v<T>(s0, k, t) < V ? __builtin_amdgcn_exp2f(fmaf(x[e], l2T, -o)) : 0.f;
+                  ex[k * E + e] = piece_v<T, TH>(s0, k, t) < V ? __builtin_amdgcn_exp2f(fmaf(x[e], l2T, -o)) : 0.f;
                   g += ex[k * E + e];
                 }
                 z += (double)g;
@@ -600,14 +612,14 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
               float x[E];
               unpack16<T>(rq[k], x);
 #pragma unroll
-              for (int e = 0; e < E; ++e) mq = piece_v<T>(s0, k, t) < V ? fmaxf(mq, x[e]) : mq;
+              for (int e = 0; e < E; ++e) mq = piece_v<T, TH>(s0, k, t) < V ? fmaxf(mq, x[e]) : mq;
             }
-            mq = block_max(mq, red);
+            mq = block_max<TH>(mq, red);
             opaque(rq);
             expo(rq, mq * l2T, eq, zq);
           } else {
 #pragma unroll
-            for (int i = 0; i < AC_CT; ++i) eq[i] = 0.f;
+            for (int i = 0; i < ac_ct<T>(); ++i) eq[i] = 0.f;
           }
           asm volatile("" : "+v"(c_lp), "+v"(c_lq), "+v"(c_u), "+v"(c_us));  // first use: here
           if (t < K) {
@@ -615,11 +627,11 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
             s_lq[t] = rawf<T>(c_lq);
             s_u[t] = __uint_as_float(c_u);
           }
-          if (t == AC_THREADS - 1) s_us = __uint_as_float(c_us);
+          if (t == TH - 1) s_us = __uint_as_float(c_us);
         }
-        zp = block_sum(zp, red);  // its barriers also publish the children's values
-        zq = block_sum(zq, red);
-        if (exchange(gslots, G, rank, ++xtag, 6, xv, ws.err, cancel, &s_xc, __float_as_uint(mp),
+        zp = block_sum<TH>(zp, red);  // its barriers also publish the children's values
+        zq = block_sum<TH>(zq, red);
+        if (exchange<TH>(gslots, G, rank, ++xtag, 6, xv, ws.err, cancel, &s_xc, __float_as_uint(mp),
                      __float_as_uint(mq), dlo(zp), dhi(zp), dlo(zq), dhi(zq)))
           return;
         // global statistics: lane k of every wave takes member k's partials (G <= 64); the
@@ -668,8 +680,8 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
           if (j == K - 1) { c_prev = c; c = cn; break; }
           // max(0, p - cn q) = fp * max(0, ep - kappa eq) on this slice, kappa = cn fq / fp
           const float kappa = (float)(cn * fq / fp);
-          const double sl = block_sum(slice_sum(kappa), red) * fp;
-          if (exchange(gslots, G, rank, ++xtag, 2, xv, ws.err, cancel, &s_xc, dlo(sl), dhi(sl))) return;
+          const double sl = block_sum<TH>(slice_sum(kappa), red) * fp;
+          if (exchange<TH>(gslots, G, rank, ++xtag, 2, xv, ws.err, cancel, &s_xc, dlo(sl), dhi(sl))) return;
           // lane k of every wave takes member k's sum (G <= 64): one LDS read and a DPP reduction
           const double S = wave_sumd(lane < G ? dof(xv[lane][0], xv[lane][1]) : 0.0);
           __syncthreads();
@@ -683,7 +695,7 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
         } else {
           // ---- bonus: smallest v whose ascending cumulative residual exceeds u * total.
           // A residual of total 0 (reachable only through rounding) falls back to the previous one.
-          // Ids ascend piece by piece: piece (k, t) holds the slice-local ids (k * 256 + t) * E ..
+          // Ids ascend piece by piece: piece (k, t) holds the slice-local ids (k * TH + t) * E ..
           // + E - 1.  The weights are staged in LDS in id order (after which the exponentials in
           // registers are dead) with their piece sums; row totals over t give the coarse
           // cumulative sum, one work-group scan over the pieces of the row that crosses the
@@ -704,18 +716,18 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
                   else w[e] = ep[k * E + e];
                   x += w[e];
                 }
-                float* dst = s_w + (k * AC_THREADS + t) * E;
+                float* dst = s_w + (k * TH + t) * E;
 #pragma unroll
                 for (int e = 0; e < E; e += 4) *(float4*)(dst + e) = make_float4(w[e], w[e + 1], w[e + 2], w[e + 3]);
-                s_g[k * AC_THREADS + t] = x;
+                s_g[k * TH + t] = x;
               }
             };
             if (kappa == 0.f) stage(std::false_type{});  // uniform branch
             else stage(std::true_type{});
             __syncthreads();
-            for (int k = wv; k < NK; k += AC_NW) {  // wave wv totals rows wv, wv + 4, ...
+            for (int k = wv; k < NK; k += NW) {  // wave wv totals rows wv, wv + NW, ...
               double x = 0.0;
-              for (int i = lane; i < AC_THREADS; i += 64) x += (double)s_g[k * AC_THREADS + i];
+              for (int i = lane; i < TH; i += 64) x += (double)s_g[k * TH + i];
               x = wave_sumd(x);
               if (lane == 0) s_col[k] = x;
             }
@@ -723,7 +735,7 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
             double col = 0.0;
             for (int k = 0; k < NK; ++k) col += s_col[k];
             const double sl = col * fp;
-            if (exchange(gslots, G, rank, ++xtag, 2, xv, ws.err, cancel, &s_xc, dlo(sl), dhi(sl))) return;
+            if (exchange<TH>(gslots, G, rank, ++xtag, 2, xv, ws.err, cancel, &s_xc, dlo(sl), dhi(sl))) return;
             // lane k holds member k's slice total; one inclusive scan gives every member the
             // same prefixes, total and owner
             const double sk = lane < G ? dof(xv[lane][0], xv[lane][1]) : 0.0;
@@ -754,7 +766,7 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
               int h = 0x7fffffff;
               double excl = 0.0;
               if (ks >= 0) {  // inclusive scan of row ks over the threads, in id order
-                const float gk = s_g[ks * AC_THREADS + t];
+                const float gk = s_g[ks * TH + t];
                 double incl = wave_scand((double)gk, lane);
                 if (lane == 63) red.d[wv] = incl;
                 if (t == 0) s_first = 0x7fffffff;
@@ -769,7 +781,7 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
               }
               if (h != 0x7fffffff) {
                 if (t == h) {  // walk the E entries of piece (ks, h)
-                  const int p0 = (ks * AC_THREADS + t) * E;  // slice-local id of its first entry
+                  const int p0 = (ks * TH + t) * E;  // slice-local id of its first entry
                   double run = excl;
                   int pick = -1, lastpos = -1;
                   for (int e = 0; e < E; ++e) {
@@ -789,7 +801,7 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
                 const int klim = ks >= 0 ? ks : NK - 1;
                 int lp = -1;
                 for (int k = 0; k <= klim; ++k) {
-                  const int p0 = (k * AC_THREADS + t) * E;
+                  const int p0 = (k * TH + t) * E;
                   for (int e = 0; e < E; ++e) lp = s_w[p0 + e] > 0.f ? s0 + p0 + e : lp;
                 }
                 for (int o = 32; o > 0; o >>= 1) lp = max(lp, __shfl_xor(lp, o));
@@ -798,7 +810,7 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
                 if (lane == 0) atomicMax(&s_lpos, lp);
                 __syncthreads();
                 if (t == 0) {
-                  const int pick = s_lpos >= 0 ? s_lpos : min(s0 + AC_SLICE, V) - 1;
+                  const int pick = s_lpos >= 0 ? s_lpos : min(s0 + ac_slice<T, TH>(), V) - 1;
                   st_u64(&ws.res[item], res_word(-1, pick));
                 }
               }
@@ -836,11 +848,11 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
         }
         __syncthreads();
         if (s_fin) {
-          for (int x = t; x <= N; x += AC_THREADS) s_rr[x] = ld_u64(&rr[x]);
+          for (int x = t; x <= N; x += TH) s_rr[x] = ld_u64(&rr[x]);
           __syncthreads();
         }
         for (int guard = 0; s_claim >= 0 && guard <= N + 1; ++guard) {  // uniform
-          for (int x = t; x <= N; x += AC_THREADS) s_rr[x] = ld_u64(&rr[x]);
+          for (int x = t; x <= N; x += TH) s_rr[x] = ld_u64(&rr[x]);
           __syncthreads();
           if (t == 0) {
             int row = s_claim, claim = -1;
@@ -891,7 +903,7 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
             a.out_tokens[(int64_t)b * (Dm + 1) + t] = t < A ? si.tok[si.path[t]] : (t == A ? bonus : 0);
           if (incr && t == 0) st_u32(cancel, 1u);  // the sequence's remaining rows are not needed
           if (!incr)  // every row result of b has been read: leave them cleared for the next call
-            for (int x = t; x <= N; x += AC_THREADS) st_u64(&rr[x], 0ull);
+            for (int x = t; x <= N; x += TH) st_u64(&rr[x], 0ull);
         }
       }
 
@@ -928,7 +940,7 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
             {
               float kv = (float)key;
               int ki = key;
-              block_argmax(kv, ki, red);
+              block_argmax<TH>(kv, ki, red);
               key = (int)kv;
             }
             if (key >= 0) {
@@ -956,21 +968,21 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
                 for (int k = 0; k < NK; ++k) {
                   float x[E];
                   unpack16<T>(raw[k], x);
-                  const int v = piece_v<T>(gs * AC_SLICE, k, t);
+                  const int v = piece_v<T, TH>(gs * ac_slice<T, TH>(), k, t);
 #pragma unroll
                   for (int e = 0; e < E; ++e)
                     if (v + e < V && x[e] > best) { best = x[e]; arg = v + e; }
                 }
               };
-              load_pieces<T>(srow, 0, V, aligned, t, r0);
+              load_pieces<T, TH>(srow, 0, V, aligned, t, r0);
               for (int gs = 0; gs < G; gs += 2) {
-                if (gs + 1 < G) load_pieces<T>(srow, (gs + 1) * AC_SLICE, V, aligned, t, r1);
+                if (gs + 1 < G) load_pieces<T, TH>(srow, (gs + 1) * ac_slice<T, TH>(), V, aligned, t, r1);
                 consume(r0, gs);
                 if (gs + 1 >= G) break;
-                if (gs + 2 < G) load_pieces<T>(srow, (gs + 2) * AC_SLICE, V, aligned, t, r0);
+                if (gs + 2 < G) load_pieces<T, TH>(srow, (gs + 2) * ac_slice<T, TH>(), V, aligned, t, r0);
                 consume(r1, gs + 1);
               }
-              block_argmax(best, arg, red);
+              block_argmax<TH>(best, arg, red);
               bonus = arg;
             }
           }
@@ -984,7 +996,7 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
             st_u32(&ws.seqdone[b], 0u);  // every row of b has been counted: ready for the next call
           }
           // every row result of b has been read: leave them cleared for the next call
-          for (int x = t; x <= N; x += AC_THREADS) st_u64(&rr[x], 0ull);
+          for (int x = t; x <= N; x += TH) st_u64(&rr[x], 0ull);
           if (t < Dm) a.accept_rows[(int64_t)b * Dm + t] = t < A ? si.path[t] + 1 : 0;
           if (t <= Dm)
             a.out_tokens[(int64_t)b * (Dm + 1) + t] = t < A ? a.tokens[(int64_t)b * N + si.path[t]] : (t == A ? bonus : 0);
@@ -1014,9 +1026,9 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
   // (a member that left early on a finished walk may have exchanged less than the others,
   // so the slots of every live row are cleared)
   if (s_last && (xtag > 0 || live_row))
-    for (int i = t; i < G * 2 * AC_XW; i += AC_THREADS) st_u64(&gslots[i / AC_XW].w[i % AC_XW], 0ull);
+    for (int i = t; i < G * 2 * AC_XW; i += TH) st_u64(&gslots[i / AC_XW].w[i % AC_XW], 0ull);
   if (s_claim) {  // stochastic: the sequence's row results, frontier, cancel flag and exit count
-    for (int x = t; x <= N; x += AC_THREADS) st_u64(&ws.res[(int64_t)bq * (N + 1) + x], 0ull);
+    for (int x = t; x <= N; x += TH) st_u64(&ws.res[(int64_t)bq * (N + 1) + x], 0ull);
     if (t == 0) {
       st_u32(&ws.frontier[bq], 0u);
       st_u32(&ws.cancel[bq], 0u);
@@ -1033,7 +1045,11 @@ __global__ void __launch_bounds__(AC_THREADS, 2) k_accept(sv_accept_args a, int3
 }
 
 int groups_G(const sv_accept_args& a) {
-  const int G = (a.V + AC_SLICE - 1) / AC_SLICE;
+  const bool st = a.mode == SV_STOCHASTIC;
+  const int slice = a.logits_dtype == SV_BF16
+                        ? (st ? ac_slice<uint16_t, ac_threads<SV_STOCHASTIC>()>() : ac_slice<uint16_t, ac_threads<SV_GREEDY>()>())
+                        : (st ? ac_slice<float, ac_threads<SV_STOCHASTIC>()>() : ac_slice<float, ac_threads<SV_GREEDY>()>());
+  const int G = (a.V + slice - 1) / slice;
   return G < 1 ? 1 : G;
 }
 // one group per row, rounded up to a whole number of groups per XCD
@@ -1101,7 +1117,7 @@ extern "C" sv_status sv_accept(const sv_accept_args* args, void* stream) {
   const size_t esz = a.logits_dtype == SV_BF16 ? 2 : 4;
   const bool aligned = ((size_t)a.V * esz) % 16 == 0 && ((uintptr_t)a.target_logits % 16) == 0 &&
                        (a.mode == SV_GREEDY || ((uintptr_t)a.draft_logits % 16) == 0);
-#define SV_ACC_LAUNCH(T, M, AL) hipLaunchKernelGGL((k_accept<T, M, AL>), grid, dim3(AC_THREADS), 0, st, a, G, ws)
+#define SV_ACC_LAUNCH(T, M, AL) hipLaunchKernelGGL((k_accept<T, M, AL>), grid, dim3(ac_threads<M>()), 0, st, a, G, ws)
   if (a.logits_dtype == SV_BF16) {
     if (a.mode == SV_STOCHASTIC) { if (aligned) SV_ACC_LAUNCH(uint16_t, SV_STOCHASTIC, true); else SV_ACC_LAUNCH(uint16_t, SV_STOCHASTIC, false); }
     else { if (aligned) SV_ACC_LAUNCH(uint16_t, SV_GREEDY, true); else SV_ACC_LAUNCH(uint16_t, SV_GREEDY, false); }
