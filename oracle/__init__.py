@@ -163,13 +163,14 @@ def accept(w, mode: Optional[str] = None, temperature: Optional[float] = None, t
     a = _AcceptArgs()
     a.B, a.N, a.V, a.max_depth = B, N, V, Dm
     a.logits_dtype = _dt(target)
-    a.mode = 0 if mode == "greedy" else 1
+    a.mode = {"greedy": 0, "stochastic": 1, "topk": 2}[mode]
     a.temperature = float(T)
     a.parents, a.tokens, a.target_logits = _p(parents), _p(tokens), _p(target)
-    if a.mode == 1:
+    if a.mode != 0:
         ua = np.ascontiguousarray(ua, dtype=np.float32)
         us = np.ascontiguousarray(us, dtype=np.float32)
-        a.draft_logits, a.u_accept, a.u_sample = _p(draft), _p(ua), _p(us)
+        a.draft_logits = _p(draft) if a.mode == 1 else None
+        a.u_accept, a.u_sample = _p(ua), _p(us)
     for k in out:
         setattr(a, k, _p(out[k]))
     if _L().orc_accept(ctypes.byref(a)) != 0:

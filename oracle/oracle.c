@@ -189,8 +189,8 @@ static void softmax_row(const void* logits, int dtype, int64_t row_off, int32_t 
 
 int orc_accept(const orc_accept_args* a) {
   const int32_t B = a->B, N = a->N, V = a->V, Dm = a->max_depth;
-  if (B < 0 || N < 1 || V < 1 || Dm < 1 || Dm > 64 || (a->mode != 0 && a->mode != 1)) return -1;
-  if (a->mode == 1 && !(a->temperature > 0.0)) return -1;
+  if (B < 0 || N < 1 || V < 1 || Dm < 1 || Dm > 64 || a->mode < 0 || a->mode > 2) return -1;
+  if (a->mode != 0 && !(a->temperature > 0.0)) return -1;
   const double EPS = 1e-6;
   int32_t* valid = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
   int32_t* depth = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
@@ -247,20 +247,26 @@ int orc_accept(const orc_accept_args* a) {
       }
       bonus = amax[stop_node + 1];
     } else {
-      /* stochastic: multi-round rejection walk from the root row */
+      /* stochastic: multi-round rejection walk from the root row.  q is the draft
+         distribution of the current row (mode 1) or the point mass at the tested
+         child's token (mode 2, deterministic drafts) */
       const double T = a->temperature;
       int32_t r = 0;
       softmax_row(a->target_logits, a->logits_dtype, ((int64_t)b * (N + 1) + 0) * V, V, T, pcur);
+      if (a->mode == 2)
+        for (int32_t v = 0; v < V; ++v) q[v] = 0.0;
       for (;;) {
-        softmax_row(a->draft_logits, a->logits_dtype, ((int64_t)b * (N + 1) + r) * V, V, T, q);
+        if (a->mode == 1) softmax_row(a->draft_logits, a->logits_dtype, ((int64_t)b * (N + 1) + r) * V, V, T, q);
         int32_t moved = 0;
         for (int32_t c = 0; c < N; ++c) {
           if (!usable[c] || par[c] + 1 != r) continue;
           const int32_t x = tok[c];
+          if (a->mode == 2) q[x] = 1.0;
           const double u = (double)a->u_accept[(int64_t)b * (N + 1) + (c + 1)];
           const double ratio = q[x] > 0.0 ? pcur[x] / q[x] : INFINITY;
           if (fabs(u - ratio) < EPS) flagged = 1;
           if (u < ratio) {
+            if (a->mode == 2) q[x] = 0.0;
             acc_path[A++] = c;
             r = c + 1;
             softmax_row(a->target_logits, a->logits_dtype, ((int64_t)b * (N + 1) + r) * V, V, T, pcur);
@@ -275,6 +281,7 @@ int orc_accept(const orc_accept_args* a) {
           } else {
             flagged = 1; /* only reachable through rounding: keep p_cur */
           }
+          if (a->mode == 2) q[x] = 0.0;
         }
         if (!moved) break;
       }

@@ -69,9 +69,13 @@ typedef struct {
 } orc_attn_args;
 int orc_tree_attention(const orc_attn_args* a);
 
-/* Speculative acceptance ([PX], [SSD]); mode 0 greedy, 1 stochastic.
+/* Speculative acceptance ([PX], [SSD]); mode 0 greedy, 1 stochastic, 2 stochastic
+ * with deterministic (top-K) drafts: the drafter's proposal for each child is the
+ * point mass at the child's token ([PX] "Objetivo-Borrador": the drafter takes
+ * its top token at each stage; "EAGLE": the top-K candidates of each node), so
+ * the walk is mode 1's with q = that point mass, and draft_logits is not read.
  * logits dtype 0 = fp32, 1 = bf16.  target/draft logits [B,N+1,V];
- * u_accept, u_sample [B,N+1] (stochastic only).
+ * u_accept, u_sample [B,N+1] (modes 1 and 2).
  * Outputs: accept_len [B], accept_rows [B,max_depth], out_tokens [B,max_depth+1],
  * num_out [B], stop_row [B], status [B], flagged [B] (stochastic: a draw was
  * within 1e-6 of its threshold). */

@@ -228,3 +228,93 @@ def test_flagging_near_threshold():
     # bonus sampling on the boundary: root residual is [0, 1]; u_s = 0 sits on C_{-1} = 0
     w.u_sample = np.array([[0.0, 0.0]], np.float32)
     assert oracle.accept(w)["flagged"][0] == 1
+
+
+# ------------------------------------------------- deterministic (top-K) drafts
+# The drafter proposes each child deterministically, so its proposal for child c
+# is the point mass at tokens[c]: accept iff u < p_cur(x); a rejection zeroes x in
+# p_cur and renormalises (sampling without replacement).  Because the first
+# emitted token of any lossless scheme follows p_root, a child with a token of
+# its own is accepted with probability exactly p_root(x).
+@pytest.mark.parametrize("case", range(4))
+def test_topk_golden(case):
+    c = golden("topk_cases.json")["cases"][case]
+    par = np.asarray(c["parents"], np.int32)[None]
+    w = ns(B=1, N=par.shape[1], parents=par, tokens=np.asarray(c["tokens"], np.int32)[None],
+           target_logits=np.asarray(c["target"], np.float32)[None], draft_logits=None,
+           u_accept=np.asarray(c["u_accept"], np.float32)[None], u_sample=np.asarray(c["u_sample"], np.float32)[None],
+           max_depth=c["max_depth"], mode="topk", temperature=1.0)
+    r = oracle.accept(w)
+    for k in ("accept_len", "num_out", "stop_row"):
+        assert int(r[k][0]) == c[k], k
+    assert r["accept_rows"][0].tolist() == c["accept_rows"]
+    assert r["out_tokens"][0].tolist() == c["out_tokens"]
+    assert r["flagged"][0] == 0
+
+
+def _topk_batch(parents, tokens, p_rows, n, seed, T=1.0):
+    par = np.tile(np.asarray(parents, np.int32), (n, 1))
+    N = par.shape[1]
+    V = p_rows.shape[-1]
+    tgt = np.ascontiguousarray(np.broadcast_to(p_rows.astype(np.float32), (n, N + 1, V)))
+    return ns(B=n, N=N, parents=par, tokens=np.tile(np.asarray(tokens, np.int32), (n, 1)), target_logits=tgt,
+              draft_logits=None, u_accept=W.uniform24(seed, 11, (n, N + 1)),
+              u_sample=W.uniform24(seed, 12, (n, N + 1)), max_depth=N, mode="topk", temperature=T)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("T", [1.0, 2.0])
+def test_topk_first_token_and_child_acceptance_exact(T):
+    """Three sibling drafts with distinct tokens, 6e5 trials: the first emitted token
+    follows p_root and child k is accepted with probability p_root(x_k) (chi-square)."""
+    V = 16
+    p_rows = W.normal(61, 1, (4, V), "f32", 1.5)
+    p0 = _softmax(p_rows[0], T)
+    toks = [int(x) for x in np.argsort(-p0, kind="stable")[:3]]  # the three most likely tokens
+    counts = np.zeros(V, np.int64)
+    which = np.zeros(4, np.int64)  # accepted child 0, 1, 2, or none
+    for s in range(3):
+        r = oracle.accept(_topk_batch([-1, -1, -1], toks, p_rows, 200_000, seed=900 + s, T=T))
+        counts += np.bincount(r["out_tokens"][:, 0], minlength=V)
+        first = np.where(r["accept_len"] >= 1, r["accept_rows"][:, 0] - 1, 3)
+        which += np.bincount(first, minlength=4)
+    assert stats.chisquare(counts, p0 * counts.sum()).pvalue > 0.01
+    pk = np.array([p0[toks[0]], p0[toks[1]], p0[toks[2]], 1 - p0[toks].sum()])
+    assert stats.chisquare(which, pk * which.sum()).pvalue > 0.01, (which, pk)
+    # power: testing every child against p_root without renormalising after a rejection
+    # gives p1, (1-p1) p2, (1-p1)(1-p2) p3 -- visibly different
+    p1, p2, p3 = p0[toks]
+    alt = np.array([p1, (1 - p1) * p2, (1 - p1) * (1 - p2) * p3, (1 - p1) * (1 - p2) * (1 - p3)])
+    assert stats.chisquare(which, alt * which.sum()).pvalue < 1e-6
+
+
+def test_topk_repeated_sibling_token_is_never_accepted():
+    """Siblings with the same token: after the first is rejected its token has mass 0."""
+    V = 8
+    p_rows = W.normal(71, 1, (4, V), "f32", 1.0)
+    r = oracle.accept(_topk_batch([-1, -1, -1], [3, 3, 6], p_rows, 50_000, seed=17))
+    assert not (r["accept_rows"][:, 0] == 2).any()
+    assert (r["accept_rows"][:, 0] == 1).any() and (r["accept_rows"][:, 0] == 3).any()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_topk_chain_equals_stochastic_with_one_hot_draft(seed):
+    """On a chain (one child per row) the deterministic draft is mode 1 with a draft row
+    whose distribution is the point mass at the child's token (logit 0 there, -1e30
+    elsewhere, so every other probability is exactly 0 in fp64)."""
+    B, N, V = 300, 4, 32
+    par = np.tile(W.tree_chain(N), (B, 1))
+    tgt = W.normal(seed, 1, (B, N + 1, V), "f32", 1.0)
+    toks = W.randint(seed, 3, B * N, 0, V - 1).astype(np.int32).reshape(B, N)
+    drf = np.full((B, N + 1, V), -1e30, np.float32)
+    for b in range(B):
+        for i in range(N):
+            drf[b, i, toks[b, i]] = 0.0  # row i is the parent row of node i on a chain
+    ua, us = W.uniform24(seed, 11, (B, N + 1)), W.uniform24(seed, 12, (B, N + 1))
+    common = dict(B=B, N=N, parents=par, tokens=toks, target_logits=tgt, u_accept=ua, u_sample=us, max_depth=N,
+                  temperature=1.0)
+    r1 = oracle.accept(ns(mode="stochastic", draft_logits=drf, **common))
+    r2 = oracle.accept(ns(mode="topk", draft_logits=None, **common))
+    for k in ("accept_len", "accept_rows", "out_tokens", "num_out", "stop_row", "status"):
+        assert np.array_equal(r1[k], r2[k]), k
+    assert (r1["accept_len"] > 0).any() and (r1["accept_len"] < N).any()

@@ -125,6 +125,25 @@ def draft_tokens(seed: int, stream: int, logits: np.ndarray, rows: np.ndarray, T
     return out
 
 
+def topk_tokens(logits: np.ndarray, parents: np.ndarray) -> np.ndarray:
+    """Deterministic drafts: the children of row r (ascending node index) take the
+    1st, 2nd, ... most likely ids of logits row r (viewed as [B, N+1, V]; the lowest
+    id first among equal logits)."""
+    B, N = parents.shape
+    out = np.zeros((B, N), dtype=np.int32)
+    for b in range(B):
+        kids = {}
+        for i in range(N):
+            kids.setdefault(int(parents[b, i]) + 1, []).append(i)
+        for r, ch in kids.items():
+            row = logits[b, r]
+            row = bf16_to_f32(row) if row.dtype == np.uint16 else row.astype(np.float32)
+            order = np.argsort(-row, kind="stable")[:len(ch)]
+            for k, i in enumerate(ch):
+                out[b, i] = order[k]
+    return out
+
+
 def randint(seed: int, stream: int, n: int, lo: int, hi: int, offset: int = 0) -> np.ndarray:
     """Integers uniform on [lo, hi] (inclusive) by multiply-shift on the top 32 bits."""
     span = hi - lo + 1
@@ -301,7 +320,8 @@ def build_workload(name: str, B: int, N: int, Hq: int, Hkv: int, D: int, V: int,
 
     parents: [B, N] int32.  prefix_len: [B].
     token_rule: 'sample' (draft from q of the parent row, temperature T),
-                'greedy' (argmax of the draft parent row), 'uniform' (uniform ids).
+                'greedy' (argmax of the draft parent row), 'uniform' (uniform ids),
+                'topk' (siblings take the top ids of the draft parent row in turn).
     target_from_draft_sigma: if set, target = draft + N(0, sigma) (rounded to dtype),
                 otherwise target and draft are independent N(0, logit_sigma).
     plant: optional [B] int array of planted match counts (greedy acceptance);
@@ -310,7 +330,7 @@ def build_workload(name: str, B: int, N: int, Hq: int, Hkv: int, D: int, V: int,
     parents = np.ascontiguousarray(parents, dtype=np.int32).reshape(B, N)
     prefix_len = np.ascontiguousarray(prefix_len, dtype=np.int32).reshape(B)
     if need_draft is None:
-        need_draft = mode == "stochastic" or token_rule in ("sample", "greedy")
+        need_draft = mode == "stochastic" or token_rule in ("sample", "greedy", "topk")
     rows = N + 1
     # logits
     if need_draft or target_from_draft_sigma is not None:
@@ -324,6 +344,8 @@ def build_workload(name: str, B: int, N: int, Hq: int, Hkv: int, D: int, V: int,
     # tokens
     if token_rule == "uniform":
         tokens = randint(seed, S_TOKENS, B * N, 0, V - 1).astype(np.int32).reshape(B, N)
+    elif token_rule == "topk":
+        tokens = topk_tokens(draft, parents)
     else:
         prow = (np.arange(B, dtype=np.int64)[:, None] * rows + _parent_rows(parents)).reshape(-1)
         T = temperature if token_rule == "sample" else 0.0
@@ -366,7 +388,7 @@ def build_workload(name: str, B: int, N: int, Hq: int, Hkv: int, D: int, V: int,
         v_cache = normal(seed, S_VC, (num_blocks, Hkv, block_size, D), dtype)
         k_cache[0] = 0  # ghost block
         v_cache[0] = 0
-    if mode == "stochastic":
+    if mode in ("stochastic", "topk"):
         u_accept = uniform24(seed, S_UACC, (B, rows))
         u_sample = uniform24(seed, S_USMP, (B, rows))
     else:
@@ -439,7 +461,9 @@ def config(cfg: int, seed: Optional[int] = None, **ov) -> Workload:
     """The five verification workloads, optionally shrunk with overrides.
 
     Overrides: B, L (prefix length, or (lo, hi) range for the batched one), V,
-    N / budgets (tree size), plant (greedy planting counts for the tiny chain).
+    N / budgets (tree size), plant (greedy planting counts for the tiny chain),
+    mode ('topk' for the stochastic ones: deterministic drafts, siblings take the
+    top ids of the draft parent row).
     """
     seed = cfg if seed is None else seed
     if cfg == 1:  # tiny chain, fp32, greedy
@@ -463,8 +487,10 @@ def config(cfg: int, seed: Optional[int] = None, **ov) -> Workload:
         L = ov.get("L", 4096)
         n_nodes = ov.get("N", 60)
         par = np.stack([tree_eagle_static(seed, n_nodes=n_nodes, stream_off=b * 100003) for b in range(B)])
-        return build_workload("eagle-static-8b", B, n_nodes, 32, 8, 128, V, "bf16", "stochastic", par,
-                              np.full(B, L), max_depth=6, seed=seed, logit_sigma=3.0, token_rule="sample")
+        mode = ov.get("mode", "stochastic")
+        return build_workload("eagle-static-8b", B, n_nodes, 32, 8, 128, V, "bf16", mode, par,
+                              np.full(B, L), max_depth=6, seed=seed, logit_sigma=3.0,
+                              token_rule="topk" if mode == "topk" else "sample")
     if cfg == 3:  # batched paged, 70B shape, greedy + commit
         B = ov.get("B", 64)
         V = ov.get("V", VOCAB_LLAMA3)
@@ -482,9 +508,10 @@ def config(cfg: int, seed: Optional[int] = None, **ov) -> Workload:
         L = ov.get("L", 2048)
         N = ov.get("N", 5)
         par = np.tile(tree_chain(N), (B, 1))
-        return build_workload("draft-target-chain-8b", B, N, 32, 8, 128, V, "bf16", "stochastic", par,
+        mode = ov.get("mode", "stochastic")
+        return build_workload("draft-target-chain-8b", B, N, 32, 8, 128, V, "bf16", mode, par,
                               np.full(B, L), max_depth=N, seed=seed, logit_sigma=3.0,
-                              target_from_draft_sigma=1.0, token_rule="sample")
+                              target_from_draft_sigma=1.0, token_rule="topk" if mode == "topk" else "sample")
     if cfg == 5:  # SSD outcome tree, 8B shape, 32K prefix, stochastic
         B = ov.get("B", 16)
         V = ov.get("V", VOCAB_LLAMA3)
@@ -492,9 +519,10 @@ def config(cfg: int, seed: Optional[int] = None, **ov) -> Workload:
         budgets = ov.get("budgets", (137, 68, 34, 17))
         par = np.stack([tree_outcome(seed, budgets=budgets, offset=b * 4099) for b in range(B)])
         N = par.shape[1]
-        return build_workload("ssd-outcome-tree-8b", B, N, 32, 8, 128, V, "bf16", "stochastic", par,
+        mode = ov.get("mode", "stochastic")
+        return build_workload("ssd-outcome-tree-8b", B, N, 32, 8, 128, V, "bf16", mode, par,
                               np.full(B, L), max_depth=10, seed=seed, logit_sigma=3.0,
-                              target_from_draft_sigma=1.0, token_rule="sample")
+                              target_from_draft_sigma=1.0, token_rule="topk" if mode == "topk" else "sample")
     raise ValueError(cfg)
 
 
