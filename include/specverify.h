@@ -73,6 +73,7 @@ typedef int32_t sv_status;
 /* acceptance modes */
 #define SV_GREEDY 0
 #define SV_STOCHASTIC 1
+#define SV_TOPK_DRAFT 2
 
 /* commit modes ([EP] sec. 2: length-based or path-index-based commit) */
 #define SV_COMMIT_PATH 0
@@ -164,9 +165,9 @@ sv_status sv_tree_attention(const sv_attn_args* args, void* stream);
  *   parents [B,N], tokens [B,N] int32 (draft token of node i), anc_bits and
  *   depth from sv_build_tree_mask; target_logits [B, N+1, V] (row r = the
  *   target's next-token logits after row r's token, row 0 = the root);
- *   draft_logits [B, N+1, V] (stochastic only; row r = the drafter's logits
+ *   draft_logits [B, N+1, V] (mode 1 only; row r = the drafter's logits
  *   its children were drawn from); u_accept, u_sample [B, N+1] float
- *   uniforms in [0,1) (stochastic only).
+ *   uniforms in [0,1) (modes 1 and 2).
  * A node is usable when its depth is > 0 and its token lies in [0, V).
  * Greedy (mode 0): a_r = argmax of target row r over the stored values, the
  *   lowest id on ties.  Node i matches when tokens[i] == a_{parents[i]+1};
@@ -182,6 +183,16 @@ sv_status sv_tree_attention(const sv_attn_args* args, void* stream);
  *   normalize(max(0, p_cur - q_r)).  When no child is accepted the walk stops
  *   at the current row and the bonus is the smallest v whose ascending-id
  *   cumulative mass of p_cur exceeds u_sample[stop row] times its total.
+ * Top-K drafts (mode 2): the drafter proposed every child deterministically
+ *   (its top candidates, [PX] "Objetivo-Borrador" and "EAGLE"), so its
+ *   proposal for child c is the point mass at x = tokens[c]; draft_logits is
+ *   not read (may be NULL).  The walk is mode 1's with that proposal: accept
+ *   iff u_accept[c+1] < p_cur(x); a rejection sets p_cur(x) to 0 and
+ *   renormalises (sampling without replacement), so a token repeated among
+ *   siblings is never accepted twice.  p(x) is taken from the row statistics
+ *   with no second pass over the row; the bonus is drawn from p_r with the
+ *   rejected tokens removed, as in mode 1 (if rounding leaves that residual
+ *   without mass, from p_r itself).
  * Outputs (device, int32): accept_len [B] (A), accept_rows [B, max_depth]
  *   (rows of the accepted path, root-most first, ghost-0 padded), out_tokens
  *   [B, max_depth+1] (accepted tokens then the bonus, 0 padded), num_out [B]

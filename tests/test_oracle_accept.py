@@ -318,3 +318,15 @@ def test_topk_chain_equals_stochastic_with_one_hot_draft(seed):
     for k in ("accept_len", "accept_rows", "out_tokens", "num_out", "stop_row", "status"):
         assert np.array_equal(r1[k], r2[k]), k
     assert (r1["accept_len"] > 0).any() and (r1["accept_len"] < N).any()
+
+
+def test_topk_token_generator_orders_by_logit_then_id():
+    """Siblings take the most likely ids of their parent row in turn, lowest id first on ties."""
+    rng = np.random.default_rng(0)
+    for _ in range(100):
+        V = int(rng.integers(1, 40))
+        n = int(rng.integers(1, V + 1))
+        lg = np.zeros((1, 2, V), np.float32)
+        lg[0, 0] = rng.integers(0, 4, V)
+        got = W.topk_tokens(lg, np.full((1, n), -1, np.int32))[0]
+        assert np.array_equal(got, np.argsort(-lg[0, 0], kind="stable")[:n])

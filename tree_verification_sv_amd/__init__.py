@@ -20,7 +20,8 @@ _lib = None
 
 SV_OK, SV_ERR_INVALID_ARGUMENT, SV_ERR_UNSUPPORTED, SV_ERR_HIP = 0, 1, 2, 4
 SV_F32, SV_BF16 = 0, 1
-SV_GREEDY, SV_STOCHASTIC = 0, 1
+SV_GREEDY, SV_STOCHASTIC, SV_TOPK_DRAFT = 0, 1, 2
+_MODES = {"greedy": SV_GREEDY, "stochastic": SV_STOCHASTIC, "topk": SV_TOPK_DRAFT}
 SV_COMMIT_PATH, SV_COMMIT_LENGTH = 0, 1
 
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -242,7 +243,11 @@ def accept_args(parents, tokens, anc_bits, depth, target_logits, max_depth, mode
     a = sv_accept_args()
     a.B, a.N, a.V, a.max_depth = B, N, V, max_depth
     a.logits_dtype = _elem(target_logits)
-    a.mode = SV_GREEDY if mode in ("greedy", SV_GREEDY) else SV_STOCHASTIC
+    if mode in _MODES:
+        mode = _MODES[mode]
+    if mode not in _MODES.values():
+        raise SpecVerifyError(f"unknown acceptance mode {mode!r}")
+    a.mode = mode
     a.temperature = float(temperature)
     a.parents, a.tokens = _ptr(parents, torch.int32, "parents"), _ptr(tokens, torch.int32, "tokens")
     a.anc_bits, a.depth = _ptr(anc_bits, torch.int64, "anc_bits"), _ptr(depth, torch.int32, "depth")
@@ -251,6 +256,7 @@ def accept_args(parents, tokens, anc_bits, depth, target_logits, max_depth, mode
         if draft_logits.dtype != target_logits.dtype:
             raise SpecVerifyError("draft and target logits must share a dtype")
         a.draft_logits = _ptr(draft_logits, name="draft_logits")
+    if a.mode != SV_GREEDY:
         a.u_accept = _ptr(u_accept, torch.float32, "u_accept")
         a.u_sample = _ptr(u_sample, torch.float32, "u_sample")
     for k in ("accept_len", "accept_rows", "out_tokens", "num_out", "stop_row", "status"):

@@ -62,7 +62,7 @@ namespace {
 // threads per work-group: 512 for greedy rows (half the work-groups of 256-thread ones,
 // fewer to dispatch), 256 for stochastic rows (smaller barriers and bonus scans, and the
 // residual staging fits two work-groups per compute unit)
-template <int MODE> constexpr int ac_threads() { return MODE == SV_STOCHASTIC ? 256 : 512; }
+template <int MODE> constexpr int ac_threads() { return MODE == SV_GREEDY ? 512 : 256; }
 constexpr int AC_NWMAX = 8;                    // waves per work-group at most
 // vocabulary entries per thread: 8 pieces of 16 bytes (64 bf16 / 32 fp32 logits), so a
 // work-group's slice is 8 * 16 bytes per thread
@@ -460,6 +460,8 @@ __device__ __forceinline__ void load_pieces(const T* row, int s0, int V, bool al
 template <typename T, int MODE, bool ALIGNED>
 __global__ void __launch_bounds__(ac_threads<MODE>(), 2) k_accept(sv_accept_args a, int32_t G, AccWs ws) {
   constexpr int TH = ac_threads<MODE>(), NW = TH / 64;
+  // STO: a rejection walk (modes 1 and 2); TOPK: deterministic drafts (q = point mass per child)
+  constexpr bool STO = MODE != SV_GREEDY, TOPK = MODE == SV_TOPK_DRAFT;
   constexpr int E = Piece<T>::E, NK = Piece<T>::NK;
   __shared__ Red red;
   __shared__ SeqInfo si;
@@ -469,8 +471,8 @@ __global__ void __launch_bounds__(ac_threads<MODE>(), 2) k_accept(sv_accept_args
   __shared__ float s_lp[SV_MAX_N], s_lq[SV_MAX_N], s_u[SV_MAX_N];  // per child: logits at its token, u_accept
   __shared__ float s_us;                                            // u_sample of the row
   // bonus: the slice's residual weights in id order, per-piece sums [k][t] and their row totals
-  __shared__ __attribute__((aligned(16))) float s_w[MODE == SV_STOCHASTIC ? ac_slice<T, TH>() : 4];
-  __shared__ float s_g[MODE == SV_STOCHASTIC ? Piece<T>::NK * TH : 4];
+  __shared__ __attribute__((aligned(16))) float s_w[STO ? ac_slice<T, TH>() : 4];
+  __shared__ float s_g[STO ? Piece<T>::NK * TH : 4];
   __shared__ double s_col[Piece<T>::NK];
   __shared__ int s_xc, s_claim, s_fin;  // walk finished (sticky); stochastic walk: claimed row, finisher
   // work-groups are dispatched round-robin over the 8 XCDs; the members of a
@@ -480,7 +482,7 @@ __global__ void __launch_bounds__(ac_threads<MODE>(), 2) k_accept(sv_accept_args
   const int grp = (idx / G) * 8 + xcd;
   const int rank = idx % G;
   const int N = a.N, V = a.V;
-  const float invT = MODE == SV_STOCHASTIC ? 1.0f / a.temperature : 1.0f;
+  const float invT = STO ? 1.0f / a.temperature : 1.0f;
   const float l2T = invT * 1.4426950408889634f;  // bulk exponentials as exp2((x - m) * log2(e) / T)
   XSlot* gslots = ws.xs + (int64_t)grp * G * 2;
   uint32_t xtag = 0;  // exchanges of this group so far (identical on every member)
@@ -503,12 +505,12 @@ __global__ void __launch_bounds__(ac_threads<MODE>(), 2) k_accept(sv_accept_args
     // stochastic, wide trees: the walk advances as rows resolve and ends the sequence's
     // remaining rows (below); chains and narrow trees, where nearly every row is on the
     // path, walk once after the last row
-    const bool incr = MODE == SV_STOCHASTIC && N > 2 * a.max_depth;
+    const bool incr = STO && N > 2 * a.max_depth;
     uint32_t* cancel = incr ? &ws.cancel[b] : nullptr;
     uint32_t cx0 = 0u;  // the sequence's walk already finished (a late work-group)
     if (incr && t == 0) cx0 = ld_u32(cancel);
     uint4 rp[NK];
-    if constexpr (MODE == SV_STOCHASTIC) load_pieces<T, TH>(prow, s0, V, aligned, t, rp);
+    if constexpr (STO) load_pieces<T, TH>(prow, s0, V, aligned, t, rp);
     asm volatile("" : "+v"(sr.tok), "+v"(sr.par), "+v"(sr.dep), "+v"(cx0));  // nothing uses them before this point
     if (cx0) s_xc = 1;
     seq_facts<TH>(a, sr, si);
@@ -547,14 +549,14 @@ __global__ void __launch_bounds__(ac_threads<MODE>(), 2) k_accept(sv_accept_args
         // the row's resolution; returns early once the sequence's walk has finished
         [&]() {
         const int K = __builtin_amdgcn_readfirstlane(si.K);
-        const bool need_q = K > 0;
+        const bool need_q = !TOPK && K > 0;  // deterministic drafts read no draft logits
         // ---- the slice: raw logits -> slice maxima -> exponentials kept in registers
         float ep[ac_ct<T>()], eq[ac_ct<T>()];
         float mp = -FLT_MAX, mq = -FLT_MAX;
         double zp = 0.0, zq = 0.0;
         {
           uint4 rq[NK];
-          load_pieces<T, TH>(qrow, s0, V, aligned, t, rq, need_q);
+          if constexpr (!TOPK) load_pieces<T, TH>(qrow, s0, V, aligned, t, rq, need_q);
           // children's logits at their tokens and their uniforms: issued after the draft
           // slice (so that nothing waits for them before it is issued), stored to LDS once
           // both slices are in
@@ -563,7 +565,7 @@ __global__ void __launch_bounds__(ac_threads<MODE>(), 2) k_accept(sv_accept_args
             const int kid = si.kids[t];
             const int x = si.tok[kid];  // usable: x in [0, V)
             c_lp = ldraw(prow, x);
-            c_lq = ldraw(qrow, x);
+            if constexpr (!TOPK) c_lq = ldraw(qrow, x);
             c_u = __float_as_uint(a.u_accept[(int64_t)b * (N + 1) + kid + 1]);
           }
           if (t == TH - 1) c_us = __float_as_uint(a.u_sample[(int64_t)b * (N + 1) + r]);
@@ -624,14 +626,21 @@ __global__ void __launch_bounds__(ac_threads<MODE>(), 2) k_accept(sv_accept_args
           asm volatile("" : "+v"(c_lp), "+v"(c_lq), "+v"(c_u), "+v"(c_us));  // first use: here
           if (t < K) {
             s_lp[t] = rawf<T>(c_lp);
-            s_lq[t] = rawf<T>(c_lq);
+            if constexpr (TOPK) {  // s_lq holds 1 where the child repeats an earlier sibling's token
+              const int x = si.tok[si.kids[t]];
+              bool dup = false;
+              for (int j = 0; j < t; ++j) dup |= si.tok[si.kids[j]] == x;
+              s_lq[t] = dup ? 1.f : 0.f;
+            } else {
+              s_lq[t] = rawf<T>(c_lq);
+            }
             s_u[t] = __uint_as_float(c_u);
           }
           if (t == TH - 1) s_us = __uint_as_float(c_us);
         }
         zp = block_sum<TH>(zp, red);  // its barriers also publish the children's values
         zq = block_sum<TH>(zq, red);
-        if (exchange<TH>(gslots, G, rank, ++xtag, 6, xv, ws.err, cancel, &s_xc, __float_as_uint(mp),
+        if (exchange<TH>(gslots, G, rank, ++xtag, TOPK ? 4 : 6, xv, ws.err, cancel, &s_xc, __float_as_uint(mp),
                      __float_as_uint(mq), dlo(zp), dhi(zp), dlo(zq), dhi(zq)))
           return;
         // global statistics: lane k of every wave takes member k's partials (G <= 64); the
@@ -668,6 +677,23 @@ __global__ void __launch_bounds__(ac_threads<MODE>(), 2) k_accept(sv_accept_args
         // ---- accept tests along the residual chain
         double c = 0.0, Dn = 1.0, c_prev = 0.0;
         int accepted = -1;
+        if constexpr (TOPK) {
+          // child j's proposal is the point mass at its token x: the test is u < p_cur(x), and
+          // a rejection zeroes x.  p_cur is p restricted to the tokens not rejected yet at this
+          // row, renormalised by their mass `rem`; a repeated token has mass 0.  No exchange:
+          // p(x) is known from the row statistics.
+          double rem = 1.0;
+          for (int j = 0; j < K; ++j) {
+            const double px = (double)expf((s_lp[j] - Mp) * invT) / Zp;
+            const bool dup = s_lq[j] != 0.f;
+            const double cur = dup ? 0.0 : px / rem;
+            if ((double)s_u[j] < cur) { accepted = si.kids[j]; break; }
+            if (!dup && rem - px > 0.0) rem -= px;  // a residual without mass (rounding only) is kept
+          }
+          // the bonus below zeroes the children's tokens (c != 0) and, should rounding leave
+          // that residual without mass, falls back to p itself (c_prev = 0)
+          if (accepted < 0 && K > 0) c = 1.0;
+        } else
         for (int j = 0; j < K; ++j) {
           const double px = (double)expf((s_lp[j] - Mp) * invT) / Zp;
           const double qx = (double)expf((s_lq[j] - Mq) * invT) / Zq;
@@ -705,7 +731,7 @@ __global__ void __launch_bounds__(ac_threads<MODE>(), 2) k_accept(sv_accept_args
           const double us = (double)s_us;
           for (int attempt = 0; attempt < 2; ++attempt) {
             // c == 0 (no rejection at this row): the weights are p itself
-            const float kappa = c == 0.0 ? 0.f : (float)(c * fq / fp);
+            const float kappa = TOPK || c == 0.0 ? 0.f : (float)(c * fq / fp);
             auto stage = [&](auto residual) {
 #pragma unroll
               for (int k = 0; k < NK; ++k) {
@@ -724,6 +750,19 @@ __global__ void __launch_bounds__(ac_threads<MODE>(), 2) k_accept(sv_accept_args
             };
             if (kappa == 0.f) stage(std::false_type{});  // uniform branch
             else stage(std::true_type{});
+            if (TOPK && c != 0.0) {  // every child was rejected: zero their tokens in this slice
+              __syncthreads();
+              const int x = t < K ? si.tok[si.kids[t]] - s0 : -1;
+              const bool mine = x >= 0 && x < ac_slice<T, TH>();
+              if (mine) s_w[x] = 0.f;
+              __syncthreads();
+              if (mine) {  // its piece's sum again (children sharing a piece write the same value)
+                const int pc = x / E;
+                float g = 0.f;
+                for (int e = 0; e < E; ++e) g += s_w[pc * E + e];
+                s_g[pc] = g;
+              }
+            }
             __syncthreads();
             for (int k = wv; k < NK; k += NW) {  // wave wv totals rows wv, wv + NW, ...
               double x = 0.0;
@@ -830,7 +869,7 @@ __global__ void __launch_bounds__(ac_threads<MODE>(), 2) k_accept(sv_accept_args
       // the next unresolved row and checks that row once more, since its publisher may have
       // looked at the frontier before the move (each side completes its store before its
       // load, so at least one of them sees the other's).
-      if (MODE == SV_STOCHASTIC && done_by_me) {
+      if (STO && done_by_me) {
         mem_complete();  // this thread's row-result store (if any) has completed
         __syncthreads();
         uint32_t* front = &ws.frontier[b];
@@ -1012,7 +1051,7 @@ __global__ void __launch_bounds__(ac_threads<MODE>(), 2) k_accept(sv_accept_args
   __syncthreads();
   // (stochastic wide trees only: elsewhere the walker is the sequence's last reader of its
   // row results and clears them itself)
-  const bool seq_item = MODE == SV_STOCHASTIC && N > 2 * a.max_depth && item < (int64_t)a.B * (N + 1);
+  const bool seq_item = MODE != SV_GREEDY && N > 2 * a.max_depth && item < (int64_t)a.B * (N + 1);
   const int bq = seq_item ? (int)(item / (N + 1)) : 0;
   if (t == 0) {
     const uint32_t og = G > 1 ? add_u32(ws.gexit + grp, 1u) : 0u;
@@ -1045,7 +1084,7 @@ __global__ void __launch_bounds__(ac_threads<MODE>(), 2) k_accept(sv_accept_args
 }
 
 int groups_G(const sv_accept_args& a) {
-  const bool st = a.mode == SV_STOCHASTIC;
+  const bool st = a.mode != SV_GREEDY;  // both walk modes share the 256-thread layout
   const int slice = a.logits_dtype == SV_BF16
                         ? (st ? ac_slice<uint16_t, ac_threads<SV_STOCHASTIC>()>() : ac_slice<uint16_t, ac_threads<SV_GREEDY>()>())
                         : (st ? ac_slice<float, ac_threads<SV_STOCHASTIC>()>() : ac_slice<float, ac_threads<SV_GREEDY>()>());
@@ -1087,14 +1126,14 @@ extern "C" sv_status sv_accept(const sv_accept_args* args, void* stream) {
   const sv_accept_args& a = *args;
   if (a.B < 0 || a.N < 1 || a.N > SV_MAX_N || a.V < 1 || a.max_depth < 1 || a.max_depth > SV_MAX_DEPTH)
     return SV_ERR_INVALID_ARGUMENT;
-  if (a.mode != SV_GREEDY && a.mode != SV_STOCHASTIC) return SV_ERR_INVALID_ARGUMENT;
+  if (a.mode != SV_GREEDY && a.mode != SV_STOCHASTIC && a.mode != SV_TOPK_DRAFT) return SV_ERR_INVALID_ARGUMENT;
   if (a.logits_dtype != SV_F32 && a.logits_dtype != SV_BF16) return SV_ERR_UNSUPPORTED;
   if (a.B == 0) return SV_OK;
   if (!a.parents || !a.tokens || !a.anc_bits || !a.depth || !a.target_logits || !a.accept_len || !a.accept_rows ||
       !a.out_tokens || !a.num_out || !a.stop_row || !a.status || !a.workspace)
     return SV_ERR_INVALID_ARGUMENT;
-  if (a.mode == SV_STOCHASTIC && (!a.draft_logits || !a.u_accept || !a.u_sample || !(a.temperature > 0.f)))
-    return SV_ERR_INVALID_ARGUMENT;
+  if (a.mode == SV_STOCHASTIC && !a.draft_logits) return SV_ERR_INVALID_ARGUMENT;
+  if (a.mode != SV_GREEDY && (!a.u_accept || !a.u_sample || !(a.temperature > 0.f))) return SV_ERR_INVALID_ARGUMENT;
   const WsLayout l = ws_layout(a);
   if (a.workspace_bytes < l.total || ((uintptr_t)a.workspace % 256)) return SV_ERR_INVALID_ARGUMENT;
   const int G = groups_G(a);
@@ -1116,13 +1155,15 @@ extern "C" sv_status sv_accept(const sv_accept_args* args, void* stream) {
   // rows start on 16 bytes when the row pitch and the base pointers are multiples of 16
   const size_t esz = a.logits_dtype == SV_BF16 ? 2 : 4;
   const bool aligned = ((size_t)a.V * esz) % 16 == 0 && ((uintptr_t)a.target_logits % 16) == 0 &&
-                       (a.mode == SV_GREEDY || ((uintptr_t)a.draft_logits % 16) == 0);
+                       (a.mode != SV_STOCHASTIC || ((uintptr_t)a.draft_logits % 16) == 0);
 #define SV_ACC_LAUNCH(T, M, AL) hipLaunchKernelGGL((k_accept<T, M, AL>), grid, dim3(ac_threads<M>()), 0, st, a, G, ws)
   if (a.logits_dtype == SV_BF16) {
     if (a.mode == SV_STOCHASTIC) { if (aligned) SV_ACC_LAUNCH(uint16_t, SV_STOCHASTIC, true); else SV_ACC_LAUNCH(uint16_t, SV_STOCHASTIC, false); }
+    else if (a.mode == SV_TOPK_DRAFT) { if (aligned) SV_ACC_LAUNCH(uint16_t, SV_TOPK_DRAFT, true); else SV_ACC_LAUNCH(uint16_t, SV_TOPK_DRAFT, false); }
     else { if (aligned) SV_ACC_LAUNCH(uint16_t, SV_GREEDY, true); else SV_ACC_LAUNCH(uint16_t, SV_GREEDY, false); }
   } else {
     if (a.mode == SV_STOCHASTIC) { if (aligned) SV_ACC_LAUNCH(float, SV_STOCHASTIC, true); else SV_ACC_LAUNCH(float, SV_STOCHASTIC, false); }
+    else if (a.mode == SV_TOPK_DRAFT) { if (aligned) SV_ACC_LAUNCH(float, SV_TOPK_DRAFT, true); else SV_ACC_LAUNCH(float, SV_TOPK_DRAFT, false); }
     else { if (aligned) SV_ACC_LAUNCH(float, SV_GREEDY, true); else SV_ACC_LAUNCH(float, SV_GREEDY, false); }
   }
 #undef SV_ACC_LAUNCH

@@ -138,7 +138,12 @@ def topk_tokens(logits: np.ndarray, parents: np.ndarray) -> np.ndarray:
         for r, ch in kids.items():
             row = logits[b, r]
             row = bf16_to_f32(row) if row.dtype == np.uint16 else row.astype(np.float32)
-            order = np.argsort(-row, kind="stable")[:len(ch)]
+            n = min(len(ch), row.size)
+            kth = np.partition(row, row.size - n)[row.size - n]  # the n-th largest value
+            above = np.nonzero(row > kth)[0]
+            cand = np.concatenate([above, np.nonzero(row == kth)[0][:n - above.size]])
+            order = cand[np.lexsort((cand, -row[cand]))]  # descending value, then ascending id
+            order = np.concatenate([order, np.zeros(len(ch) - n, np.int64)])
             for k, i in enumerate(ch):
                 out[b, i] = order[k]
     return out
