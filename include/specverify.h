@@ -136,6 +136,15 @@ sv_status sv_build_tree_mask(const int32_t* parents, int32_t B, int32_t N, int32
  * status (nullable) [B]: 5 if a needed block-table entry is 0 or >=
  * num_blocks (read as the ghost block), 6 if prefix_len is outside
  * [0, capacity] (clamped).
+ * tree_in_cache (0 or 1): 1 keeps the tree tokens' K/V inside the cache
+ *   itself, as the speculative region after the prefix ([EP] sec. 2: the
+ *   committed prefix and the per-branch speculative state of one cache, then
+ *   committed in place).  Node t's key is then cache position prefix_len[b] + t
+ *   (through the block table when paged), k_tree / v_tree are not read (may be
+ *   NULL), the capacity left for the prefix is capacity - N (status 6 and a
+ *   clamped prefix beyond it), the blocks of positions [0, prefix_len + N) are
+ *   the needed ones, and capacity >= N is required (else
+ *   SV_ERR_INVALID_ARGUMENT).
  */
 typedef struct sv_attn_args {
   int32_t B, N, Hq, Hkv, D, dtype;
@@ -155,6 +164,7 @@ typedef struct sv_attn_args {
   void* workspace;
   size_t workspace_bytes;
   int32_t* status;
+  int32_t tree_in_cache;
 } sv_attn_args;
 size_t sv_tree_attention_workspace(const sv_attn_args* args);
 sv_status sv_tree_attention(const sv_attn_args* args, void* stream);
@@ -242,6 +252,23 @@ sv_status sv_accept(const sv_accept_args* args, void* stream);
  * 5: ghost or out-of-pool block; 6: beyond capacity) and then nothing of that
  * sequence is written: new_len = L, committed_slots all 0.
  * Element size follows dtype (SV_F32 4 bytes, SV_BF16 2 bytes).
+ *
+ * tree_in_cache (0 or 1): the tree rows live in the cache at positions L + t
+ *   (node t, as in sv_tree_attention); k_tree / v_tree are not read (may be
+ *   NULL).  The commit is then an in-place compaction of the accepted path:
+ *   position L + k receives what position L + src_k - 1 held before the call
+ *   (every source row is read before any row is written, so the order of the
+ *   path does not matter), and a row already in place (src_k - 1 == k, e.g.
+ *   every row in length mode) is not moved at all ([EP] sec. 2: the path-index
+ *   commit avoids needless memory moves).  Checks add: L + N within the
+ *   capacity (6) and valid blocks for the source positions (5).  The blocks of
+ *   positions [L, L + N) must belong to this sequence alone.
+ * num_layers (>= 1; 0 is read as 1): commits that many layers in one launch.
+ *   Layer l's caches start cache_layer_stride elements after layer l-1's (both
+ *   k_cache and v_cache), its tree rows tree_layer_stride elements after layer
+ *   l-1's; every layer shares prefix_len, the accepted rows and the block
+ *   table, so the checks, new_len, committed_slots and status are those of one
+ *   layer.  Strides of 0 with num_layers > 1 are rejected.
  */
 typedef struct sv_commit_args {
   int32_t B, N, Hkv, D, dtype, max_depth, commit_mode;
@@ -257,6 +284,10 @@ typedef struct sv_commit_args {
   int32_t* new_len;
   int32_t* committed_slots;
   int32_t* status;
+  int32_t tree_in_cache;
+  int32_t num_layers;
+  int64_t cache_layer_stride;
+  int64_t tree_layer_stride;
 } sv_commit_args;
 sv_status sv_kv_commit(const sv_commit_args* args, void* stream);
 

@@ -41,7 +41,8 @@ class _AttnArgs(ctypes.Structure):
                 ("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
                 ("k_tree", ctypes.c_void_p), ("v_tree", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
                 ("prefix_len", ctypes.c_void_p), ("parents", ctypes.c_void_p), ("max_depth", ctypes.c_int32),
-                ("sel", ctypes.c_void_p), ("n_sel", ctypes.c_int64), ("out", ctypes.c_void_p)]
+                ("sel", ctypes.c_void_p), ("n_sel", ctypes.c_int64), ("out", ctypes.c_void_p),
+                ("tree_in_cache", ctypes.c_int32)]
 
 
 class _AcceptArgs(ctypes.Structure):
@@ -62,7 +63,9 @@ class _CommitArgs(ctypes.Structure):
                 ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
                 ("k_tree", ctypes.c_void_p), ("v_tree", ctypes.c_void_p), ("prefix_len", ctypes.c_void_p),
                 ("accept_len", ctypes.c_void_p), ("accept_rows", ctypes.c_void_p), ("new_len", ctypes.c_void_p),
-                ("committed_slots", ctypes.c_void_p), ("status", ctypes.c_void_p)]
+                ("committed_slots", ctypes.c_void_p), ("status", ctypes.c_void_p),
+                ("tree_in_cache", ctypes.c_int32), ("num_layers", ctypes.c_int32),
+                ("cache_layer_stride", ctypes.c_int64), ("tree_layer_stride", ctypes.c_int64)]
 
 
 def _L():
@@ -130,6 +133,7 @@ def tree_attention(w, sel: Optional[np.ndarray] = None, parents: Optional[np.nda
     a.prefix_len = _p(plen)
     a.parents = _p(parents)
     a.max_depth = w.max_depth
+    a.tree_in_cache = int(bool(getattr(w, "tree_in_cache", False)))
     if sel is not None:
         sel = np.ascontiguousarray(sel, dtype=np.int64)
         out = np.zeros((sel.size, w.D), dtype=np.float64)
@@ -179,16 +183,23 @@ def accept(w, mode: Optional[str] = None, temperature: Optional[float] = None, t
 
 
 def kv_commit(w, accept_len: np.ndarray, accept_rows: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
-              commit_mode: int = 0, prefix_len=None, block_table=None) -> dict:
-    """Commits into the given caches in place (pass copies); returns new_len, committed_slots, status."""
+              commit_mode: int = 0, prefix_len=None, block_table=None, k_tree=None, v_tree=None,
+              num_layers: int = 1) -> dict:
+    """Commits into the given caches in place (pass copies); returns new_len, committed_slots, status.
+
+    num_layers > 1: k_cache / v_cache (and k_tree / v_tree unless the tree rows are
+    in the cache) carry a leading layer dimension; every layer is committed."""
     B, N, Dm = w.B, w.N, w.max_depth
+    tic = bool(getattr(w, "tree_in_cache", False))
     plen = np.ascontiguousarray(w.prefix_len if prefix_len is None else prefix_len, dtype=np.int32)
     bt = w.block_table if block_table is None else block_table
     bt = np.ascontiguousarray(bt, dtype=np.int32) if bt is not None else None
     alen = np.ascontiguousarray(accept_len, dtype=np.int32)
     arows = np.ascontiguousarray(accept_rows, dtype=np.int32)
-    kt = np.ascontiguousarray(w.k_tree)
-    vt = np.ascontiguousarray(w.v_tree)
+    kt = w.k_tree if k_tree is None else k_tree
+    vt = w.v_tree if v_tree is None else v_tree
+    kt = None if tic else np.ascontiguousarray(kt)
+    vt = None if tic else np.ascontiguousarray(vt)
     out = dict(new_len=np.zeros(B, np.int32), committed_slots=np.zeros((B, Dm), np.int32),
                status=np.zeros(B, np.int32))
     a = _CommitArgs()
@@ -202,6 +213,11 @@ def kv_commit(w, accept_len: np.ndarray, accept_rows: np.ndarray, k_cache: np.nd
     a.k_tree, a.v_tree = _p(kt), _p(vt)
     a.prefix_len, a.accept_len, a.accept_rows = _p(plen), _p(alen), _p(arows)
     a.new_len, a.committed_slots, a.status = _p(out["new_len"]), _p(out["committed_slots"]), _p(out["status"])
+    a.tree_in_cache = int(tic)
+    a.num_layers = num_layers
+    if num_layers > 1:
+        a.cache_layer_stride = k_cache[0].size
+        a.tree_layer_stride = 0 if tic else kt[0].size
     if _L().orc_kv_commit(ctypes.byref(a)) != 0:
         raise ValueError("orc_kv_commit rejected its arguments")
     return out

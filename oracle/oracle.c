@@ -90,6 +90,18 @@ int orc_build_tree_mask(const int32_t* parents, int32_t B, int32_t N, int32_t ma
 }
 
 /* --------------------------------------------------------------- attention */
+/* Element offset of logical position j of sequence b, KV head g, in a cache that
+ * is contiguous [B,Hkv,Lcap,D] or paged [num_blocks,Hkv,bs,D] (an entry outside
+ * the pool reads the ghost block 0). */
+static int64_t attn_cache_offset(const orc_attn_args* a, int32_t b, int32_t g, int64_t j) {
+  if (a->paged) {
+    int32_t id = a->block_table[(int64_t)b * a->max_blocks + j / a->block_size];
+    if (id < 0 || id >= a->num_blocks) id = 0;
+    return (((int64_t)id * a->Hkv + g) * a->block_size + j % a->block_size) * a->D;
+  }
+  return (((int64_t)b * a->Hkv + g) * a->Lcap + j) * a->D;
+}
+
 int orc_tree_attention(const orc_attn_args* a) {
   if (a->B < 1 || a->N < 1 || a->Hkv < 1 || a->Hq % a->Hkv != 0 || a->D < 1) return -1;
   const int32_t N = a->N, Hq = a->Hq, Hkv = a->Hkv, D = a->D, G = a->Hq / a->Hkv;
@@ -108,6 +120,7 @@ int orc_tree_attention(const orc_attn_args* a) {
       len = 1;
     }
     int32_t cap = a->paged ? a->max_blocks * a->block_size : a->Lcap;
+    if (a->tree_in_cache) cap -= N; /* the speculative region follows the prefix */
     int32_t L = a->prefix_len[b];
     if (L < 0) L = 0;
     if (L > cap) L = cap;
@@ -126,6 +139,9 @@ int orc_tree_attention(const orc_attn_args* a) {
         } else {
           koff = (((int64_t)b * Hkv + g) * a->Lcap + j) * D;
         }
+        kb = a->k_cache;
+      } else if (a->tree_in_cache) {
+        koff = attn_cache_offset(a, b, g, (int64_t)L + path[j - L]);
         kb = a->k_cache;
       } else {
         int32_t t = path[j - L];
@@ -157,6 +173,9 @@ int orc_tree_attention(const orc_attn_args* a) {
         } else {
           voff = (((int64_t)b * Hkv + g) * a->Lcap + j) * D;
         }
+        vb = a->v_cache;
+      } else if (a->tree_in_cache) {
+        voff = attn_cache_offset(a, b, g, (int64_t)L + path[j - L]);
         vb = a->v_cache;
       } else {
         int32_t t = path[j - L];
@@ -323,31 +342,60 @@ int orc_accept(const orc_accept_args* a) {
 }
 
 /* --------------------------------------------------------------- KV commit */
+/* Slot of logical position pos of sequence b: 0 and *slot, or a status code
+ * (6 beyond the capacity, 5 a ghost or out-of-pool block). */
+static int commit_slot(const orc_commit_args* a, int32_t b, int64_t pos, int64_t* slot) {
+  if (a->paged) {
+    const int64_t blk = pos / a->block_size;
+    if (blk >= a->max_blocks) return 6;
+    const int32_t id = a->block_table[(int64_t)b * a->max_blocks + blk];
+    if (id < 1 || id >= a->num_blocks) return 5;
+    *slot = (int64_t)id * a->block_size + pos % a->block_size;
+  } else {
+    if (pos >= a->Lcap) return 6;
+    *slot = pos;
+  }
+  return 0;
+}
+
+/* Row offset (in rows of D elements) of slot `slot`, KV head h, sequence b, in one layer's cache. */
+static int64_t commit_cache_row(const orc_commit_args* a, int32_t b, int32_t h, int64_t slot) {
+  if (a->paged) return (slot / a->block_size * a->Hkv + h) * a->block_size + slot % a->block_size;
+  return ((int64_t)b * a->Hkv + h) * a->Lcap + slot;
+}
+
+/*
+ * [EP] sec. 2, branchable KV cache: the accepted path's K/V rows become the
+ * cache entries at positions L, L+1, ..., L+A-1 (by path index, or the first A
+ * tree rows in length mode).  Checks per sequence, in order: L >= 0 and
+ * 0 <= A <= max_depth (1); with cache-resident tree rows L + N within the
+ * capacity (6); then for k = 0 .. A-1: the source row lies in [1, N] (1), the
+ * destination position has a slot (6 / 5), and with cache-resident tree rows
+ * so does the source position L + src - 1 (5).  A failing sequence is left
+ * untouched.  With cache-resident rows every source row is read (into a copy)
+ * before any destination is written: position L + k receives the old contents
+ * of position L + src_k - 1.
+ */
 int orc_kv_commit(const orc_commit_args* a) {
   const int32_t B = a->B, N = a->N, Hkv = a->Hkv, D = a->D, Dm = a->max_depth, eb = a->elem_bytes;
-  if (B < 0 || N < 1 || Dm < 1 || (eb != 2 && eb != 4)) return -1;
+  if (B < 0 || N < 1 || Dm < 1 || Dm > 64 || (eb != 2 && eb != 4)) return -1;
+  const int32_t layers = a->num_layers < 1 ? 1 : a->num_layers;
   const size_t row_bytes = (size_t)D * eb;
+  const int64_t cap = a->paged ? (int64_t)a->max_blocks * a->block_size : a->Lcap;
+  char* copy = (char*)malloc(row_bytes * 2 * 64 * (size_t)Hkv);
   for (int32_t b = 0; b < B; ++b) {
     const int32_t L = a->prefix_len[b];
     const int32_t A = a->accept_len[b];
     int32_t code = 0;
     if (L < 0 || A < 0 || A > Dm) code = 1;
-    int64_t slot[64];
+    else if (a->tree_in_cache && (int64_t)L + N > cap) code = 6;
+    int64_t slot[64], src_slot[64];
     int32_t src[64];
     for (int32_t k = 0; k < A && code == 0; ++k) {
       src[k] = a->commit_mode == 0 ? a->accept_rows[(int64_t)b * Dm + k] : k + 1;
       if (src[k] < 1 || src[k] > N) { code = 1; break; }
-      const int64_t pos = (int64_t)L + k;
-      if (a->paged) {
-        const int64_t blk = pos / a->block_size;
-        if (blk >= a->max_blocks) { code = 6; break; }
-        const int32_t id = a->block_table[(int64_t)b * a->max_blocks + blk];
-        if (id < 1 || id >= a->num_blocks) { code = 5; break; }
-        slot[k] = (int64_t)id * a->block_size + pos % a->block_size;
-      } else {
-        if (pos >= a->Lcap) { code = 6; break; }
-        slot[k] = pos;
-      }
+      code = commit_slot(a, b, (int64_t)L + k, &slot[k]);
+      if (code == 0 && a->tree_in_cache) code = commit_slot(a, b, (int64_t)L + src[k] - 1, &src_slot[k]);
     }
     a->status[b] = code;
     for (int32_t k = 0; k < Dm; ++k) a->committed_slots[(int64_t)b * Dm + k] = 0;
@@ -355,22 +403,38 @@ int orc_kv_commit(const orc_commit_args* a) {
       a->new_len[b] = L;
       continue;
     }
-    for (int32_t k = 0; k < A; ++k) {
-      a->committed_slots[(int64_t)b * Dm + k] = (int32_t)slot[k];
-      for (int32_t h = 0; h < Hkv; ++h) {
-        const int64_t s_off = ((int64_t)b * Hkv + h) * (N + 1) + src[k];
-        int64_t d_off;
-        if (a->paged) {
-          const int64_t id = slot[k] / a->block_size, off = slot[k] % a->block_size;
-          d_off = (id * Hkv + h) * a->block_size + off;
-        } else {
-          d_off = ((int64_t)b * Hkv + h) * a->Lcap + slot[k];
-        }
-        memcpy((char*)a->k_cache + d_off * row_bytes, (const char*)a->k_tree + s_off * row_bytes, row_bytes);
-        memcpy((char*)a->v_cache + d_off * row_bytes, (const char*)a->v_tree + s_off * row_bytes, row_bytes);
+    for (int32_t l = 0; l < layers; ++l) {
+      char* kc = (char*)a->k_cache + (size_t)(l * a->cache_layer_stride) * eb;
+      char* vc = (char*)a->v_cache + (size_t)(l * a->cache_layer_stride) * eb;
+      if (a->tree_in_cache) {
+        /* read every source row first, then write */
+        for (int32_t k = 0; k < A; ++k)
+          for (int32_t h = 0; h < Hkv; ++h) {
+            const int64_t s_row = commit_cache_row(a, b, h, src_slot[k]);
+            memcpy(copy + ((size_t)(k * Hkv + h) * 2 + 0) * row_bytes, kc + s_row * row_bytes, row_bytes);
+            memcpy(copy + ((size_t)(k * Hkv + h) * 2 + 1) * row_bytes, vc + s_row * row_bytes, row_bytes);
+          }
+        for (int32_t k = 0; k < A; ++k)
+          for (int32_t h = 0; h < Hkv; ++h) {
+            const int64_t d_row = commit_cache_row(a, b, h, slot[k]);
+            memcpy(kc + d_row * row_bytes, copy + ((size_t)(k * Hkv + h) * 2 + 0) * row_bytes, row_bytes);
+            memcpy(vc + d_row * row_bytes, copy + ((size_t)(k * Hkv + h) * 2 + 1) * row_bytes, row_bytes);
+          }
+      } else {
+        const char* kt = (const char*)a->k_tree + (size_t)(l * a->tree_layer_stride) * eb;
+        const char* vt = (const char*)a->v_tree + (size_t)(l * a->tree_layer_stride) * eb;
+        for (int32_t k = 0; k < A; ++k)
+          for (int32_t h = 0; h < Hkv; ++h) {
+            const int64_t s_row = ((int64_t)b * Hkv + h) * (N + 1) + src[k];
+            const int64_t d_row = commit_cache_row(a, b, h, slot[k]);
+            memcpy(kc + d_row * row_bytes, kt + s_row * row_bytes, row_bytes);
+            memcpy(vc + d_row * row_bytes, vt + s_row * row_bytes, row_bytes);
+          }
       }
     }
+    for (int32_t k = 0; k < A; ++k) a->committed_slots[(int64_t)b * Dm + k] = (int32_t)slot[k];
     a->new_len[b] = L + A;
   }
+  free(copy);
   return 0;
 }

@@ -66,6 +66,10 @@ typedef struct {
   const int64_t* sel;         /* flat (b*N + i)*Hq + h, or NULL for all */
   int64_t n_sel;
   double* out;
+  /* 1: the tree rows live in the cache itself, node t at position prefix_len + t
+   * ([EP] sec. 2: prefix and speculative state of one branchable cache); the
+   * prefix may then fill only capacity - N positions, k_tree / v_tree unused */
+  int32_t tree_in_cache;
 } orc_attn_args;
 int orc_tree_attention(const orc_attn_args* a);
 
@@ -108,6 +112,15 @@ typedef struct {
   const int32_t* accept_len;
   const int32_t* accept_rows;
   int32_t *new_len, *committed_slots, *status;
+  /* 1: tree rows in the cache at positions L + t; the commit makes position L + k
+   * hold what position L + src_k - 1 held before the call (in-place compaction of
+   * the accepted path, [EP] sec. 2) */
+  int32_t tree_in_cache;
+  /* layers committed by one call (0 is read as 1): layer l of the caches starts
+   * cache_layer_stride elements after layer l-1, its tree rows tree_layer_stride
+   * elements after; every layer shares lengths, accepted rows and block table */
+  int32_t num_layers;
+  int64_t cache_layer_stride, tree_layer_stride;
 } orc_commit_args;
 int orc_kv_commit(const orc_commit_args* a);
 

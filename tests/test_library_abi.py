@@ -81,3 +81,26 @@ def test_no_product_module_imports_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in txt and "oracle." not in txt.replace("the oracle", ""), f
+
+
+def test_tree_in_cache_and_layer_arguments_rejected_without_launch():
+    L = sv.lib()
+    a = sv.sv_attn_args()
+    a.B, a.N, a.Hq, a.Hkv, a.D, a.dtype, a.scale = 1, 60, 32, 8, 128, sv.SV_BF16, 0.088
+    a.Lcap, a.tree_in_cache = 59, 1  # the cache cannot hold the tree rows
+    assert L.sv_tree_attention(ctypes.byref(a), None) == sv.SV_ERR_INVALID_ARGUMENT
+    a.tree_in_cache = 2
+    assert L.sv_tree_attention(ctypes.byref(a), None) == sv.SV_ERR_INVALID_ARGUMENT
+    a.Lcap, a.tree_in_cache = 4160, 1  # valid shape, but no pointers
+    assert L.sv_tree_attention(ctypes.byref(a), None) == sv.SV_ERR_INVALID_ARGUMENT
+    assert sv.sv_tree_attention_workspace(a) > 0
+    c = sv.sv_commit_args()
+    c.B, c.N, c.Hkv, c.D, c.dtype, c.max_depth, c.commit_mode, c.Lcap = 1, 4, 2, 64, sv.SV_F32, 4, 0, 64
+    c.num_layers = 3  # several layers need positive layer strides
+    assert L.sv_kv_commit(ctypes.byref(c), None) == sv.SV_ERR_INVALID_ARGUMENT
+    c.cache_layer_stride, c.tree_layer_stride = 1 << 20, 0
+    assert L.sv_kv_commit(ctypes.byref(c), None) == sv.SV_ERR_INVALID_ARGUMENT
+    c.tree_in_cache = 1  # the tree stride is not needed with the rows in the cache; pointers still are
+    assert L.sv_kv_commit(ctypes.byref(c), None) == sv.SV_ERR_INVALID_ARGUMENT
+    c.num_layers = -1
+    assert L.sv_kv_commit(ctypes.byref(c), None) == sv.SV_ERR_INVALID_ARGUMENT

@@ -56,7 +56,8 @@ class sv_attn_args(ctypes.Structure):
                 ("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
                 ("k_tree", ctypes.c_void_p), ("v_tree", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
                 ("prefix_len", ctypes.c_void_p), ("anc_bits", ctypes.c_void_p), ("out", ctypes.c_void_p),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t), ("status", ctypes.c_void_p)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t), ("status", ctypes.c_void_p),
+                ("tree_in_cache", ctypes.c_int32)]
 
 
 class sv_accept_args(ctypes.Structure):
@@ -78,7 +79,9 @@ class sv_commit_args(ctypes.Structure):
                 ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
                 ("k_tree", ctypes.c_void_p), ("v_tree", ctypes.c_void_p), ("prefix_len", ctypes.c_void_p),
                 ("accept_len", ctypes.c_void_p), ("accept_rows", ctypes.c_void_p), ("new_len", ctypes.c_void_p),
-                ("committed_slots", ctypes.c_void_p), ("status", ctypes.c_void_p)]
+                ("committed_slots", ctypes.c_void_p), ("status", ctypes.c_void_p),
+                ("tree_in_cache", ctypes.c_int32), ("num_layers", ctypes.c_int32),
+                ("cache_layer_stride", ctypes.c_int64), ("tree_layer_stride", ctypes.c_int64)]
 
 
 EXPORTS = ["sv_build_tree_mask", "sv_tree_attention_workspace", "sv_tree_attention", "sv_accept_workspace",
@@ -184,10 +187,10 @@ def sv_build_tree_mask(parents, max_depth: int, out: Optional[dict] = None, stre
 
 
 def attn_args(q, k_cache, v_cache, k_tree, v_tree, anc_bits, prefix_len, out, block_table=None, scale=None,
-              paged=False, num_blocks=0, status=None) -> sv_attn_args:
+              paged=False, num_blocks=0, status=None, tree_in_cache=False) -> sv_attn_args:
     torch = _torch()
     B, N, Hq, D = q.shape
-    Hkv = k_tree.shape[1]
+    Hkv = k_cache.shape[1]  # [B,Hkv,Lcap,D] or [num_blocks,Hkv,bs,D]
     a = sv_attn_args()
     a.B, a.N, a.Hq, a.Hkv, a.D = B, N, Hq, Hkv, D
     a.dtype = _elem(q)
@@ -201,8 +204,11 @@ def attn_args(q, k_cache, v_cache, k_tree, v_tree, anc_bits, prefix_len, out, bl
     else:
         a.Lcap = k_cache.shape[2]
         a.block_size, a.max_blocks, a.num_blocks = 16, 0, 0
+    a.tree_in_cache = int(bool(tree_in_cache))
+    if tree_in_cache:
+        k_tree = v_tree = None  # the tree rows are cache positions prefix_len + t
     for t, nm in ((k_cache, "k_cache"), (v_cache, "v_cache"), (k_tree, "k_tree"), (v_tree, "v_tree"), (out, "out")):
-        if t.dtype != q.dtype:
+        if t is not None and t.dtype != q.dtype:
             raise SpecVerifyError(f"{nm} dtype {t.dtype} differs from q dtype {q.dtype}")
     a.q, a.k_cache, a.v_cache = _ptr(q, name="q"), _ptr(k_cache, name="k_cache"), _ptr(v_cache, name="v_cache")
     a.k_tree, a.v_tree = _ptr(k_tree, name="k_tree"), _ptr(v_tree, name="v_tree")
@@ -219,13 +225,16 @@ def sv_tree_attention_workspace(args: sv_attn_args) -> int:
 
 
 def sv_tree_attention(q, k_cache, v_cache, k_tree, v_tree, anc_bits, prefix_len, block_table=None, scale=None,
-                      paged=False, num_blocks=0, out=None, workspace=None, status=None, stream=None):
-    """Ancestor-masked GQA tree attention; returns out [B,N,Hq,D] (dtype of q)."""
+                      paged=False, num_blocks=0, out=None, workspace=None, status=None, stream=None,
+                      tree_in_cache=False):
+    """Ancestor-masked GQA tree attention; returns out [B,N,Hq,D] (dtype of q).
+
+    tree_in_cache: node t's K/V is cache position prefix_len + t (k_tree / v_tree ignored)."""
     torch = _torch()
     if out is None:
         out = torch.empty_like(q)
     a = attn_args(q, k_cache, v_cache, k_tree, v_tree, anc_bits, prefix_len, out, block_table, scale, paged,
-                  num_blocks, status)
+                  num_blocks, status, tree_in_cache)
     need = sv_tree_attention_workspace(a)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = _alloc_workspace(need, q.device)
@@ -297,19 +306,39 @@ def sv_accept(parents, tokens, anc_bits, depth, target_logits, max_depth, mode="
 
 def commit_args(k_cache, v_cache, k_tree, v_tree, prefix_len, accept_len, accept_rows, max_depth, new_len,
                 committed_slots, status, block_table=None, paged=False, num_blocks=0,
-                commit_mode=SV_COMMIT_PATH) -> sv_commit_args:
+                commit_mode=SV_COMMIT_PATH, tree_in_cache=False, N=None, num_layers=1) -> sv_commit_args:
+    """num_layers > 1: k_cache / v_cache (and k_tree / v_tree) carry a leading layer dimension.
+    tree_in_cache: the tree rows are cache positions prefix_len + t; N must be given."""
     torch = _torch()
-    B, Hkv, Np1, D = k_tree.shape
+    layered = num_layers > 1
+    kc1 = k_cache[0] if layered else k_cache  # one layer's cache
+    B = prefix_len.shape[0]
+    Hkv, D = kc1.shape[1], kc1.shape[3]
+    if tree_in_cache:
+        if N is None:
+            raise SpecVerifyError("tree_in_cache needs the tree size N")
+        k_tree = v_tree = None
+    else:
+        kt1 = k_tree[0] if layered else k_tree
+        N = kt1.shape[2] - 1
     a = sv_commit_args()
-    a.B, a.N, a.Hkv, a.D = B, Np1 - 1, Hkv, D
-    a.dtype = _elem(k_tree)
+    a.B, a.N, a.Hkv, a.D = B, N, Hkv, D
+    a.dtype = _elem(k_cache)
     a.max_depth, a.commit_mode = max_depth, commit_mode
     a.paged = int(bool(paged))
     if paged:
-        a.Lcap, a.block_size, a.max_blocks = 0, k_cache.shape[2], block_table.shape[1]
-        a.num_blocks = num_blocks or k_cache.shape[0]
+        a.Lcap, a.block_size, a.max_blocks = 0, kc1.shape[2], block_table.shape[1]
+        a.num_blocks = num_blocks or kc1.shape[0]
     else:
-        a.Lcap, a.block_size, a.max_blocks, a.num_blocks = k_cache.shape[2], 16, 0, 0
+        a.Lcap, a.block_size, a.max_blocks, a.num_blocks = kc1.shape[2], 16, 0, 0
+    a.tree_in_cache = int(bool(tree_in_cache))
+    a.num_layers = num_layers
+    if layered:
+        a.cache_layer_stride = kc1.numel()
+        a.tree_layer_stride = 0 if tree_in_cache else k_tree[0].numel()
+    for t, nm in ((v_cache, "v_cache"), (k_tree, "k_tree"), (v_tree, "v_tree")):
+        if t is not None and t.dtype != k_cache.dtype:
+            raise SpecVerifyError(f"{nm} dtype {t.dtype} differs from k_cache dtype {k_cache.dtype}")
     a.k_cache, a.v_cache = _ptr(k_cache, name="k_cache"), _ptr(v_cache, name="v_cache")
     a.block_table = _ptr(block_table, torch.int32, "block_table")
     a.k_tree, a.v_tree = _ptr(k_tree, name="k_tree"), _ptr(v_tree, name="v_tree")
@@ -324,18 +353,18 @@ def commit_args(k_cache, v_cache, k_tree, v_tree, prefix_len, accept_len, accept
 
 def sv_kv_commit(k_cache, v_cache, k_tree, v_tree, prefix_len, accept_len, accept_rows, max_depth,
                  block_table=None, paged=False, num_blocks=0, commit_mode=SV_COMMIT_PATH, outs=None,
-                 stream=None) -> dict:
+                 stream=None, tree_in_cache=False, N=None, num_layers=1) -> dict:
     """Commit the accepted rows into the caches in place; returns new_len, committed_slots, status."""
     torch = _torch()
-    B = k_tree.shape[0]
-    dev = k_tree.device
+    B = prefix_len.shape[0]
+    dev = k_cache.device
     if outs is None:
         outs = dict(new_len=torch.empty(B, dtype=torch.int32, device=dev),
                     committed_slots=torch.empty((B, max_depth), dtype=torch.int32, device=dev),
                     status=torch.empty(B, dtype=torch.int32, device=dev))
     a = commit_args(k_cache, v_cache, k_tree, v_tree, prefix_len, accept_len, accept_rows, max_depth,
                     outs["new_len"], outs["committed_slots"], outs["status"], block_table, paged, num_blocks,
-                    commit_mode)
+                    commit_mode, tree_in_cache, N, num_layers)
     _check(lib().sv_kv_commit(ctypes.byref(a), _stream(stream)), "sv_kv_commit")
     return outs
 

@@ -65,7 +65,8 @@ __device__ void write_seq_status(const sv_attn_args& a, int b, int cap) {
   if (L0 < 0 || L0 > cap) {
     if (threadIdx.x == 0) s_code = SV_SEQ_CAPACITY;
   } else if (a.paged) {
-    const int nblk = (L0 + a.block_size - 1) / a.block_size;
+    // with the tree rows resident in the cache, positions L0 .. L0 + N - 1 are read too
+    const int nblk = (L0 + (a.tree_in_cache ? a.N : 0) + a.block_size - 1) / a.block_size;
     for (int k = threadIdx.x; k < nblk; k += blockDim.x) {
       const int id = a.block_table[(int64_t)b * a.max_blocks + k];
       if (id < 1 || id >= a.num_blocks) atomicOr(&s_code, SV_SEQ_BLOCK);
@@ -184,11 +185,11 @@ __global__ void __launch_bounds__(MF_THREADS, 2) k_attn_mfma(sv_attn_args a, Att
   // the valid range are clamped onto the last valid key of the tile (finite data,
   // masked out of the softmax), so no load ever leaves the tensor.
   const int64_t plane = (int64_t)b * a.Hkv + g;
-  __amdgpu_buffer_rsrc_t rk, rv;
-  const __amdgpu_buffer_rsrc_t rkt = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(kt + (plane * (N + 1) + 1) * D), 0, (int)(N * ROWB), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rvt = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(vt + (plane * (N + 1) + 1) * D), 0, (int)(N * ROWB), 0x00020000);
+  // tree rows: the separate tree K/V rows 1..N, or (tree_in_cache) cache positions
+  // L .. L + N - 1 of this sequence; L <= capacity - N, so they lie inside the cache
+  const bool tic = a.tree_in_cache != 0;
+  const bool tic_paged = tic && a.paged;
+  __amdgpu_buffer_rsrc_t rk, rv, rkt, rvt;
   if (a.paged) {
     rk = __builtin_amdgcn_make_buffer_rsrc((void*)kc, 0, (int)p.pool_bytes, 0x00020000);
     rv = __builtin_amdgcn_make_buffer_rsrc((void*)vc, 0, (int)p.pool_bytes, 0x00020000);
@@ -196,14 +197,25 @@ __global__ void __launch_bounds__(MF_THREADS, 2) k_attn_mfma(sv_attn_args a, Att
     rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + plane * a.Lcap * D), 0, (int)(a.Lcap * ROWB), 0x00020000);
     rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + plane * a.Lcap * D), 0, (int)(a.Lcap * ROWB), 0x00020000);
   }
+  if (tic_paged) {
+    rkt = rk;  // rows gathered through the block table, lane by lane
+    rvt = rv;
+  } else if (tic) {
+    rkt = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + (plane * a.Lcap + L) * D), 0, (int)(N * ROWB), 0x00020000);
+    rvt = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + (plane * a.Lcap + L) * D), 0, (int)(N * ROWB), 0x00020000);
+  } else {
+    rkt = __builtin_amdgcn_make_buffer_rsrc((void*)(kt + (plane * (N + 1) + 1) * D), 0, (int)(N * ROWB), 0x00020000);
+    rvt = __builtin_amdgcn_make_buffer_rsrc((void*)(vt + (plane * (N + 1) + 1) * D), 0, (int)(N * ROWB), 0x00020000);
+  }
   auto load_tile = [&](int tile, unsigned char* kb) {
     const bool tree = tile >= ntp;
     int klast;
+    int t0 = 0;
     uint32_t soff = 0;
     if (tree) {
-      const int t0 = (tile - ntp) * KT64;
+      t0 = (tile - ntp) * KT64;
       klast = min(KT64, N - t0) - 1;
-      soff = (uint32_t)t0 * ROWB;
+      soff = tic_paged ? 0u : (uint32_t)t0 * ROWB;
     } else {
       const int j0 = k0 + tile * KT64;
       klast = min(KT64, k1 - j0) - 1;
@@ -227,7 +239,16 @@ __global__ void __launch_bounds__(MF_THREADS, 2) k_attn_mfma(sv_attn_args a, Att
       const int r = n * TL::RPI + lane / TL::CPR;        // row this lane fills
       const int c = (lane % TL::CPR) ^ TL::swz(r);       // global chunk stored in its slot
       const int key = min(r, klast);
-      const uint32_t off = (uint32_t)((paged_tile ? (key & 15) : key) * ROWB + c * 16);
+      uint32_t off;
+      if (tree && tic_paged) {
+        // tree node t0 + key sits at logical position L + t0 + key < capacity
+        const int pos = L + t0 + key;
+        int id = a.block_table[(int64_t)b * a.max_blocks + pos / 16];
+        id = (id < 0 || id >= a.num_blocks) ? 0 : id;
+        off = (uint32_t)((((int64_t)id * a.Hkv + g) * 16 + (pos & 15)) * ROWB + c * 16);
+      } else {
+        off = (uint32_t)((paged_tile ? (key & 15) : key) * ROWB + c * 16);
+      }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_void*)(kb + n * 1024), 16, off, soff, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_void*)(kb + TL::TBYTES + n * 1024), 16, off, soff, 0, 0);
     }
@@ -613,8 +634,18 @@ __global__ void __launch_bounds__(256) k_attn_valu(sv_attn_args a, AttnPlan p) {
       const int tt = j - L;
       const uint64_t wv = anc[tt >> 6];
       ok = (wv >> (tt & 63)) & 1ull;
-      off = (((int64_t)b * a.Hkv + g) * (N + 1) + tt + 1) * D;
-      istree = 1;
+      if (a.tree_in_cache) {  // node tt at cache position j = L + tt
+        if (a.paged) {
+          int id2 = a.block_table[(int64_t)b * a.max_blocks + j / a.block_size];
+          if (id2 < 0 || id2 >= a.num_blocks) id2 = 0;
+          off = (((int64_t)id2 * a.Hkv + g) * a.block_size + j % a.block_size) * D;
+        } else {
+          off = (((int64_t)b * a.Hkv + g) * a.Lcap + j) * D;
+        }
+      } else {
+        off = (((int64_t)b * a.Hkv + g) * (N + 1) + tt + 1) * D;
+        istree = 1;
+      }
     }
     koff[t] = off;
     ktree[t] = ok ? istree : -1;
@@ -686,7 +717,8 @@ AttnPlan make_plan(const sv_attn_args& a) {
   p.G = a.Hq / a.Hkv;
   p.M = a.N * p.G;
   p.W = (a.N + 63) / 64;
-  p.cap = a.paged ? a.max_blocks * a.block_size : a.Lcap;
+  // with the tree rows resident in the cache the prefix may fill only capacity - N positions
+  p.cap = (a.paged ? a.max_blocks * a.block_size : a.Lcap) - (a.tree_in_cache ? a.N : 0);
   p.cscale = a.scale * LOG2E;
   p.pool_bytes = a.paged ? (uint32_t)((uint64_t)a.num_blocks * a.Hkv * a.block_size * a.D * 2) : 0u;
   if (!use_mfma(a)) {
@@ -730,6 +762,9 @@ sv_status validate(const sv_attn_args& a) {
   } else if (a.Lcap < 0) {
     return SV_ERR_INVALID_ARGUMENT;
   }
+  if (a.tree_in_cache != 0 && a.tree_in_cache != 1) return SV_ERR_INVALID_ARGUMENT;
+  if (a.tree_in_cache && (int64_t)(a.paged ? (int64_t)a.max_blocks * a.block_size : a.Lcap) < a.N)
+    return SV_ERR_INVALID_ARGUMENT;
   return SV_OK;
 }
 
@@ -746,7 +781,8 @@ extern "C" sv_status sv_tree_attention(const sv_attn_args* args, void* stream) {
   sv_status st = validate(a);
   if (st != SV_OK) return st;
   if (a.B == 0) return SV_OK;
-  if (!a.q || !a.k_cache || !a.v_cache || !a.k_tree || !a.v_tree || !a.prefix_len || !a.anc_bits || !a.out)
+  if (!a.q || !a.k_cache || !a.v_cache || (!a.tree_in_cache && (!a.k_tree || !a.v_tree)) || !a.prefix_len ||
+      !a.anc_bits || !a.out)
     return SV_ERR_INVALID_ARGUMENT;
   if (a.paged && !a.block_table) return SV_ERR_INVALID_ARGUMENT;
   AttnPlan p = make_plan(a);

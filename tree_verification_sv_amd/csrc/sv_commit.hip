@@ -1,96 +1,192 @@
 // KV commit of the accepted branch.  "EAGLE-Pangu: Accelerator-Safe Tree
 // Speculative Decoding on Ascend NPUs", technical summary sec. 2 (branchable
 // KV cache): committed prefix and speculative state are kept apart, and the
-// accepted path's new entries are appended, by length or by path index.
+// accepted path's new entries are committed by length or by path index; the
+// path-index commit avoids memory moves that are not needed.
 //
-// The accepted length never leaves the device: one work-group per sequence
-// reads accept_len / accept_rows / prefix_len, validates every slot first,
-// then copies K and V rows of all KV heads with 16-byte vector moves.
+// The accepted length never leaves the device.  Every kernel below first
+// checks all accepted positions of its sequence (nothing is written for a
+// sequence that fails a check), then moves whole rows with 16-byte vector
+// loads and stores.
+//  k_kv_commit           one work-group per sequence, one layer, tree rows in
+//                        their own tensor: checks, copies every KV head and
+//                        writes new_len / committed_slots / status.
+//  k_kv_commit_rows      one work-group per (sequence, KV head, layer): the
+//                        layer-batched commit and the in-place compaction of
+//                        cache-resident tree rows.  Source rows are staged in
+//                        LDS before any destination row is written, so a path
+//                        in any node order compacts correctly, and rows that
+//                        are already in place are skipped.
+//  k_kv_commit_finalize  one work-group per sequence, launched after
+//                        k_kv_commit_rows: writes new_len / committed_slots /
+//                        status (new_len may alias prefix_len, which every
+//                        k_kv_commit_rows work-group has read by then).
 #include "sv_common.h"
 
 namespace {
 
-__global__ void __launch_bounds__(256) k_kv_commit(sv_commit_args a, int32_t es) {
-  __shared__ int32_t s_code, s_L, s_A;
-  __shared__ int64_t s_slot[SV_MAX_DEPTH];
-  __shared__ int32_t s_src[SV_MAX_DEPTH];
-  const int b = blockIdx.x;
+struct CommitPlan {
+  int32_t es;   // bytes per element
+  int32_t cpr;  // 16-byte chunks per row
+};
+
+// Shared-memory result of the per-sequence checks.
+struct CommitCheck {
+  int32_t code, L, A;
+  int64_t dst[SV_MAX_DEPTH];  // destination slot of accepted position k
+  int64_t src[SV_MAX_DEPTH];  // source: tree row (separate tree rows) or cache slot (tree_in_cache)
+};
+
+__device__ __forceinline__ int64_t capacity(const sv_commit_args& a) {
+  return a.paged ? (int64_t)a.max_blocks * a.block_size : (int64_t)a.Lcap;
+}
+
+// Logical position -> slot of sequence b (checked: 0 ok, else a status code).
+__device__ __forceinline__ int32_t slot_of(const sv_commit_args& a, int b, int64_t pos, int64_t* slot) {
+  if (a.paged) {
+    const int64_t blk = pos / a.block_size;
+    if (blk >= a.max_blocks) return SV_SEQ_CAPACITY;
+    const int32_t id = a.block_table[(int64_t)b * a.max_blocks + blk];
+    if (id < 1 || id >= a.num_blocks) return SV_SEQ_BLOCK;
+    *slot = (int64_t)id * a.block_size + pos % a.block_size;
+  } else {
+    if (pos >= a.Lcap) return SV_SEQ_CAPACITY;
+    *slot = pos;
+  }
+  return 0;
+}
+
+// Checks of one sequence, one thread per accepted position (all loads issued at once):
+// L >= 0 and 0 <= A <= max_depth (1); with cache-resident tree rows L + N within the
+// capacity (6); then per position k in order: source row in [1, N] (1), destination
+// slot (6 capacity, 5 block), cache-resident source slot (5).  The first failing
+// position decides the code, as a walk in position order would.
+__device__ void commit_check(const sv_commit_args& a, int b, CommitCheck& c) {
+  __shared__ int32_t s_code;
   const int t = threadIdx.x;
   const int Dm = a.max_depth;
-  // validation, one thread per accepted position: every load is issued at once (the
-  // block-table entry is the only one that depends on another load)
   if (t == 0) s_code = 0x7fffffff;
   __syncthreads();
   const int32_t L0 = a.prefix_len[b];
   const int32_t A0 = a.accept_len[b];
+  const bool seq_ok = L0 >= 0 && A0 >= 0 && A0 <= Dm;
+  const bool fits = !a.tree_in_cache || (int64_t)L0 + a.N <= capacity(a);
   if (t == 0) {
-    s_L = L0;
-    s_A = A0;
-    if (L0 < 0 || A0 < 0 || A0 > Dm) atomicMin(&s_code, SV_SEQ_PARENT_RANGE);
+    c.L = L0;
+    c.A = A0;
+    if (!seq_ok) s_code = SV_SEQ_PARENT_RANGE;
+    else if (!fits) s_code = SV_SEQ_CAPACITY;
   }
-  if (t < Dm && L0 >= 0 && A0 >= 0 && A0 <= Dm && t < A0) {
+  if (t < Dm && seq_ok && fits && t < A0) {
     const int k = t;
-    int32_t code = 0;
     const int32_t src = a.commit_mode == SV_COMMIT_PATH ? a.accept_rows[(int64_t)b * Dm + k] : k + 1;
-    const int64_t pos = (int64_t)L0 + k;
+    int32_t code = 0;
+    int64_t dslot = 0, sslot = src;
     if (src < 1 || src > a.N) {
       code = SV_SEQ_PARENT_RANGE;
-    } else if (a.paged) {
-      const int64_t blk = pos / a.block_size;
-      if (blk >= a.max_blocks) {
-        code = SV_SEQ_CAPACITY;
-      } else {
-        const int32_t id = a.block_table[(int64_t)b * a.max_blocks + blk];
-        if (id < 1 || id >= a.num_blocks) code = SV_SEQ_BLOCK;
-        else s_slot[k] = (int64_t)id * a.block_size + pos % a.block_size;
-      }
     } else {
-      if (pos >= a.Lcap) code = SV_SEQ_CAPACITY;
-      else s_slot[k] = pos;
+      code = slot_of(a, b, (int64_t)L0 + k, &dslot);
+      if (code == 0 && a.tree_in_cache) code = slot_of(a, b, (int64_t)L0 + src - 1, &sslot);
     }
-    s_src[k] = src;
-    // the first failing position decides the code, as a walk in position order would
+    c.dst[k] = dslot;
+    c.src[k] = sslot;
     if (code != 0) atomicMin(&s_code, (k << 4) | code);
   }
   __syncthreads();
-  if (t == 0) s_code = s_code == 0x7fffffff ? 0 : (s_code & 15);
+  if (t == 0) c.code = s_code == 0x7fffffff ? 0 : (s_code & 15);
   __syncthreads();
-  const int32_t code = s_code, L = s_L, A = s_A;
-  if (t < Dm) a.committed_slots[(int64_t)b * Dm + t] = (code == 0 && t < A) ? (int32_t)s_slot[t] : 0;
-  if (code != 0) {
-    if (t == 0) {
-      a.status[b] = code;
-      a.new_len[b] = L;
-    }
-    return;
+}
+
+// Row index (in rows of D elements) of slot `slot`, KV head h, sequence b, within one layer's cache.
+__device__ __forceinline__ int64_t cache_row(const sv_commit_args& a, int b, int h, int64_t slot) {
+  if (a.paged) {
+    const int64_t id = slot / a.block_size, off = slot % a.block_size;
+    return (id * a.Hkv + h) * a.block_size + off;
   }
-  // copy A rows x Hkv heads x D elements for K and V, 16 bytes per move
-  const int chunks_per_row = (a.D * es) / 16;
-  const int64_t total = (int64_t)A * a.Hkv * chunks_per_row;
-  for (int64_t c = t; c < total; c += blockDim.x) {
-    const int ch = (int)(c % chunks_per_row);
-    const int h = (int)((c / chunks_per_row) % a.Hkv);
-    const int k = (int)(c / ((int64_t)chunks_per_row * a.Hkv));
-    const int64_t src_row = ((int64_t)b * a.Hkv + h) * (a.N + 1) + s_src[k];
-    int64_t dst_row;
-    if (a.paged) {
-      const int64_t id = s_slot[k] / a.block_size, off = s_slot[k] % a.block_size;
-      dst_row = (id * a.Hkv + h) * a.block_size + off;
-    } else {
-      dst_row = ((int64_t)b * a.Hkv + h) * a.Lcap + s_slot[k];
-    }
-    const int64_t row_bytes = (int64_t)a.D * es;
-    const uint4* ks = (const uint4*)((const char*)a.k_tree + src_row * row_bytes) + ch;
-    const uint4* vs = (const uint4*)((const char*)a.v_tree + src_row * row_bytes) + ch;
-    uint4* kd = (uint4*)((char*)a.k_cache + dst_row * row_bytes) + ch;
-    uint4* vd = (uint4*)((char*)a.v_cache + dst_row * row_bytes) + ch;
-    *kd = *ks;
-    *vd = *vs;
-  }
+  return ((int64_t)b * a.Hkv + h) * a.Lcap + slot;
+}
+
+__device__ void write_outputs(const sv_commit_args& a, int b, const CommitCheck& c) {
+  const int t = threadIdx.x;
+  const int Dm = a.max_depth;
+  if (t < Dm) a.committed_slots[(int64_t)b * Dm + t] = (c.code == 0 && t < c.A) ? (int32_t)c.dst[t] : 0;
   if (t == 0) {
-    a.status[b] = 0;
-    a.new_len[b] = L + A;  // prefix_len was read before the barrier, so aliasing is safe
+    a.status[b] = c.code;
+    a.new_len[b] = c.code == 0 ? c.L + c.A : c.L;
   }
+}
+
+__global__ void __launch_bounds__(256) k_kv_commit(sv_commit_args a, CommitPlan p) {
+  __shared__ CommitCheck c;
+  const int b = blockIdx.x;
+  const int t = threadIdx.x;
+  commit_check(a, b, c);
+  const int A = c.A;
+  if (c.code == 0) {
+    // A rows x Hkv heads x D elements for K and V, 16 bytes per move
+    const int64_t total = (int64_t)A * a.Hkv * p.cpr;
+    const int64_t row_bytes = (int64_t)a.D * p.es;
+    for (int64_t x = t; x < total; x += blockDim.x) {
+      const int ch = (int)(x % p.cpr);
+      const int h = (int)((x / p.cpr) % a.Hkv);
+      const int k = (int)(x / ((int64_t)p.cpr * a.Hkv));
+      const int64_t src_row = ((int64_t)b * a.Hkv + h) * (a.N + 1) + c.src[k];
+      const int64_t dst_row = cache_row(a, b, h, c.dst[k]);
+      const uint4* ks = (const uint4*)((const char*)a.k_tree + src_row * row_bytes) + ch;
+      const uint4* vs = (const uint4*)((const char*)a.v_tree + src_row * row_bytes) + ch;
+      uint4* kd = (uint4*)((char*)a.k_cache + dst_row * row_bytes) + ch;
+      uint4* vd = (uint4*)((char*)a.v_cache + dst_row * row_bytes) + ch;
+      *kd = *ks;
+      *vd = *vs;
+    }
+  }
+  // prefix_len was read by commit_check before its barrier, so new_len may alias it
+  write_outputs(a, b, c);
+}
+
+// K and V chunks of up to SV_MAX_DEPTH rows of at most 512 bytes (D 128 fp32)
+constexpr int STAGE_CHUNKS = SV_MAX_DEPTH * 32;
+
+__global__ void __launch_bounds__(256) k_kv_commit_rows(sv_commit_args a, CommitPlan p) {
+  __shared__ CommitCheck c;
+  __shared__ uint4 stage[2 * STAGE_CHUNKS];
+  const int b = blockIdx.x / a.Hkv;
+  const int h = blockIdx.x % a.Hkv;
+  const int layer = blockIdx.y;
+  const int t = threadIdx.x;
+  commit_check(a, b, c);
+  if (c.code != 0) return;
+  const int A = c.A;
+  const int64_t row_bytes = (int64_t)a.D * p.es;
+  char* kc = (char*)a.k_cache + layer * a.cache_layer_stride * p.es;
+  char* vc = (char*)a.v_cache + layer * a.cache_layer_stride * p.es;
+  const char* kt = a.tree_in_cache ? kc : (const char*)a.k_tree + layer * a.tree_layer_stride * p.es;
+  const char* vt = a.tree_in_cache ? vc : (const char*)a.v_tree + layer * a.tree_layer_stride * p.es;
+  const int n = A * p.cpr;
+  // every source row of the path is read before any destination row is written
+  for (int x = t; x < n; x += blockDim.x) {
+    const int k = x / p.cpr, ch = x % p.cpr;
+    if (a.tree_in_cache && c.src[k] == c.dst[k]) continue;  // already in place
+    const int64_t src_row = a.tree_in_cache ? cache_row(a, b, h, c.src[k])
+                                            : ((int64_t)b * a.Hkv + h) * (a.N + 1) + c.src[k];
+    stage[x] = *((const uint4*)(kt + src_row * row_bytes) + ch);
+    stage[STAGE_CHUNKS + x] = *((const uint4*)(vt + src_row * row_bytes) + ch);
+  }
+  __syncthreads();
+  for (int x = t; x < n; x += blockDim.x) {
+    const int k = x / p.cpr, ch = x % p.cpr;
+    if (a.tree_in_cache && c.src[k] == c.dst[k]) continue;
+    const int64_t dst_row = cache_row(a, b, h, c.dst[k]);
+    *((uint4*)(kc + dst_row * row_bytes) + ch) = stage[x];
+    *((uint4*)(vc + dst_row * row_bytes) + ch) = stage[STAGE_CHUNKS + x];
+  }
+}
+
+__global__ void __launch_bounds__(64) k_kv_commit_finalize(sv_commit_args a) {
+  __shared__ CommitCheck c;
+  const int b = blockIdx.x;
+  commit_check(a, b, c);
+  write_outputs(a, b, c);
 }
 
 }  // namespace
@@ -103,9 +199,14 @@ extern "C" sv_status sv_kv_commit(const sv_commit_args* args, void* stream) {
   if (a.D != 64 && a.D != 128) return SV_ERR_UNSUPPORTED;
   if (a.dtype != SV_F32 && a.dtype != SV_BF16) return SV_ERR_UNSUPPORTED;
   if (a.commit_mode != SV_COMMIT_PATH && a.commit_mode != SV_COMMIT_LENGTH) return SV_ERR_INVALID_ARGUMENT;
+  if (a.tree_in_cache != 0 && a.tree_in_cache != 1) return SV_ERR_INVALID_ARGUMENT;
+  if (a.num_layers < 0 || a.num_layers > 65535) return SV_ERR_INVALID_ARGUMENT;
+  const int layers = a.num_layers == 0 ? 1 : a.num_layers;
+  if (layers > 1 && (a.cache_layer_stride <= 0 || (!a.tree_in_cache && a.tree_layer_stride <= 0)))
+    return SV_ERR_INVALID_ARGUMENT;
   if (a.B == 0) return SV_OK;
-  if (!a.k_cache || !a.v_cache || !a.k_tree || !a.v_tree || !a.prefix_len || !a.accept_len || !a.new_len ||
-      !a.committed_slots || !a.status)
+  if (!a.k_cache || !a.v_cache || (!a.tree_in_cache && (!a.k_tree || !a.v_tree)) || !a.prefix_len ||
+      !a.accept_len || !a.new_len || !a.committed_slots || !a.status)
     return SV_ERR_INVALID_ARGUMENT;
   if (a.commit_mode == SV_COMMIT_PATH && !a.accept_rows) return SV_ERR_INVALID_ARGUMENT;
   if (a.paged) {
@@ -113,7 +214,17 @@ extern "C" sv_status sv_kv_commit(const sv_commit_args* args, void* stream) {
   } else if (a.Lcap < 1) {
     return SV_ERR_INVALID_ARGUMENT;
   }
-  const int es = a.dtype == SV_F32 ? 4 : 2;
-  hipLaunchKernelGGL(k_kv_commit, dim3(a.B), dim3(256), 0, (hipStream_t)stream, a, es);
+  CommitPlan p;
+  p.es = a.dtype == SV_F32 ? 4 : 2;
+  p.cpr = a.D * p.es / 16;
+  hipStream_t s = (hipStream_t)stream;
+  if (layers == 1 && !a.tree_in_cache) {
+    hipLaunchKernelGGL(k_kv_commit, dim3(a.B), dim3(256), 0, s, a, p);
+  } else {
+    const int64_t groups = (int64_t)a.B * a.Hkv;
+    if (groups > 0x7fffffff) return SV_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(k_kv_commit_rows, dim3((unsigned)groups, (unsigned)layers), dim3(256), 0, s, a, p);
+    hipLaunchKernelGGL(k_kv_commit_finalize, dim3(a.B), dim3(64), 0, s, a);
+  }
   return sv_launch_status();
 }

@@ -49,6 +49,7 @@ class StepInputs:
     num_blocks: int = 0
     scale: Optional[float] = None
     commit_mode: int = SV_COMMIT_PATH
+    tree_in_cache: bool = False  # tree K/V rows are cache positions prefix_len + t (k_tree / v_tree unused)
 
 
 class VerifyStep:
@@ -72,7 +73,8 @@ class VerifyStep:
                            status=torch.empty(B, dtype=torch.int32, device=dev))
         # argument blocks are built once; pointers stay valid for the tensors' lifetime
         self._attn = attn_args(x.q, x.k_cache, x.v_cache, x.k_tree, x.v_tree, self.mask["anc_bits"], x.prefix_len,
-                               self.out, x.block_table, x.scale, x.paged, x.num_blocks, self.attn_status)
+                               self.out, x.block_table, x.scale, x.paged, x.num_blocks, self.attn_status,
+                               x.tree_in_cache)
         need = sv_tree_attention_workspace(self._attn)
         self.attn_ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         self._attn.workspace = self.attn_ws.data_ptr() if need else None
@@ -85,7 +87,8 @@ class VerifyStep:
         self._acc.workspace_bytes = need
         self._com = commit_args(x.k_cache, x.v_cache, x.k_tree, x.v_tree, x.prefix_len, self.acc["accept_len"],
                                 self.acc["accept_rows"], Dm, self.commit["new_len"], self.commit["committed_slots"],
-                                self.commit["status"], x.block_table, x.paged, x.num_blocks, x.commit_mode)
+                                self.commit["status"], x.block_table, x.paged, x.num_blocks, x.commit_mode,
+                                x.tree_in_cache, N)
         self._L = lib()
         self._side = None
         self._ev_fork = self._ev_join = None
@@ -127,13 +130,20 @@ class VerifyStep:
         self.build_mask(main)
         self._ev_fork.record(main)
         side.wait_event(self._ev_fork)
+        # with the tree rows in the cache the commit moves rows the attention reads,
+        # so it follows the join instead of running beside the attention
+        late_commit = self.x.tree_in_cache
         if accept_first:
             self.accept(side)
-            self.kv_commit(side)
+            if not late_commit:
+                self.kv_commit(side)
             self.attention(main)
         else:
             self.attention(main)
             self.accept(side)
-            self.kv_commit(side)
+            if not late_commit:
+                self.kv_commit(side)
         self._ev_join.record(side)
         main.wait_event(self._ev_join)
+        if late_commit:
+            self.kv_commit(main)

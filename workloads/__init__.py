@@ -26,6 +26,7 @@ _lib = None
 # stream ids: one per tensor role
 S_TREE, S_TOKENS, S_Q, S_KC, S_VC, S_KT, S_VT = 1, 2, 3, 4, 5, 6, 7
 S_TGT, S_DRF, S_PERT, S_UACC, S_USMP, S_PLEN, S_PERM, S_PLANT = 8, 9, 10, 11, 12, 13, 14, 15
+S_KC2, S_VC2 = 16, 17  # cache positions added when the tree rows move into the cache
 
 VOCAB_LLAMA3 = 128256
 
@@ -305,6 +306,7 @@ class Workload:
     u_sample: Optional[np.ndarray]
     scale: float = 0.0
     seed: int = 0
+    tree_in_cache: bool = False  # tree K/V rows stored in the cache at positions prefix_len + t
 
     def __post_init__(self):
         if not self.scale:
@@ -531,6 +533,60 @@ def config(cfg: int, seed: Optional[int] = None, **ov) -> Workload:
     raise ValueError(cfg)
 
 
+def with_tree_in_cache(w: Workload) -> Workload:
+    """The same workload with the tree tokens' K/V stored inside the cache.
+
+    Node t's K/V row (tree row t+1) is written to cache position prefix_len[b] + t
+    of its sequence; the caches grow so that every sequence holds prefix_len + N
+    positions (contiguous: a larger Lcap; paged: extra blocks appended to the pool
+    and to the sequence's block table).  New cache positions outside the tree rows
+    get seeded normals.  k_tree / v_tree become None.  Data placement only.
+    """
+    import dataclasses
+    L = w.prefix_len.astype(np.int64)
+    if not w.paged:
+        Lcap = int(((int(L.max()) + w.N + 15) // 16) * 16)
+        Lcap = max(Lcap, w.Lcap)
+        shape = (w.B, w.Hkv, Lcap, w.D)
+        kc = normal(w.seed, S_KC2, shape, w.dtype)
+        vc = normal(w.seed, S_VC2, shape, w.dtype)
+        kc[:, :, :w.Lcap] = w.k_cache
+        vc[:, :, :w.Lcap] = w.v_cache
+        for b in range(w.B):
+            kc[b, :, L[b]:L[b] + w.N] = w.k_tree[b, :, 1:]
+            vc[b, :, L[b]:L[b] + w.N] = w.v_tree[b, :, 1:]
+        return dataclasses.replace(w, Lcap=Lcap, k_cache=kc, v_cache=vc, k_tree=None, v_tree=None,
+                                   tree_in_cache=True)
+    bs = w.block_size
+    have = (w.block_table > 0).sum(axis=1)
+    need = np.maximum((L + w.N + bs - 1) // bs, have)
+    extra = int((need - have).sum())
+    num_blocks = w.num_blocks + extra
+    max_blocks = max(int(need.max()), w.max_blocks)
+    bt = np.zeros((w.B, max_blocks), dtype=np.int32)
+    bt[:, :w.max_blocks] = w.block_table
+    nxt = w.num_blocks
+    for b in range(w.B):
+        for k in range(int(have[b]), int(need[b])):
+            bt[b, k] = nxt
+            nxt += 1
+    shape = (num_blocks, w.Hkv, bs, w.D)
+    kc = normal(w.seed, S_KC2, shape, w.dtype)
+    vc = normal(w.seed, S_VC2, shape, w.dtype)
+    kc[:w.num_blocks] = w.k_cache
+    vc[:w.num_blocks] = w.v_cache
+    kc[0] = 0
+    vc[0] = 0
+    for b in range(w.B):
+        for t in range(w.N):
+            pos = int(L[b]) + t
+            blk = int(bt[b, pos // bs])
+            kc[blk, :, pos % bs] = w.k_tree[b, :, t + 1]
+            vc[blk, :, pos % bs] = w.v_tree[b, :, t + 1]
+    return dataclasses.replace(w, num_blocks=num_blocks, max_blocks=max_blocks, block_table=bt, k_cache=kc,
+                               v_cache=vc, k_tree=None, v_tree=None, tree_in_cache=True)
+
+
 # ------------------------------------------------- host -> device transfer
 def to_device(w: Workload, device="cuda:0"):
     """Copy a workload's arrays to device tensors (bf16 bit patterns become torch.bfloat16)."""
@@ -560,4 +616,4 @@ def step_inputs(w: Workload, dev: dict):
                       prefix_len=dev["prefix_len"], target_logits=dev["target_logits"], max_depth=w.max_depth,
                       mode=w.mode, temperature=w.temperature, draft_logits=dev["draft_logits"],
                       u_accept=dev["u_accept"], u_sample=dev["u_sample"], block_table=dev["block_table"],
-                      paged=w.paged, num_blocks=w.num_blocks, scale=w.scale)
+                      paged=w.paged, num_blocks=w.num_blocks, scale=w.scale, tree_in_cache=w.tree_in_cache)
