@@ -52,7 +52,7 @@ class _AcceptArgs(ctypes.Structure):
                 ("draft_logits", ctypes.c_void_p), ("u_accept", ctypes.c_void_p), ("u_sample", ctypes.c_void_p),
                 ("accept_len", ctypes.c_void_p), ("accept_rows", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p),
                 ("num_out", ctypes.c_void_p), ("stop_row", ctypes.c_void_p), ("status", ctypes.c_void_p),
-                ("flagged", ctypes.c_void_p)]
+                ("flagged", ctypes.c_void_p), ("threshold", ctypes.c_double)]
 
 
 class _CommitArgs(ctypes.Structure):
@@ -148,7 +148,7 @@ def tree_attention(w, sel: Optional[np.ndarray] = None, parents: Optional[np.nda
 
 
 def accept(w, mode: Optional[str] = None, temperature: Optional[float] = None, tokens=None, parents=None,
-           target=None, draft=None, u_accept=None, u_sample=None) -> dict:
+           target=None, draft=None, u_accept=None, u_sample=None, threshold: Optional[float] = None) -> dict:
     mode = w.mode if mode is None else mode
     T = w.temperature if temperature is None else temperature
     parents = np.ascontiguousarray(w.parents if parents is None else parents, dtype=np.int32)
@@ -167,10 +167,11 @@ def accept(w, mode: Optional[str] = None, temperature: Optional[float] = None, t
     a = _AcceptArgs()
     a.B, a.N, a.V, a.max_depth = B, N, V, Dm
     a.logits_dtype = _dt(target)
-    a.mode = {"greedy": 0, "stochastic": 1, "topk": 2}[mode]
+    a.mode = {"greedy": 0, "stochastic": 1, "topk": 2, "threshold": 3}[mode]
     a.temperature = float(T)
+    a.threshold = float(getattr(w, "threshold", 0.0) if threshold is None else threshold)
     a.parents, a.tokens, a.target_logits = _p(parents), _p(tokens), _p(target)
-    if a.mode != 0:
+    if a.mode in (1, 2):
         ua = np.ascontiguousarray(ua, dtype=np.float32)
         us = np.ascontiguousarray(us, dtype=np.float32)
         a.draft_logits = _p(draft) if a.mode == 1 else None

@@ -208,7 +208,8 @@ static void softmax_row(const void* logits, int dtype, int64_t row_off, int32_t 
 
 int orc_accept(const orc_accept_args* a) {
   const int32_t B = a->B, N = a->N, V = a->V, Dm = a->max_depth;
-  if (B < 0 || N < 1 || V < 1 || Dm < 1 || Dm > 64 || a->mode < 0 || a->mode > 2) return -1;
+  if (B < 0 || N < 1 || V < 1 || Dm < 1 || Dm > 64 || a->mode < 0 || a->mode > 3) return -1;
+  if (a->mode == 3 && !(a->threshold >= 0.0 && a->threshold <= 1.0)) return -1;
   if (a->mode != 0 && !(a->temperature > 0.0)) return -1;
   const double EPS = 1e-6;
   int32_t* valid = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
@@ -265,6 +266,49 @@ int orc_accept(const orc_accept_args* a) {
         walk_to_root(par, N, Dm, stop_node, acc_path, &len);
       }
       bonus = amax[stop_node + 1];
+    } else if (a->mode == 3) {
+      /* threshold: p of each usable child's token under its parent row's softmax(l/T) */
+      const double T = a->temperature, tau = a->threshold;
+      double* pchild = (double*)malloc(sizeof(double) * (size_t)N);
+      for (int32_t r = 0; r <= N; ++r) {
+        int32_t has = 0;
+        for (int32_t c = 0; c < N; ++c) has |= usable[c] && par[c] + 1 == r;
+        if (!has) continue;
+        softmax_row(a->target_logits, a->logits_dtype, ((int64_t)b * (N + 1) + r) * V, V, T, pcur);
+        for (int32_t c = 0; c < N; ++c)
+          if (usable[c] && par[c] + 1 == r) pchild[c] = pcur[tok[c]];
+      }
+      /* a prefix is accepted when each of its own prefixes scores at least the threshold */
+      for (int32_t i = 0; i < N; ++i) {
+        if (!usable[i]) continue;
+        int32_t len = 0;
+        walk_to_root(par, N, Dm, i, path, &len);
+        int ok = 1;
+        double score = 1.0;
+        for (int32_t k = 0; k < len && ok; ++k) {
+          const int32_t t = path[k];
+          if (!usable[t]) { ok = 0; break; }
+          score *= pchild[t];
+          if (fabs(score - tau) <= 1e-5 * tau) flagged = 1;
+          if (score < tau) ok = 0;
+        }
+        if (ok && len > A) {
+          A = len;
+          stop_node = i;
+        }
+      }
+      if (stop_node >= 0) {
+        int32_t len = 0;
+        walk_to_root(par, N, Dm, stop_node, acc_path, &len);
+      }
+      free(pchild);
+      /* bonus: the target's own choice after the accepted prefix, argmax of the stop row */
+      const int64_t off = ((int64_t)b * (N + 1) + (stop_node + 1)) * V;
+      double best = -INFINITY;
+      for (int32_t v = 0; v < V; ++v) {
+        double l = load_elem(a->target_logits, a->logits_dtype, off + v);
+        if (l > best) { best = l; bonus = v; }
+      }
     } else {
       /* stochastic: multi-round rejection walk from the root row.  q is the draft
          distribution of the current row (mode 1) or the point mass at the tested

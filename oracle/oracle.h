@@ -84,7 +84,7 @@ int orc_tree_attention(const orc_attn_args* a);
  * num_out [B], stop_row [B], status [B], flagged [B] (stochastic: a draw was
  * within 1e-6 of its threshold). */
 typedef struct {
-  int32_t B, N, V, max_depth, logits_dtype, mode;
+  int32_t B, N, V, max_depth, logits_dtype, mode;  /* mode 3: threshold acceptance, see below */
   double temperature;
   const int32_t* parents;
   const int32_t* tokens;
@@ -93,6 +93,15 @@ typedef struct {
   const float* u_accept;
   const float* u_sample;
   int32_t *accept_len, *accept_rows, *out_tokens, *num_out, *stop_row, *status, *flagged;
+  /* mode 3, threshold acceptance ([PX] "Decodificacion Especulativa": every
+   * prefix of the candidates gets a probability and the longest one above an
+   * acceptance threshold is kept; the target adds one token): the score of node
+   * i is the product over its root path of p_{parent row}(token), p =
+   * softmax(target row / T); a node is accepted when every node of its path is
+   * usable and scores >= threshold; stop at the deepest accepted node (lowest
+   * index on ties); bonus = argmax of the stop row (lowest id on ties).
+   * flagged: some path score lies within a relative 1e-5 of the threshold. */
+  double threshold;
 } orc_accept_args;
 int orc_accept(const orc_accept_args* a);
 
