@@ -74,6 +74,7 @@ typedef int32_t sv_status;
 #define SV_GREEDY 0
 #define SV_STOCHASTIC 1
 #define SV_TOPK_DRAFT 2
+#define SV_THRESHOLD 3
 
 /* commit modes ([EP] sec. 2: length-based or path-index-based commit) */
 #define SV_COMMIT_PATH 0
@@ -203,6 +204,16 @@ sv_status sv_tree_attention(const sv_attn_args* args, void* stream);
  *   with no second pass over the row; the bonus is drawn from p_r with the
  *   rejected tokens removed, as in mode 1 (if rounding leaves that residual
  *   without mass, from p_r itself).
+ * Threshold (mode 3, [PX] "Decodificacion Especulativa": every prefix of the
+ *   candidates is scored with a probability and the longest one above an
+ *   acceptance threshold is kept, plus one target token): the score of node i
+ *   is the product over its root path of p_{parent row}(token), p_r =
+ *   softmax(target row r / T) (fp32 exponentials, fp64 sums and products);
+ *   node i is accepted when every node of its path is usable and its score is
+ *   >= threshold (0 <= threshold <= 1, else SV_ERR_INVALID_ARGUMENT); the stop
+ *   node is the deepest accepted node (lowest index on ties), or the root; the
+ *   bonus is the argmax of the stop row (lowest id on ties).  draft_logits,
+ *   u_accept and u_sample are not read (may be NULL).
  * Outputs (device, int32): accept_len [B] (A), accept_rows [B, max_depth]
  *   (rows of the accepted path, root-most first, ghost-0 padded), out_tokens
  *   [B, max_depth+1] (accepted tokens then the bonus, 0 padded), num_out [B]
@@ -234,6 +245,7 @@ typedef struct sv_accept_args {
   int32_t* status;
   void* workspace;
   size_t workspace_bytes;
+  float threshold;  /* mode 3 only */
 } sv_accept_args;
 size_t sv_accept_workspace(const sv_accept_args* args);
 sv_status sv_accept(const sv_accept_args* args, void* stream);

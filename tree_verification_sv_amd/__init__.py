@@ -20,13 +20,13 @@ _lib = None
 
 SV_OK, SV_ERR_INVALID_ARGUMENT, SV_ERR_UNSUPPORTED, SV_ERR_HIP = 0, 1, 2, 4
 SV_F32, SV_BF16 = 0, 1
-SV_GREEDY, SV_STOCHASTIC, SV_TOPK_DRAFT = 0, 1, 2
-_MODES = {"greedy": SV_GREEDY, "stochastic": SV_STOCHASTIC, "topk": SV_TOPK_DRAFT}
+SV_GREEDY, SV_STOCHASTIC, SV_TOPK_DRAFT, SV_THRESHOLD = 0, 1, 2, 3
+_MODES = {"greedy": SV_GREEDY, "stochastic": SV_STOCHASTIC, "topk": SV_TOPK_DRAFT, "threshold": SV_THRESHOLD}
 SV_COMMIT_PATH, SV_COMMIT_LENGTH = 0, 1
 
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-SOURCES = ["sv_api.hip", "sv_mask.hip", "sv_attention.hip", "sv_accept.hip", "sv_commit.hip"]
+SOURCES = ["sv_api.hip", "sv_mask.hip", "sv_attention.hip", "sv_accept.hip", "sv_threshold.hip", "sv_commit.hip"]
 
 
 class SpecVerifyError(RuntimeError):
@@ -68,7 +68,7 @@ class sv_accept_args(ctypes.Structure):
                 ("u_accept", ctypes.c_void_p), ("u_sample", ctypes.c_void_p), ("accept_len", ctypes.c_void_p),
                 ("accept_rows", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p), ("num_out", ctypes.c_void_p),
                 ("stop_row", ctypes.c_void_p), ("status", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("threshold", ctypes.c_float)]
 
 
 class sv_commit_args(ctypes.Structure):
@@ -245,7 +245,7 @@ def sv_tree_attention(q, k_cache, v_cache, k_tree, v_tree, anc_bits, prefix_len,
 
 
 def accept_args(parents, tokens, anc_bits, depth, target_logits, max_depth, mode, draft_logits=None,
-                u_accept=None, u_sample=None, temperature=1.0, outs=None) -> sv_accept_args:
+                u_accept=None, u_sample=None, temperature=1.0, outs=None, threshold=0.0) -> sv_accept_args:
     torch = _torch()
     B, N = parents.shape
     V = target_logits.shape[-1]
@@ -258,6 +258,7 @@ def accept_args(parents, tokens, anc_bits, depth, target_logits, max_depth, mode
         raise SpecVerifyError(f"unknown acceptance mode {mode!r}")
     a.mode = mode
     a.temperature = float(temperature)
+    a.threshold = float(threshold)
     a.parents, a.tokens = _ptr(parents, torch.int32, "parents"), _ptr(tokens, torch.int32, "tokens")
     a.anc_bits, a.depth = _ptr(anc_bits, torch.int64, "anc_bits"), _ptr(depth, torch.int32, "depth")
     a.target_logits = _ptr(target_logits, name="target_logits")
@@ -265,7 +266,7 @@ def accept_args(parents, tokens, anc_bits, depth, target_logits, max_depth, mode
         if draft_logits.dtype != target_logits.dtype:
             raise SpecVerifyError("draft and target logits must share a dtype")
         a.draft_logits = _ptr(draft_logits, name="draft_logits")
-    if a.mode != SV_GREEDY:
+    if a.mode in (SV_STOCHASTIC, SV_TOPK_DRAFT):
         a.u_accept = _ptr(u_accept, torch.float32, "u_accept")
         a.u_sample = _ptr(u_sample, torch.float32, "u_sample")
     for k in ("accept_len", "accept_rows", "out_tokens", "num_out", "stop_row", "status"):
@@ -288,13 +289,14 @@ def sv_accept_workspace(args: sv_accept_args) -> int:
 
 
 def sv_accept(parents, tokens, anc_bits, depth, target_logits, max_depth, mode="greedy", draft_logits=None,
-              u_accept=None, u_sample=None, temperature=1.0, outs=None, workspace=None, stream=None) -> dict:
+              u_accept=None, u_sample=None, temperature=1.0, outs=None, workspace=None, stream=None,
+              threshold=0.0) -> dict:
     """Speculative acceptance + bonus token; returns the dict of int32 device outputs."""
     B = parents.shape[0]
     if outs is None:
         outs = accept_outputs(B, max_depth, parents.device)
     a = accept_args(parents, tokens, anc_bits, depth, target_logits, max_depth, mode, draft_logits, u_accept,
-                    u_sample, temperature, outs)
+                    u_sample, temperature, outs, threshold)
     need = sv_accept_workspace(a)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = _alloc_workspace(need, parents.device)

@@ -1118,6 +1118,7 @@ WsLayout ws_layout(const sv_accept_args& a) {
 
 extern "C" size_t sv_accept_workspace(const sv_accept_args* args) {
   if (!args || args->B < 1 || args->N < 1 || args->V < 1) return 0;
+  if (args->mode == SV_THRESHOLD) return sv_threshold_workspace(*args);
   return ws_layout(*args).total;
 }
 
@@ -1126,12 +1127,19 @@ extern "C" sv_status sv_accept(const sv_accept_args* args, void* stream) {
   const sv_accept_args& a = *args;
   if (a.B < 0 || a.N < 1 || a.N > SV_MAX_N || a.V < 1 || a.max_depth < 1 || a.max_depth > SV_MAX_DEPTH)
     return SV_ERR_INVALID_ARGUMENT;
-  if (a.mode != SV_GREEDY && a.mode != SV_STOCHASTIC && a.mode != SV_TOPK_DRAFT) return SV_ERR_INVALID_ARGUMENT;
+  if (a.mode != SV_GREEDY && a.mode != SV_STOCHASTIC && a.mode != SV_TOPK_DRAFT && a.mode != SV_THRESHOLD)
+    return SV_ERR_INVALID_ARGUMENT;
   if (a.logits_dtype != SV_F32 && a.logits_dtype != SV_BF16) return SV_ERR_UNSUPPORTED;
+  if (a.mode == SV_THRESHOLD && (!(a.temperature > 0.f) || !(a.threshold >= 0.f && a.threshold <= 1.f)))
+    return SV_ERR_INVALID_ARGUMENT;
   if (a.B == 0) return SV_OK;
   if (!a.parents || !a.tokens || !a.anc_bits || !a.depth || !a.target_logits || !a.accept_len || !a.accept_rows ||
       !a.out_tokens || !a.num_out || !a.stop_row || !a.status || !a.workspace)
     return SV_ERR_INVALID_ARGUMENT;
+  if (a.mode == SV_THRESHOLD) {
+    if ((uintptr_t)a.workspace % 256) return SV_ERR_INVALID_ARGUMENT;
+    return sv_threshold_launch(a, (hipStream_t)stream);
+  }
   if (a.mode == SV_STOCHASTIC && !a.draft_logits) return SV_ERR_INVALID_ARGUMENT;
   if (a.mode != SV_GREEDY && (!a.u_accept || !a.u_sample || !(a.temperature > 0.f))) return SV_ERR_INVALID_ARGUMENT;
   const WsLayout l = ws_layout(a);

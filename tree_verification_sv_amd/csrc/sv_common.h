@@ -43,3 +43,7 @@ __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_wave_barrier();
 }
+
+// Threshold acceptance (sv_threshold.hip): workspace bytes and launch of both kernels.
+size_t sv_threshold_workspace(const sv_accept_args& a);
+sv_status sv_threshold_launch(const sv_accept_args& a, hipStream_t stream);

@@ -50,6 +50,7 @@ class StepInputs:
     scale: Optional[float] = None
     commit_mode: int = SV_COMMIT_PATH
     tree_in_cache: bool = False  # tree K/V rows are cache positions prefix_len + t (k_tree / v_tree unused)
+    threshold: float = 0.0       # acceptance threshold of mode "threshold"
 
 
 class VerifyStep:
@@ -80,7 +81,8 @@ class VerifyStep:
         self._attn.workspace = self.attn_ws.data_ptr() if need else None
         self._attn.workspace_bytes = need
         self._acc = accept_args(x.parents, x.tokens, self.mask["anc_bits"], self.mask["depth"], x.target_logits, Dm,
-                                x.mode, x.draft_logits, x.u_accept, x.u_sample, x.temperature, self.acc)
+                                x.mode, x.draft_logits, x.u_accept, x.u_sample, x.temperature, self.acc,
+                                x.threshold)
         need = sv_accept_workspace(self._acc)
         self.acc_ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)  # counters start at zero
         self._acc.workspace = self.acc_ws.data_ptr()
