@@ -51,7 +51,12 @@ def algorithmic_bytes(w, acc):
         stop = int(acc["stop_row"][b])
         rows += len(needed) * n_t + (0 if stop in needed else 1)
     accept = rows * V * el
-    commit = int(acc["accept_len"].sum()) * Hkv * D * 2 * e * 2
+    A = acc["accept_len"].astype(np.int64)
+    if w.tree_in_cache:  # the in-place commit moves only rows not already at their position
+        moved = sum(int((acc["accept_rows"][b, :A[b]] - 1 != np.arange(A[b])).sum()) for b in range(B))
+    else:
+        moved = int(A.sum())
+    commit = moved * Hkv * D * 2 * e * 2
     mask = 4 * B * N + B * N * (8 * W + 4 + 4 * w.max_depth)
     return dict(mask=mask, attention=attn, accept=accept, commit=commit,
                 total=mask + attn + accept + commit)
@@ -79,7 +84,7 @@ def load_traffic(kernel, kernel_src_hash, workload):
     return d.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, budget_s=10.0, max_steps=8):
+def cpu_baseline(cfg, budget_s=10.0, max_steps=8, variant=None):
     """The CPU oracle as it stands, one host thread, on whole steps of the same workload.
 
     Steps on independently seeded instances run until about ``budget_s`` seconds
@@ -90,6 +95,8 @@ def cpu_baseline(cfg, budget_s=10.0, max_steps=8):
     dt, steps, tokens = 0.0, 0, 0
     while steps < max_steps and (dt < budget_s or steps == 0):
         w = W.config(cfg, seed=cfg * 1000 + steps)
+        if variant is not None:
+            w = variant(w)
         t0 = time.perf_counter()
         oracle.build_tree_mask(w.parents, w.max_depth)
         oracle.tree_attention(w)
@@ -105,6 +112,49 @@ def cpu_baseline(cfg, budget_s=10.0, max_steps=8):
                        f"{w.mode} acceptance, commit; {dt:.1f} s on one host thread")
 
 
+def commit_layers(w, dev, acc, layers, K):
+    """Time one sv_kv_commit over `layers` layers of the workload's cache shape (HIP events).
+
+    Every layer shares the workload's tree, lengths, accepted rows and block table; the
+    caches of the extra layers are plain device allocations (their contents do not change
+    the work).  Replays are idempotent only in bytes moved, which is what is timed."""
+    import torch
+    import tree_verification_sv_amd as sv
+    kc = dev["k_cache"].unsqueeze(0).repeat(layers, *([1] * dev["k_cache"].dim()))
+    vc = dev["v_cache"].unsqueeze(0).repeat(layers, *([1] * dev["v_cache"].dim()))
+    tic = w.tree_in_cache
+    kt = None if tic else dev["k_tree"].unsqueeze(0).repeat(layers, *([1] * dev["k_tree"].dim()))
+    vt = None if tic else dev["v_tree"].unsqueeze(0).repeat(layers, *([1] * dev["v_tree"].dim()))
+    alen = torch.from_numpy(acc["accept_len"]).to(kc.device)
+    arows = torch.from_numpy(np.ascontiguousarray(acc["accept_rows"])).to(kc.device)
+    outs = dict(new_len=torch.empty(w.B, dtype=torch.int32, device=kc.device),
+                committed_slots=torch.empty((w.B, w.max_depth), dtype=torch.int32, device=kc.device),
+                status=torch.empty(w.B, dtype=torch.int32, device=kc.device))
+    run = lambda: sv.sv_kv_commit(kc, vc, kt, vt, dev["prefix_len"], alen, arows, w.max_depth,  # noqa: E731
+                                  block_table=dev["block_table"], paged=w.paged, num_blocks=w.num_blocks,
+                                  outs=outs, tree_in_cache=tic, N=w.N, num_layers=layers)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(K):
+        run()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / K
+    e = 2 if w.dtype == "bf16" else 4
+    A = acc["accept_len"].astype(np.int64)
+    if tic:  # rows already in place are not moved
+        moved = sum(int((acc["accept_rows"][bb, :A[bb]] - 1 != np.arange(A[bb])).sum()) for bb in range(w.B))
+    else:
+        moved = int(A.sum())
+    byts = layers * moved * w.Hkv * w.D * e * 2 * 2  # K and V rows, read + write
+    return dict(layers=layers, ms=round(ms, 5), rows_moved_per_layer=moved, bytes=byts,
+                gbs=round(byts / (ms * 1e-3) / 1e9, 1), tree_kv="in cache" if tic else "separate rows")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +167,14 @@ def main():
                     help="run the four stages back to back on one stream (default: acceptance and commit on a "
                          "side stream beside the attention, forked after the mask)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--acceptance", choices=["greedy", "stochastic", "topk", "threshold"], default=None,
+                    help="acceptance rule (default: the workload's own)")
+    ap.add_argument("--threshold", type=float, default=1e-4, help="score threshold of --acceptance threshold")
+    ap.add_argument("--tree-in-cache", action="store_true",
+                    help="keep the tree tokens' K/V in the cache at positions prefix_len + t (attention reads them "
+                         "there, the commit compacts the accepted path in place after the attention)")
+    ap.add_argument("--commit-layers", type=int, default=0,
+                    help="also time one layer-batched sv_kv_commit over this many layers of the workload's shape")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (reference kernel for PMC byte counters)")
     args = ap.parse_args()
@@ -138,6 +196,14 @@ def main():
     print(f"[bench] workload {w0.name} B={w0.B} N={w0.N} L={int(w0.prefix_len.max())} V={w0.V} "
           f"instances={R} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
     ws = [w0] + [W.config(args.config, seed=args.config * 1000 + r) for r in range(1, R)]
+    def variant(w):
+        if args.acceptance:
+            w.mode = args.acceptance
+            w.threshold = float(np.float32(args.threshold))
+        return W.with_tree_in_cache(w) if args.tree_in_cache else w
+
+    ws = [variant(w) for w in ws]
+    w0 = ws[0]
     devs = [W.to_device(w, dev) for w in ws]
     steps = [VerifyStep(W.step_inputs(w, d)) for w, d in zip(ws, devs)]
     stream = torch.cuda.current_stream()
@@ -211,6 +277,8 @@ def main():
         torch.cuda.synchronize()
         stage_ms[name] = a.elapsed_time(b) / K
 
+    layered = commit_layers(ws[0], devs[0], accs[0], args.commit_layers, K) if args.commit_layers else None
+
     mean_bytes = {k: float(np.mean([bb[k] for bb in byts])) for k in byts[0]}
     B, N = w0.B, w0.N
     value = B * N / (ms_step * 1e-3)
@@ -238,8 +306,11 @@ def main():
         "config": {"workload": w0.name, "batch": B, "tree_nodes": N, "prefix_len": int(w0.prefix_len.max()),
                    "q_heads": w0.Hq, "kv_heads": w0.Hkv, "head_dim": w0.D, "vocab": w0.V, "max_depth": w0.max_depth,
                    "acceptance": w0.mode, "temperature": w0.temperature, "instances_cycled": R,
+                   **({"threshold": w0.threshold} if w0.mode == "threshold" else {}),
                    "launch": "hip_graph" if use_graph else "eager",
-                   "streams": "attention | accept+commit after mask" if ov else "one"},
+                   "streams": ("attention | accept after mask, commit after both" if w0.tree_in_cache else
+                               "attention | accept+commit after mask") if ov else "one",
+                   "tree_kv": "in cache at prefix_len + t" if w0.tree_in_cache else "separate rows"},
         "accept_steps_per_s": round(B / (ms_step * 1e-3), 1),
         "hbm_gbs": round(hbm_gbs, 1),
         "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
@@ -251,9 +322,11 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "wall_s_timed": round(wall, 3),
     }
+    if layered is not None:
+        result["layered_commit"] = layered
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on one step", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(args.config)
+        result["cpu_baseline"] = cpu_baseline(args.config, variant=variant)
     print(json.dumps(result), flush=True)
 
 

@@ -307,6 +307,7 @@ class Workload:
     scale: float = 0.0
     seed: int = 0
     tree_in_cache: bool = False  # tree K/V rows stored in the cache at positions prefix_len + t
+    threshold: float = 0.0       # acceptance threshold when mode == 'threshold'
 
     def __post_init__(self):
         if not self.scale:
@@ -616,4 +617,5 @@ def step_inputs(w: Workload, dev: dict):
                       prefix_len=dev["prefix_len"], target_logits=dev["target_logits"], max_depth=w.max_depth,
                       mode=w.mode, temperature=w.temperature, draft_logits=dev["draft_logits"],
                       u_accept=dev["u_accept"], u_sample=dev["u_sample"], block_table=dev["block_table"],
-                      paged=w.paged, num_blocks=w.num_blocks, scale=w.scale, tree_in_cache=w.tree_in_cache)
+                      paged=w.paged, num_blocks=w.num_blocks, scale=w.scale, tree_in_cache=w.tree_in_cache,
+                      threshold=w.threshold)
