@@ -83,6 +83,11 @@ def _L():
         lib.orc_accept.restype = ctypes.c_int
         lib.orc_kv_commit.argtypes = [ctypes.POINTER(_CommitArgs)]
         lib.orc_kv_commit.restype = ctypes.c_int
+        i32 = ctypes.c_int32
+        lib.orc_outcome_lookup.argtypes = [i32, i32, i32, i32] + [P] * 11
+        lib.orc_outcome_lookup.restype = ctypes.c_int
+        lib.orc_saguaro_reweight.argtypes = [P, i32, i32, i32, i32, P, i32, ctypes.c_float]
+        lib.orc_saguaro_reweight.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -221,4 +226,34 @@ def kv_commit(w, accept_len: np.ndarray, accept_rows: np.ndarray, k_cache: np.nd
         a.tree_layer_stride = 0 if tic else kt[0].size
     if _L().orc_kv_commit(ctypes.byref(a)) != 0:
         raise ValueError("orc_kv_commit rejected its arguments")
+    return out
+
+
+def outcome_lookup(stop_row, out_tokens, num_out, key_row, key_token, n_keys, prepared=None) -> dict:
+    """SSD outcome lookup; key_* [B,K], prepared [B,K,P] or None.  -> hit, branch, next_tokens, n_hits."""
+    c = lambda x: np.ascontiguousarray(x, dtype=np.int32)  # noqa: E731
+    stop_row, out_tokens, num_out, key_row, key_token, n_keys = map(c, (stop_row, out_tokens, num_out, key_row,
+                                                                         key_token, n_keys))
+    B, K = key_row.shape
+    Dm = out_tokens.shape[1] - 1
+    P = 0 if prepared is None else prepared.shape[2]
+    prepared = None if prepared is None else c(prepared)
+    out = dict(hit=np.zeros(B, np.int32), branch=np.zeros(B, np.int32), n_hits=np.zeros(1, np.int32),
+               next_tokens=np.zeros((B, P), np.int32) if P else None)
+    rc = _L().orc_outcome_lookup(B, K, P, Dm, _p(stop_row), _p(out_tokens), _p(num_out), _p(key_row), _p(key_token),
+                                 _p(n_keys), _p(prepared), _p(out["hit"]), _p(out["branch"]), _p(out["next_tokens"]),
+                                 _p(out["n_hits"]))
+    if rc != 0:
+        raise ValueError("orc_outcome_lookup rejected its arguments")
+    return out
+
+
+def saguaro_reweight(draft_logits: np.ndarray, cache_tokens: np.ndarray, shift: float) -> np.ndarray:
+    """Returns a reweighted copy of draft_logits [B,R,V] (fp32 or bf16 bits); cache_tokens [B,R,C]."""
+    out = np.ascontiguousarray(draft_logits).copy()
+    ct = np.ascontiguousarray(cache_tokens, dtype=np.int32)
+    B, R, V = out.shape
+    rc = _L().orc_saguaro_reweight(_p(out), B, R, V, _dt(out), _p(ct), ct.shape[2], float(np.float32(shift)))
+    if rc != 0:
+        raise ValueError("orc_saguaro_reweight rejected its arguments")
     return out

@@ -482,3 +482,69 @@ int orc_kv_commit(const orc_commit_args* a) {
   free(copy);
   return 0;
 }
+
+/* ------------------------------------------------------- SSD outcome lookup */
+int orc_outcome_lookup(int32_t B, int32_t K, int32_t P, int32_t max_depth, const int32_t* stop_row,
+                       const int32_t* out_tokens, const int32_t* num_out, const int32_t* key_row,
+                       const int32_t* key_token, const int32_t* n_keys, const int32_t* prepared, int32_t* hit,
+                       int32_t* branch, int32_t* next_tokens, int32_t* n_hits) {
+  if (B < 0 || K < 1 || P < 0 || max_depth < 1) return -1;
+  int32_t hits = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    int32_t found = -1;
+    const int32_t n = num_out[b];
+    if (n >= 1 && n <= max_depth + 1) {
+      const int32_t row = stop_row[b];
+      const int32_t bonus = out_tokens[(int64_t)b * (max_depth + 1) + (n - 1)];
+      int32_t nk = n_keys[b];
+      if (nk > K) nk = K;
+      for (int32_t k = 0; k < nk; ++k)
+        if (key_row[(int64_t)b * K + k] == row && key_token[(int64_t)b * K + k] == bonus) {
+          found = k;
+          break;
+        }
+    }
+    hit[b] = found >= 0;
+    branch[b] = found + 1;
+    hits += found >= 0;
+    if (next_tokens)
+      for (int32_t j = 0; j < P; ++j)
+        next_tokens[(int64_t)b * P + j] = found >= 0 ? prepared[((int64_t)b * K + found) * P + j] : 0;
+  }
+  if (n_hits) n_hits[0] = hits;
+  return 0;
+}
+
+/* ------------------------------------------------------- Saguaro reweighting */
+static uint16_t float_to_bf16_rne(float f) {
+  uint32_t x;
+  memcpy(&x, &f, 4);
+  x += 0x7fffu + ((x >> 16) & 1u);
+  return (uint16_t)(x >> 16);
+}
+
+int orc_saguaro_reweight(void* draft_logits, int32_t B, int32_t R, int32_t V, int32_t dtype,
+                         const int32_t* cache_tokens, int32_t C, float shift) {
+  if (B < 0 || R < 1 || V < 1 || C < 0 || (dtype != 0 && dtype != 1)) return -1;
+  for (int32_t b = 0; b < B; ++b)
+    for (int32_t r = 0; r < R; ++r) {
+      const int32_t* list = cache_tokens + ((int64_t)b * R + r) * C;
+      for (int32_t c = 0; c < C; ++c) {
+        const int32_t v = list[c];
+        if (v < 0 || v >= V) continue;
+        int dup = 0;
+        for (int32_t e = 0; e < c; ++e) dup |= list[e] == v;
+        if (dup) continue; /* each distinct token once */
+        const int64_t idx = ((int64_t)b * R + r) * V + v;
+        if (dtype == 0) {
+          float* l = (float*)draft_logits;
+          l[idx] = l[idx] + shift;
+        } else {
+          uint16_t* l = (uint16_t*)draft_logits;
+          const float cur = (float)bf16_bits_to_double(l[idx]);
+          l[idx] = float_to_bf16_rne(cur + shift);
+        }
+      }
+    }
+  return 0;
+}

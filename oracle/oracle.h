@@ -133,6 +133,33 @@ typedef struct {
 } orc_commit_args;
 int orc_kv_commit(const orc_commit_args* a);
 
+/* Outcome lookup of speculative speculative decoding ([SSD] sec. 2: the
+ * drafter prepares speculations for likely verification outcomes -- how many
+ * tokens are accepted and which bonus token is drawn; when verification ends
+ * the outcome either hits that cache, and the prepared tokens go straight to
+ * the next verification, or misses and a fallback runs).  The outcome of
+ * sequence b is (stop_row[b], bonus = out_tokens[b, num_out[b] - 1]): the stop
+ * row names the accepted path (for a chain it is the accepted length).
+ * Prepared outcome k < min(n_keys[b], K) is (key_row[b,k], key_token[b,k]).
+ * hit[b] = 1 and branch[b] = k + 1 for the lowest matching k; else hit 0 and
+ * branch 0 (the ghost entry: no -1).  next_tokens[b] (nullable, [B,P]) =
+ * prepared[b,k,:] on a hit, zeros on a miss; n_hits[0] (nullable) = number of
+ * hits.  num_out outside [1, max_depth+1] is a miss. */
+int orc_outcome_lookup(int32_t B, int32_t K, int32_t P, int32_t max_depth, const int32_t* stop_row,
+                       const int32_t* out_tokens, const int32_t* num_out, const int32_t* key_row,
+                       const int32_t* key_token, const int32_t* n_keys, const int32_t* prepared, int32_t* hit,
+                       int32_t* branch, int32_t* next_tokens, int32_t* n_hits);
+
+/* Saguaro sampling ([SSD] sec. 3B): the drafter lowers the probability of the
+ * tokens already in the speculation cache, which raises the residual mass on
+ * them and so the chance that the bonus token lands in the cache.  Stated on
+ * logits: every distinct token v in [0, V) of cache_tokens[b, r, 0..C-1] gets
+ * draft_logits[b, r, v] += shift (shift = T ln(rho) for a factor rho on the
+ * probabilities), added in fp32 and rounded to the logits' type (bf16: nearest
+ * even); other entries of the list are ignored.  dtype 0 fp32, 1 bf16.  In place. */
+int orc_saguaro_reweight(void* draft_logits, int32_t B, int32_t R, int32_t V, int32_t dtype,
+                         const int32_t* cache_tokens, int32_t C, float shift);
+
 #ifdef __cplusplus
 }
 #endif
