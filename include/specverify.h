@@ -303,6 +303,58 @@ typedef struct sv_commit_args {
 } sv_commit_args;
 sv_status sv_kv_commit(const sv_commit_args* args, void* stream);
 
+/*
+ * sv_outcome_lookup -- outcome lookup of speculative speculative decoding
+ * ([SSD] sec. 2: while the target verifies, the drafter prepares speculations
+ * for the likely verification outcomes -- how many tokens are accepted and
+ * which bonus token is drawn; a hit sends the prepared tokens to the next
+ * verification at once, a miss falls back to synchronous drafting).
+ * The outcome of sequence b is (stop_row[b], bonus) with bonus =
+ * out_tokens[b, num_out[b] - 1], all three from sv_accept; the stop row names
+ * the accepted path (on a chain it equals the accepted length).  Prepared
+ * outcome k < min(n_keys[b], K) of sequence b is (key_row[b,k], key_token[b,k]).
+ *   hit [B]:        1 when some prepared outcome equals the real one, else 0
+ *   branch [B]:     k + 1 for the lowest such k, else 0 (the ghost entry, so
+ *                   no -1 is ever produced)
+ *   next_tokens [B, P] (nullable): prepared[b, k, :] on a hit, zeros on a miss
+ *                   (prepared [B, K, P] is then required when P > 0)
+ *   n_hits [1] (nullable): number of sequences that hit (e.g. to pick the
+ *                   fallback drafter by how many sequences miss, [SSD] sec. 3C)
+ * num_out outside [1, max_depth + 1] is a miss.  All arrays int32, device.
+ */
+typedef struct sv_outcome_args {
+  int32_t B, K, P, max_depth;
+  const int32_t* stop_row;
+  const int32_t* out_tokens;
+  const int32_t* num_out;
+  const int32_t* key_row;
+  const int32_t* key_token;
+  const int32_t* n_keys;
+  const int32_t* prepared;
+  int32_t* hit;
+  int32_t* branch;
+  int32_t* next_tokens;
+  int32_t* n_hits;
+} sv_outcome_args;
+sv_status sv_outcome_lookup(const sv_outcome_args* args, void* stream);
+
+/*
+ * sv_saguaro_reweight -- Saguaro sampling's draft reweighting ([SSD] sec. 3B:
+ * lowering the draft probability of tokens already in the speculation cache
+ * raises the residual mass on them, so the bonus token more often lands in the
+ * cache).  In place on draft_logits [B, R, V] (dtype SV_F32 or SV_BF16): for
+ * every distinct token v in [0, V) of cache_tokens[b, r, 0 .. C-1] (int32,
+ * device), draft_logits[b, r, v] += shift, added in fp32 and rounded to the
+ * logits' type (bf16: nearest even).  Entries outside [0, V) and repeats are
+ * ignored.  shift = T ln(rho) multiplies those tokens' unnormalised
+ * probabilities by rho at temperature T.  The drafter must sample from the
+ * same reweighted logits that sv_accept then receives as draft_logits; the
+ * acceptance rule keeps the output distribution exact for any draft
+ * distribution.  A non-finite shift is SV_ERR_INVALID_ARGUMENT.
+ */
+sv_status sv_saguaro_reweight(void* draft_logits, int32_t B, int32_t R, int32_t V, int32_t dtype,
+                              const int32_t* cache_tokens, int32_t C, float shift, void* stream);
+
 /* Human-readable name of an sv_status (static string). */
 const char* sv_status_string(sv_status s);
 

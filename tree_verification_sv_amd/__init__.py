@@ -26,7 +26,8 @@ SV_COMMIT_PATH, SV_COMMIT_LENGTH = 0, 1
 
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-SOURCES = ["sv_api.hip", "sv_mask.hip", "sv_attention.hip", "sv_accept.hip", "sv_threshold.hip", "sv_commit.hip"]
+SOURCES = ["sv_api.hip", "sv_mask.hip", "sv_attention.hip", "sv_accept.hip", "sv_threshold.hip", "sv_commit.hip",
+           "sv_ssd.hip"]
 
 
 class SpecVerifyError(RuntimeError):
@@ -84,8 +85,16 @@ class sv_commit_args(ctypes.Structure):
                 ("cache_layer_stride", ctypes.c_int64), ("tree_layer_stride", ctypes.c_int64)]
 
 
+class sv_outcome_args(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("K", ctypes.c_int32), ("P", ctypes.c_int32), ("max_depth", ctypes.c_int32),
+                ("stop_row", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p), ("num_out", ctypes.c_void_p),
+                ("key_row", ctypes.c_void_p), ("key_token", ctypes.c_void_p), ("n_keys", ctypes.c_void_p),
+                ("prepared", ctypes.c_void_p), ("hit", ctypes.c_void_p), ("branch", ctypes.c_void_p),
+                ("next_tokens", ctypes.c_void_p), ("n_hits", ctypes.c_void_p)]
+
+
 EXPORTS = ["sv_build_tree_mask", "sv_tree_attention_workspace", "sv_tree_attention", "sv_accept_workspace",
-           "sv_accept", "sv_kv_commit", "sv_status_string", "sv_version"]
+           "sv_accept", "sv_kv_commit", "sv_outcome_lookup", "sv_saguaro_reweight", "sv_status_string", "sv_version"]
 
 
 def lib():
@@ -109,6 +118,10 @@ def lib():
         L.sv_accept.restype = i32
         L.sv_kv_commit.argtypes = [ctypes.POINTER(sv_commit_args), P]
         L.sv_kv_commit.restype = i32
+        L.sv_outcome_lookup.argtypes = [ctypes.POINTER(sv_outcome_args), P]
+        L.sv_outcome_lookup.restype = i32
+        L.sv_saguaro_reweight.argtypes = [P, i32, i32, i32, i32, P, i32, ctypes.c_float, P]
+        L.sv_saguaro_reweight.restype = i32
         L.sv_status_string.argtypes = [i32]
         L.sv_status_string.restype = ctypes.c_char_p
         L.sv_version.argtypes = []
@@ -369,6 +382,45 @@ def sv_kv_commit(k_cache, v_cache, k_tree, v_tree, prefix_len, accept_len, accep
                     commit_mode, tree_in_cache, N, num_layers)
     _check(lib().sv_kv_commit(ctypes.byref(a), _stream(stream)), "sv_kv_commit")
     return outs
+
+
+def sv_outcome_lookup(stop_row, out_tokens, num_out, key_row, key_token, n_keys, prepared=None, outs=None,
+                      stream=None) -> dict:
+    """SSD outcome lookup on device; returns hit, branch (k+1 or 0), next_tokens (or None), n_hits."""
+    torch = _torch()
+    B, K = key_row.shape
+    Dm = out_tokens.shape[1] - 1
+    P = 0 if prepared is None else prepared.shape[2]
+    dev = key_row.device
+    if outs is None:
+        outs = dict(hit=torch.empty(B, dtype=torch.int32, device=dev),
+                    branch=torch.empty(B, dtype=torch.int32, device=dev),
+                    next_tokens=torch.empty((B, P), dtype=torch.int32, device=dev) if P else None,
+                    n_hits=torch.empty(1, dtype=torch.int32, device=dev))
+    a = sv_outcome_args()
+    a.B, a.K, a.P, a.max_depth = B, K, P, Dm
+    i32 = torch.int32
+    a.stop_row, a.out_tokens, a.num_out = (_ptr(stop_row, i32, "stop_row"), _ptr(out_tokens, i32, "out_tokens"),
+                                           _ptr(num_out, i32, "num_out"))
+    a.key_row, a.key_token, a.n_keys = (_ptr(key_row, i32, "key_row"), _ptr(key_token, i32, "key_token"),
+                                        _ptr(n_keys, i32, "n_keys"))
+    a.prepared = _ptr(prepared, i32, "prepared")
+    a.hit, a.branch = _ptr(outs["hit"], i32, "hit"), _ptr(outs["branch"], i32, "branch")
+    a.next_tokens = _ptr(outs.get("next_tokens"), i32, "next_tokens")
+    a.n_hits = _ptr(outs.get("n_hits"), i32, "n_hits")
+    _check(lib().sv_outcome_lookup(ctypes.byref(a), _stream(stream)), "sv_outcome_lookup")
+    return outs
+
+
+def sv_saguaro_reweight(draft_logits, cache_tokens, shift: float, stream=None):
+    """In-place Saguaro reweighting of draft_logits [B,R,V] at the tokens cache_tokens [B,R,C]."""
+    torch = _torch()
+    B, R, V = draft_logits.shape
+    C = cache_tokens.shape[2]
+    rc = lib().sv_saguaro_reweight(_ptr(draft_logits, name="draft_logits"), B, R, V, _elem(draft_logits),
+                                   _ptr(cache_tokens, torch.int32, "cache_tokens"), C, float(shift), _stream(stream))
+    _check(rc, "sv_saguaro_reweight")
+    return draft_logits
 
 
 def sv_status_string(code: int) -> str:
