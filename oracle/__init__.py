@@ -88,6 +88,8 @@ def _L():
         lib.orc_outcome_lookup.restype = ctypes.c_int
         lib.orc_saguaro_reweight.argtypes = [P, i32, i32, i32, i32, P, i32, ctypes.c_float]
         lib.orc_saguaro_reweight.restype = ctypes.c_int
+        lib.orc_draft_subset_logits.argtypes = [P, i32, i32, i32, P, i32, i32, P]
+        lib.orc_draft_subset_logits.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -257,3 +259,15 @@ def saguaro_reweight(draft_logits: np.ndarray, cache_tokens: np.ndarray, shift: 
     if rc != 0:
         raise ValueError("orc_saguaro_reweight rejected its arguments")
     return out
+
+
+def draft_subset_logits(sub: np.ndarray, t2d: np.ndarray) -> np.ndarray:
+    """Full-vocabulary draft logits [B,R,V] from subset logits [B,R,Vd] and t2d [V] (j+1, 0 = absent)."""
+    sub = np.ascontiguousarray(sub)
+    t2d = np.ascontiguousarray(t2d, dtype=np.int32)
+    B, R, Vd = sub.shape
+    V = t2d.size
+    full = np.empty((B, R, V), dtype=sub.dtype)
+    if _L().orc_draft_subset_logits(_p(sub), B, R, Vd, _p(t2d), V, _dt(sub), _p(full)) != 0:
+        raise ValueError("orc_draft_subset_logits rejected its arguments")
+    return full

@@ -548,3 +548,20 @@ int orc_saguaro_reweight(void* draft_logits, int32_t B, int32_t R, int32_t V, in
     }
   return 0;
 }
+
+/* ------------------------------------------------------- draft vocabulary subset */
+int orc_draft_subset_logits(const void* sub, int32_t B, int32_t R, int32_t Vd, const int32_t* t2d, int32_t V,
+                            int32_t dtype, void* full) {
+  if (B < 0 || R < 1 || Vd < 1 || V < 1 || (dtype != 0 && dtype != 1)) return -1;
+  for (int64_t row = 0; row < (int64_t)B * R; ++row)
+    for (int32_t v = 0; v < V; ++v) {
+      const int32_t j = t2d[v];
+      const int present = j >= 1 && j <= Vd;
+      if (dtype == 0) {
+        ((float*)full)[row * V + v] = present ? ((const float*)sub)[row * Vd + (j - 1)] : -INFINITY;
+      } else {
+        ((uint16_t*)full)[row * V + v] = present ? ((const uint16_t*)sub)[row * Vd + (j - 1)] : (uint16_t)0xFF80u;
+      }
+    }
+  return 0;
+}

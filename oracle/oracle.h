@@ -160,6 +160,16 @@ int orc_outcome_lookup(int32_t B, int32_t K, int32_t P, int32_t max_depth, const
 int orc_saguaro_reweight(void* draft_logits, int32_t B, int32_t R, int32_t V, int32_t dtype,
                          const int32_t* cache_tokens, int32_t C, float shift);
 
+/* Draft vocabulary subset ([EP] sec. 3, item 5: the drafter's vocabulary is a
+ * cached subset of the target's, trading speed for quality).  The drafter's
+ * logits sub [B,R,Vd] cover the subset; acceptance needs the draft distribution
+ * over the target vocabulary, where ids outside the subset have probability 0.
+ * t2d [V] maps target id v to j + 1 when v is subset entry j, 0 when v is not
+ * in the subset (values outside [0, Vd] count as 0).  full[b,r,v] =
+ * sub[b,r,t2d[v]-1], or -inf (probability 0) when absent.  dtype 0 fp32, 1 bf16. */
+int orc_draft_subset_logits(const void* sub, int32_t B, int32_t R, int32_t Vd, const int32_t* t2d, int32_t V,
+                            int32_t dtype, void* full);
+
 #ifdef __cplusplus
 }
 #endif
