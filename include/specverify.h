@@ -355,6 +355,23 @@ sv_status sv_outcome_lookup(const sv_outcome_args* args, void* stream);
 sv_status sv_saguaro_reweight(void* draft_logits, int32_t B, int32_t R, int32_t V, int32_t dtype,
                               const int32_t* cache_tokens, int32_t C, float shift, void* stream);
 
+/*
+ * sv_draft_subset_logits -- draft logits over a vocabulary subset, laid out
+ * over the target vocabulary ([EP] sec. 3, item 5: the drafter's vocabulary is
+ * a cached subset of the target's; acceptance compares full distributions,
+ * [PX] "Objetivo-Borrador").  sub_logits [B, R, Vd] are the drafter's logits
+ * over its Vd subset entries; t2d [V] int32 maps target id v to j + 1 when v is
+ * subset entry j and to 0 when v is not in the subset (values outside [0, Vd]
+ * count as 0, so no negative or out-of-range index is ever read).
+ * full_logits [B, R, V] (output, same dtype): sub_logits[b, r, t2d[v] - 1], or
+ * -inf (probability 0) for ids outside the subset.  The result is the
+ * draft_logits of sv_accept: a drafted token outside the subset never occurs,
+ * and the residual max(0, p - q) carries the target's mass on those ids.
+ * dtype SV_F32 or SV_BF16.  full_logits must not overlap sub_logits.
+ */
+sv_status sv_draft_subset_logits(const void* sub_logits, int32_t B, int32_t R, int32_t Vd, const int32_t* t2d,
+                                 int32_t V, int32_t dtype, void* full_logits, void* stream);
+
 /* Human-readable name of an sv_status (static string). */
 const char* sv_status_string(sv_status s);
 

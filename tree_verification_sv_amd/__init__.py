@@ -27,7 +27,7 @@ SV_COMMIT_PATH, SV_COMMIT_LENGTH = 0, 1
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 SOURCES = ["sv_api.hip", "sv_mask.hip", "sv_attention.hip", "sv_accept.hip", "sv_threshold.hip", "sv_commit.hip",
-           "sv_ssd.hip"]
+           "sv_ssd.hip", "sv_vocab.hip"]
 
 
 class SpecVerifyError(RuntimeError):
@@ -94,7 +94,8 @@ class sv_outcome_args(ctypes.Structure):
 
 
 EXPORTS = ["sv_build_tree_mask", "sv_tree_attention_workspace", "sv_tree_attention", "sv_accept_workspace",
-           "sv_accept", "sv_kv_commit", "sv_outcome_lookup", "sv_saguaro_reweight", "sv_status_string", "sv_version"]
+           "sv_accept", "sv_kv_commit", "sv_outcome_lookup", "sv_saguaro_reweight", "sv_draft_subset_logits",
+           "sv_status_string", "sv_version"]
 
 
 def lib():
@@ -122,6 +123,8 @@ def lib():
         L.sv_outcome_lookup.restype = i32
         L.sv_saguaro_reweight.argtypes = [P, i32, i32, i32, i32, P, i32, ctypes.c_float, P]
         L.sv_saguaro_reweight.restype = i32
+        L.sv_draft_subset_logits.argtypes = [P, i32, i32, i32, P, i32, i32, P, P]
+        L.sv_draft_subset_logits.restype = i32
         L.sv_status_string.argtypes = [i32]
         L.sv_status_string.restype = ctypes.c_char_p
         L.sv_version.argtypes = []
@@ -421,6 +424,21 @@ def sv_saguaro_reweight(draft_logits, cache_tokens, shift: float, stream=None):
                                    _ptr(cache_tokens, torch.int32, "cache_tokens"), C, float(shift), _stream(stream))
     _check(rc, "sv_saguaro_reweight")
     return draft_logits
+
+
+def sv_draft_subset_logits(sub_logits, t2d, out=None, stream=None):
+    """Full-vocabulary draft logits [B,R,V] from subset logits [B,R,Vd] and t2d [V] (j+1, 0 = absent)."""
+    torch = _torch()
+    B, R, Vd = sub_logits.shape
+    V = t2d.shape[0]
+    if out is None:
+        out = torch.empty((B, R, V), dtype=sub_logits.dtype, device=sub_logits.device)
+    if out.dtype != sub_logits.dtype:
+        raise SpecVerifyError("out and sub_logits must share a dtype")
+    rc = lib().sv_draft_subset_logits(_ptr(sub_logits, name="sub_logits"), B, R, Vd, _ptr(t2d, torch.int32, "t2d"),
+                                      V, _elem(sub_logits), _ptr(out, name="out"), _stream(stream))
+    _check(rc, "sv_draft_subset_logits")
+    return out
 
 
 def sv_status_string(code: int) -> str:
