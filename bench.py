@@ -30,6 +30,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_TFLOPS = 2500.0   # dense bf16 MFMA peak of MI355X
+VALU_FP32_TFLOPS = 157.3    # fp32 vector peak of MI355X
 MALL_BYTES = 256 * 2**20
 
 
@@ -58,8 +60,12 @@ def algorithmic_bytes(w, acc):
         moved = int(A.sum())
     commit = moved * Hkv * D * 2 * e * 2
     mask = 4 * B * N + B * N * (8 * W + 4 + 4 * w.max_depth)
+    # attention flops: q.k and p.v over the prefix and each node's root path (2 flops per multiply-add)
+    import workloads as W
+    keys = sum(int(L[b]) * N + int(W.tree_depths(w.parents[b]).sum()) for b in range(B))
+    attn_flops = 4 * Hq * D * keys
     return dict(mask=mask, attention=attn, accept=accept, commit=commit,
-                total=mask + attn + accept + commit)
+                total=mask + attn + accept + commit, attention_flops=attn_flops)
 
 
 def source_hash(files):
@@ -171,6 +177,61 @@ def commit_layers(w, dev, acc, layers, K):
                 gbs=round(byts / (ms * 1e-3) / 1e9, 1), tree_kv="in cache" if tic else "separate rows")
 
 
+def time_extras(w, dev, acc, K_steps):
+    """Time the operations around the step on this workload's shape (HIP events, K launches each):
+    the SSD outcome lookup (8 prepared outcomes of max_depth tokens per sequence), Saguaro
+    reweighting (8 cached tokens per row of the draft logits) and the draft vocabulary subset
+    (a 32000-id subset laid out over the target vocabulary)."""
+    import torch
+    import tree_verification_sv_amd as sv
+    import workloads as W
+    B, R, V, Dm = w.B, w.N + 1, w.V, w.max_depth
+    d = "cuda:0"
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(d)  # noqa: E731
+    K, P, C, Vd = 8, Dm, 8, 32000
+    res = {}
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s = torch.cuda.current_stream()
+        a.record(s)
+        for _ in range(K_steps):
+            fn()
+        b.record(s)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / K_steps
+
+    keys_r = t(W.randint(w.seed, 93, B * K, 0, w.N).reshape(B, K))
+    keys_t = t(W.randint(w.seed, 94, B * K, 0, V - 1).reshape(B, K))
+    prep = t(W.randint(w.seed, 95, B * K * P, 0, V - 1).reshape(B, K, P))
+    nk = t(np.full(B, K))
+    st, ot, no = t(acc["stop_row"]), t(acc["out_tokens"]), t(acc["num_out"])
+    outs = dict(hit=torch.empty(B, dtype=torch.int32, device=d), branch=torch.empty(B, dtype=torch.int32, device=d),
+                next_tokens=torch.empty((B, P), dtype=torch.int32, device=d),
+                n_hits=torch.empty(1, dtype=torch.int32, device=d))
+    ms = timed(lambda: sv.sv_outcome_lookup(st, ot, no, keys_r, keys_t, nk, prep, outs=outs))
+    res["outcome_lookup"] = dict(ms=round(ms, 5), batch=B, keys=K, prepared_tokens=P)
+    logits = dev["draft_logits"] if dev["draft_logits"] is not None else dev["target_logits"].clone()
+    ct = t(W.randint(w.seed, 96, B * R * C, 0, V - 1).reshape(B, R, C))
+    e = logits.element_size()
+    ms = timed(lambda: sv.sv_saguaro_reweight(logits, ct, -0.5))
+    res["saguaro_reweight"] = dict(ms=round(ms, 5), rows=B * R, cached_per_row=C)
+    ids = np.argsort(W.u64(w.seed, 97, V))[:Vd]
+    t2d = np.zeros(V, np.int32)
+    t2d[ids] = np.arange(1, Vd + 1, dtype=np.int32)
+    t2d_d = t(t2d)
+    sub = logits[:, :, :Vd].contiguous()
+    full = torch.empty_like(logits)
+    ms = timed(lambda: sv.sv_draft_subset_logits(sub, t2d_d, out=full))
+    byts = B * R * V * e + B * R * Vd * e + V * 4
+    res["draft_subset"] = dict(ms=round(ms, 5), rows=B * R, subset=Vd, bytes=byts,
+                               gbs=round(byts / (ms * 1e-3) / 1e9, 1), frac=round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -191,6 +252,8 @@ def main():
                          "there, the commit compacts the accepted path in place after the attention)")
     ap.add_argument("--commit-layers", type=int, default=0,
                     help="also time one layer-batched sv_kv_commit over this many layers of the workload's shape")
+    ap.add_argument("--extras", action="store_true",
+                    help="also time the SSD outcome lookup, Saguaro reweighting and draft vocabulary subset")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (reference kernel for PMC byte counters)")
     args = ap.parse_args()
@@ -294,6 +357,7 @@ def main():
         stage_ms[name] = a.elapsed_time(b) / K
 
     layered = commit_layers(ws[0], devs[0], accs[0], args.commit_layers, K) if args.commit_layers else None
+    extras = time_extras(ws[0], devs[0], accs[0], K) if args.extras else None
 
     mean_bytes = {k: float(np.mean([bb[k] for bb in byts])) for k in byts[0]}
     B, N = w0.B, w0.N
@@ -303,6 +367,17 @@ def main():
     dom = max(("attention", "accept"), key=lambda k: stage_ms[k])
     dom_key = {"attention": "attention", "accept": "accept"}[dom]
     achieved = mean_bytes[dom_key] / (stage_ms[dom] * 1e-3) / 1e9
+    roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    if dom == "attention":
+        # the attention is a dense contraction: it is MFMA-bound when its flops at the dense peak take
+        # longer than its bytes at the HBM peak (bf16 MFMA 2500 TFLOP/s; fp32 runs on the vector ALUs)
+        fpeak = MFMA_BF16_TFLOPS if w0.dtype == "bf16" else VALU_FP32_TFLOPS
+        flops = mean_bytes["attention_flops"]
+        if flops / (fpeak * 1e12) > mean_bytes["attention"] / (HBM_PEAK_GBS * 1e9):
+            tf = flops / (stage_ms[dom] * 1e-3) / 1e12
+            roof = {"bound": "mfma" if w0.dtype == "bf16" else "alu", "kernel": dom, "achieved": round(tf, 1),
+                    "peak": fpeak, "unit": "TFLOP/s", "frac": round(tf / fpeak, 4)}
     src = {"attention": ["tree_verification_sv_amd/csrc/sv_attention.hip"],
            "accept": ["tree_verification_sv_amd/csrc/sv_accept.hip"]}[dom]
     traffic = load_traffic(dom, source_hash(src), w0.name)
@@ -330,16 +405,18 @@ def main():
         "accept_steps_per_s": round(B / (ms_step * 1e-3), 1),
         "hbm_gbs": round(hbm_gbs, 1),
         "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
-        "bytes_per_step": {k: int(v) for k, v in mean_bytes.items()},
+        "bytes_per_step": {k: int(v) for k, v in mean_bytes.items() if k != "attention_flops"},
+        "attention_flops_per_step": int(mean_bytes["attention_flops"]),
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
         "mean_accept_len": float(np.mean([a["accept_len"].mean() for a in accs])),
         "emitted_tokens_per_s": round(float(np.mean([a["num_out"].sum() for a in accs])) / (ms_step * 1e-3), 1),
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "roofline": {**roof, "traffic": traffic if roof["bound"] == "hbm" else None},
         "wall_s_timed": round(wall, 3),
     }
     if layered is not None:
         result["layered_commit"] = layered
+    if extras is not None:
+        result["extras"] = extras
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on one step", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(args.config, variant=variant)
