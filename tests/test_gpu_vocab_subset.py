@@ -41,7 +41,8 @@ def _subset_map(seed, V, Vd, junk=0):
 
 
 @pytest.mark.parametrize("dtype,B,R,V,Vd,junk", [("bf16", 2, 7, 128256, 32000, 0), ("f32", 3, 5, 1001, 77, 40),
-                                                 ("bf16", 1, 1, 4099, 4099, 0)])
+                                                 ("bf16", 1, 1, 4099, 4099, 0),
+                                                 ("f32", 2, 3, 30011, 20000, 10)])  # 80 KB subset rows: global gather
 def test_subset_logits_bitwise(dtype, B, R, V, Vd, junk):
     import torch
     import tree_verification_sv_amd as sv

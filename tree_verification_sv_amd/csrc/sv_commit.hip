@@ -11,10 +11,11 @@
 //  k_kv_commit           one work-group per sequence, one layer, tree rows in
 //                        their own tensor: checks, copies every KV head and
 //                        writes new_len / committed_slots / status.
-//  k_kv_commit_rows      one work-group per (sequence, KV head, layer): the
-//                        layer-batched commit and the in-place compaction of
-//                        cache-resident tree rows.  Source rows are staged in
-//                        LDS before any destination row is written, so a path
+//  k_kv_commit_rows      one work-group per (sequence, run of layers), every KV
+//                        head: the layer-batched commit and the in-place
+//                        compaction of cache-resident tree rows.  Each round
+//                        loads its source rows into registers and waits for
+//                        them before any destination row is written, so a path
 //                        in any node order compacts correctly, and rows that
 //                        are already in place are skipped.
 //  k_kv_commit_finalize  one work-group per sequence, launched after
@@ -144,41 +145,63 @@ __global__ void __launch_bounds__(256) k_kv_commit(sv_commit_args a, CommitPlan 
   write_outputs(a, b, c);
 }
 
-// K and V chunks of up to SV_MAX_DEPTH rows of at most 512 bytes (D 128 fp32)
-constexpr int STAGE_CHUNKS = SV_MAX_DEPTH * 32;
+// 16-byte chunks moved per round: 8 per thread, all loaded into registers before any is
+// stored.  One (layer, KV head) unit needs at most SV_MAX_DEPTH rows x 32 chunks x 2 (K and V)
+// = 1024 of them, so a round holds at least two whole units.
+constexpr int CM_THREADS = 256;
+constexpr int CM_CPT = 8;
+constexpr int ROUND_CHUNKS = CM_THREADS * CM_CPT;
 
-__global__ void __launch_bounds__(256) k_kv_commit_rows(sv_commit_args a, CommitPlan p) {
+// One work-group per (sequence, run of `lpw` layers): every (layer, KV head) unit of the run
+// moves its accepted rows.  Units are processed in rounds of whole units: every source chunk
+// of a round is loaded (and waited for) before the barrier and stored after it, so a
+// compaction inside one cache plane never overwrites a row it still has to read.
+__global__ void __launch_bounds__(CM_THREADS) k_kv_commit_rows(sv_commit_args a, CommitPlan p, int lpw, int layers) {
   __shared__ CommitCheck c;
-  __shared__ uint4 stage[2 * STAGE_CHUNKS];
-  const int b = blockIdx.x / a.Hkv;
-  const int h = blockIdx.x % a.Hkv;
-  const int layer = blockIdx.y;
+  const int b = blockIdx.x;
+  const int l0 = blockIdx.y * lpw;
   const int t = threadIdx.x;
   commit_check(a, b, c);
   if (c.code != 0) return;
   const int A = c.A;
+  const int nl = min(lpw, layers - l0);
+  if (A == 0 || nl <= 0) return;
   const int64_t row_bytes = (int64_t)a.D * p.es;
-  char* kc = (char*)a.k_cache + layer * a.cache_layer_stride * p.es;
-  char* vc = (char*)a.v_cache + layer * a.cache_layer_stride * p.es;
-  const char* kt = a.tree_in_cache ? kc : (const char*)a.k_tree + layer * a.tree_layer_stride * p.es;
-  const char* vt = a.tree_in_cache ? vc : (const char*)a.v_tree + layer * a.tree_layer_stride * p.es;
-  const int n = A * p.cpr;
-  // every source row of the path is read before any destination row is written
-  for (int x = t; x < n; x += blockDim.x) {
-    const int k = x / p.cpr, ch = x % p.cpr;
-    if (a.tree_in_cache && c.src[k] == c.dst[k]) continue;  // already in place
-    const int64_t src_row = a.tree_in_cache ? cache_row(a, b, h, c.src[k])
-                                            : ((int64_t)b * a.Hkv + h) * (a.N + 1) + c.src[k];
-    stage[x] = *((const uint4*)(kt + src_row * row_bytes) + ch);
-    stage[STAGE_CHUNKS + x] = *((const uint4*)(vt + src_row * row_bytes) + ch);
-  }
-  __syncthreads();
-  for (int x = t; x < n; x += blockDim.x) {
-    const int k = x / p.cpr, ch = x % p.cpr;
-    if (a.tree_in_cache && c.src[k] == c.dst[k]) continue;
-    const int64_t dst_row = cache_row(a, b, h, c.dst[k]);
-    *((uint4*)(kc + dst_row * row_bytes) + ch) = stage[x];
-    *((uint4*)(vc + dst_row * row_bytes) + ch) = stage[STAGE_CHUNKS + x];
+  const int per_unit = A * p.cpr * 2;                 // K and V chunks of one (layer, head)
+  const int upr = ROUND_CHUNKS / per_unit;            // units per round (>= 2)
+  const int units = nl * a.Hkv;
+  for (int u0 = 0; u0 < units; u0 += upr) {
+    const int n = min(upr, units - u0) * per_unit;
+    uint4 v[CM_CPT];
+    int64_t dst[CM_CPT];  // byte offset of the destination chunk in its cache, -1 when none
+    bool isv[CM_CPT];
+#pragma unroll
+    for (int i = 0; i < CM_CPT; ++i) {
+      const int x = t + i * CM_THREADS;
+      dst[i] = -1;
+      isv[i] = false;
+      if (x >= n) continue;
+      const int u = u0 + x / per_unit, y = x % per_unit;
+      const int layer = l0 + u / a.Hkv, h = u % a.Hkv;
+      const int kv = y / (A * p.cpr), k = (y / p.cpr) % A, ch = y % p.cpr;
+      if (a.tree_in_cache && c.src[k] == c.dst[k]) continue;  // already in place
+      const char* base = a.tree_in_cache ? (const char*)(kv ? a.v_cache : a.k_cache) + layer * a.cache_layer_stride * p.es
+                                         : (const char*)(kv ? a.v_tree : a.k_tree) + layer * a.tree_layer_stride * p.es;
+      const int64_t src_row = a.tree_in_cache ? cache_row(a, b, h, c.src[k])
+                                              : ((int64_t)b * a.Hkv + h) * (a.N + 1) + c.src[k];
+      v[i] = *((const uint4*)(base + src_row * row_bytes) + ch);
+      dst[i] = layer * a.cache_layer_stride * p.es + cache_row(a, b, h, c.dst[k]) * row_bytes + (int64_t)ch * 16;
+      isv[i] = kv != 0;
+    }
+    // every load of the round has returned before any store of the work-group
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < CM_CPT; ++i) {
+      if (dst[i] < 0) continue;
+      *(uint4*)((char*)(isv[i] ? a.v_cache : a.k_cache) + dst[i]) = v[i];
+    }
+    __syncthreads();
   }
 }
 
@@ -221,9 +244,11 @@ extern "C" sv_status sv_kv_commit(const sv_commit_args* args, void* stream) {
   if (layers == 1 && !a.tree_in_cache) {
     hipLaunchKernelGGL(k_kv_commit, dim3(a.B), dim3(256), 0, s, a, p);
   } else {
-    const int64_t groups = (int64_t)a.B * a.Hkv;
-    if (groups > 0x7fffffff) return SV_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(k_kv_commit_rows, dim3((unsigned)groups, (unsigned)layers), dim3(256), 0, s, a, p);
+    // about a thousand work-groups: enough to fill the device, few enough that dispatch keeps up
+    int lpw = (int)(((int64_t)a.B * layers + 1023) / 1024);
+    if (lpw < 1) lpw = 1;
+    const int runs = (layers + lpw - 1) / lpw;
+    hipLaunchKernelGGL(k_kv_commit_rows, dim3((unsigned)a.B, (unsigned)runs), dim3(CM_THREADS), 0, s, a, p, lpw, layers);
     hipLaunchKernelGGL(k_kv_commit_finalize, dim3(a.B), dim3(64), 0, s, a);
   }
   return sv_launch_status();

@@ -11,17 +11,23 @@
 // deepest accepted node (lowest index on ties); the extra token is the argmax
 // of the stop row (lowest id on ties).
 //
-//  k_thr_rows<T, AL>  one work-group per (row, vocabulary slice) of the rows
-//                     that have a usable child: slice maximum with its lowest
-//                     id, and sum_v exp((l_v - m_slice) / T) (fp32 exponentials,
-//                     fp64 sums), one 16-byte partial per slice.  Other rows
-//                     exit at once, so each needed row is read from HBM once.
-//  k_thr_walk<T, AL>  one work-group per sequence: merges the partials of each
-//                     needed row, forms p_r(x) for every usable node from its
-//                     logit, scores every root path, picks the stop node,
-//                     takes the bonus from the stop row's partials (or scans a
-//                     leaf stop row itself), writes the outputs and zeroes the
-//                     sequence's partials again.
+//  k_thr_rows<T, AL>  one work-group per (row, part) of the rows with a usable
+//                     child (others exit after one scan of the parent array);
+//                     a part is a contiguous run of the row (one part per row
+//                     for large batches, up to 8 for small ones), streamed
+//                     with 8 16-byte loads per thread in flight; each
+//                     thread keeps a running maximum with its lowest id and
+//                     sum_v exp((l_v - m) / T) (fp32 exponentials, fp64 sums,
+//                     rescaled when its maximum moves); one block reduction
+//                     gives the part's (max, id, sum).  About a thousand
+//                     work-groups in all: work-group dispatch, not HBM, limits
+//                     grids of tens of thousands.
+//  k_thr_walk<T, AL>  one work-group per sequence: forms p_r(x) for every
+//                     usable node from its logit and its parent row's
+//                     statistics, scores every root path, picks the stop node,
+//                     takes the bonus from the stop row's statistics (or scans
+//                     a leaf stop row itself, 8 loads per thread in flight),
+//                     writes the outputs and zeroes the sequence's statistics.
 #include <float.h>
 #include <math.h>
 
@@ -29,16 +35,16 @@
 
 namespace {
 
-constexpr int TR_THREADS = 256;
-constexpr int TR_PIECES = 8;  // 16-byte pieces per thread and slice
+constexpr int TR_THREADS = 256;   // walk kernel
+constexpr int RW_THREADS = 512;   // row kernel and the walk's row scan
+constexpr int TR_BATCH = 8;       // 16-byte loads in flight per thread
 
-template <typename T> constexpr int tr_epp() { return 16 / (int)sizeof(T); }
-template <typename T> constexpr int tr_slice() { return TR_THREADS * TR_PIECES * tr_epp<T>(); }
+template <typename T> constexpr int tr_epc() { return 16 / (int)sizeof(T); }  // entries per 16-byte chunk
 
 struct ThrPartial {
-  float m;      // slice maximum of the stored logits
+  float m;      // row maximum of the stored logits
   int32_t arg;  // lowest id holding it
-  double z;     // sum over the slice of exp((l - m) / T)
+  double z;     // sum over the row of exp((l - m) / T)
 };
 
 // Order-preserving key of (value, id): larger value first, then the lower id.
@@ -48,6 +54,11 @@ __device__ __forceinline__ uint64_t argmax_key(float v, int id) {
   return ((uint64_t)u << 32) | (uint32_t)(0x7fffffff - id);
 }
 __device__ __forceinline__ int key_id(uint64_t k) { return 0x7fffffff - (int)(uint32_t)k; }
+__device__ __forceinline__ float key_val(uint64_t k) {
+  uint32_t u = (uint32_t)(k >> 32);
+  u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
+  return __uint_as_float(u);
+}
 
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
   for (int o = 32; o > 0; o >>= 1) {
@@ -66,29 +77,33 @@ __device__ __forceinline__ float logit(const T* row, int64_t v) {
   return load_as_f32<T>(row, v);
 }
 
-// Thread t's TR_PIECES * EPP logits of slice s (ids ascending within the thread), -inf past V.
+// Entry e of a 16-byte chunk as float.
+template <typename T>
+__device__ __forceinline__ float chunk_entry(const uint4& w, int e) {
+  const uint32_t u = e / (tr_epc<T>() / 4) == 0 ? w.x : (e / (tr_epc<T>() / 4) == 1 ? w.y : (e / (tr_epc<T>() / 4) == 2 ? w.z : w.w));
+  if constexpr (sizeof(T) == 2) return bf16_bits_to_f32((uint16_t)(u >> (16 * (e % 2))));
+  else return __uint_as_float(u);
+}
+
+// Chunk c of a row (entries c*EPC ..): a 16-byte load when whole and aligned, else entry
+// by entry with -inf past V (the -inf bit pattern of T).
 template <typename T, bool AL>
-__device__ __forceinline__ void load_slice(const T* row, int V, int s, float (&x)[TR_PIECES * tr_epp<T>()]) {
-  constexpr int EPP = tr_epp<T>();
-  const int t = threadIdx.x;
+__device__ __forceinline__ uint4 load_chunk(const T* row, int V, int c) {
+  constexpr int EPC = tr_epc<T>();
+  const int v0 = c * EPC;
+  if (AL && v0 + EPC <= V) return *(const uint4*)(row + v0);
+  uint32_t u[4];
 #pragma unroll
-  for (int k = 0; k < TR_PIECES; ++k) {
-    const int v0 = s * tr_slice<T>() + (k * TR_THREADS + t) * EPP;
-    if (AL && v0 + EPP <= V) {
-      const uint4 w = *(const uint4*)(row + v0);
-      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int e = 0; e < EPP; ++e) {
-        if constexpr (sizeof(T) == 2)
-          x[k * EPP + e] = bf16_bits_to_f32((uint16_t)(u[e / 2] >> (16 * (e % 2))));
-        else
-          x[k * EPP + e] = __uint_as_float(u[e]);
-      }
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t lo = v0 + 2 * i < V ? (uint32_t)((const uint16_t*)row)[v0 + 2 * i] : 0xFF80u;
+      const uint32_t hi = v0 + 2 * i + 1 < V ? (uint32_t)((const uint16_t*)row)[v0 + 2 * i + 1] : 0xFF80u;
+      u[i] = lo | (hi << 16);
     } else {
-#pragma unroll
-      for (int e = 0; e < EPP; ++e) x[k * EPP + e] = v0 + e < V ? logit<T>(row, v0 + e) : -INFINITY;
+      u[i] = v0 + i < V ? __float_as_uint(((const float*)row)[v0 + i]) : 0xFF800000u;
     }
   }
+  return make_uint4(u[0], u[1], u[2], u[3]);
 }
 
 // Row r of sequence b has a usable child (depth > 0 and a token in [0, V)).
@@ -102,70 +117,141 @@ __device__ bool row_needed(const sv_accept_args& a, int b, int r) {
   return __syncthreads_or(found) != 0;
 }
 
-template <typename T, bool AL>
-__global__ void __launch_bounds__(TR_THREADS) k_thr_rows(sv_accept_args a, int S, ThrPartial* part) {
-  constexpr int E = TR_PIECES * tr_epp<T>();
-  __shared__ uint64_t s_key[TR_THREADS / 64];
-  __shared__ double s_z[TR_THREADS / 64];
-  const int s = blockIdx.x % S;
-  const int64_t rowid = blockIdx.x / S;  // b * (N + 1) + r
-  const int b = (int)(rowid / (a.N + 1)), r = (int)(rowid % (a.N + 1));
-  if (!row_needed(a, b, r)) return;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const T* row = (const T*)a.target_logits + rowid * a.V;
-  float x[E];
-  load_slice<T, AL>(row, a.V, s, x);
-  // slice maximum, lowest id first (each thread scans its ids in ascending order)
-  float m = -INFINITY;
-  int id = 0x7fffffff;
-#pragma unroll
-  for (int k = 0; k < E; ++k) {
-    const int v = s * tr_slice<T>() + ((k / tr_epp<T>()) * TR_THREADS + t) * tr_epp<T>() + k % tr_epp<T>();
-    if (x[k] > m) { m = x[k]; id = v; }
-  }
-  uint64_t key = m == -INFINITY ? 0ull : argmax_key(m, id);
-  key = wave_max_u64(key);
-  if (lane == 0) s_key[w] = key;
+// Block-wide max of 64-bit keys (s_key: one slot per wave).
+template <int NT>
+__device__ __forceinline__ uint64_t block_max_key(uint64_t k, uint64_t* s_key) {
+  k = wave_max_u64(k);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s_key[threadIdx.x >> 6] = k;
   __syncthreads();
   uint64_t best = s_key[0];
-  for (int i = 1; i < TR_THREADS / 64; ++i) best = s_key[i] > best ? s_key[i] : best;
-  // the slice maximum back from its key
-  uint32_t u = (uint32_t)(best >> 32);
-  u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
-  const float ms = __uint_as_float(u);
-  const float c = 1.4426950408889634f / a.temperature;
-  double z = 0.0;
+  for (int i = 1; i < NT / 64; ++i) best = s_key[i] > best ? s_key[i] : best;
+  return best;
+}
+
+// Argmax (lowest id on ties) of one whole row by the work-group's NT threads.
+template <typename T, bool AL, int NT>
+__device__ int row_argmax(const T* row, int V, uint64_t* s_key) {
+  constexpr int EPC = tr_epc<T>();
+  const int chunks = (V + EPC - 1) / EPC;
+  const int t = threadIdx.x;
+  uint64_t best = 0ull;
+  for (int base = 0; base < chunks; base += TR_BATCH * NT) {
+    uint4 w[TR_BATCH];
 #pragma unroll
-  for (int k = 0; k < E; ++k) z += (double)exp2f((x[k] - ms) * c);  // exp2(-inf) = 0 past V
-  z = wave_sum_f64(z);
-  if (lane == 0) s_z[w] = z;
+    for (int k = 0; k < TR_BATCH; ++k) {
+      const int c = base + k * NT + t;
+      w[k] = c < chunks ? load_chunk<T, AL>(row, V, c) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < TR_BATCH; ++k) {
+      const int c = base + k * NT + t;
+      if (c >= chunks) continue;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        const int v = c * EPC + e;
+        if (v < V) {
+          const uint64_t kk = argmax_key(chunk_entry<T>(w[k], e), v);
+          best = kk > best ? kk : best;
+        }
+      }
+    }
+  }
+  return key_id(block_max_key<NT>(best, s_key));
+}
+
+template <typename T, bool AL>
+__global__ void __launch_bounds__(RW_THREADS) k_thr_rows(sv_accept_args a, int S, ThrPartial* part) {
+  constexpr int EPC = tr_epc<T>();
+  __shared__ uint64_t s_key[RW_THREADS / 64];
+  __shared__ double s_z[RW_THREADS / 64];
+  const int64_t rowid = blockIdx.x / S;  // b * (N + 1) + r
+  const int s = blockIdx.x % S;          // part of the row: a contiguous run of its chunks
+  const int b = (int)(rowid / (a.N + 1)), r = (int)(rowid % (a.N + 1));
+  if (!row_needed(a, b, r)) return;
+  const int t = threadIdx.x;
+  const int V = a.V;
+  const T* row = (const T*)a.target_logits + rowid * V;
+  const int chunks = (V + EPC - 1) / EPC;
+  const int per = (chunks + S - 1) / S;
+  const int c0 = s * per, c1 = min(chunks, c0 + per);
+  const float c2 = 1.4426950408889634f / a.temperature;
+  float m = -INFINITY;
+  int id = 0x7fffffff;
+  double z = 0.0;
+  for (int base = c0; base < c1; base += TR_BATCH * RW_THREADS) {
+    uint4 w[TR_BATCH];
+#pragma unroll
+    for (int k = 0; k < TR_BATCH; ++k) {
+      const int c = base + k * RW_THREADS + t;
+      w[k] = c < c1 ? load_chunk<T, AL>(row, V, c) : make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
+    }
+    if constexpr (sizeof(T) == 4) {  // the fill above is the bf16 pattern; make it fp32 -inf
+#pragma unroll
+      for (int k = 0; k < TR_BATCH; ++k)
+        if (base + k * RW_THREADS + t >= c1) w[k] = make_uint4(0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u);
+    }
+    // batch maximum with its lowest id (chunks and entries in ascending id order)
+    float bm = -INFINITY;
+    int bid = 0x7fffffff;
+#pragma unroll
+    for (int k = 0; k < TR_BATCH; ++k)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        const float x = chunk_entry<T>(w[k], e);
+        if (x > bm) { bm = x; bid = (base + k * RW_THREADS + t) * EPC + e; }
+      }
+    if (bm > m) {  // the running sum follows the new maximum
+      if (m != -INFINITY) z *= (double)exp2f((m - bm) * c2);
+      m = bm;
+      id = bid;
+    }
+    if (m != -INFINITY) {
+      float zb = 0.f;
+      double zd = 0.0;
+#pragma unroll
+      for (int k = 0; k < TR_BATCH; ++k) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) zb += exp2f((chunk_entry<T>(w[k], e) - m) * c2);
+        zd += (double)zb;  // fp32 sums of one chunk, fp64 across chunks
+        zb = 0.f;
+      }
+      z += zd;
+    }
+  }
+  const uint64_t best = block_max_key<RW_THREADS>(m == -INFINITY ? 0ull : argmax_key(m, id), s_key);
+  const float M = key_val(best);
+  double zt = m == -INFINITY ? 0.0 : z * (double)exp2f((m - M) * c2);
+  zt = wave_sum_f64(zt);
+  if ((t & 63) == 0) s_z[t >> 6] = zt;
   __syncthreads();
   if (t == 0) {
-    double zt = 0.0;
-    for (int i = 0; i < TR_THREADS / 64; ++i) zt += s_z[i];
+    double tot = 0.0;
+    for (int i = 0; i < RW_THREADS / 64; ++i) tot += s_z[i];
     ThrPartial p;
-    p.m = ms;
+    p.m = best == 0ull ? -INFINITY : M;  // a part past the end of a short row holds no entry
     p.arg = key_id(best);
-    p.z = zt;
+    p.z = tot;
     part[rowid * S + s] = p;
   }
 }
 
 template <typename T, bool AL>
-__global__ void __launch_bounds__(TR_THREADS) k_thr_walk(sv_accept_args a, int S, ThrPartial* part) {
+__global__ void __launch_bounds__(RW_THREADS) k_thr_walk(sv_accept_args a, int S, ThrPartial* part) {
+  constexpr int NT = RW_THREADS;
   __shared__ int32_t s_par[SV_MAX_N], s_tok[SV_MAX_N];
   __shared__ uint8_t s_use[SV_MAX_N], s_stats[SV_MAX_N + 1];
   __shared__ double s_p[SV_MAX_N];
-  __shared__ uint64_t s_key[TR_THREADS / 64];
-  __shared__ int s_bad, s_stop;
+  __shared__ uint64_t s_key[NT / 64];
+  __shared__ int s_bad;
   const int b = blockIdx.x;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int t = threadIdx.x;
   const int N = a.N, V = a.V, Dm = a.max_depth;
   const double temp = a.temperature;
   if (t == 0) s_bad = 0;
-  for (int i = t; i <= N; i += TR_THREADS) s_stats[i] = 0;
+  for (int i = t; i <= N; i += NT) s_stats[i] = 0;
   __syncthreads();
-  for (int i = t; i < N; i += TR_THREADS) {
+  for (int i = t; i < N; i += NT) {
     const int64_t o = (int64_t)b * N + i;
     const int par = a.parents[o], tok = a.tokens[o], dep = a.depth[o];
     const bool tok_ok = tok >= 0 && tok < V;
@@ -178,8 +264,8 @@ __global__ void __launch_bounds__(TR_THREADS) k_thr_walk(sv_accept_args a, int S
   }
   __syncthreads();
   const ThrPartial* pb = part + (int64_t)b * (N + 1) * S;
-  // p_r(x) of every usable node from its parent row's merged statistics
-  for (int i = t; i < N; i += TR_THREADS) {
+  // p_r(x) of every usable node from its parent row's statistics (parts merged in fp64)
+  for (int i = t; i < N; i += NT) {
     if (!s_use[i]) continue;
     const int r = s_par[i] + 1;
     const ThrPartial* pr = pb + (int64_t)r * S;
@@ -194,7 +280,7 @@ __global__ void __launch_bounds__(TR_THREADS) k_thr_walk(sv_accept_args a, int S
   __syncthreads();
   // a node is accepted when its whole root path is usable and its score reaches the threshold
   uint64_t key = 0ull;
-  for (int i = t; i < N; i += TR_THREADS) {
+  for (int i = t; i < N; i += NT) {
     if (!s_use[i]) continue;
     double score = 1.0;
     bool ok = true;
@@ -210,20 +296,12 @@ __global__ void __launch_bounds__(TR_THREADS) k_thr_walk(sv_accept_args a, int S
       key = k > key ? k : key;
     }
   }
-  key = wave_max_u64(key);
-  if (lane == 0) s_key[w] = key;
-  __syncthreads();
-  if (t == 0) {
-    uint64_t best = 0ull;
-    for (int i = 0; i < TR_THREADS / 64; ++i) best = s_key[i] > best ? s_key[i] : best;
-    s_stop = best == 0ull ? -1 : key_id(best);
-  }
-  __syncthreads();
-  const int stop = s_stop;
+  const uint64_t best = block_max_key<NT>(key, s_key);
+  const int stop = best == 0ull ? -1 : key_id(best);
   const int srow = stop + 1;
-  // bonus: argmax of the stop row, from its partials or by a scan of the row
+  // bonus: argmax of the stop row, from its statistics or by a scan of the (leaf) row
   int bonus;
-  if (s_stats[srow]) {
+  if (s_stats[srow]) {  // parts in ascending id order: the strictly larger maximum, else the earlier part
     const ThrPartial* pr = pb + (int64_t)srow * S;
     uint64_t bk = 0ull;
     for (int q = 0; q < S; ++q)
@@ -233,28 +311,7 @@ __global__ void __launch_bounds__(TR_THREADS) k_thr_walk(sv_accept_args a, int S
       }
     bonus = key_id(bk);
   } else {
-    const T* row = (const T*)a.target_logits + ((int64_t)b * (N + 1) + srow) * V;
-    uint64_t bk = 0ull;
-    const int nsl = (V + tr_slice<T>() - 1) / tr_slice<T>();
-    for (int s = 0; s < nsl; ++s) {
-      float x[TR_PIECES * tr_epp<T>()];
-      load_slice<T, AL>(row, V, s, x);
-#pragma unroll
-      for (int k = 0; k < TR_PIECES * tr_epp<T>(); ++k) {
-        const int v = s * tr_slice<T>() + ((k / tr_epp<T>()) * TR_THREADS + t) * tr_epp<T>() + k % tr_epp<T>();
-        if (v < V) {
-          const uint64_t kk = argmax_key(x[k], v);
-          bk = kk > bk ? kk : bk;
-        }
-      }
-    }
-    bk = wave_max_u64(bk);
-    __syncthreads();
-    if (lane == 0) s_key[w] = bk;
-    __syncthreads();
-    uint64_t best = s_key[0];
-    for (int i = 1; i < TR_THREADS / 64; ++i) best = s_key[i] > best ? s_key[i] : best;
-    bonus = key_id(best);
+    bonus = row_argmax<T, AL, NT>((const T*)a.target_logits + ((int64_t)b * (N + 1) + srow) * V, V, s_key);
   }
   // outputs: the stop node's root path, root-most first
   if (t == 0) {
@@ -273,32 +330,37 @@ __global__ void __launch_bounds__(TR_THREADS) k_thr_walk(sv_accept_args a, int S
   __syncthreads();
   ThrPartial* pw = part + (int64_t)b * (N + 1) * S;
   const ThrPartial zero = {0.f, 0, 0.0};
-  for (int i = t; i < (N + 1) * S; i += TR_THREADS) pw[i] = zero;
+  for (int i = t; i < (N + 1) * S; i += NT) pw[i] = zero;
 }
 
 }  // namespace
 
+// Parts per row: about a thousand work-groups in all (one part per row for large batches, up to
+// 8 parts of a row for small ones, where one work-group per row would leave most CUs idle).
+int thr_parts(const sv_accept_args& a) {
+  const int64_t rows = (int64_t)a.B * (a.N + 1);
+  int64_t S = (1024 + rows - 1) / rows;
+  return (int)(S < 1 ? 1 : (S > 8 ? 8 : S));
+}
+
 size_t sv_threshold_workspace(const sv_accept_args& a) {
-  const int slice = a.logits_dtype == SV_BF16 ? tr_slice<uint16_t>() : tr_slice<float>();
-  const size_t S = (size_t)((a.V + slice - 1) / slice);
-  return ((size_t)a.B * (a.N + 1) * S * sizeof(ThrPartial) + 255) / 256 * 256;
+  return ((size_t)a.B * (a.N + 1) * thr_parts(a) * sizeof(ThrPartial) + 255) / 256 * 256;
 }
 
 sv_status sv_threshold_launch(const sv_accept_args& a, hipStream_t st) {
   if (!(a.threshold >= 0.f && a.threshold <= 1.f)) return SV_ERR_INVALID_ARGUMENT;
   if (a.workspace_bytes < sv_threshold_workspace(a)) return SV_ERR_INVALID_ARGUMENT;
   const bool bf = a.logits_dtype == SV_BF16;
-  const int slice = bf ? tr_slice<uint16_t>() : tr_slice<float>();
-  const int S = (a.V + slice - 1) / slice;
-  const int64_t blocks = (int64_t)a.B * (a.N + 1) * S;
-  if (blocks > 0x7fffffff) return SV_ERR_UNSUPPORTED;
+  const int S = thr_parts(a);
+  const int64_t rows = (int64_t)a.B * (a.N + 1);
+  if (rows * S > 0x7fffffff) return SV_ERR_UNSUPPORTED;
   ThrPartial* part = (ThrPartial*)a.workspace;
   const size_t esz = bf ? 2 : 4;
   const bool al = ((size_t)a.V * esz) % 16 == 0 && ((uintptr_t)a.target_logits % 16) == 0;
-#define SV_THR(T, AL)                                                                              \
-  do {                                                                                             \
-    hipLaunchKernelGGL((k_thr_rows<T, AL>), dim3((unsigned)blocks), dim3(TR_THREADS), 0, st, a, S, part); \
-    hipLaunchKernelGGL((k_thr_walk<T, AL>), dim3((unsigned)a.B), dim3(TR_THREADS), 0, st, a, S, part);   \
+#define SV_THR(T, AL)                                                                                   \
+  do {                                                                                                  \
+    hipLaunchKernelGGL((k_thr_rows<T, AL>), dim3((unsigned)(rows * S)), dim3(RW_THREADS), 0, st, a, S, part); \
+    hipLaunchKernelGGL((k_thr_walk<T, AL>), dim3((unsigned)a.B), dim3(RW_THREADS), 0, st, a, S, part);       \
   } while (0)
   if (bf) {
     if (al) SV_THR(uint16_t, true); else SV_THR(uint16_t, false);
