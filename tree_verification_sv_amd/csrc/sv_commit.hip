@@ -13,11 +13,12 @@
 //                        writes new_len / committed_slots / status.
 //  k_kv_commit_rows      one work-group per (sequence, run of layers), every KV
 //                        head: the layer-batched commit and the in-place
-//                        compaction of cache-resident tree rows.  Each round
-//                        loads its source rows into registers and waits for
-//                        them before any destination row is written, so a path
-//                        in any node order compacts correctly, and rows that
-//                        are already in place are skipped.
+//                        compaction of cache-resident tree rows.  One wave
+//                        moves one (layer, head) plane: it loads all of the
+//                        plane's source rows into registers and waits for them
+//                        before writing any destination row, so a path in any
+//                        node order compacts correctly; rows already in place
+//                        are skipped.
 //  k_kv_commit_finalize  one work-group per sequence, launched after
 //                        k_kv_commit_rows: writes new_len / committed_slots /
 //                        status (new_len may alias prefix_len, which every
@@ -145,19 +146,101 @@ __global__ void __launch_bounds__(256) k_kv_commit(sv_commit_args a, CommitPlan 
   write_outputs(a, b, c);
 }
 
-// 16-byte chunks moved per round: 8 per thread, all loaded into registers before any is
-// stored.  One (layer, KV head) unit needs at most SV_MAX_DEPTH rows x 32 chunks x 2 (K and V)
-// = 1024 of them, so a round holds at least two whole units.
-constexpr int CM_THREADS = 256;
-constexpr int CM_CPT = 8;
-constexpr int ROUND_CHUNKS = CM_THREADS * CM_CPT;
+// Addresses of the layered commit: head h of a row sits hstride rows after head 0 (paged:
+// within its block; contiguous: the next head's plane), so every chunk's address is a base
+// row of its position k plus multiples of strides -- no 64-bit division per chunk.
+struct CommitRows {
+  int64_t src[SV_MAX_DEPTH], dst[SV_MAX_DEPTH];  // row of KV head 0 for accepted position k
+};
 
-// One work-group per (sequence, run of `lpw` layers): every (layer, KV head) unit of the run
-// moves its accepted rows.  Units are processed in rounds of whole units: every source chunk
-// of a round is loaded (and waited for) before the barrier and stored after it, so a
-// compaction inside one cache plane never overwrites a row it still has to read.
+__device__ void commit_rows(const sv_commit_args& a, int b, const CommitCheck& c, CommitRows& r) {
+  const int t = threadIdx.x;
+  if (t < c.A) {
+    r.dst[t] = cache_row(a, b, 0, c.dst[t]);
+    r.src[t] = a.tree_in_cache ? cache_row(a, b, 0, c.src[t]) : (int64_t)b * a.Hkv * (a.N + 1) + c.src[t];
+  }
+  __syncthreads();
+}
+
+// Chunk y of a (layer, head) unit: K or V, accepted position k, 16-byte chunk ch of the row.
+struct UnitChunk {
+  const char* src;
+  char* dst;
+  bool move;
+};
+__device__ __forceinline__ UnitChunk unit_chunk(const sv_commit_args& a, const CommitPlan& p, const CommitCheck& c,
+                                                const CommitRows& r, int layer, int h, int y, int A) {
+  const int64_t hstride = a.paged ? a.block_size : a.Lcap;
+  const int64_t tstride = a.tree_in_cache ? hstride : (int64_t)(a.N + 1);
+  const int64_t row_bytes = (int64_t)a.D * p.es;
+  const int kv = y / (A * p.cpr), k = (y / p.cpr) % A, ch = y % p.cpr;
+  UnitChunk u;
+  u.move = !(a.tree_in_cache && c.src[k] == c.dst[k]);  // a row already in place stays
+  const char* sb = a.tree_in_cache ? (const char*)(kv ? a.v_cache : a.k_cache) + layer * a.cache_layer_stride * p.es
+                                   : (const char*)(kv ? a.v_tree : a.k_tree) + layer * a.tree_layer_stride * p.es;
+  char* db = (char*)(kv ? a.v_cache : a.k_cache) + layer * a.cache_layer_stride * p.es;
+  u.src = sb + (r.src[k] + h * tstride) * row_bytes + ch * 16;
+  u.dst = db + (r.dst[k] + h * hstride) * row_bytes + ch * 16;
+  return u;
+}
+
+// Small units (at most 64 * CM_CPL chunks: bf16 D 128 up to 8 accepted rows, D 64 up to 16):
+// one work-group per (sequence, run of `lpw` layers); its four waves take batches of whole
+// (layer, KV head) units in turn; every lane loads its chunks of the batch into registers,
+// the wave waits for all of them, then stores.  Rows of one cache plane are only ever touched
+// by the wave that owns the unit, so an in-place compaction never overwrites a row it still
+// has to read, and waves never wait for each other.
+constexpr int CM_THREADS = 256;
+constexpr int CM_CPL = 4;  // chunks per lane per batch (more would spill the addresses)
+
 __global__ void __launch_bounds__(CM_THREADS) k_kv_commit_rows(sv_commit_args a, CommitPlan p, int lpw, int layers) {
   __shared__ CommitCheck c;
+  __shared__ CommitRows r;
+  const int b = blockIdx.x;
+  const int l0 = blockIdx.y * lpw;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  commit_check(a, b, c);
+  if (c.code != 0) return;
+  const int A = c.A;
+  const int nl = min(lpw, layers - l0);
+  if (A == 0 || nl <= 0) return;
+  commit_rows(a, b, c, r);
+  const int per_unit = A * p.cpr * 2;        // <= 64 * CM_CPL on this path
+  const int upb = (64 * CM_CPL) / per_unit;  // whole units per wave batch (>= 1)
+  const int units = nl * a.Hkv;
+  for (int u0 = wv * upb; u0 < units; u0 += (CM_THREADS / 64) * upb) {
+    const int nb = min(upb, units - u0) * per_unit;
+    uint4 v[CM_CPL];
+#pragma unroll
+    for (int i = 0; i < CM_CPL; ++i) {
+      const int x = lane + i * 64;
+      if (x >= nb) continue;
+      const int u = u0 + x / per_unit;
+      const UnitChunk q = unit_chunk(a, p, c, r, l0 + u / a.Hkv, u % a.Hkv, x % per_unit, A);
+      if (q.move) v[i] = *(const uint4*)q.src;
+    }
+    // every load of the batch's units has returned before any of their stores
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < CM_CPL; ++i) {
+      const int x = lane + i * 64;
+      if (x >= nb) continue;
+      const int u = u0 + x / per_unit;
+      const UnitChunk q = unit_chunk(a, p, c, r, l0 + u / a.Hkv, u % a.Hkv, x % per_unit, A);
+      if (q.move) *(uint4*)q.dst = v[i];
+    }
+  }
+}
+
+// Large units (up to 1024 chunks): rounds of whole units staged in LDS; every source chunk of a
+// round is in LDS before the barrier and written after it.
+constexpr int STAGE_CHUNKS = 2048;
+
+__global__ void __launch_bounds__(CM_THREADS) k_kv_commit_rows_lds(sv_commit_args a, CommitPlan p, int lpw,
+                                                                   int layers) {
+  __shared__ CommitCheck c;
+  __shared__ CommitRows r;
+  __shared__ uint4 stage[STAGE_CHUNKS];
   const int b = blockIdx.x;
   const int l0 = blockIdx.y * lpw;
   const int t = threadIdx.x;
@@ -166,40 +249,22 @@ __global__ void __launch_bounds__(CM_THREADS) k_kv_commit_rows(sv_commit_args a,
   const int A = c.A;
   const int nl = min(lpw, layers - l0);
   if (A == 0 || nl <= 0) return;
-  const int64_t row_bytes = (int64_t)a.D * p.es;
-  const int per_unit = A * p.cpr * 2;                 // K and V chunks of one (layer, head)
-  const int upr = ROUND_CHUNKS / per_unit;            // units per round (>= 2)
+  commit_rows(a, b, c, r);
+  const int per_unit = A * p.cpr * 2;
+  const int upr = STAGE_CHUNKS / per_unit;  // units per round (>= 2)
   const int units = nl * a.Hkv;
   for (int u0 = 0; u0 < units; u0 += upr) {
     const int n = min(upr, units - u0) * per_unit;
-    uint4 v[CM_CPT];
-    int64_t dst[CM_CPT];  // byte offset of the destination chunk in its cache, -1 when none
-    bool isv[CM_CPT];
-#pragma unroll
-    for (int i = 0; i < CM_CPT; ++i) {
-      const int x = t + i * CM_THREADS;
-      dst[i] = -1;
-      isv[i] = false;
-      if (x >= n) continue;
-      const int u = u0 + x / per_unit, y = x % per_unit;
-      const int layer = l0 + u / a.Hkv, h = u % a.Hkv;
-      const int kv = y / (A * p.cpr), k = (y / p.cpr) % A, ch = y % p.cpr;
-      if (a.tree_in_cache && c.src[k] == c.dst[k]) continue;  // already in place
-      const char* base = a.tree_in_cache ? (const char*)(kv ? a.v_cache : a.k_cache) + layer * a.cache_layer_stride * p.es
-                                         : (const char*)(kv ? a.v_tree : a.k_tree) + layer * a.tree_layer_stride * p.es;
-      const int64_t src_row = a.tree_in_cache ? cache_row(a, b, h, c.src[k])
-                                              : ((int64_t)b * a.Hkv + h) * (a.N + 1) + c.src[k];
-      v[i] = *((const uint4*)(base + src_row * row_bytes) + ch);
-      dst[i] = layer * a.cache_layer_stride * p.es + cache_row(a, b, h, c.dst[k]) * row_bytes + (int64_t)ch * 16;
-      isv[i] = kv != 0;
+    for (int x = t; x < n; x += CM_THREADS) {
+      const int u = u0 + x / per_unit;
+      const UnitChunk q = unit_chunk(a, p, c, r, l0 + u / a.Hkv, u % a.Hkv, x % per_unit, A);
+      if (q.move) stage[x] = *(const uint4*)q.src;
     }
-    // every load of the round has returned before any store of the work-group
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < CM_CPT; ++i) {
-      if (dst[i] < 0) continue;
-      *(uint4*)((char*)(isv[i] ? a.v_cache : a.k_cache) + dst[i]) = v[i];
+    for (int x = t; x < n; x += CM_THREADS) {
+      const int u = u0 + x / per_unit;
+      const UnitChunk q = unit_chunk(a, p, c, r, l0 + u / a.Hkv, u % a.Hkv, x % per_unit, A);
+      if (q.move) *(uint4*)q.dst = stage[x];
     }
     __syncthreads();
   }
@@ -248,7 +313,12 @@ extern "C" sv_status sv_kv_commit(const sv_commit_args* args, void* stream) {
     int lpw = (int)(((int64_t)a.B * layers + 1023) / 1024);
     if (lpw < 1) lpw = 1;
     const int runs = (layers + lpw - 1) / lpw;
-    hipLaunchKernelGGL(k_kv_commit_rows, dim3((unsigned)a.B, (unsigned)runs), dim3(CM_THREADS), 0, s, a, p, lpw, layers);
+    // the largest unit this call can have: max_depth accepted rows
+    if (a.max_depth * p.cpr * 2 <= 64 * CM_CPL)
+      hipLaunchKernelGGL(k_kv_commit_rows, dim3((unsigned)a.B, (unsigned)runs), dim3(CM_THREADS), 0, s, a, p, lpw, layers);
+    else
+      hipLaunchKernelGGL(k_kv_commit_rows_lds, dim3((unsigned)a.B, (unsigned)runs), dim3(CM_THREADS), 0, s, a, p, lpw,
+                         layers);
     hipLaunchKernelGGL(k_kv_commit_finalize, dim3(a.B), dim3(64), 0, s, a);
   }
   return sv_launch_status();

@@ -61,7 +61,9 @@ __global__ void __launch_bounds__(256) k_build_tree_mask(const int32_t* __restri
     uint64_t* arow = anc_bits + ((int64_t)b * N + t) * W;
     int32_t* prow = path_rows ? path_rows + ((int64_t)b * (N + 1) + (t + 1)) * max_depth : nullptr;
     if (code == 0) {
-      for (int w = 0; w < W; ++w) arow[w] = bits[w];
+#pragma unroll
+      for (int w = 0; w < SV_MAX_W; ++w)  // constant indices keep the bitset in registers
+        if (w < W) arow[w] = bits[w];
       depth_out[(int64_t)b * N + t] = count;
       if (prow) {
         // the walk from t visits depths count, count-1, ..., 1
