@@ -243,6 +243,9 @@ def main():
     ap.add_argument("--no-overlap", action="store_true",
                     help="run the four stages back to back on one stream (default: acceptance and commit on a "
                          "side stream beside the attention, forked after the mask)")
+    ap.add_argument("--attention-side", action="store_true",
+                    help="overlapped step with the attention on the side stream and acceptance + commit on the "
+                         "launch stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--acceptance", choices=["greedy", "stochastic", "topk", "threshold"], default=None,
                     help="acceptance rule (default: the workload's own)")
@@ -289,7 +292,7 @@ def main():
 
     ov = not args.no_overlap
     for i in range(args.warmup):
-        steps[i % R].run(overlap=ov)
+        steps[i % R].run(overlap=ov, attention_side=args.attention_side)
     torch.cuda.synchronize()
     if args.copy_mib:  # untimed reference copy: its FETCH/WRITE counters calibrate the byte counts
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
@@ -308,13 +311,13 @@ def main():
             side.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(side):
                 for s in steps:
-                    s.run(overlap=ov)
+                    s.run(overlap=ov, attention_side=args.attention_side)
             torch.cuda.current_stream().wait_stream(side)
             torch.cuda.synchronize()
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph):
                 for s in steps:
-                    s.run(overlap=ov)
+                    s.run(overlap=ov, attention_side=args.attention_side)
             torch.cuda.synchronize()
             for _ in range(2):
                 graph.replay()
@@ -335,10 +338,10 @@ def main():
         for _ in range(reps):
             graph.replay()
         for i in range(K - reps * R):
-            steps[i].run(overlap=ov)
+            steps[i].run(overlap=ov, attention_side=args.attention_side)
     else:
         for i in range(K):
-            steps[i % R].run(overlap=ov)
+            steps[i % R].run(overlap=ov, attention_side=args.attention_side)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0

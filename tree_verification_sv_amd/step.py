@@ -119,7 +119,7 @@ class VerifyStep:
     def kv_commit(self, stream=None):
         _check(self._L.sv_kv_commit(ctypes.byref(self._com), _stream(stream)), "sv_kv_commit")
 
-    def run(self, stream=None, overlap=False, accept_first=False):
+    def run(self, stream=None, overlap=False, accept_first=False, attention_side=False):
         if not overlap:
             self.build_mask(stream)
             self.attention(stream)
@@ -135,7 +135,13 @@ class VerifyStep:
         # with the tree rows in the cache the commit moves rows the attention reads,
         # so it follows the join instead of running beside the attention
         late_commit = self.x.tree_in_cache
-        if accept_first:
+        if attention_side and not late_commit:
+            # acceptance -> commit stay on the caller's stream right after the mask (no
+            # cross-stream wait on the longer branch); the attention takes the side stream
+            self.attention(side)
+            self.accept(main)
+            self.kv_commit(main)
+        elif accept_first:
             self.accept(side)
             if not late_commit:
                 self.kv_commit(side)
