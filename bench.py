@@ -1,10 +1,12 @@
 """Benchmark of one tree-verification step on one MI355X.
 
 A step is the whole hot path on one batch: sv_build_tree_mask, then
-sv_tree_attention on the launch stream (issued first) beside sv_accept ->
-sv_kv_commit on a side stream (both read only the mask outputs and the inputs; the commit writes
-cache slots the attention does not read), joined at the end of the step
-(--no-overlap: all four back to back on one stream).  The
+sv_tree_attention on the launch stream (issued first) beside sv_accept on a side
+stream, whose walker also commits the accepted path into the cache (the
+sv_kv_commit work inside the acceptance launch; --separate-commit: its own
+launch after sv_accept), joined at the end of the step (--no-overlap: all on one
+stream).  Both branches read only the mask outputs and the inputs; the commit
+writes cache slots the attention does not read.  The
 default workload is the EAGLE-style static tree at the Llama-3-8B attention
 shape (batch 1, 32 query / 8 KV heads, head_dim 128, 4096-token bf16 prefix,
 60-node tree of depth 6, vocab 128256, stochastic acceptance at T = 1).
@@ -246,6 +248,9 @@ def main():
     ap.add_argument("--attention-side", action="store_true",
                     help="overlapped step with the attention on the side stream and acceptance + commit on the "
                          "launch stream")
+    ap.add_argument("--separate-commit", action="store_true",
+                    help="commit with its own sv_kv_commit launch (default: the acceptance kernel commits the "
+                         "accepted path itself, one launch less; not with --tree-in-cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--acceptance", choices=["greedy", "stochastic", "topk", "threshold"], default=None,
                     help="acceptance rule (default: the workload's own)")
@@ -288,6 +293,10 @@ def main():
     w0 = ws[0]
     devs = [W.to_device(w, dev) for w in ws]
     steps = [VerifyStep(W.step_inputs(w, d)) for w, d in zip(ws, devs)]
+    fused = not args.separate_commit and not args.tree_in_cache
+    if fused:
+        for s_ in steps:
+            s_.fuse_commit(True)
     stream = torch.cuda.current_stream()
 
     ov = not args.no_overlap
@@ -404,7 +413,8 @@ def main():
                    "launch": "hip_graph" if use_graph else "eager",
                    "streams": ("attention | accept after mask, commit after both" if w0.tree_in_cache else
                                "attention | accept+commit after mask") if ov else "one",
-                   "tree_kv": "in cache at prefix_len + t" if w0.tree_in_cache else "separate rows"},
+                   "tree_kv": "in cache at prefix_len + t" if w0.tree_in_cache else "separate rows",
+                   "commit": "inside the acceptance kernel" if fused else "sv_kv_commit"},
         "accept_steps_per_s": round(B / (ms_step * 1e-3), 1),
         "hbm_gbs": round(hbm_gbs, 1),
         "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),

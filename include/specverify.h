@@ -246,6 +246,12 @@ typedef struct sv_accept_args {
   void* workspace;
   size_t workspace_bytes;
   float threshold;  /* mode 3 only */
+  /* nullable: the acceptance kernel also commits each sequence's accepted path, as
+   * sv_kv_commit(commit) would after it (same checks and outputs), from the work-group that
+   * found the path -- one launch less.  Its B, N and max_depth must equal these; only a
+   * single layer with the tree rows in their own tensor (else SV_ERR_UNSUPPORTED); the
+   * struct is read at call time.  The commit writes cache positions >= prefix_len only. */
+  const struct sv_commit_args* commit;
 } sv_accept_args;
 size_t sv_accept_workspace(const sv_accept_args* args);
 sv_status sv_accept(const sv_accept_args* args, void* stream);

@@ -69,7 +69,7 @@ class sv_accept_args(ctypes.Structure):
                 ("u_accept", ctypes.c_void_p), ("u_sample", ctypes.c_void_p), ("accept_len", ctypes.c_void_p),
                 ("accept_rows", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p), ("num_out", ctypes.c_void_p),
                 ("stop_row", ctypes.c_void_p), ("status", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t), ("threshold", ctypes.c_float)]
+                ("workspace_bytes", ctypes.c_size_t), ("threshold", ctypes.c_float), ("commit", ctypes.c_void_p)]
 
 
 class sv_commit_args(ctypes.Structure):

@@ -55,7 +55,7 @@
 
 #include <type_traits>
 
-#include "sv_common.h"
+#include "sv_commit_dev.h"
 
 namespace {
 
@@ -458,7 +458,8 @@ __device__ __forceinline__ void load_pieces(const T* row, int s0, int V, bool al
 // ALIGNED: every logits row starts on 16 bytes (decided on the host; a compile-time choice
 // keeps the two load paths from meeting in one register assignment)
 template <typename T, int MODE, bool ALIGNED>
-__global__ void __launch_bounds__(ac_threads<MODE>(), 2) k_accept(sv_accept_args a, int32_t G, AccWs ws) {
+__global__ void __launch_bounds__(ac_threads<MODE>(), 2) k_accept(sv_accept_args a, int32_t G, AccWs ws,
+                                                                  sv_commit_args cm, int32_t has_cm) {
   constexpr int TH = ac_threads<MODE>(), NW = TH / 64;
   // STO: a rejection walk (modes 1 and 2); TOPK: deterministic drafts (q = point mass per child)
   constexpr bool STO = MODE != SV_GREEDY, TOPK = MODE == SV_TOPK_DRAFT;
@@ -940,6 +941,7 @@ __global__ void __launch_bounds__(ac_threads<MODE>(), 2) k_accept(sv_accept_args
           if (t < Dm) a.accept_rows[(int64_t)b * Dm + t] = t < A ? si.path[t] + 1 : 0;
           if (t <= Dm)
             a.out_tokens[(int64_t)b * (Dm + 1) + t] = t < A ? si.tok[si.path[t]] : (t == A ? bonus : 0);
+          if (has_cm) svc::walker_commit(cm, b, A, si.path);  // the accepted path into the cache
           if (incr && t == 0) st_u32(cancel, 1u);  // the sequence's remaining rows are not needed
           if (!incr)  // every row result of b has been read: leave them cleared for the next call
             for (int x = t; x <= N; x += TH) st_u64(&rr[x], 0ull);
@@ -1039,6 +1041,7 @@ __global__ void __launch_bounds__(ac_threads<MODE>(), 2) k_accept(sv_accept_args
           if (t < Dm) a.accept_rows[(int64_t)b * Dm + t] = t < A ? si.path[t] + 1 : 0;
           if (t <= Dm)
             a.out_tokens[(int64_t)b * (Dm + 1) + t] = t < A ? a.tokens[(int64_t)b * N + si.path[t]] : (t == A ? bonus : 0);
+          if (has_cm) svc::walker_commit(cm, b, A, si.path);  // the accepted path into the cache
         }
       }
     }
@@ -1136,9 +1139,16 @@ extern "C" sv_status sv_accept(const sv_accept_args* args, void* stream) {
   if (!a.parents || !a.tokens || !a.anc_bits || !a.depth || !a.target_logits || !a.accept_len || !a.accept_rows ||
       !a.out_tokens || !a.num_out || !a.stop_row || !a.status || !a.workspace)
     return SV_ERR_INVALID_ARGUMENT;
+  sv_commit_args cm{};
+  if (a.commit) {  // the walker commits the accepted path itself
+    const sv_status cs = svc::walker_commit_ok(*a.commit, a.B, a.N, a.max_depth);
+    if (cs != SV_OK) return cs;
+    cm = *a.commit;
+  }
+  const int32_t has_cm = a.commit != nullptr;
   if (a.mode == SV_THRESHOLD) {
     if ((uintptr_t)a.workspace % 256) return SV_ERR_INVALID_ARGUMENT;
-    return sv_threshold_launch(a, (hipStream_t)stream);
+    return sv_threshold_launch(a, cm, has_cm, (hipStream_t)stream);
   }
   if (a.mode == SV_STOCHASTIC && !a.draft_logits) return SV_ERR_INVALID_ARGUMENT;
   if (a.mode != SV_GREEDY && (!a.u_accept || !a.u_sample || !(a.temperature > 0.f))) return SV_ERR_INVALID_ARGUMENT;
@@ -1164,7 +1174,8 @@ extern "C" sv_status sv_accept(const sv_accept_args* args, void* stream) {
   const size_t esz = a.logits_dtype == SV_BF16 ? 2 : 4;
   const bool aligned = ((size_t)a.V * esz) % 16 == 0 && ((uintptr_t)a.target_logits % 16) == 0 &&
                        (a.mode != SV_STOCHASTIC || ((uintptr_t)a.draft_logits % 16) == 0);
-#define SV_ACC_LAUNCH(T, M, AL) hipLaunchKernelGGL((k_accept<T, M, AL>), grid, dim3(ac_threads<M>()), 0, st, a, G, ws)
+#define SV_ACC_LAUNCH(T, M, AL) \
+  hipLaunchKernelGGL((k_accept<T, M, AL>), grid, dim3(ac_threads<M>()), 0, st, a, G, ws, cm, has_cm)
   if (a.logits_dtype == SV_BF16) {
     if (a.mode == SV_STOCHASTIC) { if (aligned) SV_ACC_LAUNCH(uint16_t, SV_STOCHASTIC, true); else SV_ACC_LAUNCH(uint16_t, SV_STOCHASTIC, false); }
     else if (a.mode == SV_TOPK_DRAFT) { if (aligned) SV_ACC_LAUNCH(uint16_t, SV_TOPK_DRAFT, true); else SV_ACC_LAUNCH(uint16_t, SV_TOPK_DRAFT, false); }

@@ -23,7 +23,7 @@
 //                        k_kv_commit_rows: writes new_len / committed_slots /
 //                        status (new_len may alias prefix_len, which every
 //                        k_kv_commit_rows work-group has read by then).
-#include "sv_common.h"
+#include "sv_commit_dev.h"
 
 namespace {
 
@@ -39,24 +39,9 @@ struct CommitCheck {
   int64_t src[SV_MAX_DEPTH];  // source: tree row (separate tree rows) or cache slot (tree_in_cache)
 };
 
-__device__ __forceinline__ int64_t capacity(const sv_commit_args& a) {
-  return a.paged ? (int64_t)a.max_blocks * a.block_size : (int64_t)a.Lcap;
-}
-
-// Logical position -> slot of sequence b (checked: 0 ok, else a status code).
-__device__ __forceinline__ int32_t slot_of(const sv_commit_args& a, int b, int64_t pos, int64_t* slot) {
-  if (a.paged) {
-    const int64_t blk = pos / a.block_size;
-    if (blk >= a.max_blocks) return SV_SEQ_CAPACITY;
-    const int32_t id = a.block_table[(int64_t)b * a.max_blocks + blk];
-    if (id < 1 || id >= a.num_blocks) return SV_SEQ_BLOCK;
-    *slot = (int64_t)id * a.block_size + pos % a.block_size;
-  } else {
-    if (pos >= a.Lcap) return SV_SEQ_CAPACITY;
-    *slot = pos;
-  }
-  return 0;
-}
+using svc::cache_row;
+using svc::capacity;
+using svc::slot_of;
 
 // Checks of one sequence, one thread per accepted position (all loads issued at once):
 // L >= 0 and 0 <= A <= max_depth (1); with cache-resident tree rows L + N within the
@@ -99,14 +84,6 @@ __device__ void commit_check(const sv_commit_args& a, int b, CommitCheck& c) {
   __syncthreads();
 }
 
-// Row index (in rows of D elements) of slot `slot`, KV head h, sequence b, within one layer's cache.
-__device__ __forceinline__ int64_t cache_row(const sv_commit_args& a, int b, int h, int64_t slot) {
-  if (a.paged) {
-    const int64_t id = slot / a.block_size, off = slot % a.block_size;
-    return (id * a.Hkv + h) * a.block_size + off;
-  }
-  return ((int64_t)b * a.Hkv + h) * a.Lcap + slot;
-}
 
 __device__ void write_outputs(const sv_commit_args& a, int b, const CommitCheck& c) {
   const int t = threadIdx.x;

@@ -46,4 +46,4 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // Threshold acceptance (sv_threshold.hip): workspace bytes and launch of both kernels.
 size_t sv_threshold_workspace(const sv_accept_args& a);
-sv_status sv_threshold_launch(const sv_accept_args& a, hipStream_t stream);
+sv_status sv_threshold_launch(const sv_accept_args& a, const sv_commit_args& cm, int32_t has_cm, hipStream_t stream);

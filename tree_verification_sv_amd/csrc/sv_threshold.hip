@@ -31,7 +31,7 @@
 #include <float.h>
 #include <math.h>
 
-#include "sv_common.h"
+#include "sv_commit_dev.h"
 
 namespace {
 
@@ -237,13 +237,15 @@ __global__ void __launch_bounds__(RW_THREADS) k_thr_rows(sv_accept_args a, int S
 }
 
 template <typename T, bool AL>
-__global__ void __launch_bounds__(RW_THREADS) k_thr_walk(sv_accept_args a, int S, ThrPartial* part) {
+__global__ void __launch_bounds__(RW_THREADS) k_thr_walk(sv_accept_args a, int S, ThrPartial* part,
+                                                          sv_commit_args cm, int32_t has_cm) {
   constexpr int NT = RW_THREADS;
   __shared__ int32_t s_par[SV_MAX_N], s_tok[SV_MAX_N];
   __shared__ uint8_t s_use[SV_MAX_N], s_stats[SV_MAX_N + 1];
   __shared__ double s_p[SV_MAX_N];
   __shared__ uint64_t s_key[NT / 64];
-  __shared__ int s_bad;
+  __shared__ int s_bad, s_A;
+  __shared__ int32_t s_path[SV_MAX_DEPTH];
   const int b = blockIdx.x;
   const int t = threadIdx.x;
   const int N = a.N, V = a.V, Dm = a.max_depth;
@@ -318,6 +320,8 @@ __global__ void __launch_bounds__(RW_THREADS) k_thr_walk(sv_accept_args a, int S
     int pathn[SV_MAX_DEPTH];
     int A = 0;
     for (int cur = stop; cur >= 0 && A < SV_MAX_DEPTH; cur = s_par[cur]) pathn[A++] = cur;
+    for (int k = 0; k < A; ++k) s_path[k] = pathn[A - 1 - k];
+    s_A = A;
     for (int k = 0; k < Dm; ++k) a.accept_rows[(int64_t)b * Dm + k] = k < A ? pathn[A - 1 - k] + 1 : 0;
     for (int k = 0; k <= Dm; ++k)
       a.out_tokens[(int64_t)b * (Dm + 1) + k] = k < A ? s_tok[pathn[A - 1 - k]] : (k == A ? bonus : 0);
@@ -326,8 +330,9 @@ __global__ void __launch_bounds__(RW_THREADS) k_thr_walk(sv_accept_args a, int S
     a.stop_row[b] = srow;
     a.status[b] = s_bad ? SV_SEQ_TOKEN : 0;
   }
-  // leave the workspace zeroed for the next call
   __syncthreads();
+  if (has_cm) svc::walker_commit(cm, b, s_A, s_path);  // the accepted path into the cache
+  // leave the workspace zeroed for the next call
   ThrPartial* pw = part + (int64_t)b * (N + 1) * S;
   const ThrPartial zero = {0.f, 0, 0.0};
   for (int i = t; i < (N + 1) * S; i += NT) pw[i] = zero;
@@ -347,7 +352,7 @@ size_t sv_threshold_workspace(const sv_accept_args& a) {
   return ((size_t)a.B * (a.N + 1) * thr_parts(a) * sizeof(ThrPartial) + 255) / 256 * 256;
 }
 
-sv_status sv_threshold_launch(const sv_accept_args& a, hipStream_t st) {
+sv_status sv_threshold_launch(const sv_accept_args& a, const sv_commit_args& cm, int32_t has_cm, hipStream_t st) {
   if (!(a.threshold >= 0.f && a.threshold <= 1.f)) return SV_ERR_INVALID_ARGUMENT;
   if (a.workspace_bytes < sv_threshold_workspace(a)) return SV_ERR_INVALID_ARGUMENT;
   const bool bf = a.logits_dtype == SV_BF16;
@@ -360,7 +365,8 @@ sv_status sv_threshold_launch(const sv_accept_args& a, hipStream_t st) {
 #define SV_THR(T, AL)                                                                                   \
   do {                                                                                                  \
     hipLaunchKernelGGL((k_thr_rows<T, AL>), dim3((unsigned)(rows * S)), dim3(RW_THREADS), 0, st, a, S, part); \
-    hipLaunchKernelGGL((k_thr_walk<T, AL>), dim3((unsigned)a.B), dim3(RW_THREADS), 0, st, a, S, part);       \
+    hipLaunchKernelGGL((k_thr_walk<T, AL>), dim3((unsigned)a.B), dim3(RW_THREADS), 0, st, a, S, part, cm,     \
+                       has_cm);                                                                                \
   } while (0)
   if (bf) {
     if (al) SV_THR(uint16_t, true); else SV_THR(uint16_t, false);

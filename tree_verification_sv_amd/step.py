@@ -92,6 +92,7 @@ class VerifyStep:
                                 self.commit["status"], x.block_table, x.paged, x.num_blocks, x.commit_mode,
                                 x.tree_in_cache, N)
         self._L = lib()
+        self._fused = False
         self._side = None
         self._ev_fork = self._ev_join = None
 
@@ -117,7 +118,17 @@ class VerifyStep:
         _check(self._L.sv_accept(ctypes.byref(self._acc), _stream(stream)), "sv_accept")
 
     def kv_commit(self, stream=None):
+        if self._fused:  # done by the acceptance kernel
+            return
         _check(self._L.sv_kv_commit(ctypes.byref(self._com), _stream(stream)), "sv_kv_commit")
+
+    def fuse_commit(self, on: bool = True):
+        """Let the acceptance kernel commit the accepted path itself (one launch less); kv_commit()
+        and run() then skip the separate commit.  Not with the tree rows in the cache."""
+        if on and self.x.tree_in_cache:
+            raise ValueError("the fused commit needs the tree rows in their own tensor")
+        self._acc.commit = ctypes.addressof(self._com) if on else None
+        self._fused = on
 
     def run(self, stream=None, overlap=False, accept_first=False, attention_side=False):
         if not overlap:
