@@ -76,3 +76,49 @@ def test_overlapped_step_and_graph_replays(cfg, over):
         bad = _diff(_snapshot(step, dev), ref)
         assert not bad, f"graph replay {i} differs in {bad}"
     del g, step, dev
+
+
+@pytest.mark.parametrize("cfg,over", [(2, {}), (3, dict(B=5, L=(40, 400), V=2500, N=32)), (5, dict(B=2, L=290, V=1500))])
+def test_fused_commit_overlapped_and_graph_replays(cfg, over):
+    """The benchmark's mode: the acceptance kernel commits, the attention runs beside it, the
+    step is a replayed graph; every output equals the one-stream step with a separate commit."""
+    import torch
+    from tree_verification_sv_amd.step import VerifyStep
+    w = W.config(cfg, **over)
+    print(f"[gpu] fused-commit step modes: {w.name} B={w.B} N={w.N} V={w.V} mode={w.mode}", flush=True)
+    dev = W.to_device(w, "cuda:0")
+    step = VerifyStep(W.step_inputs(w, dev))
+    step.run()
+    torch.cuda.synchronize()
+    ref = _snapshot(step, dev)
+
+    def clobber():
+        step.out.zero_()
+        for v in list(step.acc.values()) + list(step.commit.values()):
+            v.fill_(-7)
+        torch.cuda.synchronize()
+
+    step.fuse_commit(True)
+    for kw in (dict(), dict(overlap=True), dict(overlap=True, attention_side=True)):
+        clobber()
+        step.run(**kw)
+        torch.cuda.synchronize()
+        bad = _diff(_snapshot(step, dev), ref)
+        assert not bad, f"fused commit {kw} differs in {bad}"
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step.run(overlap=True)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step.run(overlap=True)
+    torch.cuda.synchronize()
+    for i in range(4):
+        clobber()
+        g.replay()
+        torch.cuda.synchronize()
+        bad = _diff(_snapshot(step, dev), ref)
+        assert not bad, f"fused-commit graph replay {i} differs in {bad}"
+    del g, step, dev
