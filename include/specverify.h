@@ -7,10 +7,15 @@
  *   sv_build_tree_mask  parent array -> ancestor bitsets, depths, path rows
  *   sv_tree_attention   ancestor-masked GQA attention of the draft-tree query
  *                       tokens over a contiguous or paged KV prefix
- *   sv_accept           greedy argmax matching, or full-distribution rejection
+ *   sv_accept           greedy argmax matching, full-distribution rejection
  *                       sampling with the residual normalize(max(0, p - q)),
- *                       plus the bonus token
+ *                       deterministic (top-K) drafts or threshold acceptance,
+ *                       plus the bonus token (it can also run the commit)
  *   sv_kv_commit        copy the accepted branch's KV rows into the cache
+ *
+ * Around the step: sv_outcome_lookup and sv_saguaro_reweight (speculative
+ * speculative decoding) and sv_draft_subset_logits (drafters on a vocabulary
+ * subset).
  *
  * Sources (web pages, cited by title and section):
  *  [EP]  "EAGLE-Pangu: Accelerator-Safe Tree Speculative Decoding on Ascend

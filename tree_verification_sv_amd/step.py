@@ -1,10 +1,10 @@
-"""One verification step: the four library calls in dependency order.
+"""One verification step: the library calls in dependency order.
 
 ``VerifyStep`` owns the output and workspace buffers (allocated once through
-torch), so repeated ``run()`` calls allocate nothing and issue exactly four
-C-ABI calls: sv_build_tree_mask -> sv_tree_attention -> sv_accept ->
-sv_kv_commit.  Nothing here computes; it marshals arguments and orders
-streams.
+torch), so repeated ``run()`` calls allocate nothing and issue the C-ABI calls
+sv_build_tree_mask -> sv_tree_attention -> sv_accept -> sv_kv_commit, or, after
+``fuse_commit()``, three calls with the commit done inside sv_accept.  Nothing
+here computes; it marshals arguments and orders streams.
 
 Attention and acceptance both read only the mask outputs and the step's
 inputs, and the commit writes cache slots at positions >= prefix_len, which
@@ -14,7 +14,8 @@ the caller's stream, and the caller's stream waits for the side stream at the
 end (a fork/join that HIP graph capture records as a DAG).  The attention is
 issued first by default (``accept_first=False``): measured on MI355X, the step
 is shorter when the attention's work-groups take the compute units first and
-the acceptance fills them as they free up.
+the acceptance fills them as they free up.  With the tree rows in the cache the
+commit moves rows the attention reads, so it follows the join.
 """
 from __future__ import annotations
 
