@@ -92,7 +92,7 @@ def load_traffic(kernel, kernel_src_hash, workload):
     return d.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, budget_s=10.0, variant=None):
+def cpu_baseline(cfg, budget_s=10.0, variant=None, over=None):
     """The CPU oracle as it stands, one host thread, on one step of the same workload.
 
     Mask, acceptance and commit run on the whole batch.  The attention runs on a
@@ -102,7 +102,7 @@ def cpu_baseline(cfg, budget_s=10.0, variant=None):
     """
     import oracle
     import workloads as W
-    w = W.config(cfg, seed=cfg * 1000)
+    w = W.config(cfg, seed=cfg * 1000, **(over or {}))
     if variant is not None:
         w = variant(w)
     total_rows = w.B * w.N * w.Hq
@@ -240,6 +240,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--batch", type=int, default=0,
+                    help="override the workload's batch (sequences of the same shape, each with its own tree)")
     ap.add_argument("--instances", type=int, default=0, help="input instances cycled (0: enough to defeat the MALL)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--no-overlap", action="store_true",
@@ -276,13 +278,14 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda:0"
-    w0 = W.config(args.config)
+    over = {"B": args.batch} if args.batch else {}
+    w0 = W.config(args.config, **over)
     # bytes one instance touches: the prefix K/V it reads plus its logits rows
     step_bytes_est = w0.target_logits.nbytes * 2 + int(w0.prefix_len.sum()) * w0.Hkv * w0.D * 2 * (2 if w0.dtype == "bf16" else 4)
     R = args.instances or max(1, min(32, int(np.ceil(2 * MALL_BYTES / max(step_bytes_est, 1)))))
     print(f"[bench] workload {w0.name} B={w0.B} N={w0.N} L={int(w0.prefix_len.max())} V={w0.V} "
           f"instances={R} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
-    ws = [w0] + [W.config(args.config, seed=args.config * 1000 + r) for r in range(1, R)]
+    ws = [w0] + [W.config(args.config, seed=args.config * 1000 + r, **over) for r in range(1, R)]
     def variant(w):
         if args.acceptance:
             w.mode = args.acceptance
@@ -432,7 +435,7 @@ def main():
         result["extras"] = extras
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on one step", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(args.config, variant=variant)
+        result["cpu_baseline"] = cpu_baseline(args.config, variant=variant, over=over)
     print(json.dumps(result), flush=True)
 
 
