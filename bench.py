@@ -194,7 +194,8 @@ def commit_layers(w, dev, acc, layers, K):
 
 
 def time_extras(w, dev, acc, K_steps):
-    """Time the operations around the step on this workload's shape (HIP events, K launches each):
+    """Time the operations around the step on this workload's shape (HIP events over a replayed
+    graph of K launches each):
     the SSD outcome lookup (8 prepared outcomes of max_depth tokens per sequence), Saguaro
     reweighting (8 cached tokens per row of the draft logits) and the draft vocabulary subset
     (a 32000-id subset laid out over the target vocabulary)."""
@@ -208,14 +209,27 @@ def time_extras(w, dev, acc, K_steps):
     res = {}
 
     def timed(fn):
+        """Average device time of one call: K_steps calls captured in a HIP graph and replayed,
+        so that the host's per-call overhead (larger than these small kernels) is not timed."""
         for _ in range(3):
             fn()
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(K_steps):
+                fn()
+        g.replay()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s = torch.cuda.current_stream()
         a.record(s)
-        for _ in range(K_steps):
-            fn()
+        g.replay()
         b.record(s)
         torch.cuda.synchronize()
         return a.elapsed_time(b) / K_steps
