@@ -281,6 +281,9 @@ def main():
     ap.add_argument("--separate-commit", action="store_true",
                     help="commit with its own sv_kv_commit launch (default: the acceptance kernel commits the "
                          "accepted path itself, one launch less; not with --tree-in-cache)")
+    ap.add_argument("--mask-free-accept", action="store_true",
+                    help="stochastic / top-K: the acceptance derives node depths from the parents itself and its "
+                         "branch forks before the mask")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--acceptance", choices=["greedy", "stochastic", "topk", "threshold"], default=None,
                     help="acceptance rule (default: the workload's own)")
@@ -328,6 +331,10 @@ def main():
     if fused:
         for s_ in steps:
             s_.fuse_commit(True)
+    mask_free = args.mask_free_accept and w0.mode in ("stochastic", "topk")
+    if mask_free:
+        for s_ in steps:
+            s_.mask_free_accept(True)
     stream = torch.cuda.current_stream()
 
     ov = not args.no_overlap
@@ -443,6 +450,7 @@ def main():
                    **({"threshold": w0.threshold} if w0.mode == "threshold" else {}),
                    "launch": "hip_graph" if use_graph else "eager",
                    "streams": ("attention | accept after mask, commit after both" if w0.tree_in_cache else
+                               "mask+attention | accept+commit" if mask_free else
                                "attention | accept+commit after mask") if ov else "one",
                    "tree_kv": "in cache at prefix_len + t" if w0.tree_in_cache else "separate rows",
                    "commit": "inside the acceptance kernel" if fused else "sv_kv_commit"},

@@ -62,7 +62,10 @@ namespace {
 // threads per work-group: 512 for greedy rows (half the work-groups of 256-thread ones,
 // fewer to dispatch), 256 for stochastic rows (smaller barriers and bonus scans, and the
 // residual staging fits two work-groups per compute unit)
-template <int MODE> constexpr int ac_threads() { return MODE == SV_GREEDY ? 512 : 256; }
+#ifndef SV_ACC_STO_THREADS
+#define SV_ACC_STO_THREADS 256
+#endif
+template <int MODE> constexpr int ac_threads() { return MODE == SV_GREEDY ? 512 : SV_ACC_STO_THREADS; }
 constexpr int AC_NWMAX = 8;                    // waves per work-group at most
 // vocabulary entries per thread: 8 pieces of 16 bytes (64 bf16 / 32 fp32 logits), so a
 // work-group's slice is 8 * 16 bytes per thread
@@ -323,7 +326,7 @@ __device__ __forceinline__ SeqRaw seq_fetch(const sv_accept_args& a, int b) {
     const int64_t i = (int64_t)b * a.N + t;
     r.tok = a.tokens[i];
     r.par = a.parents[i];
-    r.dep = a.depth[i];
+    r.dep = a.depth ? a.depth[i] : 0;
   }
   return r;
 }
@@ -335,13 +338,35 @@ __device__ __forceinline__ void seq_facts(const sv_accept_args& a, const SeqRaw&
   if (t == 0) si.bad_token = 0;
   __syncthreads();
   bool u = false;
+  const int pr = sr.par;
+  const bool prange = pr >= -1 && pr < N;
+  if (t < N) {
+    // an out-of-range parent is staged as -2 (only usable nodes' parents are read later)
+    si.par[t] = (int16_t)(prange ? pr : -2);
+    si.tok[t] = sr.tok;
+  }
+  int dep = sr.dep;
+  if (!a.depth) {  // uniform: no depth array, derive it from the staged parents
+    // the rule of the tree mask: the number of nodes on the root path when the walk reaches
+    // parent -1 through in-range parents within max_depth nodes, else 0 (a cycle never
+    // reaches -1, so it ends on the depth limit)
+    __syncthreads();
+    dep = 0;
+    if (t < N) {
+      int cur = t, cnt = 1;
+      for (int s = 0; s < SV_MAX_DEPTH; ++s) {  // at most max_depth - 1 <= 15 steps up
+        const int p = si.par[cur];
+        if (p == -1) { dep = cnt; break; }
+        if (p < 0 || cnt >= a.max_depth) break;
+        ++cnt;
+        cur = p;
+      }
+    }
+  }
   if (t < N) {
     const bool ok = sr.tok >= 0 && sr.tok < a.V;
     if (!ok) si.bad_token = 1;  // every writer stores the same value
-    const int pr = sr.par;
-    u = ok && sr.dep > 0 && pr >= -1 && pr < N;
-    si.par[t] = (int16_t)pr;
-    si.tok[t] = sr.tok;
+    u = ok && dep > 0 && prange;
     if (u) si.haskid[pr + 1] = 1;
   }
   if (t < SV_MAX_N) si.usable[t] = u;
@@ -1136,7 +1161,9 @@ extern "C" sv_status sv_accept(const sv_accept_args* args, void* stream) {
   if (a.mode == SV_THRESHOLD && (!(a.temperature > 0.f) || !(a.threshold >= 0.f && a.threshold <= 1.f)))
     return SV_ERR_INVALID_ARGUMENT;
   if (a.B == 0) return SV_OK;
-  if (!a.parents || !a.tokens || !a.anc_bits || !a.depth || !a.target_logits || !a.accept_len || !a.accept_rows ||
+  // modes 1 and 2 read neither mask output when depth is NULL (depths come from the parents)
+  const bool mask_free = (a.mode == SV_STOCHASTIC || a.mode == SV_TOPK_DRAFT) && !a.depth;
+  if (!a.parents || !a.tokens || (!mask_free && (!a.anc_bits || !a.depth)) || !a.target_logits || !a.accept_len || !a.accept_rows ||
       !a.out_tokens || !a.num_out || !a.stop_row || !a.status || !a.workspace)
     return SV_ERR_INVALID_ARGUMENT;
   sv_commit_args cm{};

@@ -23,8 +23,8 @@ import ctypes
 from dataclasses import dataclass
 from typing import Optional
 
-from . import (SV_COMMIT_PATH, SV_STOCHASTIC, _check, _stream, accept_args, accept_outputs, attn_args, commit_args,
-               lib, sv_accept_workspace, sv_tree_attention_workspace)
+from . import (SV_COMMIT_PATH, SV_STOCHASTIC, SV_TOPK_DRAFT, _check, _stream, accept_args, accept_outputs, attn_args,
+               commit_args, lib, sv_accept_workspace, sv_tree_attention_workspace)
 
 
 @dataclass
@@ -94,6 +94,7 @@ class VerifyStep:
                                 x.tree_in_cache, N)
         self._L = lib()
         self._fused = False
+        self._mask_free = False
         self._side = None
         self._ev_fork = self._ev_join = None
 
@@ -131,6 +132,16 @@ class VerifyStep:
         self._acc.commit = ctypes.addressof(self._com) if on else None
         self._fused = on
 
+    def mask_free_accept(self, on: bool = True):
+        """Let the acceptance derive node depths from the parent array itself (modes "stochastic"
+        and "topk" only: sv_accept gets NULL anc_bits and depth), so that it does not wait for the
+        mask; run(overlap=True) then forks before the mask and the acceptance branch starts at once."""
+        if on and self._acc.mode not in (SV_STOCHASTIC, SV_TOPK_DRAFT):
+            raise ValueError("only the stochastic and top-K modes can accept without the mask outputs")
+        self._acc.anc_bits = None if on else self.mask["anc_bits"].data_ptr()
+        self._acc.depth = None if on else self.mask["depth"].data_ptr()
+        self._mask_free = on
+
     def run(self, stream=None, overlap=False, accept_first=False, attention_side=False):
         if not overlap:
             self.build_mask(stream)
@@ -141,12 +152,26 @@ class VerifyStep:
         import torch
         main = stream if stream is not None else torch.cuda.current_stream()
         side = self._side_stream()
-        self.build_mask(main)
-        self._ev_fork.record(main)
-        side.wait_event(self._ev_fork)
         # with the tree rows in the cache the commit moves rows the attention reads,
         # so it follows the join instead of running beside the attention
         late_commit = self.x.tree_in_cache
+        if self._mask_free:
+            # the acceptance reads no mask output: its branch forks before the mask
+            self._ev_fork.record(main)
+            side.wait_event(self._ev_fork)
+            self.accept(side)
+            if not late_commit:
+                self.kv_commit(side)
+            self.build_mask(main)
+            self.attention(main)
+            self._ev_join.record(side)
+            main.wait_event(self._ev_join)
+            if late_commit:
+                self.kv_commit(main)
+            return
+        self.build_mask(main)
+        self._ev_fork.record(main)
+        side.wait_event(self._ev_fork)
         if attention_side and not late_commit:
             # acceptance -> commit stay on the caller's stream right after the mask (no
             # cross-stream wait on the longer branch); the attention takes the side stream
