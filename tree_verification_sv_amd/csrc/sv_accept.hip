@@ -20,7 +20,8 @@
 // parallel, and the walk is a pointer chase over the per-row results.
 //
 // Work decomposition.  A group of G work-groups resolves one row; each of TH
-// threads (512 greedy, 256 stochastic) owns a slice of TH * 128 bytes of the
+// threads (512 greedy; 256, or 512 in large batches, for the walk modes) owns a
+// slice of TH * 128 bytes of the
 // vocabulary.  Thread t owns the 16-byte pieces k * TH + t (k = 0 .. 7) of its
 // slice, so every load instruction of a wave reads 1 KB of consecutive logits.
 // The exponentials are computed once into registers; each later pass over the row (a
@@ -60,12 +61,16 @@
 namespace {
 
 // threads per work-group: 512 for greedy rows (half the work-groups of 256-thread ones,
-// fewer to dispatch), 256 for stochastic rows (smaller barriers and bonus scans, and the
-// residual staging fits two work-groups per compute unit)
-#ifndef SV_ACC_STO_THREADS
-#define SV_ACC_STO_THREADS 256
-#endif
-template <int MODE> constexpr int ac_threads() { return MODE == SV_GREEDY ? 512 : SV_ACC_STO_THREADS; }
+// fewer to dispatch); stochastic and top-K rows take 256 (smaller barriers and bonus scans,
+// and the residual staging fits two work-groups per compute unit) unless the batch has at
+// least AC_WIDE_ROWS rows, where 512 (half the work-groups, one per compute unit for the
+// 155 KB of LDS) measured faster on MI355X: a 4112-row outcome-tree batch 3.51 -> 3.08 ms
+// per step, while 768- and 976-row batches were 3-5% slower and batch-1 trees 13% slower
+constexpr int AC_WIDE_ROWS = 2048;
+int acc_threads(const sv_accept_args& a) {
+  if (a.mode == SV_GREEDY) return 512;
+  return (int64_t)a.B * (a.N + 1) >= AC_WIDE_ROWS ? 512 : 256;
+}
 constexpr int AC_NWMAX = 8;                    // waves per work-group at most
 // vocabulary entries per thread: 8 pieces of 16 bytes (64 bf16 / 32 fp32 logits), so a
 // work-group's slice is 8 * 16 bytes per thread
@@ -326,7 +331,9 @@ __device__ __forceinline__ SeqRaw seq_fetch(const sv_accept_args& a, int b) {
     const int64_t i = (int64_t)b * a.N + t;
     r.tok = a.tokens[i];
     r.par = a.parents[i];
-    r.dep = a.depth ? a.depth[i] : 0;
+    // without a depth array the load takes the parents (the value is then unused): an
+    // unconditional load keeps the kernel free of scratch
+    r.dep = (a.depth ? a.depth : a.parents)[i];
   }
   return r;
 }
@@ -338,11 +345,9 @@ __device__ __forceinline__ void seq_facts(const sv_accept_args& a, const SeqRaw&
   if (t == 0) si.bad_token = 0;
   __syncthreads();
   bool u = false;
-  const int pr = sr.par;
-  const bool prange = pr >= -1 && pr < N;
   if (t < N) {
     // an out-of-range parent is staged as -2 (only usable nodes' parents are read later)
-    si.par[t] = (int16_t)(prange ? pr : -2);
+    si.par[t] = (int16_t)(sr.par >= -1 && sr.par < N ? sr.par : -2);
     si.tok[t] = sr.tok;
   }
   int dep = sr.dep;
@@ -354,6 +359,7 @@ __device__ __forceinline__ void seq_facts(const sv_accept_args& a, const SeqRaw&
     dep = 0;
     if (t < N) {
       int cur = t, cnt = 1;
+#pragma unroll 1
       for (int s = 0; s < SV_MAX_DEPTH; ++s) {  // at most max_depth - 1 <= 15 steps up
         const int p = si.par[cur];
         if (p == -1) { dep = cnt; break; }
@@ -363,10 +369,11 @@ __device__ __forceinline__ void seq_facts(const sv_accept_args& a, const SeqRaw&
       }
     }
   }
-  if (t < N) {
-    const bool ok = sr.tok >= 0 && sr.tok < a.V;
+  if (t < N) {  // the thread's own staged values (no barrier needed to read them back)
+    const int pr = si.par[t], tok = si.tok[t];
+    const bool ok = tok >= 0 && tok < a.V;
     if (!ok) si.bad_token = 1;  // every writer stores the same value
-    u = ok && dep > 0 && prange;
+    u = ok && dep > 0 && pr != -2;
     if (u) si.haskid[pr + 1] = 1;
   }
   if (t < SV_MAX_N) si.usable[t] = u;
@@ -482,10 +489,10 @@ __device__ __forceinline__ void load_pieces(const T* row, int s0, int V, bool al
 // ---------------------------------------------------------------- the kernel
 // ALIGNED: every logits row starts on 16 bytes (decided on the host; a compile-time choice
 // keeps the two load paths from meeting in one register assignment)
-template <typename T, int MODE, bool ALIGNED>
-__global__ void __launch_bounds__(ac_threads<MODE>(), 2) k_accept(sv_accept_args a, int32_t G, AccWs ws,
+template <typename T, int MODE, bool ALIGNED, int TH>
+__global__ void __launch_bounds__(TH, 2) k_accept(sv_accept_args a, int32_t G, AccWs ws,
                                                                   sv_commit_args cm, int32_t has_cm) {
-  constexpr int TH = ac_threads<MODE>(), NW = TH / 64;
+  constexpr int NW = TH / 64;
   // STO: a rejection walk (modes 1 and 2); TOPK: deterministic drafts (q = point mass per child)
   constexpr bool STO = MODE != SV_GREEDY, TOPK = MODE == SV_TOPK_DRAFT;
   constexpr int E = Piece<T>::E, NK = Piece<T>::NK;
@@ -1112,10 +1119,7 @@ __global__ void __launch_bounds__(ac_threads<MODE>(), 2) k_accept(sv_accept_args
 }
 
 int groups_G(const sv_accept_args& a) {
-  const bool st = a.mode != SV_GREEDY;  // both walk modes share the 256-thread layout
-  const int slice = a.logits_dtype == SV_BF16
-                        ? (st ? ac_slice<uint16_t, ac_threads<SV_STOCHASTIC>()>() : ac_slice<uint16_t, ac_threads<SV_GREEDY>()>())
-                        : (st ? ac_slice<float, ac_threads<SV_STOCHASTIC>()>() : ac_slice<float, ac_threads<SV_GREEDY>()>());
+  const int slice = acc_threads(a) * (a.logits_dtype == SV_BF16 ? ac_ct<uint16_t>() : ac_ct<float>());
   const int G = (a.V + slice - 1) / slice;
   return G < 1 ? 1 : G;
 }
@@ -1140,6 +1144,17 @@ WsLayout ws_layout(const sv_accept_args& a) {
   l.xs = o; o = up(o + NG * G * 2 * sizeof(XSlot));
   l.total = o;
   return l;
+}
+
+template <typename T, int M, bool AL>
+void launch_accept(int TH, dim3 grid, hipStream_t st, const sv_accept_args& a, int G, const AccWs& ws,
+                   const sv_commit_args& cm, int32_t has_cm) {
+  if constexpr (M == SV_GREEDY) {
+    hipLaunchKernelGGL((k_accept<T, M, AL, 512>), grid, dim3(512), 0, st, a, G, ws, cm, has_cm);
+  } else {
+    if (TH == 512) hipLaunchKernelGGL((k_accept<T, M, AL, 512>), grid, dim3(512), 0, st, a, G, ws, cm, has_cm);
+    else hipLaunchKernelGGL((k_accept<T, M, AL, 256>), grid, dim3(256), 0, st, a, G, ws, cm, has_cm);
+  }
 }
 
 }  // namespace
@@ -1201,8 +1216,8 @@ extern "C" sv_status sv_accept(const sv_accept_args* args, void* stream) {
   const size_t esz = a.logits_dtype == SV_BF16 ? 2 : 4;
   const bool aligned = ((size_t)a.V * esz) % 16 == 0 && ((uintptr_t)a.target_logits % 16) == 0 &&
                        (a.mode != SV_STOCHASTIC || ((uintptr_t)a.draft_logits % 16) == 0);
-#define SV_ACC_LAUNCH(T, M, AL) \
-  hipLaunchKernelGGL((k_accept<T, M, AL>), grid, dim3(ac_threads<M>()), 0, st, a, G, ws, cm, has_cm)
+  const int TH = acc_threads(a);
+#define SV_ACC_LAUNCH(T, M, AL) launch_accept<T, M, AL>(TH, grid, st, a, G, ws, cm, has_cm)
   if (a.logits_dtype == SV_BF16) {
     if (a.mode == SV_STOCHASTIC) { if (aligned) SV_ACC_LAUNCH(uint16_t, SV_STOCHASTIC, true); else SV_ACC_LAUNCH(uint16_t, SV_STOCHASTIC, false); }
     else if (a.mode == SV_TOPK_DRAFT) { if (aligned) SV_ACC_LAUNCH(uint16_t, SV_TOPK_DRAFT, true); else SV_ACC_LAUNCH(uint16_t, SV_TOPK_DRAFT, false); }
