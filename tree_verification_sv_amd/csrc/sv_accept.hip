@@ -62,14 +62,17 @@ namespace {
 
 // threads per work-group: 512 for greedy rows (half the work-groups of 256-thread ones,
 // fewer to dispatch); stochastic and top-K rows take 256 (smaller barriers and bonus scans,
-// and the residual staging fits two work-groups per compute unit) unless the batch has at
-// least AC_WIDE_ROWS rows, where 512 (half the work-groups, one per compute unit for the
-// 155 KB of LDS) measured faster on MI355X: a 4112-row outcome-tree batch 3.51 -> 3.08 ms
-// per step, while 768- and 976-row batches were 3-5% slower and batch-1 trees 13% slower
+// and the residual staging fits two work-groups per compute unit) except for batches of
+// wide trees (N >= AC_WIDE_N, where the walk cancels most rows) with at least AC_WIDE_ROWS
+// rows, where 512 (half the work-groups, one per compute unit for the 155 KB of LDS) measured
+// faster on MI355X: 256-node trees at batch 16 (4112 rows) 3.38 -> 2.93 ms per step, at batch
+// 8 even; 60-node trees were slower with 512 at every batch (batch 64, 3904 rows: 1.11 ->
+// 1.18 ms; batch 1: 13%), and so were 768-row chains
 constexpr int AC_WIDE_ROWS = 2048;
+constexpr int AC_WIDE_N = 128;
 int acc_threads(const sv_accept_args& a) {
   if (a.mode == SV_GREEDY) return 512;
-  return (int64_t)a.B * (a.N + 1) >= AC_WIDE_ROWS ? 512 : 256;
+  return a.N >= AC_WIDE_N && (int64_t)a.B * (a.N + 1) >= AC_WIDE_ROWS ? 512 : 256;
 }
 constexpr int AC_NWMAX = 8;                    // waves per work-group at most
 // vocabulary entries per thread: 8 pieces of 16 bytes (64 bf16 / 32 fp32 logits), so a
