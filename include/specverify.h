@@ -69,6 +69,7 @@ typedef int32_t sv_status;
 #define SV_OK 0
 #define SV_ERR_INVALID_ARGUMENT 1
 #define SV_ERR_UNSUPPORTED 2
+#define SV_ERR_BAD_TREE 3          /* SV_FLAG_VALIDATE: a sequence's device status is non-zero (read back by the call) */
 #define SV_ERR_HIP 4
 
 /* element types */
@@ -80,6 +81,15 @@ typedef int32_t sv_status;
 #define SV_STOCHASTIC 1
 #define SV_TOPK_DRAFT 2
 #define SV_THRESHOLD 3
+
+/* call flags.  SV_FLAG_VALIDATE selects the reference mode of [EP] sec. 2
+ * ("Metodologia": a reference mode with invariant checks next to the fast
+ * fused path): the call additionally checks its inputs, waits for the stream,
+ * reads the per-sequence status back and returns SV_ERR_BAD_TREE when any
+ * sequence reports a non-zero code.  It synchronises the stream (so it is
+ * rejected with SV_ERR_INVALID_ARGUMENT while the stream is being captured).
+ * Without it (performance mode) a call only enqueues work. */
+#define SV_FLAG_VALIDATE 1u
 
 /* commit modes ([EP] sec. 2: length-based or path-index-based commit) */
 #define SV_COMMIT_PATH 0
@@ -94,6 +104,7 @@ typedef int32_t sv_status;
 #define SV_SEQ_BLOCK 5          /* a needed block-table entry is 0 (ghost) or outside the pool */
 #define SV_SEQ_CAPACITY 6       /* prefix_len (+ accepted rows) exceeds the cache capacity */
 #define SV_SEQ_TIMEOUT 7        /* sv_accept: a bounded wait between cooperating work-groups expired */
+#define SV_SEQ_NONFINITE 8      /* sv_accept: a logits row holds NaN or +Inf, or no finite entry */
 
 /*
  * sv_build_tree_mask -- tree tensorisation ([EP] sec. 2, "Semantica de
@@ -111,12 +122,15 @@ typedef int32_t sv_status;
  *   status    [B] int32: 0, or the smallest code among the sequence's nodes.
  * Checks per node while walking up (in this order): parent in [-1, N) (code
  * 1), parent not already on the walk (code 2), path length <= max_depth
- * (code 3).  An invalid node gets anc_bits = {i}, depth 0 and an all-ghost
- * path row; valid nodes are unaffected by invalid ones.
+ * (code 3).  The walk stops at the first failing check, so a cycle longer
+ * than max_depth reports code 3.  An invalid node gets anc_bits = {i}, depth
+ * 0 and an all-ghost path row; valid nodes are unaffected by invalid ones.
+ * flags: 0, or SV_FLAG_VALIDATE (wait, read status back, SV_ERR_BAD_TREE for
+ * a malformed tree in any sequence).
  */
 sv_status sv_build_tree_mask(const int32_t* parents, int32_t B, int32_t N, int32_t max_depth,
                              uint64_t* anc_bits, int32_t* depth, int32_t* path_rows, int32_t* status,
-                             void* stream);
+                             uint32_t flags, void* stream);
 
 /*
  * sv_tree_attention -- ancestor-masked GQA attention of the tree's query
@@ -227,7 +241,17 @@ sv_status sv_tree_attention(const sv_attn_args* args, void* stream);
  * Outputs (device, int32): accept_len [B] (A), accept_rows [B, max_depth]
  *   (rows of the accepted path, root-most first, ghost-0 padded), out_tokens
  *   [B, max_depth+1] (accepted tokens then the bonus, 0 padded), num_out [B]
- *   (A+1), stop_row [B], status [B] (4 if some token id is out of range).
+ *   (A+1), stop_row [B], status [B] (4 if some token id is out of range; 8
+ *   if the walk reached a row whose statistics are not finite, see below).
+ * Non-finite logits.  Modes 1 and 2 check every row they resolve: a row whose
+ *   softmax normaliser is not a finite positive number (a NaN or +Inf logit,
+ *   or no finite entry; -Inf entries alone are probability 0 and allowed)
+ *   accepts no child and gives bonus 0, and a walk that stops there reports
+ *   status 8.  With SV_FLAG_VALIDATE (flags) every row of target_logits (and
+ *   of draft_logits in mode 1) is scanned after the acceptance: a row with a
+ *   NaN or +Inf entry, or with no finite entry, sets status 8 for its
+ *   sequence unless an earlier code is set; the call then waits for the
+ *   stream and returns SV_ERR_BAD_TREE if any status is non-zero.
  * workspace: at least sv_accept_workspace(args) bytes, 256-byte aligned,
  *   zero-filled by the caller before its first use; every call leaves it
  *   zeroed again.  Calls that overlap in time must not share a workspace.
@@ -260,11 +284,15 @@ typedef struct sv_accept_args {
    * sv_kv_commit(commit) would after it (same checks and outputs), from the work-group that
    * found the path -- one launch less.  Its B, N and max_depth must equal these; only a
    * single layer with the tree rows in their own tensor (else SV_ERR_UNSUPPORTED); the
-   * struct is read at call time.  The commit writes cache positions >= prefix_len only. */
+   * struct is read at call time.  The commit writes cache positions >= prefix_len only, but it
+   * writes new_len, so new_len must not alias prefix_len while anything that reads prefix_len
+   * (sv_tree_attention) may still run beside it. */
   const struct sv_commit_args* commit;
+  uint32_t flags;   /* 0 or SV_FLAG_VALIDATE */
 } sv_accept_args;
 size_t sv_accept_workspace(const sv_accept_args* args);
 sv_status sv_accept(const sv_accept_args* args, void* stream);
+
 
 /*
  * sv_kv_commit -- append the accepted branch's KV to the cache ([EP] sec. 2,

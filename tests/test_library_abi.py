@@ -33,11 +33,11 @@ def test_library_exports_every_declared_symbol():
 def test_bad_arguments_rejected_without_launch():
     L = sv.lib()
     # N = 0, max_depth = 0 and N > 256 are argument errors
-    assert L.sv_build_tree_mask(None, 1, 0, 4, None, None, None, None, None) == sv.SV_ERR_INVALID_ARGUMENT
-    assert L.sv_build_tree_mask(None, 1, 4, 0, None, None, None, None, None) == sv.SV_ERR_INVALID_ARGUMENT
-    assert L.sv_build_tree_mask(None, 1, 257, 4, None, None, None, None, None) == sv.SV_ERR_INVALID_ARGUMENT
+    assert L.sv_build_tree_mask(None, 1, 0, 4, None, None, None, None, 0, None) == sv.SV_ERR_INVALID_ARGUMENT
+    assert L.sv_build_tree_mask(None, 1, 4, 0, None, None, None, None, 0, None) == sv.SV_ERR_INVALID_ARGUMENT
+    assert L.sv_build_tree_mask(None, 1, 257, 4, None, None, None, None, 0, None) == sv.SV_ERR_INVALID_ARGUMENT
     # B = 0 is a no-op
-    assert L.sv_build_tree_mask(None, 0, 4, 4, None, None, None, None, None) == sv.SV_OK
+    assert L.sv_build_tree_mask(None, 0, 4, 4, None, None, None, None, 0, None) == sv.SV_OK
     a = sv.sv_attn_args()
     a.B, a.N, a.Hq, a.Hkv, a.D, a.dtype, a.scale = 1, 4, 8, 3, 128, sv.SV_BF16, 0.088
     assert L.sv_tree_attention(ctypes.byref(a), None) == sv.SV_ERR_INVALID_ARGUMENT  # Hq % Hkv

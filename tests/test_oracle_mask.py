@@ -33,7 +33,7 @@ def _relabel(parents, perm):
     return out
 
 
-@pytest.mark.parametrize("case", range(7))
+@pytest.mark.parametrize("case", range(9))
 def test_golden_cases(case):
     c = golden("tree_mask_cases.json")["cases"][case]
     par = np.array([c["parents"]], dtype=np.int32)

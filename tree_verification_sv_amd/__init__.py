@@ -18,11 +18,13 @@ _ROOT = os.path.dirname(_HERE)
 LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 _lib = None
 
-SV_OK, SV_ERR_INVALID_ARGUMENT, SV_ERR_UNSUPPORTED, SV_ERR_HIP = 0, 1, 2, 4
+SV_OK, SV_ERR_INVALID_ARGUMENT, SV_ERR_UNSUPPORTED, SV_ERR_BAD_TREE, SV_ERR_HIP = 0, 1, 2, 3, 4
 SV_F32, SV_BF16 = 0, 1
 SV_GREEDY, SV_STOCHASTIC, SV_TOPK_DRAFT, SV_THRESHOLD = 0, 1, 2, 3
 _MODES = {"greedy": SV_GREEDY, "stochastic": SV_STOCHASTIC, "topk": SV_TOPK_DRAFT, "threshold": SV_THRESHOLD}
 SV_COMMIT_PATH, SV_COMMIT_LENGTH = 0, 1
+SV_FLAG_VALIDATE = 1
+SV_SEQ_NONFINITE = 8
 
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -69,7 +71,8 @@ class sv_accept_args(ctypes.Structure):
                 ("u_accept", ctypes.c_void_p), ("u_sample", ctypes.c_void_p), ("accept_len", ctypes.c_void_p),
                 ("accept_rows", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p), ("num_out", ctypes.c_void_p),
                 ("stop_row", ctypes.c_void_p), ("status", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t), ("threshold", ctypes.c_float), ("commit", ctypes.c_void_p)]
+                ("workspace_bytes", ctypes.c_size_t), ("threshold", ctypes.c_float), ("commit", ctypes.c_void_p),
+                ("flags", ctypes.c_uint32)]
 
 
 class sv_commit_args(ctypes.Structure):
@@ -107,7 +110,7 @@ def lib():
                                   "tree_verification_sv_amd.build()")
         L = ctypes.CDLL(LIB_PATH)
         P, i32 = ctypes.c_void_p, ctypes.c_int32
-        L.sv_build_tree_mask.argtypes = [P, i32, i32, i32, P, P, P, P, P]
+        L.sv_build_tree_mask.argtypes = [P, i32, i32, i32, P, P, P, P, ctypes.c_uint32, P]
         L.sv_build_tree_mask.restype = i32
         L.sv_tree_attention_workspace.argtypes = [ctypes.POINTER(sv_attn_args)]
         L.sv_tree_attention_workspace.restype = ctypes.c_size_t
@@ -183,8 +186,10 @@ def _alloc_workspace(nbytes, device):
 
 
 # ------------------------------------------------------------ entry points
-def sv_build_tree_mask(parents, max_depth: int, out: Optional[dict] = None, stream=None) -> dict:
-    """parents [B,N] int32 -> dict(anc_bits [B,N,W] int64 (uint64 bits), depth, path_rows, status)."""
+def sv_build_tree_mask(parents, max_depth: int, out: Optional[dict] = None, stream=None, validate=False) -> dict:
+    """parents [B,N] int32 -> dict(anc_bits [B,N,W] int64 (uint64 bits), depth, path_rows, status).
+
+    validate: reference mode (SV_FLAG_VALIDATE) -- the call waits and raises on a malformed tree."""
     torch = _torch()
     B, N = parents.shape
     W = (N + 63) // 64
@@ -197,7 +202,7 @@ def sv_build_tree_mask(parents, max_depth: int, out: Optional[dict] = None, stre
     rc = lib().sv_build_tree_mask(_ptr(parents, torch.int32, "parents"), B, N, max_depth,
                                   _ptr(out["anc_bits"], torch.int64, "anc_bits"), _ptr(out["depth"], torch.int32),
                                   _ptr(out.get("path_rows"), torch.int32), _ptr(out["status"], torch.int32),
-                                  _stream(stream))
+                                  SV_FLAG_VALIDATE if validate else 0, _stream(stream))
     _check(rc, "sv_build_tree_mask")
     return out
 
@@ -261,7 +266,7 @@ def sv_tree_attention(q, k_cache, v_cache, k_tree, v_tree, anc_bits, prefix_len,
 
 
 def accept_args(parents, tokens, anc_bits, depth, target_logits, max_depth, mode, draft_logits=None,
-                u_accept=None, u_sample=None, temperature=1.0, outs=None, threshold=0.0) -> sv_accept_args:
+                u_accept=None, u_sample=None, temperature=1.0, outs=None, threshold=0.0, flags=0) -> sv_accept_args:
     torch = _torch()
     B, N = parents.shape
     V = target_logits.shape[-1]
@@ -275,6 +280,7 @@ def accept_args(parents, tokens, anc_bits, depth, target_logits, max_depth, mode
     a.mode = mode
     a.temperature = float(temperature)
     a.threshold = float(threshold)
+    a.flags = int(flags)
     a.parents, a.tokens = _ptr(parents, torch.int32, "parents"), _ptr(tokens, torch.int32, "tokens")
     a.anc_bits, a.depth = _ptr(anc_bits, torch.int64, "anc_bits"), _ptr(depth, torch.int32, "depth")
     a.target_logits = _ptr(target_logits, name="target_logits")
@@ -306,13 +312,16 @@ def sv_accept_workspace(args: sv_accept_args) -> int:
 
 def sv_accept(parents, tokens, anc_bits, depth, target_logits, max_depth, mode="greedy", draft_logits=None,
               u_accept=None, u_sample=None, temperature=1.0, outs=None, workspace=None, stream=None,
-              threshold=0.0) -> dict:
-    """Speculative acceptance + bonus token; returns the dict of int32 device outputs."""
+              threshold=0.0, validate=False) -> dict:
+    """Speculative acceptance + bonus token; returns the dict of int32 device outputs.
+
+    validate: reference mode (SV_FLAG_VALIDATE) -- logits rows are scanned for non-finite values and
+    the call waits and raises SpecVerifyError when a sequence reports a non-zero status."""
     B = parents.shape[0]
     if outs is None:
         outs = accept_outputs(B, max_depth, parents.device)
     a = accept_args(parents, tokens, anc_bits, depth, target_logits, max_depth, mode, draft_logits, u_accept,
-                    u_sample, temperature, outs, threshold)
+                    u_sample, temperature, outs, threshold, SV_FLAG_VALIDATE if validate else 0)
     need = sv_accept_workspace(a)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = _alloc_workspace(need, parents.device)

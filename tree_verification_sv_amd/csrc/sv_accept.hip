@@ -88,14 +88,17 @@ struct XSlot {      // one work-group's partials for one exchange: (tag << 32) |
   uint64_t w[AC_XW];
 };
 
-// A resolved row, one 64-bit word (0 = not resolved in this call): bit 63 set, bits
-// 32..62 the first accepted child node + 1 (0 when all children were rejected), bits
-// 0..31 the bonus token if the walk stops here (stochastic) / the argmax (greedy).
+// A resolved row, one 64-bit word (0 = not resolved in this call): bit 63 set, bit 62 set
+// when the row's statistics are not finite (AC_RES_BAD), bits 32..61 the first accepted
+// child node + 1 (0 when all children were rejected), bits 0..31 the bonus token if the walk
+// stops here (stochastic) / the argmax (greedy).
+constexpr uint64_t AC_RES_BAD = 1ull << 62;
 __device__ __forceinline__ uint64_t res_word(int child, int token) {
   return (1ull << 63) | ((uint64_t)(uint32_t)(child + 1) << 32) | (uint32_t)token;
 }
 __device__ __forceinline__ bool res_ready(uint64_t v) { return (v >> 63) != 0; }
-__device__ __forceinline__ int res_child(uint64_t v) { return (int)((v >> 32) & 0x7fffffffu) - 1; }
+__device__ __forceinline__ bool res_bad(uint64_t v) { return (v & AC_RES_BAD) != 0; }
+__device__ __forceinline__ int res_child(uint64_t v) { return (int)((v >> 32) & 0x3fffffffu) - 1; }
 __device__ __forceinline__ int res_token(uint64_t v) { return (int)(uint32_t)v; }
 constexpr uint32_t AC_FRONT_BUSY = 0xffffffffu;  // the walk's frontier is claimed by a work-group
 
@@ -511,6 +514,8 @@ __global__ void __launch_bounds__(TH, 2) k_accept(sv_accept_args a, int32_t G, A
   __shared__ float s_g[STO ? Piece<T>::NK * TH : 4];
   __shared__ double s_col[Piece<T>::NK];
   __shared__ int s_xc, s_claim, s_fin;  // walk finished (sticky); stochastic walk: claimed row, finisher
+  __shared__ int s_bad;                 // the stop row's statistics were not finite
+  __shared__ int s_to;                  // a bounded wait of this call expired: no commit, status 7
   // work-groups are dispatched round-robin over the 8 XCDs; the members of a
   // group share an XCD (the grid size is a multiple of 8 * G)
   const int t = threadIdx.x, lane = t & 63;
@@ -696,6 +701,16 @@ __global__ void __launch_bounds__(TH, 2) k_accept(sv_accept_args a, int32_t G, A
           Zq = wave_sumd(on && need_q ? dof(xv[k][4], xv[k][5]) * sq : 0.0);
           fp = __shfl(sp, rank) / Zp;                   // p(v) = ep(v) * fp on this slice
           fq = need_q ? __shfl(sq, rank) / Zq : 0.0;
+        }
+        // a row without a finite positive normaliser (a NaN or +Inf logit, or no finite entry)
+        // accepts no child: the walk stops here with bonus 0 and the sequence reports status 8.
+        // Every member holds the same totals, so all of them leave here together.
+        if (!(Zp > 0.0 && Zp < (double)INFINITY) || (need_q && !(Zq > 0.0 && Zq < (double)INFINITY))) {
+          if (rank == 0) {
+            if (t == 0) st_u64(&ws.res[item], res_word(-1, 0) | AC_RES_BAD);
+            done_by_me = 1;
+          }
+          return;
         }
         // residual weight of one entry in units of fp: max(0, ep - kappa eq) for kappa > 0
         auto wgt = [&](int i, float kappa) -> float { return fmaxf(fmaf(-kappa, eq[i], ep[i]), 0.f); };
@@ -963,6 +978,8 @@ __global__ void __launch_bounds__(TH, 2) k_accept(sv_accept_args a, int32_t G, A
             }
             si.flag = (n << 16) | row;  // A and the stop row
             s_hit = res_token(s_rr[row]);
+            s_bad = res_bad(s_rr[row]) ? 1 : 0;
+            s_to = ld_u32(ws.err) != 0;
           }
           __syncthreads();
           const int A = si.flag >> 16, stop_row = si.flag & 0xffff, bonus = s_hit;
@@ -971,12 +988,14 @@ __global__ void __launch_bounds__(TH, 2) k_accept(sv_accept_args a, int32_t G, A
             a.accept_len[b] = A;
             a.num_out[b] = A + 1;
             a.stop_row[b] = stop_row;
-            a.status[b] = ld_u32(ws.err) ? SV_SEQ_TIMEOUT : (si.bad_token ? SV_SEQ_TOKEN : 0);
+            a.status[b] = s_to ? SV_SEQ_TIMEOUT
+                               : (si.bad_token ? SV_SEQ_TOKEN : (s_bad ? SV_SEQ_NONFINITE : 0));
           }
           if (t < Dm) a.accept_rows[(int64_t)b * Dm + t] = t < A ? si.path[t] + 1 : 0;
           if (t <= Dm)
             a.out_tokens[(int64_t)b * (Dm + 1) + t] = t < A ? si.tok[si.path[t]] : (t == A ? bonus : 0);
-          if (has_cm) svc::walker_commit(cm, b, A, si.path);  // the accepted path into the cache
+          // the accepted path into the cache (nothing after a timeout: the path may be wrong)
+          if (has_cm) svc::walker_commit(cm, b, s_to ? 0 : A, si.path);
           if (incr && t == 0) st_u32(cancel, 1u);  // the sequence's remaining rows are not needed
           if (!incr)  // every row result of b has been read: leave them cleared for the next call
             for (int x = t; x <= N; x += TH) st_u64(&rr[x], 0ull);
@@ -995,6 +1014,7 @@ __global__ void __launch_bounds__(TH, 2) k_accept(sv_accept_args a, int32_t G, A
         __syncthreads();
         if (s_last) {
           // ----------------------------------------------------- walk of sequence b
+          if (t == 0) s_to = ld_u32(ws.err) != 0;  // read after the barriers below
           int A = 0, stop_row = 0, bonus = 0;
           uint64_t* rr = ws.res + (int64_t)b * (N + 1);
           {
@@ -1068,7 +1088,7 @@ __global__ void __launch_bounds__(TH, 2) k_accept(sv_accept_args a, int32_t G, A
             a.accept_len[b] = A;
             a.num_out[b] = A + 1;
             a.stop_row[b] = stop_row;
-            a.status[b] = ld_u32(ws.err) ? SV_SEQ_TIMEOUT : (si.bad_token ? SV_SEQ_TOKEN : 0);
+            a.status[b] = s_to ? SV_SEQ_TIMEOUT : (si.bad_token ? SV_SEQ_TOKEN : 0);
             st_u32(&ws.seqdone[b], 0u);  // every row of b has been counted: ready for the next call
           }
           // every row result of b has been read: leave them cleared for the next call
@@ -1076,7 +1096,8 @@ __global__ void __launch_bounds__(TH, 2) k_accept(sv_accept_args a, int32_t G, A
           if (t < Dm) a.accept_rows[(int64_t)b * Dm + t] = t < A ? si.path[t] + 1 : 0;
           if (t <= Dm)
             a.out_tokens[(int64_t)b * (Dm + 1) + t] = t < A ? a.tokens[(int64_t)b * N + si.path[t]] : (t == A ? bonus : 0);
-          if (has_cm) svc::walker_commit(cm, b, A, si.path);  // the accepted path into the cache
+          // the accepted path into the cache (nothing after a timeout: the path may be wrong)
+          if (has_cm) svc::walker_commit(cm, b, s_to ? 0 : A, si.path);
         }
       }
     }
@@ -1112,6 +1133,22 @@ __global__ void __launch_bounds__(TH, 2) k_accept(sv_accept_args a, int32_t G, A
       st_u32(&ws.seqexit[bq], 0u);
     }
   }
+  // After a timeout some row may never have been published (members that stopped waiting can
+  // disagree), so some walk may never have run: the last work-group of the grid reports status 7
+  // for every sequence and clears every per-sequence word for the next call.  Every other
+  // work-group has exited, so nothing reads these words any more.
+  const bool timed_out = s_fin && ld_u32(ws.err) != 0;
+  if (timed_out) {
+    for (int x = t; x < a.B; x += TH) {
+      st_i(&a.status[x], SV_SEQ_TIMEOUT);
+      st_u32(&ws.seqdone[x], 0u);
+      st_u32(&ws.frontier[x], 0u);
+      st_u32(&ws.cancel[x], 0u);
+      st_u32(&ws.seqexit[x], 0u);
+    }
+    for (int64_t x = t; x < (int64_t)a.B * (N + 1); x += TH) st_u64(&ws.res[x], 0ull);
+  }
+  __syncthreads();  // every thread has read the timeout word before it is cleared
   if (t == 0) {
     if (G > 1 && s_last) st_u32(ws.gexit + grp, 0u);
     if (s_fin) {  // clear the timeout flag
@@ -1119,6 +1156,41 @@ __global__ void __launch_bounds__(TH, 2) k_accept(sv_accept_args a, int32_t G, A
       st_u32(ws.err + 1, 0u);
     }
   }
+}
+
+// SV_FLAG_VALIDATE: one work-group per logits row (target rows, then draft rows in mode 1) looks
+// for a NaN or +Inf entry, or a row without any finite entry, and sets status 8 for the
+// sequence unless the acceptance already reported a code.
+template <typename T>
+__device__ __forceinline__ void nf_check(T x, bool& bad, bool& finite);
+template <>
+__device__ __forceinline__ void nf_check<uint16_t>(uint16_t h, bool& bad, bool& finite) {
+  const bool fin = (h & 0x7f80u) != 0x7f80u;
+  finite |= fin;
+  bad |= !fin && h != 0xff80u;  // NaN or +Inf (-Inf is probability 0)
+}
+template <>
+__device__ __forceinline__ void nf_check<float>(float x, bool& bad, bool& finite) {
+  const bool fin = isfinite(x);
+  finite |= fin;
+  bad |= !fin && !(x < 0.f && isinf(x));
+}
+template <typename T>
+__global__ void __launch_bounds__(256) k_nonfinite_rows(const T* __restrict__ target, const T* __restrict__ draft,
+                                                        int32_t B, int32_t R, int32_t V, int32_t* __restrict__ status) {
+  __shared__ int s_any_bad, s_any_fin;
+  const int64_t row = blockIdx.x;  // [0, B*R) target rows, [B*R, 2*B*R) draft rows
+  const int64_t nrows = (int64_t)B * R;
+  const T* p = (row < nrows ? target + row * V : draft + (row - nrows) * V);
+  const int b = (int)((row < nrows ? row : row - nrows) / R);
+  if (threadIdx.x == 0) { s_any_bad = 0; s_any_fin = 0; }
+  __syncthreads();
+  bool bad = false, fin = false;
+  for (int v = threadIdx.x; v < V; v += 256) nf_check<T>(p[v], bad, fin);
+  if (bad) s_any_bad = 1;
+  if (fin) s_any_fin = 1;
+  __syncthreads();
+  if (threadIdx.x == 0 && (s_any_bad || !s_any_fin)) atomicCAS(&status[b], 0, SV_SEQ_NONFINITE);
 }
 
 int groups_G(const sv_accept_args& a) {
@@ -1160,6 +1232,22 @@ void launch_accept(int TH, dim3 grid, hipStream_t st, const sv_accept_args& a, i
   }
 }
 
+// SV_FLAG_VALIDATE, after the acceptance kernels: scan every logits row the call could read,
+// then wait and read the status back.
+sv_status validate_logits(const sv_accept_args& a, hipStream_t st) {
+  const int64_t rows = (int64_t)a.B * (a.N + 1) * (a.mode == SV_STOCHASTIC ? 2 : 1);
+  if (rows > 0x7fffffff) return SV_ERR_UNSUPPORTED;
+  if (a.logits_dtype == SV_BF16)
+    hipLaunchKernelGGL(k_nonfinite_rows<uint16_t>, dim3((unsigned)rows), dim3(256), 0, st,
+                       (const uint16_t*)a.target_logits, (const uint16_t*)a.draft_logits, a.B, a.N + 1, a.V, a.status);
+  else
+    hipLaunchKernelGGL(k_nonfinite_rows<float>, dim3((unsigned)rows), dim3(256), 0, st,
+                       (const float*)a.target_logits, (const float*)a.draft_logits, a.B, a.N + 1, a.V, a.status);
+  const sv_status ls = sv_launch_status();
+  if (ls != SV_OK) return ls;
+  return sv_validate_status(a.status, a.B, st);
+}
+
 }  // namespace
 
 extern "C" size_t sv_accept_workspace(const sv_accept_args* args) {
@@ -1178,6 +1266,7 @@ extern "C" sv_status sv_accept(const sv_accept_args* args, void* stream) {
   if (a.logits_dtype != SV_F32 && a.logits_dtype != SV_BF16) return SV_ERR_UNSUPPORTED;
   if (a.mode == SV_THRESHOLD && (!(a.temperature > 0.f) || !(a.threshold >= 0.f && a.threshold <= 1.f)))
     return SV_ERR_INVALID_ARGUMENT;
+  if (a.flags & ~(uint32_t)SV_FLAG_VALIDATE) return SV_ERR_INVALID_ARGUMENT;
   if (a.B == 0) return SV_OK;
   // modes 1 and 2 read neither mask output when depth is NULL (depths come from the parents)
   const bool mask_free = (a.mode == SV_STOCHASTIC || a.mode == SV_TOPK_DRAFT) && !a.depth;
@@ -1191,9 +1280,17 @@ extern "C" sv_status sv_accept(const sv_accept_args* args, void* stream) {
     cm = *a.commit;
   }
   const int32_t has_cm = a.commit != nullptr;
+  const bool validate = (a.flags & SV_FLAG_VALIDATE) != 0;
+  if (validate) {
+    if (a.mode == SV_STOCHASTIC && !a.draft_logits) return SV_ERR_INVALID_ARGUMENT;
+    const sv_status r = sv_validate_ready((hipStream_t)stream);
+    if (r != SV_OK) return r;
+  }
   if (a.mode == SV_THRESHOLD) {
     if ((uintptr_t)a.workspace % 256) return SV_ERR_INVALID_ARGUMENT;
-    return sv_threshold_launch(a, cm, has_cm, (hipStream_t)stream);
+    const sv_status r = sv_threshold_launch(a, cm, has_cm, (hipStream_t)stream);
+    if (r != SV_OK || !validate) return r;
+    return validate_logits(a, (hipStream_t)stream);
   }
   if (a.mode == SV_STOCHASTIC && !a.draft_logits) return SV_ERR_INVALID_ARGUMENT;
   if (a.mode != SV_GREEDY && (!a.u_accept || !a.u_sample || !(a.temperature > 0.f))) return SV_ERR_INVALID_ARGUMENT;
@@ -1231,5 +1328,8 @@ extern "C" sv_status sv_accept(const sv_accept_args* args, void* stream) {
     else { if (aligned) SV_ACC_LAUNCH(float, SV_GREEDY, true); else SV_ACC_LAUNCH(float, SV_GREEDY, false); }
   }
 #undef SV_ACC_LAUNCH
-  return sv_launch_status();
+  const sv_status ls = sv_launch_status();
+  if (ls != SV_OK || !validate) return ls;
+  return validate_logits(a, st);
 }
+

@@ -6,6 +6,7 @@ extern "C" const char* sv_status_string(sv_status s) {
     case SV_OK: return "ok";
     case SV_ERR_INVALID_ARGUMENT: return "invalid argument";
     case SV_ERR_UNSUPPORTED: return "unsupported shape or type";
+    case SV_ERR_BAD_TREE: return "validation found a data error (see the status array)";
     case SV_ERR_HIP: return "HIP launch error";
     default: return "unknown status";
   }

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "specverify.h"
 
 #define SV_MAX_N 256
@@ -35,6 +37,26 @@ __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p, int64_
 static inline sv_status sv_launch_status() {
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+// SV_FLAG_VALIDATE (reference mode): a synchronous call needs a stream that is not being
+// captured into a graph.  Checked before anything is enqueued.
+static inline sv_status sv_validate_ready(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) return SV_ERR_HIP;
+  return cs == hipStreamCaptureStatusNone ? SV_OK : SV_ERR_INVALID_ARGUMENT;
+}
+
+// SV_FLAG_VALIDATE: wait for the stream and read the per-sequence status back;
+// SV_ERR_BAD_TREE when some sequence reports a non-zero code.
+static inline sv_status sv_validate_status(const int32_t* status, int32_t B, hipStream_t st) {
+  std::vector<int32_t> h((size_t)B);
+  if (hipMemcpyAsync(h.data(), status, (size_t)B * sizeof(int32_t), hipMemcpyDeviceToHost, st) != hipSuccess)
+    return SV_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return SV_ERR_HIP;
+  for (int32_t b = 0; b < B; ++b)
+    if (h[(size_t)b] != 0) return SV_ERR_BAD_TREE;
+  return SV_OK;
 }
 
 // Wait until this wave's outstanding LDS operations have completed, so that

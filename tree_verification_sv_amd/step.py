@@ -111,7 +111,7 @@ class VerifyStep:
         m = self.mask
         _check(self._L.sv_build_tree_mask(self.x.parents.data_ptr(), self.B, self.N, self.x.max_depth,
                                           m["anc_bits"].data_ptr(), m["depth"].data_ptr(), m["path_rows"].data_ptr(),
-                                          m["status"].data_ptr(), _stream(stream)), "sv_build_tree_mask")
+                                          m["status"].data_ptr(), 0, _stream(stream)), "sv_build_tree_mask")
 
     def attention(self, stream=None):
         _check(self._L.sv_tree_attention(ctypes.byref(self._attn), _stream(stream)), "sv_tree_attention")
@@ -143,6 +143,9 @@ class VerifyStep:
         self._mask_free = on
 
     def run(self, stream=None, overlap=False, accept_first=False, attention_side=False):
+        if overlap and self._com.new_len == self._attn.prefix_len:
+            # the commit beside the attention writes new_len while the attention reads prefix_len
+            raise ValueError("new_len must not alias prefix_len when the commit overlaps the attention")
         if not overlap:
             self.build_mask(stream)
             self.attention(stream)
