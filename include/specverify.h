@@ -71,6 +71,7 @@ typedef int32_t sv_status;
 #define SV_ERR_UNSUPPORTED 2
 #define SV_ERR_BAD_TREE 3          /* SV_FLAG_VALIDATE: a sequence's device status is non-zero (read back by the call) */
 #define SV_ERR_HIP 4
+#define SV_ERR_SCRATCH_LIMIT 5     /* sv_accept_noalloc: the call needs more than SV_ACCEPT_SCRATCH_BYTES */
 
 /* element types */
 #define SV_F32 0
@@ -293,6 +294,23 @@ typedef struct sv_accept_args {
 size_t sv_accept_workspace(const sv_accept_args* args);
 sv_status sv_accept(const sv_accept_args* args, void* stream);
 
+/*
+ * sv_accept_noalloc -- sv_accept for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, arguments and outputs as sv_accept, but
+ * args->workspace and args->workspace_bytes are ignored and the workspace is
+ * a library-owned device array of SV_ACCEPT_SCRATCH_BYTES (4 MiB) per GPU,
+ * kept until the process ends.  Nothing is allocated by the call: no hipMalloc,
+ * hipFree or allocating library routine.  The first call on a device looks up
+ * the array's address (hipGetSymbolAddress) and enqueues one clearing kernel on
+ * `stream` before the acceptance kernels; later calls enqueue only those.
+ * Calls whose workspace (sv_accept_workspace) would exceed the array return
+ * SV_ERR_SCRATCH_LIMIT and enqueue nothing.  Every call on one GPU shares the
+ * array and leaves it zeroed: calls that overlap in time on one GPU (several
+ * streams, several host threads) race and must be serialised by the caller.
+ */
+#define SV_ACCEPT_SCRATCH_BYTES (4u << 20)
+sv_status sv_accept_noalloc(const sv_accept_args* args, void* stream);
 
 /*
  * sv_kv_commit -- append the accepted branch's KV to the cache ([EP] sec. 2,

@@ -18,7 +18,8 @@ _ROOT = os.path.dirname(_HERE)
 LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 _lib = None
 
-SV_OK, SV_ERR_INVALID_ARGUMENT, SV_ERR_UNSUPPORTED, SV_ERR_BAD_TREE, SV_ERR_HIP = 0, 1, 2, 3, 4
+SV_OK, SV_ERR_INVALID_ARGUMENT, SV_ERR_UNSUPPORTED, SV_ERR_BAD_TREE, SV_ERR_HIP, SV_ERR_SCRATCH_LIMIT = 0, 1, 2, 3, 4, 5
+SV_ACCEPT_SCRATCH_BYTES = 4 << 20
 SV_F32, SV_BF16 = 0, 1
 SV_GREEDY, SV_STOCHASTIC, SV_TOPK_DRAFT, SV_THRESHOLD = 0, 1, 2, 3
 _MODES = {"greedy": SV_GREEDY, "stochastic": SV_STOCHASTIC, "topk": SV_TOPK_DRAFT, "threshold": SV_THRESHOLD}
@@ -97,7 +98,7 @@ class sv_outcome_args(ctypes.Structure):
 
 
 EXPORTS = ["sv_build_tree_mask", "sv_tree_attention_workspace", "sv_tree_attention", "sv_accept_workspace",
-           "sv_accept", "sv_kv_commit", "sv_outcome_lookup", "sv_saguaro_reweight", "sv_draft_subset_logits",
+           "sv_accept", "sv_accept_noalloc", "sv_kv_commit", "sv_outcome_lookup", "sv_saguaro_reweight", "sv_draft_subset_logits",
            "sv_status_string", "sv_version"]
 
 
@@ -120,6 +121,8 @@ def lib():
         L.sv_accept_workspace.restype = ctypes.c_size_t
         L.sv_accept.argtypes = [ctypes.POINTER(sv_accept_args), P]
         L.sv_accept.restype = i32
+        L.sv_accept_noalloc.argtypes = [ctypes.POINTER(sv_accept_args), P]
+        L.sv_accept_noalloc.restype = i32
         L.sv_kv_commit.argtypes = [ctypes.POINTER(sv_commit_args), P]
         L.sv_kv_commit.restype = i32
         L.sv_outcome_lookup.argtypes = [ctypes.POINTER(sv_outcome_args), P]

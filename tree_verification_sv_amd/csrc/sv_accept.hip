@@ -54,6 +54,7 @@
 #include <float.h>
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "sv_commit_dev.h"
@@ -1333,3 +1334,60 @@ extern "C" sv_status sv_accept(const sv_accept_args* args, void* stream) {
   return validate_logits(a, st);
 }
 
+// ---------------------------------------------------------------- no-allocation variant
+// sv_accept_noalloc runs sv_accept with a workspace that lives in the library itself: a
+// file-scope device array of SV_ACCEPT_SCRATCH_BYTES, one copy per GPU, held until the
+// process ends.  Its device address comes from hipGetSymbolAddress, taken once per device
+// with that device current; host code never passes the array's own name to a kernel (on the
+// host that name is a stand-in, not a device address).  The array starts zeroed (static
+// storage) and is cleared once more by a fill kernel on the caller's stream the first time a
+// device is used (a kernel, not a memset, so that the first call may sit inside a captured
+// graph); every acceptance launch leaves the workspace zeroed again, as the workspace
+// contract of sv_accept requires.  Every call on one GPU shares the array: calls that
+// overlap in time on one GPU race.
+static __device__ __align__(256) unsigned char scratch[SV_ACCEPT_SCRATCH_BYTES];
+
+namespace {
+constexpr int SV_SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[SV_SCRATCH_MAX_DEVICES];
+
+__global__ void __launch_bounds__(256) k_zero16(uint4* __restrict__ p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// The scratch array's device address on the current device (set up on first use).
+sv_status scratch_for_current_device(hipStream_t st, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SV_ERR_HIP;
+  if (dev < 0 || dev >= SV_SCRATCH_MAX_DEVICES) return SV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SV_ERR_HIP;
+    hipLaunchKernelGGL(k_zero16, dim3(256), dim3(256), 0, st, (uint4*)p, (size_t)SV_ACCEPT_SCRATCH_BYTES / 16);
+    if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SV_OK;
+}
+}  // namespace
+
+extern "C" sv_status sv_accept_noalloc(const sv_accept_args* args, void* stream) {
+  if (!args) return SV_ERR_INVALID_ARGUMENT;
+  sv_accept_args a = *args;
+  a.workspace = nullptr;
+  a.workspace_bytes = 0;
+  if (a.B == 0) return sv_accept(&a, stream);  // argument checks only; nothing to launch
+  const size_t need = sv_accept_workspace(&a);
+  if (need == 0) return SV_ERR_INVALID_ARGUMENT;  // shape rejected by the workspace query
+  if (need > (size_t)SV_ACCEPT_SCRATCH_BYTES) return SV_ERR_SCRATCH_LIMIT;
+  void* p = nullptr;
+  const sv_status s = scratch_for_current_device((hipStream_t)stream, &p);
+  if (s != SV_OK) return s;
+  a.workspace = p;
+  a.workspace_bytes = (size_t)SV_ACCEPT_SCRATCH_BYTES;
+  return sv_accept(&a, stream);
+}
