@@ -194,12 +194,12 @@ sv_status sv_tree_attention(const sv_attn_args* args, void* stream);
  * sv_accept -- speculative acceptance and the bonus token ([PX], [SSD]).
  * Inputs:
  *   parents [B,N], tokens [B,N] int32 (draft token of node i), anc_bits and
- *   depth from sv_build_tree_mask (modes 1 and 2 may pass both as NULL: the
- *   kernel then derives each node's depth from parents by the same rule --
- *   the node count of its root path when that path reaches -1 through
+ *   depth from sv_build_tree_mask (modes 0, 1 and 2 may pass both as NULL:
+ *   the kernel then derives each node's depth from parents by the same rule
+ *   -- the node count of its root path when that path reaches -1 through
  *   in-range parents within max_depth nodes, else 0 -- and the call does not
- *   wait for the mask; modes 0 and 3 return SV_ERR_INVALID_ARGUMENT for a
- *   NULL one); target_logits [B, N+1, V] (row r = the
+ *   wait for the mask; mode 3 returns SV_ERR_INVALID_ARGUMENT for a NULL
+ *   one); target_logits [B, N+1, V] (row r = the
  *   target's next-token logits after row r's token, row 0 = the root);
  *   draft_logits [B, N+1, V] (mode 1 only; row r = the drafter's logits
  *   its children were drawn from); u_accept, u_sample [B, N+1] float

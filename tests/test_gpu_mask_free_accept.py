@@ -1,5 +1,5 @@
 """GPU vs oracle parity for acceptance without the mask outputs (sv_accept with NULL
-anc_bits and depth, modes 1 and 2): the kernel derives each node's depth from the parent
+anc_bits and depth, modes 0, 1 and 2): the kernel derives each node's depth from the parent
 array by the mask's rule, so the outputs must equal the oracle's, and the GPU path that
 reads the mask's depths, byte for byte -- on valid trees and on malformed ones (a parent
 out of range, self and two-node cycles, paths longer than max_depth).  The mask outputs
@@ -74,6 +74,8 @@ CASES = [
     ("cfg5-stochastic", lambda: W.config(5, B=3, L=290, V=1500)),
     ("cfg2-topk", lambda: W.config(2, mode="topk")),
     ("cfg4-topk", lambda: W.config(4, B=6, L=161, V=2999, mode="topk")),
+    ("cfg3-greedy", lambda: W.config(3, B=16, L=(16, 90))),
+    ("cfg1-greedy", lambda: W.config(1, B=5, plant=[0, 1, 2, 3, 4])),
 ]
 
 
@@ -88,7 +90,7 @@ def test_mask_free_accept_matches_oracle(name):
 
 
 @pytest.mark.parametrize("cfg,over", [(4, dict(B=6, L=161, V=2999)), (5, dict(B=5, L=290, V=1500)),
-                                      (4, dict(B=6, L=161, V=2999, mode="topk"))])
+                                      (4, dict(B=6, L=161, V=2999, mode="topk")), (3, dict(B=8, L=(16, 90)))])
 def test_mask_free_accept_malformed_trees(cfg, over):
     w = _malformed(W.config(cfg, **over))
     if cfg == 5:
@@ -100,7 +102,7 @@ def test_mask_free_accept_malformed_trees(cfg, over):
     assert (got["acc"]["accept_len"] <= w.max_depth).all()
 
 
-@pytest.mark.parametrize("cfg,over", [(2, {}), (5, dict(B=2, L=290, V=1500))])
+@pytest.mark.parametrize("cfg,over", [(2, {}), (5, dict(B=2, L=290, V=1500)), (3, dict(B=8, L=(16, 90)))])
 def test_mask_free_fused_commit(cfg, over):
     """The walker's commit with the depths derived in the kernel equals the commit after the mask."""
     w = W.config(cfg, **over)

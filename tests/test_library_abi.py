@@ -107,8 +107,8 @@ def test_tree_in_cache_and_layer_arguments_rejected_without_launch():
 
 
 def test_accept_without_mask_outputs_only_in_walk_modes():
-    """NULL anc_bits and depth are allowed only in modes 1 and 2 (depths derived in the kernel);
-    greedy and threshold acceptance read the mask outputs and reject them before any launch."""
+    """NULL anc_bits and depth are allowed in modes 0, 1 and 2 (depths and root paths derived in
+    the kernel); threshold acceptance reads the mask outputs and rejects them before any launch."""
     L = sv.lib()
     acc = sv.sv_accept_args()
     acc.B, acc.N, acc.V, acc.max_depth, acc.temperature, acc.threshold = 1, 4, 10, 4, 1.0, 0.5
@@ -118,7 +118,7 @@ def test_accept_without_mask_outputs_only_in_walk_modes():
               "accept_rows", "out_tokens", "num_out", "stop_row", "status", "workspace"):
         setattr(acc, k, fake)
     acc.workspace_bytes = 1 << 20
-    for mode in (sv.SV_GREEDY, sv.SV_THRESHOLD):
+    for mode in (sv.SV_THRESHOLD,):
         acc.mode = mode
         acc.anc_bits, acc.depth = None, None
         assert L.sv_accept(ctypes.byref(acc), None) == sv.SV_ERR_INVALID_ARGUMENT

@@ -51,1112 +51,26 @@
 // oldest unfinished one has finished, so that group is resident or next in
 // line: no group waits for a work-group that cannot start.  The waits are
 // bounded all the same (status SV_SEQ_TIMEOUT).
-#include <float.h>
-#include <math.h>
-
 #include <mutex>
-#include <type_traits>
 
-#include "sv_commit_dev.h"
+#include "sv_accept_dev.h"
 
 namespace {
 
-// threads per work-group: 512 for greedy rows (half the work-groups of 256-thread ones,
-// fewer to dispatch); stochastic and top-K rows take 256 (smaller barriers and bonus scans,
-// and the residual staging fits two work-groups per compute unit) except for batches of
-// wide trees (N >= AC_WIDE_N, where the walk cancels most rows) with at least AC_WIDE_ROWS
-// rows, where 512 (half the work-groups, one per compute unit for the 155 KB of LDS) measured
-// faster on MI355X: 256-node trees at batch 16 (4112 rows) 3.38 -> 2.93 ms per step, at batch
-// 8 even; 60-node trees were slower with 512 at every batch (batch 64, 3904 rows: 1.11 ->
-// 1.18 ms; batch 1: 13%), and so were 768-row chains
-constexpr int AC_WIDE_ROWS = 2048;
-constexpr int AC_WIDE_N = 128;
-int acc_threads(const sv_accept_args& a) {
-  if (a.mode == SV_GREEDY) return 512;
-  return a.N >= AC_WIDE_N && (int64_t)a.B * (a.N + 1) >= AC_WIDE_ROWS ? 512 : 256;
-}
-constexpr int AC_NWMAX = 8;                    // waves per work-group at most
-// vocabulary entries per thread: 8 pieces of 16 bytes (64 bf16 / 32 fp32 logits), so a
-// work-group's slice is 8 * 16 bytes per thread
-template <typename T> constexpr int ac_ct() { return 8 * (16 / (int)sizeof(T)); }
-template <typename T, int TH> constexpr int ac_slice() { return TH * ac_ct<T>(); }
-constexpr int AC_MAXG = 64;                    // work-groups per row group (vocabulary up to 1M entries)
-constexpr int AC_XW = 8;                       // tagged words per exchange slot
-constexpr int AC_XV = 6;                       // words an exchange carries at most
-constexpr uint32_t AC_SPIN_LIMIT = 1u << 20;   // bounded wait for a group partner (polls)
-
-struct XSlot {      // one work-group's partials for one exchange: (tag << 32) | payload
-  uint64_t w[AC_XW];
-};
-
-// A resolved row, one 64-bit word (0 = not resolved in this call): bit 63 set, bit 62 set
-// when the row's statistics are not finite (AC_RES_BAD), bits 32..61 the first accepted
-// child node + 1 (0 when all children were rejected), bits 0..31 the bonus token if the walk
-// stops here (stochastic) / the argmax (greedy).
-constexpr uint64_t AC_RES_BAD = 1ull << 62;
-__device__ __forceinline__ uint64_t res_word(int child, int token) {
-  return (1ull << 63) | ((uint64_t)(uint32_t)(child + 1) << 32) | (uint32_t)token;
-}
-__device__ __forceinline__ bool res_ready(uint64_t v) { return (v >> 63) != 0; }
-__device__ __forceinline__ bool res_bad(uint64_t v) { return (v & AC_RES_BAD) != 0; }
-__device__ __forceinline__ int res_child(uint64_t v) { return (int)((v >> 32) & 0x3fffffffu) - 1; }
-__device__ __forceinline__ int res_token(uint64_t v) { return (int)(uint32_t)v; }
-constexpr uint32_t AC_FRONT_BUSY = 0xffffffffu;  // the walk's frontier is claimed by a work-group
-
-struct AccWs {        // workspace views
-  uint32_t* gexit;    // [groups] group exit counters
-  uint32_t* seqdone;  // [B] rows resolved per sequence (greedy)
-  uint32_t* err;      // [0] wait-timeout flag, [1] work-groups exited
-  uint64_t* res;      // [B, N+1] resolved rows
-  uint32_t* frontier; // [B] stochastic walk: the first row of the path not yet resolved
-  uint32_t* cancel;   // [B] stochastic walk finished: remaining rows are not needed
-  uint32_t* seqexit;  // [B] stochastic: work-groups of the sequence that have exited
-  XSlot* xs;          // [groups * G * 2]: (group * G + rank) * 2 + exchange parity
-};
-
-template <typename T>
-__device__ __forceinline__ float ldf(const T* p, int64_t i) { return load_as_f32<T>(p, i); }
-// raw bits of one logit, and their value (split so that the conversion can be placed late)
-template <typename T> __device__ __forceinline__ uint32_t ldraw(const T* p, int64_t i);
-template <> __device__ __forceinline__ uint32_t ldraw<float>(const float* p, int64_t i) { return __float_as_uint(p[i]); }
-template <> __device__ __forceinline__ uint32_t ldraw<uint16_t>(const uint16_t* p, int64_t i) { return p[i]; }
-template <typename T> __device__ __forceinline__ float rawf(uint32_t b) {
-  return sizeof(T) == 2 ? __uint_as_float(b << 16) : __uint_as_float(b);
-}
-
-// ---------------------------------------------------------------- reductions
-// Cross-lane steps use DPP moves (a few cycles each) instead of LDS permutes.
-// Within a 16-lane row: quad permutations and the row mirrors for butterflies,
-// row shifts for the scan; across rows: lane reads for reductions and the row
-// broadcasts of lanes 15 and 31 for the scan.  Results are identical in every
-// lane, and the order of operations is fixed, so every work-group that reduces
-// the same values gets the same bits.
-enum : int {
-  DPP_XOR1 = 0xB1,         // quad_perm [1, 0, 3, 2]
-  DPP_XOR2 = 0x4E,         // quad_perm [2, 3, 0, 1]
-  DPP_ROW_SHR1 = 0x111,    // row_shr:n = 0x110 + n
-  DPP_ROW_MIRROR = 0x140,
-  DPP_ROW_HALF_MIRROR = 0x141,
-  DPP_ROW_BCAST15 = 0x142,
-  DPP_ROW_BCAST31 = 0x143,
-};
-template <int CTRL, int ROWS = 0xf, bool BC = true>
-__device__ __forceinline__ uint32_t dpp32(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWS, 0xf, BC);
-}
-template <int CTRL, int ROWS = 0xf, bool BC = true>
-__device__ __forceinline__ float dppf(float x) { return __uint_as_float(dpp32<CTRL, ROWS, BC>(__float_as_uint(x))); }
-template <int CTRL, int ROWS = 0xf, bool BC = true>
-__device__ __forceinline__ double dppd(double x) {
-  const uint64_t b = (uint64_t)__double_as_longlong(x);
-  const uint64_t lo = dpp32<CTRL, ROWS, BC>((uint32_t)b), hi = dpp32<CTRL, ROWS, BC>((uint32_t)(b >> 32));
-  return __longlong_as_double((long long)((hi << 32) | lo));
-}
-__device__ __forceinline__ float lanef(float x, int l) { return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x), l)); }
-__device__ __forceinline__ double laned(double x, int l) {
-  const uint64_t b = (uint64_t)__double_as_longlong(x);
-  const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((uint32_t)b, l);
-  const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((uint32_t)(b >> 32), l);
-  return __longlong_as_double((long long)((hi << 32) | lo));
-}
-__device__ __forceinline__ float wave_maxf(float x) {
-  x = fmaxf(x, dppf<DPP_XOR1>(x));
-  x = fmaxf(x, dppf<DPP_XOR2>(x));
-  x = fmaxf(x, dppf<DPP_ROW_HALF_MIRROR>(x));
-  x = fmaxf(x, dppf<DPP_ROW_MIRROR>(x));  // every lane of a row holds the row's maximum
-  return fmaxf(fmaxf(lanef(x, 0), lanef(x, 16)), fmaxf(lanef(x, 32), lanef(x, 48)));
-}
-__device__ __forceinline__ double wave_sumd(double x) {
-  x += dppd<DPP_XOR1>(x);
-  x += dppd<DPP_XOR2>(x);
-  x += dppd<DPP_ROW_HALF_MIRROR>(x);
-  x += dppd<DPP_ROW_MIRROR>(x);  // every lane of a row holds the row's sum
-  return (laned(x, 0) + laned(x, 16)) + (laned(x, 32) + laned(x, 48));
-}
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(v, o);
-    const int oi = __shfl_xor(i, o);
-    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
-  }
-}
-// inclusive prefix sum over the 64 lanes of a wave, ascending lane order
-__device__ __forceinline__ double wave_scand(double x, int lane) {
-  (void)lane;
-  x += dppd<DPP_ROW_SHR1 + 0>(x);  // shifted-in lanes read 0
-  x += dppd<DPP_ROW_SHR1 + 1>(x);
-  x += dppd<DPP_ROW_SHR1 + 3>(x);
-  x += dppd<DPP_ROW_SHR1 + 7>(x);  // inclusive scan within each row of 16
-  x += dppd<DPP_ROW_BCAST15, 0xa, false>(x);  // rows 1, 3 add lane 15 of the row before
-  x += dppd<DPP_ROW_BCAST31, 0xc, false>(x);  // rows 2, 3 add lane 31
-  return x;
-}
-
-struct Red {
-  float f[AC_NWMAX];
-  double d[AC_NWMAX];
-  int i[AC_NWMAX];
-};
-
-template <int TH>
-__device__ __forceinline__ float block_max(float x, Red& r) {
-  x = wave_maxf(x);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) r.f[threadIdx.x >> 6] = x;
-  __syncthreads();
-  float m = r.f[0];
-  for (int k = 1; k < TH / 64; ++k) m = fmaxf(m, r.f[k]);
-  return m;
-}
-template <int TH>
-__device__ __forceinline__ double block_sum(double x, Red& r) {
-  x = wave_sumd(x);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) r.d[threadIdx.x >> 6] = x;
-  __syncthreads();
-  double s = 0.0;
-  for (int k = 0; k < TH / 64; ++k) s += r.d[k];
-  return s;
-}
-template <int TH>
-__device__ __forceinline__ void block_argmax(float& v, int& i, Red& r) {
-  wave_argmax(v, i);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) { r.f[threadIdx.x >> 6] = v; r.i[threadIdx.x >> 6] = i; }
-  __syncthreads();
-  v = r.f[0];
-  i = r.i[0];
-  for (int k = 1; k < TH / 64; ++k)
-    if (r.f[k] > v || (r.f[k] == v && r.i[k] < i)) { v = r.f[k]; i = r.i[k]; }
-}
-
-// ---------------------------------------------------------------- cross-work-group messages
-// Values crossing work-groups are written with relaxed device-scope atomic
-// stores and read with relaxed device-scope atomic loads (both coherent at
-// device scope).  Exchange words carry their tag in the same 64-bit word as
-// the payload.  Row results are published before the per-sequence counter:
-// the writer waits for its stores to complete (s_waitcnt) and then bumps the
-// counter.  Neither order needs a cache write-back or invalidation.
-#define AGENT __HIP_MEMORY_SCOPE_AGENT
-__device__ __forceinline__ void st_u32(uint32_t* p, uint32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, AGENT); }
-__device__ __forceinline__ void st_u64(uint64_t* p, uint64_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, AGENT); }
-__device__ __forceinline__ uint32_t ld_u32(uint32_t* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, AGENT); }
-__device__ __forceinline__ uint64_t ld_u64(uint64_t* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, AGENT); }
-__device__ __forceinline__ uint32_t add_u32(uint32_t* p, uint32_t v) { return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, AGENT); }
-__device__ __forceinline__ bool cas_u32(uint32_t* p, uint32_t expect, uint32_t v) {
-  return __hip_atomic_compare_exchange_strong(p, &expect, v, __ATOMIC_RELAXED, __ATOMIC_RELAXED, AGENT);
-}
-__device__ __forceinline__ void st_i(int32_t* p, int32_t v) { st_u32((uint32_t*)p, (uint32_t)v); }
-__device__ __forceinline__ int32_t ld_i(int32_t* p) { return (int32_t)ld_u32((uint32_t*)p); }
-// wait until this thread's memory operations have completed
-__device__ __forceinline__ void mem_complete() {
-  __builtin_amdgcn_s_waitcnt(0);
-  asm volatile("" ::: "memory");
-}
-__device__ __forceinline__ uint32_t dlo(double x) { return (uint32_t)__double_as_longlong(x); }
-__device__ __forceinline__ uint32_t dhi(double x) { return (uint32_t)((uint64_t)__double_as_longlong(x) >> 32); }
-__device__ __forceinline__ double dof(uint32_t lo, uint32_t hi) {
-  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-}
-
-// Exchange number `tag` (>= 1, the same on every member) of a group: this
-// work-group publishes the nw words w0..w5 (identical in all its threads) and
-// collects every member's words into xv[rank][word].  Slots alternate by tag
-// parity: a member can only reach exchange tag+2 after every member has
-// published tag+1, that is after every member has collected exchange tag.
-// The wait is bounded: on timeout the error flag is raised, and once it is
-// raised no thread waits any more, so every wave exits (results then carry
-// status SV_SEQ_TIMEOUT).
-// cancel (nullable): the sequence's walk-finished flag.  It is read once per
-// exchange (alongside the polls) and while waiting; once it is seen set, the
-// work-group's sticky flag *xc is set and the exchange returns true (the row's
-// result is no longer needed; a member that waits for a member that has left
-// sees the flag too).
-template <int TH>
-__device__ __forceinline__ bool exchange(XSlot* gs, int G, int rank, uint32_t tag, int nw, uint32_t (*xv)[AC_XV],
-                                         uint32_t* err, uint32_t* cancel, int* xc, uint32_t w0, uint32_t w1,
-                                         uint32_t w2 = 0, uint32_t w3 = 0, uint32_t w4 = 0, uint32_t w5 = 0) {
-  const int t = threadIdx.x;
-  const int par = tag & 1;
-  if (t < nw) {
-    const uint32_t w = t == 0 ? w0 : t == 1 ? w1 : t == 2 ? w2 : t == 3 ? w3 : t == 4 ? w4 : w5;
-    st_u64(&gs[rank * 2 + par].w[t], ((uint64_t)tag << 32) | w);
-  }
-  const uint32_t c0 = (cancel && t == 0) ? ld_u32(cancel) : 0u;  // overlaps the polls below
-  for (int q = t; q < G * nw; q += TH) {
-    const int k = q / nw, i = q - k * nw;
-    uint64_t* p = &gs[k * 2 + par].w[i];
-    uint64_t v = ld_u64(p);
-    uint32_t spins = 0;
-    while ((uint32_t)(v >> 32) != tag) {
-      ++spins;
-      if ((spins & 63) == 0 && (spins > AC_SPIN_LIMIT || ld_u32(err) != 0)) {
-        st_u32(err, 1u);
-        break;
-      }
-      // every fourth poll also reads the cancel flag; both loads are in flight together
-      const bool chk = cancel != nullptr && (spins & 3) == 0;
-      v = ld_u64(p);
-      const uint32_t cv = chk ? ld_u32(cancel) : 0u;
-      if (cv != 0u) {
-        *xc = 1;
-        break;
-      }
-    }
-    xv[k][i] = (uint32_t)v;
-  }
-  if (c0) *xc = 1;
-  __syncthreads();
-  return *xc != 0;
-}
-
-struct SeqInfo {    // per-sequence facts every work-group derives the same way
-  int32_t tok[SV_MAX_N];
-  int16_t par[SV_MAX_N];
-  uint8_t usable[SV_MAX_N];
-  uint8_t haskid[SV_MAX_N + 1];  // row has a usable child
-  int16_t kids[SV_MAX_N];     // usable children of the current row, ascending
-  int32_t wcount[AC_NWMAX];
-  int32_t wlive[AC_NWMAX];
-  int32_t K;                  // number of usable children of the current row
-  int32_t nlive;              // rows this sequence resolves
-  int32_t bad_token;
-  int32_t path[SV_MAX_DEPTH];
-  int32_t flag;
-};
-
-// per-sequence facts: usable nodes, rows with children, live-row count (one node per thread).
-// The loads are issued by seq_fetch ahead of the slice loads, so that waiting for them does
-// not wait for the slice.
-struct SeqRaw {
-  int32_t tok, par, dep;
-};
-__device__ __forceinline__ SeqRaw seq_fetch(const sv_accept_args& a, int b) {
-  SeqRaw r{0, -2, 0};
-  const int t = threadIdx.x;
-  if (t < a.N) {
-    const int64_t i = (int64_t)b * a.N + t;
-    r.tok = a.tokens[i];
-    r.par = a.parents[i];
-    // without a depth array the load takes the parents (the value is then unused): an
-    // unconditional load keeps the kernel free of scratch
-    r.dep = (a.depth ? a.depth : a.parents)[i];
-  }
-  return r;
-}
-template <int TH>
-__device__ __forceinline__ void seq_facts(const sv_accept_args& a, const SeqRaw& sr, SeqInfo& si) {
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int N = a.N;
-  for (int x = t; x <= N; x += TH) si.haskid[x] = 0;
-  if (t == 0) si.bad_token = 0;
-  __syncthreads();
-  bool u = false;
-  if (t < N) {
-    // an out-of-range parent is staged as -2 (only usable nodes' parents are read later)
-    si.par[t] = (int16_t)(sr.par >= -1 && sr.par < N ? sr.par : -2);
-    si.tok[t] = sr.tok;
-  }
-  int dep = sr.dep;
-  if (!a.depth) {  // uniform: no depth array, derive it from the staged parents
-    // the rule of the tree mask: the number of nodes on the root path when the walk reaches
-    // parent -1 through in-range parents within max_depth nodes, else 0 (a cycle never
-    // reaches -1, so it ends on the depth limit)
-    __syncthreads();
-    dep = 0;
-    if (t < N) {
-      int cur = t, cnt = 1;
-#pragma unroll 1
-      for (int s = 0; s < SV_MAX_DEPTH; ++s) {  // at most max_depth - 1 <= 15 steps up
-        const int p = si.par[cur];
-        if (p == -1) { dep = cnt; break; }
-        if (p < 0 || cnt >= a.max_depth) break;
-        ++cnt;
-        cur = p;
-      }
-    }
-  }
-  if (t < N) {  // the thread's own staged values (no barrier needed to read them back)
-    const int pr = si.par[t], tok = si.tok[t];
-    const bool ok = tok >= 0 && tok < a.V;
-    if (!ok) si.bad_token = 1;  // every writer stores the same value
-    u = ok && dep > 0 && pr != -2;
-    if (u) si.haskid[pr + 1] = 1;
-  }
-  if (t < SV_MAX_N) si.usable[t] = u;
-  __syncthreads();
-  // live rows: greedy -- rows with a usable child; stochastic -- rows of usable nodes
-  const bool live = a.mode == SV_GREEDY ? (t >= 1 && t <= N && si.haskid[t]) : u;
-  const uint64_t lm = __ballot(live);
-  if (lane == 0) si.wlive[wv] = __popcll(lm);
-  __syncthreads();
-  if (t == 0) {
-    int nl = 0;
-    for (int k = 0; k < TH / 64; ++k) nl += si.wlive[k];
-    si.nlive = nl + 1;  // + the root row
-  }
-  __syncthreads();
-}
-
-// usable children of row r in ascending index, from the sequence facts
-template <int TH>
-__device__ __forceinline__ void row_kids(int N, int r, SeqInfo& si) {
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const bool kid = t < N && si.usable[t] && si.par[t] + 1 == r;
-  const uint64_t m = __ballot(kid);
-  if (lane == 0) si.wcount[wv] = __popcll(m);
-  __syncthreads();
-  int off = 0, K = 0;
-  for (int k = 0; k < TH / 64; ++k) {
-    if (k < wv) off += si.wcount[k];
-    K += si.wcount[k];
-  }
-  if (kid) si.kids[off + __popcll(m & ((1ull << lane) - 1ull))] = t;
-  if (t == 0) si.K = K;
-  __syncthreads();
-}
-
-__device__ __forceinline__ bool row_live(const sv_accept_args& a, const SeqInfo& si, int r) {
-  if (r == 0) return true;
-  return a.mode == SV_GREEDY ? si.haskid[r] != 0 : si.usable[r - 1] != 0;
-}
-
-// ---------------------------------------------------------------- slice loads
-template <typename T> struct Piece {
-  static constexpr int E = 16 / sizeof(T);  // entries per 16-byte piece
-  static constexpr int NK = ac_ct<T>() / E;  // pieces per thread
-};
-template <typename T> __device__ __forceinline__ T lowest_of();
-template <> __device__ __forceinline__ float lowest_of<float>() { return -FLT_MAX; }
-template <> __device__ __forceinline__ uint16_t lowest_of<uint16_t>() { return 0xff7f; }  // bf16 -3.39e38
-__device__ __forceinline__ uint32_t bits_of(float x) { return __float_as_uint(x); }
-__device__ __forceinline__ uint32_t bits_of(uint16_t x) { return (uint32_t)x; }
-// the 16 bytes of w as E = 16/sizeof(T) floats
-template <typename T> __device__ __forceinline__ void unpack16(const uint4& w, float (&x)[16 / sizeof(T)]);
-template <> __device__ __forceinline__ void unpack16<uint16_t>(const uint4& w, float (&x)[8]) {
-  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    x[2 * h] = __uint_as_float(ww[h] << 16);
-    x[2 * h + 1] = __uint_as_float(ww[h] & 0xffff0000u);
-  }
-}
-template <> __device__ __forceinline__ void unpack16<float>(const uint4& w, float (&x)[4]) {
-  x[0] = __uint_as_float(w.x); x[1] = __uint_as_float(w.y); x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
-}
-// hide the register values from the optimiser, so that values derived from
-// them are recomputed where they are used rather than kept alive in between
-template <int NK>
-__device__ __forceinline__ void opaque(uint4 (&raw)[NK]) {
-#pragma unroll
-  for (int k = 0; k < NK; ++k) asm volatile("" : "+v"(raw[k].x), "+v"(raw[k].y), "+v"(raw[k].z), "+v"(raw[k].w));
-}
-// first entry of piece k of thread t in a slice starting at s0
-template <typename T, int TH>
-__device__ __forceinline__ int piece_v(int s0, int k, int t) { return s0 + (k * TH + t) * Piece<T>::E; }
-
-// Thread t's pieces of one logits row.  `aligned`: the row starts on 16 bytes
-// and V * sizeof(T) is a multiple of 16, so each piece lies wholly inside or
-// wholly past the row; the loads then go through a buffer resource sized to
-// the row, which returns zeros for pieces past V.  Otherwise entries are
-// loaded one by one and entries past V read as the lowest value.  Callers
-// treat pieces starting at or past V as absent.  `present` false (uniform):
-// the row is not needed; aligned loads are still issued, against an empty
-// range, so they return zeros without touching memory and the register
-// assignment does not depend on the branch.
-template <typename T, int TH>
-__device__ __forceinline__ void load_pieces(const T* row, int s0, int V, bool aligned, int t,
-                                            uint4 (&raw)[Piece<T>::NK], bool present = true) {
-  constexpr int E = Piece<T>::E;
-  if (aligned) {
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)row, 0, present ? V * (int)sizeof(T) : 0, 0x00020000);
-    const int vo = (s0 + t * E) * (int)sizeof(T);
-#pragma unroll
-    for (int k = 0; k < Piece<T>::NK; ++k)
-      raw[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, k * TH * 16, 0));
-  } else if (!present) {
-#pragma unroll
-    for (int k = 0; k < Piece<T>::NK; ++k) raw[k] = make_uint4(0u, 0u, 0u, 0u);
-  } else {
-#pragma unroll
-    for (int k = 0; k < Piece<T>::NK; ++k) {
-      const int v = piece_v<T, TH>(s0, k, t);
-      uint32_t wd[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const T x = v + e < V ? row[v + e] : lowest_of<T>();
-        wd[e * sizeof(T) / 4] |= bits_of(x) << (8 * ((e * sizeof(T)) % 4));
-      }
-      raw[k] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-    }
-  }
-}
-
-// ---------------------------------------------------------------- the kernel
-// ALIGNED: every logits row starts on 16 bytes (decided on the host; a compile-time choice
-// keeps the two load paths from meeting in one register assignment)
 template <typename T, int MODE, bool ALIGNED, int TH>
 __global__ void __launch_bounds__(TH, 2) k_accept(sv_accept_args a, int32_t G, AccWs ws,
                                                                   sv_commit_args cm, int32_t has_cm) {
-  constexpr int NW = TH / 64;
-  // STO: a rejection walk (modes 1 and 2); TOPK: deterministic drafts (q = point mass per child)
-  constexpr bool STO = MODE != SV_GREEDY, TOPK = MODE == SV_TOPK_DRAFT;
-  constexpr int E = Piece<T>::E, NK = Piece<T>::NK;
-  __shared__ Red red;
-  __shared__ SeqInfo si;
-  __shared__ int32_t s_last, s_hit, s_first, s_lpos;
-  __shared__ uint64_t s_match[SV_MAX_W];
-  __shared__ uint32_t xv[AC_MAXG][AC_XV];                          // collected group partials
-  __shared__ float s_lp[SV_MAX_N], s_lq[SV_MAX_N], s_u[SV_MAX_N];  // per child: logits at its token, u_accept
-  __shared__ float s_us;                                            // u_sample of the row
-  // bonus: the slice's residual weights in id order, per-piece sums [k][t] and their row totals
+  constexpr bool STO = MODE != SV_GREEDY;
+  constexpr int RF = STO ? ac_slice<T, TH>() / Piece<T>::NK : 1;  // floats per piece row of the staging area
+  __shared__ AccShared<T, TH, STO> S;
   __shared__ __attribute__((aligned(16))) float s_w[STO ? ac_slice<T, TH>() : 4];
-  __shared__ float s_g[STO ? Piece<T>::NK * TH : 4];
-  __shared__ double s_col[Piece<T>::NK];
-  __shared__ int s_xc, s_claim, s_fin;  // walk finished (sticky); stochastic walk: claimed row, finisher
-  __shared__ int s_bad;                 // the stop row's statistics were not finite
-  __shared__ int s_to;                  // a bounded wait of this call expired: no commit, status 7
-  // work-groups are dispatched round-robin over the 8 XCDs; the members of a
-  // group share an XCD (the grid size is a multiple of 8 * G)
-  const int t = threadIdx.x, lane = t & 63;
-  const int xcd = blockIdx.x % 8, idx = blockIdx.x / 8;
-  const int grp = (idx / G) * 8 + xcd;
-  const int rank = idx % G;
-  const int N = a.N, V = a.V;
-  const float invT = STO ? 1.0f / a.temperature : 1.0f;
-  const float l2T = invT * 1.4426950408889634f;  // bulk exponentials as exp2((x - m) * log2(e) / T)
-  XSlot* gslots = ws.xs + (int64_t)grp * G * 2;
-  uint32_t xtag = 0;  // exchanges of this group so far (identical on every member)
-  const int64_t item = grp;
-  const int s0 = rank * ac_slice<T, TH>();  // this work-group's slice of the vocabulary
-  if (t == 0) s_xc = 0;
-  bool live_row = false;
-
-  if (item < (int64_t)a.B * (N + 1)) {
-    // uniform, and kept in scalar registers so that the slice loads take a scalar resource
-    const int b = __builtin_amdgcn_readfirstlane((int)(item / (N + 1)));
-    const int r = __builtin_amdgcn_readfirstlane((int)(item % (N + 1)));
-    const T* prow = (const T*)a.target_logits + ((int64_t)b * (N + 1) + r) * V;
-    const T* qrow = MODE == SV_STOCHASTIC ? (const T*)a.draft_logits + ((int64_t)b * (N + 1) + r) * V : nullptr;
-    constexpr bool aligned = ALIGNED;
-    // stochastic: nearly every row is resolved, so the target slice is fetched before the
-    // sequence facts that confirm it is needed (its latency overlaps them); the facts'
-    // own loads go first
-    SeqRaw sr = seq_fetch(a, b);
-    // stochastic, wide trees: the walk advances as rows resolve and ends the sequence's
-    // remaining rows (below); chains and narrow trees, where nearly every row is on the
-    // path, walk once after the last row
-    const bool incr = STO && N > 2 * a.max_depth;
-    uint32_t* cancel = incr ? &ws.cancel[b] : nullptr;
-    uint32_t cx0 = 0u;  // the sequence's walk already finished (a late work-group)
-    if (incr && t == 0) cx0 = ld_u32(cancel);
-    uint4 rp[NK];
-    if constexpr (STO) load_pieces<T, TH>(prow, s0, V, aligned, t, rp);
-    asm volatile("" : "+v"(sr.tok), "+v"(sr.par), "+v"(sr.dep), "+v"(cx0));  // nothing uses them before this point
-    if (cx0) s_xc = 1;
-    seq_facts<TH>(a, sr, si);
-    live_row = row_live(a, si, r);  // the same on every member of the group
-    if (live_row && !s_xc) {
-      row_kids<TH>(N, r, si);
-      int done_by_me = 0;  // this work-group wrote the row result
-
-      if constexpr (MODE == SV_GREEDY) {
-        float best = -FLT_MAX;
-        int arg = 0x7fffffff;
-        {
-          load_pieces<T, TH>(prow, s0, V, aligned, t, rp);
-#pragma unroll
-          for (int k = 0; k < NK; ++k) {
-            float x[E];
-            unpack16<T>(rp[k], x);
-            const int v = piece_v<T, TH>(s0, k, t);
-#pragma unroll
-            for (int e = 0; e < E; ++e)  // a thread visits its entries in ascending id
-              if (v + e < V && x[e] > best) { best = x[e]; arg = v + e; }
-          }
-        }
-        block_argmax<TH>(best, arg, red);
-        exchange<TH>(gslots, G, rank, ++xtag, 2, xv, ws.err, nullptr, &s_xc, __float_as_uint(best), (uint32_t)arg);
-        if (rank == 0) {
-          if (t < 64) {  // wave 0: lane k takes member k's best; the butterfly keeps the lowest id on ties
-            float bv = lane < G ? __uint_as_float(xv[lane][0]) : -FLT_MAX;
-            int bi = lane < G ? (int)xv[lane][1] : 0x7fffffff;
-            wave_argmax(bv, bi);
-            if (t == 0) st_u64(&ws.res[item], res_word(-1, bi));
-          }
-          done_by_me = 1;
-        }
-      } else {
-        // the row's resolution; returns early once the sequence's walk has finished
-        [&]() {
-        const int K = __builtin_amdgcn_readfirstlane(si.K);
-        const bool need_q = !TOPK && K > 0;  // deterministic drafts read no draft logits
-        // ---- the slice: raw logits -> slice maxima -> exponentials kept in registers
-        float ep[ac_ct<T>()], eq[ac_ct<T>()];
-        float mp = -FLT_MAX, mq = -FLT_MAX;
-        double zp = 0.0, zq = 0.0;
-        {
-          uint4 rq[NK];
-          if constexpr (!TOPK) load_pieces<T, TH>(qrow, s0, V, aligned, t, rq, need_q);
-          // children's logits at their tokens and their uniforms: issued after the draft
-          // slice (so that nothing waits for them before it is issued), stored to LDS once
-          // both slices are in
-          uint32_t c_lp = 0u, c_lq = 0u, c_u = 0u, c_us = 0u;
-          if (t < K) {
-            const int kid = si.kids[t];
-            const int x = si.tok[kid];  // usable: x in [0, V)
-            c_lp = ldraw(prow, x);
-            if constexpr (!TOPK) c_lq = ldraw(qrow, x);
-            c_u = __float_as_uint(a.u_accept[(int64_t)b * (N + 1) + kid + 1]);
-          }
-          if (t == TH - 1) c_us = __float_as_uint(a.u_sample[(int64_t)b * (N + 1) + r]);
-#pragma unroll
-          for (int k = 0; k < NK; ++k) {
-            float x[E];
-            unpack16<T>(rp[k], x);
-#pragma unroll
-            for (int e = 0; e < E; ++e) mp = piece_v<T, TH>(s0, k, t) < V ? fmaxf(mp, x[e]) : mp;
-          }
-          mp = block_max<TH>(mp, red);
-          opaque(rp);  // unpack again below instead of keeping the unpacked floats alive
-          const float op = mp * l2T;  // exp2(x * l2T - op): one FMA per entry
-          const bool whole = s0 + ac_slice<T, TH>() <= V;  // uniform: no entry of the slice lies past V
-          auto expo = [&](const uint4 (&raw)[NK], float o, float (&ex)[ac_ct<T>()], double& z) {
-            if (whole) {
-#pragma unroll
-              for (int k = 0; k < NK; ++k) {
-                float x[E], g = 0.f;  // fp32 partial of one piece, fp64 across pieces
-                unpack16<T>(raw[k], x);
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                  ex[k * E + e] = __builtin_amdgcn_exp2f(fmaf(x[e], l2T, -o));
-                  g += ex[k * E + e];
-                }
-                z += (double)g;
-              }
-            } else {
-#pragma unroll
-              for (int k = 0; k < NK; ++k) {
-                float x[E], g = 0.f;
-                unpack16<T>(raw[k], x);
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                  ex[k * E + e] = piece_v<T, TH>(s0, k, t) < V ? __builtin_amdgcn_exp2f(fmaf(x[e], l2T, -o)) : 0.f;
-                  g += ex[k * E + e];
-                }
-                z += (double)g;
-              }
-            }
-          };
-          expo(rp, op, ep, zp);
-          if (need_q) {
-#pragma unroll
-            for (int k = 0; k < NK; ++k) {
-              float x[E];
-              unpack16<T>(rq[k], x);
-#pragma unroll
-              for (int e = 0; e < E; ++e) mq = piece_v<T, TH>(s0, k, t) < V ? fmaxf(mq, x[e]) : mq;
-            }
-            mq = block_max<TH>(mq, red);
-            opaque(rq);
-            expo(rq, mq * l2T, eq, zq);
-          } else {
-#pragma unroll
-            for (int i = 0; i < ac_ct<T>(); ++i) eq[i] = 0.f;
-          }
-          asm volatile("" : "+v"(c_lp), "+v"(c_lq), "+v"(c_u), "+v"(c_us));  // first use: here
-          if (t < K) {
-            s_lp[t] = rawf<T>(c_lp);
-            if constexpr (TOPK) {  // s_lq holds 1 where the child repeats an earlier sibling's token
-              const int x = si.tok[si.kids[t]];
-              bool dup = false;
-              for (int j = 0; j < t; ++j) dup |= si.tok[si.kids[j]] == x;
-              s_lq[t] = dup ? 1.f : 0.f;
-            } else {
-              s_lq[t] = rawf<T>(c_lq);
-            }
-            s_u[t] = __uint_as_float(c_u);
-          }
-          if (t == TH - 1) s_us = __uint_as_float(c_us);
-        }
-        zp = block_sum<TH>(zp, red);  // its barriers also publish the children's values
-        zq = block_sum<TH>(zq, red);
-        if (exchange<TH>(gslots, G, rank, ++xtag, TOPK ? 4 : 6, xv, ws.err, cancel, &s_xc, __float_as_uint(mp),
-                     __float_as_uint(mq), dlo(zp), dhi(zp), dlo(zq), dhi(zq)))
-          return;
-        // global statistics: lane k of every wave takes member k's partials (G <= 64); the
-        // butterfly reductions give every lane, wave and member the same values
-        double Zp, Zq, fp, fq;
-        float Mp, Mq;
-        {
-          const bool on = lane < G;
-          const int k = on ? lane : 0;
-          const float mpk = on ? __uint_as_float(xv[k][0]) : -FLT_MAX;
-          const float mqk = on ? __uint_as_float(xv[k][1]) : -FLT_MAX;
-          Mp = wave_maxf(mpk);
-          Mq = wave_maxf(mqk);
-          const double sp = on ? exp2((double)(mpk - Mp) * (double)l2T) : 0.0;  // member k's scale
-          const double sq = on && need_q ? exp2((double)(mqk - Mq) * (double)l2T) : 0.0;
-          Zp = wave_sumd(on ? dof(xv[k][2], xv[k][3]) * sp : 0.0);
-          Zq = wave_sumd(on && need_q ? dof(xv[k][4], xv[k][5]) * sq : 0.0);
-          fp = __shfl(sp, rank) / Zp;                   // p(v) = ep(v) * fp on this slice
-          fq = need_q ? __shfl(sq, rank) / Zq : 0.0;
-        }
-        // a row without a finite positive normaliser (a NaN or +Inf logit, or no finite entry)
-        // accepts no child: the walk stops here with bonus 0 and the sequence reports status 8.
-        // Every member holds the same totals, so all of them leave here together.
-        if (!(Zp > 0.0 && Zp < (double)INFINITY) || (need_q && !(Zq > 0.0 && Zq < (double)INFINITY))) {
-          if (rank == 0) {
-            if (t == 0) st_u64(&ws.res[item], res_word(-1, 0) | AC_RES_BAD);
-            done_by_me = 1;
-          }
-          return;
-        }
-        // residual weight of one entry in units of fp: max(0, ep - kappa eq) for kappa > 0
-        auto wgt = [&](int i, float kappa) -> float { return fmaxf(fmaf(-kappa, eq[i], ep[i]), 0.f); };
-        auto slice_sum = [&](float kappa) -> double {  // kappa > 0
-          double acc = 0.0;
-#pragma unroll
-          for (int k = 0; k < NK; ++k) {
-            float g = 0.f;  // fp32 partial of one piece, fp64 across pieces
-#pragma unroll
-            for (int e = 0; e < E; ++e) g += wgt(k * E + e, kappa);
-            acc += (double)g;
-          }
-          return acc;
-        };
-        // ---- accept tests along the residual chain
-        double c = 0.0, Dn = 1.0, c_prev = 0.0;
-        int accepted = -1;
-        if constexpr (TOPK) {
-          // child j's proposal is the point mass at its token x: the test is u < p_cur(x), and
-          // a rejection zeroes x.  p_cur is p restricted to the tokens not rejected yet at this
-          // row, renormalised by their mass `rem`; a repeated token has mass 0.  No exchange:
-          // p(x) is known from the row statistics.
-          double rem = 1.0;
-          for (int j = 0; j < K; ++j) {
-            const double px = (double)expf((s_lp[j] - Mp) * invT) / Zp;
-            const bool dup = s_lq[j] != 0.f;
-            const double cur = dup ? 0.0 : px / rem;
-            if ((double)s_u[j] < cur) { accepted = si.kids[j]; break; }
-            if (!dup && rem - px > 0.0) rem -= px;  // a residual without mass (rounding only) is kept
-          }
-          // the bonus below zeroes the children's tokens (c != 0) and, should rounding leave
-          // that residual without mass, falls back to p itself (c_prev = 0)
-          if (accepted < 0 && K > 0) c = 1.0;
-        } else
-        for (int j = 0; j < K; ++j) {
-          const double px = (double)expf((s_lp[j] - Mp) * invT) / Zp;
-          const double qx = (double)expf((s_lq[j] - Mq) * invT) / Zq;
-          const double cur = fmax(0.0, px - c * qx) / Dn;
-          const double u = (double)s_u[j];
-          if (qx > 0.0 ? (u < cur / qx) : true) { accepted = si.kids[j]; break; }
-          // rejection: next residual coefficient; its normaliser is needed only for a later test,
-          // after the last child the bonus scan below computes it as its total
-          const double cn = c + Dn;
-          if (j == K - 1) { c_prev = c; c = cn; break; }
-          // max(0, p - cn q) = fp * max(0, ep - kappa eq) on this slice, kappa = cn fq / fp
-          const float kappa = (float)(cn * fq / fp);
-          const double sl = block_sum<TH>(slice_sum(kappa), red) * fp;
-          if (exchange<TH>(gslots, G, rank, ++xtag, 2, xv, ws.err, cancel, &s_xc, dlo(sl), dhi(sl))) return;
-          // lane k of every wave takes member k's sum (G <= 64): one LDS read and a DPP reduction
-          const double S = wave_sumd(lane < G ? dof(xv[lane][0], xv[lane][1]) : 0.0);
-          __syncthreads();
-          if (S > 0.0) { c = cn; Dn = S; }  // S == 0 only through rounding: keep the residual
-        }
-        if (accepted >= 0) {
-          if (rank == 0) {
-            if (t == 0) st_u64(&ws.res[item], res_word(accepted, -1));
-            done_by_me = 1;
-          }
-        } else {
-          // ---- bonus: smallest v whose ascending cumulative residual exceeds u * total.
-          // A residual of total 0 (reachable only through rounding) falls back to the previous one.
-          // Ids ascend piece by piece: piece (k, t) holds the slice-local ids (k * TH + t) * E ..
-          // + E - 1.  The weights are staged in LDS in id order (after which the exponentials in
-          // registers are dead) with their piece sums; row totals over t give the coarse
-          // cumulative sum, one work-group scan over the pieces of the row that crosses the
-          // threshold finds the piece, and one thread walks its E entries.  Piece sums are fp32
-          // over E entries; every sum above that is fp64.
-          const int wv = t >> 6;
-          const double us = (double)s_us;
-          for (int attempt = 0; attempt < 2; ++attempt) {
-            // c == 0 (no rejection at this row): the weights are p itself
-            const float kappa = TOPK || c == 0.0 ? 0.f : (float)(c * fq / fp);
-            auto stage = [&](auto residual) {
-#pragma unroll
-              for (int k = 0; k < NK; ++k) {
-                float w[E], x = 0.f;
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                  if constexpr (decltype(residual)::value) w[e] = wgt(k * E + e, kappa);
-                  else w[e] = ep[k * E + e];
-                  x += w[e];
-                }
-                float* dst = s_w + (k * TH + t) * E;
-#pragma unroll
-                for (int e = 0; e < E; e += 4) *(float4*)(dst + e) = make_float4(w[e], w[e + 1], w[e + 2], w[e + 3]);
-                s_g[k * TH + t] = x;
-              }
-            };
-            if (kappa == 0.f) stage(std::false_type{});  // uniform branch
-            else stage(std::true_type{});
-            if (TOPK && c != 0.0) {  // every child was rejected: zero their tokens in this slice
-              __syncthreads();
-              const int x = t < K ? si.tok[si.kids[t]] - s0 : -1;
-              const bool mine = x >= 0 && x < ac_slice<T, TH>();
-              if (mine) s_w[x] = 0.f;
-              __syncthreads();
-              if (mine) {  // its piece's sum again (children sharing a piece write the same value)
-                const int pc = x / E;
-                float g = 0.f;
-                for (int e = 0; e < E; ++e) g += s_w[pc * E + e];
-                s_g[pc] = g;
-              }
-            }
-            __syncthreads();
-            for (int k = wv; k < NK; k += NW) {  // wave wv totals rows wv, wv + NW, ...
-              double x = 0.0;
-              for (int i = lane; i < TH; i += 64) x += (double)s_g[k * TH + i];
-              x = wave_sumd(x);
-              if (lane == 0) s_col[k] = x;
-            }
-            __syncthreads();
-            double col = 0.0;
-            for (int k = 0; k < NK; ++k) col += s_col[k];
-            const double sl = col * fp;
-            if (exchange<TH>(gslots, G, rank, ++xtag, 2, xv, ws.err, cancel, &s_xc, dlo(sl), dhi(sl))) return;
-            // lane k holds member k's slice total; one inclusive scan gives every member the
-            // same prefixes, total and owner
-            const double sk = lane < G ? dof(xv[lane][0], xv[lane][1]) : 0.0;
-            const double incl_k = wave_scand(sk, lane);
-            const double total = laned(incl_k, G - 1);
-            const double before = laned(incl_k - sk, rank);
-            if (!(total > 0.0) && attempt == 0 && c != 0.0) {  // uniform: retry with the previous residual
-              c = c_prev;
-              __syncthreads();
-              continue;
-            }
-            // the slice whose inclusive prefix first exceeds the threshold draws the token
-            const double thr = us * total;
-            int owner = G - 1;
-            {
-              const uint64_t over = __ballot(lane < G && incl_k > thr);
-              if (over) owner = __ffsll((long long)over) - 1;
-            }
-            if (rank == owner) {
-              const double lthr = (thr - before) / fp;  // threshold in this slice's units
-              // the piece row whose cumulative total first exceeds it (uniform)
-              int ks = -1;
-              double below = 0.0;
-              for (int k = 0; k < NK; ++k) {
-                if (below + s_col[k] > lthr) { ks = k; break; }
-                below += s_col[k];
-              }
-              int h = 0x7fffffff;
-              double excl = 0.0;
-              if (ks >= 0) {  // inclusive scan of row ks over the threads, in id order
-                const float gk = s_g[ks * TH + t];
-                double incl = wave_scand((double)gk, lane);
-                if (lane == 63) red.d[wv] = incl;
-                if (t == 0) s_first = 0x7fffffff;
-                __syncthreads();
-                for (int w2 = 0; w2 < wv; ++w2) incl += red.d[w2];
-                incl += below;
-                excl = incl - (double)gk;
-                const uint64_t over = __ballot(incl > lthr);  // one atomic per wave
-                if (over && lane == 0) atomicMin(&s_first, wv * 64 + __ffsll((long long)over) - 1);
-                __syncthreads();
-                h = s_first;
-              }
-              if (h != 0x7fffffff) {
-                if (t == h) {  // walk the E entries of piece (ks, h)
-                  const int p0 = (ks * TH + t) * E;  // slice-local id of its first entry
-                  double run = excl;
-                  int pick = -1, lastpos = -1;
-                  for (int e = 0; e < E; ++e) {
-                    const float w = s_w[p0 + e];
-                    if (w > 0.f) {
-                      lastpos = s0 + p0 + e;
-                      run += (double)w;
-                      if (pick < 0 && run > lthr) pick = s0 + p0 + e;
-                    }
-                  }
-                  if (pick < 0) pick = lastpos >= 0 ? lastpos : min(s0 + p0 + E, V) - 1;
-                  st_u64(&ws.res[item], res_word(-1, pick));
-                }
-              } else {
-                // rounding left the threshold unreached: the highest id with a positive weight
-                // (in rows up to ks when a row was found, else in the whole slice)
-                const int klim = ks >= 0 ? ks : NK - 1;
-                int lp = -1;
-                for (int k = 0; k <= klim; ++k) {
-                  const int p0 = (k * TH + t) * E;
-                  for (int e = 0; e < E; ++e) lp = s_w[p0 + e] > 0.f ? s0 + p0 + e : lp;
-                }
-                for (int o = 32; o > 0; o >>= 1) lp = max(lp, __shfl_xor(lp, o));
-                if (t == 0) s_lpos = -1;
-                __syncthreads();
-                if (lane == 0) atomicMax(&s_lpos, lp);
-                __syncthreads();
-                if (t == 0) {
-                  const int pick = s_lpos >= 0 ? s_lpos : min(s0 + ac_slice<T, TH>(), V) - 1;
-                  st_u64(&ws.res[item], res_word(-1, pick));
-                }
-              }
-              done_by_me = 1;
-            }
-            break;
-          }
-        }
-        }();
-      }
-
-      // ---- stochastic: the walk advances as rows resolve.  frontier[b] is the first row of
-      // the accepted path not yet resolved.  The work-group that publishes that row claims
-      // the frontier (compare-and-swap to BUSY) and follows the path through the rows that
-      // are already resolved; it either reaches the stop row (it then writes the outputs
-      // and raises cancel[b], so the sequence's other rows stop) or moves the frontier to
-      // the next unresolved row and checks that row once more, since its publisher may have
-      // looked at the frontier before the move (each side completes its store before its
-      // load, so at least one of them sees the other's).
-      if (STO && done_by_me) {
-        mem_complete();  // this thread's row-result store (if any) has completed
-        __syncthreads();
-        uint32_t* front = &ws.frontier[b];
-        uint64_t* rr = ws.res + (int64_t)b * (N + 1);
-        uint64_t* s_rr = (uint64_t*)s_w;  // the sequence's row results (the bonus staging buffer is free)
-        if (t == 0) {
-          s_fin = 0;
-          if (incr) {
-            s_claim = cas_u32(front, (uint32_t)r, AC_FRONT_BUSY) ? r : -1;
-          } else {  // the last row of the sequence to resolve walks
-            s_claim = -1;
-            s_fin = add_u32(&ws.seqdone[b], 1u) + 1 == (uint32_t)si.nlive;
-            if (s_fin) st_u32(&ws.seqdone[b], 0u);  // every row of b has been counted
-          }
-        }
-        __syncthreads();
-        if (s_fin) {
-          for (int x = t; x <= N; x += TH) s_rr[x] = ld_u64(&rr[x]);
-          __syncthreads();
-        }
-        for (int guard = 0; s_claim >= 0 && guard <= N + 1; ++guard) {  // uniform
-          for (int x = t; x <= N; x += TH) s_rr[x] = ld_u64(&rr[x]);
-          __syncthreads();
-          if (t == 0) {
-            int row = s_claim, claim = -1;
-            bool stop = false;
-            for (int n = 0; n <= N + 1; ++n) {
-              const uint64_t v = s_rr[row];
-              if (!res_ready(v)) break;
-              const int ch = res_child(v);
-              if (ch < 0 || ch >= N) { stop = true; break; }
-              row = ch + 1;
-            }
-            if (stop) {
-              s_fin = 1;
-            } else {
-              st_u32(front, (uint32_t)row);
-              mem_complete();
-              if (res_ready(ld_u64(&rr[row])) && cas_u32(front, (uint32_t)row, AC_FRONT_BUSY)) claim = row;
-            }
-            s_claim = claim;
-          }
-          __syncthreads();
-        }
-        if (s_fin) {
-          // the path from the root in the LDS copy: every row on it was resolved before the
-          // frontier passed it
-          if (t == 0) {
-            int row = 0, n = 0;
-            for (;;) {
-              const int ch = res_child(s_rr[row]);
-              if (ch < 0 || ch >= N || n >= SV_MAX_DEPTH) break;
-              si.path[n++] = ch;
-              row = ch + 1;
-            }
-            si.flag = (n << 16) | row;  // A and the stop row
-            s_hit = res_token(s_rr[row]);
-            s_bad = res_bad(s_rr[row]) ? 1 : 0;
-            s_to = ld_u32(ws.err) != 0;
-          }
-          __syncthreads();
-          const int A = si.flag >> 16, stop_row = si.flag & 0xffff, bonus = s_hit;
-          const int Dm = a.max_depth;
-          if (t == 0) {
-            a.accept_len[b] = A;
-            a.num_out[b] = A + 1;
-            a.stop_row[b] = stop_row;
-            a.status[b] = s_to ? SV_SEQ_TIMEOUT
-                               : (si.bad_token ? SV_SEQ_TOKEN : (s_bad ? SV_SEQ_NONFINITE : 0));
-          }
-          if (t < Dm) a.accept_rows[(int64_t)b * Dm + t] = t < A ? si.path[t] + 1 : 0;
-          if (t <= Dm)
-            a.out_tokens[(int64_t)b * (Dm + 1) + t] = t < A ? si.tok[si.path[t]] : (t == A ? bonus : 0);
-          // the accepted path into the cache (nothing after a timeout: the path may be wrong)
-          if (has_cm) svc::walker_commit(cm, b, s_to ? 0 : A, si.path);
-          if (incr && t == 0) st_u32(cancel, 1u);  // the sequence's remaining rows are not needed
-          if (!incr)  // every row result of b has been read: leave them cleared for the next call
-            for (int x = t; x <= N; x += TH) st_u64(&rr[x], 0ull);
-        }
-      }
-
-      // ---- greedy: the work-group that wrote the row result counts it; the last row of a
-      // sequence walks
-      if (MODE == SV_GREEDY && done_by_me) {
-        mem_complete();  // this thread's row-result stores (if any) have completed
-        __syncthreads();
-        if (t == 0) {
-          const uint32_t old = add_u32(&ws.seqdone[b], 1u);
-          s_last = old + 1 == (uint32_t)si.nlive;
-        }
-        __syncthreads();
-        if (s_last) {
-          // ----------------------------------------------------- walk of sequence b
-          if (t == 0) s_to = ld_u32(ws.err) != 0;  // read after the barriers below
-          int A = 0, stop_row = 0, bonus = 0;
-          uint64_t* rr = ws.res + (int64_t)b * (N + 1);
-          {
-            // match[i]: token equals its parent row's argmax; accepted: the whole root path matches
-            {  // wave w holds nodes 64 w .. 64 w + 63: its ballot is bitset word w
-              const uint64_t mb =
-                  __ballot(t < N && si.usable[t] && a.tokens[(int64_t)b * N + t] == res_token(ld_u64(&rr[si.par[t] + 1])));
-              if (lane == 0 && (t >> 6) < SV_MAX_W) s_match[t >> 6] = mb;
-            }
-            __syncthreads();
-            const int W = (N + 63) / 64;
-            int key = -1;
-            if (t < N && si.usable[t]) {
-              const uint64_t* arow = a.anc_bits + ((int64_t)b * N + t) * W;
-              bool ok = true;
-              for (int w = 0; w < W; ++w) ok &= (arow[w] & ~s_match[w]) == 0;
-              if (ok) key = (a.depth[(int64_t)b * N + t] << 9) | (511 - t);  // deepest, then lowest index
-            }
-            {
-              float kv = (float)key;
-              int ki = key;
-              block_argmax<TH>(kv, ki, red);
-              key = (int)kv;
-            }
-            if (key >= 0) {
-              A = key >> 9;
-              const int stop = 511 - (key & 511);
-              stop_row = stop + 1;
-              if (t == 0) {
-                int node = stop;
-                for (int k = A - 1; k >= 0; --k) { si.path[k] = node; node = si.par[node]; }
-              }
-            }
-            if (row_live(a, si, stop_row)) {
-              if (t == 0) s_hit = res_token(ld_u64(&rr[stop_row]));
-              __syncthreads();
-              bonus = s_hit;
-            } else {
-              // leaf stop row: argmax by this work-group, one slice at a time with the next
-              // slice's loads in flight (a thread visits its entries in ascending id)
-              const T* srow = (const T*)a.target_logits + ((int64_t)b * (N + 1) + stop_row) * V;
-              float best = -FLT_MAX;
-              int arg = 0x7fffffff;
-              uint4 r0[NK], r1[NK];
-              auto consume = [&](const uint4 (&raw)[NK], int gs) {
-#pragma unroll
-                for (int k = 0; k < NK; ++k) {
-                  float x[E];
-                  unpack16<T>(raw[k], x);
-                  const int v = piece_v<T, TH>(gs * ac_slice<T, TH>(), k, t);
-#pragma unroll
-                  for (int e = 0; e < E; ++e)
-                    if (v + e < V && x[e] > best) { best = x[e]; arg = v + e; }
-                }
-              };
-              load_pieces<T, TH>(srow, 0, V, aligned, t, r0);
-              for (int gs = 0; gs < G; gs += 2) {
-                if (gs + 1 < G) load_pieces<T, TH>(srow, (gs + 1) * ac_slice<T, TH>(), V, aligned, t, r1);
-                consume(r0, gs);
-                if (gs + 1 >= G) break;
-                if (gs + 2 < G) load_pieces<T, TH>(srow, (gs + 2) * ac_slice<T, TH>(), V, aligned, t, r0);
-                consume(r1, gs + 1);
-              }
-              block_argmax<TH>(best, arg, red);
-              bonus = arg;
-            }
-          }
-          __syncthreads();
-          const int Dm = a.max_depth;
-          if (t == 0) {
-            a.accept_len[b] = A;
-            a.num_out[b] = A + 1;
-            a.stop_row[b] = stop_row;
-            a.status[b] = s_to ? SV_SEQ_TIMEOUT : (si.bad_token ? SV_SEQ_TOKEN : 0);
-            st_u32(&ws.seqdone[b], 0u);  // every row of b has been counted: ready for the next call
-          }
-          // every row result of b has been read: leave them cleared for the next call
-          for (int x = t; x <= N; x += TH) st_u64(&rr[x], 0ull);
-          if (t < Dm) a.accept_rows[(int64_t)b * Dm + t] = t < A ? si.path[t] + 1 : 0;
-          if (t <= Dm)
-            a.out_tokens[(int64_t)b * (Dm + 1) + t] = t < A ? a.tokens[(int64_t)b * N + si.path[t]] : (t == A ? bonus : 0);
-          // the accepted path into the cache (nothing after a timeout: the path may be wrong)
-          if (has_cm) svc::walker_commit(cm, b, s_to ? 0 : A, si.path);
-        }
-      }
-    }
-  }
-
-  // ---- leave every counter and exchange slot zeroed for the next call.  The three exit
-  // counts (group, sequence, grid) are independent and go out together; the last arrival
-  // at each clears what it guards.
-  mem_complete();  // this work-group's stores (results, outputs) have completed
-  __syncthreads();
-  // (stochastic wide trees only: elsewhere the walker is the sequence's last reader of its
-  // row results and clears them itself)
-  const bool seq_item = MODE != SV_GREEDY && N > 2 * a.max_depth && item < (int64_t)a.B * (N + 1);
-  const int bq = seq_item ? (int)(item / (N + 1)) : 0;
-  if (t == 0) {
-    const uint32_t og = G > 1 ? add_u32(ws.gexit + grp, 1u) : 0u;
-    const uint32_t os = seq_item ? add_u32(&ws.seqexit[bq], 1u) : 0u;
-    const uint32_t oe = add_u32(ws.err + 1, 1u);
-    s_last = G == 1 || og + 1 == (uint32_t)G;  // every member of the group passed its last exchange
-    s_claim = seq_item && os + 1 == (uint32_t)((N + 1) * G);  // every work-group of the sequence left
-    s_fin = oe + 1 == gridDim.x;                              // the whole grid has finished
-  }
-  __syncthreads();
-  // (a member that left early on a finished walk may have exchanged less than the others,
-  // so the slots of every live row are cleared)
-  if (s_last && (xtag > 0 || live_row))
-    for (int i = t; i < G * 2 * AC_XW; i += TH) st_u64(&gslots[i / AC_XW].w[i % AC_XW], 0ull);
-  if (s_claim) {  // stochastic: the sequence's row results, frontier, cancel flag and exit count
-    for (int x = t; x <= N; x += TH) st_u64(&ws.res[(int64_t)bq * (N + 1) + x], 0ull);
-    if (t == 0) {
-      st_u32(&ws.frontier[bq], 0u);
-      st_u32(&ws.cancel[bq], 0u);
-      st_u32(&ws.seqexit[bq], 0u);
-    }
-  }
-  // After a timeout some row may never have been published (members that stopped waiting can
-  // disagree), so some walk may never have run: the last work-group of the grid reports status 7
-  // for every sequence and clears every per-sequence word for the next call.  Every other
-  // work-group has exited, so nothing reads these words any more.
-  const bool timed_out = s_fin && ld_u32(ws.err) != 0;
-  if (timed_out) {
-    for (int x = t; x < a.B; x += TH) {
-      st_i(&a.status[x], SV_SEQ_TIMEOUT);
-      st_u32(&ws.seqdone[x], 0u);
-      st_u32(&ws.frontier[x], 0u);
-      st_u32(&ws.cancel[x], 0u);
-      st_u32(&ws.seqexit[x], 0u);
-    }
-    for (int64_t x = t; x < (int64_t)a.B * (N + 1); x += TH) st_u64(&ws.res[x], 0ull);
-  }
-  __syncthreads();  // every thread has read the timeout word before it is cleared
-  if (t == 0) {
-    if (G > 1 && s_last) st_u32(ws.gexit + grp, 0u);
-    if (s_fin) {  // clear the timeout flag
-      st_u32(ws.err, 0u);
-      st_u32(ws.err + 1, 0u);
-    }
-  }
+  SwView sw;  // (assigned, not brace-initialised: LDS addresses are not constant initialisers)
+  sw.p01 = s_w;
+  sw.p23 = s_w + 2 * RF;
+  sw.p47 = s_w + 4 * RF;
+  sw.rf = RF;
+  const AccRole role{(int)blockIdx.x, (int)gridDim.x, AC_REGION_ALL, 0, (a.N + 1) * G};
+  accept_body<T, MODE, ALIGNED, TH, true>(a, G, ws, cm, has_cm, role, S, sw);
 }
 
 // SV_FLAG_VALIDATE: one work-group per logits row (target rows, then draft rows in mode 1) looks
@@ -1192,34 +106,6 @@ __global__ void __launch_bounds__(256) k_nonfinite_rows(const T* __restrict__ ta
   if (fin) s_any_fin = 1;
   __syncthreads();
   if (threadIdx.x == 0 && (s_any_bad || !s_any_fin)) atomicCAS(&status[b], 0, SV_SEQ_NONFINITE);
-}
-
-int groups_G(const sv_accept_args& a) {
-  const int slice = acc_threads(a) * (a.logits_dtype == SV_BF16 ? ac_ct<uint16_t>() : ac_ct<float>());
-  const int G = (a.V + slice - 1) / slice;
-  return G < 1 ? 1 : G;
-}
-// one group per row, rounded up to a whole number of groups per XCD
-int64_t num_groups(const sv_accept_args& a) { return ((int64_t)a.B * (a.N + 1) + 7) / 8 * 8; }
-
-struct WsLayout {
-  size_t gexit, seqdone, err, res, frontier, cancel, seqexit, xs, total;
-};
-WsLayout ws_layout(const sv_accept_args& a) {
-  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  const size_t NG = (size_t)num_groups(a), G = (size_t)groups_G(a);
-  WsLayout l{};
-  size_t o = 0;
-  l.gexit = o; o = up(o + NG * 4);
-  l.seqdone = o; o = up(o + (size_t)a.B * 4);
-  l.err = o; o = up(o + 8);
-  l.res = o; o = up(o + (size_t)a.B * (a.N + 1) * sizeof(uint64_t));
-  l.frontier = o; o = up(o + (size_t)a.B * 4);
-  l.cancel = o; o = up(o + (size_t)a.B * 4);
-  l.seqexit = o; o = up(o + (size_t)a.B * 4);
-  l.xs = o; o = up(o + NG * G * 2 * sizeof(XSlot));
-  l.total = o;
-  return l;
 }
 
 template <typename T, int M, bool AL>
@@ -1269,8 +155,8 @@ extern "C" sv_status sv_accept(const sv_accept_args* args, void* stream) {
     return SV_ERR_INVALID_ARGUMENT;
   if (a.flags & ~(uint32_t)SV_FLAG_VALIDATE) return SV_ERR_INVALID_ARGUMENT;
   if (a.B == 0) return SV_OK;
-  // modes 1 and 2 read neither mask output when depth is NULL (depths come from the parents)
-  const bool mask_free = (a.mode == SV_STOCHASTIC || a.mode == SV_TOPK_DRAFT) && !a.depth;
+  // modes 0, 1 and 2 read neither mask output when depth is NULL (depths come from the parents)
+  const bool mask_free = a.mode != SV_THRESHOLD && !a.depth;
   if (!a.parents || !a.tokens || (!mask_free && (!a.anc_bits || !a.depth)) || !a.target_logits || !a.accept_len || !a.accept_rows ||
       !a.out_tokens || !a.num_out || !a.stop_row || !a.status || !a.workspace)
     return SV_ERR_INVALID_ARGUMENT;
@@ -1301,16 +187,7 @@ extern "C" sv_status sv_accept(const sv_accept_args* args, void* stream) {
   if (G > AC_MAXG) return SV_ERR_UNSUPPORTED;
   const int64_t blocks = num_groups(a) * G;
   if (blocks > 0x7fffffff) return SV_ERR_UNSUPPORTED;
-  char* base = (char*)a.workspace;
-  AccWs ws;
-  ws.gexit = (uint32_t*)(base + l.gexit);
-  ws.seqdone = (uint32_t*)(base + l.seqdone);
-  ws.err = (uint32_t*)(base + l.err);
-  ws.res = (uint64_t*)(base + l.res);
-  ws.frontier = (uint32_t*)(base + l.frontier);
-  ws.cancel = (uint32_t*)(base + l.cancel);
-  ws.seqexit = (uint32_t*)(base + l.seqexit);
-  ws.xs = (XSlot*)(base + l.xs);
+  const AccWs ws = ws_views(a.workspace, l);
   hipStream_t st = (hipStream_t)stream;
   const dim3 grid((unsigned)blocks);
   // rows start on 16 bytes when the row pitch and the base pointers are multiples of 16

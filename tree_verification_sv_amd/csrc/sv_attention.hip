@@ -27,7 +27,7 @@
 #include <float.h>
 #include <math.h>
 
-#include "sv_common.h"
+#include "sv_attn_dev.h"
 
 namespace {
 
@@ -40,7 +40,6 @@ constexpr int KT = 64;  // keys per tile
 #ifndef SV_ATTN_MIN_SPLIT_TILES
 #define SV_ATTN_MIN_SPLIT_TILES 2  // a prefix split covers at least this many tiles
 #endif
-constexpr float LOG2E = 1.4426950408889634f;
 constexpr int TARGET_WG = 256;
 
 struct AttnPlan {
@@ -50,31 +49,6 @@ struct AttnPlan {
   uint16_t* opart;  // [units][nsplit][QT][D] bf16: the split's output row O / l
   float* mlpart;    // [units][nsplit][QT][2]: running max (scaled by log2 e) and l
 };
-
-__device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
-
-// Data checks behind the optional status array, run by one work-group per
-// sequence: 6 when prefix_len lies outside [0, capacity] (it is clamped), 5 when
-// a needed block-table entry is the ghost block 0 or outside the pool (read as
-// the ghost block).
-__device__ void write_seq_status(const sv_attn_args& a, int b, int cap) {
-  __shared__ int s_code;
-  if (threadIdx.x == 0) s_code = 0;
-  __syncthreads();
-  const int L0 = a.prefix_len[b];
-  if (L0 < 0 || L0 > cap) {
-    if (threadIdx.x == 0) s_code = SV_SEQ_CAPACITY;
-  } else if (a.paged) {
-    // with the tree rows resident in the cache, positions L0 .. L0 + N - 1 are read too
-    const int nblk = (L0 + (a.tree_in_cache ? a.N : 0) + a.block_size - 1) / a.block_size;
-    for (int k = threadIdx.x; k < nblk; k += blockDim.x) {
-      const int id = a.block_table[(int64_t)b * a.max_blocks + k];
-      if (id < 1 || id >= a.num_blocks) atomicOr(&s_code, SV_SEQ_BLOCK);
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) a.status[b] = s_code;
-}
 
 // ------------------------------------------------------------------ MFMA path
 // One 64-key tile in LDS: K rows then V rows, row-major without padding.  The
@@ -98,35 +72,6 @@ struct Tile {
     return CPR == 16 ? (((r << 1) & 14) | ((r >> 3) & 1)) : ((r & 6) | ((r >> 3) & 1));
   }
 };
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// 32-bit LDS address of a pointer into a __shared__ array
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-// Transposing 8-byte LDS reads (ds_read_b64_tr_b16): in every 16-lane group,
-// lane 4q+e receives element e of the 8-byte pieces addressed by lanes q, 4+q,
-// 8+q and 12+q.  Written as inline assembly: through the builtin, the compiler
-// cannot tell these reads from the tile buffer that is still being filled by
-// direct global->LDS loads and would wait for those loads as well.
-// Four transposing reads (two d-blocks, low and high 8 keys) issued without waiting;
-// tr_wait<N> must run before the values are used: it waits until at most N LDS
-// operations are outstanding, and ties the registers to that point so that the
-// compiler neither reads nor moves them earlier.
-__device__ __forceinline__ void tr_read_issue(uint2 (&lo)[2], uint2 (&hi)[2], const uint32_t (&alo)[2],
-                                              const uint32_t (&ahi)[2]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %4\n\tds_read_b64_tr_b16 %1, %5\n\t"
-      "ds_read_b64_tr_b16 %2, %6\n\tds_read_b64_tr_b16 %3, %7"
-      : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1])
-      : "v"(alo[0]), "v"(ahi[0]), "v"(alo[1]), "v"(ahi[1])
-      : "memory");
-}
-template <int N>
-__device__ __forceinline__ void tr_wait(uint2 (&lo)[2], uint2 (&hi)[2]) {
-  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(lo[0]), "+v"(hi[0]), "+v"(lo[1]), "+v"(hi[1]) : "n"(N) : "memory");
-}
 
 template <int D>
 __global__ void __launch_bounds__(MF_THREADS, 2) k_attn_mfma(sv_attn_args a, AttnPlan p) {

@@ -1,0 +1,566 @@
+// Device code of the ancestor-masked tree attention shared by sv_attention.hip
+// (the sv_tree_attention kernels) and sv_step.hip (the one-launch verification
+// step): LDS helpers, the per-sequence data checks, and the step's attention and
+// merge roles.
+//
+// "EAGLE-Pangu: Accelerator-Safe Tree Speculative Decoding on Ascend NPUs",
+// technical summary sec. 2 ("Ejecucion del Maestro con Mascara de Arbol
+// Fusionada"): each draft token attends to the committed prefix, to its
+// ancestors and to itself.  In the one-launch step the ancestor sets are derived
+// from the parent array inside the launch ("Semantica de Tensores de Arbol
+// Segura": the same walk and checks as sv_build_tree_mask), so no mask launch
+// precedes the attention.
+#pragma once
+#include <float.h>
+#include <math.h>
+
+#include "sv_mask_dev.h"
+
+namespace {
+
+constexpr float LOG2E = 1.4426950408889634f;
+
+__device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
+
+// Data checks behind the optional status array, run by one work-group per
+// sequence: 6 when prefix_len lies outside [0, capacity] (it is clamped), 5 when
+// a needed block-table entry is the ghost block 0 or outside the pool (read as
+// the ghost block).
+__device__ void write_seq_status(const sv_attn_args& a, int b, int cap) {
+  __shared__ int s_code;
+  if (threadIdx.x == 0) s_code = 0;
+  __syncthreads();
+  const int L0 = a.prefix_len[b];
+  if (L0 < 0 || L0 > cap) {
+    if (threadIdx.x == 0) s_code = SV_SEQ_CAPACITY;
+  } else if (a.paged) {
+    // with the tree rows resident in the cache, positions L0 .. L0 + N - 1 are read too
+    const int nblk = (L0 + (a.tree_in_cache ? a.N : 0) + a.block_size - 1) / a.block_size;
+    for (int k = threadIdx.x; k < nblk; k += blockDim.x) {
+      const int id = a.block_table[(int64_t)b * a.max_blocks + k];
+      if (id < 1 || id >= a.num_blocks) atomicOr(&s_code, SV_SEQ_BLOCK);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) a.status[b] = s_code;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 32-bit LDS address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// Transposing 8-byte LDS reads (ds_read_b64_tr_b16): in every 16-lane group,
+// lane 4q+e receives element e of the 8-byte pieces addressed by lanes q, 4+q,
+// 8+q and 12+q.  Written as inline assembly: through the builtin, the compiler
+// cannot tell these reads from the tile buffer that is still being filled by
+// direct global->LDS loads and would wait for those loads as well.
+// Four transposing reads (two d-blocks, low and high 8 keys) issued without waiting;
+// tr_wait<N> must run before the values are used: it waits until at most N LDS
+// operations are outstanding, and ties the registers to that point so that the
+// compiler neither reads nor moves them earlier.
+__device__ __forceinline__ void tr_read_issue(uint2 (&lo)[2], uint2 (&hi)[2], const uint32_t (&alo)[2],
+                                              const uint32_t (&ahi)[2]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\tds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\tds_read_b64_tr_b16 %3, %7"
+      : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1])
+      : "v"(alo[0]), "v"(ahi[0]), "v"(alo[1]), "v"(ahi[1])
+      : "memory");
+}
+template <int N>
+__device__ __forceinline__ void tr_wait(uint2 (&lo)[2], uint2 (&hi)[2]) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(lo[0]), "+v"(hi[0]), "+v"(lo[1]), "+v"(hi[1]) : "n"(N) : "memory");
+}
+
+// ------------------------------------------------------------------ one-launch step: attention
+// The step's work-groups have 256 threads (four waves), so that an attention
+// work-group and an acceptance work-group can share a compute unit (two
+// work-groups of at most 80 KB of LDS each).  An attention work-group owns one
+// (sequence, KV head) pair, a tile of 128 query rows (wave w: rows 32 w .. 32 w +
+// 31) and a key range of the prefix (the pair's last split also takes the tree
+// keys), in 32-key K/V tiles streamed into LDS by direct loads, one tile in flight
+// while the other is consumed.  The MFMA tiling, swizzle, online softmax and
+// transposing V reads are those of k_attn_mfma with one 32-key block per tile.
+// Several splits write normalised bf16 rows O / l with fp32 (m, l) and count in
+// on the unit's arrival counter (release); merge work-groups, placed after every
+// attention work-group in the grid, wait for the count (acquire) and combine.
+constexpr int ST_WAVES = 4;
+constexpr int ST_THREADS = 64 * ST_WAVES;
+constexpr int ST_KT = 32;              // keys per tile
+constexpr int ST_QT = 32 * ST_WAVES;   // query rows per work-group
+constexpr uint32_t ST_SPIN_LIMIT = 1u << 22;  // bounded wait of a merge work-group (polls)
+
+template <int D>
+struct STile {
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  static constexpr int ROWB = D * 2;                 // bytes per row
+  static constexpr int RPI = 64 / CPR;               // rows filled by one load instruction
+  static constexpr int IPW = ST_KT / RPI / ST_WAVES;  // load instructions per wave per tensor
+  static constexpr int RPW = RPI * IPW;              // rows filled by one wave (8, within one 16-token block)
+  static constexpr int TBYTES = ST_KT * ROWB;        // one tensor of the tile
+  static constexpr int BUF = 2 * TBYTES;             // K and V
+  static constexpr int QBYTES = ST_QT * ROWB;        // the work-group's query rows
+  __device__ static __forceinline__ int swz(int r) {
+    return CPR == 16 ? (((r << 1) & 14) | ((r >> 3) & 1)) : ((r & 6) | ((r >> 3) & 1));
+  }
+};
+
+struct StepAttnPlan {
+  int32_t G, M, qtiles, nsplit, chunk, ntt, W, cap;
+  float cscale;          // scale * log2(e)
+  uint32_t pool_bytes;   // paged: bytes of one K (or V) pool, < 4 GiB
+  int32_t nunits;        // B * Hkv * qtiles
+  int32_t nwg;           // attention work-groups in use (B * Hkv * nsplit * qtiles)
+  int32_t mrows;         // output rows per merge work-group
+  int32_t mper;          // merge work-groups per (sequence, KV head) pair
+  uint16_t* opart;       // [unit][split][ST_QT][D] bf16: the split's output row O / l
+  float* mlpart;         // [unit][split][ST_QT][2]: running max (scaled by log2 e) and l
+  uint32_t* arrive;      // [unit] splits that have written their partials
+};
+
+// Ancestor bitsets of every node of sequence b into LDS (anc[i * 4 + w], four words per node),
+// by the rule of sv_build_tree_mask: walk up at most max_depth nodes; a parent out of range,
+// a revisited node or a path longer than max_depth makes the node invalid, and an invalid node
+// sees only itself.  spar: N ints of LDS.  Every thread of the work-group calls it.
+__device__ __forceinline__ void step_ancestors(const int32_t* __restrict__ parents, int b, int N, int max_depth,
+                                               int32_t* spar, uint64_t* anc) {
+  const int t = threadIdx.x;
+  for (int i = t; i < N; i += blockDim.x) spar[i] = parents[(int64_t)b * N + i];
+  __syncthreads();
+  for (int i = t; i < N; i += blockDim.x) {
+    uint64_t bits[SV_MAX_W] = {0, 0, 0, 0};
+    bit_set(bits, i);
+    int count = 1, cur = i;
+    bool ok = true;
+    for (int step = 0; step <= SV_MAX_DEPTH; ++step) {  // every iteration exits or grows count
+      const int pp = spar[cur];
+      if (pp < -1 || pp >= N) { ok = false; break; }
+      if (pp == -1) break;
+      if (bit_get(bits, pp)) { ok = false; break; }
+      if (count + 1 > max_depth) { ok = false; break; }
+      bit_set(bits, pp);
+      ++count;
+      cur = pp;
+    }
+    if (!ok) {  // an invalid node sees only itself
+      bits[0] = bits[1] = bits[2] = bits[3] = 0;
+      bit_set(bits, i);
+    }
+#pragma unroll
+    for (int w = 0; w < SV_MAX_W; ++w) anc[i * 4 + w] = bits[w];
+  }
+  __syncthreads();
+}
+
+// One attention work-group of the step.  lid: its index among the attention work-groups;
+// kvA, kvB: the two K/V tile buffers (separate LDS arrays, so that the direct loads into one
+// are known not to alias reads of the other), qsb: the query rows, aux: >= 9 KB of LDS for
+// the ancestor bitsets (last split only).  `parents` and max_depth come from the acceptance
+// arguments.  Every thread calls it; it returns after the unit's arrival count (if any).
+template <int D>
+__device__ __forceinline__ void step_attention(const sv_attn_args& a, const StepAttnPlan& p, int lid,
+                                               const int32_t* __restrict__ parents, int max_depth,
+                                               unsigned char* kvA, unsigned char* kvB, unsigned char* qsb,
+                                               unsigned char* aux) {
+  using TL = STile<D>;
+  constexpr int DS = D / 16;  // 16-wide k-steps of S = K Q^T
+  constexpr int DB = D / 32;  // 32-wide d-blocks of O^T
+  constexpr uint32_t ROWB = TL::ROWB;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lq = lane & 31;
+  const int hf = lane >> 5;
+  if (w < ST_WAVES / 2) __builtin_amdgcn_s_setprio(1);
+
+  // lid = ((pair * nsplit) + split) * qtiles + qtile: the query tiles of one key range are
+  // neighbours (same XCD, same time), so the second reads the range from L2
+  const int qtile = lid % p.qtiles;
+  const int split = (lid / p.qtiles) % p.nsplit;
+  const int pair = lid / (p.qtiles * p.nsplit);
+  const int b = pair / a.Hkv;
+  const int g = pair % a.Hkv;
+  const int N = a.N, Hq = a.Hq, G = p.G;
+
+  if (a.status && g == 0 && qtile == 0 && split == 0) write_seq_status(a, b, p.cap);
+  const int L = clamp_len(a.prefix_len[b], p.cap);
+  const int k0 = split * p.chunk;
+  const int k1 = min(k0 + p.chunk, L);
+  const int ntp = k1 > k0 ? (k1 - k0 + ST_KT - 1) / ST_KT : 0;
+  const bool last = split == p.nsplit - 1;
+  const int ntt = last ? p.ntt : 0;
+  const int ntiles = ntp + ntt;
+
+  uint64_t* anc = (uint64_t*)aux;                       // [N][4]
+  int32_t* spar = (int32_t*)(aux + SV_MAX_N * 4 * 8);  // [N]
+  const int mw = qtile * ST_QT + w * 32;
+  const bool active = mw < p.M;  // uniform: the wave has at least one valid query row
+
+  const __bf16* qg = (const __bf16*)a.q;
+  const uint16_t* kc = (const uint16_t*)a.k_cache;
+  const uint16_t* vc = (const uint16_t*)a.v_cache;
+  const uint16_t* kt = (const uint16_t*)a.k_tree;
+  const uint16_t* vt = (const uint16_t*)a.v_tree;
+  const int64_t plane = (int64_t)b * a.Hkv + g;
+  const bool tic = a.tree_in_cache != 0;
+  const bool tic_paged = tic && a.paged;
+  __amdgpu_buffer_rsrc_t rk, rv, rkt, rvt;
+  if (a.paged) {
+    rk = __builtin_amdgcn_make_buffer_rsrc((void*)kc, 0, (int)p.pool_bytes, 0x00020000);
+    rv = __builtin_amdgcn_make_buffer_rsrc((void*)vc, 0, (int)p.pool_bytes, 0x00020000);
+  } else {
+    rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + plane * a.Lcap * D), 0, (int)(a.Lcap * ROWB), 0x00020000);
+    rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + plane * a.Lcap * D), 0, (int)(a.Lcap * ROWB), 0x00020000);
+  }
+  if (tic_paged) {
+    rkt = rk;
+    rvt = rv;
+  } else if (tic) {
+    rkt = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + (plane * a.Lcap + L) * D), 0, (int)(N * ROWB), 0x00020000);
+    rvt = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + (plane * a.Lcap + L) * D), 0, (int)(N * ROWB), 0x00020000);
+  } else {
+    rkt = __builtin_amdgcn_make_buffer_rsrc((void*)(kt + (plane * (N + 1) + 1) * D), 0, (int)(N * ROWB), 0x00020000);
+    rvt = __builtin_amdgcn_make_buffer_rsrc((void*)(vt + (plane * (N + 1) + 1) * D), 0, (int)(N * ROWB), 0x00020000);
+  }
+  // wave w fills rows RPW w .. RPW w + RPW - 1 of K and of V; keys past the valid range are
+  // clamped onto the tile's last valid key (finite data, masked out of the softmax)
+  auto load_tile = [&](int tile, unsigned char* kb) {
+    const bool tree = tile >= ntp;
+    int klast;
+    int t0 = 0;
+    uint32_t soff = 0;
+    if (tree) {
+      t0 = (tile - ntp) * ST_KT;
+      klast = min(ST_KT, N - t0) - 1;
+      soff = tic_paged ? 0u : (uint32_t)t0 * ROWB;
+    } else {
+      const int j0 = k0 + tile * ST_KT;
+      klast = min(ST_KT, k1 - j0) - 1;
+      if (a.paged) {
+        // the wave's 8 rows lie in one 16-token block; past the end the clamped key's block
+        const int blk = (j0 + min(TL::RPW * w, klast)) / 16;
+        int id = __builtin_amdgcn_readfirstlane(a.block_table[(int64_t)b * a.max_blocks + blk]);
+        id = (id < 0 || id >= a.num_blocks) ? 0 : id;
+        soff = (uint32_t)(((int64_t)id * a.Hkv + g) * 16) * ROWB;
+      } else {
+        soff = (uint32_t)j0 * ROWB;
+      }
+    }
+    const bool paged_tile = !tree && a.paged;
+    const __amdgpu_buffer_rsrc_t rK = tree ? rkt : rk;
+    const __amdgpu_buffer_rsrc_t rV = tree ? rvt : rv;
+#pragma unroll
+    for (int it = 0; it < TL::IPW; ++it) {
+      const int n = w * TL::IPW + it;              // 1-KB piece of the tile (uniform)
+      const int r = n * TL::RPI + lane / TL::CPR;  // row this lane fills
+      const int c = (lane % TL::CPR) ^ TL::swz(r);
+      const int key = min(r, klast);
+      uint32_t off;
+      if (tree && tic_paged) {
+        const int pos = L + t0 + key;
+        int id = a.block_table[(int64_t)b * a.max_blocks + pos / 16];
+        id = (id < 0 || id >= a.num_blocks) ? 0 : id;
+        off = (uint32_t)((((int64_t)id * a.Hkv + g) * 16 + (pos & 15)) * ROWB + c * 16);
+      } else {
+        off = (uint32_t)((paged_tile ? (key & 15) : key) * ROWB + c * 16);
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_void*)(kb + n * 1024), 16, off, soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_void*)(kb + TL::TBYTES + n * 1024), 16, off, soff, 0, 0);
+    }
+  };
+
+  if (0 < ntiles) load_tile(0, kvA);
+  {  // the query rows (rows past M repeat row M - 1; their outputs are never written)
+    constexpr int NQ = ST_QT * TL::CPR / 64 / ST_WAVES;
+#pragma unroll
+    for (int it = 0; it < NQ; ++it) {
+      const int n = w * NQ + it;
+      const int r = n * TL::RPI + lane / TL::CPR;
+      const int c = (lane % TL::CPR) ^ TL::swz(r);
+      const int m = min(qtile * ST_QT + r, p.M - 1);
+      const int node = m / G, h = g * G + m % G;
+      __builtin_amdgcn_global_load_lds((const void*)(qg + (((int64_t)b * N + node) * Hq + h) * D + c * 8),
+                                       (lds_void*)(qsb + n * 1024), 16, 0, 0);
+    }
+  }
+  // the last split reads the tree keys: ancestor bitsets of every node, from the parents
+  if (ntt > 0) step_ancestors(parents, b, N, max_depth, spar, anc);
+  const int qm = mw + lq;
+  const int qnode = qm < p.M ? qm / G : -1;
+
+  sv_f32x16 oacc[DB];
+  float mrun = -INFINITY, lrun = 0.f;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+
+  const int k_off = lq * ROWB;
+  const int k_swz = TL::swz(lq);
+  const int tr_row = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tr_half = (lane & 1) * 8;
+  const int tr_swz_lo = TL::swz(tr_row), tr_swz_hi = TL::swz(tr_row + 8);
+
+  auto compute = [&](int tile, const unsigned char* Kb) {
+    const unsigned char* Vb = Kb + TL::TBYTES;
+    const bool tree = tile >= ntp;
+    const int j0 = k0 + tile * ST_KT;
+    const int t0 = (tile - ntp) * ST_KT;
+    // ---- S^T = K Q^T for one 32-key block; the fragments of step ds + 1 are read under the
+    // MFMAs of step ds
+    sv_f32x16 sacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+    sv_bf16x8 qf[2], kf[2];
+    auto frag = [&](int ds, int buf) {
+      const int kslot = ((2 * ds + hf) ^ k_swz) * 16;
+      qf[buf] = *(const sv_bf16x8*)(qsb + (w * 32) * ROWB + k_off + kslot);
+      kf[buf] = *(const sv_bf16x8*)(Kb + k_off + kslot);
+    };
+    frag(0, 0);
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      if (ds + 1 < DS) frag(ds + 1, (ds + 1) & 1);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds & 1], qf[ds & 1], sacc, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- masks + online softmax (lane owns query column lq; keys 8 (r/4) + 4 hf + r%4)
+    const bool full = !tree && (j0 + ST_KT <= k1);
+    if (!full && !tree) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (j0 + kk >= k1) sacc[r] = -INFINITY;
+      }
+    } else if (tree) {
+      // bits t0 .. t0 + 31 of the query node's bitset: one half of one 64-bit word
+      uint64_t aw = qnode >= 0 ? anc[qnode * 4 + (t0 >> 6)] >> (t0 & 63) : 0ull;
+      const int lim = N - t0;  // keys of the tile that are tree nodes (>= 1)
+      if (lim < 32) aw &= (1ull << lim) - 1ull;
+      const uint32_t a_lo = (uint32_t)(aw >> (4 * hf));
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (((a_lo >> (8 * (r >> 2) + (r & 3))) & 1u) == 0) sacc[r] = -INFINITY;
+    }
+    float mt = sacc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sacc[r]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mnew = fmaxf(mrun, mt);
+    const float ms = mnew == -INFINITY ? 0.f : mnew * p.cscale;
+    const float alpha = __builtin_amdgcn_exp2f(mrun * p.cscale - ms);
+    const bool moved = mnew != mrun;
+    sv_bf16x8 pf[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pf[r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[r], p.cscale, -ms));
+    float psum0 = 0.f, psum1 = 0.f;
+    const sv_bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const sv_bf16x8 v = pf[t2];
+      psum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one2, psum0, false);
+      psum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one2, psum1, false);
+      psum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one2, psum0, false);
+      psum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one2, psum1, false);
+    }
+    float psum = psum0 + psum1;
+    psum += __shfl_xor(psum, 32);
+    lrun = lrun * alpha + psum;
+    mrun = mnew;
+    if (__ballot(moved)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- O^T += V^T P^T; the 16-key step t2 holds keys 16 t2 + 4 hf + {0..3, 8..11}, in
+    // half-steps of two d-blocks whose transposing reads go out one half-step ahead
+    constexpr int NH = DB;  // 2 steps x DB / 2 halves
+    uint2 vlo[2][2], vhi[2][2];
+    auto tr_issue = [&](int h, int buf) {
+      const int t2 = h / (DB / 2), d0 = (h % (DB / 2)) * 2;
+      const uint32_t rlo = lds_addr(Vb) + (16 * t2 + tr_row) * ROWB + tr_half;
+      const uint32_t rhi = rlo + 8 * ROWB;
+      uint32_t alo[2], ahi[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = 4 * (d0 + j) + tr_chunk;
+        alo[j] = rlo + ((c ^ tr_swz_lo) << 4);
+        ahi[j] = rhi + ((c ^ tr_swz_hi) << 4);
+      }
+      tr_read_issue(vlo[buf], vhi[buf], alo, ahi);
+    };
+    tr_issue(0, 0);
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const int buf = h & 1;
+      if (h + 1 < NH) {
+        tr_issue(h + 1, buf ^ 1);
+        tr_wait<4>(vlo[buf], vhi[buf]);
+      } else {
+        tr_wait<0>(vlo[buf], vhi[buf]);
+      }
+      const int t2 = h / (DB / 2), d0 = (h % (DB / 2)) * 2;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const sv_bf16x8 vf = __builtin_bit_cast(sv_bf16x8, make_uint4(vlo[buf][j].x, vlo[buf][j].y, vhi[buf][j].x, vhi[buf][j].y));
+        oacc[d0 + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t2], oacc[d0 + j], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  for (int tile = 0; tile < ntiles; tile += 2) {
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of `tile` (and the Q rows) have landed
+    __syncthreads();                // ... and everyone's; every wave is done with tile - 1
+    if (tile + 1 < ntiles) load_tile(tile + 1, kvB);
+    if (active) compute(tile, kvA);
+    if (tile + 1 >= ntiles) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tile + 2 < ntiles) load_tile(tile + 2, kvA);
+    if (active) compute(tile + 1, kvB);
+  }
+
+  // ---- write: bf16 output (one split) or the split's partial: O / l in bf16, (m, l) in fp32.
+  // The wave stages its rows in its own query rows of LDS, then stores whole rows.
+  const int unit = pair * p.qtiles + qtile;
+  const int64_t pidx = (int64_t)unit * p.nsplit + split;
+  if (active) {
+    unsigned char* ob = qsb + (w * 32) * ROWB;
+    const int ql = w * 32 + lq;
+    const int m = qtile * ST_QT + ql;
+    const float inv = lrun > 0.f ? 1.f / lrun : 0.f;
+    if (p.nsplit > 1 && hf == 0 && m < p.M)
+      *(float2*)(p.mlpart + (pidx * ST_QT + ql) * 2) = make_float2(mrun * p.cscale, lrun);
+    const int sw = TL::swz(lq);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int c = 4 * db + rq;
+        const uint32_t w0 = f32_to_bf16_bits(oacc[db][4 * rq + 0] * inv) |
+                            ((uint32_t)f32_to_bf16_bits(oacc[db][4 * rq + 1] * inv) << 16);
+        const uint32_t w1 = f32_to_bf16_bits(oacc[db][4 * rq + 2] * inv) |
+                            ((uint32_t)f32_to_bf16_bits(oacc[db][4 * rq + 3] * inv) << 16);
+        *(uint2*)(ob + lq * ROWB + ((c ^ sw) << 4) + 8 * hf) = make_uint2(w0, w1);
+      }
+    wave_lds_sync();
+    constexpr int CPR = TL::CPR, RPO = 64 / CPR;
+#pragma unroll
+    for (int i = 0; i < 32 / RPO; ++i) {
+      const int r = i * RPO + lane / CPR;
+      const int ch = lane % CPR;
+      const uint4 v = *(const uint4*)(ob + r * ROWB + ((ch ^ TL::swz(r)) << 4));
+      const int qr = w * 32 + r;
+      const int mm = qtile * ST_QT + qr;
+      if (mm < p.M) {
+        uint16_t* orow = p.nsplit == 1 ? (uint16_t*)a.out + (((int64_t)b * N + mm / G) * Hq + g * G + mm % G) * D
+                                       : p.opart + (pidx * ST_QT + qr) * D;
+        *(uint4*)(orow + ch * 8) = v;
+      }
+    }
+  }
+  if (p.nsplit > 1) {
+    __syncthreads();  // every wave's partial stores precede the release below
+    if (t == 0) __hip_atomic_fetch_add(&p.arrive[unit], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// One merge work-group of the step: output rows m0 .. m0 + mrows - 1 of one (sequence, KV head)
+// pair.  It waits (bounded) until every split of the units those rows belong to has counted in,
+// then combines the splits' normalised rows with weights exp2(m_s - max) l_s, as
+// k_attn_combine does.  TPR threads per row, one 16-byte chunk each.  s_f: LDS for
+// (256 / TPR) x 64 split weights.  On an expired wait the sequence's attention status is 7.
+template <int D>
+__device__ __forceinline__ void step_merge(const sv_attn_args& a, const StepAttnPlan& p, int mid, float* s_f) {
+  constexpr int TPR = D / 8;                // threads per output row
+  constexpr int RPP = ST_THREADS / TPR;     // rows per pass
+  constexpr int SB = 16;                    // split rows in flight per thread
+  const int t = threadIdx.x;
+  const int pair = mid / p.mper, part = mid % p.mper;
+  const int b = pair / a.Hkv, g = pair % a.Hkv;
+  const int m0 = part * p.mrows;
+  const int m1 = min(m0 + p.mrows, p.M);
+  if (m0 >= m1) return;  // uniform
+  __shared__ int s_late;
+  if (t == 0) {
+    int late = 0;
+    for (int q = m0 / ST_QT; q <= (m1 - 1) / ST_QT; ++q) {
+      uint32_t* cnt = &p.arrive[pair * p.qtiles + q];
+      uint32_t spins = 0;
+      while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)p.nsplit) {
+        if (++spins > ST_SPIN_LIMIT) { late = 1; break; }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the splits' partials are visible after their release
+    s_late = late;
+  }
+  __syncthreads();
+  if (s_late && a.status) atomicMax(&a.status[b], SV_SEQ_TIMEOUT);
+  const int ns = p.nsplit;
+  const int G = p.G;
+  const int lr = t / TPR, c = t % TPR;
+  for (int mb = m0; mb < m1; mb += RPP) {
+    const int m = mb + lr;
+    const bool on = m < m1;
+    const int mm = on ? m : m1 - 1;
+    const int unit = pair * p.qtiles + mm / ST_QT, ql = mm % ST_QT;
+    // weights: thread c of the row takes splits c, c + TPR, ...; max and sum over the row's lanes
+    float mx = -INFINITY;
+    for (int s = c; s < ns; s += TPR) mx = fmaxf(mx, p.mlpart[(((int64_t)unit * ns + s) * ST_QT + ql) * 2]);
+#pragma unroll
+    for (int o = TPR / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    float lsum = 0.f;
+    for (int s = c; s < ns; s += TPR) {
+      const float2 ml = *(const float2*)(p.mlpart + (((int64_t)unit * ns + s) * ST_QT + ql) * 2);
+      const float f = ml.x == -INFINITY ? 0.f : exp2f(ml.x - mx) * ml.y;
+      s_f[lr * 64 + s] = f;
+      lsum += f;
+    }
+#pragma unroll
+    for (int o = TPR / 2; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
+    wave_lds_sync();  // the row's weights come from lanes of the same wave
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += SB) {
+      uint4 part[SB];
+#pragma unroll
+      for (int k = 0; k < SB; ++k) {
+        const int s = min(s0 + k, ns - 1);
+        part[k] = *(const uint4*)(p.opart + (((int64_t)unit * ns + s) * ST_QT + ql) * D + c * 8);
+      }
+#pragma unroll
+      for (int k = 0; k < SB; ++k) {
+        if (s0 + k >= ns) break;
+        const float f = s_f[lr * 64 + s0 + k];
+        const uint32_t ww[4] = {part[k].x, part[k].y, part[k].z, part[k].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          acc[2 * h] = fmaf(f, __uint_as_float(ww[h] << 16), acc[2 * h]);
+          acc[2 * h + 1] = fmaf(f, __uint_as_float(ww[h] & 0xffff0000u), acc[2 * h + 1]);
+        }
+      }
+    }
+    const float inv = (mx != -INFINITY && lsum > 0.f) ? 1.f / lsum : 0.f;
+    if (on) {
+      uint32_t o4[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        o4[h] = f32_to_bf16_bits(acc[2 * h] * inv) | ((uint32_t)f32_to_bf16_bits(acc[2 * h + 1] * inv) << 16);
+      const int node = m / G, hh = g * G + m % G;
+      *(uint4*)((uint16_t*)a.out + (((int64_t)b * a.N + node) * a.Hq + hh) * D + c * 8) =
+          make_uint4(o4[0], o4[1], o4[2], o4[3]);
+    }
+    wave_lds_sync();  // the weights are read before the next pass overwrites them
+  }
+}
+
+}  // namespace

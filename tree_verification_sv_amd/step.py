@@ -23,7 +23,7 @@ import ctypes
 from dataclasses import dataclass
 from typing import Optional
 
-from . import (SV_COMMIT_PATH, SV_STOCHASTIC, SV_TOPK_DRAFT, _check, _stream, accept_args, accept_outputs, attn_args,
+from . import (SV_COMMIT_PATH, SV_GREEDY, SV_STOCHASTIC, SV_TOPK_DRAFT, _check, _stream, accept_args, accept_outputs, attn_args,
                commit_args, lib, sv_accept_workspace, sv_tree_attention_workspace)
 
 
@@ -133,11 +133,11 @@ class VerifyStep:
         self._fused = on
 
     def mask_free_accept(self, on: bool = True):
-        """Let the acceptance derive node depths from the parent array itself (modes "stochastic"
-        and "topk" only: sv_accept gets NULL anc_bits and depth), so that it does not wait for the
+        """Let the acceptance derive node depths from the parent array itself (every mode but
+        "threshold": sv_accept gets NULL anc_bits and depth), so that it does not wait for the
         mask; run(overlap=True) then forks before the mask and the acceptance branch starts at once."""
-        if on and self._acc.mode not in (SV_STOCHASTIC, SV_TOPK_DRAFT):
-            raise ValueError("only the stochastic and top-K modes can accept without the mask outputs")
+        if on and self._acc.mode not in (SV_GREEDY, SV_STOCHASTIC, SV_TOPK_DRAFT):
+            raise ValueError("threshold acceptance needs the mask outputs")
         self._acc.anc_bits = None if on else self.mask["anc_bits"].data_ptr()
         self._acc.depth = None if on else self.mask["depth"].data_ptr()
         self._mask_free = on
