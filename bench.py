@@ -1,23 +1,27 @@
 """Benchmark of one tree-verification step on one MI355X.
 
-A step is the whole hot path on one batch: sv_build_tree_mask, then
-sv_tree_attention on the launch stream (issued first) beside sv_accept on a side
-stream, whose walker also commits the accepted path into the cache (the
-sv_kv_commit work inside the acceptance launch; --separate-commit: its own
-launch after sv_accept), joined at the end of the step (--no-overlap: all on one
-stream).  Both branches read only the mask outputs and the inputs; the commit
-writes cache slots the attention does not read.  The
-default workload is the EAGLE-style static tree at the Llama-3-8B attention
-shape (batch 1, 32 query / 8 KV heads, head_dim 128, 4096-token bf16 prefix,
-60-node tree of depth 6, vocab 128256, stochastic acceptance at T = 1).
+A step is the whole hot path on one batch: the tree mask, the ancestor-masked
+tree attention, the acceptance with its bonus token and the commit of the
+accepted path.  By default it is one sv_verify_step launch (when the call
+supports the workload); --separate-calls runs sv_build_tree_mask, then
+sv_tree_attention beside sv_accept (whose walker commits the accepted path;
+--separate-commit: its own sv_kv_commit launch) on a side stream, joined at the
+end of the step (--no-overlap: all on one stream).  The default workload is
+the EAGLE-style static tree at the Llama-3-8B attention shape (batch 1, 32
+query / 8 KV heads, head_dim 128, 4096-token bf16 prefix, 60-node tree of
+depth 6, vocab 128256, stochastic acceptance at T = 1).
 
 Inputs are resident in HBM before timing starts.  R independent input
 instances are cycled so that the working set (R x step bytes) exceeds twice
-the 256 MB Infinity Cache and every step reads HBM, not a warm cache.
+the 256 MB Infinity Cache and every step reads HBM, not a warm cache.  The
+timed region is one replay of a HIP graph of exactly K steps (instances
+cycled), repeated --reps times; ms_per_step is the median.  Stage times come
+from graphs of K launches of one stage each.
 
 Prints one JSON line: value = verified tree tokens/s (B*N / step time), with
 the roofline of the dominant kernel measured live with HIP events on the
-launch stream, and the CPU oracle timed on a bounded sample on the host.
+launch stream, a measured streaming-read ceiling, and the CPU oracle timed on
+a bounded sample on the host (with the count of flagged stochastic draws).
 """
 import argparse
 import hashlib
@@ -92,19 +96,54 @@ def load_traffic(kernel, kernel_src_hash, workload):
     return d.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, budget_s=10.0, variant=None, over=None):
-    """The CPU oracle as it stands, one host thread, on one step of the same workload.
+def host_info():
+    """Host threads available to this process and the CPU model, for the baseline lines."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return n, model
 
-    Mask, acceptance and commit run on the whole batch.  The attention runs on a
-    seeded sample of query rows (b, node, head) sized to about ``budget_s`` seconds
-    and is scaled linearly to all B*N*Hq rows (every row costs the same prefix
-    pass up to its own few tree keys).  Input generation is not timed.
+
+def seq_slice(w, b):
+    """Sequence b of a workload as a batch of one (the paged K/V pool is shared, not copied)."""
+    import dataclasses
+    sl = lambda x: None if x is None else x[b:b + 1]  # noqa: E731
+    kw = dict(B=1, parents=sl(w.parents), tokens=sl(w.tokens), prefix_len=sl(w.prefix_len), q=sl(w.q),
+              k_tree=sl(w.k_tree), v_tree=sl(w.v_tree), block_table=sl(w.block_table),
+              target_logits=sl(w.target_logits), draft_logits=sl(w.draft_logits), u_accept=sl(w.u_accept),
+              u_sample=sl(w.u_sample))
+    if not w.paged:
+        kw.update(k_cache=sl(w.k_cache), v_cache=sl(w.v_cache))
+    return dataclasses.replace(w, **kw)
+
+
+def cpu_baseline(cfg, budget_s=10.0, variant=None, over=None):
+    """The CPU oracle as it stands on one step of the same workload, on one host thread and
+    fanned out over host threads.
+
+    Mask, acceptance and commit run on the whole batch; the attention runs on a seeded sample of
+    query rows (b, node, head) sized to about ``budget_s`` seconds and is scaled linearly to all
+    B*N*Hq rows (every row costs the same prefix pass up to its own few tree keys).  The
+    all-threads line runs every stage in parallel: mask, acceptance and commit over sequences,
+    the attention sample over row chunks.  Input generation is not timed.
     """
     import oracle
     import workloads as W
+    from concurrent.futures import ThreadPoolExecutor
     w = W.config(cfg, seed=cfg * 1000, **(over or {}))
     if variant is not None:
         w = variant(w)
+    nproc, cpu_model = host_info()
     total_rows = w.B * w.N * w.Hq
     t0 = time.perf_counter()
     oracle.build_tree_mask(w.parents, w.max_depth)
@@ -129,25 +168,71 @@ def cpu_baseline(cfg, budget_s=10.0, variant=None, over=None):
     t_com = time.perf_counter() - t0
     dt = t_mask + t_attn + t_acc + t_com
     scaled = "all rows" if sel.size == total_rows else f"{sel.size} of {total_rows} rows, scaled linearly"
-    one = dict(value=round(w.B * w.N / dt, 3), unit="tokens/s", cores=1, kind="oracle",
+    one = dict(value=round(w.B * w.N / dt, 3), unit="tokens/s", cores=1, kind="oracle", nproc=nproc,
+               cpu_model=cpu_model,
                sample=f"one verification step of the {w.name} workload (B={w.B}, N={w.N}, "
                       f"L={int(w.prefix_len.max())}, V={w.V}, {w.mode} acceptance) on one host thread: mask, "
-                      f"acceptance and commit on the whole batch ({t_mask + t_acc + t_com:.1f} s), fp64 attention "
+                      f"acceptance and commit on the whole batch ({t_mask + t_acc + t_com:.2f} s), fp64 attention "
                       f"on {scaled} ({t_attn:.1f} s for the step)")
-    # the same attention sample fanned out over host threads (the oracle's C code runs without
-    # the interpreter lock); mask, acceptance and commit keep their one-thread times
-    from concurrent.futures import ThreadPoolExecutor
-    nthreads = max(1, min(16, os.cpu_count() or 1))
+    # every stage over host threads (the oracle's C code runs outside the interpreter lock)
+    nthreads = max(1, min(16, nproc))
+    seqs = [seq_slice(w, b) for b in range(w.B)]
     chunks = [c for c in np.array_split(sel, nthreads) if c.size]
-    t0 = time.perf_counter()
-    with ThreadPoolExecutor(max_workers=len(chunks)) as ex:
+    kc, vc = w.k_cache.copy(), w.v_cache.copy()
+    with ThreadPoolExecutor(max_workers=nthreads) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(lambda s_: oracle.build_tree_mask(s_.parents, s_.max_depth), seqs))
+        t_mask_mt = time.perf_counter() - t0
+        t0 = time.perf_counter()
         list(ex.map(lambda c: oracle.tree_attention(w, sel=np.ascontiguousarray(c)), chunks))
-    t_attn_mt = (time.perf_counter() - t0) * total_rows / sel.size
-    dt_mt = t_mask + t_attn_mt + t_acc + t_com
-    many = dict(value=round(w.B * w.N / dt_mt, 3), unit="tokens/s", cores=len(chunks), kind="oracle",
-                sample=f"as cpu_baseline, with the attention rows split over {len(chunks)} host threads "
-                       f"({t_attn_mt:.1f} s for the step's attention)")
+        t_attn_mt = (time.perf_counter() - t0) * total_rows / sel.size
+        t0 = time.perf_counter()
+        accs = list(ex.map(oracle.accept, seqs))
+        t_acc_mt = time.perf_counter() - t0
+        kcs = [kc if w.paged else kc[b:b + 1] for b in range(w.B)]
+        vcs = [vc if w.paged else vc[b:b + 1] for b in range(w.B)]
+        t0 = time.perf_counter()
+        list(ex.map(lambda i: oracle.kv_commit(seqs[i], accs[i]["accept_len"], accs[i]["accept_rows"], kcs[i], vcs[i]),
+                    range(w.B)))
+        t_com_mt = time.perf_counter() - t0
+    dt_mt = t_mask_mt + t_attn_mt + t_acc_mt + t_com_mt
+    many = dict(value=round(w.B * w.N / dt_mt, 3), unit="tokens/s", cores=nthreads, kind="oracle", nproc=nproc,
+                cpu_model=cpu_model,
+                sample=f"as cpu_baseline with every stage over {nthreads} host threads: mask, acceptance and "
+                       f"commit over the {w.B} sequences ({t_mask_mt + t_acc_mt + t_com_mt:.2f} s), the attention "
+                       f"sample over row chunks ({t_attn_mt:.1f} s for the step)")
     return one, many
+
+
+def flagged_draws(ws):
+    """Stochastic draws of the timed instances that the oracle flags (within 1e-6 of a threshold):
+    the sequences excluded from exact comparison."""
+    import oracle
+    if ws[0].mode not in ("stochastic", "topk", "threshold"):
+        return 0
+    return int(sum(int(oracle.accept(w)["flagged"].sum()) for w in ws))
+
+
+def stream_read_ceiling(dev, gib=2, reps=5):
+    """A measured streaming-read ceiling: torch's sum over a fresh 2 GiB fp32 tensor (far larger
+    than the 256 MB last-level cache), median of `reps` timed calls."""
+    import torch
+    x = torch.ones((gib << 30) // 4, dtype=torch.float32, device=dev)
+    out = torch.empty((), dtype=torch.float32, device=dev)
+    for _ in range(2):
+        torch.sum(x, dim=0, out=out)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.sum(x, dim=0, out=out)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    del x
+    ms = float(np.median(ts))
+    return round((gib << 30) / (ms * 1e-3) / 1e9, 1)
 
 
 def commit_layers(w, dev, acc, layers, K):
@@ -284,6 +369,10 @@ def main():
     ap.add_argument("--mask-free-accept", action="store_true",
                     help="stochastic / top-K: the acceptance derives node depths from the parents itself and its "
                          "branch forks before the mask")
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="run the step as separate library calls (mask, attention, acceptance, commit) instead "
+                         "of one sv_verify_step launch")
+    ap.add_argument("--reps", type=int, default=5, help="timed repetitions of the K-step graph (median reported)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--acceptance", choices=["greedy", "stochastic", "topk", "threshold"], default=None,
                     help="acceptance rule (default: the workload's own)")
@@ -335,11 +424,20 @@ def main():
     if mask_free:
         for s_ in steps:
             s_.mask_free_accept(True)
+    one = False
+    if not args.separate_calls and not mask_free:
+        one = all([s_.one_launch(True) for s_ in steps])
+        if not one:
+            print("[bench] sv_verify_step does not support this workload; timing the separate calls",
+                  file=sys.stderr, flush=True)
+            for s_ in steps:
+                s_.one_launch(False)
     stream = torch.cuda.current_stream()
 
     ov = not args.no_overlap
+    run = lambda i: steps[i % R].run(overlap=ov, attention_side=args.attention_side)  # noqa: E731
     for i in range(args.warmup):
-        steps[i % R].run(overlap=ov, attention_side=args.attention_side)
+        run(i)
     torch.cuda.synchronize()
     if args.copy_mib:  # untimed reference copy: its FETCH/WRITE counters calibrate the byte counts
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
@@ -349,74 +447,97 @@ def main():
         del src, dst
     accs = [{k: v.cpu().numpy() for k, v in s.acc.items()} for s in steps]
     byts = [algorithmic_bytes(w, a) for w, a in zip(ws, accs)]
+    K = args.steps
 
+    def capture(fn, n):
+        """One HIP graph of n calls fn(i), captured on a side stream after one eager round."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(min(n, R)):
+                fn(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        return g
+
+    def timed(g_or_fn, reps):
+        """Per-repetition milliseconds of one graph replay (or one eager call of fn) on the launch stream."""
+        ts = []
+        for _ in range(reps):
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a_.record(stream)
+            if callable(g_or_fn):
+                g_or_fn()
+            else:
+                g_or_fn.replay()
+            b_.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a_.elapsed_time(b_))
+        return ts
+
+    # ---- timed region: exactly K steps per repetition (one graph of K steps cycling the
+    # instances, or K eager steps), median of `reps` repetitions
     use_graph = not args.no_graph
     graph = None
     if use_graph:
         try:
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                for s in steps:
-                    s.run(overlap=ov, attention_side=args.attention_side)
-            torch.cuda.current_stream().wait_stream(side)
-            torch.cuda.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
-                for s in steps:
-                    s.run(overlap=ov, attention_side=args.attention_side)
-            torch.cuda.synchronize()
-            for _ in range(2):
-                graph.replay()
-            torch.cuda.synchronize()
+            graph = capture(run, K)
         except Exception as ex:  # capture not available: fall back to eager launches
             print(f"[bench] graph capture failed ({ex}); timing eager launches", file=sys.stderr)
-            graph = None
-            use_graph = False
-
-    # ---- timed region: exactly K steps
-    K = args.steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+            graph, use_graph = None, False
     t0 = time.perf_counter()
-    e0.record(stream)
-    if graph is not None:
-        reps = K // R
-        for _ in range(reps):
-            graph.replay()
-        for i in range(K - reps * R):
-            steps[i].run(overlap=ov, attention_side=args.attention_side)
-    else:
-        for i in range(K):
-            steps[i % R].run(overlap=ov, attention_side=args.attention_side)
-    e1.record(stream)
-    torch.cuda.synchronize()
+    rep_ms = timed(graph if graph is not None else (lambda: [run(i) for i in range(K)]), args.reps)
     wall = time.perf_counter() - t0
-    ms_step = e0.elapsed_time(e1) / K
+    ms_step = float(np.median(rep_ms)) / K
+    del graph
 
-    # ---- per-stage durations, each stage launched alone K times on the same stream
+    # ---- per-stage durations: K launches of one stage in a graph of their own (median of reps)
     stage_ms = {}
-    for name in ("build_mask", "attention", "accept", "kv_commit"):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record(stream)
-        for i in range(K):
-            getattr(steps[i % R], name)()
-        b.record(stream)
-        torch.cuda.synchronize()
-        stage_ms[name] = a.elapsed_time(b) / K
+    if one:
+        stage_names = ("verify_step",)
+        stage_fn = {"verify_step": lambda i: steps[i % R].run()}
+    else:
+        stage_names = ("build_mask", "attention", "accept") + (() if steps[0]._fused else ("kv_commit",))
+        stage_fn = {nm: (lambda nm_: lambda i: getattr(steps[i % R], nm_)())(nm) for nm in stage_names}
+    for name in stage_names:
+        try:
+            g = capture(stage_fn[name], K) if use_graph else None
+        except Exception:
+            g = None
+        ts = timed(g if g is not None else (lambda: [stage_fn[name](i) for i in range(K)]), args.reps)
+        stage_ms[name] = float(np.median(ts)) / K
+        del g
 
     layered = commit_layers(ws[0], devs[0], accs[0], args.commit_layers, K) if args.commit_layers else None
     extras = time_extras(ws[0], devs[0], accs[0], K) if args.extras else None
+    ceiling = stream_read_ceiling(dev)
 
     mean_bytes = {k: float(np.mean([bb[k] for bb in byts])) for k in byts[0]}
     B, N = w0.B, w0.N
     value = B * N / (ms_step * 1e-3)
     hbm_gbs = mean_bytes["total"] / (ms_step * 1e-3) / 1e9
-    # dominant stage by measured time; the attention stage for this workload
-    dom = max(("attention", "accept"), key=lambda k: stage_ms[k])
-    dom_key = {"attention": "attention", "accept": "accept"}[dom]
-    achieved = mean_bytes[dom_key] / (stage_ms[dom] * 1e-3) / 1e9
+    # the dominant kernel: the one-launch step itself, or the slower of attention and acceptance
+    if one:
+        dom, dom_bytes, dom_ms = "verify_step", mean_bytes["total"], stage_ms["verify_step"]
+        src = ["tree_verification_sv_amd/csrc/sv_step.hip", "tree_verification_sv_amd/csrc/sv_accept_dev.h",
+               "tree_verification_sv_amd/csrc/sv_attn_dev.h", "tree_verification_sv_amd/csrc/sv_mask_dev.h",
+               "tree_verification_sv_amd/csrc/sv_commit_dev.h"]
+    else:
+        dom = max(("attention", "accept"), key=lambda k: stage_ms[k])
+        dom_bytes, dom_ms = mean_bytes[dom], stage_ms[dom]
+        src = {"attention": ["tree_verification_sv_amd/csrc/sv_attention.hip",
+                             "tree_verification_sv_amd/csrc/sv_attn_dev.h"],
+               "accept": ["tree_verification_sv_amd/csrc/sv_accept.hip",
+                          "tree_verification_sv_amd/csrc/sv_accept_dev.h"]}[dom]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4)}
     if dom == "attention":
@@ -425,11 +546,9 @@ def main():
         fpeak = MFMA_BF16_TFLOPS if w0.dtype == "bf16" else VALU_FP32_TFLOPS
         flops = mean_bytes["attention_flops"]
         if flops / (fpeak * 1e12) > mean_bytes["attention"] / (HBM_PEAK_GBS * 1e9):
-            tf = flops / (stage_ms[dom] * 1e-3) / 1e12
+            tf = flops / (dom_ms * 1e-3) / 1e12
             roof = {"bound": "mfma" if w0.dtype == "bf16" else "alu", "kernel": dom, "achieved": round(tf, 1),
                     "peak": fpeak, "unit": "TFLOP/s", "frac": round(tf / fpeak, 4)}
-    src = {"attention": ["tree_verification_sv_amd/csrc/sv_attention.hip"],
-           "accept": ["tree_verification_sv_amd/csrc/sv_accept.hip"]}[dom]
     traffic = load_traffic(dom, source_hash(src), w0.name)
     result = {
         "metric": "verified tree tokens/sec + HBM GB/s (% peak), 8B-shape tree verify, 1 MI355X",
@@ -448,15 +567,21 @@ def main():
                    "q_heads": w0.Hq, "kv_heads": w0.Hkv, "head_dim": w0.D, "vocab": w0.V, "max_depth": w0.max_depth,
                    "acceptance": w0.mode, "temperature": w0.temperature, "instances_cycled": R,
                    **({"threshold": w0.threshold} if w0.mode == "threshold" else {}),
-                   "launch": "hip_graph" if use_graph else "eager",
-                   "streams": ("attention | accept after mask, commit after both" if w0.tree_in_cache else
+                   "launch": ("hip_graph" if use_graph else "eager") + (" of one sv_verify_step launch per step"
+                                                                        if one else " of the separate calls"),
+                   "streams": "one" if (one or not ov) else
+                              ("attention | accept after mask, commit after both" if w0.tree_in_cache else
                                "mask+attention | accept+commit" if mask_free else
-                               "attention | accept+commit after mask") if ov else "one",
+                               "attention | accept+commit after mask"),
                    "tree_kv": "in cache at prefix_len + t" if w0.tree_in_cache else "separate rows",
-                   "commit": "inside the acceptance kernel" if fused else "sv_kv_commit"},
+                   "commit": "inside the acceptance" if steps[0]._fused else "sv_kv_commit"},
+        "timing": {"reps": len(rep_ms), "ms_per_step_reps": [round(x / K, 5) for x in rep_ms],
+                   "statistic": "median of the repetitions, each one replay of a graph of exactly K steps"},
         "accept_steps_per_s": round(B / (ms_step * 1e-3), 1),
         "hbm_gbs": round(hbm_gbs, 1),
         "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
+        "stream_read_gbs": ceiling,
+        "frac_of_stream_read": round(hbm_gbs / ceiling, 4) if ceiling else None,
         "bytes_per_step": {k: int(v) for k, v in mean_bytes.items() if k != "attention_flops"},
         "attention_flops_per_step": int(mean_bytes["attention_flops"]),
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
@@ -471,6 +596,7 @@ def main():
         result["extras"] = extras
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on one step", file=sys.stderr, flush=True)
+        result["flagged_draws"] = flagged_draws(ws)
         result["cpu_baseline"], result["cpu_baseline_all_cores"] = cpu_baseline(args.config, variant=variant,
                                                                                   over=over)
     print(json.dumps(result), flush=True)

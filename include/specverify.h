@@ -366,6 +366,48 @@ typedef struct sv_commit_args {
 sv_status sv_kv_commit(const sv_commit_args* args, void* stream);
 
 /*
+ * sv_verify_step -- the whole verification step in one launch: the tree
+ * tensorisation, sv_tree_attention, sv_accept and (when accept->commit is set)
+ * the commit of the accepted path, with the same inputs, outputs and results as
+ * those calls in sequence ([EP] sec. 2: the tree mask fused into the target's
+ * execution; [EP] sec. 4: mask construction and tensorisation overhead, with
+ * verification and cache commit dominating; [PX] "Inferencia con
+ * Decodificacion Especulativa": the accepted count stays on the device).  A
+ * step of separate calls is a chain of dependent launches whose gaps dominate
+ * at small batches; one launch removes them.
+ *   attn:   the attention arguments; attn->anc_bits is not read (each node's
+ *           ancestor set is derived from accept->parents inside the launch, by
+ *           the rule of sv_build_tree_mask); attn->workspace is not used.
+ *   accept: the acceptance arguments (modes 0, 1 and 2); accept->anc_bits and
+ *           accept->depth are not read; accept->workspace is not used;
+ *           accept->commit as for sv_accept.  flags must be 0 (the reference
+ *           mode runs the separate calls).
+ *   anc_bits, depth, mask_status (and path_rows, nullable): when set, the
+ *           mask outputs of sv_build_tree_mask are written too (all three, or
+ *           none of them; NULL skips that work).
+ *   workspace: at least sv_verify_step_workspace(args) bytes, 256-byte aligned,
+ *           zero-filled before its first use; every call leaves its counters
+ *           zeroed again (the attention's split partials in it hold data).
+ * Requirements (else SV_ERR_UNSUPPORTED, nothing enqueued): bf16 attention
+ * (head_dim 64 or 128), bf16 logits whose rows start on 16 bytes (V a multiple
+ * of 8), equal B and N in both argument blocks, and no commit when the tree
+ * rows are in the cache (that commit moves rows the attention reads).
+ * attn->status additionally reports 7 if a wait inside the launch expired.
+ */
+typedef struct sv_step_args {
+  const sv_attn_args* attn;
+  const sv_accept_args* accept;
+  uint64_t* anc_bits;     /* optional mask outputs [B, N, W] */
+  int32_t* depth;         /* [B, N] */
+  int32_t* path_rows;     /* [B, N+1, max_depth], nullable */
+  int32_t* mask_status;   /* [B] */
+  void* workspace;
+  size_t workspace_bytes;
+} sv_step_args;
+size_t sv_verify_step_workspace(const sv_step_args* args);
+sv_status sv_verify_step(const sv_step_args* args, void* stream);
+
+/*
  * sv_outcome_lookup -- outcome lookup of speculative speculative decoding
  * ([SSD] sec. 2: while the target verifies, the drafter prepares speculations
  * for the likely verification outcomes -- how many tokens are accepted and

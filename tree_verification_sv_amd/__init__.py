@@ -30,7 +30,7 @@ SV_SEQ_NONFINITE = 8
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 SOURCES = ["sv_api.hip", "sv_mask.hip", "sv_attention.hip", "sv_accept.hip", "sv_threshold.hip", "sv_commit.hip",
-           "sv_ssd.hip", "sv_vocab.hip"]
+           "sv_ssd.hip", "sv_vocab.hip", "sv_step.hip"]
 
 
 class SpecVerifyError(RuntimeError):
@@ -89,6 +89,12 @@ class sv_commit_args(ctypes.Structure):
                 ("cache_layer_stride", ctypes.c_int64), ("tree_layer_stride", ctypes.c_int64)]
 
 
+class sv_step_args(ctypes.Structure):
+    _fields_ = [("attn", ctypes.c_void_p), ("accept", ctypes.c_void_p), ("anc_bits", ctypes.c_void_p),
+                ("depth", ctypes.c_void_p), ("path_rows", ctypes.c_void_p), ("mask_status", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
 class sv_outcome_args(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("K", ctypes.c_int32), ("P", ctypes.c_int32), ("max_depth", ctypes.c_int32),
                 ("stop_row", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p), ("num_out", ctypes.c_void_p),
@@ -98,7 +104,7 @@ class sv_outcome_args(ctypes.Structure):
 
 
 EXPORTS = ["sv_build_tree_mask", "sv_tree_attention_workspace", "sv_tree_attention", "sv_accept_workspace",
-           "sv_accept", "sv_accept_noalloc", "sv_kv_commit", "sv_outcome_lookup", "sv_saguaro_reweight", "sv_draft_subset_logits",
+           "sv_accept", "sv_accept_noalloc", "sv_kv_commit", "sv_verify_step_workspace", "sv_verify_step", "sv_outcome_lookup", "sv_saguaro_reweight", "sv_draft_subset_logits",
            "sv_status_string", "sv_version"]
 
 
@@ -125,6 +131,10 @@ def lib():
         L.sv_accept_noalloc.restype = i32
         L.sv_kv_commit.argtypes = [ctypes.POINTER(sv_commit_args), P]
         L.sv_kv_commit.restype = i32
+        L.sv_verify_step_workspace.argtypes = [ctypes.POINTER(sv_step_args)]
+        L.sv_verify_step_workspace.restype = ctypes.c_size_t
+        L.sv_verify_step.argtypes = [ctypes.POINTER(sv_step_args), P]
+        L.sv_verify_step.restype = i32
         L.sv_outcome_lookup.argtypes = [ctypes.POINTER(sv_outcome_args), P]
         L.sv_outcome_lookup.restype = i32
         L.sv_saguaro_reweight.argtypes = [P, i32, i32, i32, i32, P, i32, ctypes.c_float, P]

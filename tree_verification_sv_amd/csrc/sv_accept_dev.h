@@ -543,8 +543,31 @@ __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, 
   const int s0 = rank * ac_slice<T, TH>();  // this work-group's slice of the vocabulary
   if (t == 0) s_xc = 0;
   bool live_row = false;
+  bool skip = false;  // a leaf-region group whose row the walk cannot need any more
+  if (role.region == AC_REGION_LEAVES && item < (int64_t)a.B * (N + 1)) {
+    // A walk reaches a leaf row only through its parent row's accepted child, so the group
+    // waits, before any other load, until the parent row is resolved or the sequence's walk
+    // has finished, and works only when the parent accepted this row's node.  The parent's
+    // group belongs to the region of rows with children, which every XCD dispatches before this
+    // one, so the wait ends (it is bounded all the same; on expiry the row is resolved anyway).
+    if (t == 0) {
+      const int bb = (int)(item / (N + 1)), rr = (int)(item % (N + 1));
+      const int pr = rr > 0 ? a.parents[(int64_t)bb * N + rr - 1] : -2;
+      int gone = 0;
+      for (uint32_t spins = 0; spins < AC_SPIN_LIMIT; ++spins) {
+        if (ld_u32(&ws.cancel[bb]) != 0u) { gone = 1; break; }
+        if (pr < -1 || pr >= N) break;  // not a usable node: the facts below say so
+        const uint64_t v = ld_u64(&ws.res[(int64_t)bb * (N + 1) + pr + 1]);
+        if (res_ready(v)) { gone = res_child(v) != rr - 1; break; }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      s_xc = gone;
+    }
+    __syncthreads();
+    skip = s_xc != 0;
+  }
 
-  if (item < (int64_t)a.B * (N + 1)) {
+  if (item < (int64_t)a.B * (N + 1) && !skip) {
     // uniform, and kept in scalar registers so that the slice loads take a scalar resource
     const int b = __builtin_amdgcn_readfirstlane((int)(item / (N + 1)));
     const int r = __builtin_amdgcn_readfirstlane((int)(item % (N + 1)));

@@ -31,434 +31,23 @@
 
 namespace {
 
-constexpr int AT_WAVES = 4;
-constexpr int AT_THREADS = 64 * AT_WAVES;
-constexpr int MF_WAVES = 8;                // waves of the MFMA kernel (two per SIMD)
-constexpr int MF_THREADS = 64 * MF_WAVES;
-constexpr int MF_QB = 1;                   // 32-row query blocks per wave
-constexpr int KT = 64;  // keys per tile
 #ifndef SV_ATTN_MIN_SPLIT_TILES
 #define SV_ATTN_MIN_SPLIT_TILES 2  // a prefix split covers at least this many tiles
 #endif
 constexpr int TARGET_WG = 256;
-
-struct AttnPlan {
-  int32_t G, M, QB, QT, qtiles, nsplit, chunk, ntt, W, cap;
-  float cscale;  // scale * log2(e)
-  uint32_t pool_bytes;  // paged: bytes of one K (or V) pool, < 4 GiB
-  uint16_t* opart;  // [units][nsplit][QT][D] bf16: the split's output row O / l
-  float* mlpart;    // [units][nsplit][QT][2]: running max (scaled by log2 e) and l
-};
-
+constexpr int AT_WAVES = 4;
+constexpr int AT_THREADS = 64 * AT_WAVES;
 // ------------------------------------------------------------------ MFMA path
-// One 64-key tile in LDS: K rows then V rows, row-major without padding.  The
-// 16-byte chunks of row r are stored XOR-swizzled (global chunk c sits in slot
-// c ^ swz(r)), which keeps both the 16-byte K fragment reads and the 8-byte
-// transposing V reads free of bank conflicts.  Tiles are written by direct
-// global -> LDS loads (each load instruction of a wave fills 1 KB: lane l's 16
-// bytes land at byte 16 l), so staging a tile costs no registers.
-template <int D>
-struct Tile {
-  static constexpr int KT = 64;
-  static constexpr int CPR = D / 8;                   // 16-byte chunks per row
-  static constexpr int ROWB = D * 2;                  // bytes per row
-  static constexpr int RPI = 64 / CPR;                // rows filled by one load instruction
-  static constexpr int IPW = KT / RPI / MF_WAVES;     // load instructions per wave per tensor
-  static constexpr int RPW = RPI * IPW;               // rows filled by one wave
-  static constexpr int TBYTES = KT * ROWB;            // one tensor of the tile
-  static constexpr int BUF = 2 * TBYTES;              // K and V
-  static constexpr int QROWS = 32 * MF_QB * MF_WAVES;  // query rows per work-group
-  __device__ static __forceinline__ int swz(int r) {
-    return CPR == 16 ? (((r << 1) & 14) | ((r >> 3) & 1)) : ((r & 6) | ((r >> 3) & 1));
-  }
-};
-
 template <int D>
 __global__ void __launch_bounds__(MF_THREADS, 2) k_attn_mfma(sv_attn_args a, AttnPlan p) {
-  using TL = Tile<D>;
-  constexpr int QB = MF_QB;             // 32-row query blocks per wave
-  constexpr int KT64 = TL::KT;
-  constexpr int DS = D / 16;            // 16-wide k-steps of S = K Q^T
-  constexpr int DB = D / 32;            // 32-wide d-blocks of O^T
-  constexpr uint32_t ROWB = TL::ROWB;
-  // two tile buffers as separate arrays: the compiler can then tell that the loads
-  // streaming into one never alias the reads of the other, and does not wait on them
-  __shared__ __attribute__((aligned(1024))) unsigned char kvA[TL::BUF];
-  __shared__ __attribute__((aligned(1024))) unsigned char kvB[TL::BUF];
-  __shared__ __attribute__((aligned(1024))) unsigned char qsb[TL::QROWS * TL::ROWB];  // the work-group's query rows
-
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform wave index
-  const int lq = lane & 31;  // query column / key row inside a 32-block
-  const int hf = lane >> 5;  // which half of the k dimension this lane feeds
-  // the two waves sharing a SIMD get different issue priorities, so that one runs ahead
-  // of the other inside each tile and its softmax overlaps the other's MFMAs
-  if (w < MF_WAVES / 2) __builtin_amdgcn_s_setprio(1);
-
+  __shared__ __attribute__((aligned(1024))) unsigned char kvA[Tile<D>::BUF];
+  __shared__ __attribute__((aligned(1024))) unsigned char kvB[Tile<D>::BUF];
+  __shared__ __attribute__((aligned(1024))) unsigned char qsb[Tile<D>::QROWS * Tile<D>::ROWB];
   // XCD-aware block order: consecutive logical ids land on the same XCD
   const int nb = gridDim.x;
   const int bid = blockIdx.x;
   const int lid = (nb % 8 == 0) ? (bid % 8) * (nb / 8) + bid / 8 : bid;
-  const int qtile = lid % p.qtiles;
-  const int split = (lid / p.qtiles) % p.nsplit;
-  const int pair = lid / (p.qtiles * p.nsplit);
-  const int b = pair / a.Hkv;
-  const int g = pair % a.Hkv;
-  const int N = a.N, Hq = a.Hq, G = p.G;
-
-  if (a.status && g == 0 && qtile == 0 && split == 0) write_seq_status(a, b, p.cap);
-  const int L = clamp_len(a.prefix_len[b], p.cap);
-  const int k0 = split * p.chunk;
-  const int k1 = min(k0 + p.chunk, L);
-  const int ntp = k1 > k0 ? (k1 - k0 + KT64 - 1) / KT64 : 0;
-  const bool last = split == p.nsplit - 1;
-  const int ntt = last ? p.ntt : 0;
-  const int ntiles = ntp + ntt;
-
-  // rows of this wave: m = qtile * QT + w * 32 QB + qb * 32 + lq
-  const int mw = qtile * p.QT + w * 32 * QB;
-  const bool active = mw < p.M;  // uniform: the wave has at least one valid query row
-
-  const __bf16* qg = (const __bf16*)a.q;
-  const uint16_t* kc = (const uint16_t*)a.k_cache;
-  const uint16_t* vc = (const uint16_t*)a.v_cache;
-  const uint16_t* kt = (const uint16_t*)a.k_tree;
-  const uint16_t* vt = (const uint16_t*)a.v_tree;
-
-  // ---- tile loads: wave w fills rows RPW w .. RPW w + RPW - 1 of K and of V.  Keys past
-  // the valid range are clamped onto the last valid key of the tile (finite data,
-  // masked out of the softmax), so no load ever leaves the tensor.
-  const int64_t plane = (int64_t)b * a.Hkv + g;
-  // tree rows: the separate tree K/V rows 1..N, or (tree_in_cache) cache positions
-  // L .. L + N - 1 of this sequence; L <= capacity - N, so they lie inside the cache
-  const bool tic = a.tree_in_cache != 0;
-  const bool tic_paged = tic && a.paged;
-  __amdgpu_buffer_rsrc_t rk, rv, rkt, rvt;
-  if (a.paged) {
-    rk = __builtin_amdgcn_make_buffer_rsrc((void*)kc, 0, (int)p.pool_bytes, 0x00020000);
-    rv = __builtin_amdgcn_make_buffer_rsrc((void*)vc, 0, (int)p.pool_bytes, 0x00020000);
-  } else {
-    rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + plane * a.Lcap * D), 0, (int)(a.Lcap * ROWB), 0x00020000);
-    rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + plane * a.Lcap * D), 0, (int)(a.Lcap * ROWB), 0x00020000);
-  }
-  if (tic_paged) {
-    rkt = rk;  // rows gathered through the block table, lane by lane
-    rvt = rv;
-  } else if (tic) {
-    rkt = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + (plane * a.Lcap + L) * D), 0, (int)(N * ROWB), 0x00020000);
-    rvt = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + (plane * a.Lcap + L) * D), 0, (int)(N * ROWB), 0x00020000);
-  } else {
-    rkt = __builtin_amdgcn_make_buffer_rsrc((void*)(kt + (plane * (N + 1) + 1) * D), 0, (int)(N * ROWB), 0x00020000);
-    rvt = __builtin_amdgcn_make_buffer_rsrc((void*)(vt + (plane * (N + 1) + 1) * D), 0, (int)(N * ROWB), 0x00020000);
-  }
-  auto load_tile = [&](int tile, unsigned char* kb) {
-    const bool tree = tile >= ntp;
-    int klast;
-    int t0 = 0;
-    uint32_t soff = 0;
-    if (tree) {
-      t0 = (tile - ntp) * KT64;
-      klast = min(KT64, N - t0) - 1;
-      soff = tic_paged ? 0u : (uint32_t)t0 * ROWB;
-    } else {
-      const int j0 = k0 + tile * KT64;
-      klast = min(KT64, k1 - j0) - 1;
-      if (a.paged) {
-        // the wave's rows lie in one 16-token block (RPW divides 16); past the end the
-        // clamped key min(r, klast) = klast, so its block is the one used
-        const int blk = (j0 + min(TL::RPW * w, klast)) / 16;
-        int id = __builtin_amdgcn_readfirstlane(a.block_table[(int64_t)b * a.max_blocks + blk]);
-        id = (id < 0 || id >= a.num_blocks) ? 0 : id;
-        soff = (uint32_t)(((int64_t)id * a.Hkv + g) * 16) * ROWB;
-      } else {
-        soff = (uint32_t)j0 * ROWB;
-      }
-    }
-    const bool paged_tile = !tree && a.paged;
-    const __amdgpu_buffer_rsrc_t rK = tree ? rkt : rk;
-    const __amdgpu_buffer_rsrc_t rV = tree ? rvt : rv;
-#pragma unroll
-    for (int it = 0; it < TL::IPW; ++it) {
-      const int n = w * TL::IPW + it;                    // 1-KB piece of the tile (uniform)
-      const int r = n * TL::RPI + lane / TL::CPR;        // row this lane fills
-      const int c = (lane % TL::CPR) ^ TL::swz(r);       // global chunk stored in its slot
-      const int key = min(r, klast);
-      uint32_t off;
-      if (tree && tic_paged) {
-        // tree node t0 + key sits at logical position L + t0 + key < capacity
-        const int pos = L + t0 + key;
-        int id = a.block_table[(int64_t)b * a.max_blocks + pos / 16];
-        id = (id < 0 || id >= a.num_blocks) ? 0 : id;
-        off = (uint32_t)((((int64_t)id * a.Hkv + g) * 16 + (pos & 15)) * ROWB + c * 16);
-      } else {
-        off = (uint32_t)((paged_tile ? (key & 15) : key) * ROWB + c * 16);
-      }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_void*)(kb + n * 1024), 16, off, soff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_void*)(kb + TL::TBYTES + n * 1024), 16, off, soff, 0, 0);
-    }
-  };
-
-  if (0 < ntiles) load_tile(0, kvA);
-
-  // ---- the work-group's query rows into LDS, swizzled like K (rows past M repeat row
-  // M - 1; their outputs are never written).  The B operand of S^T = K Q^T for lane
-  // (lq, hf) and k-step ds is Q row lq, d = 16*ds + 8*hf .. +7.
-  {
-    constexpr int NQ = TL::QROWS * TL::CPR / 64 / MF_WAVES;  // 1-KB pieces per wave
-#pragma unroll
-    for (int it = 0; it < NQ; ++it) {
-      const int n = w * NQ + it;
-      const int r = n * TL::RPI + lane / TL::CPR;
-      const int c = (lane % TL::CPR) ^ TL::swz(r);
-      const int m = min(qtile * p.QT + r, p.M - 1);
-      const int node = m / G, h = g * G + m % G;
-      __builtin_amdgcn_global_load_lds((const void*)(qg + (((int64_t)b * N + node) * Hq + h) * D + c * 8),
-                                       (lds_void*)(qsb + n * 1024), 16, 0, 0);
-    }
-  }
-  int qnode[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int m = mw + qb * 32 + lq;
-    qnode[qb] = m < p.M ? m / G : -1;
-  }
-
-  sv_f32x16 oacc[QB][DB];
-  float mrun[QB], lrun[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    mrun[qb] = -INFINITY;
-    lrun[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.f;
-  }
-
-  // lane-constant parts of the LDS fragment reads
-  const int k_off = lq * ROWB;                       // K row lq of a 32-key block (+ 32 kb rows)
-  const int k_swz = TL::swz(lq);
-  // transposing V reads: source lane (16 u + 4 j + q) addresses row 4 (u / 2) + j (+ 8 for
-  // the upper half) at element column 16 (u % 2) + 4 q, i.e. chunk 2 (u % 2) + q / 2, half q % 2
-  const int tr_row = 4 * (lane >> 5) + ((lane & 15) >> 2);
-  const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const int tr_half = (lane & 1) * 8;
-  const int tr_swz_lo = TL::swz(tr_row), tr_swz_hi = TL::swz(tr_row + 8);
-
-  auto compute = [&](int tile, const unsigned char* Kb) {
-    const unsigned char* Vb = Kb + TL::TBYTES;
-    const bool tree = tile >= ntp;
-    const int j0 = k0 + tile * KT64;
-    const int t0 = (tile - ntp) * KT64;
-
-    // ---- S^T = K Q^T for two 32-key blocks
-    sv_f32x16 sacc[QB][2];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[qb][kb][r] = 0.f;
-    // the fragments of k-step ds + 1 are read while the MFMAs of step ds run, so the LDS
-    // latency is hidden behind them
-    sv_bf16x8 qf[2][QB], kf[2][2];
-    auto frag = [&](int ds, int buf) {
-      const int kslot = ((2 * ds + hf) ^ k_swz) * 16;  // Q and K rows share the swizzle of row lq
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-        qf[buf][qb] = *(const sv_bf16x8*)(qsb + (w * 32 * QB + qb * 32) * ROWB + k_off + kslot);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) kf[buf][kb] = *(const sv_bf16x8*)(Kb + kb * 32 * ROWB + k_off + kslot);
-    };
-    frag(0, 0);
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      if (ds + 1 < DS) frag(ds + 1, (ds + 1) & 1);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds & 1][kb], qf[ds & 1][qb], sacc[qb][kb], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);  // one step in flight at a time (register pressure)
-    }
-
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- masks + online softmax (lane owns query column lq; keys 32 kb + 8 (r/4) + 4 hf + r%4)
-    const bool full = !tree && (j0 + KT64 <= k1);
-    sv_bf16x8 pf[QB][2][2];
-    bool moved = false;
-    float alpha[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      // scores stay unscaled here; the scale (times log2 e) is folded into the exponent
-      if (!full && !tree) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kk = 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (j0 + kk >= k1) sacc[qb][kb][r] = -INFINITY;
-          }
-      } else if (tree) {
-        const int wi = t0 >> 6;  // uniform: the tile is one 64-bit mask word of the query node's bitset
-        uint64_t aw = qnode[qb] >= 0 ? a.anc_bits[((int64_t)b * N + qnode[qb]) * p.W + wi] : 0ull;
-        const int lim = N - t0;  // keys of the tile that are tree nodes
-        if (lim < 64) aw &= (1ull << lim) - 1ull;
-        // shift this lane's key half to bit 0, so every register tests a constant bit
-        const uint64_t sh = aw >> (4 * hf);
-        const uint32_t a_lo = (uint32_t)sh, a_hi = (uint32_t)(sh >> 32);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const uint32_t word = kb == 0 ? a_lo : a_hi;
-            if (((word >> (8 * (r >> 2) + (r & 3))) & 1u) == 0) sacc[qb][kb][r] = -INFINITY;
-          }
-      }
-      float mt = sacc[qb][0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[qb][kb][r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mnew = fmaxf(mrun[qb], mt);  // running maximum of the unscaled scores
-      const float ms = mnew == -INFINITY ? 0.f : mnew * p.cscale;  // nothing visible yet: weights stay 0
-      alpha[qb] = __builtin_amdgcn_exp2f(mrun[qb] * p.cscale - ms);
-      moved |= mnew != mrun[qb];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          pf[qb][kb][r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][r], p.cscale, -ms));
-      // the row sum of the bf16 weights the P V product uses: two per dot instruction
-      float psum0 = 0.f, psum1 = 0.f;
-      const sv_bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          const sv_bf16x8 v = pf[qb][kb][t2];
-          psum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one2, psum0, false);
-          psum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one2, psum1, false);
-          psum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one2, psum0, false);
-          psum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one2, psum1, false);
-        }
-      float psum = psum0 + psum1;
-      psum += __shfl_xor(psum, 32);
-      lrun[qb] = lrun[qb] * alpha[qb] + psum;
-      mrun[qb] = mnew;
-      __builtin_amdgcn_sched_barrier(0);  // one query block at a time (register pressure)
-    }
-    // rescale the accumulators only when some lane's running maximum moved
-    if (__ballot(moved)) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha[qb];
-    }
-
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- O^T += V^T P^T; the 16-key step (kb, t2) holds keys 32 kb + 16 t2 + 4 hf + {0..3, 8..11}.
-    // Half-steps of two d-blocks: the transposing reads of half-step h + 1 are issued before
-    // the MFMAs of half-step h, which wait only for their own reads (LDS reads complete in
-    // order, so at most the 4 newer reads may still be outstanding).
-    constexpr int NH = 2 * DB;  // 4 steps (kb, t2) x DB / 2 halves
-    uint2 vlo[2][2], vhi[2][2];
-    auto tr_issue = [&](int h, int buf) {
-      const int st = h / (DB / 2), d0 = (h % (DB / 2)) * 2;  // step kb * 2 + t2, first d-block
-      const int kb = st >> 1, t2 = st & 1;
-      const uint32_t rlo = lds_addr(Vb) + (32 * kb + 16 * t2 + tr_row) * ROWB + tr_half;
-      const uint32_t rhi = rlo + 8 * ROWB;
-      uint32_t alo[2], ahi[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int c = 4 * (d0 + j) + tr_chunk;
-        alo[j] = rlo + ((c ^ tr_swz_lo) << 4);
-        ahi[j] = rhi + ((c ^ tr_swz_hi) << 4);
-      }
-      tr_read_issue(vlo[buf], vhi[buf], alo, ahi);
-    };
-    tr_issue(0, 0);
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      const int buf = h & 1;
-      if (h + 1 < NH) {
-        tr_issue(h + 1, buf ^ 1);
-        tr_wait<4>(vlo[buf], vhi[buf]);
-      } else {
-        tr_wait<0>(vlo[buf], vhi[buf]);
-      }
-      const int st = h / (DB / 2), d0 = (h % (DB / 2)) * 2;
-      const int kb = st >> 1, t2 = st & 1;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const sv_bf16x8 vf = __builtin_bit_cast(sv_bf16x8, make_uint4(vlo[buf][j].x, vlo[buf][j].y, vhi[buf][j].x, vhi[buf][j].y));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          oacc[qb][d0 + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][kb][t2], oacc[qb][d0 + j], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // ---- main loop: even tiles compute from kvA while the next tile streams into kvB, and back
-  for (int tile = 0; tile < ntiles; tile += 2) {
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of `tile` (and the Q rows) have landed
-    __syncthreads();                // ... and everyone's; every wave is done with tile - 1
-    if (tile + 1 < ntiles) load_tile(tile + 1, kvB);
-    if (active) compute(tile, kvA);
-    if (tile + 1 >= ntiles) break;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tile + 2 < ntiles) load_tile(tile + 2, kvA);
-    if (active) compute(tile + 1, kvB);
-  }
-  if (!active) return;
-
-  // ---- write: bf16 output (single split) or per-split partials: the normalised row
-  // O / l in bf16 and (m, l) in fp32.  The wave stages its rows in its own query rows of
-  // LDS (no other wave reads them, and its own reads of them are done), swizzled like the
-  // query layout, then stores whole rows with 16 consecutive bytes per lane.
-  const int unit = pair * p.qtiles + qtile;
-  const int64_t pidx = (int64_t)unit * p.nsplit + split;
-  unsigned char* ob = qsb + (w * 32 * QB) * ROWB;
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int ql = w * 32 * QB + qb * 32 + lq;
-    const int m = qtile * p.QT + ql;
-    const float inv = lrun[qb] > 0.f ? 1.f / lrun[qb] : 0.f;
-    if (p.nsplit > 1 && hf == 0 && m < p.M)
-      *(float2*)(p.mlpart + (pidx * p.QT + ql) * 2) = make_float2(mrun[qb] * p.cscale, lrun[qb]);
-    const int sw = TL::swz(lq);
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int c = 4 * db + rq;  // 16-byte chunk of elements db*32 + 8 rq .. + 7; this lane holds half hf
-        const uint32_t w0 = f32_to_bf16_bits(oacc[qb][db][4 * rq + 0] * inv) |
-                            ((uint32_t)f32_to_bf16_bits(oacc[qb][db][4 * rq + 1] * inv) << 16);
-        const uint32_t w1 = f32_to_bf16_bits(oacc[qb][db][4 * rq + 2] * inv) |
-                            ((uint32_t)f32_to_bf16_bits(oacc[qb][db][4 * rq + 3] * inv) << 16);
-        *(uint2*)(ob + (qb * 32 + lq) * ROWB + ((c ^ sw) << 4) + 8 * hf) = make_uint2(w0, w1);
-      }
-  }
-  constexpr int CPR = TL::CPR, RPO = 64 / CPR;  // 16-byte chunks per row, rows per store
-#pragma unroll
-  for (int i = 0; i < 32 * QB / RPO; ++i) {
-    const int r = i * RPO + lane / CPR;  // row of the wave's block
-    const int ch = lane % CPR;
-    const uint4 v = *(const uint4*)(ob + r * ROWB + ((ch ^ TL::swz(r)) << 4));
-    const int ql = w * 32 * QB + r;
-    const int m = qtile * p.QT + ql;
-    if (m < p.M) {
-      uint16_t* orow = p.nsplit == 1 ? (uint16_t*)a.out + (((int64_t)b * N + m / G) * Hq + g * G + m % G) * D
-                                     : p.opart + (pidx * p.QT + ql) * D;
-      *(uint4*)(orow + ch * 8) = v;
-    }
-  }
+  attn_mfma_body<D>(a, p, lid, kvA, kvB, qsb, nullptr, 0, nullptr);
 }
 
 // merge split partials: one wave per output row (b, node, head).  Every load
@@ -696,7 +285,10 @@ size_t workspace_bytes(const sv_attn_args& a, const AttnPlan& p) {
   return obytes + parts * 2 * sizeof(float);
 }
 
-sv_status validate(const sv_attn_args& a) {
+}  // namespace
+
+// Argument checks of sv_tree_attention (also used by the one-launch step).
+sv_status sv_attn_validate(const sv_attn_args& a) {
   if (a.B < 0 || a.N < 1 || a.N > SV_MAX_N || a.Hq < 1 || a.Hkv < 1 || a.Hq % a.Hkv) return SV_ERR_INVALID_ARGUMENT;
   if (a.Hq / a.Hkv > 16) return SV_ERR_UNSUPPORTED;
   if (a.D != 64 && a.D != 128) return SV_ERR_UNSUPPORTED;
@@ -713,17 +305,19 @@ sv_status validate(const sv_attn_args& a) {
   return SV_OK;
 }
 
+namespace {
+
 }  // namespace
 
 extern "C" size_t sv_tree_attention_workspace(const sv_attn_args* args) {
-  if (!args || validate(*args) != SV_OK || args->B == 0) return 0;
+  if (!args || sv_attn_validate(*args) != SV_OK || args->B == 0) return 0;
   return workspace_bytes(*args, make_plan(*args));
 }
 
 extern "C" sv_status sv_tree_attention(const sv_attn_args* args, void* stream) {
   if (!args) return SV_ERR_INVALID_ARGUMENT;
   const sv_attn_args& a = *args;
-  sv_status st = validate(a);
+  sv_status st = sv_attn_validate(a);
   if (st != SV_OK) return st;
   if (a.B == 0) return SV_OK;
   if (!a.q || !a.k_cache || !a.v_cache || (!a.tree_in_cache && (!a.k_tree || !a.v_tree)) || !a.prefix_len ||

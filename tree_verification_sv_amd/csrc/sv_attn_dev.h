@@ -26,7 +26,7 @@ __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L
 // sequence: 6 when prefix_len lies outside [0, capacity] (it is clamped), 5 when
 // a needed block-table entry is the ghost block 0 or outside the pool (read as
 // the ghost block).
-__device__ void write_seq_status(const sv_attn_args& a, int b, int cap) {
+__device__ __forceinline__ void write_seq_status(const sv_attn_args& a, int b, int cap) {
   __shared__ int s_code;
   if (threadIdx.x == 0) s_code = 0;
   __syncthreads();
@@ -74,50 +74,45 @@ __device__ __forceinline__ void tr_wait(uint2 (&lo)[2], uint2 (&hi)[2]) {
   asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(lo[0]), "+v"(hi[0]), "+v"(lo[1]), "+v"(hi[1]) : "n"(N) : "memory");
 }
 
-// ------------------------------------------------------------------ one-launch step: attention
-// The step's work-groups have 256 threads (four waves), so that an attention
-// work-group and an acceptance work-group can share a compute unit (two
-// work-groups of at most 80 KB of LDS each).  An attention work-group owns one
-// (sequence, KV head) pair, a tile of 128 query rows (wave w: rows 32 w .. 32 w +
-// 31) and a key range of the prefix (the pair's last split also takes the tree
-// keys), in 32-key K/V tiles streamed into LDS by direct loads, one tile in flight
-// while the other is consumed.  The MFMA tiling, swizzle, online softmax and
-// transposing V reads are those of k_attn_mfma with one 32-key block per tile.
-// Several splits write normalised bf16 rows O / l with fp32 (m, l) and count in
-// on the unit's arrival counter (release); merge work-groups, placed after every
-// attention work-group in the grid, wait for the count (acquire) and combine.
-constexpr int ST_WAVES = 4;
-constexpr int ST_THREADS = 64 * ST_WAVES;
-constexpr int ST_KT = 32;              // keys per tile
-constexpr int ST_QT = 32 * ST_WAVES;   // query rows per work-group
-constexpr uint32_t ST_SPIN_LIMIT = 1u << 22;  // bounded wait of a merge work-group (polls)
+// ------------------------------------------------------------------ MFMA attention
+constexpr uint32_t AT_SPIN_LIMIT = 1u << 22;  // bounded wait of a merge work-group of the one-launch step (polls)
+constexpr int MF_WAVES = 8;                // waves of the MFMA kernel (two per SIMD)
+constexpr int MF_THREADS = 64 * MF_WAVES;
+constexpr int MF_QB = 1;                   // 32-row query blocks per wave
+constexpr int KT = 64;  // keys per tile
 
+struct AttnPlan {
+  int32_t G, M, QB, QT, qtiles, nsplit, chunk, ntt, W, cap;
+  float cscale;  // scale * log2(e)
+  uint32_t pool_bytes;  // paged: bytes of one K (or V) pool, < 4 GiB
+  uint16_t* opart;  // [units][nsplit][QT][D] bf16: the split's output row O / l
+  float* mlpart;    // [units][nsplit][QT][2]: running max (scaled by log2 e) and l
+  // one-launch step only: splits count in on arrive[unit] after their partials (release),
+  // and mper merge work-groups of mrows output rows each combine a (sequence, KV head) pair
+  uint32_t* arrive;
+  int32_t nunits, nwg, mrows, mper;
+};
+
+// One 64-key tile in LDS: K rows then V rows, row-major without padding.  The
+// 16-byte chunks of row r are stored XOR-swizzled (global chunk c sits in slot
+// c ^ swz(r)), which keeps both the 16-byte K fragment reads and the 8-byte
+// transposing V reads free of bank conflicts.  Tiles are written by direct
+// global -> LDS loads (each load instruction of a wave fills 1 KB: lane l's 16
+// bytes land at byte 16 l), so staging a tile costs no registers.
 template <int D>
-struct STile {
-  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
-  static constexpr int ROWB = D * 2;                 // bytes per row
-  static constexpr int RPI = 64 / CPR;               // rows filled by one load instruction
-  static constexpr int IPW = ST_KT / RPI / ST_WAVES;  // load instructions per wave per tensor
-  static constexpr int RPW = RPI * IPW;              // rows filled by one wave (8, within one 16-token block)
-  static constexpr int TBYTES = ST_KT * ROWB;        // one tensor of the tile
-  static constexpr int BUF = 2 * TBYTES;             // K and V
-  static constexpr int QBYTES = ST_QT * ROWB;        // the work-group's query rows
+struct Tile {
+  static constexpr int KT = 64;
+  static constexpr int CPR = D / 8;                   // 16-byte chunks per row
+  static constexpr int ROWB = D * 2;                  // bytes per row
+  static constexpr int RPI = 64 / CPR;                // rows filled by one load instruction
+  static constexpr int IPW = KT / RPI / MF_WAVES;     // load instructions per wave per tensor
+  static constexpr int RPW = RPI * IPW;               // rows filled by one wave
+  static constexpr int TBYTES = KT * ROWB;            // one tensor of the tile
+  static constexpr int BUF = 2 * TBYTES;              // K and V
+  static constexpr int QROWS = 32 * MF_QB * MF_WAVES;  // query rows per work-group
   __device__ static __forceinline__ int swz(int r) {
     return CPR == 16 ? (((r << 1) & 14) | ((r >> 3) & 1)) : ((r & 6) | ((r >> 3) & 1));
   }
-};
-
-struct StepAttnPlan {
-  int32_t G, M, qtiles, nsplit, chunk, ntt, W, cap;
-  float cscale;          // scale * log2(e)
-  uint32_t pool_bytes;   // paged: bytes of one K (or V) pool, < 4 GiB
-  int32_t nunits;        // B * Hkv * qtiles
-  int32_t nwg;           // attention work-groups in use (B * Hkv * nsplit * qtiles)
-  int32_t mrows;         // output rows per merge work-group
-  int32_t mper;          // merge work-groups per (sequence, KV head) pair
-  uint16_t* opart;       // [unit][split][ST_QT][D] bf16: the split's output row O / l
-  float* mlpart;         // [unit][split][ST_QT][2]: running max (scaled by log2 e) and l
-  uint32_t* arrive;      // [unit] splits that have written their partials
 };
 
 // Ancestor bitsets of every node of sequence b into LDS (anc[i * 4 + w], four words per node),
@@ -154,29 +149,33 @@ __device__ __forceinline__ void step_ancestors(const int32_t* __restrict__ paren
   __syncthreads();
 }
 
-// One attention work-group of the step.  lid: its index among the attention work-groups;
-// kvA, kvB: the two K/V tile buffers (separate LDS arrays, so that the direct loads into one
-// are known not to alias reads of the other), qsb: the query rows, aux: >= 9 KB of LDS for
-// the ancestor bitsets (last split only).  `parents` and max_depth come from the acceptance
-// arguments.  Every thread calls it; it returns after the unit's arrival count (if any).
+// The work of one attention work-group (logical index lid, MF_THREADS threads): see the file
+// comment of sv_attention.hip.  kvA, kvB: the two K/V tile buffers and qsb: the query rows,
+// three separate LDS arrays (so that the direct loads into one are known not to alias the
+// reads of another).  derive_parents (nullable): the ancestor sets of the query nodes are
+// derived from this parent array into aux (>= 9 KB of LDS) by the rule of sv_build_tree_mask
+// instead of being read from a.anc_bits.  p.arrive (nullable): after writing its partial the
+// work-group counts in on its unit's counter with a release.  Every thread calls it.
 template <int D>
-__device__ __forceinline__ void step_attention(const sv_attn_args& a, const StepAttnPlan& p, int lid,
-                                               const int32_t* __restrict__ parents, int max_depth,
-                                               unsigned char* kvA, unsigned char* kvB, unsigned char* qsb,
+__device__ __forceinline__ void attn_mfma_body(const sv_attn_args& a, const AttnPlan& p, int lid, unsigned char* kvA,
+                                               unsigned char* kvB, unsigned char* qsb,
+                                               const int32_t* __restrict__ derive_parents, int max_depth,
                                                unsigned char* aux) {
-  using TL = STile<D>;
-  constexpr int DS = D / 16;  // 16-wide k-steps of S = K Q^T
-  constexpr int DB = D / 32;  // 32-wide d-blocks of O^T
+  using TL = Tile<D>;
+  constexpr int QB = MF_QB;             // 32-row query blocks per wave
+  constexpr int KT64 = TL::KT;
+  constexpr int DS = D / 16;            // 16-wide k-steps of S = K Q^T
+  constexpr int DB = D / 32;            // 32-wide d-blocks of O^T
   constexpr uint32_t ROWB = TL::ROWB;
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int lq = lane & 31;
-  const int hf = lane >> 5;
-  if (w < ST_WAVES / 2) __builtin_amdgcn_s_setprio(1);
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform wave index
+  const int lq = lane & 31;  // query column / key row inside a 32-block
+  const int hf = lane >> 5;  // which half of the k dimension this lane feeds
+  // the two waves sharing a SIMD get different issue priorities, so that one runs ahead
+  // of the other inside each tile and its softmax overlaps the other's MFMAs
+  if (w < MF_WAVES / 2) __builtin_amdgcn_s_setprio(1);
 
-  // lid = ((pair * nsplit) + split) * qtiles + qtile: the query tiles of one key range are
-  // neighbours (same XCD, same time), so the second reads the range from L2
   const int qtile = lid % p.qtiles;
   const int split = (lid / p.qtiles) % p.nsplit;
   const int pair = lid / (p.qtiles * p.nsplit);
@@ -188,14 +187,13 @@ __device__ __forceinline__ void step_attention(const sv_attn_args& a, const Step
   const int L = clamp_len(a.prefix_len[b], p.cap);
   const int k0 = split * p.chunk;
   const int k1 = min(k0 + p.chunk, L);
-  const int ntp = k1 > k0 ? (k1 - k0 + ST_KT - 1) / ST_KT : 0;
+  const int ntp = k1 > k0 ? (k1 - k0 + KT64 - 1) / KT64 : 0;
   const bool last = split == p.nsplit - 1;
   const int ntt = last ? p.ntt : 0;
   const int ntiles = ntp + ntt;
 
-  uint64_t* anc = (uint64_t*)aux;                       // [N][4]
-  int32_t* spar = (int32_t*)(aux + SV_MAX_N * 4 * 8);  // [N]
-  const int mw = qtile * ST_QT + w * 32;
+  // rows of this wave: m = qtile * QT + w * 32 QB + qb * 32 + lq
+  const int mw = qtile * p.QT + w * 32 * QB;
   const bool active = mw < p.M;  // uniform: the wave has at least one valid query row
 
   const __bf16* qg = (const __bf16*)a.q;
@@ -203,7 +201,13 @@ __device__ __forceinline__ void step_attention(const sv_attn_args& a, const Step
   const uint16_t* vc = (const uint16_t*)a.v_cache;
   const uint16_t* kt = (const uint16_t*)a.k_tree;
   const uint16_t* vt = (const uint16_t*)a.v_tree;
+
+  // ---- tile loads: wave w fills rows RPW w .. RPW w + RPW - 1 of K and of V.  Keys past
+  // the valid range are clamped onto the last valid key of the tile (finite data,
+  // masked out of the softmax), so no load ever leaves the tensor.
   const int64_t plane = (int64_t)b * a.Hkv + g;
+  // tree rows: the separate tree K/V rows 1..N, or (tree_in_cache) cache positions
+  // L .. L + N - 1 of this sequence; L <= capacity - N, so they lie inside the cache
   const bool tic = a.tree_in_cache != 0;
   const bool tic_paged = tic && a.paged;
   __amdgpu_buffer_rsrc_t rk, rv, rkt, rvt;
@@ -215,7 +219,7 @@ __device__ __forceinline__ void step_attention(const sv_attn_args& a, const Step
     rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + plane * a.Lcap * D), 0, (int)(a.Lcap * ROWB), 0x00020000);
   }
   if (tic_paged) {
-    rkt = rk;
+    rkt = rk;  // rows gathered through the block table, lane by lane
     rvt = rv;
   } else if (tic) {
     rkt = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + (plane * a.Lcap + L) * D), 0, (int)(N * ROWB), 0x00020000);
@@ -224,22 +228,21 @@ __device__ __forceinline__ void step_attention(const sv_attn_args& a, const Step
     rkt = __builtin_amdgcn_make_buffer_rsrc((void*)(kt + (plane * (N + 1) + 1) * D), 0, (int)(N * ROWB), 0x00020000);
     rvt = __builtin_amdgcn_make_buffer_rsrc((void*)(vt + (plane * (N + 1) + 1) * D), 0, (int)(N * ROWB), 0x00020000);
   }
-  // wave w fills rows RPW w .. RPW w + RPW - 1 of K and of V; keys past the valid range are
-  // clamped onto the tile's last valid key (finite data, masked out of the softmax)
   auto load_tile = [&](int tile, unsigned char* kb) {
     const bool tree = tile >= ntp;
     int klast;
     int t0 = 0;
     uint32_t soff = 0;
     if (tree) {
-      t0 = (tile - ntp) * ST_KT;
-      klast = min(ST_KT, N - t0) - 1;
+      t0 = (tile - ntp) * KT64;
+      klast = min(KT64, N - t0) - 1;
       soff = tic_paged ? 0u : (uint32_t)t0 * ROWB;
     } else {
-      const int j0 = k0 + tile * ST_KT;
-      klast = min(ST_KT, k1 - j0) - 1;
+      const int j0 = k0 + tile * KT64;
+      klast = min(KT64, k1 - j0) - 1;
       if (a.paged) {
-        // the wave's 8 rows lie in one 16-token block; past the end the clamped key's block
+        // the wave's rows lie in one 16-token block (RPW divides 16); past the end the
+        // clamped key min(r, klast) = klast, so its block is the one used
         const int blk = (j0 + min(TL::RPW * w, klast)) / 16;
         int id = __builtin_amdgcn_readfirstlane(a.block_table[(int64_t)b * a.max_blocks + blk]);
         id = (id < 0 || id >= a.num_blocks) ? 0 : id;
@@ -253,12 +256,13 @@ __device__ __forceinline__ void step_attention(const sv_attn_args& a, const Step
     const __amdgpu_buffer_rsrc_t rV = tree ? rvt : rv;
 #pragma unroll
     for (int it = 0; it < TL::IPW; ++it) {
-      const int n = w * TL::IPW + it;              // 1-KB piece of the tile (uniform)
-      const int r = n * TL::RPI + lane / TL::CPR;  // row this lane fills
-      const int c = (lane % TL::CPR) ^ TL::swz(r);
+      const int n = w * TL::IPW + it;                    // 1-KB piece of the tile (uniform)
+      const int r = n * TL::RPI + lane / TL::CPR;        // row this lane fills
+      const int c = (lane % TL::CPR) ^ TL::swz(r);       // global chunk stored in its slot
       const int key = min(r, klast);
       uint32_t off;
       if (tree && tic_paged) {
+        // tree node t0 + key sits at logical position L + t0 + key < capacity
         const int pos = L + t0 + key;
         int id = a.block_table[(int64_t)b * a.max_blocks + pos / 16];
         id = (id < 0 || id >= a.num_blocks) ? 0 : id;
@@ -272,33 +276,54 @@ __device__ __forceinline__ void step_attention(const sv_attn_args& a, const Step
   };
 
   if (0 < ntiles) load_tile(0, kvA);
-  {  // the query rows (rows past M repeat row M - 1; their outputs are never written)
-    constexpr int NQ = ST_QT * TL::CPR / 64 / ST_WAVES;
+
+  // ---- the work-group's query rows into LDS, swizzled like K (rows past M repeat row
+  // M - 1; their outputs are never written).  The B operand of S^T = K Q^T for lane
+  // (lq, hf) and k-step ds is Q row lq, d = 16*ds + 8*hf .. +7.
+  {
+    constexpr int NQ = TL::QROWS * TL::CPR / 64 / MF_WAVES;  // 1-KB pieces per wave
 #pragma unroll
     for (int it = 0; it < NQ; ++it) {
       const int n = w * NQ + it;
       const int r = n * TL::RPI + lane / TL::CPR;
       const int c = (lane % TL::CPR) ^ TL::swz(r);
-      const int m = min(qtile * ST_QT + r, p.M - 1);
+      const int m = min(qtile * p.QT + r, p.M - 1);
       const int node = m / G, h = g * G + m % G;
       __builtin_amdgcn_global_load_lds((const void*)(qg + (((int64_t)b * N + node) * Hq + h) * D + c * 8),
                                        (lds_void*)(qsb + n * 1024), 16, 0, 0);
     }
   }
-  // the last split reads the tree keys: ancestor bitsets of every node, from the parents
-  if (ntt > 0) step_ancestors(parents, b, N, max_depth, spar, anc);
-  const int qm = mw + lq;
-  const int qnode = qm < p.M ? qm / G : -1;
-
-  sv_f32x16 oacc[DB];
-  float mrun = -INFINITY, lrun = 0.f;
+  // the last split reads the tree keys: in the one-launch step their masks come from the
+  // parent array, derived here into LDS
+  const uint64_t* anc_lds = nullptr;
+  if (derive_parents && ntt > 0) {
+    step_ancestors(derive_parents, b, N, max_depth, (int32_t*)(aux + SV_MAX_N * 4 * 8), (uint64_t*)aux);
+    anc_lds = (const uint64_t*)aux;
+  }
+  int qnode[QB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  for (int qb = 0; qb < QB; ++qb) {
+    const int m = mw + qb * 32 + lq;
+    qnode[qb] = m < p.M ? m / G : -1;
+  }
 
-  const int k_off = lq * ROWB;
+  sv_f32x16 oacc[QB][DB];
+  float mrun[QB], lrun[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    mrun[qb] = -INFINITY;
+    lrun[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.f;
+  }
+
+  // lane-constant parts of the LDS fragment reads
+  const int k_off = lq * ROWB;                       // K row lq of a 32-key block (+ 32 kb rows)
   const int k_swz = TL::swz(lq);
+  // transposing V reads: source lane (16 u + 4 j + q) addresses row 4 (u / 2) + j (+ 8 for
+  // the upper half) at element column 16 (u % 2) + 4 q, i.e. chunk 2 (u % 2) + q / 2, half q % 2
   const int tr_row = 4 * (lane >> 5) + ((lane & 15) >> 2);
   const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int tr_half = (lane & 1) * 8;
@@ -307,84 +332,129 @@ __device__ __forceinline__ void step_attention(const sv_attn_args& a, const Step
   auto compute = [&](int tile, const unsigned char* Kb) {
     const unsigned char* Vb = Kb + TL::TBYTES;
     const bool tree = tile >= ntp;
-    const int j0 = k0 + tile * ST_KT;
-    const int t0 = (tile - ntp) * ST_KT;
-    // ---- S^T = K Q^T for one 32-key block; the fragments of step ds + 1 are read under the
-    // MFMAs of step ds
-    sv_f32x16 sacc;
+    const int j0 = k0 + tile * KT64;
+    const int t0 = (tile - ntp) * KT64;
+
+    // ---- S^T = K Q^T for two 32-key blocks
+    sv_f32x16 sacc[QB][2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-    sv_bf16x8 qf[2], kf[2];
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[qb][kb][r] = 0.f;
+    // the fragments of k-step ds + 1 are read while the MFMAs of step ds run, so the LDS
+    // latency is hidden behind them
+    sv_bf16x8 qf[2][QB], kf[2][2];
     auto frag = [&](int ds, int buf) {
-      const int kslot = ((2 * ds + hf) ^ k_swz) * 16;
-      qf[buf] = *(const sv_bf16x8*)(qsb + (w * 32) * ROWB + k_off + kslot);
-      kf[buf] = *(const sv_bf16x8*)(Kb + k_off + kslot);
+      const int kslot = ((2 * ds + hf) ^ k_swz) * 16;  // Q and K rows share the swizzle of row lq
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        qf[buf][qb] = *(const sv_bf16x8*)(qsb + (w * 32 * QB + qb * 32) * ROWB + k_off + kslot);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) kf[buf][kb] = *(const sv_bf16x8*)(Kb + kb * 32 * ROWB + k_off + kslot);
     };
     frag(0, 0);
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
       if (ds + 1 < DS) frag(ds + 1, (ds + 1) & 1);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds & 1], qf[ds & 1], sacc, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds & 1][kb], qf[ds & 1][qb], sacc[qb][kb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);  // one step in flight at a time (register pressure)
     }
+
     __builtin_amdgcn_sched_barrier(0);
-    // ---- masks + online softmax (lane owns query column lq; keys 8 (r/4) + 4 hf + r%4)
-    const bool full = !tree && (j0 + ST_KT <= k1);
-    if (!full && !tree) {
+    // ---- masks + online softmax (lane owns query column lq; keys 32 kb + 8 (r/4) + 4 hf + r%4)
+    const bool full = !tree && (j0 + KT64 <= k1);
+    sv_bf16x8 pf[QB][2][2];
+    bool moved = false;
+    float alpha[QB];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = 8 * (r >> 2) + 4 * hf + (r & 3);
-        if (j0 + kk >= k1) sacc[r] = -INFINITY;
+    for (int qb = 0; qb < QB; ++qb) {
+      // scores stay unscaled here; the scale (times log2 e) is folded into the exponent
+      if (!full && !tree) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kk = 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (j0 + kk >= k1) sacc[qb][kb][r] = -INFINITY;
+          }
+      } else if (tree) {
+        const int wi = t0 >> 6;  // uniform: the tile is one 64-bit mask word of the query node's bitset
+        uint64_t aw = qnode[qb] < 0 ? 0ull
+                      : (anc_lds ? anc_lds[qnode[qb] * 4 + wi] : a.anc_bits[((int64_t)b * N + qnode[qb]) * p.W + wi]);
+        const int lim = N - t0;  // keys of the tile that are tree nodes
+        if (lim < 64) aw &= (1ull << lim) - 1ull;
+        // shift this lane's key half to bit 0, so every register tests a constant bit
+        const uint64_t sh = aw >> (4 * hf);
+        const uint32_t a_lo = (uint32_t)sh, a_hi = (uint32_t)(sh >> 32);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t word = kb == 0 ? a_lo : a_hi;
+            if (((word >> (8 * (r >> 2) + (r & 3))) & 1u) == 0) sacc[qb][kb][r] = -INFINITY;
+          }
       }
-    } else if (tree) {
-      // bits t0 .. t0 + 31 of the query node's bitset: one half of one 64-bit word
-      uint64_t aw = qnode >= 0 ? anc[qnode * 4 + (t0 >> 6)] >> (t0 & 63) : 0ull;
-      const int lim = N - t0;  // keys of the tile that are tree nodes (>= 1)
-      if (lim < 32) aw &= (1ull << lim) - 1ull;
-      const uint32_t a_lo = (uint32_t)(aw >> (4 * hf));
+      float mt = sacc[qb][0][0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (((a_lo >> (8 * (r >> 2) + (r & 3))) & 1u) == 0) sacc[r] = -INFINITY;
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[qb][kb][r]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float mnew = fmaxf(mrun[qb], mt);  // running maximum of the unscaled scores
+      const float ms = mnew == -INFINITY ? 0.f : mnew * p.cscale;  // nothing visible yet: weights stay 0
+      alpha[qb] = __builtin_amdgcn_exp2f(mrun[qb] * p.cscale - ms);
+      moved |= mnew != mrun[qb];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          pf[qb][kb][r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][r], p.cscale, -ms));
+      // the row sum of the bf16 weights the P V product uses: two per dot instruction
+      float psum0 = 0.f, psum1 = 0.f;
+      const sv_bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const sv_bf16x8 v = pf[qb][kb][t2];
+          psum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one2, psum0, false);
+          psum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one2, psum1, false);
+          psum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one2, psum0, false);
+          psum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one2, psum1, false);
+        }
+      float psum = psum0 + psum1;
+      psum += __shfl_xor(psum, 32);
+      lrun[qb] = lrun[qb] * alpha[qb] + psum;
+      mrun[qb] = mnew;
+      __builtin_amdgcn_sched_barrier(0);  // one query block at a time (register pressure)
     }
-    float mt = sacc[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sacc[r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mnew = fmaxf(mrun, mt);
-    const float ms = mnew == -INFINITY ? 0.f : mnew * p.cscale;
-    const float alpha = __builtin_amdgcn_exp2f(mrun * p.cscale - ms);
-    const bool moved = mnew != mrun;
-    sv_bf16x8 pf[2];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) pf[r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[r], p.cscale, -ms));
-    float psum0 = 0.f, psum1 = 0.f;
-    const sv_bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      const sv_bf16x8 v = pf[t2];
-      psum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one2, psum0, false);
-      psum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one2, psum1, false);
-      psum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one2, psum0, false);
-      psum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one2, psum1, false);
-    }
-    float psum = psum0 + psum1;
-    psum += __shfl_xor(psum, 32);
-    lrun = lrun * alpha + psum;
-    mrun = mnew;
+    // rescale the accumulators only when some lane's running maximum moved
     if (__ballot(moved)) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha[qb];
     }
+
     __builtin_amdgcn_sched_barrier(0);
-    // ---- O^T += V^T P^T; the 16-key step t2 holds keys 16 t2 + 4 hf + {0..3, 8..11}, in
-    // half-steps of two d-blocks whose transposing reads go out one half-step ahead
-    constexpr int NH = DB;  // 2 steps x DB / 2 halves
+    // ---- O^T += V^T P^T; the 16-key step (kb, t2) holds keys 32 kb + 16 t2 + 4 hf + {0..3, 8..11}.
+    // Half-steps of two d-blocks: the transposing reads of half-step h + 1 are issued before
+    // the MFMAs of half-step h, which wait only for their own reads (LDS reads complete in
+    // order, so at most the 4 newer reads may still be outstanding).
+    constexpr int NH = 2 * DB;  // 4 steps (kb, t2) x DB / 2 halves
     uint2 vlo[2][2], vhi[2][2];
     auto tr_issue = [&](int h, int buf) {
-      const int t2 = h / (DB / 2), d0 = (h % (DB / 2)) * 2;
-      const uint32_t rlo = lds_addr(Vb) + (16 * t2 + tr_row) * ROWB + tr_half;
+      const int st = h / (DB / 2), d0 = (h % (DB / 2)) * 2;  // step kb * 2 + t2, first d-block
+      const int kb = st >> 1, t2 = st & 1;
+      const uint32_t rlo = lds_addr(Vb) + (32 * kb + 16 * t2 + tr_row) * ROWB + tr_half;
       const uint32_t rhi = rlo + 8 * ROWB;
       uint32_t alo[2], ahi[2];
 #pragma unroll
@@ -405,16 +475,20 @@ __device__ __forceinline__ void step_attention(const sv_attn_args& a, const Step
       } else {
         tr_wait<0>(vlo[buf], vhi[buf]);
       }
-      const int t2 = h / (DB / 2), d0 = (h % (DB / 2)) * 2;
+      const int st = h / (DB / 2), d0 = (h % (DB / 2)) * 2;
+      const int kb = st >> 1, t2 = st & 1;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const sv_bf16x8 vf = __builtin_bit_cast(sv_bf16x8, make_uint4(vlo[buf][j].x, vlo[buf][j].y, vhi[buf][j].x, vhi[buf][j].y));
-        oacc[d0 + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t2], oacc[d0 + j], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          oacc[qb][d0 + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][kb][t2], oacc[qb][d0 + j], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
+  // ---- main loop: even tiles compute from kvA while the next tile streams into kvB, and back
   for (int tile = 0; tile < ntiles; tile += 2) {
     __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of `tile` (and the Q rows) have landed
     __syncthreads();                // ... and everyone's; every wave is done with tile - 1
@@ -426,47 +500,50 @@ __device__ __forceinline__ void step_attention(const sv_attn_args& a, const Step
     if (tile + 2 < ntiles) load_tile(tile + 2, kvA);
     if (active) compute(tile + 1, kvB);
   }
-
-  // ---- write: bf16 output (one split) or the split's partial: O / l in bf16, (m, l) in fp32.
-  // The wave stages its rows in its own query rows of LDS, then stores whole rows.
+  // ---- write: bf16 output (single split) or per-split partials: the normalised row
+  // O / l in bf16 and (m, l) in fp32.  The wave stages its rows in its own query rows of
+  // LDS (no other wave reads them, and its own reads of them are done), swizzled like the
+  // query layout, then stores whole rows with 16 consecutive bytes per lane.
   const int unit = pair * p.qtiles + qtile;
   const int64_t pidx = (int64_t)unit * p.nsplit + split;
   if (active) {
-    unsigned char* ob = qsb + (w * 32) * ROWB;
-    const int ql = w * 32 + lq;
-    const int m = qtile * ST_QT + ql;
-    const float inv = lrun > 0.f ? 1.f / lrun : 0.f;
+  unsigned char* ob = qsb + (w * 32 * QB) * ROWB;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int ql = w * 32 * QB + qb * 32 + lq;
+    const int m = qtile * p.QT + ql;
+    const float inv = lrun[qb] > 0.f ? 1.f / lrun[qb] : 0.f;
     if (p.nsplit > 1 && hf == 0 && m < p.M)
-      *(float2*)(p.mlpart + (pidx * ST_QT + ql) * 2) = make_float2(mrun * p.cscale, lrun);
+      *(float2*)(p.mlpart + (pidx * p.QT + ql) * 2) = make_float2(mrun[qb] * p.cscale, lrun[qb]);
     const int sw = TL::swz(lq);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const int c = 4 * db + rq;
-        const uint32_t w0 = f32_to_bf16_bits(oacc[db][4 * rq + 0] * inv) |
-                            ((uint32_t)f32_to_bf16_bits(oacc[db][4 * rq + 1] * inv) << 16);
-        const uint32_t w1 = f32_to_bf16_bits(oacc[db][4 * rq + 2] * inv) |
-                            ((uint32_t)f32_to_bf16_bits(oacc[db][4 * rq + 3] * inv) << 16);
-        *(uint2*)(ob + lq * ROWB + ((c ^ sw) << 4) + 8 * hf) = make_uint2(w0, w1);
+        const int c = 4 * db + rq;  // 16-byte chunk of elements db*32 + 8 rq .. + 7; this lane holds half hf
+        const uint32_t w0 = f32_to_bf16_bits(oacc[qb][db][4 * rq + 0] * inv) |
+                            ((uint32_t)f32_to_bf16_bits(oacc[qb][db][4 * rq + 1] * inv) << 16);
+        const uint32_t w1 = f32_to_bf16_bits(oacc[qb][db][4 * rq + 2] * inv) |
+                            ((uint32_t)f32_to_bf16_bits(oacc[qb][db][4 * rq + 3] * inv) << 16);
+        *(uint2*)(ob + (qb * 32 + lq) * ROWB + ((c ^ sw) << 4) + 8 * hf) = make_uint2(w0, w1);
       }
-    wave_lds_sync();
-    constexpr int CPR = TL::CPR, RPO = 64 / CPR;
+  }
+  constexpr int CPR = TL::CPR, RPO = 64 / CPR;  // 16-byte chunks per row, rows per store
 #pragma unroll
-    for (int i = 0; i < 32 / RPO; ++i) {
-      const int r = i * RPO + lane / CPR;
-      const int ch = lane % CPR;
-      const uint4 v = *(const uint4*)(ob + r * ROWB + ((ch ^ TL::swz(r)) << 4));
-      const int qr = w * 32 + r;
-      const int mm = qtile * ST_QT + qr;
-      if (mm < p.M) {
-        uint16_t* orow = p.nsplit == 1 ? (uint16_t*)a.out + (((int64_t)b * N + mm / G) * Hq + g * G + mm % G) * D
-                                       : p.opart + (pidx * ST_QT + qr) * D;
-        *(uint4*)(orow + ch * 8) = v;
-      }
+  for (int i = 0; i < 32 * QB / RPO; ++i) {
+    const int r = i * RPO + lane / CPR;  // row of the wave's block
+    const int ch = lane % CPR;
+    const uint4 v = *(const uint4*)(ob + r * ROWB + ((ch ^ TL::swz(r)) << 4));
+    const int ql = w * 32 * QB + r;
+    const int m = qtile * p.QT + ql;
+    if (m < p.M) {
+      uint16_t* orow = p.nsplit == 1 ? (uint16_t*)a.out + (((int64_t)b * N + m / G) * Hq + g * G + m % G) * D
+                                     : p.opart + (pidx * p.QT + ql) * D;
+      *(uint4*)(orow + ch * 8) = v;
     }
   }
-  if (p.nsplit > 1) {
+  }  // active
+  if (p.arrive && p.nsplit > 1) {
     __syncthreads();  // every wave's partial stores precede the release below
     if (t == 0) __hip_atomic_fetch_add(&p.arrive[unit], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -476,11 +553,11 @@ __device__ __forceinline__ void step_attention(const sv_attn_args& a, const Step
 // pair.  It waits (bounded) until every split of the units those rows belong to has counted in,
 // then combines the splits' normalised rows with weights exp2(m_s - max) l_s, as
 // k_attn_combine does.  TPR threads per row, one 16-byte chunk each.  s_f: LDS for
-// (256 / TPR) x 64 split weights.  On an expired wait the sequence's attention status is 7.
-template <int D>
-__device__ __forceinline__ void step_merge(const sv_attn_args& a, const StepAttnPlan& p, int mid, float* s_f) {
+// (TH / TPR) x 64 split weights.  On an expired wait the sequence's attention status is 7.
+template <int D, int TH>
+__device__ __forceinline__ void step_merge(const sv_attn_args& a, const AttnPlan& p, int mid, float* s_f) {
   constexpr int TPR = D / 8;                // threads per output row
-  constexpr int RPP = ST_THREADS / TPR;     // rows per pass
+  constexpr int RPP = TH / TPR;             // rows per pass
   constexpr int SB = 16;                    // split rows in flight per thread
   const int t = threadIdx.x;
   const int pair = mid / p.mper, part = mid % p.mper;
@@ -491,11 +568,11 @@ __device__ __forceinline__ void step_merge(const sv_attn_args& a, const StepAttn
   __shared__ int s_late;
   if (t == 0) {
     int late = 0;
-    for (int q = m0 / ST_QT; q <= (m1 - 1) / ST_QT; ++q) {
+    for (int q = m0 / p.QT; q <= (m1 - 1) / p.QT; ++q) {
       uint32_t* cnt = &p.arrive[pair * p.qtiles + q];
       uint32_t spins = 0;
       while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)p.nsplit) {
-        if (++spins > ST_SPIN_LIMIT) { late = 1; break; }
+        if (++spins > AT_SPIN_LIMIT) { late = 1; break; }
         __builtin_amdgcn_s_sleep(1);
       }
     }
@@ -511,15 +588,15 @@ __device__ __forceinline__ void step_merge(const sv_attn_args& a, const StepAttn
     const int m = mb + lr;
     const bool on = m < m1;
     const int mm = on ? m : m1 - 1;
-    const int unit = pair * p.qtiles + mm / ST_QT, ql = mm % ST_QT;
+    const int unit = pair * p.qtiles + mm / p.QT, ql = mm % p.QT;
     // weights: thread c of the row takes splits c, c + TPR, ...; max and sum over the row's lanes
     float mx = -INFINITY;
-    for (int s = c; s < ns; s += TPR) mx = fmaxf(mx, p.mlpart[(((int64_t)unit * ns + s) * ST_QT + ql) * 2]);
+    for (int s = c; s < ns; s += TPR) mx = fmaxf(mx, p.mlpart[(((int64_t)unit * ns + s) * p.QT + ql) * 2]);
 #pragma unroll
     for (int o = TPR / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
     float lsum = 0.f;
     for (int s = c; s < ns; s += TPR) {
-      const float2 ml = *(const float2*)(p.mlpart + (((int64_t)unit * ns + s) * ST_QT + ql) * 2);
+      const float2 ml = *(const float2*)(p.mlpart + (((int64_t)unit * ns + s) * p.QT + ql) * 2);
       const float f = ml.x == -INFINITY ? 0.f : exp2f(ml.x - mx) * ml.y;
       s_f[lr * 64 + s] = f;
       lsum += f;
@@ -535,12 +612,11 @@ __device__ __forceinline__ void step_merge(const sv_attn_args& a, const StepAttn
 #pragma unroll
       for (int k = 0; k < SB; ++k) {
         const int s = min(s0 + k, ns - 1);
-        part[k] = *(const uint4*)(p.opart + (((int64_t)unit * ns + s) * ST_QT + ql) * D + c * 8);
+        part[k] = *(const uint4*)(p.opart + (((int64_t)unit * ns + s) * p.QT + ql) * D + c * 8);
       }
 #pragma unroll
       for (int k = 0; k < SB; ++k) {
-        if (s0 + k >= ns) break;
-        const float f = s_f[lr * 64 + s0 + k];
+        const float f = s0 + k < ns ? s_f[lr * 64 + min(s0 + k, 63)] : 0.f;  // past the splits: weight 0
         const uint32_t ww[4] = {part[k].x, part[k].y, part[k].z, part[k].w};
 #pragma unroll
         for (int h = 0; h < 4; ++h) {

@@ -41,7 +41,7 @@ __device__ __forceinline__ int64_t cache_row(const sv_commit_args& a, int b, int
 // of the path and A its length.  Same checks, outputs and "nothing written on error" as
 // sv_kv_commit: L >= 0 and 0 <= A <= max_depth (1), source row in [1, N] (1), destination slot
 // (6 capacity, 5 block), the first failing position deciding the code.
-__device__ void walker_commit(const sv_commit_args& c, int b, int A, const int32_t* path) {
+__device__ __forceinline__ void walker_commit(const sv_commit_args& c, int b, int A, const int32_t* path) {
   __shared__ int64_t wc_slot[SV_MAX_DEPTH];
   __shared__ int32_t wc_src[SV_MAX_DEPTH];
   __shared__ int32_t wc_code, wc_L;

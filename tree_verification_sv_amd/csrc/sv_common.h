@@ -66,6 +66,9 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Argument checks of sv_tree_attention (sv_attention.hip).
+sv_status sv_attn_validate(const sv_attn_args& a);
+
 // Threshold acceptance (sv_threshold.hip): workspace bytes and launch of both kernels.
 size_t sv_threshold_workspace(const sv_accept_args& a);
 sv_status sv_threshold_launch(const sv_accept_args& a, const sv_commit_args& cm, int32_t has_cm, hipStream_t stream);

@@ -24,7 +24,7 @@ from dataclasses import dataclass
 from typing import Optional
 
 from . import (SV_COMMIT_PATH, SV_GREEDY, SV_STOCHASTIC, SV_TOPK_DRAFT, _check, _stream, accept_args, accept_outputs, attn_args,
-               commit_args, lib, sv_accept_workspace, sv_tree_attention_workspace)
+               commit_args, lib, sv_accept_workspace, sv_step_args, sv_tree_attention_workspace)
 
 
 @dataclass
@@ -93,6 +93,7 @@ class VerifyStep:
                                 self.commit["status"], x.block_table, x.paged, x.num_blocks, x.commit_mode,
                                 x.tree_in_cache, N)
         self._L = lib()
+        self._one = None  # sv_step_args of the one-launch step (see one_launch())
         self._fused = False
         self._mask_free = False
         self._side = None
@@ -142,7 +143,36 @@ class VerifyStep:
         self._acc.depth = None if on else self.mask["depth"].data_ptr()
         self._mask_free = on
 
+    def one_launch(self, on: bool = True, mask_outputs: bool = True):
+        """Run the step as one sv_verify_step launch: the mask (written to self.mask when
+        mask_outputs), the attention, the acceptance and -- after fuse_commit() -- the commit.
+        Returns False (and stays off) when the call does not support these arguments."""
+        import torch
+        if not on:
+            self._one = None
+            return False
+        a = sv_step_args()
+        a.attn = ctypes.addressof(self._attn)
+        a.accept = ctypes.addressof(self._acc)
+        if mask_outputs:
+            m = self.mask
+            a.anc_bits, a.depth = m["anc_bits"].data_ptr(), m["depth"].data_ptr()
+            a.path_rows, a.mask_status = m["path_rows"].data_ptr(), m["status"].data_ptr()
+        need = int(self._L.sv_verify_step_workspace(ctypes.byref(a)))
+        if need == 0:
+            self._one = None
+            return False
+        self.step_ws = torch.zeros(need, dtype=torch.uint8, device=self.x.parents.device)  # counters start at zero
+        a.workspace, a.workspace_bytes = self.step_ws.data_ptr(), need
+        self._one = a
+        return True
+
     def run(self, stream=None, overlap=False, accept_first=False, attention_side=False):
+        if self._one is not None:  # the whole step in one launch (stream order only)
+            _check(self._L.sv_verify_step(ctypes.byref(self._one), _stream(stream)), "sv_verify_step")
+            if not self._fused:
+                self.kv_commit(stream)
+            return
         if overlap and self._com.new_len == self._attn.prefix_len:
             # the commit beside the attention writes new_len while the attention reads prefix_len
             raise ValueError("new_len must not alias prefix_len when the commit overlaps the attention")
