@@ -15,19 +15,19 @@
 // 512-thread work-groups, one per compute unit, in dispatch order (each region
 // starts on a multiple of 8 blocks, so its blocks keep the round-robin XCD
 // order):
-//   1. acceptance groups of the rows that have a usable child (and the root):
-//      the acceptance's critical path, dispatched first;
+//   1. attention work-groups (the MFMA attention body of sv_attn_dev.h, eight
+//      waves, two per SIMD): the longest chain of the step, so they take their
+//      compute units first; the last split of each (sequence, KV head) pair
+//      derives its query nodes' ancestor sets from the parent array itself;
 //   2. the mask outputs, when the caller asks for them (one work-group per
 //      sequence; nothing else reads them);
-//   3. attention work-groups (the MFMA attention body of sv_attn_dev.h, eight
-//      waves, two per SIMD); the last split of each (sequence, KV head) pair
-//      derives its query nodes' ancestor sets from the parent array itself;
+//   3. acceptance groups of the rows that have a usable child (and the root);
 //   4. merge work-groups, which wait for the attention splits they combine --
 //      only for work-groups dispatched before them, so the wait always ends;
 //   5. acceptance groups of the leaf rows: the walk needs a leaf row only when
 //      it stops there, so these run last and exit at once once the walk is done
-//      (stochastic and top-K walks over wide trees; otherwise region 1 takes
-//      every row).
+//      (stochastic and top-K walks over wide trees; otherwise region 3 takes
+//      every row).  They wait only for rows of region 3.
 // The acceptance's bonus staging area is laid over the attention's tile and query
 // buffers (a work-group runs one role), 155 KB of LDS in all.
 #include "sv_accept_dev.h"
@@ -49,9 +49,9 @@ struct StepKArgs {
   int32_t* m_depth;
   int32_t* m_path;
   int32_t* m_status;
-  int32_t r_mask, r_att, r_merge, r_leaf, r_end;  // first block of regions 2..5, and the grid size
-  int32_t na1, nacc;    // acceptance work-groups of region 1, of regions 1 and 5
-  int32_t ng1;          // row groups of region 1 (the leaf region's groups follow them)
+  int32_t r_mask, r_acc, r_merge, r_leaf, r_end;  // first block of regions 2..5, and the grid size
+  int32_t na1, nacc;    // acceptance work-groups of region 3, of regions 3 and 5
+  int32_t ng1;          // row groups of region 3 (the leaf region's groups follow them)
   uint32_t* exit_count; // work-groups of the launch that have finished
 };
 
@@ -83,8 +83,20 @@ __global__ void __launch_bounds__(MF_THREADS, 1) k_verify_step(StepKArgs k) {
   __shared__ __attribute__((aligned(1024))) unsigned char s_q[QB];
   __shared__ StepAux<T, TH, STO> s_aux;
   const int bid = blockIdx.x;
-  if (bid < k.r_mask || (bid >= k.r_leaf && bid < k.r_end)) {
-    // ---- acceptance (regions 1 and 5)
+  if (bid < k.r_mask) {
+    // ---- attention: XCD-aware order (consecutive logical ids on one XCD)
+    const int nb = k.r_mask;
+    const int lid = (bid % 8) * (nb / 8) + bid / 8;
+    if (lid < k.ap.nwg)
+      attn_mfma_body<D>(k.at, k.ap, lid, s_kvA, s_kvB, s_q, k.ac.parents, k.ac.max_depth, (unsigned char*)&s_aux);
+  } else if (bid < k.r_acc) {
+    // ---- mask outputs, one work-group per sequence
+    const int b = bid - k.r_mask;
+    if (b < k.ac.B)
+      mask_seq(k.ac.parents, k.ac.N, k.ac.max_depth, (k.ac.N + 63) / 64, k.m_anc, k.m_depth, k.m_path, k.m_status, b,
+               s_aux.mask.spar, &s_aux.mask.worst);
+  } else if (bid < k.r_merge || (bid >= k.r_leaf && bid < k.r_end)) {
+    // ---- acceptance (regions 3 and 5)
     const bool leaf = bid >= k.r_leaf;
     SwView sw;
     sw.p01 = (float*)s_kvA;
@@ -93,22 +105,10 @@ __global__ void __launch_bounds__(MF_THREADS, 1) k_verify_step(StepKArgs k) {
     sw.rf = RF;
     const bool split = k.nacc > k.na1;
     const int per_seq = (k.ac.N + 1) * k.G * (split ? 2 : 1);
-    const AccRole role{leaf ? bid - k.r_leaf : bid, k.nacc,
+    const AccRole role{leaf ? bid - k.r_leaf : bid - k.r_acc, k.nacc,
                        leaf ? AC_REGION_LEAVES : (split ? AC_REGION_INNER : AC_REGION_ALL), leaf ? k.ng1 : 0,
                        per_seq};
     accept_body<T, MODE, true, TH, false>(k.ac, k.G, k.ws, k.cm, k.has_cm, role, s_aux.acc, sw);
-  } else if (bid < k.r_att) {
-    // ---- mask outputs, one work-group per sequence
-    const int b = bid - k.r_mask;
-    if (b < k.ac.B)
-      mask_seq(k.ac.parents, k.ac.N, k.ac.max_depth, (k.ac.N + 63) / 64, k.m_anc, k.m_depth, k.m_path, k.m_status, b,
-               s_aux.mask.spar, &s_aux.mask.worst);
-  } else if (bid < k.r_merge) {
-    // ---- attention: XCD-aware order (consecutive logical ids on one XCD)
-    const int pos = bid - k.r_att, nb = k.r_merge - k.r_att;
-    const int lid = (pos % 8) * (nb / 8) + pos / 8;
-    if (lid < k.ap.nwg)
-      attn_mfma_body<D>(k.at, k.ap, lid, s_kvA, s_kvB, s_q, k.ac.parents, k.ac.max_depth, (unsigned char*)&s_aux);
   } else if (bid < k.r_leaf) {
     // ---- merge of the attention splits
     const int pos = bid - k.r_merge, nb = k.r_leaf - k.r_merge;
@@ -271,11 +271,11 @@ extern "C" sv_status sv_verify_step(const sv_step_args* sp, void* stream) {
   const int64_t natt = up8(p0.nwg);
   const int64_t nmerge = up8((int64_t)ac.B * at.Hkv * p0.mper);
   const int64_t na2 = step_leaf_region(ac) ? na1 : 0;
-  const int64_t total = na1 + nmask + natt + nmerge + na2;
+  const int64_t total = natt + nmask + na1 + nmerge + na2;
   if (total > 0x7fffffff) return SV_ERR_UNSUPPORTED;
-  k.r_mask = (int32_t)na1;
-  k.r_att = (int32_t)(na1 + nmask);
-  k.r_merge = (int32_t)(k.r_att + natt);
+  k.r_mask = (int32_t)natt;
+  k.r_acc = (int32_t)(natt + nmask);
+  k.r_merge = (int32_t)(k.r_acc + na1);
   k.r_leaf = (int32_t)(k.r_merge + nmerge);
   k.r_end = (int32_t)total;
   k.na1 = (int32_t)na1;
