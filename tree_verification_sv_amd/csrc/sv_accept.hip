@@ -61,16 +61,9 @@ template <typename T, int MODE, bool ALIGNED, int TH>
 __global__ void __launch_bounds__(TH, 2) k_accept(sv_accept_args a, int32_t G, AccWs ws,
                                                                   sv_commit_args cm, int32_t has_cm) {
   constexpr bool STO = MODE != SV_GREEDY;
-  constexpr int RF = STO ? ac_slice<T, TH>() / Piece<T>::NK : 1;  // floats per piece row of the staging area
   __shared__ AccShared<T, TH, STO> S;
-  __shared__ __attribute__((aligned(16))) float s_w[STO ? ac_slice<T, TH>() : 4];
-  SwView sw;  // (assigned, not brace-initialised: LDS addresses are not constant initialisers)
-  sw.p01 = s_w;
-  sw.p23 = s_w + 2 * RF;
-  sw.p47 = s_w + 4 * RF;
-  sw.rf = RF;
   const AccRole role{(int)blockIdx.x, (int)gridDim.x, AC_REGION_ALL, 0, (a.N + 1) * G};
-  accept_body<T, MODE, ALIGNED, TH, true>(a, G, ws, cm, has_cm, role, S, sw);
+  accept_body<T, MODE, ALIGNED, TH, true>(a, G, ws, cm, has_cm, role, S);
 }
 
 // SV_FLAG_VALIDATE: one work-group per logits row (target rows, then draft rows in mode 1) looks
@@ -113,9 +106,11 @@ void launch_accept(int TH, dim3 grid, hipStream_t st, const sv_accept_args& a, i
                    const sv_commit_args& cm, int32_t has_cm) {
   if constexpr (M == SV_GREEDY) {
     hipLaunchKernelGGL((k_accept<T, M, AL, 512>), grid, dim3(512), 0, st, a, G, ws, cm, has_cm);
-  } else {
+  } else if constexpr (AL) {
     if (TH == 512) hipLaunchKernelGGL((k_accept<T, M, AL, 512>), grid, dim3(512), 0, st, a, G, ws, cm, has_cm);
     else hipLaunchKernelGGL((k_accept<T, M, AL, 256>), grid, dim3(256), 0, st, a, G, ws, cm, has_cm);
+  } else {  // rows off 16 bytes: always 256 threads (acc_threads)
+    hipLaunchKernelGGL((k_accept<T, M, AL, 256>), grid, dim3(256), 0, st, a, G, ws, cm, has_cm);
   }
 }
 
@@ -183,18 +178,18 @@ extern "C" sv_status sv_accept(const sv_accept_args* args, void* stream) {
   if (a.mode != SV_GREEDY && (!a.u_accept || !a.u_sample || !(a.temperature > 0.f))) return SV_ERR_INVALID_ARGUMENT;
   const WsLayout l = ws_layout(a);
   if (a.workspace_bytes < l.total || ((uintptr_t)a.workspace % 256)) return SV_ERR_INVALID_ARGUMENT;
-  const int G = groups_G(a);
+  // rows start on 16 bytes when the row pitch and the base pointers are multiples of 16
+  const size_t esz = a.logits_dtype == SV_BF16 ? 2 : 4;
+  const bool aligned = ((size_t)a.V * esz) % 16 == 0 && ((uintptr_t)a.target_logits % 16) == 0 &&
+                       (a.mode != SV_STOCHASTIC || ((uintptr_t)a.draft_logits % 16) == 0);
+  const int TH = acc_threads(a, aligned);
+  const int G = groups_G_th(a, TH);
   if (G > AC_MAXG) return SV_ERR_UNSUPPORTED;
   const int64_t blocks = num_groups(a) * G;
   if (blocks > 0x7fffffff) return SV_ERR_UNSUPPORTED;
   const AccWs ws = ws_views(a.workspace, l);
   hipStream_t st = (hipStream_t)stream;
   const dim3 grid((unsigned)blocks);
-  // rows start on 16 bytes when the row pitch and the base pointers are multiples of 16
-  const size_t esz = a.logits_dtype == SV_BF16 ? 2 : 4;
-  const bool aligned = ((size_t)a.V * esz) % 16 == 0 && ((uintptr_t)a.target_logits % 16) == 0 &&
-                       (a.mode != SV_STOCHASTIC || ((uintptr_t)a.draft_logits % 16) == 0);
-  const int TH = acc_threads(a);
 #define SV_ACC_LAUNCH(T, M, AL) launch_accept<T, M, AL>(TH, grid, st, a, G, ws, cm, has_cm)
   if (a.logits_dtype == SV_BF16) {
     if (a.mode == SV_STOCHASTIC) { if (aligned) SV_ACC_LAUNCH(uint16_t, SV_STOCHASTIC, true); else SV_ACC_LAUNCH(uint16_t, SV_STOCHASTIC, false); }

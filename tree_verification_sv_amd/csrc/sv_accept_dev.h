@@ -18,12 +18,14 @@ namespace {
 // rows, where 512 (half the work-groups, one per compute unit for the 155 KB of LDS) measured
 // faster on MI355X: 256-node trees at batch 16 (4112 rows) 3.38 -> 2.93 ms per step, at batch
 // 8 even; 60-node trees were slower with 512 at every batch (batch 64, 3904 rows: 1.11 ->
-// 1.18 ms; batch 1: 13%), and so were 768-row chains
+// 1.18 ms; batch 1: 13%), and so were 768-row chains.  Rows that do not start on 16 bytes
+// (`aligned` false) take 256 in these modes: their element-wise loads need more registers
+// than a 512-thread work-group has.
 constexpr int AC_WIDE_ROWS = 2048;
 constexpr int AC_WIDE_N = 128;
-int acc_threads(const sv_accept_args& a) {
+int acc_threads(const sv_accept_args& a, bool aligned) {
   if (a.mode == SV_GREEDY) return 512;
-  return a.N >= AC_WIDE_N && (int64_t)a.B * (a.N + 1) >= AC_WIDE_ROWS ? 512 : 256;
+  return aligned && a.N >= AC_WIDE_N && (int64_t)a.B * (a.N + 1) >= AC_WIDE_ROWS ? 512 : 256;
 }
 constexpr int AC_NWMAX = 8;                    // waves per work-group at most
 // vocabulary entries per thread: 8 pieces of 16 bytes (64 bf16 / 32 fp32 logits), so a
@@ -144,7 +146,7 @@ __device__ __forceinline__ double wave_scand(double x, int lane) {
 
 struct Red {
   float f[AC_NWMAX];
-  double d[AC_NWMAX];
+  double d[AC_NWMAX], d2[AC_NWMAX];
   int i[AC_NWMAX];
 };
 
@@ -167,6 +169,25 @@ __device__ __forceinline__ double block_sum(double x, Red& r) {
   double s = 0.0;
   for (int k = 0; k < TH / 64; ++k) s += r.d[k];
   return s;
+}
+// two block sums with one pair of barriers
+template <int TH>
+__device__ __forceinline__ void block_sum2(double& x, double& y, Red& r) {
+  x = wave_sumd(x);
+  y = wave_sumd(y);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    r.d[threadIdx.x >> 6] = x;
+    r.d2[threadIdx.x >> 6] = y;
+  }
+  __syncthreads();
+  double s = 0.0, s2 = 0.0;
+  for (int k = 0; k < TH / 64; ++k) {
+    s += r.d[k];
+    s2 += r.d2[k];
+  }
+  x = s;
+  y = s2;
 }
 template <int TH>
 __device__ __forceinline__ void block_argmax(float& v, int& i, Red& r) {
@@ -469,7 +490,7 @@ __device__ __forceinline__ void load_pieces(const T* row, int s0, int V, bool al
 // ALIGNED: every logits row starts on 16 bytes (decided on the host; a compile-time choice
 // keeps the two load paths from meeting in one register assignment)
 
-// The acceptance body's LDS, apart from the bonus staging area.
+// The acceptance body's LDS.
 template <typename T, int TH, bool STO>
 struct AccShared {
   Red red;
@@ -484,34 +505,18 @@ struct AccShared {
   int s_xc, s_claim, s_fin;  // walk finished (sticky); stochastic walk: claimed row, finisher
   int s_bad;                 // the stop row's statistics were not finite
   int s_to;                  // a bounded wait of this call expired: no commit, status 7
-};
-
-// The bonus staging area: the slice's residual weights in id order, NK piece rows of TH * E
-// floats (piece row k holds the pieces k * TH + t).  Rows 0-1, 2-3 and 4-7 may lie in three
-// separate LDS arrays (a kernel that also runs other roles can lend it their buffers).
-struct SwView {
-  float* p01;
-  float* p23;
-  float* p47;
-  int rf;  // floats per piece row
-  __device__ __forceinline__ float* row(int k) const {  // three candidates and two selects
-    float* r01 = p01 + k * rf;
-    float* r23 = p23 + (k - 2) * rf;
-    float* r47 = p47 + (k - 4) * rf;
-    return k < 2 ? r01 : (k < 4 ? r23 : r47);
-  }
-  __device__ __forceinline__ float& at(int x) const { return row(x / rf)[x % rf]; }
+  uint64_t rr[STO ? SV_MAX_N + 1 : 1];  // stochastic walk: the sequence's row results
 };
 
 // The resolution of one row slice by one work-group of a row group (see the file comment of
 // sv_accept.hip), callable from any kernel whose work-groups have TH threads.  `role` places the
-// work-group among the acceptance work-groups of its launch; S and sw are its LDS.
+// work-group among the acceptance work-groups of its launch; S is its LDS.
 // PREFETCH: the target slice is loaded before the sequence facts that say whether the row is
 // needed (its latency then overlaps theirs); otherwise after them, and only for needed rows.
 template <typename T, int MODE, bool ALIGNED, int TH, bool PREFETCH>
 __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, const AccWs& ws,
                                             const sv_commit_args& cm, int32_t has_cm, const AccRole role,
-                                            AccShared<T, TH, MODE != SV_GREEDY>& S, const SwView sw) {
+                                            AccShared<T, TH, MODE != SV_GREEDY>& S) {
   constexpr int NW = TH / 64;
   // STO: a rejection walk (modes 1 and 2); TOPK: deterministic drafts (q = point mass per child)
   constexpr bool STO = MODE != SV_GREEDY, TOPK = MODE == SV_TOPK_DRAFT;
@@ -715,14 +720,14 @@ __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, 
           }
           if (t == TH - 1) s_us = __uint_as_float(c_us);
         }
-        zp = block_sum<TH>(zp, red);  // its barriers also publish the children's values
-        zq = block_sum<TH>(zq, red);
+        block_sum2<TH>(zp, zq, red);  // its barriers also publish the children's values
         if (exchange<TH>(gslots, G, rank, ++xtag, TOPK ? 4 : 6, xv, ws.err, cancel, &s_xc, __float_as_uint(mp),
                      __float_as_uint(mq), dlo(zp), dhi(zp), dlo(zq), dhi(zq)))
           return;
         // global statistics: lane k of every wave takes member k's partials (G <= 64); the
         // butterfly reductions give every lane, wave and member the same values
-        double Zp, Zq, fp, fq;
+        double Zp, Zq, fp, fq, rq;  // rq = fq / fp: residual coefficients in this slice's units
+        double iZp, iZq;            // 1 / Zp, 1 / Zq: the tests below multiply instead of dividing
         float Mp, Mq;
         {
           const bool on = lane < G;
@@ -735,8 +740,12 @@ __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, 
           const double sq = on && need_q ? exp2((double)(mqk - Mq) * (double)l2T) : 0.0;
           Zp = wave_sumd(on ? dof(xv[k][2], xv[k][3]) * sp : 0.0);
           Zq = wave_sumd(on && need_q ? dof(xv[k][4], xv[k][5]) * sq : 0.0);
-          fp = __shfl(sp, rank) / Zp;                   // p(v) = ep(v) * fp on this slice
-          fq = need_q ? __shfl(sq, rank) / Zq : 0.0;
+          iZp = 1.0 / Zp;
+          iZq = need_q ? 1.0 / Zq : 0.0;
+          const double spr = __shfl(sp, rank), sqr = __shfl(sq, rank);
+          fp = spr * iZp;  // p(v) = ep(v) * fp on this slice
+          fq = need_q ? sqr * iZq : 0.0;
+          rq = need_q && spr > 0.0 ? (sqr * Zp) / (spr * Zq) : 0.0;
         }
         // a row without a finite positive normaliser (a NaN or +Inf logit, or no finite entry)
         // accepts no child: the walk stops here with bonus 0 and the sequence reports status 8.
@@ -771,10 +780,9 @@ __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, 
           // p(x) is known from the row statistics.
           double rem = 1.0;
           for (int j = 0; j < K; ++j) {
-            const double px = (double)expf((s_lp[j] - Mp) * invT) / Zp;
+            const double px = (double)expf((s_lp[j] - Mp) * invT) * iZp;
             const bool dup = s_lq[j] != 0.f;
-            const double cur = dup ? 0.0 : px / rem;
-            if ((double)s_u[j] < cur) { accepted = si.kids[j]; break; }
+            if (!dup && (double)s_u[j] * rem < px) { accepted = si.kids[j]; break; }  // u < px / rem
             if (!dup && rem - px > 0.0) rem -= px;  // a residual without mass (rounding only) is kept
           }
           // the bonus below zeroes the children's tokens (c != 0) and, should rounding leave
@@ -782,17 +790,17 @@ __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, 
           if (accepted < 0 && K > 0) c = 1.0;
         } else
         for (int j = 0; j < K; ++j) {
-          const double px = (double)expf((s_lp[j] - Mp) * invT) / Zp;
-          const double qx = (double)expf((s_lq[j] - Mq) * invT) / Zq;
-          const double cur = fmax(0.0, px - c * qx) / Dn;
+          const double px = (double)expf((s_lp[j] - Mp) * invT) * iZp;
+          const double qx = (double)expf((s_lq[j] - Mq) * invT) * iZq;
           const double u = (double)s_u[j];
-          if (qx > 0.0 ? (u < cur / qx) : true) { accepted = si.kids[j]; break; }
+          // u < max(0, px - c qx) / (Dn qx), with Dn > 0
+          if (qx > 0.0 ? (u * qx * Dn < fmax(0.0, px - c * qx)) : true) { accepted = si.kids[j]; break; }
           // rejection: next residual coefficient; its normaliser is needed only for a later test,
           // after the last child the bonus scan below computes it as its total
           const double cn = c + Dn;
           if (j == K - 1) { c_prev = c; c = cn; break; }
           // max(0, p - cn q) = fp * max(0, ep - kappa eq) on this slice, kappa = cn fq / fp
-          const float kappa = (float)(cn * fq / fp);
+          const float kappa = (float)(cn * rq);
           const double sl = block_sum<TH>(slice_sum(kappa), red) * fp;
           if (exchange<TH>(gslots, G, rank, ++xtag, 2, xv, ws.err, cancel, &s_xc, dlo(sl), dhi(sl))) return;
           // lane k of every wave takes member k's sum (G <= 64): one LDS read and a DPP reduction
@@ -809,46 +817,38 @@ __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, 
           // ---- bonus: smallest v whose ascending cumulative residual exceeds u * total.
           // A residual of total 0 (reachable only through rounding) falls back to the previous one.
           // Ids ascend piece by piece: piece (k, t) holds the slice-local ids (k * TH + t) * E ..
-          // + E - 1.  The weights are staged in LDS in id order (after which the exponentials in
-          // registers are dead) with their piece sums; row totals over t give the coarse
-          // cumulative sum, one work-group scan over the pieces of the row that crosses the
-          // threshold finds the piece, and one thread walks its E entries.  Piece sums are fp32
-          // over E entries; every sum above that is fp64.
+          // + E - 1.  Every thread sums its pieces' weights from the exponentials in its
+          // registers; piece-row totals give the coarse cumulative sum, one work-group scan over
+          // the pieces of the row that crosses the threshold finds the piece, and the thread that
+          // holds it walks its E entries, again from its registers.  Piece sums are fp32 over E
+          // entries; every sum above that is fp64.
           const int wv = t >> 6;
           const double us = (double)s_us;
           for (int attempt = 0; attempt < 2; ++attempt) {
             // c == 0 (no rejection at this row): the weights are p itself
-            const float kappa = TOPK || c == 0.0 ? 0.f : (float)(c * fq / fp);
-            auto stage = [&](auto residual) {
-#pragma unroll
-              for (int k = 0; k < NK; ++k) {
-                float w[E], x = 0.f;
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                  if constexpr (decltype(residual)::value) w[e] = wgt(k * E + e, kappa);
-                  else w[e] = ep[k * E + e];
-                  x += w[e];
-                }
-                float* dst = sw.row(k) + t * E;
-#pragma unroll
-                for (int e = 0; e < E; e += 4) *(float4*)(dst + e) = make_float4(w[e], w[e + 1], w[e + 2], w[e + 3]);
-                s_g[k * TH + t] = x;
-              }
-            };
-            if (kappa == 0.f) stage(std::false_type{});  // uniform branch
-            else stage(std::true_type{});
-            if (TOPK && c != 0.0) {  // every child was rejected: zero their tokens in this slice
-              __syncthreads();
-              const int x = t < K ? si.tok[si.kids[t]] - s0 : -1;
-              const bool mine = x >= 0 && x < ac_slice<T, TH>();
-              if (mine) sw.at(x) = 0.f;
-              __syncthreads();
-              if (mine) {  // its piece's sum again (children sharing a piece write the same value)
+            const float kappa = TOPK || c == 0.0 ? 0.f : (float)(c * rq);
+            // top-K drafts whose children were all rejected: the children's tokens get weight 0;
+            // bit k * E + e of zm marks such a token among this thread's entries
+            uint64_t zm = 0ull;
+            if (TOPK && c != 0.0) {
+              for (int j = 0; j < K; ++j) {
+                const int x = si.tok[si.kids[j]] - s0;
+                if (x < 0 || x >= ac_slice<T, TH>()) continue;
                 const int pc = x / E;
-                float g = 0.f;
-                for (int e = 0; e < E; ++e) g += sw.at(pc * E + e);
-                s_g[pc] = g;
+                if (pc % TH == t) zm |= 1ull << ((pc / TH) * E + x % E);
               }
+            }
+            // weight of entry i of this thread (i a compile-time index into the registers)
+            auto wz = [&](int i) -> float {
+              const float w = kappa == 0.f ? ep[i] : wgt(i, kappa);
+              return ((zm >> i) & 1ull) ? 0.f : w;
+            };
+#pragma unroll
+            for (int k = 0; k < NK; ++k) {
+              float g = 0.f;
+#pragma unroll
+              for (int e = 0; e < E; ++e) g += wz(k * E + e);
+              s_g[k * TH + t] = g;
             }
             __syncthreads();
             for (int k = wv; k < NK; k += NW) {  // wave wv totals rows wv, wv + NW, ...
@@ -907,18 +907,25 @@ __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, 
               }
               if (h != 0x7fffffff) {
                 if (t == h) {  // walk the E entries of piece (ks, h)
-                  const int p0 = (ks * TH + t) * E;  // slice-local id of its first entry
+                  float w[E];
+#pragma unroll
+                  for (int e = 0; e < E; ++e) w[e] = 0.f;
+#pragma unroll
+                  for (int k = 0; k < NK; ++k)
+#pragma unroll
+                    for (int e = 0; e < E; ++e) w[e] = k == ks ? wz(k * E + e) : w[e];
+                  const int v0 = s0 + (ks * TH + t) * E;  // id of its first entry
                   double run = excl;
                   int pick = -1, lastpos = -1;
+#pragma unroll
                   for (int e = 0; e < E; ++e) {
-                    const float w = sw.row(ks)[t * E + e];
-                    if (w > 0.f) {
-                      lastpos = s0 + p0 + e;
-                      run += (double)w;
-                      if (pick < 0 && run > lthr) pick = s0 + p0 + e;
+                    if (w[e] > 0.f) {
+                      lastpos = v0 + e;
+                      run += (double)w[e];
+                      if (pick < 0 && run > lthr) pick = v0 + e;
                     }
                   }
-                  if (pick < 0) pick = lastpos >= 0 ? lastpos : min(s0 + p0 + E, V) - 1;
+                  if (pick < 0) pick = lastpos >= 0 ? lastpos : min(v0 + E, V) - 1;
                   st_u64(&ws.res[item], res_word(-1, pick));
                 }
               } else {
@@ -926,10 +933,11 @@ __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, 
                 // (in rows up to ks when a row was found, else in the whole slice)
                 const int klim = ks >= 0 ? ks : NK - 1;
                 int lp = -1;
-                for (int k = 0; k <= klim; ++k) {
-                  const int p0 = (k * TH + t) * E;
-                  for (int e = 0; e < E; ++e) lp = sw.row(k)[t * E + e] > 0.f ? s0 + p0 + e : lp;
-                }
+#pragma unroll
+                for (int k = 0; k < NK; ++k)
+#pragma unroll
+                  for (int e = 0; e < E; ++e)
+                    lp = (k <= klim && wz(k * E + e) > 0.f) ? s0 + (k * TH + t) * E + e : lp;
                 for (int o = 32; o > 0; o >>= 1) lp = max(lp, __shfl_xor(lp, o));
                 if (t == 0) s_lpos = -1;
                 __syncthreads();
@@ -961,7 +969,7 @@ __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, 
         __syncthreads();
         uint32_t* front = &ws.frontier[b];
         uint64_t* rr = ws.res + (int64_t)b * (N + 1);
-        uint64_t* s_rr = (uint64_t*)sw.row(0);  // the sequence's row results (the bonus staging area is free)
+        uint64_t* s_rr = S.rr;  // the sequence's row results
         if (t == 0) {
           s_fin = 0;
           if (incr) {
@@ -1206,7 +1214,7 @@ int groups_G_th(const sv_accept_args& a, int TH) {
   const int G = (a.V + slice - 1) / slice;
   return G < 1 ? 1 : G;
 }
-int groups_G(const sv_accept_args& a) { return groups_G_th(a, acc_threads(a)); }
+int groups_G(const sv_accept_args& a, bool aligned) { return groups_G_th(a, acc_threads(a, aligned)); }
 // one group per row, rounded up to a whole number of groups per XCD
 int64_t num_groups(const sv_accept_args& a) { return ((int64_t)a.B * (a.N + 1) + 7) / 8 * 8; }
 
@@ -1230,7 +1238,8 @@ WsLayout ws_layout_g(const sv_accept_args& a, int G, int regions) {
   l.total = o;
   return l;
 }
-WsLayout ws_layout(const sv_accept_args& a) { return ws_layout_g(a, groups_G(a), 1); }
+// sized for the larger of the two group sizes (the row alignment is known only at the launch)
+WsLayout ws_layout(const sv_accept_args& a) { return ws_layout_g(a, groups_G(a, false), 1); }
 AccWs ws_views(void* workspace, const WsLayout& l) {
   char* base = (char*)workspace;
   AccWs ws;

@@ -28,8 +28,8 @@
 //      it stops there, so these run last and exit at once once the walk is done
 //      (stochastic and top-K walks over wide trees; otherwise region 3 takes
 //      every row).  They wait only for rows of region 3.
-// The acceptance's bonus staging area is laid over the attention's tile and query
-// buffers (a work-group runs one role), 155 KB of LDS in all.
+// The roles share the LDS (a work-group runs one role): the attention's tile and query
+// buffers, and one union of the other roles' state.
 #include "sv_accept_dev.h"
 #include "sv_attn_dev.h"
 
@@ -75,12 +75,9 @@ __global__ void __launch_bounds__(MF_THREADS, 1) k_verify_step(StepKArgs k) {
   constexpr int TH = MF_THREADS;
   using T = uint16_t;
   using TL = Tile<D>;
-  constexpr int RF = ac_slice<T, TH>() / Piece<T>::NK;  // floats per piece row of the bonus staging area
-  constexpr int KVB = TL::BUF > 2 * RF * 4 ? TL::BUF : 2 * RF * 4;
-  constexpr int QB = TL::QROWS * TL::ROWB > 4 * RF * 4 ? TL::QROWS * TL::ROWB : 4 * RF * 4;
-  __shared__ __attribute__((aligned(1024))) unsigned char s_kvA[KVB];
-  __shared__ __attribute__((aligned(1024))) unsigned char s_kvB[KVB];
-  __shared__ __attribute__((aligned(1024))) unsigned char s_q[QB];
+  __shared__ __attribute__((aligned(1024))) unsigned char s_kvA[TL::BUF];
+  __shared__ __attribute__((aligned(1024))) unsigned char s_kvB[TL::BUF];
+  __shared__ __attribute__((aligned(1024))) unsigned char s_q[TL::QROWS * TL::ROWB];
   __shared__ StepAux<T, TH, STO> s_aux;
   const int bid = blockIdx.x;
   if (bid < k.r_mask) {
@@ -98,17 +95,12 @@ __global__ void __launch_bounds__(MF_THREADS, 1) k_verify_step(StepKArgs k) {
   } else if (bid < k.r_merge || (bid >= k.r_leaf && bid < k.r_end)) {
     // ---- acceptance (regions 3 and 5)
     const bool leaf = bid >= k.r_leaf;
-    SwView sw;
-    sw.p01 = (float*)s_kvA;
-    sw.p23 = (float*)s_kvB;
-    sw.p47 = (float*)s_q;
-    sw.rf = RF;
     const bool split = k.nacc > k.na1;
     const int per_seq = (k.ac.N + 1) * k.G * (split ? 2 : 1);
     const AccRole role{leaf ? bid - k.r_leaf : bid - k.r_acc, k.nacc,
                        leaf ? AC_REGION_LEAVES : (split ? AC_REGION_INNER : AC_REGION_ALL), leaf ? k.ng1 : 0,
                        per_seq};
-    accept_body<T, MODE, true, TH, false>(k.ac, k.G, k.ws, k.cm, k.has_cm, role, s_aux.acc, sw);
+    accept_body<T, MODE, true, TH, false>(k.ac, k.G, k.ws, k.cm, k.has_cm, role, s_aux.acc);
   } else if (bid < k.r_leaf) {
     // ---- merge of the attention splits
     const int pos = bid - k.r_merge, nb = k.r_leaf - k.r_merge;
