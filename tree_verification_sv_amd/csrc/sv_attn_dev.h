@@ -14,6 +14,8 @@
 #include <float.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "sv_mask_dev.h"
 
 namespace {
@@ -80,6 +82,7 @@ constexpr int MF_WAVES = 8;                // waves of the MFMA kernel (two per 
 constexpr int MF_THREADS = 64 * MF_WAVES;
 constexpr int MF_QB = 1;                   // 32-row query blocks per wave
 constexpr int KT = 64;  // keys per tile
+constexpr float AT_LAZY = 8.f;  // log2 of the largest weight before the reference maximum moves
 
 struct AttnPlan {
   int32_t G, M, QB, QT, qtiles, nsplit, chunk, ntt, W, cap;
@@ -406,10 +409,14 @@ __device__ __forceinline__ void attn_mfma_body(const sv_attn_args& a, const Attn
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[qb][kb][r]);
       mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mnew = fmaxf(mrun[qb], mt);  // running maximum of the unscaled scores
+      // The reference maximum moves only when a score exceeds it by more than 2^AT_LAZY in the
+      // weights (or at the first visible score): the weights then stay below 2^AT_LAZY, exact in
+      // bf16's range and in the fp32 sums, and most tiles skip the rescale of the accumulators.
+      const bool up = mt * p.cscale > mrun[qb] * p.cscale + AT_LAZY;  // false while mt is -inf
+      const float mnew = up ? mt : mrun[qb];
       const float ms = mnew == -INFINITY ? 0.f : mnew * p.cscale;  // nothing visible yet: weights stay 0
-      alpha[qb] = __builtin_amdgcn_exp2f(mrun[qb] * p.cscale - ms);
-      moved |= mnew != mrun[qb];
+      alpha[qb] = up ? __builtin_amdgcn_exp2f(mrun[qb] * p.cscale - ms) : 1.f;
+      moved |= up;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
