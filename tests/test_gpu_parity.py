@@ -233,3 +233,14 @@ def test_chi_square_gpu(shape):
     p0 /= p0.sum()
     chi = stats.chisquare(counts, p0 * counts.sum())
     assert chi.pvalue > 0.01, chi
+
+
+@pytest.mark.parametrize("B,N,V", [(20, 32, 3001), (16, 40, 40000), (24, 24, 300)])
+def test_greedy_row_streamer(B, N, V):
+    """Greedy batches of at least 512 rows: one work-group streams each whole row (rows off 16
+    bytes, several slices per row, and a vocabulary smaller than one slice)."""
+    w = W.config(3, B=B, N=N, V=V, L=(16, 80))
+    assert w.B * (w.N + 1) >= 512 and w.mode == "greedy"
+    print(f"[gpu] greedy streamer B={w.B} N={w.N} V={w.V}", flush=True)
+    r = run_step(w, ("mask", "accept"))
+    compare_accept(r["acc"], oracle.accept(w), allow_flagged=False)

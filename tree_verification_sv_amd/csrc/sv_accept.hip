@@ -22,7 +22,8 @@
 // Work decomposition.  A group of G work-groups resolves one row; each of TH
 // threads (512 greedy; 256, or 512 in large batches, for the walk modes) owns a
 // slice of TH * 128 bytes of the
-// vocabulary.  Thread t owns the 16-byte pieces k * TH + t (k = 0 .. 7) of its
+// vocabulary (greedy batches of 512 rows or more: G = 1, and the work-group
+// streams the whole row slice by slice with the next slice's loads in flight).  Thread t owns the 16-byte pieces k * TH + t (k = 0 .. 7) of its
 // slice, so every load instruction of a wave reads 1 KB of consecutive logits.
 // The exponentials are computed once into registers; each later pass over the row (a
 // rejection's residual sum, the bonus scan) is a few register operations per
@@ -183,7 +184,7 @@ extern "C" sv_status sv_accept(const sv_accept_args* args, void* stream) {
   const bool aligned = ((size_t)a.V * esz) % 16 == 0 && ((uintptr_t)a.target_logits % 16) == 0 &&
                        (a.mode != SV_STOCHASTIC || ((uintptr_t)a.draft_logits % 16) == 0);
   const int TH = acc_threads(a, aligned);
-  const int G = groups_G_th(a, TH);
+  const int G = launch_G(a, TH);
   if (G > AC_MAXG) return SV_ERR_UNSUPPORTED;
   const int64_t blocks = num_groups(a) * G;
   if (blocks > 0x7fffffff) return SV_ERR_UNSUPPORTED;

@@ -486,6 +486,34 @@ __device__ __forceinline__ void load_pieces(const T* row, int s0, int V, bool al
   }
 }
 
+// This thread's argmax over a whole logits row (lowest id on ties), one TH-thread slice at a time
+// with the next slice's loads in flight; a thread visits its entries in ascending id.
+template <typename T, int TH>
+__device__ __forceinline__ void argmax_row(const T* row, int V, bool aligned, int t, float& best, int& arg) {
+  constexpr int E = Piece<T>::E, NK = Piece<T>::NK;
+  const int ns = (V + ac_slice<T, TH>() - 1) / ac_slice<T, TH>();
+  uint4 r0[NK], r1[NK];
+  auto consume = [&](const uint4 (&raw)[NK], int gs) {
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      float x[E];
+      unpack16<T>(raw[k], x);
+      const int v = piece_v<T, TH>(gs * ac_slice<T, TH>(), k, t);
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (v + e < V && x[e] > best) { best = x[e]; arg = v + e; }
+    }
+  };
+  load_pieces<T, TH>(row, 0, V, aligned, t, r0);
+  for (int gs = 0; gs < ns; gs += 2) {
+    if (gs + 1 < ns) load_pieces<T, TH>(row, (gs + 1) * ac_slice<T, TH>(), V, aligned, t, r1);
+    consume(r0, gs);
+    if (gs + 1 >= ns) break;
+    if (gs + 2 < ns) load_pieces<T, TH>(row, (gs + 2) * ac_slice<T, TH>(), V, aligned, t, r0);
+    consume(r1, gs + 1);
+  }
+}
+
 // ---------------------------------------------------------------- the kernel
 // ALIGNED: every logits row starts on 16 bytes (decided on the host; a compile-time choice
 // keeps the two load paths from meeting in one register assignment)
@@ -601,7 +629,16 @@ __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, 
       row_kids<TH>(N, r, si);
       int done_by_me = 0;  // this work-group wrote the row result
 
-      if constexpr (MODE == SV_GREEDY) {
+      if (MODE == SV_GREEDY && G == 1) {
+        // greedy, one work-group per row (large batches): the whole row streams through the
+        // work-group one slice at a time with the next slice's loads in flight; no exchange
+        float best = -FLT_MAX;
+        int arg = 0x7fffffff;
+        argmax_row<T, TH>(prow, V, aligned, t, best, arg);
+        block_argmax<TH>(best, arg, red);
+        if (t == 0) st_u64(&ws.res[item], res_word(-1, arg));
+        done_by_me = 1;
+      } else if constexpr (MODE == SV_GREEDY) {
         float best = -FLT_MAX;
         int arg = 0x7fffffff;
         {
@@ -1107,26 +1144,7 @@ __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, 
               const T* srow = (const T*)a.target_logits + ((int64_t)b * (N + 1) + stop_row) * V;
               float best = -FLT_MAX;
               int arg = 0x7fffffff;
-              uint4 r0[NK], r1[NK];
-              auto consume = [&](const uint4 (&raw)[NK], int gs) {
-#pragma unroll
-                for (int k = 0; k < NK; ++k) {
-                  float x[E];
-                  unpack16<T>(raw[k], x);
-                  const int v = piece_v<T, TH>(gs * ac_slice<T, TH>(), k, t);
-#pragma unroll
-                  for (int e = 0; e < E; ++e)
-                    if (v + e < V && x[e] > best) { best = x[e]; arg = v + e; }
-                }
-              };
-              load_pieces<T, TH>(srow, 0, V, aligned, t, r0);
-              for (int gs = 0; gs < G; gs += 2) {
-                if (gs + 1 < G) load_pieces<T, TH>(srow, (gs + 1) * ac_slice<T, TH>(), V, aligned, t, r1);
-                consume(r0, gs);
-                if (gs + 1 >= G) break;
-                if (gs + 2 < G) load_pieces<T, TH>(srow, (gs + 2) * ac_slice<T, TH>(), V, aligned, t, r0);
-                consume(r1, gs + 1);
-              }
+              argmax_row<T, TH>(srow, V, aligned, t, best, arg);
               block_argmax<TH>(best, arg, red);
               bonus = arg;
             }
@@ -1215,6 +1233,14 @@ int groups_G_th(const sv_accept_args& a, int TH) {
   return G < 1 ? 1 : G;
 }
 int groups_G(const sv_accept_args& a, bool aligned) { return groups_G_th(a, acc_threads(a, aligned)); }
+// Greedy batches of at least AC_STREAM_ROWS rows resolve each row with one work-group that streams
+// the whole row (no exchange, a quarter of the work-groups to dispatch); smaller batches split a
+// row over a group of G work-groups for parallelism.
+constexpr int64_t AC_STREAM_ROWS = 512;
+int launch_G(const sv_accept_args& a, int TH) {
+  if (a.mode == SV_GREEDY && (int64_t)a.B * (a.N + 1) >= AC_STREAM_ROWS) return 1;
+  return groups_G_th(a, TH);
+}
 // one group per row, rounded up to a whole number of groups per XCD
 int64_t num_groups(const sv_accept_args& a) { return ((int64_t)a.B * (a.N + 1) + 7) / 8 * 8; }
 

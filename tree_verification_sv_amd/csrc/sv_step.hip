@@ -161,7 +161,7 @@ AttnPlan step_plan(const sv_attn_args& a) {
   return p;
 }
 
-int step_G(const sv_accept_args& a) { return groups_G_th(a, MF_THREADS); }
+int step_G(const sv_accept_args& a) { return launch_G(a, MF_THREADS); }
 bool step_leaf_region(const sv_accept_args& a) { return a.mode != SV_GREEDY && a.N > 2 * a.max_depth; }
 
 struct StepLayout {
