@@ -113,8 +113,12 @@ struct Tile {
   static constexpr int TBYTES = KT * ROWB;            // one tensor of the tile
   static constexpr int BUF = 2 * TBYTES;              // K and V
   static constexpr int QROWS = 32 * MF_QB * MF_WAVES;  // query rows per work-group
+  // Any 16 consecutive rows (8 row pairs for D = 64) take distinct slots, so the 16-lane groups
+  // of a 16-byte fragment read hit every bank once; and each aligned group of 4 rows differs in
+  // bits 2-3 of the slot, so the 32-lane groups of an 8-byte transposing V read (4 rows x 4
+  // chunks x 2 halves) do too.
   __device__ static __forceinline__ int swz(int r) {
-    return CPR == 16 ? (((r << 1) & 14) | ((r >> 3) & 1)) : ((r & 6) | ((r >> 3) & 1));
+    return CPR == 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
   }
 };
 
