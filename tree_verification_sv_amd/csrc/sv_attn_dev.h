@@ -76,6 +76,17 @@ __device__ __forceinline__ void tr_wait(uint2 (&lo)[2], uint2 (&hi)[2]) {
   asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(lo[0]), "+v"(hi[0]), "+v"(lo[1]), "+v"(hi[1]) : "n"(N) : "memory");
 }
 
+// x combined with the same lane of the other 32-lane half of the wave, through one
+// v_permlane32_swap (no LDS round trip): every lane gets op(x[l], x[l ^ 32])
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ------------------------------------------------------------------ MFMA attention
 constexpr uint32_t AT_SPIN_LIMIT = 1u << 22;  // bounded wait of a merge work-group of the one-launch step (polls)
 constexpr int MF_WAVES = 8;                // waves of the MFMA kernel (two per SIMD)
@@ -407,12 +418,15 @@ __device__ __forceinline__ void attn_mfma_body(const sv_attn_args& a, const Attn
             if (((word >> (8 * (r >> 2) + (r & 3))) & 1u) == 0) sacc[qb][kb][r] = -INFINITY;
           }
       }
-      float mt = sacc[qb][0][0];
+      // maximum over the lane's 32 scores in four independent chains, then across the two
+      // halves of the wave (lanes l and l + 32 hold the two key halves of query column l)
+      float mc[4] = {sacc[qb][0][0], sacc[qb][0][1], sacc[qb][0][2], sacc[qb][0][3]};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[qb][kb][r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+        for (int r = 0; r < 16; ++r)
+          if (kb || r >= 4) mc[r & 3] = fmaxf(mc[r & 3], sacc[qb][kb][r]);
+      float mt = halves_max(fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3])));
       // The reference maximum moves only when a score exceeds it by more than 2^AT_LAZY in the
       // weights (or at the first visible score): the weights then stay below 2^AT_LAZY, exact in
       // bf16's range and in the fp32 sums, and most tiles skip the rescale of the accumulators.
@@ -427,20 +441,19 @@ __device__ __forceinline__ void attn_mfma_body(const sv_attn_args& a, const Attn
         for (int r = 0; r < 16; ++r)
           pf[qb][kb][r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][r], p.cscale, -ms));
       // the row sum of the bf16 weights the P V product uses: two per dot instruction
-      float psum0 = 0.f, psum1 = 0.f;
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
       const sv_bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2) {
           const sv_bf16x8 v = pf[qb][kb][t2];
-          psum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one2, psum0, false);
-          psum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one2, psum1, false);
-          psum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one2, psum0, false);
-          psum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one2, psum1, false);
+          ps[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one2, ps[0], false);
+          ps[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one2, ps[1], false);
+          ps[2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one2, ps[2], false);
+          ps[3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one2, ps[3], false);
         }
-      float psum = psum0 + psum1;
-      psum += __shfl_xor(psum, 32);
+      const float psum = halves_sum((ps[0] + ps[1]) + (ps[2] + ps[3]));
       lrun[qb] = lrun[qb] * alpha[qb] + psum;
       mrun[qb] = mnew;
       __builtin_amdgcn_sched_barrier(0);  // one query block at a time (register pressure)
