@@ -39,6 +39,10 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_TFLOPS = 2500.0   # dense bf16 MFMA peak of MI355X
 VALU_FP32_TFLOPS = 157.3    # fp32 vector peak of MI355X
 MALL_BYTES = 256 * 2**20
+# batches up to this many logits rows run the step as one sv_verify_step launch (MI355X:
+# eagle-static-8b, 61 rows, 33 vs 43 us; draft-target-chain-8b, 768 rows, 427 vs 371 us;
+# batched-paged-70b, 2112 rows, 608 vs 580 us)
+ONE_LAUNCH_MAX_ROWS = 256
 
 
 def algorithmic_bytes(w, acc):
@@ -372,6 +376,11 @@ def main():
     ap.add_argument("--separate-calls", action="store_true",
                     help="run the step as separate library calls (mask, attention, acceptance, commit) instead "
                          "of one sv_verify_step launch")
+    ap.add_argument("--one-launch", action="store_true",
+                    help="run the step as one sv_verify_step launch whatever the batch (default: one launch for "
+                         f"batches of at most {ONE_LAUNCH_MAX_ROWS} logits rows, where the separate calls' launch "
+                         "gaps dominate; the separate calls above that, where the two branches filling the device "
+                         "side by side measured faster on MI355X)")
     ap.add_argument("--reps", type=int, default=5, help="timed repetitions of the K-step graph (median reported)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--acceptance", choices=["greedy", "stochastic", "topk", "threshold"], default=None,
@@ -425,7 +434,8 @@ def main():
         for s_ in steps:
             s_.mask_free_accept(True)
     one = False
-    if not args.separate_calls and not mask_free:
+    rows = w0.B * (w0.N + 1)
+    if not args.separate_calls and not mask_free and (args.one_launch or rows <= ONE_LAUNCH_MAX_ROWS):
         one = all([s_.one_launch(True) for s_ in steps])
         if not one:
             print("[bench] sv_verify_step does not support this workload; timing the separate calls",
