@@ -204,10 +204,18 @@ __device__ __forceinline__ void block_argmax(float& v, int& i, Red& r) {
 // ---------------------------------------------------------------- cross-work-group messages
 // Values crossing work-groups are written with relaxed device-scope atomic
 // stores and read with relaxed device-scope atomic loads (both coherent at
-// device scope).  Exchange words carry their tag in the same 64-bit word as
-// the payload.  Row results are published before the per-sequence counter:
-// the writer waits for its stores to complete (s_waitcnt) and then bumps the
-// counter.  Neither order needs a cache write-back or invalidation.
+// device scope: on gfx950 they bypass the per-XCD caches that are not
+// coherent with each other).  Exchange words carry their tag in the same
+// 64-bit word as the payload.  Row results are published before the
+// per-sequence counter: the writer waits for its stores to complete
+// (s_waitcnt) and then bumps the counter; the reader issues its loads of the
+// results only after the counter value it depends on has returned.  Neither
+// order needs a cache write-back or invalidation, because no plain
+// (non-atomic) store carries data between work-groups.  Device-scope
+// release/acquire on these counters was measured and rejected: a release
+// writes back the XCD's whole L2 and an acquire invalidates it, which evicts
+// the logits rows other work-groups are streaming (the 60-node bf16 tree step
+// went from 33 to 60 us, the 64x32 greedy acceptance from 84 to 188 us).
 #define AGENT __HIP_MEMORY_SCOPE_AGENT
 __device__ __forceinline__ void st_u32(uint32_t* p, uint32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, AGENT); }
 __device__ __forceinline__ void st_u64(uint64_t* p, uint64_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, AGENT); }
