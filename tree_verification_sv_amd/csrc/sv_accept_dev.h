@@ -594,13 +594,15 @@ __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, 
     if (t == 0) {
       const int bb = (int)(item / (N + 1)), rr = (int)(item % (N + 1));
       const int pr = rr > 0 ? a.parents[(int64_t)bb * N + rr - 1] : -2;
+      uint32_t cv = ld_u32(&ws.cancel[bb]);  // in flight together with the parent's load
       int gone = 0;
       for (uint32_t spins = 0; spins < AC_SPIN_LIMIT; ++spins) {
-        if (ld_u32(&ws.cancel[bb]) != 0u) { gone = 1; break; }
+        if (cv != 0u) { gone = 1; break; }
         if (pr < -1 || pr >= N) break;  // not a usable node: the facts below say so
         const uint64_t v = ld_u64(&ws.res[(int64_t)bb * (N + 1) + pr + 1]);
         if (res_ready(v)) { gone = res_child(v) != rr - 1; break; }
         __builtin_amdgcn_s_sleep(2);
+        cv = ld_u32(&ws.cancel[bb]);
       }
       s_xc = gone;
     }

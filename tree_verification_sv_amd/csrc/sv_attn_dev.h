@@ -87,6 +87,17 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Split partials that a merge work-group of the same launch reads are written and read with
+// relaxed device-scope atomic 64-bit accesses (coherent across the XCDs' caches); the writer
+// waits for its stores to complete before it counts in, and the merge loads them only after
+// it has seen every split's count.  No cache write-back or invalidation is needed.
+__device__ __forceinline__ void st_dev64(void* p, uint64_t v) {
+  __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev64(const void* p) {
+  return __hip_atomic_load((uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ------------------------------------------------------------------ MFMA attention
 constexpr uint32_t AT_SPIN_LIMIT = 1u << 22;  // bounded wait of a merge work-group of the one-launch step (polls)
 constexpr int MF_WAVES = 8;                // waves of the MFMA kernel (two per SIMD)
@@ -537,8 +548,13 @@ __device__ __forceinline__ void attn_mfma_body(const sv_attn_args& a, const Attn
     const int ql = w * 32 * QB + qb * 32 + lq;
     const int m = qtile * p.QT + ql;
     const float inv = lrun[qb] > 0.f ? 1.f / lrun[qb] : 0.f;
-    if (p.nsplit > 1 && hf == 0 && m < p.M)
-      *(float2*)(p.mlpart + (pidx * p.QT + ql) * 2) = make_float2(mrun[qb] * p.cscale, lrun[qb]);
+    if (p.nsplit > 1 && hf == 0 && m < p.M) {
+      float* dst = p.mlpart + (pidx * p.QT + ql) * 2;
+      if (p.arrive)  // read by a merge work-group of this launch
+        st_dev64(dst, ((uint64_t)__float_as_uint(lrun[qb]) << 32) | __float_as_uint(mrun[qb] * p.cscale));
+      else
+        *(float2*)dst = make_float2(mrun[qb] * p.cscale, lrun[qb]);
+    }
     const int sw = TL::swz(lq);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -563,13 +579,21 @@ __device__ __forceinline__ void attn_mfma_body(const sv_attn_args& a, const Attn
     if (m < p.M) {
       uint16_t* orow = p.nsplit == 1 ? (uint16_t*)a.out + (((int64_t)b * N + m / G) * Hq + g * G + m % G) * D
                                      : p.opart + (pidx * p.QT + ql) * D;
-      *(uint4*)(orow + ch * 8) = v;
+      if (p.nsplit > 1 && p.arrive) {
+        st_dev64(orow + ch * 8, ((uint64_t)v.y << 32) | v.x);
+        st_dev64(orow + ch * 8 + 4, ((uint64_t)v.w << 32) | v.z);
+      } else {
+        *(uint4*)(orow + ch * 8) = v;
+      }
     }
   }
   }  // active
   if (p.arrive && p.nsplit > 1) {
-    __syncthreads();  // every wave's partial stores precede the release below
-    if (t == 0) __hip_atomic_fetch_add(&p.arrive[unit], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
+    asm volatile("" ::: "memory");
+    __syncthreads();  // ... and every wave's, before the split counts in
+    if (t == 0) __hip_atomic_fetch_add(&p.arrive[unit], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -600,7 +624,6 @@ __device__ __forceinline__ void step_merge(const sv_attn_args& a, const AttnPlan
         __builtin_amdgcn_s_sleep(1);
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the splits' partials are visible after their release
     s_late = late;
   }
   __syncthreads();
@@ -615,12 +638,14 @@ __device__ __forceinline__ void step_merge(const sv_attn_args& a, const AttnPlan
     const int unit = pair * p.qtiles + mm / p.QT, ql = mm % p.QT;
     // weights: thread c of the row takes splits c, c + TPR, ...; max and sum over the row's lanes
     float mx = -INFINITY;
-    for (int s = c; s < ns; s += TPR) mx = fmaxf(mx, p.mlpart[(((int64_t)unit * ns + s) * p.QT + ql) * 2]);
+    for (int s = c; s < ns; s += TPR)
+      mx = fmaxf(mx, __uint_as_float((uint32_t)ld_dev64(p.mlpart + (((int64_t)unit * ns + s) * p.QT + ql) * 2)));
 #pragma unroll
     for (int o = TPR / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
     float lsum = 0.f;
     for (int s = c; s < ns; s += TPR) {
-      const float2 ml = *(const float2*)(p.mlpart + (((int64_t)unit * ns + s) * p.QT + ql) * 2);
+      const uint64_t mlw = ld_dev64(p.mlpart + (((int64_t)unit * ns + s) * p.QT + ql) * 2);
+      const float2 ml = make_float2(__uint_as_float((uint32_t)mlw), __uint_as_float((uint32_t)(mlw >> 32)));
       const float f = ml.x == -INFINITY ? 0.f : exp2f(ml.x - mx) * ml.y;
       s_f[lr * 64 + s] = f;
       lsum += f;
@@ -636,7 +661,9 @@ __device__ __forceinline__ void step_merge(const sv_attn_args& a, const AttnPlan
 #pragma unroll
       for (int k = 0; k < SB; ++k) {
         const int s = min(s0 + k, ns - 1);
-        part[k] = *(const uint4*)(p.opart + (((int64_t)unit * ns + s) * p.QT + ql) * D + c * 8);
+        const uint16_t* src = p.opart + (((int64_t)unit * ns + s) * p.QT + ql) * D + c * 8;
+        const uint64_t lo = ld_dev64(src), hi = ld_dev64(src + 4);
+        part[k] = make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
       }
 #pragma unroll
       for (int k = 0; k < SB; ++k) {

@@ -108,15 +108,12 @@ __global__ void __launch_bounds__(MF_THREADS, 1) k_verify_step(StepKArgs k) {
     if (mid < k.ac.B * k.at.Hkv * k.ap.mper) step_merge<D, TH>(k.at, k.ap, mid, s_aux.mrg);
   }
   // ---- the last work-group of the launch leaves the attention's arrival counters zeroed.  The
-  // merge work-groups read those counters: their exit counts are releases (the count is one
-  // release sequence), and the last work-group acquires before it clears.
+  // merge work-groups read those counters before they count out (their polls have returned), so
+  // once every work-group has counted out no read of them is left.
   __syncthreads();
   if (threadIdx.x == 0) {
-    const bool merge = bid >= k.r_merge && bid < k.r_leaf;
-    const uint32_t o = merge ? __hip_atomic_fetch_add(k.exit_count, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT)
-                             : __hip_atomic_fetch_add(k.exit_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t o = __hip_atomic_fetch_add(k.exit_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (o + 1 == gridDim.x) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       for (int u = 0; u < k.ap.nunits && k.ap.nsplit > 1; ++u)
         __hip_atomic_store(&k.ap.arrive[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(k.exit_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
