@@ -53,13 +53,12 @@ def _run(w, one, fused=True, mask_outputs=True):
 
 def _counters_zero(w, ws):
     """The counters of the step's workspace are zero: the acceptance part at its start (exit
-    counters, row words, exchange slots; one or two regions of row groups) and the attention's
+    counters, row words, exchange slots) and the attention's
     arrival and exit counters at its end (the split partials between them hold data)."""
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
     B, N = w.B, w.N
     G = max(1, -(-w.V // (512 * 64)))
-    regions = 2 if (w.mode != "greedy" and N > 2 * w.max_depth) else 1
-    NG = (B * (N + 1) + 7) // 8 * 8 * regions
+    NG = (B * (N + 1) + 7) // 8 * 8
     o = up(NG * 4)
     for n in (B * 4, 8, B * (N + 1) * 8, B * 4, B * 4, B * 4, NG * G * 2 * 64):
         o = up(o + n)
@@ -74,8 +73,17 @@ def _d64(B=3, N=40, V=4096, L=200, mode="stochastic"):
                             logit_sigma=3.0, token_rule="sample")
 
 
+def _p_eq_q(w):
+    """Draft logits equal to the target's: every first child is accepted, so the walks of wide
+    trees stop at rows without children (drawn by the walker's work-group)."""
+    w.draft_logits = w.target_logits.copy()
+    return w
+
+
 CASES = [
     ("eagle-static-8b", lambda: W.config(2)),
+    ("eagle-static-8b-b3-p==q", lambda: _p_eq_q(W.config(2, B=3, L=100, V=12000))),
+    ("outcome-tree-8b-small-p==q", lambda: _p_eq_q(W.config(5, B=2, L=300, V=2048))),
     ("eagle-static-8b-topk", lambda: W.config(2, mode="topk")),
     ("eagle-static-8b-b3-short", lambda: W.config(2, B=3, L=100, V=12000)),
     ("batched-paged-70b-small", lambda: W.config(3, B=6, L=(16, 300), V=8192)),

@@ -21,19 +21,22 @@
 //
 // Work decomposition.  A group of G work-groups resolves one row; each of TH
 // threads (512 greedy; 256, or 512 in large batches, for the walk modes) owns a
-// slice of TH * 128 bytes of the
-// vocabulary (greedy batches of 512 rows or more: G = 1, and the work-group
-// streams the whole row slice by slice with the next slice's loads in flight).  Thread t owns the 16-byte pieces k * TH + t (k = 0 .. 7) of its
-// slice, so every load instruction of a wave reads 1 KB of consecutive logits.
+// slice of TH * 128 bytes of the vocabulary (greedy batches of 512 rows or
+// more: G = 1, and the work-group streams the whole row slice by slice with the
+// next slice's loads in flight).  Thread t owns the 16-byte pieces k * TH + t
+// (k = 0 .. 7) of its slice, so every load instruction of a wave reads 1 KB of
+// consecutive logits.
 // The exponentials are computed once into registers; each later pass over the row (a
 // rejection's residual sum, the bonus scan) is a few register operations per
 // entry.  Members of a group trade per-slice partials through tagged 64-bit
 // words (tag and payload in one atomic word, so a reader that sees the tag
 // also sees the value).  Greedy rows need one pass (slice max / argmax, lowest
-// id on ties).  Rows resolved: greedy -- the root row and rows with a usable
-// child (a leaf stop row's argmax is taken by the walker); stochastic -- the
-// root row and the rows of all usable nodes (leaf rows only read the target
-// logits); the work-groups of other rows exit at once.
+// id on ties).  Rows resolved: the root row and the rows with a usable child
+// (a walk that stops at a row without one needs only that row's argmax or its
+// target distribution, which the walker's work-group takes itself); stochastic
+// chains and narrow trees also resolve the rows of all other usable nodes (leaf
+// rows read the target logits only).  The work-groups of other rows exit at
+// once.
 //
 // The walk.  Greedy, and stochastic chains or narrow trees (N <= 2 max_depth,
 // where nearly every row is on the path): the group that completes the last
@@ -58,13 +61,16 @@
 
 namespace {
 
-template <typename T, int MODE, bool ALIGNED, int TH>
+// PRE: fetch the target slice before the sequence facts (stochastic chains and narrow trees,
+// which resolve nearly every row); without it, wide trees resolve only the rows with a usable
+// child and the walker draws a stop row without children itself
+template <typename T, int MODE, bool ALIGNED, int TH, bool PRE>
 __global__ void __launch_bounds__(TH, 2) k_accept(sv_accept_args a, int32_t G, AccWs ws,
                                                                   sv_commit_args cm, int32_t has_cm) {
   constexpr bool STO = MODE != SV_GREEDY;
   __shared__ AccShared<T, TH, STO> S;
-  const AccRole role{(int)blockIdx.x, (int)gridDim.x, AC_REGION_ALL, 0, (a.N + 1) * G};
-  accept_body<T, MODE, ALIGNED, TH, true>(a, G, ws, cm, has_cm, role, S);
+  const AccRole role{(int)blockIdx.x, (int)gridDim.x, (a.N + 1) * G};
+  accept_body<T, MODE, ALIGNED, TH, PRE>(a, G, ws, cm, has_cm, role, S);
 }
 
 // SV_FLAG_VALIDATE: one work-group per logits row (target rows, then draft rows in mode 1) looks
@@ -105,13 +111,18 @@ __global__ void __launch_bounds__(256) k_nonfinite_rows(const T* __restrict__ ta
 template <typename T, int M, bool AL>
 void launch_accept(int TH, dim3 grid, hipStream_t st, const sv_accept_args& a, int G, const AccWs& ws,
                    const sv_commit_args& cm, int32_t has_cm) {
+  // the walk modes prefetch unless the walk advances as rows resolve (wide trees: only rows with a
+  // usable child are resolved, and 512-thread groups are only taken for wide trees)
+  const bool pre = !(a.N > 2 * a.max_depth);
   if constexpr (M == SV_GREEDY) {
-    hipLaunchKernelGGL((k_accept<T, M, AL, 512>), grid, dim3(512), 0, st, a, G, ws, cm, has_cm);
+    hipLaunchKernelGGL((k_accept<T, M, AL, 512, true>), grid, dim3(512), 0, st, a, G, ws, cm, has_cm);
   } else if constexpr (AL) {
-    if (TH == 512) hipLaunchKernelGGL((k_accept<T, M, AL, 512>), grid, dim3(512), 0, st, a, G, ws, cm, has_cm);
-    else hipLaunchKernelGGL((k_accept<T, M, AL, 256>), grid, dim3(256), 0, st, a, G, ws, cm, has_cm);
+    if (TH == 512) hipLaunchKernelGGL((k_accept<T, M, AL, 512, false>), grid, dim3(512), 0, st, a, G, ws, cm, has_cm);
+    else if (pre) hipLaunchKernelGGL((k_accept<T, M, AL, 256, true>), grid, dim3(256), 0, st, a, G, ws, cm, has_cm);
+    else hipLaunchKernelGGL((k_accept<T, M, AL, 256, false>), grid, dim3(256), 0, st, a, G, ws, cm, has_cm);
   } else {  // rows off 16 bytes: always 256 threads (acc_threads)
-    hipLaunchKernelGGL((k_accept<T, M, AL, 256>), grid, dim3(256), 0, st, a, G, ws, cm, has_cm);
+    if (pre) hipLaunchKernelGGL((k_accept<T, M, AL, 256, true>), grid, dim3(256), 0, st, a, G, ws, cm, has_cm);
+    else hipLaunchKernelGGL((k_accept<T, M, AL, 256, false>), grid, dim3(256), 0, st, a, G, ws, cm, has_cm);
   }
 }
 

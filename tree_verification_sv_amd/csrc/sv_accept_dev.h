@@ -402,24 +402,11 @@ __device__ __forceinline__ bool row_live(const sv_accept_args& a, const SeqInfo&
   return a.mode == SV_GREEDY ? si.haskid[r] != 0 : si.usable[r - 1] != 0;
 }
 
-// Regions of acceptance work-groups.  A launch may split the rows of every sequence over two
-// regions of its grid: rows with a usable child (and the root), whose results the walk always
-// needs, early in the grid; leaf rows, which the walk needs only when it stops at a leaf,
-// late in the grid (their work-groups exit at once when the walk has already finished).
-enum : int { AC_REGION_ALL = 0, AC_REGION_INNER = 1, AC_REGION_LEAVES = 2 };
-__device__ __forceinline__ bool region_keeps(int region, const SeqInfo& si, int r) {
-  if (region == AC_REGION_ALL) return true;
-  const bool inner = r == 0 || si.haskid[r] != 0;
-  return region == AC_REGION_INNER ? inner : !inner;
-}
-
 // Where a work-group sits among the acceptance work-groups of its launch.
 struct AccRole {
-  int bid;       // index among the work-groups of its region (regions start on a multiple of 8)
-  int nblocks;   // acceptance work-groups of the launch, all regions
-  int region;    // AC_REGION_*
-  int grp_off;   // groups of the regions before this one (exchange slots, exit counters)
-  int seq_wgs;   // acceptance work-groups per sequence, all regions
+  int bid;       // index among the acceptance work-groups of its launch (they start on a multiple of 8)
+  int nblocks;   // acceptance work-groups of the launch
+  int seq_wgs;   // acceptance work-groups per sequence
 };
 
 // ---------------------------------------------------------------- slice loads
@@ -522,6 +509,161 @@ __device__ __forceinline__ void argmax_row(const T* row, int V, bool aligned, in
   }
 }
 
+// ---------------------------------------------------------------- a stop row without children
+// A walk that accepts a node whose row has no usable child stops there, and the bonus is a draw
+// from p = softmax(l / T) of that row alone: the smallest id whose ascending cumulative weight
+// exp2((x - M) l2T) exceeds u times the row total (M the row maximum).  Such rows are resolved
+// on demand by the walker's work-group: wave w streams the contiguous pieces of R rounds of 64
+// pieces, so wave totals are the row's prefix sums in id order.  Pass 1 takes the maximum;
+// pass 2 sums the fp32 piece weights in fp64 per wave and per batch of AC_LB rounds (kept in
+// LDS); the wave holding the threshold re-reads the one batch that crosses it (now in the L2
+// cache) and scans it round by round.  Returns the row-result word: token 0 with AC_RES_BAD
+// when the row has no finite positive total, as a row resolved by its group reports.
+// s_bs: LDS for NW * ceil(R / AC_LB) doubles (at most 512 for any V the acceptance accepts).
+constexpr int AC_LB = 8;  // rounds per batch: loads in flight per lane
+template <typename T, int TH>
+__device__ uint64_t leaf_bonus(const T* row, int V, bool aligned, float l2T, float u, Red& red, double* s_bs,
+                               int32_t* s_pick) {
+  constexpr int E = Piece<T>::E, NW = TH / 64;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int pieces = (V + E - 1) / E;
+  const int R = ((pieces + 63) / 64 + NW - 1) / NW;  // rounds per wave
+  const int NB = (R + AC_LB - 1) / AC_LB;            // batches per wave
+  const int pw = wv * R * 64;                        // first piece of this wave
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)row, 0, aligned ? V * (int)sizeof(T) : 0, 0x00020000);
+  auto load = [&](int pc) -> uint4 {  // piece pc (entries past V read as the lowest value)
+    if (aligned) return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, pc * 16, 0, 0));
+    uint32_t wd[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int v = pc * E + e;
+      const T x = v < V ? row[v] : lowest_of<T>();
+      wd[e * sizeof(T) / 4] |= bits_of(x) << (8 * ((e * sizeof(T)) % 4));
+    }
+    return make_uint4(wd[0], wd[1], wd[2], wd[3]);
+  };
+  auto valid = [&](int j, int pc) { return j < R && pc < pieces; };  // round j of this wave
+  // ---- pass 1: the maximum
+  float mx = -FLT_MAX;
+  for (int j0 = 0; j0 < R; j0 += AC_LB) {
+    uint4 raw[AC_LB];
+#pragma unroll
+    for (int k = 0; k < AC_LB; ++k) raw[k] = load(pw + (j0 + k) * 64 + lane);
+#pragma unroll
+    for (int k = 0; k < AC_LB; ++k) {
+      const int pc = pw + (j0 + k) * 64 + lane;
+      float x[E];
+      unpack16<T>(raw[k], x);
+#pragma unroll
+      for (int e = 0; e < E; ++e) mx = valid(j0 + k, pc) && pc * E + e < V ? fmaxf(mx, x[e]) : mx;
+    }
+  }
+  const float M = block_max<TH>(mx, red);
+  const float o = M * l2T;  // exp2(x * l2T - o): one FMA per entry
+  auto weights = [&](const uint4& raw, int pc, bool on, float (&w)[E]) -> float {
+    float x[E], g = 0.f;
+    unpack16<T>(raw, x);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      w[e] = on && pc * E + e < V ? __builtin_amdgcn_exp2f(fmaf(x[e], l2T, -o)) : 0.f;
+      g += w[e];
+    }
+    return g;
+  };
+  // ---- pass 2: batch and wave totals
+  double wsum = 0.0;
+  for (int j0 = 0, bi = 0; j0 < R; j0 += AC_LB, ++bi) {
+    uint4 raw[AC_LB];
+#pragma unroll
+    for (int k = 0; k < AC_LB; ++k) raw[k] = load(pw + (j0 + k) * 64 + lane);
+    double bs = 0.0;
+#pragma unroll
+    for (int k = 0; k < AC_LB; ++k) {
+      const int pc = pw + (j0 + k) * 64 + lane;
+      float w[E];
+      bs += (double)weights(raw[k], pc, valid(j0 + k, pc), w);
+    }
+    bs = wave_sumd(bs);
+    if (lane == 0) s_bs[wv * NB + bi] = bs;
+    wsum += bs;
+  }
+  __syncthreads();
+  if (lane == 0) red.d[wv] = wsum;
+  __syncthreads();
+  double Z = 0.0;
+  for (int k = 0; k < NW; ++k) Z += red.d[k];
+  if (!(Z > 0.0 && Z < (double)INFINITY)) return res_word(-1, 0) | AC_RES_BAD;  // uniform
+  const double thr = (double)u * Z;
+  // the wave, then the batch, whose inclusive prefix first exceeds the threshold (rounding that
+  // leaves it unreached: the last one with a positive total)
+  int ow = -1;
+  double before = 0.0;
+  {
+    double run = 0.0;
+    int lastw = 0;
+    double lastb = 0.0;
+    for (int k = 0; k < NW; ++k) {
+      const double d = red.d[k];
+      if (ow < 0 && d > 0.0 && run + d > thr) { ow = k; before = run; }
+      if (d > 0.0) { lastw = k; lastb = run; }
+      run += d;
+    }
+    if (ow < 0) { ow = lastw; before = lastb; }
+  }
+  if (t == 0) *s_pick = -1;
+  __syncthreads();
+  if (wv == ow) {
+    // batch: lane i takes batch i's total (NB <= 64)
+    const double bsl = lane < NB ? s_bs[ow * NB + lane] : 0.0;
+    const double incl = wave_scand(bsl, lane) + before;
+    const uint64_t over = __ballot(lane < NB && bsl > 0.0 && incl > thr);
+    const uint64_t pos = __ballot(lane < NB && bsl > 0.0);
+    const int bi = over ? __ffsll((long long)over) - 1 : (pos ? 63 - __clzll((long long)pos) : 0);
+    double run = laned(incl - bsl, bi);  // cumulative weight before the batch
+    const int j0 = bi * AC_LB;
+    uint4 raw[AC_LB];
+#pragma unroll
+    for (int k = 0; k < AC_LB; ++k) raw[k] = load(pw + (j0 + k) * 64 + lane);
+    int pick = -1, lastpos = -1;
+#pragma unroll
+    for (int k = 0; k < AC_LB; ++k) {
+      const int pc = pw + (j0 + k) * 64 + lane;
+      float w[E];
+      const float g = weights(raw[k], pc, valid(j0 + k, pc), w);
+      int lp = -1;
+#pragma unroll
+      for (int e = 0; e < E; ++e) lp = w[e] > 0.f ? pc * E + e : lp;
+      for (int s2 = 32; s2 > 0; s2 >>= 1) lp = max(lp, __shfl_xor(lp, s2));
+      lastpos = max(lastpos, lp);
+      const double ic = wave_scand((double)g, lane) + run;
+      const uint64_t ov = __ballot(g > 0.f && ic > thr);
+      if (ov) {  // uniform: lane h holds the crossing piece; it walks its E entries
+        const int h = __ffsll((long long)ov) - 1;
+        if (lane == h) {
+          double r2 = ic - (double)g;
+          int last = -1;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            if (w[e] > 0.f) {
+              last = pc * E + e;
+              r2 += (double)w[e];
+              if (pick < 0 && r2 > thr) pick = pc * E + e;
+            }
+          }
+          *s_pick = pick >= 0 ? pick : last;
+        }
+        pick = 0;  // found (the value is in LDS)
+        break;
+      }
+      run = laned(ic, 63);
+    }
+    if (pick < 0 && lane == 0) *s_pick = lastpos >= 0 ? lastpos : V - 1;
+  }
+  __syncthreads();
+  return res_word(-1, *s_pick);
+}
+
 // ---------------------------------------------------------------- the kernel
 // ALIGNED: every logits row starts on 16 bytes (decided on the host; a compile-time choice
 // keeps the two load paths from meeting in one register assignment)
@@ -536,9 +678,11 @@ struct AccShared {
   uint32_t xv[AC_MAXG][AC_XV];                          // collected group partials
   float s_lp[SV_MAX_N], s_lq[SV_MAX_N], s_u[SV_MAX_N];  // per child: logits at its token, u_accept
   float s_us;                                           // u_sample of the row
-  float s_g[STO ? Piece<T>::NK * TH : 4];               // bonus: per-piece sums [k][t]
+  alignas(16) float s_g[STO ? Piece<T>::NK * TH : 4];   // bonus: per-piece sums [k][t] (a walker's leaf
+                                                        // draw: batch totals, doubles)
   double s_col[Piece<T>::NK];                           // ... and their row totals
   int s_xc, s_claim, s_fin;  // walk finished (sticky); stochastic walk: claimed row, finisher
+  int s_leaf;                // stochastic walk: a stop row without children, drawn by the walker
   int s_bad;                 // the stop row's statistics were not finite
   int s_to;                  // a bounded wait of this call expired: no commit, status 7
   uint64_t rr[STO ? SV_MAX_N + 1 : 1];  // stochastic walk: the sequence's row results
@@ -549,6 +693,7 @@ struct AccShared {
 // work-group among the acceptance work-groups of its launch; S is its LDS.
 // PREFETCH: the target slice is loaded before the sequence facts that say whether the row is
 // needed (its latency then overlaps theirs); otherwise after them, and only for needed rows.
+// Either choice gives the same results; prefetching pays where nearly every row is resolved.
 template <typename T, int MODE, bool ALIGNED, int TH, bool PREFETCH>
 __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, const AccWs& ws,
                                             const sv_commit_args& cm, int32_t has_cm, const AccRole role,
@@ -577,63 +722,41 @@ __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, 
   const int N = a.N, V = a.V;
   const float invT = STO ? 1.0f / a.temperature : 1.0f;
   const float l2T = invT * 1.4426950408889634f;  // bulk exponentials as exp2((x - m) * log2(e) / T)
-  const int64_t gslot = (int64_t)grp + role.grp_off;  // exchange slots and exit counter of the group
+  const int64_t gslot = grp;  // exchange slots and exit counter of the group
   XSlot* gslots = ws.xs + gslot * G * 2;
   uint32_t xtag = 0;  // exchanges of this group so far (identical on every member)
   const int64_t item = grp;
   const int s0 = rank * ac_slice<T, TH>();  // this work-group's slice of the vocabulary
   if (t == 0) s_xc = 0;
   bool live_row = false;
-  bool skip = false;  // a leaf-region group whose row the walk cannot need any more
-  if (role.region == AC_REGION_LEAVES && item < (int64_t)a.B * (N + 1)) {
-    // A walk reaches a leaf row only through its parent row's accepted child, so the group
-    // waits, before any other load, until the parent row is resolved or the sequence's walk
-    // has finished, and works only when the parent accepted this row's node.  The parent's
-    // group belongs to the region of rows with children, which every XCD dispatches before this
-    // one, so the wait ends (it is bounded all the same; on expiry the row is resolved anyway).
-    if (t == 0) {
-      const int bb = (int)(item / (N + 1)), rr = (int)(item % (N + 1));
-      const int pr = rr > 0 ? a.parents[(int64_t)bb * N + rr - 1] : -2;
-      uint32_t cv = ld_u32(&ws.cancel[bb]);  // in flight together with the parent's load
-      int gone = 0;
-      for (uint32_t spins = 0; spins < AC_SPIN_LIMIT; ++spins) {
-        if (cv != 0u) { gone = 1; break; }
-        if (pr < -1 || pr >= N) break;  // not a usable node: the facts below say so
-        const uint64_t v = ld_u64(&ws.res[(int64_t)bb * (N + 1) + pr + 1]);
-        if (res_ready(v)) { gone = res_child(v) != rr - 1; break; }
-        __builtin_amdgcn_s_sleep(2);
-        cv = ld_u32(&ws.cancel[bb]);
-      }
-      s_xc = gone;
-    }
-    __syncthreads();
-    skip = s_xc != 0;
-  }
-
-  if (item < (int64_t)a.B * (N + 1) && !skip) {
+  if (item < (int64_t)a.B * (N + 1)) {
     // uniform, and kept in scalar registers so that the slice loads take a scalar resource
     const int b = __builtin_amdgcn_readfirstlane((int)(item / (N + 1)));
     const int r = __builtin_amdgcn_readfirstlane((int)(item % (N + 1)));
     const T* prow = (const T*)a.target_logits + ((int64_t)b * (N + 1) + r) * V;
     const T* qrow = MODE == SV_STOCHASTIC ? (const T*)a.draft_logits + ((int64_t)b * (N + 1) + r) * V : nullptr;
     constexpr bool aligned = ALIGNED;
-    // stochastic: nearly every row is resolved, so the target slice is fetched before the
-    // sequence facts that confirm it is needed (its latency overlaps them); the facts'
-    // own loads go first
     SeqRaw sr = seq_fetch(a, b);
     // stochastic, wide trees: the walk advances as rows resolve and ends the sequence's
-    // remaining rows (below); chains and narrow trees, where nearly every row is on the
-    // path, walk once after the last row
+    // remaining rows (below); without the prefetch, rows without a usable child are not
+    // resolved here -- the walker draws the bonus of such a stop row itself (leaf_bonus).
+    // Chains and narrow trees, where nearly every row is on the path, resolve every row and
+    // walk once after the last one.
     const bool incr = STO && N > 2 * a.max_depth;
+    const bool wleaf = !PREFETCH && incr;  // stop rows without children: drawn by the walker
     uint32_t* cancel = incr ? &ws.cancel[b] : nullptr;
     uint32_t cx0 = 0u;  // the sequence's walk already finished (a late work-group)
     if (incr && t == 0) cx0 = ld_u32(cancel);
+    // PREFETCH (chains and narrow trees, which resolve nearly every row): the target slice is
+    // fetched before the sequence facts that confirm it is needed (its latency overlaps theirs;
+    // the facts' own loads go first); otherwise after the facts, for the rows resolved
     uint4 rp[NK];
     if constexpr (STO && PREFETCH) load_pieces<T, TH>(prow, s0, V, aligned, t, rp);
     asm volatile("" : "+v"(sr.tok), "+v"(sr.par), "+v"(sr.dep), "+v"(cx0));  // nothing uses them before this point
     if (cx0) s_xc = 1;
     seq_facts<TH>(a, sr, si);
-    live_row = row_live(a, si, r) && region_keeps(role.region, si, r);  // the same on every member
+    // the same on every member
+    live_row = row_live(a, si, r) && (!wleaf || r == 0 || si.haskid[r] != 0);
     if constexpr (STO && !PREFETCH) load_pieces<T, TH>(prow, s0, V, aligned, t, rp, live_row && !s_xc);
     if (live_row && !s_xc) {
       row_kids<TH>(N, r, si);
@@ -1019,6 +1142,7 @@ __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, 
         uint64_t* s_rr = S.rr;  // the sequence's row results
         if (t == 0) {
           s_fin = 0;
+          S.s_leaf = -1;
           if (incr) {
             s_claim = cas_u32(front, (uint32_t)r, AC_FRONT_BUSY) ? r : -1;
           } else {  // the last row of the sequence to resolve walks
@@ -1047,6 +1171,9 @@ __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, 
             }
             if (stop) {
               s_fin = 1;
+            } else if (wleaf && row > 0 && !si.haskid[row]) {  // a stop row without children
+              S.s_leaf = row;
+              s_fin = 1;
             } else {
               st_u32(front, (uint32_t)row);
               mem_complete();
@@ -1056,9 +1183,17 @@ __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, 
           }
           __syncthreads();
         }
+        if (!PREFETCH && S.s_leaf >= 0) {  // uniform: its bonus is drawn here, from the target row alone
+          const int lr = S.s_leaf;
+          const uint64_t wd =
+              leaf_bonus<T, TH>((const T*)a.target_logits + ((int64_t)b * (N + 1) + lr) * V, V, aligned, l2T,
+                                a.u_sample[(int64_t)b * (N + 1) + lr], red, (double*)S.s_g, &s_first);
+          if (t == 0) s_rr[lr] = wd;
+          __syncthreads();
+        }
         if (s_fin) {
           // the path from the root in the LDS copy: every row on it was resolved before the
-          // frontier passed it
+          // frontier passed it (a stop row without children: drawn just above)
           if (t == 0) {
             int row = 0, n = 0;
             for (;;) {

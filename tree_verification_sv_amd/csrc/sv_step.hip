@@ -11,7 +11,7 @@
 // the accepted count stays on the device.
 //
 // A step of the separate calls is a chain of dependent launches whose gaps,
-// not bytes, set its time at batch 1.  Here one grid runs five regions of
+// not bytes, set its time at batch 1.  Here one grid runs four regions of
 // 512-thread work-groups, one per compute unit, in dispatch order (each region
 // starts on a multiple of 8 blocks, so its blocks keep the round-robin XCD
 // order):
@@ -21,13 +21,11 @@
 //      derives its query nodes' ancestor sets from the parent array itself;
 //   2. the mask outputs, when the caller asks for them (one work-group per
 //      sequence; nothing else reads them);
-//   3. acceptance groups of the rows that have a usable child (and the root);
+//   3. acceptance groups, one per row (over wide trees the stochastic and top-K
+//      walks resolve only rows with a usable child and the root: a walk that
+//      stops at a leaf draws that row's bonus in the walker's work-group);
 //   4. merge work-groups, which wait for the attention splits they combine --
-//      only for work-groups dispatched before them, so the wait always ends;
-//   5. acceptance groups of the leaf rows: the walk needs a leaf row only when
-//      it stops there, so these run last and exit at once once the walk is done
-//      (stochastic and top-K walks over wide trees; otherwise region 3 takes
-//      every row).  They wait only for rows of region 3.
+//      only for work-groups dispatched before them, so the wait always ends.
 // The roles share the LDS (a work-group runs one role): the attention's tile and query
 // buffers, and one union of the other roles' state.
 #include "sv_accept_dev.h"
@@ -49,9 +47,8 @@ struct StepKArgs {
   int32_t* m_depth;
   int32_t* m_path;
   int32_t* m_status;
-  int32_t r_mask, r_acc, r_merge, r_leaf, r_end;  // first block of regions 2..5, and the grid size
-  int32_t na1, nacc;    // acceptance work-groups of region 3, of regions 3 and 5
-  int32_t ng1;          // row groups of region 3 (the leaf region's groups follow them)
+  int32_t r_mask, r_acc, r_merge, r_end;  // first block of regions 2..4, and the grid size
+  int32_t nacc;         // acceptance work-groups
   uint32_t* exit_count; // work-groups of the launch that have finished
 };
 
@@ -92,18 +89,13 @@ __global__ void __launch_bounds__(MF_THREADS, 1) k_verify_step(StepKArgs k) {
     if (b < k.ac.B)
       mask_seq(k.ac.parents, k.ac.N, k.ac.max_depth, (k.ac.N + 63) / 64, k.m_anc, k.m_depth, k.m_path, k.m_status, b,
                s_aux.mask.spar, &s_aux.mask.worst);
-  } else if (bid < k.r_merge || (bid >= k.r_leaf && bid < k.r_end)) {
-    // ---- acceptance (regions 3 and 5)
-    const bool leaf = bid >= k.r_leaf;
-    const bool split = k.nacc > k.na1;
-    const int per_seq = (k.ac.N + 1) * k.G * (split ? 2 : 1);
-    const AccRole role{leaf ? bid - k.r_leaf : bid - k.r_acc, k.nacc,
-                       leaf ? AC_REGION_LEAVES : (split ? AC_REGION_INNER : AC_REGION_ALL), leaf ? k.ng1 : 0,
-                       per_seq};
+  } else if (bid < k.r_merge) {
+    // ---- acceptance
+    const AccRole role{bid - k.r_acc, k.nacc, (k.ac.N + 1) * k.G};
     accept_body<T, MODE, true, TH, false>(k.ac, k.G, k.ws, k.cm, k.has_cm, role, s_aux.acc);
-  } else if (bid < k.r_leaf) {
+  } else {
     // ---- merge of the attention splits
-    const int pos = bid - k.r_merge, nb = k.r_leaf - k.r_merge;
+    const int pos = bid - k.r_merge, nb = k.r_end - k.r_merge;
     const int mid = (pos % 8) * (nb / 8) + pos / 8;
     if (mid < k.ac.B * k.at.Hkv * k.ap.mper) step_merge<D, TH>(k.at, k.ap, mid, s_aux.mrg);
   }
@@ -159,7 +151,6 @@ AttnPlan step_plan(const sv_attn_args& a) {
 }
 
 int step_G(const sv_accept_args& a) { return launch_G(a, MF_THREADS); }
-bool step_leaf_region(const sv_accept_args& a) { return a.mode != SV_GREEDY && a.N > 2 * a.max_depth; }
 
 struct StepLayout {
   WsLayout acc;
@@ -168,7 +159,7 @@ struct StepLayout {
 StepLayout step_layout(const sv_attn_args& at, const sv_accept_args& ac, const AttnPlan& p) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   StepLayout l{};
-  l.acc = ws_layout_g(ac, step_G(ac), step_leaf_region(ac) ? 2 : 1);
+  l.acc = ws_layout_g(ac, step_G(ac), 1);
   size_t o = l.acc.total;
   const size_t parts = (size_t)p.nunits * (p.nsplit > 1 ? p.nsplit : 0) * p.QT;
   l.opart = o; o = up(o + parts * at.D * sizeof(uint16_t));
@@ -255,21 +246,17 @@ extern "C" sv_status sv_verify_step(const sv_step_args* sp, void* stream) {
   k.m_path = s.path_rows;
   k.m_status = s.mask_status;
   auto up8 = [](int64_t x) { return (x + 7) / 8 * 8; };
-  const int64_t na1 = num_groups(ac) * k.G;  // a multiple of 8 * G
+  const int64_t nacc = num_groups(ac) * k.G;  // a multiple of 8 * G
   const int64_t nmask = s.anc_bits ? up8(ac.B) : 0;
   const int64_t natt = up8(p0.nwg);
   const int64_t nmerge = up8((int64_t)ac.B * at.Hkv * p0.mper);
-  const int64_t na2 = step_leaf_region(ac) ? na1 : 0;
-  const int64_t total = natt + nmask + na1 + nmerge + na2;
+  const int64_t total = natt + nmask + nacc + nmerge;
   if (total > 0x7fffffff) return SV_ERR_UNSUPPORTED;
   k.r_mask = (int32_t)natt;
   k.r_acc = (int32_t)(natt + nmask);
-  k.r_merge = (int32_t)(k.r_acc + na1);
-  k.r_leaf = (int32_t)(k.r_merge + nmerge);
+  k.r_merge = (int32_t)(k.r_acc + nacc);
   k.r_end = (int32_t)total;
-  k.na1 = (int32_t)na1;
-  k.ng1 = (int32_t)num_groups(ac);
-  k.nacc = (int32_t)(na1 + na2);
+  k.nacc = (int32_t)nacc;
   hipStream_t hs = (hipStream_t)stream;
   const dim3 grid((unsigned)total), block(MF_THREADS);
 #define SV_STEP(D_, M_) hipLaunchKernelGGL((k_verify_step<D_, M_>), grid, block, 0, hs, k)
