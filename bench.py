@@ -40,10 +40,14 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_TFLOPS = 2500.0   # dense bf16 MFMA peak of MI355X
 VALU_FP32_TFLOPS = 157.3    # fp32 vector peak of MI355X
 MALL_BYTES = 256 * 2**20
-# batches up to this many logits rows run the step as one sv_verify_step launch (MI355X:
-# eagle-static-8b, 61 rows, 33 vs 43 us; draft-target-chain-8b, 768 rows, 427 vs 371 us;
-# batched-paged-70b, 2112 rows, 608 vs 580 us)
+# batches up to this many logits rows run the step as one sv_verify_step launch, and stochastic
+# or top-K walks over wide trees (the walk advances as rows resolve) up to ONE_LAUNCH_MAX_ROWS_WIDE
+# (MI355X, one launch vs separate calls: eagle-static-8b 61 rows 33 vs 42 us, its batch 4 84 vs
+# 94 us, batch 8 152 vs 154 us, batch 16 (976 rows) 254 vs 270 us; draft-target-chain-8b, 768
+# rows, 467 vs 390 us; batched-paged-70b, 2112 rows, 586 vs 566 us; outcome-tree-8b, 4112 rows,
+# 2900 vs 2749 us)
 ONE_LAUNCH_MAX_ROWS = 256
+ONE_LAUNCH_MAX_ROWS_WIDE = 1024
 
 
 def algorithmic_bytes(w, acc):
@@ -395,9 +399,10 @@ def main():
                          "of one sv_verify_step launch")
     ap.add_argument("--one-launch", action="store_true",
                     help="run the step as one sv_verify_step launch whatever the batch (default: one launch for "
-                         f"batches of at most {ONE_LAUNCH_MAX_ROWS} logits rows, where the separate calls' launch "
-                         "gaps dominate; the separate calls above that, where the two branches filling the device "
-                         "side by side measured faster on MI355X)")
+                         f"batches of at most {ONE_LAUNCH_MAX_ROWS} logits rows, or {ONE_LAUNCH_MAX_ROWS_WIDE} for "
+                         "stochastic and top-K walks over wide trees, where the separate calls' launch gaps dominate; "
+                         "the separate calls above that, where the two branches filling the device side by side "
+                         "measured faster on MI355X)")
     ap.add_argument("--reps", type=int, default=5, help="timed repetitions of the K-step graph (median reported)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--acceptance", choices=["greedy", "stochastic", "topk", "threshold"], default=None,
@@ -452,7 +457,9 @@ def main():
             s_.mask_free_accept(True)
     one = False
     rows = w0.B * (w0.N + 1)
-    if not args.separate_calls and not mask_free and (args.one_launch or rows <= ONE_LAUNCH_MAX_ROWS):
+    wide = w0.mode in ("stochastic", "topk") and w0.N > 2 * w0.max_depth
+    limit = ONE_LAUNCH_MAX_ROWS_WIDE if wide else ONE_LAUNCH_MAX_ROWS
+    if not args.separate_calls and not mask_free and (args.one_launch or rows <= limit):
         one = all([s_.one_launch(True) for s_ in steps])
         if not one:
             print("[bench] sv_verify_step does not support this workload; timing the separate calls",
