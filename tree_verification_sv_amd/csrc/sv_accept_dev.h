@@ -443,6 +443,11 @@ __device__ __forceinline__ void opaque(uint4 (&raw)[NK]) {
 template <typename T, int TH>
 __device__ __forceinline__ int piece_v(int s0, int k, int t) { return s0 + (k * TH + t) * Piece<T>::E; }
 
+// Cache policy of the slice loads: non-temporal (nt).  Every logits byte is read once, so the
+// lines are marked for early eviction and leave the caches to the data that is reused (the
+// attention's query rows, the exchange words).  MI355X, one-launch 60-node tree step: 33.2 ->
+// 32.2 us.
+constexpr int AC_NT = 2;
 // Thread t's pieces of one logits row.  `aligned`: the row starts on 16 bytes
 // and V * sizeof(T) is a multiple of 16, so each piece lies wholly inside or
 // wholly past the row; the loads then go through a buffer resource sized to
@@ -462,7 +467,7 @@ __device__ __forceinline__ void load_pieces(const T* row, int s0, int V, bool al
     const int vo = (s0 + t * E) * (int)sizeof(T);
 #pragma unroll
     for (int k = 0; k < Piece<T>::NK; ++k)
-      raw[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, k * TH * 16, 0));
+      raw[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, k * TH * 16, AC_NT));
   } else if (!present) {
 #pragma unroll
     for (int k = 0; k < Piece<T>::NK; ++k) raw[k] = make_uint4(0u, 0u, 0u, 0u);

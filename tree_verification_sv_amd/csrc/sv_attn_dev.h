@@ -105,6 +105,7 @@ constexpr int MF_THREADS = 64 * MF_WAVES;
 constexpr int MF_QB = 1;                   // 32-row query blocks per wave
 constexpr int KT = 64;  // keys per tile
 constexpr float AT_LAZY = 8.f;  // log2 of the largest weight before the reference maximum moves
+constexpr int AT_NT = 2;        // cache policy of the K/V tile loads: non-temporal
 
 struct AttnPlan {
   int32_t G, M, QB, QT, qtiles, nsplit, chunk, ntt, W, cap;
@@ -299,8 +300,10 @@ __device__ __forceinline__ void attn_mfma_body(const sv_attn_args& a, const Attn
       } else {
         off = (uint32_t)((paged_tile ? (key & 15) : key) * ROWB + c * 16);
       }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_void*)(kb + n * 1024), 16, off, soff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_void*)(kb + TL::TBYTES + n * 1024), 16, off, soff, 0, 0);
+      // non-temporal: each K/V row is read by one work-group once (the query rows, read by every
+      // split of a pair, keep the default policy)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_void*)(kb + n * 1024), 16, off, soff, 0, AT_NT);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_void*)(kb + TL::TBYTES + n * 1024), 16, off, soff, 0, AT_NT);
     }
   };
 
