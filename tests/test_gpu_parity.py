@@ -235,10 +235,13 @@ def test_chi_square_gpu(shape):
     assert chi.pvalue > 0.01, chi
 
 
-@pytest.mark.parametrize("B,N,V", [(20, 32, 3001), (16, 40, 40000), (24, 24, 300)])
+@pytest.mark.parametrize("B,N,V", [(20, 32, 3001), (16, 40, 40000), (24, 24, 300), (600, 3, 4096), (2, 255, 1000),
+                                   (1100, 3, 1024), (300, 15, 70000)])
 def test_greedy_row_streamer(B, N, V):
-    """Greedy batches of at least 512 rows: one work-group streams each whole row (rows off 16
-    bytes, several slices per row, and a vocabulary smaller than one slice)."""
+    """Greedy batches of at least 512 rows, streamed whole by work-groups that each take an equal
+    share of the batch's needed (row, slice) items -- rows split between work-groups included --
+    or, above the list's capacity of 4352 rows, a few work-groups per sequence (rows off 16
+    bytes, several slices per row, a vocabulary smaller than one slice, two wide trees)."""
     w = W.config(3, B=B, N=N, V=V, L=(16, 80))
     assert w.B * (w.N + 1) >= 512 and w.mode == "greedy"
     print(f"[gpu] greedy streamer B={w.B} N={w.N} V={w.V}", flush=True)

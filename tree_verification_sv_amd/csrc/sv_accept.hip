@@ -73,6 +73,14 @@ __global__ void __launch_bounds__(TH, 2) k_accept(sv_accept_args a, int32_t G, A
   accept_body<T, MODE, ALIGNED, TH, PRE>(a, G, ws, cm, has_cm, role, S);
 }
 
+// greedy batches of at least AC_STREAM_ROWS rows: rows_wps(a) work-groups per sequence
+template <typename T, bool ALIGNED>
+__global__ void __launch_bounds__(512, 2) k_accept_rows(sv_accept_args a, int32_t wps, AccWs ws, sv_commit_args cm,
+                                                        int32_t has_cm) {
+  __shared__ AccShared<T, 512, false> S;
+  greedy_rows_body<T, ALIGNED, 512>(a, wps, ws, cm, has_cm, S);
+}
+
 // SV_FLAG_VALIDATE: one work-group per logits row (target rows, then draft rows in mode 1) looks
 // for a NaN or +Inf entry, or a row without any finite entry, and sets status 8 for the
 // sequence unless the acceptance already reported a code.
@@ -112,17 +120,26 @@ template <typename T, int M, bool AL>
 void launch_accept(int TH, dim3 grid, hipStream_t st, const sv_accept_args& a, int G, const AccWs& ws,
                    const sv_commit_args& cm, int32_t has_cm) {
   // the walk modes prefetch unless the walk advances as rows resolve (wide trees: only rows with a
-  // usable child are resolved, and 512-thread groups are only taken for wide trees)
-  const bool pre = !(a.N > 2 * a.max_depth);
+  // usable child are resolved, and 512-thread groups are only taken for wide trees); fp32 logits
+  // (the small-vocabulary path) always prefetch and resolve every row, which keeps those kernels
+  // free of the walker's leaf draw and of its register pressure
+  constexpr bool LEAF = sizeof(T) == 2;
+  const bool pre = !LEAF || !(a.N > 2 * a.max_depth);
   if constexpr (M == SV_GREEDY) {
-    hipLaunchKernelGGL((k_accept<T, M, AL, 512, true>), grid, dim3(512), 0, st, a, G, ws, cm, has_cm);
+    if (G == 1) {  // whole rows streamed by a few work-groups per sequence
+      const int wps = rows_wps(a);
+      hipLaunchKernelGGL((k_accept_rows<T, AL>), dim3((unsigned)rows_grid(a, 512, wps)), dim3(512), 0, st, a, wps, ws,
+                         cm, has_cm);
+    } else {
+      hipLaunchKernelGGL((k_accept<T, M, AL, 512, true>), grid, dim3(512), 0, st, a, G, ws, cm, has_cm);
+    }
   } else if constexpr (AL) {
-    if (TH == 512) hipLaunchKernelGGL((k_accept<T, M, AL, 512, false>), grid, dim3(512), 0, st, a, G, ws, cm, has_cm);
+    if (TH == 512) hipLaunchKernelGGL((k_accept<T, M, AL, 512, !LEAF>), grid, dim3(512), 0, st, a, G, ws, cm, has_cm);
     else if (pre) hipLaunchKernelGGL((k_accept<T, M, AL, 256, true>), grid, dim3(256), 0, st, a, G, ws, cm, has_cm);
-    else hipLaunchKernelGGL((k_accept<T, M, AL, 256, false>), grid, dim3(256), 0, st, a, G, ws, cm, has_cm);
+    else if constexpr (LEAF) hipLaunchKernelGGL((k_accept<T, M, AL, 256, false>), grid, dim3(256), 0, st, a, G, ws, cm, has_cm);
   } else {  // rows off 16 bytes: always 256 threads (acc_threads)
     if (pre) hipLaunchKernelGGL((k_accept<T, M, AL, 256, true>), grid, dim3(256), 0, st, a, G, ws, cm, has_cm);
-    else hipLaunchKernelGGL((k_accept<T, M, AL, 256, false>), grid, dim3(256), 0, st, a, G, ws, cm, has_cm);
+    else if constexpr (LEAF) hipLaunchKernelGGL((k_accept<T, M, AL, 256, false>), grid, dim3(256), 0, st, a, G, ws, cm, has_cm);
   }
 }
 

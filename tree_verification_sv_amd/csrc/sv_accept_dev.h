@@ -33,6 +33,8 @@ constexpr int AC_NWMAX = 8;                    // waves per work-group at most
 template <typename T> constexpr int ac_ct() { return 8 * (16 / (int)sizeof(T)); }
 template <typename T, int TH> constexpr int ac_slice() { return TH * ac_ct<T>(); }
 constexpr int AC_MAXG = 64;                    // work-groups per row group (vocabulary up to 1M entries)
+constexpr int AC_BLIST = 4352;                 // greedy batch streams: rows of the batch at most
+constexpr int AC_WALKQ = 16;                   // greedy batch streams: walks per work-group at most
 constexpr int AC_XW = 8;                       // tagged words per exchange slot
 constexpr int AC_XV = 6;                       // words an exchange carries at most
 constexpr uint32_t AC_SPIN_LIMIT = 1u << 20;   // bounded wait for a group partner (polls)
@@ -527,7 +529,7 @@ __device__ __forceinline__ void argmax_row(const T* row, int V, bool aligned, in
 // s_bs: LDS for NW * ceil(R / AC_LB) doubles (at most 512 for any V the acceptance accepts).
 constexpr int AC_LB = 8;  // rounds per batch: loads in flight per lane
 template <typename T, int TH>
-__device__ uint64_t leaf_bonus(const T* row, int V, bool aligned, float l2T, float u, Red& red, double* s_bs,
+__device__ __forceinline__ uint64_t leaf_bonus(const T* row, int V, bool aligned, float l2T, float u, Red& red, double* s_bs,
                                int32_t* s_pick) {
   constexpr int E = Piece<T>::E, NW = TH / 64;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
@@ -630,40 +632,43 @@ __device__ uint64_t leaf_bonus(const T* row, int V, bool aligned, float l2T, flo
     uint4 raw[AC_LB];
 #pragma unroll
     for (int k = 0; k < AC_LB; ++k) raw[k] = load(pw + (j0 + k) * 64 + lane);
-    int pick = -1, lastpos = -1;
+    bool found = false;  // uniform over the wave
+    int lastpos = -1;
 #pragma unroll
     for (int k = 0; k < AC_LB; ++k) {
-      const int pc = pw + (j0 + k) * 64 + lane;
-      float w[E];
-      const float g = weights(raw[k], pc, valid(j0 + k, pc), w);
-      int lp = -1;
+      if (!found) {
+        const int pc = pw + (j0 + k) * 64 + lane;
+        float w[E];
+        const float g = weights(raw[k], pc, valid(j0 + k, pc), w);
+        int lp = -1;
 #pragma unroll
-      for (int e = 0; e < E; ++e) lp = w[e] > 0.f ? pc * E + e : lp;
-      for (int s2 = 32; s2 > 0; s2 >>= 1) lp = max(lp, __shfl_xor(lp, s2));
-      lastpos = max(lastpos, lp);
-      const double ic = wave_scand((double)g, lane) + run;
-      const uint64_t ov = __ballot(g > 0.f && ic > thr);
-      if (ov) {  // uniform: lane h holds the crossing piece; it walks its E entries
-        const int h = __ffsll((long long)ov) - 1;
-        if (lane == h) {
-          double r2 = ic - (double)g;
-          int last = -1;
+        for (int e = 0; e < E; ++e) lp = w[e] > 0.f ? pc * E + e : lp;
+        for (int s2 = 32; s2 > 0; s2 >>= 1) lp = max(lp, __shfl_xor(lp, s2));
+        lastpos = max(lastpos, lp);
+        const double ic = wave_scand((double)g, lane) + run;
+        const uint64_t ov = __ballot(g > 0.f && ic > thr);
+        if (ov) {  // lane h holds the crossing piece; it walks its E entries
+          const int h = __ffsll((long long)ov) - 1;
+          if (lane == h) {
+            double r2 = ic - (double)g;
+            int pick = -1, last = -1;
 #pragma unroll
-          for (int e = 0; e < E; ++e) {
-            if (w[e] > 0.f) {
-              last = pc * E + e;
-              r2 += (double)w[e];
-              if (pick < 0 && r2 > thr) pick = pc * E + e;
+            for (int e = 0; e < E; ++e) {
+              if (w[e] > 0.f) {
+                last = pc * E + e;
+                r2 += (double)w[e];
+                if (pick < 0 && r2 > thr) pick = pc * E + e;
+              }
             }
+            *s_pick = pick >= 0 ? pick : last;
           }
-          *s_pick = pick >= 0 ? pick : last;
+          found = true;
+        } else {
+          run = laned(ic, 63);
         }
-        pick = 0;  // found (the value is in LDS)
-        break;
       }
-      run = laned(ic, 63);
     }
-    if (pick < 0 && lane == 0) *s_pick = lastpos >= 0 ? lastpos : V - 1;
+    if (!found && lane == 0) *s_pick = lastpos >= 0 ? lastpos : V - 1;
   }
   __syncthreads();
   return res_word(-1, *s_pick);
@@ -691,7 +696,348 @@ struct AccShared {
   int s_bad;                 // the stop row's statistics were not finite
   int s_to;                  // a bounded wait of this call expired: no commit, status 7
   uint64_t rr[STO ? SV_MAX_N + 1 : 1];  // stochastic walk: the sequence's row results
+  int16_t rows[STO ? 1 : SV_MAX_N + 1];  // greedy row streams: the rows the walk needs, ascending
+  uint8_t bflag[STO ? 1 : AC_BLIST];     // greedy batch streams: row of the batch needed
+  uint16_t blist[STO ? 1 : AC_BLIST];    // ... the needed rows of the batch, ascending
+  int32_t bscan[AC_NWMAX + 1];           // ... block scan
+  int32_t walkq[AC_WALKQ + 1];           // ... sequences this work-group walks (count first)
 };
+
+// The greedy walk of sequence b, by the work-group that counted its last needed row: the
+// accepted node is the deepest one (lowest index on ties) whose whole root path matches the
+// parents' argmax; the bonus is the stop row's argmax (streamed here for a row without a usable
+// child, which no work-group resolved).  Writes the outputs, clears the sequence's row results
+// and counter for the next call, and commits the accepted path when asked to.
+// KEYS: the row results are argmax keys (orderable value << 32 | ~index) rather than result words.
+template <typename T, int TH, bool KEYS = false>
+__device__ __forceinline__ void greedy_walk(const sv_accept_args& a, const AccWs& ws, const sv_commit_args& cm, int32_t has_cm,
+                            int b, bool aligned, AccShared<T, TH, false>& S) {
+  auto row_token = [](uint64_t v) { return KEYS ? (int)(0xffffffffu - (uint32_t)v) : res_token(v); };
+  const int t = threadIdx.x, lane = t & 63;
+  const int N = a.N, V = a.V;
+  SeqInfo& si = S.si;
+  Red& red = S.red;
+  uint64_t* s_match = S.s_match;
+  int32_t &s_hit = S.s_hit, &s_to = S.s_to;
+  // ----------------------------------------------------- walk of sequence b
+  if (t == 0) s_to = ld_u32(ws.err) != 0;  // read after the barriers below
+  int A = 0, stop_row = 0, bonus = 0;
+  uint64_t* rr = ws.res + (int64_t)b * (N + 1);
+  {
+    // match[i]: token equals its parent row's argmax; accepted: the whole root path matches
+    {  // wave w holds nodes 64 w .. 64 w + 63: its ballot is bitset word w
+      const uint64_t mb =
+          __ballot(t < N && si.usable[t] && a.tokens[(int64_t)b * N + t] == row_token(ld_u64(&rr[si.par[t] + 1])));
+      if (lane == 0 && (t >> 6) < SV_MAX_W) s_match[t >> 6] = mb;
+    }
+    __syncthreads();
+    int key = -1;
+    if (t < N && si.usable[t]) {
+      // up the root path of t (si.dep[t] nodes, all in range for a usable node): t is
+      // accepted when every node on it matches
+      const int dt = si.dep[t];
+      bool ok = true;
+      int cur = t;
+      for (int st = 0; st < dt; ++st) {
+        ok &= ((s_match[cur >> 6] >> (cur & 63)) & 1ull) != 0;
+        cur = si.par[cur];
+      }
+      if (ok) key = (dt << 9) | (511 - t);  // deepest, then lowest index
+    }
+    {
+      float kv = (float)key;
+      int ki = key;
+      block_argmax<TH>(kv, ki, red);
+      key = (int)kv;
+    }
+    if (key >= 0) {
+      A = key >> 9;
+      const int stop = 511 - (key & 511);
+      stop_row = stop + 1;
+      if (t == 0) {
+        int node = stop;
+        for (int k = A - 1; k >= 0; --k) { si.path[k] = node; node = si.par[node]; }
+      }
+    }
+    if (row_live(a, si, stop_row)) {
+      if (t == 0) s_hit = row_token(ld_u64(&rr[stop_row]));
+      __syncthreads();
+      bonus = s_hit;
+    } else {
+      // leaf stop row: argmax by this work-group, one slice at a time with the next
+      // slice's loads in flight (a thread visits its entries in ascending id)
+      const T* srow = (const T*)a.target_logits + ((int64_t)b * (N + 1) + stop_row) * V;
+      float best = -FLT_MAX;
+      int arg = 0x7fffffff;
+      argmax_row<T, TH>(srow, V, aligned, t, best, arg);
+      block_argmax<TH>(best, arg, red);
+      bonus = arg;
+    }
+  }
+  __syncthreads();
+  const int Dm = a.max_depth;
+  if (t == 0) {
+    a.accept_len[b] = A;
+    a.num_out[b] = A + 1;
+    a.stop_row[b] = stop_row;
+    a.status[b] = s_to ? SV_SEQ_TIMEOUT : (si.bad_token ? SV_SEQ_TOKEN : 0);
+    st_u32(&ws.seqdone[b], 0u);  // every row of b has been counted: ready for the next call
+  }
+  // every row result of b has been read: leave them cleared for the next call
+  for (int x = t; x <= N; x += TH) st_u64(&rr[x], 0ull);
+  if (t < Dm) a.accept_rows[(int64_t)b * Dm + t] = t < A ? si.path[t] + 1 : 0;
+  if (t <= Dm)
+    a.out_tokens[(int64_t)b * (Dm + 1) + t] = t < A ? a.tokens[(int64_t)b * N + si.path[t]] : (t == A ? bonus : 0);
+  // the accepted path into the cache (nothing after a timeout: the path may be wrong)
+  if (has_cm) svc::walker_commit(cm, b, s_to ? 0 : A, si.path);
+}
+
+// Greedy batches whose B (N + 1) rows fit the LDS list: the needed rows of the whole batch are
+// one list, and its (row, slice) items are split into equal contiguous ranges, one per
+// work-group, so every work-group streams the same number of slices (to within one).  Every
+// work-group derives the batch's needed rows itself (the root and the rows with a usable
+// child, by the rule of the sequence facts).  A row split between work-groups is combined by a
+// device-scope atomic maximum of its 64-bit key -- the orderable value bits of its maximum over
+// the complement of its index, so that the largest key is the largest value with the lowest
+// index -- and a per-sequence count of finished items names the work-group that walks it.
+__device__ __forceinline__ uint64_t argmax_key(float v, int i) {
+  if (v == 0.f) v = 0.f;  // -0 and +0 compare equal, as in the row scan
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (0xffffffffu - (uint32_t)i);
+}
+template <typename T, bool ALIGNED, int TH>
+__device__ __forceinline__ void greedy_batch_body(const sv_accept_args& a, const AccWs& ws, const sv_commit_args& cm,
+                                                  int32_t has_cm, AccShared<T, TH, false>& S) {
+  constexpr int E = Piece<T>::E, NK = Piece<T>::NK, NW = TH / 64;
+  constexpr int SL = ac_slice<T, TH>();
+  constexpr bool aligned = ALIGNED;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int N = a.N, V = a.V, B = a.B, R = N + 1, rows = B * R;
+  Red& red = S.red;
+  // ---- the needed rows of the batch
+  for (int x = t; x < rows; x += TH) S.bflag[x] = x % R == 0;
+  if (t == 0) S.walkq[0] = 0;
+  __syncthreads();
+  for (int n = t; n < B * N; n += TH) {
+    const int b = n / N, i = n - b * N;
+    const int pr = a.parents[n], tok = a.tokens[n];
+    if (pr < -1 || pr >= N || tok < 0 || tok >= V) continue;
+    int dep = 0;
+    if (a.depth) {
+      dep = a.depth[n];
+    } else {  // nodes on the root path within max_depth, through in-range parents
+      int cur = i, cnt = 1;
+      for (int st = 0; st < SV_MAX_DEPTH; ++st) {
+        const int p = a.parents[(int64_t)b * N + cur];
+        if (p == -1) { dep = cnt; break; }
+        if (p < 0 || p >= N || cnt >= a.max_depth) break;
+        ++cnt;
+        cur = p;
+      }
+    }
+    if (dep > 0) S.bflag[b * R + pr + 1] = 1;  // every writer stores the same value
+  }
+  __syncthreads();
+  // ascending list: thread t scans a contiguous chunk, a block scan places it
+  const int C = (rows + TH - 1) / TH;
+  const int x0 = min(rows, t * C), x1 = min(rows, x0 + C);
+  int c = 0;
+  for (int x = x0; x < x1; ++x) c += S.bflag[x];
+  int incl = c;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) S.bscan[wv] = incl;
+  __syncthreads();
+  int pos = incl - c, total = 0;
+  for (int k = 0; k < NW; ++k) {
+    if (k < wv) pos += S.bscan[k];
+    total += S.bscan[k];
+  }
+  for (int x = x0; x < x1; ++x)
+    if (S.bflag[x]) S.blist[pos++] = (uint16_t)x;
+  __syncthreads();
+  // ---- this work-group's items: (row, slice) pairs i0 .. i1 - 1 of the list
+  const int ns = (V + SL - 1) / SL;
+  const int items = total * ns;
+  const int per = (items + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int i0 = min(items, (int)blockIdx.x * per), i1 = min(items, i0 + per);
+  const T* target = (const T*)a.target_logits;
+  auto row_of = [&](int i) { return __builtin_amdgcn_readfirstlane((int)S.blist[i / ns]); };
+  auto load_item = [&](int i, uint4 (&r)[NK]) {
+    load_pieces<T, TH>(target + (int64_t)row_of(i) * V, (i % ns) * SL, V, aligned, t, r);
+  };
+  float best = -FLT_MAX;
+  int arg = 0x7fffffff;
+  int first = i0;  // first item of the current row in this range
+  auto consume = [&](const uint4 (&raw)[NK], int i) {
+    const int s0 = (i % ns) * SL;
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      float x[E];
+      unpack16<T>(raw[k], x);
+      const int v = piece_v<T, TH>(s0, k, t);
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (v + e < V && x[e] > best) { best = x[e]; arg = v + e; }
+    }
+    if (i % ns == ns - 1 || i == i1 - 1) {  // the row ends here, or the range does (uniform)
+      block_argmax<TH>(best, arg, red);
+      const int row = row_of(i);
+      if (t == 0) {
+        __hip_atomic_fetch_max(&ws.res[row], argmax_key(best, arg), __ATOMIC_RELAXED, AGENT);
+        mem_complete();  // the key has been combined before the count below
+        const int b = row / R;
+        int cnt = 0;
+        for (int x = b * R; x < (b + 1) * R; ++x) cnt += S.bflag[x];
+        const uint32_t n = (uint32_t)(i - first + 1);
+        if (add_u32(&ws.seqdone[b], n) + n == (uint32_t)(cnt * ns)) S.walkq[1 + S.walkq[0]++] = b;
+      }
+      first = i + 1;
+      best = -FLT_MAX;
+      arg = 0x7fffffff;
+    }
+  };
+  const int nitems = i1 - i0;
+  uint4 r0[NK], r1[NK];
+  if (nitems > 0) load_item(i0, r0);
+  for (int i = 0; i < nitems; i += 2) {
+    if (i + 1 < nitems) load_item(i0 + i + 1, r1);
+    consume(r0, i0 + i);
+    if (i + 1 >= nitems) break;
+    if (i + 2 < nitems) load_item(i0 + i + 2, r0);
+    consume(r1, i0 + i + 1);
+  }
+  __syncthreads();
+  // ---- the walks of the sequences whose last item this work-group counted
+  const int nw = S.walkq[0];
+  for (int q = 0; q < nw; ++q) {
+    const int b = S.walkq[1 + q];
+    seq_facts<TH>(a, seq_fetch(a, b), S.si);
+    greedy_walk<T, TH, true>(a, ws, cm, has_cm, b, aligned, S);
+    __syncthreads();
+  }
+}
+
+// Greedy batches of at least AC_STREAM_ROWS logits rows: wps work-groups per sequence stream
+// the rows the walk needs -- the root and the rows with a usable child -- work-group j of
+// sequence b taking every wps-th of them in ascending order, so rows without a usable child
+// cost no work-group at all.  The work-group's row slices form one stream with the next
+// slice's loads in flight across row boundaries; each row's argmax (lowest id on ties: a
+// thread visits its entries in ascending id, and the block reduction keeps the lower index)
+// is one block reduction at its last slice.  The work-group that counts a sequence's last
+// needed row walks it.  No work-group waits for another; a timeout word already set when the
+// launch starts is reported as status 7 by every walk and cleared by the last work-group.
+constexpr int AC_ROWS_WGS = 512;  // work-groups aimed at: two 512-thread work-groups per CU
+// the part of greedy_rows_body for sequence b, work-group j of its wps
+template <typename T, bool ALIGNED, int TH>
+__device__ __forceinline__ void greedy_rows_seq(const sv_accept_args& a, int wps, int b, int j, const AccWs& ws,
+                                                const sv_commit_args& cm, int32_t has_cm,
+                                                AccShared<T, TH, false>& S) {
+  constexpr int E = Piece<T>::E, NK = Piece<T>::NK, NW = TH / 64;
+  constexpr int SL = ac_slice<T, TH>();
+  constexpr bool aligned = ALIGNED;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int N = a.N, V = a.V;
+  SeqInfo& si = S.si;
+  Red& red = S.red;
+  seq_facts<TH>(a, seq_fetch(a, b), si);
+  // the needed rows, ascending
+  const bool need = t <= N && (t == 0 || si.haskid[t] != 0);
+  const uint64_t m = __ballot(need);
+  if (lane == 0) si.wcount[wv] = __popcll(m);
+  __syncthreads();
+  int off = 0, cnt = 0;
+  for (int k = 0; k < NW; ++k) {
+    if (k < wv) off += si.wcount[k];
+    cnt += si.wcount[k];
+  }
+  if (need) S.rows[off + __popcll(m & ((1ull << lane) - 1ull))] = (int16_t)t;
+  __syncthreads();
+  const int mine = cnt > j ? (cnt - j + wps - 1) / wps : 0;  // rows j, j + wps, ... of the list
+  const int ns = (V + SL - 1) / SL;                            // slices per row
+  const int items = mine * ns;
+  const T* target = (const T*)a.target_logits + (int64_t)b * (N + 1) * V;
+  auto row_of = [&](int i) { return __builtin_amdgcn_readfirstlane((int)S.rows[j + (i / ns) * wps]); };
+  auto load_item = [&](int i, uint4 (&r)[NK]) {
+    load_pieces<T, TH>(target + (int64_t)row_of(i) * V, (i % ns) * SL, V, aligned, t, r);
+  };
+  float best = -FLT_MAX;
+  int arg = 0x7fffffff;
+  auto consume = [&](const uint4 (&raw)[NK], int i) {
+    const int s0 = (i % ns) * SL;
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      float x[E];
+      unpack16<T>(raw[k], x);
+      const int v = piece_v<T, TH>(s0, k, t);
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (v + e < V && x[e] > best) { best = x[e]; arg = v + e; }
+    }
+    if (i % ns == ns - 1) {  // the row's last slice (uniform)
+      block_argmax<TH>(best, arg, red);
+      if (t == 0) st_u64(&ws.res[(int64_t)b * (N + 1) + row_of(i)], res_word(-1, arg));
+      best = -FLT_MAX;
+      arg = 0x7fffffff;
+    }
+  };
+  uint4 r0[NK], r1[NK];
+  if (items > 0) load_item(0, r0);
+  for (int i = 0; i < items; i += 2) {
+    if (i + 1 < items) load_item(i + 1, r1);
+    consume(r0, i);
+    if (i + 1 >= items) break;
+    if (i + 2 < items) load_item(i + 2, r0);
+    consume(r1, i + 1);
+  }
+  if (mine == 0) return;  // uniform
+  mem_complete();  // this thread's row-result stores (if any) have completed
+  __syncthreads();
+  if (t == 0) {
+    const uint32_t old = add_u32(&ws.seqdone[b], (uint32_t)mine);
+    S.s_last = old + (uint32_t)mine == (uint32_t)si.nlive;
+  }
+  __syncthreads();
+  if (S.s_last) greedy_walk<T, TH>(a, ws, cm, has_cm, b, aligned, S);
+}
+template <typename T, bool ALIGNED, int TH>
+__device__ __forceinline__ void greedy_rows_body(const sv_accept_args& a, int wps, const AccWs& ws,
+                                                 const sv_commit_args& cm, int32_t has_cm,
+                                                 AccShared<T, TH, false>& S) {
+  const int t = threadIdx.x;
+  if (wps == 0) {  // one list for the whole batch
+    greedy_batch_body<T, ALIGNED, TH>(a, ws, cm, has_cm, S);
+  } else {
+    const int b = (int)(blockIdx.x / (unsigned)wps), j = (int)(blockIdx.x % (unsigned)wps);
+    if (b < a.B) greedy_rows_seq<T, ALIGNED, TH>(a, wps, b, j, ws, cm, has_cm, S);
+  }
+  // every work-group counts out; the last one leaves the timeout word zeroed
+  mem_complete();
+  __syncthreads();
+  if (t == 0 && add_u32(ws.err + 1, 1u) + 1 == gridDim.x) {
+    st_u32(ws.err, 0u);
+    st_u32(ws.err + 1, 0u);
+  }
+}
+// work-groups per sequence of greedy_rows_body, or 0 for one list over the batch (grid:
+// rows_grid); a work-group's range then ends at most AC_BLIST / AC_ROWS_WGS + 2 rows, so at
+// most that many walks, which AC_WALKQ holds
+inline int rows_wps(const sv_accept_args& a) {
+  if ((int64_t)a.B * (a.N + 1) <= AC_BLIST) return 0;
+  const int w = (AC_ROWS_WGS + a.B - 1) / a.B;
+  return w < 1 ? 1 : (w > a.N + 1 ? a.N + 1 : w);
+}
+static_assert(AC_BLIST / AC_ROWS_WGS + 2 <= AC_WALKQ, "walk queue");
+inline int64_t rows_grid(const sv_accept_args& a, int TH, int wps) {
+  if (wps > 0) return (int64_t)a.B * wps;
+  const int64_t slices = (a.V + (int64_t)TH * (a.logits_dtype == SV_BF16 ? 64 : 32) - 1) /
+                         ((int64_t)TH * (a.logits_dtype == SV_BF16 ? 64 : 32));
+  const int64_t items = (int64_t)a.B * (a.N + 1) * slices;  // an upper bound of the list's items
+  return items < AC_ROWS_WGS ? items : AC_ROWS_WGS;
+}
 
 // The resolution of one row slice by one work-group of a row group (see the file comment of
 // sv_accept.hip), callable from any kernel whose work-groups have TH threads.  `role` places the
@@ -1235,86 +1581,16 @@ __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, 
 
       // ---- greedy: the work-group that wrote the row result counts it; the last row of a
       // sequence walks
-      if (MODE == SV_GREEDY && done_by_me) {
-        mem_complete();  // this thread's row-result stores (if any) have completed
-        __syncthreads();
-        if (t == 0) {
-          const uint32_t old = add_u32(&ws.seqdone[b], 1u);
-          s_last = old + 1 == (uint32_t)si.nlive;
-        }
-        __syncthreads();
-        if (s_last) {
-          // ----------------------------------------------------- walk of sequence b
-          if (t == 0) s_to = ld_u32(ws.err) != 0;  // read after the barriers below
-          int A = 0, stop_row = 0, bonus = 0;
-          uint64_t* rr = ws.res + (int64_t)b * (N + 1);
-          {
-            // match[i]: token equals its parent row's argmax; accepted: the whole root path matches
-            {  // wave w holds nodes 64 w .. 64 w + 63: its ballot is bitset word w
-              const uint64_t mb =
-                  __ballot(t < N && si.usable[t] && a.tokens[(int64_t)b * N + t] == res_token(ld_u64(&rr[si.par[t] + 1])));
-              if (lane == 0 && (t >> 6) < SV_MAX_W) s_match[t >> 6] = mb;
-            }
-            __syncthreads();
-            int key = -1;
-            if (t < N && si.usable[t]) {
-              // up the root path of t (si.dep[t] nodes, all in range for a usable node): t is
-              // accepted when every node on it matches
-              const int dt = si.dep[t];
-              bool ok = true;
-              int cur = t;
-              for (int st = 0; st < dt; ++st) {
-                ok &= ((s_match[cur >> 6] >> (cur & 63)) & 1ull) != 0;
-                cur = si.par[cur];
-              }
-              if (ok) key = (dt << 9) | (511 - t);  // deepest, then lowest index
-            }
-            {
-              float kv = (float)key;
-              int ki = key;
-              block_argmax<TH>(kv, ki, red);
-              key = (int)kv;
-            }
-            if (key >= 0) {
-              A = key >> 9;
-              const int stop = 511 - (key & 511);
-              stop_row = stop + 1;
-              if (t == 0) {
-                int node = stop;
-                for (int k = A - 1; k >= 0; --k) { si.path[k] = node; node = si.par[node]; }
-              }
-            }
-            if (row_live(a, si, stop_row)) {
-              if (t == 0) s_hit = res_token(ld_u64(&rr[stop_row]));
-              __syncthreads();
-              bonus = s_hit;
-            } else {
-              // leaf stop row: argmax by this work-group, one slice at a time with the next
-              // slice's loads in flight (a thread visits its entries in ascending id)
-              const T* srow = (const T*)a.target_logits + ((int64_t)b * (N + 1) + stop_row) * V;
-              float best = -FLT_MAX;
-              int arg = 0x7fffffff;
-              argmax_row<T, TH>(srow, V, aligned, t, best, arg);
-              block_argmax<TH>(best, arg, red);
-              bonus = arg;
-            }
+      if constexpr (MODE == SV_GREEDY) {
+        if (done_by_me) {
+          mem_complete();  // this thread's row-result stores (if any) have completed
+          __syncthreads();
+          if (t == 0) {
+            const uint32_t old = add_u32(&ws.seqdone[b], 1u);
+            s_last = old + 1 == (uint32_t)si.nlive;
           }
           __syncthreads();
-          const int Dm = a.max_depth;
-          if (t == 0) {
-            a.accept_len[b] = A;
-            a.num_out[b] = A + 1;
-            a.stop_row[b] = stop_row;
-            a.status[b] = s_to ? SV_SEQ_TIMEOUT : (si.bad_token ? SV_SEQ_TOKEN : 0);
-            st_u32(&ws.seqdone[b], 0u);  // every row of b has been counted: ready for the next call
-          }
-          // every row result of b has been read: leave them cleared for the next call
-          for (int x = t; x <= N; x += TH) st_u64(&rr[x], 0ull);
-          if (t < Dm) a.accept_rows[(int64_t)b * Dm + t] = t < A ? si.path[t] + 1 : 0;
-          if (t <= Dm)
-            a.out_tokens[(int64_t)b * (Dm + 1) + t] = t < A ? a.tokens[(int64_t)b * N + si.path[t]] : (t == A ? bonus : 0);
-          // the accepted path into the cache (nothing after a timeout: the path may be wrong)
-          if (has_cm) svc::walker_commit(cm, b, s_to ? 0 : A, si.path);
+          if (s_last) greedy_walk<T, TH>(a, ws, cm, has_cm, b, aligned, S);
         }
       }
     }

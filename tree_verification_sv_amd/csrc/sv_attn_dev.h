@@ -610,6 +610,7 @@ __device__ __forceinline__ void step_merge(const sv_attn_args& a, const AttnPlan
   constexpr int TPR = D / 8;                // threads per output row
   constexpr int RPP = TH / TPR;             // rows per pass
   constexpr int SB = 16;                    // split rows in flight per thread
+  constexpr int MLN = 64 / TPR;             // (m, l) pairs per thread (at most 64 splits)
   const int t = threadIdx.x;
   const int pair = mid / p.mper, part = mid % p.mper;
   const int b = pair / a.Hkv, g = pair % a.Hkv;
@@ -639,19 +640,40 @@ __device__ __forceinline__ void step_merge(const sv_attn_args& a, const AttnPlan
     const bool on = m < m1;
     const int mm = on ? m : m1 - 1;
     const int unit = pair * p.qtiles + mm / p.QT, ql = mm % p.QT;
-    // weights: thread c of the row takes splits c, c + TPR, ...; max and sum over the row's lanes
+    // every load of the row goes out first (one memory round trip): thread c takes the (m, l) of
+    // splits c, c + TPR, ... and its 16-byte chunk of the first SB splits' rows
+    uint64_t mlw[MLN];
+#pragma unroll
+    for (int i = 0; i < MLN; ++i)
+      mlw[i] = ld_dev64(p.mlpart + (((int64_t)unit * ns + min(c + i * TPR, ns - 1)) * p.QT + ql) * 2);
+    uint4 part[SB];
+    auto load_parts = [&](int s0) {
+#pragma unroll
+      for (int k = 0; k < SB; ++k) {
+        const int s = min(s0 + k, ns - 1);
+        const uint16_t* src = p.opart + (((int64_t)unit * ns + s) * p.QT + ql) * D + c * 8;
+        const uint64_t lo = ld_dev64(src), hi = ld_dev64(src + 4);
+        part[k] = make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
+      }
+    };
+    load_parts(0);
+    // weights exp2(m_s - max) l_s: max and sum over the row's lanes
     float mx = -INFINITY;
-    for (int s = c; s < ns; s += TPR)
-      mx = fmaxf(mx, __uint_as_float((uint32_t)ld_dev64(p.mlpart + (((int64_t)unit * ns + s) * p.QT + ql) * 2)));
+#pragma unroll
+    for (int i = 0; i < MLN; ++i)
+      if (c + i * TPR < ns) mx = fmaxf(mx, __uint_as_float((uint32_t)mlw[i]));
 #pragma unroll
     for (int o = TPR / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
     float lsum = 0.f;
-    for (int s = c; s < ns; s += TPR) {
-      const uint64_t mlw = ld_dev64(p.mlpart + (((int64_t)unit * ns + s) * p.QT + ql) * 2);
-      const float2 ml = make_float2(__uint_as_float((uint32_t)mlw), __uint_as_float((uint32_t)(mlw >> 32)));
-      const float f = ml.x == -INFINITY ? 0.f : exp2f(ml.x - mx) * ml.y;
-      s_f[lr * 64 + s] = f;
-      lsum += f;
+#pragma unroll
+    for (int i = 0; i < MLN; ++i) {
+      const int s = c + i * TPR;
+      const float ms = __uint_as_float((uint32_t)mlw[i]), ls = __uint_as_float((uint32_t)(mlw[i] >> 32));
+      const float f = ms == -INFINITY ? 0.f : exp2f(ms - mx) * ls;
+      if (s < ns) {
+        s_f[lr * 64 + s] = f;
+        lsum += f;
+      }
     }
 #pragma unroll
     for (int o = TPR / 2; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
@@ -660,14 +682,7 @@ __device__ __forceinline__ void step_merge(const sv_attn_args& a, const AttnPlan
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     for (int s0 = 0; s0 < ns; s0 += SB) {
-      uint4 part[SB];
-#pragma unroll
-      for (int k = 0; k < SB; ++k) {
-        const int s = min(s0 + k, ns - 1);
-        const uint16_t* src = p.opart + (((int64_t)unit * ns + s) * p.QT + ql) * D + c * 8;
-        const uint64_t lo = ld_dev64(src), hi = ld_dev64(src + 4);
-        part[k] = make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
-      }
+      if (s0 > 0) load_parts(s0);
 #pragma unroll
       for (int k = 0; k < SB; ++k) {
         const float f = s0 + k < ns ? s_f[lr * 64 + min(s0 + k, 63)] : 0.f;  // past the splits: weight 0
