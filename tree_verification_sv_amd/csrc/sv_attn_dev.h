@@ -375,9 +375,9 @@ __device__ __forceinline__ void attn_mfma_body(const sv_attn_args& a, const Attn
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[qb][kb][r] = 0.f;
-    // the fragments of k-step ds + 1 are read while the MFMAs of step ds run, so the LDS
-    // latency is hidden behind them
-    sv_bf16x8 qf[2][QB], kf[2][2];
+    // the fragments of k-steps ds + 1 and ds + 2 are read while the MFMAs of step ds run, so
+    // the LDS latency is hidden behind them
+    sv_bf16x8 qf[3][QB], kf[3][2];
     auto frag = [&](int ds, int buf) {
       const int kslot = ((2 * ds + hf) ^ k_swz) * 16;  // Q and K rows share the swizzle of row lq
 #pragma unroll
@@ -387,14 +387,15 @@ __device__ __forceinline__ void attn_mfma_body(const sv_attn_args& a, const Attn
       for (int kb = 0; kb < 2; ++kb) kf[buf][kb] = *(const sv_bf16x8*)(Kb + kb * 32 * ROWB + k_off + kslot);
     };
     frag(0, 0);
+    frag(1, 1);
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
-      if (ds + 1 < DS) frag(ds + 1, (ds + 1) & 1);
+      if (ds + 2 < DS) frag(ds + 2, (ds + 2) % 3);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds & 1][kb], qf[ds & 1][qb], sacc[qb][kb], 0, 0, 0);
+          sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds % 3][kb], qf[ds % 3][qb], sacc[qb][kb], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);  // one step in flight at a time (register pressure)
     }
 
@@ -484,11 +485,11 @@ __device__ __forceinline__ void attn_mfma_body(const sv_attn_args& a, const Attn
 
     __builtin_amdgcn_sched_barrier(0);
     // ---- O^T += V^T P^T; the 16-key step (kb, t2) holds keys 32 kb + 16 t2 + 4 hf + {0..3, 8..11}.
-    // Half-steps of two d-blocks: the transposing reads of half-step h + 1 are issued before
-    // the MFMAs of half-step h, which wait only for their own reads (LDS reads complete in
-    // order, so at most the 4 newer reads may still be outstanding).
+    // Half-steps of two d-blocks: the transposing reads of half-steps h + 1 and h + 2 are
+    // issued before the MFMAs of half-step h, which wait only for their own reads (LDS reads
+    // complete in order, so at most the 8 newer reads may still be outstanding).
     constexpr int NH = 2 * DB;  // 4 steps (kb, t2) x DB / 2 halves
-    uint2 vlo[2][2], vhi[2][2];
+    uint2 vlo[3][2], vhi[3][2];
     auto tr_issue = [&](int h, int buf) {
       const int st = h / (DB / 2), d0 = (h % (DB / 2)) * 2;  // step kb * 2 + t2, first d-block
       const int kb = st >> 1, t2 = st & 1;
@@ -504,11 +505,14 @@ __device__ __forceinline__ void attn_mfma_body(const sv_attn_args& a, const Attn
       tr_read_issue(vlo[buf], vhi[buf], alo, ahi);
     };
     tr_issue(0, 0);
+    tr_issue(1, 1);
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
-      const int buf = h & 1;
-      if (h + 1 < NH) {
-        tr_issue(h + 1, buf ^ 1);
+      const int buf = h % 3;
+      if (h + 2 < NH) {
+        tr_issue(h + 2, (h + 2) % 3);
+        tr_wait<8>(vlo[buf], vhi[buf]);
+      } else if (h + 1 < NH) {
         tr_wait<4>(vlo[buf], vhi[buf]);
       } else {
         tr_wait<0>(vlo[buf], vhi[buf]);
