@@ -236,14 +236,31 @@ def test_chi_square_gpu(shape):
 
 
 @pytest.mark.parametrize("B,N,V", [(20, 32, 3001), (16, 40, 40000), (24, 24, 300), (600, 3, 4096), (2, 255, 1000),
-                                   (1100, 3, 1024), (300, 15, 70000)])
+                                   (40, 40, 100000), (48, 24, 98311), (8, 255, 98305), (6, 200, 98311),
+                                   (12, 100, 40000), (1100, 3, 1024), (300, 15, 70000)])
 def test_greedy_row_streamer(B, N, V):
-    """Greedy batches of at least 512 rows, streamed whole by work-groups that each take an equal
-    share of the batch's needed (row, slice) items -- rows split between work-groups included --
-    or, above the list's capacity of 4352 rows, a few work-groups per sequence (rows off 16
-    bytes, several slices per row, a vocabulary smaller than one slice, two wide trees)."""
+    """Greedy batches of at least 512 rows, each row read by one work-group.  From 16 sequences
+    on, a work-group per sequence follows its accepted path row by row; below that, whole rows of
+    the batch's needed-row list are streamed, the first by work-group index and the rest taken
+    from a device-wide counter (two rows ahead for rows of one or two slices, one row ahead from
+    three slices on), several rows per work-group, leaf stop rows handed back into the walker's
+    stream.  Rows off 16 bytes, vocabularies smaller than one slice, wide trees."""
     w = W.config(3, B=B, N=N, V=V, L=(16, 80))
     assert w.B * (w.N + 1) >= 512 and w.mode == "greedy"
     print(f"[gpu] greedy streamer B={w.B} N={w.N} V={w.V}", flush=True)
+    r = run_step(w, ("mask", "accept"))
+    compare_accept(r["acc"], oracle.accept(w), allow_flagged=False)
+
+
+@pytest.mark.parametrize("B,N,V", [(32, 20, 40000), (40, 20, 33333), (8, 80, 70000), (10, 60, 50001)])
+def test_greedy_rows_fp32(B, N, V):
+    """fp32 logits in both greedy forms of batches of at least 512 rows: per-sequence chains
+    (B >= 16) and the streamed row list (B < 16, several slices per row), rows on and off 16 bytes."""
+    seed = 31 + B
+    par = np.stack([W.tree_random_recursive(seed, N, 6, offset=b * N) for b in range(B)])
+    w = W.build_workload("greedy-f32", B, N, 8, 2, 64, V, "f32", "greedy", par, np.full(B, 64), max_depth=6,
+                         seed=seed, logit_sigma=3.0, token_rule="uniform", plant=W.plant_pairs(seed, par),
+                         need_draft=False)
+    print(f"[gpu] greedy fp32 B={B} N={N} V={V}", flush=True)
     r = run_step(w, ("mask", "accept"))
     compare_accept(r["acc"], oracle.accept(w), allow_flagged=False)

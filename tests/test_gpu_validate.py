@@ -146,8 +146,12 @@ def _ws_err_offset(B, N):
 
 
 @pytest.mark.parametrize("cfg,over", [(2, dict(B=2, L=64, V=5003)), (3, dict(B=4, L=(16, 80), V=3001)),
+                                      (3, dict(B=16, L=(16, 80), V=70000)), (3, dict(B=8, N=80, L=(16, 80), V=40000)),
                                       (4, dict(B=6, L=64, V=2999))])
 def test_timeout_word_reports_status_7_then_recovers(cfg, over):
+    """A timeout word set before the call: every sequence reports status 7, the workspace is left
+    zeroed, and the next call matches the oracle (row groups with exchanges; greedy chains of two
+    work-groups per sequence; the greedy row list)."""
     import torch
     import tree_verification_sv_amd as sv
     from tree_verification_sv_amd.step import VerifyStep

@@ -73,12 +73,23 @@ __global__ void __launch_bounds__(TH, 2) k_accept(sv_accept_args a, int32_t G, A
   accept_body<T, MODE, ALIGNED, TH, PRE>(a, G, ws, cm, has_cm, role, S);
 }
 
-// greedy batches of at least AC_STREAM_ROWS rows: rows_wps(a) work-groups per sequence
+// greedy batches of at least AC_STREAM_ROWS rows and fewer than AC_CHAIN_B sequences: the
+// needed rows as one list.  bf16 rows on 16 bytes fit two work-groups per CU (four waves per
+// SIMD, 128 registers) without spilling; the other forms keep one work-group per CU.
 template <typename T, bool ALIGNED>
-__global__ void __launch_bounds__(512, 2) k_accept_rows(sv_accept_args a, int32_t wps, AccWs ws, sv_commit_args cm,
-                                                        int32_t has_cm) {
+constexpr int rows_wgs_per_cu() { return ALIGNED && sizeof(T) == 2 ? 2 : 1; }
+template <typename T, bool ALIGNED>
+__global__ void __launch_bounds__(512, (2 * rows_wgs_per_cu<T, ALIGNED>()))
+    k_accept_rows(sv_accept_args a, AccWs ws, sv_commit_args cm, int32_t has_cm) {
   __shared__ AccShared<T, 512, false> S;
-  greedy_rows_body<T, ALIGNED, 512>(a, wps, ws, cm, has_cm, S);
+  greedy_rows_body<T, ALIGNED, 512, false>(a, 0, ws, cm, has_cm, S);
+}
+// ... and of AC_CHAIN_B sequences or more: a chain per sequence, G work-groups per row
+template <typename T, bool ALIGNED>
+__global__ void __launch_bounds__(512, 2) k_accept_chain(sv_accept_args a, int32_t G, AccWs ws, sv_commit_args cm,
+                                                         int32_t has_cm) {
+  __shared__ AccShared<T, 512, false> S;
+  greedy_rows_body<T, ALIGNED, 512, true>(a, G, ws, cm, has_cm, S);
 }
 
 // SV_FLAG_VALIDATE: one work-group per logits row (target rows, then draft rows in mode 1) looks
@@ -126,10 +137,15 @@ void launch_accept(int TH, dim3 grid, hipStream_t st, const sv_accept_args& a, i
   constexpr bool LEAF = sizeof(T) == 2;
   const bool pre = !LEAF || !(a.N > 2 * a.max_depth);
   if constexpr (M == SV_GREEDY) {
-    if (G == 1) {  // whole rows streamed by a few work-groups per sequence
-      const int wps = rows_wps(a);
-      hipLaunchKernelGGL((k_accept_rows<T, AL>), dim3((unsigned)rows_grid(a, 512, wps)), dim3(512), 0, st, a, wps, ws,
-                         cm, has_cm);
+    if (G == 1) {  // rows read whole: a chain per sequence, or the batch's needed rows as one list
+      if (rows_chain(a)) {
+        const int CG = chain_G(a, 512);
+        hipLaunchKernelGGL((k_accept_chain<T, AL>), dim3((unsigned)chain_grid(a, CG)), dim3(512), 0, st, a, CG, ws, cm,
+                           has_cm);
+      } else {
+        hipLaunchKernelGGL((k_accept_rows<T, AL>), dim3((unsigned)rows_grid(a, rows_wgs_per_cu<T, AL>())), dim3(512), 0, st,
+                           a, ws, cm, has_cm);
+      }
     } else {
       hipLaunchKernelGGL((k_accept<T, M, AL, 512, true>), grid, dim3(512), 0, st, a, G, ws, cm, has_cm);
     }

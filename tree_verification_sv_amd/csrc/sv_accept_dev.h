@@ -34,7 +34,7 @@ template <typename T> constexpr int ac_ct() { return 8 * (16 / (int)sizeof(T)); 
 template <typename T, int TH> constexpr int ac_slice() { return TH * ac_ct<T>(); }
 constexpr int AC_MAXG = 64;                    // work-groups per row group (vocabulary up to 1M entries)
 constexpr int AC_BLIST = 4352;                 // greedy batch streams: rows of the batch at most
-constexpr int AC_WALKQ = 16;                   // greedy batch streams: walks per work-group at most
+constexpr int AC_LEAFROW = 1 << 30;            // greedy batch streams: a stream entry that is a leaf stop row
 constexpr int AC_XW = 8;                       // tagged words per exchange slot
 constexpr int AC_XV = 6;                       // words an exchange carries at most
 constexpr uint32_t AC_SPIN_LIMIT = 1u << 20;   // bounded wait for a group partner (polls)
@@ -60,7 +60,7 @@ constexpr uint32_t AC_FRONT_BUSY = 0xffffffffu;  // the walk's frontier is claim
 struct AccWs {        // workspace views
   uint32_t* gexit;    // [groups] group exit counters
   uint32_t* seqdone;  // [B] rows resolved per sequence (greedy)
-  uint32_t* err;      // [0] wait-timeout flag, [1] work-groups exited
+  uint32_t* err;      // [0] wait-timeout flag, [1] work-groups exited, [2] greedy batch streams: rows taken
   uint64_t* res;      // [B, N+1] resolved rows
   uint32_t* frontier; // [B] stochastic walk: the first row of the path not yet resolved
   uint32_t* cancel;   // [B] stochastic walk finished: remaining rows are not needed
@@ -700,19 +700,25 @@ struct AccShared {
   uint8_t bflag[STO ? 1 : AC_BLIST];     // greedy batch streams: row of the batch needed
   uint16_t blist[STO ? 1 : AC_BLIST];    // ... the needed rows of the batch, ascending
   int32_t bscan[AC_NWMAX + 1];           // ... block scan
-  int32_t walkq[AC_WALKQ + 1];           // ... sequences this work-group walks (count first)
+  uint16_t bseq[STO ? 1 : AC_BLIST / 2 + 1];  // ... first list position of each sequence
+  int32_t ring[4];                       // ... this work-group's next rows (list positions or leaf rows)
+  int32_t q_inj;                         // ... a leaf stop row waiting for a ring slot
+  int32_t q_pend, q_ended;               // ... row j + D's entry when not from the counter; counter run out
+  int32_t rowarg[STO ? 1 : SV_MAX_N + 1];  // greedy chains: argmax of each followed row
+  int32_t q_head, q_tail;                  // ... rows to follow: S.rows[q_head .. q_tail)
 };
 
 // The greedy walk of sequence b, by the work-group that counted its last needed row: the
 // accepted node is the deepest one (lowest index on ties) whose whole root path matches the
-// parents' argmax; the bonus is the stop row's argmax (streamed here for a row without a usable
-// child, which no work-group resolved).  Writes the outputs, clears the sequence's row results
-// and counter for the next call, and commits the accepted path when asked to.
-// KEYS: the row results are argmax keys (orderable value << 32 | ~index) rather than result words.
-template <typename T, int TH, bool KEYS = false>
-__device__ __forceinline__ void greedy_walk(const sv_accept_args& a, const AccWs& ws, const sv_commit_args& cm, int32_t has_cm,
+// parents' argmax; the bonus is the stop row's argmax (for a row without a usable child, which
+// no work-group resolved, streamed here -- or, with DEFER, left to the caller, who gets the
+// stream entry AC_LEAFROW | A << 13 | (batch row) back and writes the bonus token itself).
+// Writes the outputs, clears the sequence's row results and counter for the next call, and
+// commits the accepted path when asked to.  Returns -1 when nothing is left to the caller.
+template <typename T, int TH, bool DEFER = false>
+__device__ __forceinline__ int greedy_walk(const sv_accept_args& a, const AccWs& ws, const sv_commit_args& cm, int32_t has_cm,
                             int b, bool aligned, AccShared<T, TH, false>& S) {
-  auto row_token = [](uint64_t v) { return KEYS ? (int)(0xffffffffu - (uint32_t)v) : res_token(v); };
+  auto row_token = [](uint64_t v) { return res_token(v); };
   const int t = threadIdx.x, lane = t & 63;
   const int N = a.N, V = a.V;
   SeqInfo& si = S.si;
@@ -721,7 +727,7 @@ __device__ __forceinline__ void greedy_walk(const sv_accept_args& a, const AccWs
   int32_t &s_hit = S.s_hit, &s_to = S.s_to;
   // ----------------------------------------------------- walk of sequence b
   if (t == 0) s_to = ld_u32(ws.err) != 0;  // read after the barriers below
-  int A = 0, stop_row = 0, bonus = 0;
+  int A = 0, stop_row = 0, bonus = 0, left = -1;
   uint64_t* rr = ws.res + (int64_t)b * (N + 1);
   {
     // match[i]: token equals its parent row's argmax; accepted: the whole root path matches
@@ -763,6 +769,8 @@ __device__ __forceinline__ void greedy_walk(const sv_accept_args& a, const AccWs
       if (t == 0) s_hit = row_token(ld_u64(&rr[stop_row]));
       __syncthreads();
       bonus = s_hit;
+    } else if constexpr (DEFER) {
+      left = AC_LEAFROW | (A << 13) | (b * (N + 1) + stop_row);
     } else {
       // leaf stop row: argmax by this work-group, one slice at a time with the next
       // slice's loads in flight (a thread visits its entries in ascending id)
@@ -786,57 +794,73 @@ __device__ __forceinline__ void greedy_walk(const sv_accept_args& a, const AccWs
   // every row result of b has been read: leave them cleared for the next call
   for (int x = t; x <= N; x += TH) st_u64(&rr[x], 0ull);
   if (t < Dm) a.accept_rows[(int64_t)b * Dm + t] = t < A ? si.path[t] + 1 : 0;
-  if (t <= Dm)
+  if (t <= Dm && !(t == A && left >= 0))
     a.out_tokens[(int64_t)b * (Dm + 1) + t] = t < A ? a.tokens[(int64_t)b * N + si.path[t]] : (t == A ? bonus : 0);
   // the accepted path into the cache (nothing after a timeout: the path may be wrong)
   if (has_cm) svc::walker_commit(cm, b, s_to ? 0 : A, si.path);
+  return left;
 }
 
-// Greedy batches whose B (N + 1) rows fit the LDS list: the needed rows of the whole batch are
-// one list, and its (row, slice) items are split into equal contiguous ranges, one per
-// work-group, so every work-group streams the same number of slices (to within one).  Every
-// work-group derives the batch's needed rows itself (the root and the rows with a usable
-// child, by the rule of the sequence facts).  A row split between work-groups is combined by a
-// device-scope atomic maximum of its 64-bit key -- the orderable value bits of its maximum over
-// the complement of its index, so that the largest key is the largest value with the lowest
-// index -- and a per-sequence count of finished items names the work-group that walks it.
-__device__ __forceinline__ uint64_t argmax_key(float v, int i) {
-  if (v == 0.f) v = 0.f;  // -0 and +0 compare equal, as in the row scan
-  uint32_t u = __float_as_uint(v);
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (0xffffffffu - (uint32_t)i);
-}
+// Greedy batches whose B (N + 1) rows fit the LDS list: every work-group derives the batch's
+// needed rows -- the root and the rows with a usable child, by the rule of the sequence facts --
+// as one ascending list and streams whole rows of it: its first rows by its index, the rest taken
+// from a device-wide counter, each early enough (two slices before it is needed, or two rows ahead for rows of fewer than three
+// slices) that the counter's round trip hides behind the loads.  A
+// work-group streams its rows' slices with the next slice's loads in flight across row
+// boundaries, stores each row's argmax (lowest id on ties) as its result word and counts the
+// row for its sequence; the work-group that counts a sequence's last needed row walks it at
+// once, while the stream goes on, so the walks spread over the launch instead of piling up
+// at its end.  A walk that stops on a row without children (never streamed) hands that row
+// back: it joins the work-group's own stream, and its argmax becomes the bonus token.  No
+// work-group waits for another; a timeout word already set when the launch starts is reported
+// as status 7 by every walk and cleared by the last work-group.
 template <typename T, bool ALIGNED, int TH>
 __device__ __forceinline__ void greedy_batch_body(const sv_accept_args& a, const AccWs& ws, const sv_commit_args& cm,
                                                   int32_t has_cm, AccShared<T, TH, false>& S) {
   constexpr int E = Piece<T>::E, NK = Piece<T>::NK, NW = TH / 64;
   constexpr int SL = ac_slice<T, TH>();
   constexpr bool aligned = ALIGNED;
+  constexpr int END = -1;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int N = a.N, V = a.V, B = a.B, R = N + 1, rows = B * R;
+  const int N = a.N, V = a.V, B = a.B, R = N + 1, rows = B * R, BN = B * N, Dm = a.max_depth;
+  uint32_t* const queue = ws.err + 2;  // list positions handed out by the counter so far
   Red& red = S.red;
+  const int ns = (V + SL - 1) / SL;  // slices per row
+  const int D = ns >= 3 ? 1 : 2;     // rows taken ahead of the one being streamed
+  // work-group g starts on list positions g (and g + grid when D = 2); the counter hands out
+  // the positions from D * grid on
+  const uint32_t G = gridDim.x, first = (uint32_t)D * G;
   // ---- the needed rows of the batch
   for (int x = t; x < rows; x += TH) S.bflag[x] = x % R == 0;
-  if (t == 0) S.walkq[0] = 0;
   __syncthreads();
-  for (int n = t; n < B * N; n += TH) {
-    const int b = n / N, i = n - b * N;
-    const int pr = a.parents[n], tok = a.tokens[n];
-    if (pr < -1 || pr >= N || tok < 0 || tok >= V) continue;
-    int dep = 0;
-    if (a.depth) {
-      dep = a.depth[n];
-    } else {  // nodes on the root path within max_depth, through in-range parents
-      int cur = i, cnt = 1;
-      for (int st = 0; st < SV_MAX_DEPTH; ++st) {
-        const int p = a.parents[(int64_t)b * N + cur];
-        if (p == -1) { dep = cnt; break; }
-        if (p < 0 || p >= N || cnt >= a.max_depth) break;
-        ++cnt;
-        cur = p;
-      }
+  constexpr int PU = 4;  // nodes per thread whose loads are issued together
+  for (int n0 = 0; n0 < BN; n0 += TH * PU) {
+    int pr[PU], tk[PU], dp[PU];
+#pragma unroll
+    for (int u = 0; u < PU; ++u) {
+      const int n = n0 + u * TH + t;
+      pr[u] = n < BN ? a.parents[n] : -2;
+      tk[u] = n < BN ? a.tokens[n] : -1;
+      dp[u] = n < BN && a.depth ? a.depth[n] : 0;
     }
-    if (dep > 0) S.bflag[b * R + pr + 1] = 1;  // every writer stores the same value
+#pragma unroll
+    for (int u = 0; u < PU; ++u) {
+      const int n = n0 + u * TH + t;
+      if (n >= BN || pr[u] < -1 || pr[u] >= N || tk[u] < 0 || tk[u] >= V) continue;
+      const int b = n / N;
+      int dep = dp[u];
+      if (!a.depth) {  // nodes on the root path within max_depth, through in-range parents
+        int cur = n - b * N, cnt = 1;
+        for (int st = 0; st < SV_MAX_DEPTH; ++st) {
+          const int p = a.parents[(int64_t)b * N + cur];
+          if (p == -1) { dep = cnt; break; }
+          if (p < 0 || p >= N || cnt >= Dm) break;
+          ++cnt;
+          cur = p;
+        }
+      }
+      if (dep > 0) S.bflag[b * R + pr[u] + 1] = 1;  // every writer stores the same value
+    }
   }
   __syncthreads();
   // ascending list: thread t scans a contiguous chunk, a block scan places it
@@ -859,184 +883,331 @@ __device__ __forceinline__ void greedy_batch_body(const sv_accept_args& a, const
   for (int x = x0; x < x1; ++x)
     if (S.bflag[x]) S.blist[pos++] = (uint16_t)x;
   __syncthreads();
-  // ---- this work-group's items: (row, slice) pairs i0 .. i1 - 1 of the list
-  const int ns = (V + SL - 1) / SL;
-  const int items = total * ns;
-  const int per = (items + (int)gridDim.x - 1) / (int)gridDim.x;
-  const int i0 = min(items, (int)blockIdx.x * per), i1 = min(items, i0 + per);
+  // every sequence has its root row in the list: its rows are bseq[b] .. bseq[b + 1] - 1
+  for (int p = t; p < total; p += TH) {
+    const int b = S.blist[p] / R;
+    if (p == 0 || S.blist[p - 1] / R != b) S.bseq[b] = (uint16_t)p;
+  }
+  if (t == 0) {
+    S.bseq[B] = (uint16_t)total;
+    S.ring[0] = blockIdx.x < (uint32_t)total ? (int)blockIdx.x : END;
+    S.ring[1] = D == 2 && blockIdx.x + G < (uint32_t)total ? (int)(blockIdx.x + G) : END;
+    S.q_ended = first >= (uint32_t)total;
+    S.q_inj = END;
+  }
+  __syncthreads();
+  // ---- this work-group's stream: rows j = 0, 1, ... (S.ring[j & 3]), ns slices each
+  int e_cur = S.ring[0];
+  if (e_cur == END) return;  // uniform
   const T* target = (const T*)a.target_logits;
-  auto row_of = [&](int i) { return __builtin_amdgcn_readfirstlane((int)S.blist[i / ns]); };
-  auto load_item = [&](int i, uint4 (&r)[NK]) {
-    load_pieces<T, TH>(target + (int64_t)row_of(i) * V, (i % ns) * SL, V, aligned, t, r);
+  auto row_of = [&](int e) {
+    return __builtin_amdgcn_readfirstlane((e & AC_LEAFROW) ? (e & 8191) : (int)S.blist[e]);
+  };
+  auto load_item = [&](int e, int s, uint4 (&r)[NK]) {
+    load_pieces<T, TH>(target + (int64_t)row_of(e) * V, s * SL, V, aligned, t, r);
   };
   float best = -FLT_MAX;
   int arg = 0x7fffffff;
-  int first = i0;  // first item of the current row in this range
-  auto consume = [&](const uint4 (&raw)[NK], int i) {
-    const int s0 = (i % ns) * SL;
+  int j = 0, s = 0;
+  uint32_t taken = ~0u;  // (thread 0) the counter's answer for row j + D, ~0: none asked
+  const int s_take = D == 1 ? ns - 3 : 0, s_put = D == 1 ? ns - 2 : ns - 1;
+  // (thread 0) row j + D's entry into its ring slot, published by the next barrier
+  auto put = [&]() {
+    int e = S.q_pend;
+    if (taken != ~0u) {
+      e = taken < (uint32_t)total ? (int)taken : END;
+      if (e == END) S.q_ended = 1;
+    }
+    S.ring[(j + D) & 3] = e;
+  };
+  auto step = [&](uint4 (&cur)[NK], uint4 (&nxt)[NK]) -> bool {
+    if (s == s_take && t == 0) {  // row j + D: a handed-back leaf row first, else the counter
+      taken = ~0u;
+      S.q_pend = S.q_inj;
+      if (S.q_inj != END) S.q_inj = END;
+      else if (!S.q_ended) taken = first + add_u32(queue, 1u);  // its value is needed only at slice s_put
+    }
+    int e_nx = e_cur, s_nx = s + 1;
+    if (s_nx == ns) {
+      e_nx = S.ring[(j + 1) & 3];
+      s_nx = 0;
+    }
+    if (e_nx != END) load_item(e_nx, s_nx, nxt);
+    // this slice
+    const int s0 = s * SL;
 #pragma unroll
     for (int k = 0; k < NK; ++k) {
       float x[E];
-      unpack16<T>(raw[k], x);
+      unpack16<T>(cur[k], x);
       const int v = piece_v<T, TH>(s0, k, t);
 #pragma unroll
       for (int e = 0; e < E; ++e)
         if (v + e < V && x[e] > best) { best = x[e]; arg = v + e; }
     }
-    if (i % ns == ns - 1 || i == i1 - 1) {  // the row ends here, or the range does (uniform)
-      block_argmax<TH>(best, arg, red);
-      const int row = row_of(i);
-      if (t == 0) {
-        __hip_atomic_fetch_max(&ws.res[row], argmax_key(best, arg), __ATOMIC_RELAXED, AGENT);
-        mem_complete();  // the key has been combined before the count below
-        const int b = row / R;
-        int cnt = 0;
-        for (int x = b * R; x < (b + 1) * R; ++x) cnt += S.bflag[x];
-        const uint32_t n = (uint32_t)(i - first + 1);
-        if (add_u32(&ws.seqdone[b], n) + n == (uint32_t)(cnt * ns)) S.walkq[1 + S.walkq[0]++] = b;
+    if (s_nx != 0) {
+      if (D == 1 && s == s_put) {
+        if (t == 0) put();
+        __syncthreads();
       }
-      first = i + 1;
-      best = -FLT_MAX;
-      arg = 0x7fffffff;
+      ++s;
+      return true;
     }
+    // ---- the end of row j
+    if (D == 2 && t == 0) put();  // published by the reduction's barriers
+    block_argmax<TH>(best, arg, red);
+    const int row = row_of(e_cur), b = row / R;
+    if (e_cur & AC_LEAFROW) {  // a walk's leaf stop row: its argmax is the bonus token
+      if (t == 0) a.out_tokens[(int64_t)b * (Dm + 1) + ((e_cur >> 13) & 31)] = arg;
+    } else {
+      if (t == 0) {
+        st_u64(&ws.res[row], res_word(-1, arg));
+        mem_complete();  // the result is visible before the count below
+        const uint32_t need = (uint32_t)(S.bseq[b + 1] - S.bseq[b]);
+        S.s_last = add_u32(&ws.seqdone[b], 1u) + 1 == need;
+      }
+      __syncthreads();
+      if (S.s_last) {  // uniform: the sequence's last row, walk it now
+        seq_facts<TH>(a, seq_fetch(a, b), S.si);
+        const int left = greedy_walk<T, TH, true>(a, ws, cm, has_cm, b, aligned, S);
+        if (left != END && t == 0) {  // the first ring slot still free, else the next take
+          if (S.ring[(j + 1) & 3] == END) S.ring[(j + 1) & 3] = left;
+          else if (D == 2 && S.ring[(j + 2) & 3] == END) S.ring[(j + 2) & 3] = left;
+          else S.q_inj = left;
+        }
+        __syncthreads();
+      }
+    }
+    best = -FLT_MAX;
+    arg = 0x7fffffff;
+    if (e_nx == END) {  // nothing was in flight: a walk may just have handed back a row
+      e_nx = S.ring[(j + 1) & 3];
+      if (e_nx == END) return false;
+      load_item(e_nx, 0, nxt);
+    }
+    ++j;
+    s = 0;
+    e_cur = e_nx;
+    return true;
   };
-  const int nitems = i1 - i0;
   uint4 r0[NK], r1[NK];
-  if (nitems > 0) load_item(i0, r0);
-  for (int i = 0; i < nitems; i += 2) {
-    if (i + 1 < nitems) load_item(i0 + i + 1, r1);
-    consume(r0, i0 + i);
-    if (i + 1 >= nitems) break;
-    if (i + 2 < nitems) load_item(i0 + i + 2, r0);
-    consume(r1, i0 + i + 1);
-  }
-  __syncthreads();
-  // ---- the walks of the sequences whose last item this work-group counted
-  const int nw = S.walkq[0];
-  for (int q = 0; q < nw; ++q) {
-    const int b = S.walkq[1 + q];
-    seq_facts<TH>(a, seq_fetch(a, b), S.si);
-    greedy_walk<T, TH, true>(a, ws, cm, has_cm, b, aligned, S);
-    __syncthreads();
+  load_item(e_cur, 0, r0);
+  while (step(r0, r1) && step(r1, r0)) {
   }
 }
 
-// Greedy batches of at least AC_STREAM_ROWS logits rows: wps work-groups per sequence stream
-// the rows the walk needs -- the root and the rows with a usable child -- work-group j of
-// sequence b taking every wps-th of them in ascending order, so rows without a usable child
-// cost no work-group at all.  The work-group's row slices form one stream with the next
-// slice's loads in flight across row boundaries; each row's argmax (lowest id on ties: a
-// thread visits its entries in ascending id, and the block reduction keeps the lower index)
-// is one block reduction at its last slice.  The work-group that counts a sequence's last
-// needed row walks it.  No work-group waits for another; a timeout word already set when the
-// launch starts is reported as status 7 by every walk and cleared by the last work-group.
-constexpr int AC_ROWS_WGS = 512;  // work-groups aimed at: two 512-thread work-groups per CU
-// the part of greedy_rows_body for sequence b, work-group j of its wps
+// This thread's argmax (lowest id on ties) over the slices s0, s0 + step, ... of a logits row,
+// with up to DEPTH slices in flight; a thread visits its entries in ascending id.
+template <typename T, int TH, int DEPTH>
+__device__ __forceinline__ void argmax_slices(const T* row, int V, bool aligned, int t, int s0, int step, float& best,
+                                              int& arg) {
+  constexpr int E = Piece<T>::E, NK = Piece<T>::NK, SL = ac_slice<T, TH>();
+  const int ns = (V + SL - 1) / SL;
+  const int n = s0 < ns ? (ns - s0 + step - 1) / step : 0;  // slices of this work-group
+  uint4 r[DEPTH][NK];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+    if (d < n) load_pieces<T, TH>(row, (s0 + d * step) * SL, V, aligned, t, r[d]);
+  for (int g = 0; g < n; g += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      if (g + d < n) {
+        const int sv = (s0 + (g + d) * step) * SL;
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+          float x[E];
+          unpack16<T>(r[d][k], x);
+          const int v = piece_v<T, TH>(sv, k, t);
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            if (v + e < V && x[e] > best) { best = x[e]; arg = v + e; }
+        }
+        if (g + d + DEPTH < n) load_pieces<T, TH>(row, (s0 + (g + d + DEPTH) * step) * SL, V, aligned, t, r[d]);
+      }
+    }
+  }
+}
+
+// Greedy batches of at least AC_CHAIN_B sequences: a group of G work-groups per sequence
+// follows the accepted path itself, row after row -- the root row's argmax names the children
+// that match, their rows name theirs, and so on -- so it reads only the rows of nodes whose
+// whole root path matches, plus the stop row for its bonus, rather than every row with a usable
+// child.  All children that match one row (equal sibling tokens) are followed, breadth first,
+// since the accepted node is the deepest match (lowest index on ties).  A CU streams only a few
+// tens of GB/s by itself, so a row is split over the G members (slices rank, rank + G, ...,
+// all in flight at once), whose (maximum, index) pairs meet in one exchange per row; every
+// member then takes the same decisions.  Member 0 writes the outputs and commits the accepted
+// path when asked to.  A timeout of an exchange, or a timeout word already set when the launch
+// starts, is reported as status 7 (the word is cleared by the last work-group).
+constexpr int AC_CHAIN_B = 16;
+constexpr int AC_CHAIN_G = 4;
+// members per sequence: the batch's groups about fill the 256 CUs, each member holding a slice
+inline int chain_G(const sv_accept_args& a, int TH) {
+  const int64_t sl = (int64_t)TH * (a.logits_dtype == SV_BF16 ? 64 : 32);  // entries per slice
+  const int ns = (int)((a.V + sl - 1) / sl);
+  int g = 1;
+  while (g * 2 <= AC_CHAIN_G && g * 2 <= ns && (int64_t)a.B * g * 2 <= 256) g *= 2;
+  return g;
+}
 template <typename T, bool ALIGNED, int TH>
-__device__ __forceinline__ void greedy_rows_seq(const sv_accept_args& a, int wps, int b, int j, const AccWs& ws,
-                                                const sv_commit_args& cm, int32_t has_cm,
-                                                AccShared<T, TH, false>& S) {
-  constexpr int E = Piece<T>::E, NK = Piece<T>::NK, NW = TH / 64;
-  constexpr int SL = ac_slice<T, TH>();
+__device__ __forceinline__ void greedy_chain_seq(const sv_accept_args& a, int b, int rank, int G, XSlot* gslots,
+                                                 const AccWs& ws, const sv_commit_args& cm, int32_t has_cm,
+                                                 AccShared<T, TH, false>& S) {
   constexpr bool aligned = ALIGNED;
+  constexpr int CD = ALIGNED ? 4 : 1;  // slices in flight (rows off 16 bytes load entry by entry: a register each)
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int N = a.N, V = a.V;
+  const int N = a.N, V = a.V, Dm = a.max_depth;
   SeqInfo& si = S.si;
   Red& red = S.red;
   seq_facts<TH>(a, seq_fetch(a, b), si);
-  // the needed rows, ascending
-  const bool need = t <= N && (t == 0 || si.haskid[t] != 0);
-  const uint64_t m = __ballot(need);
-  if (lane == 0) si.wcount[wv] = __popcll(m);
-  __syncthreads();
-  int off = 0, cnt = 0;
-  for (int k = 0; k < NW; ++k) {
-    if (k < wv) off += si.wcount[k];
-    cnt += si.wcount[k];
+  for (int x = t; x < N; x += TH) S.bflag[x] = 0;  // node matched, and every node above it did
+  if (t == 0) {
+    S.s_xc = 0;
+    S.rows[0] = 0;  // rows to follow: the root row first
+    S.q_head = 0;
+    S.q_tail = 1;
   }
-  if (need) S.rows[off + __popcll(m & ((1ull << lane) - 1ull))] = (int16_t)t;
   __syncthreads();
-  const int mine = cnt > j ? (cnt - j + wps - 1) / wps : 0;  // rows j, j + wps, ... of the list
-  const int ns = (V + SL - 1) / SL;                            // slices per row
-  const int items = mine * ns;
-  const T* target = (const T*)a.target_logits + (int64_t)b * (N + 1) * V;
-  auto row_of = [&](int i) { return __builtin_amdgcn_readfirstlane((int)S.rows[j + (i / ns) * wps]); };
-  auto load_item = [&](int i, uint4 (&r)[NK]) {
-    load_pieces<T, TH>(target + (int64_t)row_of(i) * V, (i % ns) * SL, V, aligned, t, r);
-  };
-  float best = -FLT_MAX;
-  int arg = 0x7fffffff;
-  auto consume = [&](const uint4 (&raw)[NK], int i) {
-    const int s0 = (i % ns) * SL;
-#pragma unroll
-    for (int k = 0; k < NK; ++k) {
-      float x[E];
-      unpack16<T>(raw[k], x);
-      const int v = piece_v<T, TH>(s0, k, t);
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        if (v + e < V && x[e] > best) { best = x[e]; arg = v + e; }
-    }
-    if (i % ns == ns - 1) {  // the row's last slice (uniform)
-      block_argmax<TH>(best, arg, red);
-      if (t == 0) st_u64(&ws.res[(int64_t)b * (N + 1) + row_of(i)], res_word(-1, arg));
+  const T* rows = (const T*)a.target_logits + (int64_t)b * (N + 1) * V;
+  uint32_t xtag = 0;  // exchanges so far (the same on every member)
+  // the argmax of row r over the whole group (lowest id on ties), in every thread
+  auto row_argmax = [&](int r) {
+    float best = -FLT_MAX;
+    int arg = 0x7fffffff;
+    argmax_slices<T, TH, CD>(rows + (int64_t)r * V, V, aligned, t, rank, G, best, arg);
+    block_argmax<TH>(best, arg, red);
+    if (G > 1) {
+      exchange<TH>(gslots, G, rank, ++xtag, 2, S.xv, ws.err, nullptr, &S.s_xc, __float_as_uint(best), (uint32_t)arg);
       best = -FLT_MAX;
       arg = 0x7fffffff;
+      for (int k = 0; k < G; ++k) {  // members hold disjoint slices: the larger value, then the lower id
+        const float v = __uint_as_float(S.xv[k][0]);
+        const int i = (int)S.xv[k][1];
+        if (v > best || (v == best && i < arg)) { best = v; arg = i; }
+      }
     }
+    return arg;
   };
-  uint4 r0[NK], r1[NK];
-  if (items > 0) load_item(0, r0);
-  for (int i = 0; i < items; i += 2) {
-    if (i + 1 < items) load_item(i + 1, r1);
-    consume(r0, i);
-    if (i + 1 >= items) break;
-    if (i + 2 < items) load_item(i + 2, r0);
-    consume(r1, i + 1);
+  int A = 0, stop_row = 0;
+  bool settled = false;  // the accepted node is known
+  for (;;) {
+    const int h = S.q_head;
+    if (h == S.q_tail) {  // uniform
+      if (settled) break;
+      settled = true;
+      // the accepted node: the deepest match, lowest index on ties
+      int key = -1;
+      if (t < N && S.bflag[t]) key = (si.dep[t] << 9) | (511 - t);
+      {
+        float kv = (float)key;
+        int ki = key;
+        block_argmax<TH>(kv, ki, red);
+        key = (int)kv;
+      }
+      if (key >= 0) {
+        A = key >> 9;
+        const int stop = 511 - (key & 511);
+        stop_row = stop + 1;
+        if (t == 0) {
+          int node = stop;
+          for (int k = A - 1; k >= 0; --k) { si.path[k] = node; node = si.par[node]; }
+        }
+      }
+      // a followed stop row's argmax is known; one without usable children is read last
+      if (stop_row != 0 && !si.haskid[stop_row]) {
+        if (t == 0) S.rows[S.q_tail++] = (int16_t)stop_row;
+        __syncthreads();
+      }
+      continue;
+    }
+    const int r = S.rows[h];
+    const int arg = row_argmax(r);
+    // the usable children of row r whose token is its argmax; those with usable children of
+    // their own are followed next (each row is queued at most once: a node has one parent)
+    const bool m = t < N && si.usable[t] && si.par[t] + 1 == r && si.tok[t] == arg;
+    if (m) S.bflag[t] = 1;
+    const bool push = m && si.haskid[t + 1];
+    const uint64_t pm = __ballot(push);
+    if (lane == 0) si.wcount[wv] = __popcll(pm);
+    __syncthreads();
+    int off = S.q_tail, add = 0;
+    for (int k = 0; k < TH / 64; ++k) {
+      if (k < wv) off += si.wcount[k];
+      add += si.wcount[k];
+    }
+    if (push) S.rows[off + __popcll(pm & ((1ull << lane) - 1ull))] = (int16_t)(t + 1);
+    __syncthreads();  // every thread has read q_tail and the counts
+    if (t == 0) {
+      S.rowarg[r] = arg;
+      S.q_head = h + 1;
+      S.q_tail += add;
+    }
+    __syncthreads();
   }
-  if (mine == 0) return;  // uniform
-  mem_complete();  // this thread's row-result stores (if any) have completed
+  const int bonus = S.rowarg[stop_row];
+  if (t == 0) S.s_to = ld_u32(ws.err) != 0;  // set before the launch, or by a wait of this call that expired
   __syncthreads();
+  if (rank != 0) return;
+  const bool to = S.s_to != 0;
   if (t == 0) {
-    const uint32_t old = add_u32(&ws.seqdone[b], (uint32_t)mine);
-    S.s_last = old + (uint32_t)mine == (uint32_t)si.nlive;
+    a.accept_len[b] = A;
+    a.num_out[b] = A + 1;
+    a.stop_row[b] = stop_row;
+    a.status[b] = to ? SV_SEQ_TIMEOUT : (si.bad_token ? SV_SEQ_TOKEN : 0);
   }
-  __syncthreads();
-  if (S.s_last) greedy_walk<T, TH>(a, ws, cm, has_cm, b, aligned, S);
+  if (t < Dm) a.accept_rows[(int64_t)b * Dm + t] = t < A ? si.path[t] + 1 : 0;
+  if (t <= Dm)
+    a.out_tokens[(int64_t)b * (Dm + 1) + t] = t < A ? a.tokens[(int64_t)b * N + si.path[t]] : (t == A ? bonus : 0);
+  // the accepted path into the cache (nothing after a timeout: the path may be wrong)
+  if (has_cm) svc::walker_commit(cm, b, to ? 0 : A, si.path);
 }
-template <typename T, bool ALIGNED, int TH>
-__device__ __forceinline__ void greedy_rows_body(const sv_accept_args& a, int wps, const AccWs& ws,
-                                                 const sv_commit_args& cm, int32_t has_cm,
-                                                 AccShared<T, TH, false>& S) {
+
+// G: members per sequence of a chain (chain_G; the grid is chain_grid), unused for the list
+template <typename T, bool ALIGNED, int TH, bool CHAIN>
+__device__ __forceinline__ void greedy_rows_body(const sv_accept_args& a, int G, const AccWs& ws, const sv_commit_args& cm,
+                                                 int32_t has_cm, AccShared<T, TH, false>& S) {
   const int t = threadIdx.x;
-  if (wps == 0) {  // one list for the whole batch
-    greedy_batch_body<T, ALIGNED, TH>(a, ws, cm, has_cm, S);
+  if constexpr (CHAIN) {
+    // work-groups are dispatched round-robin over the 8 XCDs: the members of a sequence's group
+    // are consecutive work-groups of one XCD
+    const int bid = (int)blockIdx.x, xcd = bid % 8, idx = bid / 8;
+    const int b = (idx / G) * 8 + xcd, rank = idx % G;
+    if (b < a.B) {
+      XSlot* gslots = ws.xs + (int64_t)b * G * 2;
+      greedy_chain_seq<T, ALIGNED, TH>(a, b, rank, G, gslots, ws, cm, has_cm, S);
+      if (G > 1) {  // the group's last member leaves its exchange slots and exit count zeroed
+        mem_complete();
+        __syncthreads();
+        if (t == 0) S.s_last = add_u32(ws.gexit + b, 1u) + 1 == (uint32_t)G;
+        __syncthreads();
+        if (S.s_last) {
+          for (int i = t; i < G * 2 * AC_XW; i += TH) st_u64(&gslots[i / AC_XW].w[i % AC_XW], 0ull);
+          if (t == 0) st_u32(ws.gexit + b, 0u);
+        }
+      }
+    }
   } else {
-    const int b = (int)(blockIdx.x / (unsigned)wps), j = (int)(blockIdx.x % (unsigned)wps);
-    if (b < a.B) greedy_rows_seq<T, ALIGNED, TH>(a, wps, b, j, ws, cm, has_cm, S);
+    greedy_batch_body<T, ALIGNED, TH>(a, ws, cm, has_cm, S);  // one list for the batch
   }
-  // every work-group counts out; the last one leaves the timeout word zeroed
+  // every work-group counts out; the last one leaves the timeout word and the counters zeroed
   mem_complete();
   __syncthreads();
   if (t == 0 && add_u32(ws.err + 1, 1u) + 1 == gridDim.x) {
     st_u32(ws.err, 0u);
     st_u32(ws.err + 1, 0u);
+    st_u32(ws.err + 2, 0u);
   }
 }
-// work-groups per sequence of greedy_rows_body, or 0 for one list over the batch (grid:
-// rows_grid); a work-group's range then ends at most AC_BLIST / AC_ROWS_WGS + 2 rows, so at
-// most that many walks, which AC_WALKQ holds
-inline int rows_wps(const sv_accept_args& a) {
-  if ((int64_t)a.B * (a.N + 1) <= AC_BLIST) return 0;
-  const int w = (AC_ROWS_WGS + a.B - 1) / a.B;
-  return w < 1 ? 1 : (w > a.N + 1 ? a.N + 1 : w);
-}
-static_assert(AC_BLIST / AC_ROWS_WGS + 2 <= AC_WALKQ, "walk queue");
-inline int64_t rows_grid(const sv_accept_args& a, int TH, int wps) {
-  if (wps > 0) return (int64_t)a.B * wps;
-  const int64_t slices = (a.V + (int64_t)TH * (a.logits_dtype == SV_BF16 ? 64 : 32) - 1) /
-                         ((int64_t)TH * (a.logits_dtype == SV_BF16 ? 64 : 32));
-  const int64_t items = (int64_t)a.B * (a.N + 1) * slices;  // an upper bound of the list's items
-  return items < AC_ROWS_WGS ? items : AC_ROWS_WGS;
+// the greedy form of a batch: chains for AC_CHAIN_B sequences or more, else one list
+inline bool rows_chain(const sv_accept_args& a) { return a.B >= AC_CHAIN_B; }
+// chains: whole groups of 8 sequences (one per XCD) of G members each
+inline int64_t chain_grid(const sv_accept_args& a, int G) { return ((int64_t)a.B + 7) / 8 * 8 * G; }
+static_assert((AC_CHAIN_B - 1) * (SV_MAX_N + 1) <= AC_BLIST, "a batch below AC_CHAIN_B fits the list");
+static_assert(AC_BLIST <= 8192 && SV_MAX_DEPTH < 32, "leaf stream entries: batch row in 13 bits, depth in 5");
+// one list over the batch: as many work-groups as the CUs hold at once (per_cu on each of the
+// 256 CUs), fewer when the batch has fewer rows
+inline int64_t rows_grid(const sv_accept_args& a, int per_cu) {
+  const int64_t rows = (int64_t)a.B * (a.N + 1), wgs = 256 * per_cu;  // rows: an upper bound of the list's
+  return rows < wgs ? rows : wgs;
 }
 
 // The resolution of one row slice by one work-group of a row group (see the file comment of
@@ -1659,9 +1830,9 @@ int groups_G_th(const sv_accept_args& a, int TH) {
   return G < 1 ? 1 : G;
 }
 int groups_G(const sv_accept_args& a, bool aligned) { return groups_G_th(a, acc_threads(a, aligned)); }
-// Greedy batches of at least AC_STREAM_ROWS rows resolve each row with one work-group that streams
-// the whole row (no exchange, a quarter of the work-groups to dispatch); smaller batches split a
-// row over a group of G work-groups for parallelism.
+// Greedy batches of at least AC_STREAM_ROWS rows read each row they need with one work-group
+// (no exchange: a chain per sequence, or the batch's needed rows as one list); smaller batches
+// split a row over a group of G work-groups for parallelism.
 constexpr int64_t AC_STREAM_ROWS = 512;
 int launch_G(const sv_accept_args& a, int TH) {
   if (a.mode == SV_GREEDY && (int64_t)a.B * (a.N + 1) >= AC_STREAM_ROWS) return 1;
@@ -1681,12 +1852,14 @@ WsLayout ws_layout_g(const sv_accept_args& a, int G, int regions) {
   size_t o = 0;
   l.gexit = o; o = up(o + NG * 4);
   l.seqdone = o; o = up(o + (size_t)a.B * 4);
-  l.err = o; o = up(o + 8);
+  l.err = o; o = up(o + 16);
   l.res = o; o = up(o + (size_t)a.B * (a.N + 1) * sizeof(uint64_t));
   l.frontier = o; o = up(o + (size_t)a.B * 4);
   l.cancel = o; o = up(o + (size_t)a.B * 4);
   l.seqexit = o; o = up(o + (size_t)a.B * 4);
-  l.xs = o; o = up(o + NG * (size_t)G * 2 * sizeof(XSlot));
+  // (also the greedy chains' slots: AC_CHAIN_G members per sequence)
+  const size_t nxs = std::max(NG * (size_t)G, (size_t)a.B * AC_CHAIN_G) * 2;
+  l.xs = o; o = up(o + nxs * sizeof(XSlot));
   l.total = o;
   return l;
 }
