@@ -62,11 +62,17 @@ def algorithmic_bytes(w, acc):
         attn += int(((L + w.block_size - 1) // w.block_size).sum()) * 4
     n_t = 2 if w.mode == "stochastic" else 1
     rows = 0
-    for b in range(B):
-        par = w.parents[b]
-        needed = {0} | set((par[par >= 0] + 1).tolist())
-        stop = int(acc["stop_row"][b])
-        rows += len(needed) * n_t + (0 if stop in needed else 1)
+    if w.mode == "greedy":
+        # the accepted path's rows, the stop row included: where the path goes next is known
+        # only from the argmax of the row before, and no other row decides the result (sibling
+        # tokens that tie would add the rows below the tie)
+        rows = int((acc["accept_len"].astype(np.int64) + 1).sum())
+    else:  # every row of a node with a child (and the draft rows in mode 1), plus the stop row
+        for b in range(B):
+            par = w.parents[b]
+            needed = {0} | set((par[par >= 0] + 1).tolist())
+            stop = int(acc["stop_row"][b])
+            rows += len(needed) * n_t + (0 if stop in needed else 1)
     accept = rows * V * el
     A = acc["accept_len"].astype(np.int64)
     if w.tree_in_cache:  # the in-place commit moves only rows not already at their position

@@ -91,6 +91,12 @@ typedef int32_t sv_status;
  * rejected with SV_ERR_INVALID_ARGUMENT while the stream is being captured).
  * Without it (performance mode) a call only enqueues work. */
 #define SV_FLAG_VALIDATE 1u
+/* SV_FLAG_ROW_LIST (sv_accept only): greedy batches of at least 512 logits rows whose B*(N+1)
+ * rows fit 4352 resolve every row that has a usable child -- the batch's needed rows streamed
+ * as one list -- instead of following each sequence's accepted path row by row (which reads
+ * only the path's rows and the stop row, and which the call picks by itself when the list
+ * would read many bytes).  The results are the same; other calls ignore the flag. */
+#define SV_FLAG_ROW_LIST 2u
 
 /* commit modes ([EP] sec. 2: length-based or path-index-based commit) */
 #define SV_COMMIT_PATH 0
@@ -289,7 +295,7 @@ typedef struct sv_accept_args {
    * writes new_len, so new_len must not alias prefix_len while anything that reads prefix_len
    * (sv_tree_attention) may still run beside it. */
   const struct sv_commit_args* commit;
-  uint32_t flags;   /* 0 or SV_FLAG_VALIDATE */
+  uint32_t flags;   /* 0, or SV_FLAG_VALIDATE and/or SV_FLAG_ROW_LIST */
 } sv_accept_args;
 size_t sv_accept_workspace(const sv_accept_args* args);
 sv_status sv_accept(const sv_accept_args* args, void* stream);

@@ -29,14 +29,16 @@ def out_f64(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def run_step(w, stages=("mask", "attention", "accept", "commit")):
-    """Run the chosen stages of one verification step on cuda:0; return numpy results."""
+def run_step(w, stages=("mask", "attention", "accept", "commit"), acc_flags=0):
+    """Run the chosen stages of one verification step on cuda:0; return numpy results.
+    acc_flags: extra sv_accept flags (SV_FLAG_ROW_LIST)."""
     import torch
     from tree_verification_sv_amd.step import VerifyStep
     print(f"[gpu] {w.name} B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} D={w.D} V={w.V} paged={w.paged} "
           f"L=[{int(w.prefix_len.min())},{int(w.prefix_len.max())}] mode={w.mode} stages={stages}", flush=True)
     dev = W.to_device(w, "cuda:0")
     step = VerifyStep(W.step_inputs(w, dev))
+    step._acc.flags |= acc_flags
     if "mask" in stages:
         step.build_mask()
     if "attention" in stages:

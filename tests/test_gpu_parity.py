@@ -235,32 +235,42 @@ def test_chi_square_gpu(shape):
     assert chi.pvalue > 0.01, chi
 
 
-@pytest.mark.parametrize("B,N,V", [(20, 32, 3001), (16, 40, 40000), (24, 24, 300), (600, 3, 4096), (2, 255, 1000),
-                                   (40, 40, 100000), (48, 24, 98311), (8, 255, 98305), (6, 200, 98311),
-                                   (12, 100, 40000), (1100, 3, 1024), (300, 15, 70000)])
-def test_greedy_row_streamer(B, N, V):
-    """Greedy batches of at least 512 rows, each row read by one work-group.  From 16 sequences
-    on, a work-group per sequence follows its accepted path row by row; below that, whole rows of
-    the batch's needed-row list are streamed, the first by work-group index and the rest taken
-    from a device-wide counter (two rows ahead for rows of one or two slices, one row ahead from
-    three slices on), several rows per work-group, leaf stop rows handed back into the walker's
+@pytest.mark.parametrize("B,N,V,form", [(20, 32, 3001, "auto"), (20, 32, 3001, "list"), (16, 40, 40000, "auto"),
+                                        (16, 40, 40000, "list"), (24, 24, 300, "auto"), (600, 3, 4096, "auto"),
+                                        (600, 3, 4096, "list"), (2, 255, 1000, "auto"), (40, 40, 100000, "auto"),
+                                        (40, 40, 100000, "list"), (48, 24, 98311, "auto"), (48, 24, 98311, "list"),
+                                        (8, 255, 98305, "auto"), (8, 255, 98305, "list"), (6, 200, 98311, "auto"),
+                                        (6, 200, 98311, "list"), (12, 100, 40000, "auto"),
+                                        (1100, 3, 1024, "auto"), (300, 15, 70000, "auto")])
+def test_greedy_row_streamer(B, N, V, form):
+    """Greedy batches of at least 512 rows, each row read whole.  Where the batch's needed rows
+    are many bytes (form "auto": (40, 40, 100000), (48, 24, 98311), (8, 255, 98305),
+    (6, 200, 98311), and the batches beyond the list), a group of work-groups per sequence follows
+    its accepted path row by row; otherwise, or with SV_FLAG_ROW_LIST (form "list"), whole rows of the batch's
+    needed-row list are streamed, the first by work-group index and the rest taken from a
+    device-wide counter (two rows ahead for rows of one or two slices, one row ahead from three
+    slices on), several rows per work-group, leaf stop rows handed back into the walker's
     stream.  Rows off 16 bytes, vocabularies smaller than one slice, wide trees."""
+    import tree_verification_sv_amd as sv
     w = W.config(3, B=B, N=N, V=V, L=(16, 80))
     assert w.B * (w.N + 1) >= 512 and w.mode == "greedy"
-    print(f"[gpu] greedy streamer B={w.B} N={w.N} V={w.V}", flush=True)
-    r = run_step(w, ("mask", "accept"))
+    print(f"[gpu] greedy streamer B={w.B} N={w.N} V={w.V} form={form}", flush=True)
+    r = run_step(w, ("mask", "accept"), acc_flags=sv.SV_FLAG_ROW_LIST if form == "list" else 0)
     compare_accept(r["acc"], oracle.accept(w), allow_flagged=False)
-
 
 @pytest.mark.parametrize("B,N,V", [(32, 20, 40000), (40, 20, 33333), (8, 80, 70000), (10, 60, 50001)])
 def test_greedy_rows_fp32(B, N, V):
     """fp32 logits in both greedy forms of batches of at least 512 rows: per-sequence chains
-    (B >= 16) and the streamed row list (B < 16, several slices per row), rows on and off 16 bytes."""
+    (the first two shapes) and the streamed row list (the last two, and SV_FLAG_ROW_LIST),
+    several slices per row, rows on and off 16 bytes."""
+    import tree_verification_sv_amd as sv
     seed = 31 + B
     par = np.stack([W.tree_random_recursive(seed, N, 6, offset=b * N) for b in range(B)])
     w = W.build_workload("greedy-f32", B, N, 8, 2, 64, V, "f32", "greedy", par, np.full(B, 64), max_depth=6,
                          seed=seed, logit_sigma=3.0, token_rule="uniform", plant=W.plant_pairs(seed, par),
                          need_draft=False)
-    print(f"[gpu] greedy fp32 B={B} N={N} V={V}", flush=True)
-    r = run_step(w, ("mask", "accept"))
-    compare_accept(r["acc"], oracle.accept(w), allow_flagged=False)
+    ref = oracle.accept(w)
+    for flags in (0, sv.SV_FLAG_ROW_LIST):
+        print(f"[gpu] greedy fp32 B={B} N={N} V={V} flags={flags}", flush=True)
+        r = run_step(w, ("mask", "accept"), acc_flags=flags)
+        compare_accept(r["acc"], ref, allow_flagged=False)

@@ -146,7 +146,7 @@ def _ws_err_offset(B, N):
 
 
 @pytest.mark.parametrize("cfg,over", [(2, dict(B=2, L=64, V=5003)), (3, dict(B=4, L=(16, 80), V=3001)),
-                                      (3, dict(B=16, L=(16, 80), V=70000)), (3, dict(B=8, N=80, L=(16, 80), V=40000)),
+                                      (3, dict(B=16, L=(16, 80))), (3, dict(B=8, N=80, L=(16, 80), V=40000)),
                                       (4, dict(B=6, L=64, V=2999))])
 def test_timeout_word_reports_status_7_then_recovers(cfg, over):
     """A timeout word set before the call: every sequence reports status 7, the workspace is left

@@ -25,6 +25,7 @@ SV_GREEDY, SV_STOCHASTIC, SV_TOPK_DRAFT, SV_THRESHOLD = 0, 1, 2, 3
 _MODES = {"greedy": SV_GREEDY, "stochastic": SV_STOCHASTIC, "topk": SV_TOPK_DRAFT, "threshold": SV_THRESHOLD}
 SV_COMMIT_PATH, SV_COMMIT_LENGTH = 0, 1
 SV_FLAG_VALIDATE = 1
+SV_FLAG_ROW_LIST = 2
 SV_SEQ_NONFINITE = 8
 
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -86,10 +86,10 @@ __global__ void __launch_bounds__(512, (2 * rows_wgs_per_cu<T, ALIGNED>()))
 }
 // ... and of AC_CHAIN_B sequences or more: a chain per sequence, G work-groups per row
 template <typename T, bool ALIGNED>
-__global__ void __launch_bounds__(512, 2) k_accept_chain(sv_accept_args a, int32_t G, AccWs ws, sv_commit_args cm,
-                                                         int32_t has_cm) {
-  __shared__ AccShared<T, 512, false> S;
-  greedy_rows_body<T, ALIGNED, 512, true>(a, G, ws, cm, has_cm, S);
+__global__ void __launch_bounds__(AC_CHAIN_TH, 2)
+    k_accept_chain(sv_accept_args a, int32_t G, AccWs ws, sv_commit_args cm, int32_t has_cm) {
+  __shared__ AccShared<T, AC_CHAIN_TH, false> S;
+  greedy_rows_body<T, ALIGNED, AC_CHAIN_TH, true>(a, G, ws, cm, has_cm, S);
 }
 
 // SV_FLAG_VALIDATE: one work-group per logits row (target rows, then draft rows in mode 1) looks
@@ -139,9 +139,9 @@ void launch_accept(int TH, dim3 grid, hipStream_t st, const sv_accept_args& a, i
   if constexpr (M == SV_GREEDY) {
     if (G == 1) {  // rows read whole: a chain per sequence, or the batch's needed rows as one list
       if (rows_chain(a)) {
-        const int CG = chain_G(a, 512);
-        hipLaunchKernelGGL((k_accept_chain<T, AL>), dim3((unsigned)chain_grid(a, CG)), dim3(512), 0, st, a, CG, ws, cm,
-                           has_cm);
+        const int CG = chain_G(a);
+        hipLaunchKernelGGL((k_accept_chain<T, AL>), dim3((unsigned)chain_grid(a, CG)), dim3(AC_CHAIN_TH), 0, st, a, CG, ws,
+                           cm, has_cm);
       } else {
         hipLaunchKernelGGL((k_accept_rows<T, AL>), dim3((unsigned)rows_grid(a, rows_wgs_per_cu<T, AL>())), dim3(512), 0, st,
                            a, ws, cm, has_cm);
@@ -193,7 +193,7 @@ extern "C" sv_status sv_accept(const sv_accept_args* args, void* stream) {
   if (a.logits_dtype != SV_F32 && a.logits_dtype != SV_BF16) return SV_ERR_UNSUPPORTED;
   if (a.mode == SV_THRESHOLD && (!(a.temperature > 0.f) || !(a.threshold >= 0.f && a.threshold <= 1.f)))
     return SV_ERR_INVALID_ARGUMENT;
-  if (a.flags & ~(uint32_t)SV_FLAG_VALIDATE) return SV_ERR_INVALID_ARGUMENT;
+  if (a.flags & ~(uint32_t)(SV_FLAG_VALIDATE | SV_FLAG_ROW_LIST)) return SV_ERR_INVALID_ARGUMENT;
   if (a.B == 0) return SV_OK;
   // modes 0, 1 and 2 read neither mask output when depth is NULL (depths come from the parents)
   const bool mask_free = a.mode != SV_THRESHOLD && !a.depth;

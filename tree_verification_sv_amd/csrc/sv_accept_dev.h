@@ -996,17 +996,24 @@ __device__ __forceinline__ void greedy_batch_body(const sv_accept_args& a, const
 }
 
 // This thread's argmax (lowest id on ties) over the slices s0, s0 + step, ... of a logits row,
-// with up to DEPTH slices in flight; a thread visits its entries in ascending id.
+// with up to DEPTH slices in flight; a thread visits its entries in ascending id.  has_pre: the
+// first slice's loads were issued already, into `pre`.
 template <typename T, int TH, int DEPTH>
 __device__ __forceinline__ void argmax_slices(const T* row, int V, bool aligned, int t, int s0, int step, float& best,
-                                              int& arg) {
+                                              int& arg, bool has_pre, const uint4 (&pre)[Piece<T>::NK]) {
   constexpr int E = Piece<T>::E, NK = Piece<T>::NK, SL = ac_slice<T, TH>();
   const int ns = (V + SL - 1) / SL;
   const int n = s0 < ns ? (ns - s0 + step - 1) / step : 0;  // slices of this work-group
   uint4 r[DEPTH][NK];
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d)
-    if (d < n) load_pieces<T, TH>(row, (s0 + d * step) * SL, V, aligned, t, r[d]);
+  for (int d = 0; d < DEPTH; ++d) {
+    if (d == 0 && has_pre) {
+#pragma unroll
+      for (int k = 0; k < NK; ++k) r[0][k] = pre[k];
+    } else if (d < n) {
+      load_pieces<T, TH>(row, (s0 + d * step) * SL, V, aligned, t, r[d]);
+    }
+  }
   for (int g = 0; g < n; g += DEPTH) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
@@ -1039,13 +1046,16 @@ __device__ __forceinline__ void argmax_slices(const T* row, int V, bool aligned,
 // path when asked to.  A timeout of an exchange, or a timeout word already set when the launch
 // starts, is reported as status 7 (the word is cleared by the last work-group).
 constexpr int AC_CHAIN_B = 16;
-constexpr int AC_CHAIN_G = 4;
-// members per sequence: the batch's groups about fill the 256 CUs, each member holding a slice
-inline int chain_G(const sv_accept_args& a, int TH) {
-  const int64_t sl = (int64_t)TH * (a.logits_dtype == SV_BF16 ? 64 : 32);  // entries per slice
+constexpr int AC_CHAIN_TH = 256;  // threads per chain work-group (512 / AC_CHAIN_TH work-groups per CU)
+constexpr int AC_CHAIN_G = 8;     // members per sequence at most
+// members per sequence: the batch's groups about fill the CUs (256 of them, each holding
+// 512 / AC_CHAIN_TH members at once), each member holding a slice
+inline int chain_G(const sv_accept_args& a) {
+  const int64_t sl = (int64_t)AC_CHAIN_TH * (a.logits_dtype == SV_BF16 ? 64 : 32);  // entries per slice
   const int ns = (int)((a.V + sl - 1) / sl);
+  const int64_t room = 256 * (512 / AC_CHAIN_TH);
   int g = 1;
-  while (g * 2 <= AC_CHAIN_G && g * 2 <= ns && (int64_t)a.B * g * 2 <= 256) g *= 2;
+  while (g * 2 <= AC_CHAIN_G && g * 2 <= ns && (int64_t)a.B * g * 2 <= room) g *= 2;
   return g;
 }
 template <typename T, bool ALIGNED, int TH>
@@ -1058,7 +1068,12 @@ __device__ __forceinline__ void greedy_chain_seq(const sv_accept_args& a, int b,
   const int N = a.N, V = a.V, Dm = a.max_depth;
   SeqInfo& si = S.si;
   Red& red = S.red;
-  seq_facts<TH>(a, seq_fetch(a, b), si);
+  const T* rows = (const T*)a.target_logits + (int64_t)b * (N + 1) * V;
+  // the root row is read first in any case: its first slice's loads go out with the sequence's
+  uint4 pre[Piece<T>::NK];
+  const SeqRaw sr = seq_fetch(a, b);
+  load_pieces<T, TH>(rows, rank * ac_slice<T, TH>(), V, aligned, t, pre, rank * ac_slice<T, TH>() < V);
+  seq_facts<TH>(a, sr, si);
   for (int x = t; x < N; x += TH) S.bflag[x] = 0;  // node matched, and every node above it did
   if (t == 0) {
     S.s_xc = 0;
@@ -1067,13 +1082,13 @@ __device__ __forceinline__ void greedy_chain_seq(const sv_accept_args& a, int b,
     S.q_tail = 1;
   }
   __syncthreads();
-  const T* rows = (const T*)a.target_logits + (int64_t)b * (N + 1) * V;
   uint32_t xtag = 0;  // exchanges so far (the same on every member)
   // the argmax of row r over the whole group (lowest id on ties), in every thread
   auto row_argmax = [&](int r) {
     float best = -FLT_MAX;
     int arg = 0x7fffffff;
-    argmax_slices<T, TH, CD>(rows + (int64_t)r * V, V, aligned, t, rank, G, best, arg);
+    const T* row = rows + (int64_t)r * V;
+    argmax_slices<T, TH, CD>(row, V, aligned, t, rank, G, best, arg, r == 0, pre);
     block_argmax<TH>(best, arg, red);
     if (G > 1) {
       exchange<TH>(gslots, G, rank, ++xtag, 2, S.xv, ws.err, nullptr, &S.s_xc, __float_as_uint(best), (uint32_t)arg);
@@ -1197,11 +1212,20 @@ __device__ __forceinline__ void greedy_rows_body(const sv_accept_args& a, int G,
     st_u32(ws.err + 2, 0u);
   }
 }
-// the greedy form of a batch: chains for AC_CHAIN_B sequences or more, else one list
-inline bool rows_chain(const sv_accept_args& a) { return a.B >= AC_CHAIN_B; }
+// The greedy form of a batch: chains when the list cannot hold the batch's rows, else (or with
+// SV_FLAG_ROW_LIST) the list when it would read few bytes -- about half the batch's rows under
+// 48 MB from AC_CHAIN_B sequences on, under 96 MB below -- and chains otherwise.  The bounds
+// are where the two forms took about the same time on MI355X: a chain costs its longest path's
+// rows one after another (a slice load and an exchange each), the list its bytes plus a few
+// dependent steps at either end.
+inline bool rows_chain(const sv_accept_args& a) {
+  if ((int64_t)a.B * (a.N + 1) > AC_BLIST) return true;
+  if (a.flags & SV_FLAG_ROW_LIST) return false;
+  const double half = (double)a.B * (a.N + 1) / 2 * (double)a.V * (a.logits_dtype == SV_BF16 ? 2 : 4);
+  return half >= (a.B >= AC_CHAIN_B ? 48.0 : 96.0) * (1 << 20);
+}
 // chains: whole groups of 8 sequences (one per XCD) of G members each
 inline int64_t chain_grid(const sv_accept_args& a, int G) { return ((int64_t)a.B + 7) / 8 * 8 * G; }
-static_assert((AC_CHAIN_B - 1) * (SV_MAX_N + 1) <= AC_BLIST, "a batch below AC_CHAIN_B fits the list");
 static_assert(AC_BLIST <= 8192 && SV_MAX_DEPTH < 32, "leaf stream entries: batch row in 13 bits, depth in 5");
 // one list over the batch: as many work-groups as the CUs hold at once (per_cu on each of the
 // 256 CUs), fewer when the batch has fewer rows
