@@ -390,7 +390,10 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--no-overlap", action="store_true",
                     help="run the four stages back to back on one stream (default: acceptance and commit on a "
-                         "side stream beside the attention, forked after the mask)")
+                         "side stream beside the attention, forked after the mask, except for stochastic wide "
+                         "trees of more than 1024 rows)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="the side-stream form also for stochastic wide trees of more than 1024 rows")
     ap.add_argument("--attention-side", action="store_true",
                     help="overlapped step with the attention on the side stream and acceptance + commit on the "
                          "launch stream")
@@ -474,7 +477,11 @@ def main():
                 s_.one_launch(False)
     stream = torch.cuda.current_stream()
 
-    ov = not args.no_overlap
+    # Stochastic wide trees of many rows run on one stream: most of their acceptance grid is
+    # row groups that leave at their start (the rows of walks that have already finished), and
+    # dispatched beside the attention they slow both (outcome-tree-8b, MI355X: 3.13 ms per step
+    # overlapped against 2.58 ms on one stream).
+    ov = not args.no_overlap and (args.overlap or not (wide and rows > ONE_LAUNCH_MAX_ROWS_WIDE))
     run = lambda i: steps[i % R].run(overlap=ov, attention_side=args.attention_side)  # noqa: E731
     for i in range(args.warmup):
         run(i)

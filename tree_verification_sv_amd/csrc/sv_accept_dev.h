@@ -1271,10 +1271,17 @@ __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, 
   const int64_t gslot = grp;  // exchange slots and exit counter of the group
   XSlot* gslots = ws.xs + gslot * G * 2;
   uint32_t xtag = 0;  // exchanges of this group so far (identical on every member)
-  const int64_t item = grp;
+  // the row this group resolves (index b (N + 1) + r).  Stochastic wide trees take the rows
+  // row-major over the batch -- row r of every sequence before row r + 1 -- so that the rows
+  // near the roots, where the walks run, resolve first; once a walk has finished, the groups of
+  // its sequence's remaining rows leave at their start.  Elsewhere sequence-major.
+  const bool wide = STO && N > 2 * a.max_depth;
+  const int64_t nrows = (int64_t)a.B * (N + 1);
+  const int64_t item = wide && grp < nrows ? (int64_t)(grp % a.B) * (N + 1) + grp / a.B : grp;
   const int s0 = rank * ac_slice<T, TH>();  // this work-group's slice of the vocabulary
   if (t == 0) s_xc = 0;
   bool live_row = false;
+  bool gone = false;  // (wide trees) the walk had finished when this work-group started
   if (item < (int64_t)a.B * (N + 1)) {
     // uniform, and kept in scalar registers so that the slice loads take a scalar resource
     const int b = __builtin_amdgcn_readfirstlane((int)(item / (N + 1)));
@@ -1288,7 +1295,7 @@ __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, 
     // resolved here -- the walker draws the bonus of such a stop row itself (leaf_bonus).
     // Chains and narrow trees, where nearly every row is on the path, resolve every row and
     // walk once after the last one.
-    const bool incr = STO && N > 2 * a.max_depth;
+    const bool incr = wide;
     const bool wleaf = !PREFETCH && incr;  // stop rows without children: drawn by the walker
     uint32_t* cancel = incr ? &ws.cancel[b] : nullptr;
     uint32_t cx0 = 0u;  // the sequence's walk already finished (a late work-group)
@@ -1300,9 +1307,15 @@ __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, 
     if constexpr (STO && PREFETCH) load_pieces<T, TH>(prow, s0, V, aligned, t, rp);
     asm volatile("" : "+v"(sr.tok), "+v"(sr.par), "+v"(sr.dep), "+v"(cx0));  // nothing uses them before this point
     if (cx0) s_xc = 1;
-    seq_facts<TH>(a, sr, si);
-    // the same on every member
-    live_row = row_live(a, si, r) && (!wleaf || r == 0 || si.haskid[r] != 0);
+    if (incr) {  // uniform: a finished walk needs nothing more from this row
+      __syncthreads();
+      gone = s_xc != 0;
+    }
+    if (!gone) {
+      seq_facts<TH>(a, sr, si);
+      // the same on every member
+      live_row = row_live(a, si, r) && (!wleaf || r == 0 || si.haskid[r] != 0);
+    }
     if constexpr (STO && !PREFETCH) load_pieces<T, TH>(prow, s0, V, aligned, t, rp, live_row && !s_xc);
     if (live_row && !s_xc) {
       row_kids<TH>(N, r, si);
@@ -1810,8 +1823,8 @@ __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, 
   }
   __syncthreads();
   // (a member that left early on a finished walk may have exchanged less than the others,
-  // so the slots of every live row are cleared)
-  if (s_last && (xtag > 0 || live_row))
+  // so the slots of every live row are cleared, and of every row a member left at its start)
+  if (s_last && (xtag > 0 || live_row || gone))
     for (int i = t; i < G * 2 * AC_XW; i += TH) st_u64(&gslots[i / AC_XW].w[i % AC_XW], 0ull);
   if (s_claim) {  // stochastic: the sequence's row results, frontier, cancel flag and exit count
     for (int x = t; x <= N; x += TH) st_u64(&ws.res[(int64_t)bq * (N + 1) + x], 0ull);

@@ -15,7 +15,10 @@ end (a fork/join that HIP graph capture records as a DAG).  The attention is
 issued first by default (``accept_first=False``): measured on MI355X, the step
 is shorter when the attention's work-groups take the compute units first and
 the acceptance fills them as they free up.  With the tree rows in the cache the
-commit moves rows the attention reads, so it follows the join.
+commit moves rows the attention reads, so it follows the join.  Stochastic
+acceptance over wide trees of many rows is faster without the fork: most of
+its row groups leave at their start once their sequence's walk has finished,
+and those dispatches beside the attention slow both.
 """
 from __future__ import annotations
 
