@@ -1240,7 +1240,10 @@ inline int64_t rows_grid(const sv_accept_args& a, int per_cu) {
 // PREFETCH: the target slice is loaded before the sequence facts that say whether the row is
 // needed (its latency then overlaps theirs); otherwise after them, and only for needed rows.
 // Either choice gives the same results; prefetching pays where nearly every row is resolved.
-template <typename T, int MODE, bool ALIGNED, int TH, bool PREFETCH>
+// ROWMAJOR: stochastic wide trees take their rows row-major over the batch, and row groups of
+// finished walks leave at their start (the separate acceptance launch; the one-launch step,
+// which holds few rows, keeps sequence-major rows).
+template <typename T, int MODE, bool ALIGNED, int TH, bool PREFETCH, bool ROWMAJOR = true>
 __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, const AccWs& ws,
                                             const sv_commit_args& cm, int32_t has_cm, const AccRole role,
                                             AccShared<T, TH, MODE != SV_GREEDY>& S) {
@@ -1271,13 +1274,14 @@ __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, 
   const int64_t gslot = grp;  // exchange slots and exit counter of the group
   XSlot* gslots = ws.xs + gslot * G * 2;
   uint32_t xtag = 0;  // exchanges of this group so far (identical on every member)
-  // the row this group resolves (index b (N + 1) + r).  Stochastic wide trees take the rows
-  // row-major over the batch -- row r of every sequence before row r + 1 -- so that the rows
-  // near the roots, where the walks run, resolve first; once a walk has finished, the groups of
-  // its sequence's remaining rows leave at their start.  Elsewhere sequence-major.
+  // the row this group resolves (index b (N + 1) + r).  Stochastic wide trees (ROWMAJOR) take
+  // the rows row-major over the batch -- row r of every sequence before row r + 1 -- so that
+  // the rows near the roots, where the walks run, resolve first; once a walk has finished, the
+  // groups of its sequence's remaining rows leave at their start.  Elsewhere sequence-major.
   const bool wide = STO && N > 2 * a.max_depth;
   const int64_t nrows = (int64_t)a.B * (N + 1);
-  const int64_t item = wide && grp < nrows ? (int64_t)(grp % a.B) * (N + 1) + grp / a.B : grp;
+  const int64_t item =
+      ROWMAJOR && wide && grp < nrows ? (int64_t)(grp % a.B) * (N + 1) + grp / a.B : (int64_t)grp;
   const int s0 = rank * ac_slice<T, TH>();  // this work-group's slice of the vocabulary
   if (t == 0) s_xc = 0;
   bool live_row = false;
@@ -1307,7 +1311,7 @@ __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, 
     if constexpr (STO && PREFETCH) load_pieces<T, TH>(prow, s0, V, aligned, t, rp);
     asm volatile("" : "+v"(sr.tok), "+v"(sr.par), "+v"(sr.dep), "+v"(cx0));  // nothing uses them before this point
     if (cx0) s_xc = 1;
-    if (incr) {  // uniform: a finished walk needs nothing more from this row
+    if (ROWMAJOR && incr) {  // uniform: a finished walk needs nothing more from this row
       __syncthreads();
       gone = s_xc != 0;
     }

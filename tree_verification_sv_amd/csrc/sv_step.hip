@@ -92,7 +92,7 @@ __global__ void __launch_bounds__(MF_THREADS, 1) k_verify_step(StepKArgs k) {
   } else if (bid < k.r_merge) {
     // ---- acceptance
     const AccRole role{bid - k.r_acc, k.nacc, (k.ac.N + 1) * k.G};
-    accept_body<T, MODE, true, TH, false>(k.ac, k.G, k.ws, k.cm, k.has_cm, role, s_aux.acc);
+    accept_body<T, MODE, true, TH, false, false>(k.ac, k.G, k.ws, k.cm, k.has_cm, role, s_aux.acc);
   } else {
     // ---- merge of the attention splits
     const int pos = bid - k.r_merge, nb = k.r_end - k.r_merge;
