@@ -43,11 +43,12 @@ __global__ void __launch_bounds__(MF_THREADS, 2) k_attn_mfma(sv_attn_args a, Att
   __shared__ __attribute__((aligned(1024))) unsigned char kvA[Tile<D>::BUF];
   __shared__ __attribute__((aligned(1024))) unsigned char kvB[Tile<D>::BUF];
   __shared__ __attribute__((aligned(1024))) unsigned char qsb[Tile<D>::QROWS * Tile<D>::ROWB];
+  __shared__ int32_t s_bt[AT_BT_MAX];
   // XCD-aware block order: consecutive logical ids land on the same XCD
   const int nb = gridDim.x;
   const int bid = blockIdx.x;
   const int lid = (nb % 8 == 0) ? (bid % 8) * (nb / 8) + bid / 8 : bid;
-  attn_mfma_body<D>(a, p, lid, kvA, kvB, qsb, nullptr, 0, nullptr);
+  attn_mfma_body<D>(a, p, lid, kvA, kvB, qsb, nullptr, 0, nullptr, s_bt);
 }
 
 // merge split partials: one wave per output row (b, node, head).  Every load

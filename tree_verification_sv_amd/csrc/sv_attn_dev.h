@@ -185,12 +185,15 @@ __device__ __forceinline__ void step_ancestors(const int32_t* __restrict__ paren
 // reads of another).  derive_parents (nullable): the ancestor sets of the query nodes are
 // derived from this parent array into aux (>= 9 KB of LDS) by the rule of sv_build_tree_mask
 // instead of being read from a.anc_bits.  p.arrive (nullable): after writing its partial the
-// work-group counts in on its unit's counter with a release.  Every thread calls it.
+// work-group counts in on its unit's counter with a release.  bt_lds (nullable, AT_BT_MAX
+// entries of LDS): on the paged path the block ids of the work-group's key range are read into
+// it once, so that no tile load waits for a block-table read.  Every thread calls it.
+constexpr int AT_BT_MAX = 512;  // block ids held in LDS: key ranges of up to 8192 tokens
 template <int D>
 __device__ __forceinline__ void attn_mfma_body(const sv_attn_args& a, const AttnPlan& p, int lid, unsigned char* kvA,
                                                unsigned char* kvB, unsigned char* qsb,
                                                const int32_t* __restrict__ derive_parents, int max_depth,
-                                               unsigned char* aux) {
+                                               unsigned char* aux, int32_t* bt_lds = nullptr) {
   using TL = Tile<D>;
   constexpr int QB = MF_QB;             // 32-row query blocks per wave
   constexpr int KT64 = TL::KT;
@@ -258,6 +261,21 @@ __device__ __forceinline__ void attn_mfma_body(const sv_attn_args& a, const Attn
     rkt = __builtin_amdgcn_make_buffer_rsrc((void*)(kt + (plane * (N + 1) + 1) * D), 0, (int)(N * ROWB), 0x00020000);
     rvt = __builtin_amdgcn_make_buffer_rsrc((void*)(vt + (plane * (N + 1) + 1) * D), 0, (int)(N * ROWB), 0x00020000);
   }
+  // paged prefix: the block ids of blocks bt0 .. of the key range, sanitised, into LDS
+  int bt0 = 0;
+  bool bt_pre = false;
+  if (a.paged && bt_lds && ntp > 0) {
+    bt0 = k0 / 16;
+    const int nbk = (k1 - 1) / 16 - bt0 + 1;
+    if (nbk <= AT_BT_MAX) {  // uniform
+      for (int i = t; i < nbk; i += MF_THREADS) {
+        const int id = a.block_table[(int64_t)b * a.max_blocks + bt0 + i];
+        bt_lds[i] = (id < 0 || id >= a.num_blocks) ? 0 : id;
+      }
+      __syncthreads();
+      bt_pre = true;
+    }
+  }
   auto load_tile = [&](int tile, unsigned char* kb) {
     const bool tree = tile >= ntp;
     int klast;
@@ -274,8 +292,13 @@ __device__ __forceinline__ void attn_mfma_body(const sv_attn_args& a, const Attn
         // the wave's rows lie in one 16-token block (RPW divides 16); past the end the
         // clamped key min(r, klast) = klast, so its block is the one used
         const int blk = (j0 + min(TL::RPW * w, klast)) / 16;
-        int id = __builtin_amdgcn_readfirstlane(a.block_table[(int64_t)b * a.max_blocks + blk]);
-        id = (id < 0 || id >= a.num_blocks) ? 0 : id;
+        int id;
+        if (bt_pre) {
+          id = __builtin_amdgcn_readfirstlane(bt_lds[blk - bt0]);
+        } else {
+          id = __builtin_amdgcn_readfirstlane(a.block_table[(int64_t)b * a.max_blocks + blk]);
+          id = (id < 0 || id >= a.num_blocks) ? 0 : id;
+        }
         soff = (uint32_t)(((int64_t)id * a.Hkv + g) * 16) * ROWB;
       } else {
         soff = (uint32_t)j0 * ROWB;
