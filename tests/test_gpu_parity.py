@@ -258,6 +258,40 @@ def test_greedy_row_streamer(B, N, V, form):
     r = run_step(w, ("mask", "accept"), acc_flags=sv.SV_FLAG_ROW_LIST if form == "list" else 0)
     compare_accept(r["acc"], oracle.accept(w), allow_flagged=False)
 
+def _tied_siblings(w):
+    """Every sibling of a node that matches its parent row's argmax gets that node's token, so
+    rows have several matching children: the accepted node is then the deepest match, lowest
+    index on ties, over several matching branches."""
+    rows = W.bf16_to_f32(w.target_logits) if w.target_logits.dtype == np.uint16 else w.target_logits
+    am = rows.argmax(axis=2)  # first index of the maximum: the lowest id on ties
+    tok = w.tokens.copy()
+    for b in range(w.B):
+        par = w.parents[b]
+        for i in range(w.N):
+            if tok[b, i] == am[b, par[i] + 1]:
+                tok[b, par == par[i]] = tok[b, i]
+    w.tokens = tok
+    return w
+
+
+@pytest.mark.parametrize("form", ["auto", "list"])
+def test_greedy_tied_siblings(form):
+    """Greedy batches whose rows have several matching children (equal sibling tokens): the
+    chains follow every matching child breadth first, the row list resolves every needed row;
+    both must give the oracle's deepest match with the lowest index."""
+    import tree_verification_sv_amd as sv
+    w = _tied_siblings(W.config(3, B=24, N=40, L=(16, 80)))
+    par = w.parents
+    multi = 0
+    for b in range(w.B):
+        rows = W.bf16_to_f32(w.target_logits[b]).argmax(axis=1)
+        m = w.tokens[b] == rows[par[b] + 1]
+        multi += sum(int(m[par[b] == p].sum()) > 1 for p in set(par[b].tolist()))
+    assert multi > 0, "no row with several matching children"
+    print(f"[gpu] greedy tied siblings B={w.B} N={w.N} form={form} rows with ties={multi}", flush=True)
+    r = run_step(w, ("mask", "accept"), acc_flags=sv.SV_FLAG_ROW_LIST if form == "list" else 0)
+    compare_accept(r["acc"], oracle.accept(w), allow_flagged=False)
+
 @pytest.mark.parametrize("B,N,V", [(32, 20, 40000), (40, 20, 33333), (8, 80, 70000), (10, 60, 50001)])
 def test_greedy_rows_fp32(B, N, V):
     """fp32 logits in both greedy forms of batches of at least 512 rows: per-sequence chains
