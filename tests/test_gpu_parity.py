@@ -292,6 +292,65 @@ def test_greedy_tied_siblings(form):
     r = run_step(w, ("mask", "accept"), acc_flags=sv.SV_FLAG_ROW_LIST if form == "list" else 0)
     compare_accept(r["acc"], oracle.accept(w), allow_flagged=False)
 
+def _fill_rows(w, picks):
+    """Overwrite logits rows: (b, r, kind) with kind 'ninf' (every entry -inf), 'nan' (every entry
+    NaN) or 'mixed' (NaN at the first 8 ids and every 1000th, the rest unchanged)."""
+    x = w.target_logits.copy()
+    bf = x.dtype == np.uint16
+    ninf, nan = (np.uint16(0xFF80), np.uint16(0x7FC0)) if bf else (np.float32(-np.inf), np.float32(np.nan))
+    for b, r, kind in picks:
+        if kind == "ninf":
+            x[b, r, :] = ninf
+        elif kind == "nan":
+            x[b, r, :] = nan
+        else:
+            x[b, r, :8] = nan
+            x[b, r, ::1000] = nan
+    w.target_logits = x
+    return w
+
+
+@pytest.mark.parametrize("form,over", [("groups", dict(B=6, N=32, V=70000)), ("list", dict(B=8, N=80, V=40000)),
+                                       ("chain", dict(B=24, N=40))])
+def test_greedy_nonfinite_rows(form, over):
+    """Greedy argmax over rows with -inf and NaN entries, as the oracle takes it: a NaN is never
+    the maximum and a row without an entry above -inf has argmax 0 -- for root rows and for the
+    stop rows of the unmodified batch, through row groups with exchanges, the row list and the
+    path chains."""
+    w = W.config(3, L=(16, 80), **over)
+    picks = [(0, 0, "ninf"), (1, 0, "nan"), (2, 0, "mixed")]
+    ref0 = oracle.accept(w)
+    kinds = ("ninf", "nan", "mixed")
+    picks += [(b, int(ref0["stop_row"][b]), kinds[b % 3]) for b in range(3, w.B)]
+    w = _fill_rows(w, picks)
+    ref = oracle.accept(w)
+    print(f"[gpu] greedy non-finite rows form={form} B={w.B} N={w.N} V={w.V}", flush=True)
+    r = run_step(w, ("mask", "accept"))
+    compare_accept(r["acc"], ref, allow_flagged=False)
+
+
+def test_threshold_bonus_nonfinite_stop_rows():
+    """Threshold acceptance whose stop rows have no usable children and hold -inf or NaN entries:
+    those rows enter no score, so the accepted paths stay, and the bonus is their argmax as the
+    oracle takes it (NaN never the maximum, id 0 when no entry is above -inf)."""
+    w = W.config(3, B=16, N=32, V=3001, L=(16, 80))
+    w.mode = "threshold"
+    w.threshold = float(np.float32(1e-3))
+    ref0 = oracle.accept(w)
+    kinds = ("ninf", "nan", "mixed")
+    picks = []
+    for b in range(w.B):
+        sr = int(ref0["stop_row"][b])
+        if sr > 0 and not (w.parents[b] == sr - 1).any():  # a stop row without children
+            picks.append((b, sr, kinds[len(picks) % 3]))
+    assert len(picks) >= 3, "too few leaf stop rows"
+    w = _fill_rows(w, picks)
+    ref = oracle.accept(w)
+    assert np.array_equal(ref["accept_len"], ref0["accept_len"])
+    print(f"[gpu] threshold non-finite stop rows: {len(picks)}", flush=True)
+    r = run_step(w, ("mask", "accept"))
+    compare_accept(r["acc"], ref, allow_flagged=True)
+
 @pytest.mark.parametrize("B,N,V", [(32, 20, 40000), (40, 20, 33333), (8, 80, 70000), (10, 60, 50001)])
 def test_greedy_rows_fp32(B, N, V):
     """fp32 logits in both greedy forms of batches of at least 512 rows: per-sequence chains

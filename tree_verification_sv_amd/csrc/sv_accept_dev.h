@@ -55,6 +55,11 @@ __device__ __forceinline__ bool res_ready(uint64_t v) { return (v >> 63) != 0; }
 __device__ __forceinline__ bool res_bad(uint64_t v) { return (v & AC_RES_BAD) != 0; }
 __device__ __forceinline__ int res_child(uint64_t v) { return (int)((v >> 32) & 0x3fffffffu) - 1; }
 __device__ __forceinline__ int res_token(uint64_t v) { return (int)(uint32_t)v; }
+// Greedy argmax scans start from (-inf, no id) and take an entry only when it is larger, so a
+// row without an entry above -inf (every entry -inf or NaN) ends with no id: its argmax is then
+// id 0, the lowest id of an all-equal row.
+constexpr int AC_NO_ID = 0x7fffffff;
+__device__ __forceinline__ int greedy_token(int arg) { return arg == AC_NO_ID ? 0 : arg; }
 constexpr uint32_t AC_FRONT_BUSY = 0xffffffffu;  // the walk's frontier is claimed by a work-group
 
 struct AccWs {        // workspace views
@@ -775,11 +780,11 @@ __device__ __forceinline__ int greedy_walk(const sv_accept_args& a, const AccWs&
       // leaf stop row: argmax by this work-group, one slice at a time with the next
       // slice's loads in flight (a thread visits its entries in ascending id)
       const T* srow = (const T*)a.target_logits + ((int64_t)b * (N + 1) + stop_row) * V;
-      float best = -FLT_MAX;
-      int arg = 0x7fffffff;
+      float best = -INFINITY;
+      int arg = AC_NO_ID;
       argmax_row<T, TH>(srow, V, aligned, t, best, arg);
       block_argmax<TH>(best, arg, red);
-      bonus = arg;
+      bonus = greedy_token(arg);
     }
   }
   __syncthreads();
@@ -906,8 +911,8 @@ __device__ __forceinline__ void greedy_batch_body(const sv_accept_args& a, const
   auto load_item = [&](int e, int s, uint4 (&r)[NK]) {
     load_pieces<T, TH>(target + (int64_t)row_of(e) * V, s * SL, V, aligned, t, r);
   };
-  float best = -FLT_MAX;
-  int arg = 0x7fffffff;
+  float best = -INFINITY;
+  int arg = AC_NO_ID;
   int j = 0, s = 0;
   uint32_t taken = ~0u;  // (thread 0) the counter's answer for row j + D, ~0: none asked
   const int s_take = D == 1 ? ns - 3 : 0, s_put = D == 1 ? ns - 2 : ns - 1;
@@ -955,6 +960,7 @@ __device__ __forceinline__ void greedy_batch_body(const sv_accept_args& a, const
     // ---- the end of row j
     if (D == 2 && t == 0) put();  // published by the reduction's barriers
     block_argmax<TH>(best, arg, red);
+    arg = greedy_token(arg);
     const int row = row_of(e_cur), b = row / R;
     if (e_cur & AC_LEAFROW) {  // a walk's leaf stop row: its argmax is the bonus token
       if (t == 0) a.out_tokens[(int64_t)b * (Dm + 1) + ((e_cur >> 13) & 31)] = arg;
@@ -977,8 +983,8 @@ __device__ __forceinline__ void greedy_batch_body(const sv_accept_args& a, const
         __syncthreads();
       }
     }
-    best = -FLT_MAX;
-    arg = 0x7fffffff;
+    best = -INFINITY;
+    arg = AC_NO_ID;
     if (e_nx == END) {  // nothing was in flight: a walk may just have handed back a row
       e_nx = S.ring[(j + 1) & 3];
       if (e_nx == END) return false;
@@ -1085,22 +1091,22 @@ __device__ __forceinline__ void greedy_chain_seq(const sv_accept_args& a, int b,
   uint32_t xtag = 0;  // exchanges so far (the same on every member)
   // the argmax of row r over the whole group (lowest id on ties), in every thread
   auto row_argmax = [&](int r) {
-    float best = -FLT_MAX;
-    int arg = 0x7fffffff;
+    float best = -INFINITY;
+    int arg = AC_NO_ID;
     const T* row = rows + (int64_t)r * V;
     argmax_slices<T, TH, CD>(row, V, aligned, t, rank, G, best, arg, r == 0, pre);
     block_argmax<TH>(best, arg, red);
     if (G > 1) {
       exchange<TH>(gslots, G, rank, ++xtag, 2, S.xv, ws.err, nullptr, &S.s_xc, __float_as_uint(best), (uint32_t)arg);
-      best = -FLT_MAX;
-      arg = 0x7fffffff;
+      best = -INFINITY;
+      arg = AC_NO_ID;
       for (int k = 0; k < G; ++k) {  // members hold disjoint slices: the larger value, then the lower id
         const float v = __uint_as_float(S.xv[k][0]);
         const int i = (int)S.xv[k][1];
         if (v > best || (v == best && i < arg)) { best = v; arg = i; }
       }
     }
-    return arg;
+    return greedy_token(arg);
   };
   int A = 0, stop_row = 0;
   bool settled = false;  // the accepted node is known
@@ -1328,15 +1334,15 @@ __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, 
       if (MODE == SV_GREEDY && G == 1) {
         // greedy, one work-group per row (large batches): the whole row streams through the
         // work-group one slice at a time with the next slice's loads in flight; no exchange
-        float best = -FLT_MAX;
-        int arg = 0x7fffffff;
+        float best = -INFINITY;
+        int arg = AC_NO_ID;
         argmax_row<T, TH>(prow, V, aligned, t, best, arg);
         block_argmax<TH>(best, arg, red);
-        if (t == 0) st_u64(&ws.res[item], res_word(-1, arg));
+        if (t == 0) st_u64(&ws.res[item], res_word(-1, greedy_token(arg)));
         done_by_me = 1;
       } else if constexpr (MODE == SV_GREEDY) {
-        float best = -FLT_MAX;
-        int arg = 0x7fffffff;
+        float best = -INFINITY;
+        int arg = AC_NO_ID;
         {
           load_pieces<T, TH>(prow, s0, V, aligned, t, rp);
 #pragma unroll
@@ -1353,10 +1359,10 @@ __device__ __forceinline__ void accept_body(const sv_accept_args& a, int32_t G, 
         exchange<TH>(gslots, G, rank, ++xtag, 2, xv, ws.err, nullptr, &s_xc, __float_as_uint(best), (uint32_t)arg);
         if (rank == 0) {
           if (t < 64) {  // wave 0: lane k takes member k's best; the butterfly keeps the lowest id on ties
-            float bv = lane < G ? __uint_as_float(xv[lane][0]) : -FLT_MAX;
-            int bi = lane < G ? (int)xv[lane][1] : 0x7fffffff;
+            float bv = lane < G ? __uint_as_float(xv[lane][0]) : -INFINITY;
+            int bi = lane < G ? (int)xv[lane][1] : AC_NO_ID;
             wave_argmax(bv, bi);
-            if (t == 0) st_u64(&ws.res[item], res_word(-1, bi));
+            if (t == 0) st_u64(&ws.res[item], res_word(-1, greedy_token(bi)));
           }
           done_by_me = 1;
         }

@@ -150,14 +150,16 @@ __device__ int row_argmax(const T* row, int V, uint64_t* s_key) {
 #pragma unroll
       for (int e = 0; e < EPC; ++e) {
         const int v = c * EPC + e;
-        if (v < V) {
-          const uint64_t kk = argmax_key(chunk_entry<T>(w[k], e), v);
+        const float x = chunk_entry<T>(w[k], e);
+        if (v < V && x == x) {  // a NaN is never the maximum (as in a scan that takes only larger entries)
+          const uint64_t kk = argmax_key(x, v);
           best = kk > best ? kk : best;
         }
       }
     }
   }
-  return key_id(block_max_key<NT>(best, s_key));
+  const uint64_t k = block_max_key<NT>(best, s_key);
+  return k == 0ull ? 0 : key_id(k);  // no entry but NaN: id 0
 }
 
 template <typename T, bool AL>
@@ -311,7 +313,7 @@ __global__ void __launch_bounds__(RW_THREADS) k_thr_walk(sv_accept_args a, int S
         const uint64_t k = argmax_key(pr[q].m, pr[q].arg);
         bk = k > bk ? k : bk;
       }
-    bonus = key_id(bk);
+    bonus = bk == 0ull ? 0 : key_id(bk);  // every entry -inf or NaN: id 0
   } else {
     bonus = row_argmax<T, AL, NT>((const T*)a.target_logits + ((int64_t)b * (N + 1) + srow) * V, V, s_key);
   }
