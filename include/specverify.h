@@ -92,10 +92,12 @@ typedef int32_t sv_status;
  * Without it (performance mode) a call only enqueues work. */
 #define SV_FLAG_VALIDATE 1u
 /* SV_FLAG_ROW_LIST (sv_accept only): greedy batches of at least 512 logits rows whose B*(N+1)
- * rows fit 4352 resolve every row that has a usable child -- the batch's needed rows streamed
- * as one list -- instead of following each sequence's accepted path row by row (which reads
- * only the path's rows and the stop row, and which the call picks by itself when the list
- * would read many bytes).  The results are the same; other calls ignore the flag. */
+ * rows fit 4352, and threshold batches (mode 3), resolve every row that has a usable child --
+ * greedy: the batch's needed rows streamed as one list; threshold: the statistics of every such
+ * row, then one walk per sequence -- instead of following each sequence's accepted (passing)
+ * paths row by row (which reads only those paths' rows and the stop row, and which the call
+ * picks by itself when the rows would be many bytes).  The results are the same; other calls
+ * ignore the flag. */
 #define SV_FLAG_ROW_LIST 2u
 
 /* commit modes ([EP] sec. 2: length-based or path-index-based commit) */

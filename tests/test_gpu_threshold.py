@@ -32,22 +32,22 @@ def _f32(x):
     return float(np.float32(x))
 
 
-def _gpu_threshold(w, tau, T, tokens=None, workspace=None):
+def _gpu_threshold(w, tau, T, tokens=None, workspace=None, row_list=False):
     import torch
     import tree_verification_sv_amd as sv
     dev = W.to_device(w, "cuda:0")
     tok = dev["tokens"] if tokens is None else torch.from_numpy(np.ascontiguousarray(tokens, np.int32)).cuda()
     m = sv.sv_build_tree_mask(dev["parents"], w.max_depth)
     out = sv.sv_accept(dev["parents"], tok, m["anc_bits"], m["depth"], dev["target_logits"], w.max_depth,
-                       mode="threshold", temperature=T, threshold=tau, workspace=workspace)
+                       mode="threshold", temperature=T, threshold=tau, workspace=workspace, row_list=row_list)
     torch.cuda.synchronize()
     return {k: to_np(v) for k, v in out.items()}
 
 
-def _check(w, tau, T, tokens=None):
+def _check(w, tau, T, tokens=None, row_list=False):
     tau, T = _f32(tau), _f32(T)
-    print(f"[gpu] threshold {w.name} B={w.B} N={w.N} V={w.V} tau={tau:.3g} T={T:.3g}", flush=True)
-    got = _gpu_threshold(w, tau, T, tokens)
+    print(f"[gpu] threshold {w.name} B={w.B} N={w.N} V={w.V} tau={tau:.3g} T={T:.3g} row_list={row_list}", flush=True)
+    got = _gpu_threshold(w, tau, T, tokens, row_list=row_list)
     ref = oracle.accept(w, mode="threshold", temperature=T, threshold=tau, tokens=tokens)
     nflag = compare_accept(got, ref)
     print(f"  accept_len {got['accept_len'].tolist()[:16]} flagged {nflag}")
@@ -82,8 +82,30 @@ def test_threshold_small(cfg):
 
 @pytest.mark.parametrize("cfg", [2, 3])
 def test_threshold_full_size(cfg):
+    """Full size: batched-paged-70b follows the passing paths (chains); with SV_FLAG_ROW_LIST, and
+    at eagle-static-8b, every needed row's statistics and one walk per sequence."""
     w = W.config(cfg)
     for tau in (1e-7, 1e-3):
+        for row_list in (False, True):
+            _check(w, tau, 1.0, row_list=row_list)
+
+
+@pytest.mark.parametrize("over", [dict(B=24, N=40), dict(B=16, N=32, V=100000), dict(B=8, N=120)])
+def test_threshold_chains(over):
+    """Threshold chains (rows of many bytes): groups of up to eight work-groups per sequence follow
+    the passing paths; several thresholds and a temperature, against the oracle."""
+    w = W.config(3, L=(16, 80), **over)
+    for T in (1.0, 0.7):
+        for tau in (1e-6, 1e-3, 0.05):
+            _check(w, tau, T)
+
+
+def test_threshold_chains_fp32():
+    """fp32 logits through the threshold chains (rows on 16 bytes, several slices per member)."""
+    par = np.stack([W.tree_random_recursive(5, 20, 6, offset=b * 20) for b in range(32)])
+    w = W.build_workload("fp32-thr", 32, 20, 4, 2, 64, 40000, "f32", "greedy", par, np.full(32, 8), max_depth=6,
+                         seed=5, logit_sigma=1.0, token_rule="uniform", plant=W.plant_pairs(5, par), need_draft=False)
+    for tau in (1e-6, 1e-3):
         _check(w, tau, 1.0)
 
 

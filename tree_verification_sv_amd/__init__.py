@@ -326,16 +326,19 @@ def sv_accept_workspace(args: sv_accept_args) -> int:
 
 def sv_accept(parents, tokens, anc_bits, depth, target_logits, max_depth, mode="greedy", draft_logits=None,
               u_accept=None, u_sample=None, temperature=1.0, outs=None, workspace=None, stream=None,
-              threshold=0.0, validate=False) -> dict:
+              threshold=0.0, validate=False, row_list=False) -> dict:
     """Speculative acceptance + bonus token; returns the dict of int32 device outputs.
 
     validate: reference mode (SV_FLAG_VALIDATE) -- logits rows are scanned for non-finite values and
-    the call waits and raises SpecVerifyError when a sequence reports a non-zero status."""
+    the call waits and raises SpecVerifyError when a sequence reports a non-zero status.
+    row_list: SV_FLAG_ROW_LIST -- greedy and threshold batches resolve every needed row instead of
+    following the accepted paths (same results)."""
     B = parents.shape[0]
     if outs is None:
         outs = accept_outputs(B, max_depth, parents.device)
     a = accept_args(parents, tokens, anc_bits, depth, target_logits, max_depth, mode, draft_logits, u_accept,
-                    u_sample, temperature, outs, threshold, SV_FLAG_VALIDATE if validate else 0)
+                    u_sample, temperature, outs, threshold,
+                    (SV_FLAG_VALIDATE if validate else 0) | (SV_FLAG_ROW_LIST if row_list else 0))
     need = sv_accept_workspace(a)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = _alloc_workspace(need, parents.device)

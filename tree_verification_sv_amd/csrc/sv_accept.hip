@@ -85,11 +85,12 @@ __global__ void __launch_bounds__(512, (2 * rows_wgs_per_cu<T, ALIGNED>()))
   greedy_rows_body<T, ALIGNED, 512, false>(a, 0, ws, cm, has_cm, S);
 }
 // ... and of AC_CHAIN_B sequences or more: a chain per sequence, G work-groups per row
-template <typename T, bool ALIGNED>
+// (THR: threshold acceptance, mode 3)
+template <typename T, bool ALIGNED, bool THR = false>
 __global__ void __launch_bounds__(AC_CHAIN_TH, 2)
     k_accept_chain(sv_accept_args a, int32_t G, AccWs ws, sv_commit_args cm, int32_t has_cm) {
   __shared__ AccShared<T, AC_CHAIN_TH, false> S;
-  greedy_rows_body<T, ALIGNED, AC_CHAIN_TH, true>(a, G, ws, cm, has_cm, S);
+  greedy_rows_body<T, ALIGNED, AC_CHAIN_TH, true, THR>(a, G, ws, cm, has_cm, S);
 }
 
 // SV_FLAG_VALIDATE: one work-group per logits row (target rows, then draft rows in mode 1) looks
@@ -179,7 +180,10 @@ sv_status validate_logits(const sv_accept_args& a, hipStream_t st) {
 
 extern "C" size_t sv_accept_workspace(const sv_accept_args* args) {
   if (!args || args->B < 1 || args->N < 1 || args->V < 1) return 0;
-  if (args->mode == SV_THRESHOLD) return sv_threshold_workspace(*args);
+  if (args->mode == SV_THRESHOLD) {  // either form (chains or row statistics): the larger
+    const size_t c = ws_layout(*args).total, r = sv_threshold_workspace(*args);
+    return c > r ? c : r;
+  }
   return ws_layout(*args).total;
 }
 
@@ -215,7 +219,25 @@ extern "C" sv_status sv_accept(const sv_accept_args* args, void* stream) {
   }
   if (a.mode == SV_THRESHOLD) {
     if ((uintptr_t)a.workspace % 256) return SV_ERR_INVALID_ARGUMENT;
-    const sv_status r = sv_threshold_launch(a, cm, has_cm, (hipStream_t)stream);
+    sv_status r;
+    // chains along the passing paths (k_accept_chain, mode 3) for rows on 16 bytes
+    const size_t esz = a.logits_dtype == SV_BF16 ? 2 : 4;
+    const bool al = ((size_t)a.V * esz) % 16 == 0 && ((uintptr_t)a.target_logits % 16) == 0;
+    if (al && thr_chain(a)) {
+      const WsLayout l = ws_layout(a);
+      if (a.workspace_bytes < l.total) return SV_ERR_INVALID_ARGUMENT;
+      const AccWs ws = ws_views(a.workspace, l);
+      const int CG = chain_G(a);
+      const dim3 grid((unsigned)chain_grid(a, CG)), block(AC_CHAIN_TH);
+      hipStream_t st = (hipStream_t)stream;
+      if (a.logits_dtype == SV_BF16)
+        hipLaunchKernelGGL((k_accept_chain<uint16_t, true, true>), grid, block, 0, st, a, CG, ws, cm, has_cm);
+      else
+        hipLaunchKernelGGL((k_accept_chain<float, true, true>), grid, block, 0, st, a, CG, ws, cm, has_cm);
+      r = sv_launch_status();
+    } else {
+      r = sv_threshold_launch(a, cm, has_cm, (hipStream_t)stream);
+    }
     if (r != SV_OK || !validate) return r;
     return validate_logits(a, (hipStream_t)stream);
   }

@@ -710,6 +710,7 @@ struct AccShared {
   int32_t q_inj;                         // ... a leaf stop row waiting for a ring slot
   int32_t q_pend, q_ended;               // ... row j + D's entry when not from the counter; counter run out
   int32_t rowarg[STO ? 1 : SV_MAX_N + 1];  // greedy chains: argmax of each followed row
+  double nscore[STO ? 1 : SV_MAX_N];       // threshold chains: score of each passing node
   int32_t q_head, q_tail;                  // ... rows to follow: S.rows[q_head .. q_tail)
 };
 
@@ -1182,8 +1183,210 @@ __device__ __forceinline__ void greedy_chain_seq(const sv_accept_args& a, int b,
   if (has_cm) svc::walker_commit(cm, b, to ? 0 : A, si.path);
 }
 
-// G: members per sequence of a chain (chain_G; the grid is chain_grid), unused for the list
-template <typename T, bool ALIGNED, int TH, bool CHAIN>
+// Threshold acceptance (mode 3) over batches whose needed rows are many bytes: the group of a
+// sequence follows the paths whose score stays at or above the threshold, row after row, as the
+// greedy chains do.  A followed row's statistics -- its maximum with the lowest id holding it and
+// Z = sum_v exp((l_v - m) / T) (fp32 exponentials, fp64 sums, rescaled when a thread's maximum
+// moves) -- meet in one exchange; each usable child of the row gets p = exp((l - M) / T) / Z and
+// the score of its parent times p, and the children at or above the threshold that have usable
+// children of their own are followed next.  So only the rows of passing nodes, and the stop row
+// for its bonus (its argmax, lowest id on ties), are read.
+template <typename T, bool ALIGNED, int TH>
+__device__ __forceinline__ void thr_chain_seq(const sv_accept_args& a, int b, int rank, int G, XSlot* gslots,
+                                              const AccWs& ws, const sv_commit_args& cm, int32_t has_cm,
+                                              AccShared<T, TH, false>& S) {
+  constexpr bool aligned = ALIGNED;
+  constexpr int E = Piece<T>::E, NK = Piece<T>::NK, SL = ac_slice<T, TH>();
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int N = a.N, V = a.V, Dm = a.max_depth;
+  SeqInfo& si = S.si;
+  Red& red = S.red;
+  const float c2 = 1.4426950408889634f / a.temperature;  // exp((x - m) / T) = exp2((x - m) c2)
+  const double temp = a.temperature;
+  const T* rows = (const T*)a.target_logits + (int64_t)b * (N + 1) * V;
+  seq_facts<TH>(a, seq_fetch(a, b), si);
+  for (int x = t; x < N; x += TH) S.bflag[x] = 0;  // node at or above the threshold, and its path too
+  if (t == 0) {
+    S.s_xc = 0;
+    S.rows[0] = 0;  // rows to follow: the root row first
+    S.q_head = 0;
+    S.q_tail = 1;
+  }
+  __syncthreads();
+  uint32_t xtag = 0;  // exchanges so far (the same on every member)
+  const int ns = (V + SL - 1) / SL;
+  const int nmine = rank < ns ? (ns - rank + G - 1) / G : 0;  // slices rank, rank + G, ...
+  // statistics of row r over the whole group, in every thread: M, the lowest id holding it, Z
+  auto row_stats = [&](int r, float& M, int& ID, double& Z) {
+    const T* row = rows + (int64_t)r * V;
+    float m = -INFINITY;
+    int id = AC_NO_ID;
+    double z = 0.0;
+    // two slices in flight (one for rows off 16 bytes, which load entry by entry)
+    constexpr int TD = ALIGNED ? 2 : 1;
+    uint4 raw[TD][NK];
+    if (nmine > 0) load_pieces<T, TH>(row, rank * SL, V, aligned, t, raw[0]);
+    for (int q = 0; q < nmine; q += TD) {
+#pragma unroll
+      for (int d = 0; d < TD; ++d) {
+        if (q + d < nmine) {
+          if (TD == 2 && q + d + 1 < nmine)
+            load_pieces<T, TH>(row, (rank + (q + d + 1) * G) * SL, V, aligned, t, raw[(d + 1) % TD]);
+          const int s0 = (rank + (q + d) * G) * SL;
+          // this thread's entries of the slice (ascending ids): maximum and lowest id, then the
+          // sum at that maximum, merged into the running pair
+          float sm = -INFINITY;
+          int sid = AC_NO_ID;
+#pragma unroll
+          for (int k = 0; k < NK; ++k) {
+            float x[E];
+            unpack16<T>(raw[d][k], x);
+            const int v = piece_v<T, TH>(s0, k, t);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+              if (v + e < V && x[e] > sm) { sm = x[e]; sid = v + e; }
+          }
+          if (sm != -INFINITY) {
+            double zd = 0.0;
+#pragma unroll
+            for (int k = 0; k < NK; ++k) {
+              float x[E], g = 0.f;
+              unpack16<T>(raw[d][k], x);
+              const int v = piece_v<T, TH>(s0, k, t);
+#pragma unroll
+              for (int e = 0; e < E; ++e)
+                if (v + e < V) g += exp2f((x[e] - sm) * c2);
+              zd += (double)g;
+            }
+            if (sm > m) {
+              z = (m == -INFINITY ? 0.0 : z * (double)exp2f((m - sm) * c2)) + zd;
+              m = sm;
+              id = sid;
+            } else {
+              z += zd * (double)exp2f((sm - m) * c2);
+            }
+          }
+          if (TD == 1 && q + 1 < nmine) load_pieces<T, TH>(row, (rank + (q + 1) * G) * SL, V, aligned, t, raw[0]);
+        }
+      }
+    }
+    // the work-group: maximum with the lowest id, sums rescaled to it
+    float bm = m;
+    int bid = id;
+    block_argmax<TH>(bm, bid, red);
+    const double zt = block_sum<TH>(m == -INFINITY ? 0.0 : z * (double)exp2f((m - bm) * c2), red);
+    M = bm;
+    ID = bid;
+    Z = zt;
+    if (G > 1) {
+      exchange<TH>(gslots, G, rank, ++xtag, 4, S.xv, ws.err, nullptr, &S.s_xc, __float_as_uint(bm), (uint32_t)bid,
+                   dlo(zt), dhi(zt));
+      M = -INFINITY;
+      ID = AC_NO_ID;
+      for (int k = 0; k < G; ++k) {  // members hold disjoint slices: the larger value, then the lower id
+        const float v = __uint_as_float(S.xv[k][0]);
+        const int i = (int)S.xv[k][1];
+        if (v > M || (v == M && i < ID)) { M = v; ID = i; }
+      }
+      Z = 0.0;
+      for (int k = 0; k < G; ++k) {
+        const float v = __uint_as_float(S.xv[k][0]);
+        if (v != -INFINITY) Z += dof(S.xv[k][2], S.xv[k][3]) * exp(((double)v - (double)M) / temp);
+      }
+    }
+    ID = greedy_token(ID);
+  };
+  int A = 0, stop_row = 0;
+  bool settled = false;  // the accepted node is known
+  for (;;) {
+    const int h = S.q_head;
+    if (h == S.q_tail) {  // uniform
+      if (settled) break;
+      settled = true;
+      // the accepted node: the deepest node at or above the threshold, lowest index on ties
+      int key = -1;
+      if (t < N && S.bflag[t]) key = (si.dep[t] << 9) | (511 - t);
+      {
+        float kv = (float)key;
+        int ki = key;
+        block_argmax<TH>(kv, ki, red);
+        key = (int)kv;
+      }
+      if (key >= 0) {
+        A = key >> 9;
+        const int stop = 511 - (key & 511);
+        stop_row = stop + 1;
+        if (t == 0) {
+          int node = stop;
+          for (int k = A - 1; k >= 0; --k) { si.path[k] = node; node = si.par[node]; }
+        }
+      }
+      // a followed stop row's argmax is known; one without usable children is read last
+      if (stop_row != 0 && !si.haskid[stop_row]) {
+        if (t == 0) S.rows[S.q_tail++] = (int16_t)stop_row;
+        __syncthreads();
+      }
+      continue;
+    }
+    const int r = S.rows[h];
+    row_kids<TH>(N, r, si);  // the usable children of row r, ascending
+    const int K = si.K;
+    float lc = 0.f;  // this thread's child's logit at its token
+    if (t < K) lc = load_as_f32<T>(rows + (int64_t)r * V, si.tok[si.kids[t]]);
+    float M;
+    int ID;
+    double Z;
+    row_stats(r, M, ID, Z);
+    const double sr = r == 0 ? 1.0 : S.nscore[r - 1];
+    bool push = false;
+    int c = 0;
+    if (t < K) {
+      c = si.kids[t];
+      const double sc = sr * (exp(((double)lc - (double)M) / temp) / Z);
+      if (sc >= (double)a.threshold) {
+        S.nscore[c] = sc;
+        S.bflag[c] = 1;
+        push = si.haskid[c + 1] != 0;
+      }
+    }
+    const uint64_t pm = __ballot(push);
+    if (lane == 0) si.wcount[wv] = __popcll(pm);
+    __syncthreads();
+    int off = S.q_tail, add = 0;
+    for (int k = 0; k < TH / 64; ++k) {
+      if (k < wv) off += si.wcount[k];
+      add += si.wcount[k];
+    }
+    if (push) S.rows[off + __popcll(pm & ((1ull << lane) - 1ull))] = (int16_t)(c + 1);
+    __syncthreads();  // every thread has read q_tail and the counts
+    if (t == 0) {
+      S.rowarg[r] = ID;
+      S.q_head = h + 1;
+      S.q_tail += add;
+    }
+    __syncthreads();
+  }
+  const int bonus = S.rowarg[stop_row];
+  if (t == 0) S.s_to = ld_u32(ws.err) != 0;  // set before the launch, or by a wait of this call that expired
+  __syncthreads();
+  if (rank != 0) return;
+  const bool to = S.s_to != 0;
+  if (t == 0) {
+    a.accept_len[b] = A;
+    a.num_out[b] = A + 1;
+    a.stop_row[b] = stop_row;
+    a.status[b] = to ? SV_SEQ_TIMEOUT : (si.bad_token ? SV_SEQ_TOKEN : 0);
+  }
+  if (t < Dm) a.accept_rows[(int64_t)b * Dm + t] = t < A ? si.path[t] + 1 : 0;
+  if (t <= Dm)
+    a.out_tokens[(int64_t)b * (Dm + 1) + t] = t < A ? a.tokens[(int64_t)b * N + si.path[t]] : (t == A ? bonus : 0);
+  // the accepted path into the cache (nothing after a timeout: the path may be wrong)
+  if (has_cm) svc::walker_commit(cm, b, to ? 0 : A, si.path);
+}
+
+// G: members per sequence of a chain (chain_G; the grid is chain_grid), unused for the list.
+// THR: the chains of threshold acceptance (mode 3) instead of greedy ones.
+template <typename T, bool ALIGNED, int TH, bool CHAIN, bool THR = false>
 __device__ __forceinline__ void greedy_rows_body(const sv_accept_args& a, int G, const AccWs& ws, const sv_commit_args& cm,
                                                  int32_t has_cm, AccShared<T, TH, false>& S) {
   const int t = threadIdx.x;
@@ -1194,7 +1397,8 @@ __device__ __forceinline__ void greedy_rows_body(const sv_accept_args& a, int G,
     const int b = (idx / G) * 8 + xcd, rank = idx % G;
     if (b < a.B) {
       XSlot* gslots = ws.xs + (int64_t)b * G * 2;
-      greedy_chain_seq<T, ALIGNED, TH>(a, b, rank, G, gslots, ws, cm, has_cm, S);
+      if constexpr (THR) thr_chain_seq<T, ALIGNED, TH>(a, b, rank, G, gslots, ws, cm, has_cm, S);
+      else greedy_chain_seq<T, ALIGNED, TH>(a, b, rank, G, gslots, ws, cm, has_cm, S);
       if (G > 1) {  // the group's last member leaves its exchange slots and exit count zeroed
         mem_complete();
         __syncthreads();
@@ -1224,12 +1428,19 @@ __device__ __forceinline__ void greedy_rows_body(const sv_accept_args& a, int G,
 // are where the two forms took about the same time on MI355X: a chain costs its longest path's
 // rows one after another (a slice load and an exchange each), the list its bytes plus a few
 // dependent steps at either end.
-inline bool rows_chain(const sv_accept_args& a) {
-  if ((int64_t)a.B * (a.N + 1) > AC_BLIST) return true;
-  if (a.flags & SV_FLAG_ROW_LIST) return false;
+inline bool chain_pays(const sv_accept_args& a) {
   const double half = (double)a.B * (a.N + 1) / 2 * (double)a.V * (a.logits_dtype == SV_BF16 ? 2 : 4);
   return half >= (a.B >= AC_CHAIN_B ? 48.0 : 96.0) * (1 << 20);
 }
+inline bool rows_chain(const sv_accept_args& a) {
+  if ((int64_t)a.B * (a.N + 1) > AC_BLIST) return true;
+  if (a.flags & SV_FLAG_ROW_LIST) return false;
+  return chain_pays(a);
+}
+// Threshold acceptance: chains by the same bound (rows on 16 bytes), else (or with
+// SV_FLAG_ROW_LIST) the row statistics of every row with a usable child and one walk per
+// sequence (sv_threshold.hip).
+inline bool thr_chain(const sv_accept_args& a) { return !(a.flags & SV_FLAG_ROW_LIST) && chain_pays(a); }
 // chains: whole groups of 8 sequences (one per XCD) of G members each
 inline int64_t chain_grid(const sv_accept_args& a, int G) { return ((int64_t)a.B + 7) / 8 * 8 * G; }
 static_assert(AC_BLIST <= 8192 && SV_MAX_DEPTH < 32, "leaf stream entries: batch row in 13 bits, depth in 5");
