@@ -50,6 +50,32 @@ ONE_LAUNCH_MAX_ROWS = 256
 ONE_LAUNCH_MAX_ROWS_WIDE = 1024
 
 
+def threshold_rows(w, acc):
+    """Logits rows a threshold walk must read: breadth first from the root row through the
+    children whose path score p_r(token) products stay at or above the threshold."""
+    import workloads as W
+    T, tau = float(w.temperature), float(w.threshold)
+    n = 0
+    for b in range(w.B):
+        par, tok = w.parents[b], w.tokens[b]
+        kids = {}
+        for i in range(w.N):
+            kids.setdefault(int(par[i]) + 1, []).append(i)
+        todo, seen = [(0, 1.0)], set()
+        while todo:
+            r, sc = todo.pop()
+            seen.add(r)
+            row = w.target_logits[b, r]
+            x = (W.bf16_to_f32(row) if row.dtype == np.uint16 else row).astype(np.float64) / T
+            p = np.exp(x - x.max())
+            p /= p.sum()
+            for c in kids.get(r, []):
+                if 0 <= tok[c] < w.V and sc * p[tok[c]] >= tau and c + 1 in kids:
+                    todo.append((c + 1, sc * p[tok[c]]))
+        n += len(seen) + (0 if int(acc["stop_row"][b]) in seen else 1)
+    return n
+
+
 def algorithmic_bytes(w, acc):
     """Bytes each stage must move at minimum (per step), from the workload and its accept results."""
     e = 2 if w.dtype == "bf16" else 4
@@ -67,6 +93,11 @@ def algorithmic_bytes(w, acc):
         # only from the argmax of the row before, and no other row decides the result (sibling
         # tokens that tie would add the rows below the tie)
         rows = int((acc["accept_len"].astype(np.int64) + 1).sum())
+    elif w.mode == "threshold":
+        # the rows of the root and of every node whose path scores at least the threshold and
+        # that has children (a deeper passing node can only be found through them), plus the
+        # stop row when it has none
+        rows = threshold_rows(w, acc)
     else:  # every row of a node with a child (and the draft rows in mode 1), plus the stop row
         for b in range(B):
             par = w.parents[b]
