@@ -51,10 +51,14 @@ CASES = [
     (3, dict(B=2, L=(16, 40), V=3001), "greedy"),
     (2, dict(B=2, L=64, V=12000, mode="topk"), "topk"),
     (2, dict(B=1, L=64, V=4000, mode="topk"), "topk"),
+    (3, dict(B=16, N=32, L=(16, 80), V=100000), "greedy"),  # path chains (rows of many bytes)
+    (3, dict(B=2, L=(16, 40), V=3001), "greedy"),
+    (3, dict(B=8, N=80, L=(16, 80), V=40000), "greedy"),  # the row list (512 rows or more)
+    (3, dict(B=3, L=(16, 40), V=5001), "greedy"),
 ]
 
 
-@pytest.mark.parametrize("pair", [(0, 1), (2, 3), (4, 5)])
+@pytest.mark.parametrize("pair", [(0, 1), (2, 3), (4, 5), (6, 7), (8, 9)])
 def test_noalloc_equals_sv_accept_twice(pair):
     for k in pair:  # two calls in a row, the second with the smaller input
         cfg, ov, mode = CASES[k]
@@ -71,7 +75,8 @@ def test_noalloc_equals_sv_accept_twice(pair):
 
 
 def test_noalloc_threshold_mode():
-    for ov in (dict(B=4, L=(16, 80), V=9001), dict(B=2, L=(16, 40), V=3001)):
+    # path chains (rows of many bytes), then the two-launch form on smaller inputs
+    for ov in (dict(B=16, N=32, L=(16, 80), V=100000), dict(B=4, L=(16, 80), V=9001), dict(B=2, L=(16, 40), V=3001)):
         w = W.config(3, **ov)
         w.mode = "threshold"
         w.threshold = float(np.float32(1e-3))
