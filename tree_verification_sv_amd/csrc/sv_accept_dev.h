@@ -800,8 +800,11 @@ __device__ __forceinline__ int greedy_walk(const sv_accept_args& a, const AccWs&
   // every row result of b has been read: leave them cleared for the next call
   for (int x = t; x <= N; x += TH) st_u64(&rr[x], 0ull);
   if (t < Dm) a.accept_rows[(int64_t)b * Dm + t] = t < A ? si.path[t] + 1 : 0;
-  if (t <= Dm && !(t == A && left >= 0))
-    a.out_tokens[(int64_t)b * (Dm + 1) + t] = t < A ? a.tokens[(int64_t)b * N + si.path[t]] : (t == A ? bonus : 0);
+  if (t <= Dm && !(t == A && left >= 0)) {
+    int tt = t;  // opaque copy: the lane's address is formed here, not held in registers across callers' loops
+    asm volatile("" : "+v"(tt));
+    a.out_tokens[(int64_t)b * (Dm + 1) + tt] = tt < A ? a.tokens[(int64_t)b * N + si.path[tt]] : (tt == A ? bonus : 0);
+  }
   // the accepted path into the cache (nothing after a timeout: the path may be wrong)
   if (has_cm) svc::walker_commit(cm, b, s_to ? 0 : A, si.path);
   return left;
