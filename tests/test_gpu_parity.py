@@ -143,10 +143,15 @@ def test_leak_free_on_gpu():
     assert np.array_equal(r0["out"][0, node], r1["out"][0, node])
 
 
-@pytest.mark.parametrize("variant", ["peaky", "short_prefix", "empty_prefix", "d64", "gqa1", "n256"])
+@pytest.mark.parametrize("variant", ["peaky", "short_prefix", "empty_prefix", "d64", "gqa1", "n256", "lpt_b256",
+                                     "lpt_b257"])
 def test_attention_variants(variant):
-    """Non-vacuity and edge shapes: sharp softmax, tree-dominated keys, L = 0, D = 64, G = 1, N = 256."""
-    if variant == "peaky":
+    """Non-vacuity and edge shapes: sharp softmax, tree-dominated keys, L = 0, D = 64, G = 1, N = 256;
+    paged batches of 256 and 257 ragged sequences with many equal lengths (one work-group per
+    (sequence, KV head): the longest-first order at 256, the plain order above it)."""
+    if variant.startswith("lpt_"):
+        w = W.config(3, B=int(variant[5:]), L=(16, 80), V=64)
+    elif variant == "peaky":
         w = W.config(2, L=700, V=64)
         w.q = W.f32_to_bf16(W.bf16_to_f32(w.q) * 8.0)
     elif variant == "short_prefix":

@@ -38,16 +38,63 @@ constexpr int TARGET_WG = 256;
 constexpr int AT_WAVES = 4;
 constexpr int AT_THREADS = 64 * AT_WAVES;
 // ------------------------------------------------------------------ MFMA path
+// Batches whose work-groups each own a whole (sequence, KV head) pair -- one query tile, one
+// split -- are dispatched longest sequence first: with prefix lengths of very different sizes
+// (a batch of live requests) an in-order dispatch leaves the last long sequences running alone
+// on a few CUs, while longest-first list scheduling bounds the tail by the shortest jobs.  A
+// batch whose lengths are all equal keeps the XCD-aware order (measured faster there).
+constexpr int AT_LPT_MAX_B = 256;  // batches up to this size are ordered (one LDS scan of B lengths)
+
+bool attn_longest_first(const sv_attn_args& a, const AttnPlan& p) {
+  return p.nsplit == 1 && p.qtiles == 1 && a.B > 1 && a.B <= AT_LPT_MAX_B;
+}
+
 template <int D>
-__global__ void __launch_bounds__(MF_THREADS, 2) k_attn_mfma(sv_attn_args a, AttnPlan p) {
+__global__ void __launch_bounds__(MF_THREADS, 2) k_attn_mfma(sv_attn_args a, AttnPlan p, int longest_first) {
   __shared__ __attribute__((aligned(1024))) unsigned char kvA[Tile<D>::BUF];
   __shared__ __attribute__((aligned(1024))) unsigned char kvB[Tile<D>::BUF];
   __shared__ __attribute__((aligned(1024))) unsigned char qsb[Tile<D>::QROWS * Tile<D>::ROWB];
   __shared__ int32_t s_bt[AT_BT_MAX];
-  // XCD-aware block order: consecutive logical ids land on the same XCD
   const int nb = gridDim.x;
   const int bid = blockIdx.x;
-  const int lid = (nb % 8 == 0) ? (bid % 8) * (nb / 8) + bid / 8 : bid;
+  int lid = -1;
+  if (longest_first) {  // uniform
+    // block bid takes the pair (sequence of rank bid / Hkv by length, KV head bid % Hkv): the
+    // round-robin placement of blocks on XCDs then gives every XCD the same mix of lengths, and
+    // each XCD starts its longest work first.  Rank: longer first, lower index first on ties.
+    const int r = bid / a.Hkv, t = threadIdx.x, lane = t & 63, w = t >> 6;
+    __shared__ int32_t s_pick;
+    for (int i = t; i < a.B; i += MF_THREADS) s_bt[i] = clamp_len(a.prefix_len[i], p.cap);
+    __syncthreads();
+    // every wave holds all B lengths (lane j % 64 of register j / 64; -1 past B) and ranks
+    // i = w, w + 8, ... with one ballot per 64 lengths; lane k holds the length of its k-th i
+    constexpr int NQ = AT_LPT_MAX_B / 64;
+    int lj[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) lj[q] = 64 * q + lane < a.B ? s_bt[64 * q + lane] : -1;
+    const int l0 = s_bt[0];
+    uint64_t differ = 0;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) differ |= __ballot(lj[q] >= 0 && lj[q] != l0);
+    if (!differ) s_pick = -1;  // equal lengths (every wave sees the same): the XCD-aware order below
+    const int mine = w + MF_WAVES * lane;
+    const int lmine = mine < a.B ? s_bt[mine] : 0;
+    for (int k = 0; differ && w + MF_WAVES * k < a.B; ++k) {  // uniform per wave
+      const int i = w + MF_WAVES * k;
+      const int li = __shfl(lmine, k);
+      int rank = 0;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        rank += __popcll(__ballot((lj[q] > li) | ((lj[q] == li) & (64 * q + lane < i))));
+      if (rank == r && lane == 0) s_pick = i;  // ranks are a permutation of 0 .. B-1: one writer
+    }
+    __syncthreads();
+    const int pick = s_pick;
+    lid = pick >= 0 ? pick * a.Hkv + bid % a.Hkv : -1;
+    __syncthreads();  // s_bt is the block-id table of the body from here on
+  }
+  // XCD-aware block order: consecutive logical ids land on the same XCD
+  if (!longest_first || lid < 0) lid = (nb % 8 == 0) ? (bid % 8) * (nb / 8) + bid / 8 : bid;
   attn_mfma_body<D>(a, p, lid, kvA, kvB, qsb, nullptr, 0, nullptr, s_bt);
 }
 
@@ -338,8 +385,9 @@ extern "C" sv_status sv_tree_attention(const sv_attn_args* args, void* stream) {
   if (use_mfma(a)) {
     const int64_t grid = (int64_t)a.B * a.Hkv * p.qtiles * p.nsplit;
     if (grid > 0x7fffffff) return SV_ERR_UNSUPPORTED;
-    if (a.D == 128) hipLaunchKernelGGL(k_attn_mfma<128>, dim3(grid), dim3(MF_THREADS), 0, s, a, p);
-    else hipLaunchKernelGGL(k_attn_mfma<64>, dim3(grid), dim3(MF_THREADS), 0, s, a, p);
+    const int lf = attn_longest_first(a, p) ? 1 : 0;
+    if (a.D == 128) hipLaunchKernelGGL(k_attn_mfma<128>, dim3(grid), dim3(MF_THREADS), 0, s, a, p, lf);
+    else hipLaunchKernelGGL(k_attn_mfma<64>, dim3(grid), dim3(MF_THREADS), 0, s, a, p, lf);
     if (p.nsplit > 1) {
       const int64_t rows = (int64_t)a.B * a.N * a.Hq;
       const dim3 cg((unsigned)((rows + 3) / 4));
